@@ -1,0 +1,216 @@
+"""CPU oracle for the elementwise operations -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline
+leg may import this package.  The product path (the HIP library and its
+Python binding) never imports it and shares no code with it.
+
+Each function wraps the plain scalar C loop of the same name in ``oracle.c``
+(built by ``oracle/build.py``) and works on numpy arrays:
+
+* ``add_f32(a, b)``            c = a + b, binary32
+* ``add_f16(a, b)``            binary16 bits in, binary16 bits out (uint16)
+* ``add_bf16(a, b)``           bfloat16 bits in, bfloat16 bits out (uint16)
+* ``saxpy_f32(alpha, x, y)``   returns fmaf(alpha, x, y) (y is not modified)
+* ``relu_f32(x)``              IEEE maximum(x, +0)
+* ``copy_f32(x)``              bitwise copy
+* ``gather_f32(x, stride)``    out[i] = x[(stride*i) mod n], bitwise
+
+plus the scalar conversions and the binary32 ulp distance.  Parity status:
+all functions pinned (see ``tests/test_oracle.py``); none unpinned.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        from . import build as _build
+        _build.build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    for name in ("oracle_add_f32", "oracle_add_f16", "oracle_add_bf16"):
+        getattr(lib, name).argtypes = [vp, vp, vp, sz]
+        getattr(lib, name).restype = None
+    lib.oracle_saxpy_f32.argtypes = [ctypes.c_float, vp, vp, sz]
+    lib.oracle_saxpy_f32.restype = None
+    for name in ("oracle_relu_f32", "oracle_copy_f32",
+                 "oracle_f32_to_f16_array", "oracle_f16_to_f32_array",
+                 "oracle_f32_to_bf16_array", "oracle_bf16_to_f32_array"):
+        getattr(lib, name).argtypes = [vp, vp, sz]
+        getattr(lib, name).restype = None
+    lib.oracle_gather_f32.argtypes = [vp, vp, sz, sz]
+    lib.oracle_gather_f32.restype = None
+    for name in ("oracle_f32_range_to_f16", "oracle_f32_range_to_bf16"):
+        getattr(lib, name).argtypes = [ctypes.c_uint32, ctypes.c_uint32, vp]
+        getattr(lib, name).restype = None
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_ulp_distance_f32.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.oracle_ulp_distance_f32.restype = ctypes.c_uint64
+    lib.oracle_fpenv_ok.argtypes = []
+    lib.oracle_fpenv_ok.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(arr):
+    return arr.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as(arr, dtype):
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {arr.dtype}")
+    return arr.reshape(-1)
+
+
+def _check_env(lib):
+    if not lib.oracle_fpenv_ok():
+        raise RuntimeError("oracle: MXCSR has FTZ/DAZ set or a non-RNE rounding mode")
+
+
+def fpenv_ok() -> bool:
+    """True when the host FP environment is IEEE default (no FTZ/DAZ, RNE)."""
+    return bool(_load().oracle_fpenv_ok())
+
+
+def _binary(name, a, b, dtype):
+    lib = _load()
+    _check_env(lib)
+    a = _as(a, dtype)
+    b = _as(b, dtype)
+    if a.shape != b.shape:
+        raise ValueError("shape mismatch")
+    c = np.empty_like(a)
+    getattr(lib, name)(_ptr(a), _ptr(b), _ptr(c), a.size)
+    return c
+
+
+def add_f32(a, b):
+    """c = a + b in binary32."""
+    return _binary("oracle_add_f32", a, b, np.float32)
+
+
+def add_f16(a, b):
+    """binary16 add via binary32 then RNE; uint16 bit patterns in and out."""
+    return _binary("oracle_add_f16", a, b, np.uint16)
+
+
+def add_bf16(a, b):
+    """bfloat16 add via binary32 then RNE; uint16 bit patterns in and out."""
+    return _binary("oracle_add_bf16", a, b, np.uint16)
+
+
+def saxpy_f32(alpha, x, y):
+    """Returns fmaf(alpha, x[i], y[i]) for every i; ``y`` is left unchanged."""
+    lib = _load()
+    _check_env(lib)
+    x = _as(x, np.float32)
+    out = np.array(_as(y, np.float32), copy=True)
+    if x.shape != out.shape:
+        raise ValueError("shape mismatch")
+    lib.oracle_saxpy_f32(float(np.float32(alpha)), _ptr(x), _ptr(out), x.size)
+    return out
+
+
+def relu_f32(x):
+    """IEEE 754-2019 maximum(x, +0) per element."""
+    lib = _load()
+    _check_env(lib)
+    x = _as(x, np.float32)
+    y = np.empty_like(x)
+    lib.oracle_relu_f32(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def copy_f32(x):
+    """Bitwise copy."""
+    lib = _load()
+    x = _as(x, np.float32)
+    y = np.empty_like(x)
+    lib.oracle_copy_f32(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def gather_f32(x, stride):
+    """out[i] = x[(stride*i) mod n], bitwise; exact index arithmetic."""
+    lib = _load()
+    x = _as(x, np.float32)
+    y = np.empty_like(x)
+    if x.size:
+        lib.oracle_gather_f32(_ptr(x), _ptr(y), x.size, int(stride))
+    return y
+
+
+def f32_to_f16(x):
+    lib = _load()
+    x = _as(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib.oracle_f32_to_f16_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def f16_to_f32(h):
+    lib = _load()
+    h = _as(h, np.uint16)
+    y = np.empty(h.shape, np.float32)
+    lib.oracle_f16_to_f32_array(_ptr(h), _ptr(y), h.size)
+    return y
+
+
+def f32_to_bf16(x):
+    lib = _load()
+    x = _as(x, np.float32)
+    y = np.empty(x.shape, np.uint16)
+    lib.oracle_f32_to_bf16_array(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def bf16_to_f32(h):
+    lib = _load()
+    h = _as(h, np.uint16)
+    y = np.empty(h.shape, np.float32)
+    lib.oracle_bf16_to_f32_array(_ptr(h), _ptr(y), h.size)
+    return y
+
+
+def f32_range_to_f16(start, count):
+    """Convert the binary32 bit patterns start..start+count-1 to binary16."""
+    lib = _load()
+    y = np.empty(count, np.uint16)
+    lib.oracle_f32_range_to_f16(start, count, _ptr(y))
+    return y
+
+
+def f32_range_to_bf16(start, count):
+    """Convert the binary32 bit patterns start..start+count-1 to bfloat16."""
+    lib = _load()
+    y = np.empty(count, np.uint16)
+    lib.oracle_f32_range_to_bf16(start, count, _ptr(y))
+    return y
+
+
+def ulp_distance_f32(a, b) -> int:
+    """|ord(a) - ord(b)| for two binary32 values (not NaN)."""
+    return int(_load().oracle_ulp_distance_f32(float(np.float32(a)), float(np.float32(b))))
+
+
+def library_path() -> str:
+    _load()
+    return _LIB_PATH

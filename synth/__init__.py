@@ -1,0 +1,142 @@
+"""Seeded synthetic inputs for the elementwise workloads.
+
+This module is shared by the tests, the bench and the smoke check.  It holds
+only the input recipe -- which distribution, which seed, which size, which
+pointer offset -- and none of the arithmetic of the operations themselves.
+
+Recipe (the pages use unseeded ``torch.randn``; every draw here is seeded):
+
+* uniform[-1, 1):  ``u = rng.random(n, dtype=float32)``; ``2*u - 1`` in
+  float32.  Every value is a multiple of 2^-23 in [-1, 1); -0.0, subnormals
+  and 1.0 cannot occur (both steps are exact in binary32).
+* normal(0, 1):    ``rng.standard_normal(n, dtype=float32)``.
+* binary16 / bfloat16 inputs "cast from fp32": the float32 draw above cast
+  round-to-nearest-even by numpy (``astype(float16)``) or torch CPU
+  (``.to(bfloat16)``), kept as uint16 bit patterns.
+* The generator is numpy ``Generator(PCG64(seed))``; A is drawn before B from
+  one generator.
+"""
+from dataclasses import dataclass, field
+import hashlib
+
+import numpy as np
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def uniform_pm1(g: np.random.Generator, n: int) -> np.ndarray:
+    """n float32 values uniform on [-1, 1) (multiples of 2^-23)."""
+    u = g.random(n, dtype=np.float32)
+    u *= np.float32(2.0)
+    u -= np.float32(1.0)
+    return u
+
+
+def normal01(g: np.random.Generator, n: int) -> np.ndarray:
+    """n float32 standard-normal values."""
+    return g.standard_normal(n, dtype=np.float32)
+
+
+def to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> binary16 (numpy RNE cast), as uint16 bit patterns."""
+    return x.astype(np.float16).view(np.uint16)
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 (torch CPU RNE cast), as uint16 bit patterns."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def sha256(arr: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(arr).view(np.uint8)).hexdigest()
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One configuration: operation, size, input recipe, pointer offsets.
+
+    ``offsets`` gives, per buffer role, how many elements past a 256-byte
+    aligned allocation the pointer handed to the library starts.
+    """
+    name: str
+    op: str               # add_f32 | add_f16 | add_bf16 | saxpy_f32 | relu_f32 | copy_f32 | gather_f32
+    n: int
+    seed: int
+    dist: str             # "uniform" | "normal"
+    offsets: dict = field(default_factory=dict)
+    alpha: float = 0.0    # saxpy only
+    stride: int = 0       # gather only
+    description: str = ""
+
+
+def _w(*args, **kw):
+    return Workload(*args, **kw)
+
+
+# The five configurations (plus the aligned headline add and the contiguous
+# copy that the strided gather is compared with).
+WORKLOADS = {
+    "cfg1_add_f32_2e20": _w(
+        "cfg1_add_f32_2e20", "add_f32", 1 << 20, 101, "uniform",
+        description="fp32 C=A+B, n=2^20, aligned, A,B uniform[-1,1)"),
+    "cfg2_add_f32_2e28p3_offA1": _w(
+        "cfg2_add_f32_2e28p3_offA1", "add_f32", (1 << 28) + 3, 102, "uniform",
+        offsets={"a": 1},
+        description="fp32 C=A+B, n=2^28+3, A offset by one element (4 B), A,B uniform[-1,1)"),
+    "cfg3_saxpy_f32_32M": _w(
+        "cfg3_saxpy_f32_32M", "saxpy_f32", 1 << 25, 103, "normal", alpha=2.5,
+        description="fp32 SAXPY in place y = 2.5*x + y, n=2^25, x,y normal(0,1)"),
+    "cfg4a_add_f16_2e28": _w(
+        "cfg4a_add_f16_2e28", "add_f16", 1 << 28, 104, "uniform",
+        description="fp16 C=A+B, n=2^28, A,B uniform[-1,1) cast RNE from fp32"),
+    "cfg4b_add_bf16_2e28": _w(
+        "cfg4b_add_bf16_2e28", "add_bf16", 1 << 28, 105, "uniform",
+        description="bf16 C=A+B, n=2^28, A,B uniform[-1,1) cast RNE from fp32"),
+    "cfg4c_relu_f32_2e28": _w(
+        "cfg4c_relu_f32_2e28", "relu_f32", 1 << 28, 106, "normal",
+        description="fp32 ReLU y=max(x,0), n=2^28, x normal(0,1), out of place"),
+    "cfg5a_copy_f32_2e26": _w(
+        "cfg5a_copy_f32_2e26", "copy_f32", 1 << 26, 107, "uniform",
+        description="fp32 contiguous copy out[i]=in[i], n=2^26, in uniform[-1,1)"),
+    "cfg5b_gather_f32_2e26_s2": _w(
+        "cfg5b_gather_f32_2e26_s2", "gather_f32", 1 << 26, 107, "uniform", stride=2,
+        description="fp32 strided gather out[i]=in[(2*i) mod n], n=2^26, in uniform[-1,1)"),
+    "headline_add_f32_2e28": _w(
+        "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
+        description="fp32 C=A+B, n=2^28, all buffers aligned"),
+}
+
+# Number of inputs each operation reads, and its element type.
+OP_INPUTS = {
+    "add_f32": ("a", "b"), "add_f16": ("a", "b"), "add_bf16": ("a", "b"),
+    "saxpy_f32": ("x", "y"), "relu_f32": ("x",), "copy_f32": ("x",),
+    "gather_f32": ("x",),
+}
+OP_DTYPE = {
+    "add_f32": np.float32, "add_f16": np.uint16, "add_bf16": np.uint16,
+    "saxpy_f32": np.float32, "relu_f32": np.float32, "copy_f32": np.float32,
+    "gather_f32": np.float32,
+}
+
+
+def make_inputs(op: str, n: int, seed: int, dist: str = "uniform") -> dict:
+    """Draw the inputs of ``op`` (numpy arrays keyed by role) for n elements."""
+    g = rng(seed)
+    draw = uniform_pm1 if dist == "uniform" else normal01
+    out = {}
+    for role in OP_INPUTS[op]:
+        x = draw(g, n)
+        if op == "add_f16":
+            x = to_f16_bits(x)
+        elif op == "add_bf16":
+            x = to_bf16_bits(x)
+        out[role] = x
+    return out
+
+
+def workload_inputs(w: Workload) -> dict:
+    return make_inputs(w.op, w.n, w.seed, w.dist)
