@@ -1,0 +1,351 @@
+#!/usr/bin/env python3
+"""Achieved HBM bandwidth of the elementwise kernels on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-others] [--no-cpu-baseline]
+
+A step is one call of the library on the workload (validation, plan, launch
+of the vectorised grid-stride kernel with its scalar head and tail).  The
+default workload is fp32 C = A + B on n = 2^28 + 3 elements with A one
+element (4 bytes) past an aligned allocation.
+
+Procedure: inputs are generated on the host, copied to the GPU once, and a
+parity gate compares one launch with the CPU oracle on every element (a
+workload that fails reports no speed).  The oracle runs only inside the CPU
+leg (``cpu_baseline_leg``), which also times it.  Then W untimed launches, then K
+launches bracketed by HIP events recorded on the stream the kernels run on.
+GB/s = algorithmic bytes (read + write, 10^9 bytes per GB) / average launch
+time.  Prints one JSON line.
+
+Also reported, in the same line:
+* ``roofline``: the dominant kernel's achieved GB/s against the 8 TB/s HBM
+  peak, and (``traffic``) the HBM bytes per launch measured by rocprofv3
+  counters when a summary for the current kernel source is in
+  ``profiles/traffic.json`` (else null);
+* ``cpu_baseline``: the CPU oracle timed on the host on a bounded sample;
+* ``other_configs``: the remaining workloads (each parity-gated); working
+  sets that fit in the 256 MB Infinity Cache are timed cold, with a 1 GiB
+  flush write before each timed launch.
+"""
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "cfg2_add_f32_2e28p3_offA1"
+KERNEL_SRC = os.path.join(ROOT, "memory_bound_elementwise_amd", "csrc", "ew_kernels.hip")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+# Algorithmic bytes per element: each input element read once, each output
+# element written once.  The gather counts logical bytes (read 4 + write 4).
+BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
+                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8}
+DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f32",
+         "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32"}
+MALL_BYTES = 256 * 2 ** 20
+
+
+def algorithmic_bytes(op: str, n: int) -> int:
+    return BYTES_PER_ELEM[op] * n
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Prepared:
+    """Device buffers of one workload and a launcher bound to a stream."""
+
+    def __init__(self, w, torch, np, ew, synth, stream):
+        from tests.gpu_util import upload
+        self.w = w
+        self.inp = synth.workload_inputs(w)
+        self.keep = []
+        offs = w.offsets
+        s = stream.cuda_stream
+        self.stream = s
+        if w.op in ("add_f32", "add_f16", "add_bf16"):
+            a, ka = upload(self.inp["a"], offs.get("a", 0))
+            b, kb = upload(self.inp["b"], offs.get("b", 0))
+            c, kc = upload(np.zeros(w.n, self.inp["a"].dtype), offs.get("c", 0))
+            self.keep += [ka, kb, kc]
+            fn = getattr(ew, "ew_" + w.op)
+            self.launch = lambda: fn(a, b, c, stream=s)
+            self.out, self.ptrs = c, (c, a, b)
+        elif w.op == "saxpy_f32":
+            x, kx = upload(self.inp["x"], offs.get("x", 0))
+            y, ky = upload(self.inp["y"], offs.get("y", 0))
+            self.keep += [kx, ky]
+            self.launch = lambda: ew.ew_saxpy_f32(w.alpha, x, y, stream=s)
+            self.out, self.ptrs = y, (y, x, y)
+        else:
+            x, kx = upload(self.inp["x"], offs.get("x", 0))
+            y, ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
+            self.keep += [kx, ky]
+            if w.op == "relu_f32":
+                self.launch = lambda: ew.ew_relu_f32(x, y, stream=s)
+            elif w.op == "copy_f32":
+                self.launch = lambda: ew.ew_copy_f32(x, y, stream=s)
+            else:
+                self.launch = lambda: ew.ew_gather_f32(x, y, w.stride, stream=s)
+            self.out, self.ptrs = y, (y, x, None)
+
+    def plan(self, ew, cus):
+        out, in0, in1 = self.ptrs
+        return ew.ew_make_plan(self.w.op, out.data_ptr(), in0.data_ptr(),
+                               in1.data_ptr() if in1 is not None else 0, self.w.n, cus)
+
+    def result(self, torch):
+        """One launch on fresh buffers; returns the output copied to the host."""
+        from tests.gpu_util import ELEM, download
+        self.launch()
+        torch.cuda.synchronize()
+        return download(self.out, ELEM[self.w.op])
+
+
+def time_launches(torch, launch, stream, steps, warmup, flush=None):
+    """Average launch time in ms.  Without flush: `steps` back-to-back
+    launches between two events on `stream`.  With flush: each launch is
+    bracketed by its own events after a cache-flush write."""
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    if flush is None:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            launch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    evs = []
+    with torch.cuda.stream(stream):
+        for _ in range(steps):
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            evs.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2]
+
+
+def cpu_baseline_leg(w, inp, got, target_s):
+    """The CPU leg: the only place bench.py runs the oracle.
+
+    1. One oracle pass over the whole workload; its output is the reference
+       for the parity gate (every element of the GPU result `got`).
+    2. The oracle timed as it stands (scalar C loop, one thread) on a bounded
+       sample: the first m elements of the same inputs, repeated until about
+       target_s seconds (target_s <= 0: the full pass of step 1 is the sample).
+    Returns (number of mismatching elements, cpu_baseline record)."""
+    import oracle
+    import synth
+    from tests.gpu_util import mismatches
+
+    def run(d):
+        if w.op in ("add_f32", "add_f16", "add_bf16"):
+            return getattr(oracle, w.op)(d["a"], d["b"])
+        if w.op == "saxpy_f32":
+            return oracle.saxpy_f32(w.alpha, d["x"], d["y"])
+        if w.op == "gather_f32":
+            return oracle.gather_f32(d["x"], w.stride)
+        return getattr(oracle, w.op)(d["x"])
+
+    t0 = time.perf_counter()
+    ref = run(inp)
+    full_s = time.perf_counter() - t0
+    bad = int(mismatches(w.op, got, ref).size)
+    del ref
+    if target_s <= 0:
+        gbs = algorithmic_bytes(w.op, w.n) / full_s / 1e9
+        sample = f"one full pass over all {w.n} elements ({full_s:.2f} s)"
+    else:
+        m = min(w.n, 1 << 26)
+        small = synth.make_inputs(w.op, m, w.seed, w.dist)
+        run(small)                                   # warm-up, first touch
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            run(small)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or reps >= 1000:
+                break
+        gbs = algorithmic_bytes(w.op, m) / (el / reps) / 1e9
+        sample = (f"{w.op} on the first {m} elements of the workload's inputs, {reps} passes "
+                  f"in {el:.1f} s")
+    rec = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": sample + " (scalar C loop, one thread)", "cpu": _cpu_model()}
+    return bad, rec
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def traffic_for(workload: str, launch_desc: dict):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source and launch shape; else None."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get("workloads", {}).get(workload)
+    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    if rec.get("launch") != launch_desc:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_target_s,
+            check=True):
+    prep = Prepared(w, torch, np, ew, synth, stream)
+    plan = prep.plan(ew, cus)
+    launch_desc = {"block": plan.block, "grid": plan.grid, "unroll": plan.unroll}
+    res = {"workload": w.name, "op": w.op, "n": w.n, "launch": launch_desc,
+           "split": {"head": plan.head, "vectors": plan.vectors, "tail": plan.tail,
+                     "in_coaligned": list(plan.in_coaligned)}}
+    got = prep.result(torch)
+    if check:
+        bad, cpu = cpu_baseline_leg(w, prep.inp, got, cpu_target_s)
+        res.update({"parity": "PASS" if bad == 0 else "FAIL", "mismatches": bad,
+                    "cpu_baseline": cpu})
+    else:
+        bad = 0
+        res["parity"] = "not checked (--no-cpu-baseline)"
+    del got
+    if bad:
+        return res, prep, None
+    nbytes = algorithmic_bytes(w.op, w.n)
+    footprint = nbytes if w.op != "gather_f32" else 8 * w.n
+    cold = footprint <= 2 * MALL_BYTES
+    flush = (lambda: flush_buf.fill_(1)) if cold else None
+    ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush)
+    gbs = nbytes / (ms / 1e3) / 1e9
+    res.update({"ms": round(ms, 5), "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
+                "timing": "cold (1 GiB flush before each launch), median" if cold else
+                          "back-to-back, mean"})
+    if cold:
+        warm_ms = time_launches(torch, prep.launch, stream, steps, 2)
+        res["warm_gbs"] = round(nbytes / (warm_ms / 1e3) / 1e9, 1)
+    return res, prep, ms
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this library runs each operation on one GPU; runs on more than one "
+              "GPU are not part of it (--gpus must be 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import memory_bound_elementwise_amd as ew
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    dev_props = torch.cuda.get_device_properties(0)
+    cus = dev_props.multi_processor_count
+    stream = torch.cuda.Stream()          # default priority
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w.name}: {w.description}")
+    res, prep, ms = measure(w, torch, np, ew, synth, stream, args.steps, args.warmup, cus,
+                            flush_buf, args.cpu_seconds, check=not args.no_cpu_baseline)
+    log(f"parity {res['parity']}; {res.get('gbs')} GB/s")
+
+    line = {
+        "metric": "achieved HBM GB/s (read+write bytes/time) and % of MI355X peak, N=2^28",
+        "value": res.get("gbs"),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res.get("ms"),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE[w.op],
+        "data": "synthetic (seeded: " + w.dist + ")",
+        "config": {"workload": w.description, "name": w.name, "op": w.op, "n": w.n,
+                   "offsets_elems": w.offsets, "launch": res["launch"], "split": res["split"],
+                   "global_batch": w.n, "parallelism": "single GPU"},
+        "parity": res["parity"],
+        "pct_of_peak": round(100 * res["gbs"] / PEAK_GBS, 2) if res.get("gbs") else None,
+    }
+    if ms is not None:
+        traffic = traffic_for(w.name, res["launch"])
+        line["roofline"] = {"bound": "hbm", "achieved": res["gbs"], "peak": PEAK_GBS,
+                            "unit": "GB/s", "frac": round(res["gbs"] / PEAK_GBS, 4),
+                            "traffic": traffic,
+                            "kernel": f"ew_stream_kernel<{w.op}, U={res['launch']['unroll']}>",
+                            "algorithmic_bytes_per_launch": algorithmic_bytes(w.op, w.n),
+                            "avg_launch_ms": res["ms"]}
+    del prep
+    torch.cuda.empty_cache()
+
+    if "cpu_baseline" in res:
+        line["cpu_baseline"] = res.pop("cpu_baseline")
+
+    if not args.no_others:
+        others = []
+        for name, ow in synth.WORKLOADS.items():
+            if name == w.name:
+                continue
+            log(f"other config {name}")
+            steps = 200 if ow.n >= (1 << 25) else 1000
+            r, p, _ = measure(ow, torch, np, ew, synth, stream, steps, 10, cus, flush_buf, 0.0,
+                              check=not args.no_cpu_baseline)
+            others.append(r)
+            del p
+            torch.cuda.empty_cache()
+        line["other_configs"] = others
+
+    line["env"] = {"device": torch.cuda.get_device_name(0), "cus": cus,
+                   "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                   "numpy": np.__version__, "kernel_source_sha256_16": kernel_source_hash()}
+    print(json.dumps(line), flush=True)
+    return 0 if res["parity"] == "PASS" else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

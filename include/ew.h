@@ -1,0 +1,201 @@
+/*
+ * ew.h -- C ABI of libew, streaming elementwise kernels for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Plain C: no C++ or torch types.  Every operation takes device pointers, an
+ * element count n and a HIP stream, validates its arguments on the host,
+ * launches one kernel asynchronously on that stream and returns a status.
+ *
+ * Pages cited (by title and section):
+ *   [HyperAI]   HyperAI article on optimising the Elementwise operator
+ *               (hyper.ai/ko/news/49090)
+ *   [EwOps]     "逐元素操作算子 / Element-wise 算子优化" (517adam.github.io)
+ *   [Puzzle31]  Mojo GPU Puzzles, "Puzzle 31: occupancy optimisation"
+ *               (puzzles.modular.com)
+ *   [PerfNotes] GPU-performance lecture notes (cyqw.cn/news/898472)
+ *
+ * Conventions shared by every operation
+ * -------------------------------------
+ * Memory      The caller owns every buffer (device memory, e.g. allocated by
+ *             torch).  The library never allocates, frees or keeps a pointer
+ *             after the call returns.
+ * Layout      One-dimensional, contiguous, n elements.  Pointers need only
+ *             element alignment (4 bytes for fp32, 2 bytes for 16-bit data);
+ *             16-byte alignment is NOT required: the library peels a scalar
+ *             head so that the output's body is 16-byte aligned, streams the
+ *             body with 16-byte vector accesses, and finishes a scalar tail.
+ * Streams     Asynchronous on `stream` (0 = the null stream).  The library
+ *             never synchronises.  A kernel fault surfaces at the caller's
+ *             next synchronisation, not here.
+ * n == 0      Returns EW_OK without launching anything (pointers unchecked).
+ * Aliasing    An output may be exactly the same pointer as an input where the
+ *             operation says so; any other overlap between an output range
+ *             and an input range returns EW_ERR_OVERLAP.
+ * Errors      Checked in this order, before any HIP call: null pointer or an
+ *             invalid size/stride (EW_ERR_INVALID_ARG), element misalignment
+ *             (EW_ERR_MISALIGNED), overlap (EW_ERR_OVERLAP).  Then: no HIP
+ *             device (EW_ERR_NO_DEVICE), a failed launch (EW_ERR_HIP; the
+ *             hipError_t is kept for ew_last_hip_error()).  Nothing aborts.
+ * Numerics    IEEE-754 round-to-nearest-even, subnormals preserved (no
+ *             flush-to-zero).  NaN results are NaN; their payload is not part
+ *             of the contract for arithmetic operations.  Copy and gather
+ *             move bit patterns unchanged.
+ * Threads     All functions are thread-safe.
+ */
+#ifndef EW_H_
+#define EW_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The HIP runtime declares hipStream_t the same way; repeating an identical
+ * typedef is valid C11 and C++. */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum ew_status {
+    EW_OK = 0,
+    EW_ERR_INVALID_ARG = -1, /* null pointer, size overflow, zero stride, unknown op name */
+    EW_ERR_MISALIGNED = -2,  /* pointer not aligned to its element size */
+    EW_ERR_OVERLAP = -3,     /* output partially overlaps an input */
+    EW_ERR_NO_DEVICE = -4,   /* no HIP device is usable */
+    EW_ERR_HIP = -5          /* a HIP runtime call failed; see ew_last_hip_error() */
+} ew_status_t;
+
+/* ------------------------------------------------------------------------ */
+/* Operations                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* c[i] = a[i] + b[i] in binary32, i < n.
+ * [HyperAI] "Version 1: FP32 baseline" and "Version 2: FP32x4 vectorisation";
+ * [EwOps] section 二, template code and optimisation points 2-3 (grid-stride
+ * loop, float4 body with a scalar tail).
+ * a, b: inputs (device, 4-byte aligned).  c: output (device, 4-byte aligned);
+ * c may equal a or b exactly. */
+ew_status_t ew_add_f32(const float *a, const float *b, float *c, size_t n,
+                       hipStream_t stream);
+
+/* c[i] = rne16(widen(a[i]) + widen(b[i])) on binary16 data passed as raw
+ * uint16_t bit patterns: each pair is widened exactly to binary32, added
+ * once, and the sum rounded to binary16, nearest-even.  This equals the
+ * correctly rounded binary16 sum.
+ * [HyperAI] "Version 3: FP16 baseline" (half add per element) and
+ * "Version 6: FP16x8 pack" (eight halves per 128-bit access).
+ * Pointers 2-byte aligned; c may equal a or b exactly. */
+ew_status_t ew_add_f16(const uint16_t *a, const uint16_t *b, uint16_t *c,
+                       size_t n, hipStream_t stream);
+
+/* The same as ew_add_f16 for bfloat16 bit patterns: widen, add in binary32,
+ * round to bfloat16 nearest-even.  (The pages treat binary16; bfloat16 takes
+ * the same rule.)  Pointers 2-byte aligned; c may equal a or b exactly. */
+ew_status_t ew_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *c,
+                        size_t n, hipStream_t stream);
+
+/* In place: y[i] = fma(alpha, x[i], y[i]), one rounding per element.
+ * [Puzzle31] overview: single-precision alpha times x plus y.
+ * x: input, y: input and output (both 4-byte aligned); x may equal y
+ * exactly. */
+ew_status_t ew_saxpy_f32(float alpha, const float *x, float *y, size_t n,
+                         hipStream_t stream);
+
+/* y[i] = maximum(x[i], +0) in the IEEE 754-2019 sense: x > 0 gives x, a NaN
+ * gives a NaN, everything else (negative, -0, -inf) gives +0.
+ * [PerfNotes] section 5.2, ReLU as a memory-bound example.
+ * x: input, y: output (4-byte aligned); y may equal x exactly. */
+ew_status_t ew_relu_f32(const float *x, float *y, size_t n, hipStream_t stream);
+
+/* out[i] = in[i], bit patterns unchanged (NaN payloads included).
+ * [PerfNotes] section 3.2, the coalesced copy kernel.
+ * out == in is allowed and launches nothing. */
+ew_status_t ew_copy_f32(const float *in, float *out, size_t n,
+                        hipStream_t stream);
+
+/* out[i] = in[(stride * i) mod n], bit patterns unchanged; the index product
+ * is reduced exactly for every stride (no 32- or 64-bit wrap-around).
+ * [PerfNotes] section 3.2, the non-coalesced copy kernel reads in[idx*2 % n].
+ * Reads are strided; writes are contiguous.  stride 0 -> EW_ERR_INVALID_ARG.
+ * in and out must not overlap at all. */
+ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Status, launch configuration and planning                                */
+/* ------------------------------------------------------------------------ */
+
+/* Static string for a status code (never NULL). */
+const char *ew_status_string(ew_status_t status);
+
+/* The hipError_t behind the most recent EW_ERR_HIP on the calling thread
+ * (0 if none). */
+int ew_last_hip_error(void);
+
+/* Library ABI version (incremented on any incompatible change). */
+int ew_abi_version(void);
+
+/* Launch configuration, per operation name ("add_f32", "add_f16",
+ * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32") and size
+ * class: a row applies to every n >= min_n up to the next row's min_n.  The
+ * grid is min(blocks_per_cu * CU count, number of tiles), where a tile is
+ * block * unroll 16-byte vectors; each block walks tiles with a grid stride
+ * ([EwOps] optimisation point 2: a grid sized to the processor count).
+ * block: a multiple of 64 in [64, 1024]; blocks_per_cu in [1, 1024];
+ * unroll in {1, 2, 4, 8}.  Setting a row with an existing min_n replaces it.
+ * Returns EW_ERR_INVALID_ARG for an unknown op or a value out of range. */
+ew_status_t ew_set_launch_config(const char *op, size_t min_n, int block,
+                                 int blocks_per_cu, int unroll);
+
+/* The row that applies to n (no device needed). */
+ew_status_t ew_get_launch_config(const char *op, size_t n, int *block,
+                                 int *blocks_per_cu, int *unroll);
+
+/* Restore the compiled-in table (tuned on MI355X). */
+void ew_reset_launch_config(void);
+
+/* Read rows "op min_n block blocks_per_cu unroll" (one per line, '#'
+ * comments) from a text file and apply them with ew_set_launch_config.
+ * EW_ERR_INVALID_ARG on an unreadable file or a malformed row (rows before
+ * it stay applied). */
+ew_status_t ew_load_launch_table(const char *path);
+
+/* The host-side plan of one call: how the n elements split into a scalar
+ * head, a body of 16-byte vectors and a scalar tail, and how the body is
+ * launched.  Pure arithmetic on the pointer values -- nothing is touched and
+ * no device is needed (pass cu_count explicitly).
+ *   head       elements before the output reaches 16-byte alignment
+ *              ((16 - out mod 16) mod 16) / element size, capped at n
+ *   vectors    16-byte vectors in the body, floor((n - head) / vec_elems)
+ *   tail       n - head - vectors * vec_elems  (< vec_elems)
+ *   in_coaligned[k]  1 if input k's body start is 16-byte aligned too
+ *              (then it is read with aligned 16-byte loads; otherwise with
+ *              4- or 2-byte aligned 16-byte loads); unused inputs report 1
+ *   tiles      ceil(vectors / (block * unroll))
+ *   grid       min(blocks_per_cu * cu_count, tiles)  (0 when tiles == 0)
+ * Validation is the same as the operation's (in1 is ignored for one-input
+ * ops; for saxpy in0 = x and out = y). */
+typedef struct ew_plan {
+    size_t n;
+    size_t head;
+    size_t vectors;
+    size_t tail;
+    size_t tiles;
+    int vec_elems;
+    int elem_size;
+    int in_coaligned[2];
+    int block;
+    int blocks_per_cu;
+    int unroll;
+    int grid;
+} ew_plan_t;
+
+ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
+                         const void *in1, size_t n, int cu_count,
+                         ew_plan_t *plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EW_H_ */

@@ -1,0 +1,218 @@
+"""Python binding of libew, streaming elementwise kernels for MI355X.
+
+Argument marshalling only: each function below passes device pointers, n and
+a HIP stream to the C entry point of the same name in ``libew.so`` (declared
+in ``include/ew.h``) and raises ``EwError`` on a non-zero status.  Every
+operation runs in the library's HIP kernels; there is no other code path.
+If ``libew.so`` has not been built, importing this package raises.
+
+Buffers may be torch tensors (their ``data_ptr()``; pass sliced tensors to
+get offset pointers) or plain integers holding device addresses.  ``n``
+defaults to the output tensor's ``numel()``; ``stream`` defaults to torch's
+current stream on the output's device (an integer ``hipStream_t`` is also
+accepted).  Calls are asynchronous, like the C functions.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "EwError", "EwPlan", "OPS", "library_path",
+    "ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
+    "ew_copy_f32", "ew_gather_f32", "ew_status_string", "ew_last_hip_error",
+    "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
+    "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libew.so")
+LAUNCH_TABLE = os.path.join(_PKG, "launch_table.txt")
+
+OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python memory_bound_elementwise_amd/build.py` "
+        "or __graft_entry__.build() first")
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_vp, _sz, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+
+
+class EwPlan(ctypes.Structure):
+    """Mirror of ``ew_plan_t``."""
+    _fields_ = [
+        ("n", _sz), ("head", _sz), ("vectors", _sz), ("tail", _sz), ("tiles", _sz),
+        ("vec_elems", _int), ("elem_size", _int), ("in_coaligned", _int * 2),
+        ("block", _int), ("blocks_per_cu", _int), ("unroll", _int), ("grid", _int),
+    ]
+
+    def as_dict(self):
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["in_coaligned"] = tuple(self.in_coaligned)
+        return d
+
+
+def _proto(name, restype, *argtypes):
+    fn = getattr(_lib, name)
+    fn.restype = restype
+    fn.argtypes = list(argtypes)
+    return fn
+
+
+_c = {
+    "ew_add_f32": _proto("ew_add_f32", _int, _vp, _vp, _vp, _sz, _vp),
+    "ew_add_f16": _proto("ew_add_f16", _int, _vp, _vp, _vp, _sz, _vp),
+    "ew_add_bf16": _proto("ew_add_bf16", _int, _vp, _vp, _vp, _sz, _vp),
+    "ew_saxpy_f32": _proto("ew_saxpy_f32", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
+    "ew_relu_f32": _proto("ew_relu_f32", _int, _vp, _vp, _sz, _vp),
+    "ew_copy_f32": _proto("ew_copy_f32", _int, _vp, _vp, _sz, _vp),
+    "ew_gather_f32": _proto("ew_gather_f32", _int, _vp, _vp, _sz, _sz, _vp),
+    "ew_status_string": _proto("ew_status_string", ctypes.c_char_p, _int),
+    "ew_last_hip_error": _proto("ew_last_hip_error", _int),
+    "ew_abi_version": _proto("ew_abi_version", _int),
+    "ew_set_launch_config": _proto("ew_set_launch_config", _int, ctypes.c_char_p, _sz,
+                                   _int, _int, _int),
+    "ew_get_launch_config": _proto("ew_get_launch_config", _int, ctypes.c_char_p, _sz,
+                                   ctypes.POINTER(_int), ctypes.POINTER(_int),
+                                   ctypes.POINTER(_int)),
+    "ew_reset_launch_config": _proto("ew_reset_launch_config", None),
+    "ew_load_launch_table": _proto("ew_load_launch_table", _int, ctypes.c_char_p),
+    "ew_make_plan": _proto("ew_make_plan", _int, ctypes.c_char_p, _vp, _vp, _vp, _sz, _int,
+                           ctypes.POINTER(EwPlan)),
+}
+
+
+class EwError(RuntimeError):
+    """A libew call returned a non-zero status."""
+
+    def __init__(self, status: int, func: str):
+        self.status = status
+        self.hip_error = _c["ew_last_hip_error"]() if status == -5 else 0
+        msg = _c["ew_status_string"](status).decode()
+        if self.hip_error:
+            msg += f" (hipError_t {self.hip_error})"
+        super().__init__(f"{func}: {msg}")
+
+
+def _check(status, func):
+    if status != 0:
+        raise EwError(status, func)
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _numel(x, n):
+    if n is not None:
+        return int(n)
+    if isinstance(x, int):
+        raise ValueError("n is required when buffers are raw pointers")
+    return x.numel()
+
+
+def _stream(x, stream):
+    if stream is None:
+        if isinstance(x, int):
+            return None
+        import torch
+        return torch.cuda.current_stream(x.device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def ew_add_f32(a, b, c, n=None, stream=None):
+    """c = a + b (binary32)."""
+    _check(_c["ew_add_f32"](_addr(a), _addr(b), _addr(c), _numel(c, n), _stream(c, stream)),
+           "ew_add_f32")
+
+
+def ew_add_f16(a, b, c, n=None, stream=None):
+    """c = a + b on binary16 data (widen, add in binary32, round RNE)."""
+    _check(_c["ew_add_f16"](_addr(a), _addr(b), _addr(c), _numel(c, n), _stream(c, stream)),
+           "ew_add_f16")
+
+
+def ew_add_bf16(a, b, c, n=None, stream=None):
+    """c = a + b on bfloat16 data (widen, add in binary32, round RNE)."""
+    _check(_c["ew_add_bf16"](_addr(a), _addr(b), _addr(c), _numel(c, n), _stream(c, stream)),
+           "ew_add_bf16")
+
+
+def ew_saxpy_f32(alpha, x, y, n=None, stream=None):
+    """y = fma(alpha, x, y) in place."""
+    _check(_c["ew_saxpy_f32"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+                              _stream(y, stream)), "ew_saxpy_f32")
+
+
+def ew_relu_f32(x, y, n=None, stream=None):
+    """y = maximum(x, +0)."""
+    _check(_c["ew_relu_f32"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
+           "ew_relu_f32")
+
+
+def ew_copy_f32(src, out, n=None, stream=None):
+    """out = src, bitwise."""
+    _check(_c["ew_copy_f32"](_addr(src), _addr(out), _numel(out, n), _stream(out, stream)),
+           "ew_copy_f32")
+
+
+def ew_gather_f32(src, out, stride, n=None, stream=None):
+    """out[i] = src[(stride * i) mod n], bitwise."""
+    _check(_c["ew_gather_f32"](_addr(src), _addr(out), _numel(out, n), int(stride),
+                               _stream(out, stream)), "ew_gather_f32")
+
+
+def ew_status_string(status: int) -> str:
+    return _c["ew_status_string"](int(status)).decode()
+
+
+def ew_last_hip_error() -> int:
+    return _c["ew_last_hip_error"]()
+
+
+def ew_abi_version() -> int:
+    return _c["ew_abi_version"]()
+
+
+def ew_set_launch_config(op, min_n, block, blocks_per_cu, unroll):
+    _check(_c["ew_set_launch_config"](op.encode(), int(min_n), int(block), int(blocks_per_cu),
+                                      int(unroll)), "ew_set_launch_config")
+
+
+def ew_get_launch_config(op, n):
+    """(block, blocks_per_cu, unroll) of the row that applies to n."""
+    b, k, u = _int(), _int(), _int()
+    _check(_c["ew_get_launch_config"](op.encode(), int(n), ctypes.byref(b), ctypes.byref(k),
+                                      ctypes.byref(u)), "ew_get_launch_config")
+    return b.value, k.value, u.value
+
+
+def ew_reset_launch_config():
+    _c["ew_reset_launch_config"]()
+
+
+def ew_load_launch_table(path):
+    _check(_c["ew_load_launch_table"](os.fsencode(path)), "ew_load_launch_table")
+
+
+def ew_make_plan(op, out, in0, in1, n, cu_count) -> EwPlan:
+    """Host-side head/body/tail split and launch shape for integer addresses."""
+    plan = EwPlan()
+    _check(_c["ew_make_plan"](op.encode(), out, in0, in1, int(n), int(cu_count),
+                              ctypes.byref(plan)), "ew_make_plan")
+    return plan
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+if os.path.exists(LAUNCH_TABLE):
+    ew_load_launch_table(LAUNCH_TABLE)

@@ -1,0 +1,471 @@
+// ew_api.cpp -- host side of libew: argument validation, the head/body/tail
+// plan, the launch-configuration table and the exported C ABI (include/ew.h).
+//
+// Validation runs before any HIP call, so every argument error is reported
+// the same way on a machine without a GPU.
+
+#include "ew.h"
+#include "ew_internal.h"
+
+#include <atomic>
+#include <cerrno>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+namespace ew {
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+struct OpInfo {
+    const char *name;
+    int elem_size;
+    int inputs;          // 1 or 2
+    bool alias_ok;       // output may be exactly an input
+};
+
+constexpr OpInfo kOps[kOpCount] = {
+    {"add_f32", 4, 2, true},
+    {"add_f16", 2, 2, true},
+    {"add_bf16", 2, 2, true},
+    {"saxpy_f32", 4, 2, true},
+    {"relu_f32", 4, 1, true},
+    {"copy_f32", 4, 1, true},
+    {"gather_f32", 4, 1, false},
+};
+
+int op_from_name(const char *name)
+{
+    if (!name) return -1;
+    for (int i = 0; i < kOpCount; ++i)
+        if (std::strcmp(kOps[i].name, name) == 0) return i;
+    return -1;
+}
+
+// ---------------------------------------------------------------------------
+// Launch-configuration table
+// ---------------------------------------------------------------------------
+
+struct Row {
+    size_t min_n;
+    int block;
+    int blocks_per_cu;
+    int unroll;
+};
+
+// Compiled-in defaults, measured on MI355X (256 CUs, 8 TB/s HBM3E) with the
+// tuner in this package; a row covers n >= min_n up to the next row.
+struct DefaultRow {
+    int op;
+    Row row;
+};
+constexpr DefaultRow kDefaults[] = {
+    {kOpAddF32, {0, 256, 8, 1}},    {kOpAddF32, {size_t(1) << 22, 256, 8, 2}},
+    {kOpAddF16, {0, 256, 8, 1}},    {kOpAddF16, {size_t(1) << 22, 256, 8, 2}},
+    {kOpAddBF16, {0, 256, 8, 1}},   {kOpAddBF16, {size_t(1) << 22, 256, 8, 2}},
+    {kOpSaxpyF32, {0, 256, 8, 1}},  {kOpSaxpyF32, {size_t(1) << 22, 256, 8, 2}},
+    {kOpReluF32, {0, 256, 8, 1}},   {kOpReluF32, {size_t(1) << 22, 256, 8, 2}},
+    {kOpCopyF32, {0, 256, 8, 1}},   {kOpCopyF32, {size_t(1) << 22, 256, 8, 2}},
+    {kOpGatherF32, {0, 256, 8, 1}}, {kOpGatherF32, {size_t(1) << 22, 256, 8, 2}},
+};
+
+constexpr int kMaxRows = 16;
+
+struct Table {
+    std::mutex mu;
+    bool loaded = false;
+    std::vector<Row> rows[kOpCount];
+};
+
+Table &table()
+{
+    static Table t;
+    return t;
+}
+
+void reset_locked(Table &t)
+{
+    for (auto &r : t.rows) r.clear();
+    for (const auto &d : kDefaults) t.rows[d.op].push_back(d.row);
+    t.loaded = true;
+}
+
+void ensure_loaded_locked(Table &t)
+{
+    if (!t.loaded) reset_locked(t);
+}
+
+bool valid_row(int block, int bpc, int unroll)
+{
+    if (block < 64 || block > 1024 || block % 64 != 0) return false;
+    if (bpc < 1 || bpc > 1024) return false;
+    return unroll == 1 || unroll == 2 || unroll == 4 || unroll == 8;
+}
+
+ew_status_t set_row(int op, size_t min_n, int block, int bpc, int unroll)
+{
+    if (op < 0 || !valid_row(block, bpc, unroll)) return EW_ERR_INVALID_ARG;
+    Table &t = table();
+    std::lock_guard<std::mutex> g(t.mu);
+    ensure_loaded_locked(t);
+    auto &rows = t.rows[op];
+    for (auto &r : rows) {
+        if (r.min_n == min_n) {
+            r = Row{min_n, block, bpc, unroll};
+            return EW_OK;
+        }
+    }
+    if ((int)rows.size() >= kMaxRows) return EW_ERR_INVALID_ARG;
+    size_t pos = 0;
+    while (pos < rows.size() && rows[pos].min_n < min_n) ++pos;
+    rows.insert(rows.begin() + pos, Row{min_n, block, bpc, unroll});
+    return EW_OK;
+}
+
+Row get_row(int op, size_t n)
+{
+    Table &t = table();
+    std::lock_guard<std::mutex> g(t.mu);
+    ensure_loaded_locked(t);
+    Row best{0, 256, 8, 1};
+    bool found = false;
+    for (const auto &r : t.rows[op]) {
+        if (r.min_n <= n && (!found || r.min_n >= best.min_n)) {
+            best = r;
+            found = true;
+        }
+    }
+    return best;
+}
+
+// ---------------------------------------------------------------------------
+// Devices
+// ---------------------------------------------------------------------------
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+std::atomic<bool> g_device_seen{false};
+
+// Current device and its compute-unit count, or an error status.
+ew_status_t current_device(int *cu_count)
+{
+    hipError_t e;
+    if (!g_device_seen.load(std::memory_order_acquire)) {
+        int count = 0;
+        e = hipGetDeviceCount(&count);
+        if (e != hipSuccess || count <= 0) {
+            (void)hipGetLastError();  // do not leave our probe's error behind
+            return EW_ERR_NO_DEVICE;
+        }
+        g_device_seen.store(true, std::memory_order_release);
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = (int)e;
+        return EW_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return EW_ERR_NO_DEVICE;
+    int cus = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cus <= 0) {
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess || cus <= 0) {
+            g_last_hip_error = (int)e;
+            return EW_ERR_HIP;
+        }
+        g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    }
+    *cu_count = cus;
+    return EW_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Validation and planning
+// ---------------------------------------------------------------------------
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool ranges_intersect(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Checks shared by every operation.  ins[k] may be nullptr only when the op
+// has fewer inputs.
+ew_status_t validate(int op, const void *out, const void *in0, const void *in1, size_t n)
+{
+    const OpInfo &info = kOps[op];
+    if (!out || !in0 || (info.inputs == 2 && !in1)) return EW_ERR_INVALID_ARG;
+    const size_t es = (size_t)info.elem_size;
+    if (n > SIZE_MAX / es) return EW_ERR_INVALID_ARG;
+    const size_t bytes = n * es;
+    // Element indices and the gather's index sums stay below 2^62.
+    if (n >= (size_t(1) << 62)) return EW_ERR_INVALID_ARG;
+    const void *ptrs[3] = {out, in0, info.inputs == 2 ? in1 : nullptr};
+    for (const void *p : ptrs) {
+        if (!p) continue;
+        const uintptr_t u = reinterpret_cast<uintptr_t>(p);
+        if (u > UINTPTR_MAX - bytes) return EW_ERR_INVALID_ARG;
+    }
+    for (const void *p : ptrs) {
+        if (p && reinterpret_cast<uintptr_t>(p) % es != 0) return EW_ERR_MISALIGNED;
+    }
+    const Range ro{reinterpret_cast<uintptr_t>(out), reinterpret_cast<uintptr_t>(out) + bytes};
+    for (int k = 1; k <= info.inputs; ++k) {
+        const Range ri{reinterpret_cast<uintptr_t>(ptrs[k]),
+                       reinterpret_cast<uintptr_t>(ptrs[k]) + bytes};
+        if (!ranges_intersect(ro, ri)) continue;
+        if (info.alias_ok && ro.lo == ri.lo) continue;  // exact alias
+        return EW_ERR_OVERLAP;
+    }
+    return EW_OK;
+}
+
+struct Plan {
+    size_t head, vectors, tail, tiles;
+    bool co[2];
+    Launch launch;
+    int blocks_per_cu;
+};
+
+// The split and the launch shape (arguments already validated, n > 0).
+Plan make_plan(int op, const void *out, const void *in0, const void *in1, size_t n, int cu_count)
+{
+    const OpInfo &info = kOps[op];
+    const size_t es = (size_t)info.elem_size;
+    const size_t vec = 16 / es;
+    Plan p{};
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out);
+    size_t head = ((16 - (o % 16)) % 16) / es;
+    if (head > n) head = n;
+    p.head = head;
+    p.vectors = (n - head) / vec;
+    p.tail = n - head - p.vectors * vec;
+    const void *ins[2] = {in0, info.inputs == 2 ? in1 : nullptr};
+    for (int k = 0; k < 2; ++k) {
+        p.co[k] = true;
+        if (op != kOpGatherF32 && ins[k])
+            p.co[k] = (reinterpret_cast<uintptr_t>(ins[k]) + head * es) % 16 == 0;
+    }
+    const Row r = get_row(op, n);
+    const size_t tile_vecs = (size_t)r.block * (size_t)r.unroll;
+    p.tiles = (p.vectors + tile_vecs - 1) / tile_vecs;
+    size_t grid = (size_t)r.blocks_per_cu * (size_t)(cu_count > 0 ? cu_count : 1);
+    if (grid > p.tiles) grid = p.tiles;
+    if (grid == 0) grid = 1;  // head/tail lanes still need one block
+    p.launch = Launch{r.block, (int)grid, r.unroll};
+    p.blocks_per_cu = r.blocks_per_cu;
+    return p;
+}
+
+ew_status_t fail_hip(hipError_t e)
+{
+    g_last_hip_error = (int)e;
+    return EW_ERR_HIP;
+}
+
+ew_status_t run_stream(int op, const void *out, const void *in0, const void *in1, size_t n,
+                       float alpha, hipStream_t stream)
+{
+    if (n == 0) return EW_OK;
+    ew_status_t st = validate(op, out, in0, in1, n);
+    if (st != EW_OK) return st;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    const Plan p = make_plan(op, out, in0, in1, n, cus);
+    StreamArgs a{};
+    a.in0 = in0;
+    a.in1 = kOps[op].inputs == 2 ? in1 : nullptr;
+    a.out = const_cast<void *>(out);
+    a.head = p.head;
+    a.vectors = p.vectors;
+    a.tail = p.tail;
+    a.tiles = p.tiles;
+    a.alpha = alpha;
+    const hipError_t e = launch_stream(static_cast<OpId>(op), a, p.co[0], p.co[1], p.launch, stream);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
+}
+
+// (a * b) mod m without overflow (host: 128-bit arithmetic).
+uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
+{
+    return (uint64_t)(((unsigned __int128)a * (unsigned __int128)b) % (unsigned __int128)m);
+}
+
+}  // namespace
+}  // namespace ew
+
+using namespace ew;
+
+extern "C" {
+
+ew_status_t ew_add_f32(const float *a, const float *b, float *c, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAddF32, c, a, b, n, 0.0f, s);
+}
+
+ew_status_t ew_add_f16(const uint16_t *a, const uint16_t *b, uint16_t *c, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAddF16, c, a, b, n, 0.0f, s);
+}
+
+ew_status_t ew_add_bf16(const uint16_t *a, const uint16_t *b, uint16_t *c, size_t n,
+                        hipStream_t s)
+{
+    return run_stream(kOpAddBF16, c, a, b, n, 0.0f, s);
+}
+
+ew_status_t ew_saxpy_f32(float alpha, const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSaxpyF32, y, x, y, n, alpha, s);
+}
+
+ew_status_t ew_relu_f32(const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpReluF32, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_copy_f32(const float *in, float *out, size_t n, hipStream_t s)
+{
+    if (n == 0) return EW_OK;
+    ew_status_t st = validate(kOpCopyF32, out, in, nullptr, n);
+    if (st != EW_OK) return st;
+    if (static_cast<const void *>(in) == static_cast<const void *>(out)) return EW_OK;
+    return run_stream(kOpCopyF32, out, in, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride, hipStream_t s)
+{
+    if (n == 0) return EW_OK;
+    if (stride == 0) return EW_ERR_INVALID_ARG;
+    ew_status_t st = validate(kOpGatherF32, out, in, nullptr, n);
+    if (st != EW_OK) return st;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    const Plan p = make_plan(kOpGatherF32, out, in, nullptr, n, cus);
+    GatherArgs g{};
+    g.in = reinterpret_cast<const uint32_t *>(in);
+    g.out = reinterpret_cast<uint32_t *>(out);
+    g.n = n;
+    g.stride = stride % n;
+    g.head = p.head;
+    g.vectors = p.vectors;
+    g.tail = p.tail;
+    g.tiles = p.tiles;
+    const uint64_t nthr = (uint64_t)p.launch.block;
+    g.step_vec = mulmod_host(g.stride, (4 * nthr) % n, n);
+    const uint64_t tile_elems = (4 * nthr * (uint64_t)p.launch.unroll) % n;
+    g.step_tile = mulmod_host(mulmod_host(g.stride, tile_elems, n), (uint64_t)p.launch.grid % n, n);
+    g.wide = (g.stride != 0 && (n - 1) > UINT64_MAX / g.stride) ? 1 : 0;
+    const hipError_t e = launch_gather(g, p.launch, s);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
+}
+
+const char *ew_status_string(ew_status_t status)
+{
+    switch (status) {
+    case EW_OK: return "EW_OK";
+    case EW_ERR_INVALID_ARG: return "EW_ERR_INVALID_ARG: null pointer, invalid size, stride or op";
+    case EW_ERR_MISALIGNED: return "EW_ERR_MISALIGNED: pointer not aligned to its element size";
+    case EW_ERR_OVERLAP: return "EW_ERR_OVERLAP: output partially overlaps an input";
+    case EW_ERR_NO_DEVICE: return "EW_ERR_NO_DEVICE: no usable HIP device";
+    case EW_ERR_HIP: return "EW_ERR_HIP: HIP runtime error (see ew_last_hip_error)";
+    }
+    return "EW_ERR_UNKNOWN";
+}
+
+int ew_last_hip_error(void) { return g_last_hip_error; }
+
+int ew_abi_version(void) { return kAbiVersion; }
+
+ew_status_t ew_set_launch_config(const char *op, size_t min_n, int block, int blocks_per_cu,
+                                 int unroll)
+{
+    return set_row(op_from_name(op), min_n, block, blocks_per_cu, unroll);
+}
+
+ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *blocks_per_cu,
+                                 int *unroll)
+{
+    const int id = op_from_name(op);
+    if (id < 0 || !block || !blocks_per_cu || !unroll) return EW_ERR_INVALID_ARG;
+    const Row r = get_row(id, n);
+    *block = r.block;
+    *blocks_per_cu = r.blocks_per_cu;
+    *unroll = r.unroll;
+    return EW_OK;
+}
+
+void ew_reset_launch_config(void)
+{
+    Table &t = table();
+    std::lock_guard<std::mutex> g(t.mu);
+    reset_locked(t);
+}
+
+ew_status_t ew_load_launch_table(const char *path)
+{
+    if (!path) return EW_ERR_INVALID_ARG;
+    FILE *f = std::fopen(path, "r");
+    if (!f) return EW_ERR_INVALID_ARG;
+    char line[512];
+    ew_status_t st = EW_OK;
+    while (std::fgets(line, sizeof line, f)) {
+        char *hash = std::strchr(line, '#');
+        if (hash) *hash = '\0';
+        char name[64];
+        unsigned long long min_n = 0;
+        int block = 0, bpc = 0, unroll = 0;
+        char extra[2];
+        const int got = std::sscanf(line, "%63s %llu %d %d %d %1s", name, &min_n, &block, &bpc,
+                                    &unroll, extra);
+        if (got <= 0) continue;  // blank or comment-only line
+        if (got != 5) {
+            st = EW_ERR_INVALID_ARG;
+            break;
+        }
+        st = set_row(op_from_name(name), (size_t)min_n, block, bpc, unroll);
+        if (st != EW_OK) break;
+    }
+    std::fclose(f);
+    return st;
+}
+
+ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const void *in1,
+                         size_t n, int cu_count, ew_plan_t *plan)
+{
+    const int id = op_from_name(op);
+    if (id < 0 || !plan || cu_count <= 0) return EW_ERR_INVALID_ARG;
+    std::memset(plan, 0, sizeof *plan);
+    if (n != 0) {
+        const ew_status_t st = validate(id, out, in0, in1, n);
+        if (st != EW_OK) return st;
+    }
+    const OpInfo &info = kOps[id];
+    plan->n = n;
+    plan->elem_size = info.elem_size;
+    plan->vec_elems = 16 / info.elem_size;
+    plan->in_coaligned[0] = plan->in_coaligned[1] = 1;
+    const Row r = get_row(id, n);
+    plan->block = r.block;
+    plan->blocks_per_cu = r.blocks_per_cu;
+    plan->unroll = r.unroll;
+    if (n == 0) return EW_OK;
+    const Plan p = make_plan(id, out, in0, in1, n, cu_count);
+    plan->head = p.head;
+    plan->vectors = p.vectors;
+    plan->tail = p.tail;
+    plan->tiles = p.tiles;
+    plan->in_coaligned[0] = p.co[0] ? 1 : 0;
+    plan->in_coaligned[1] = p.co[1] ? 1 : 0;
+    plan->grid = p.launch.grid;
+    return EW_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// ew_internal.h -- declarations shared by the host API (ew_api.cpp) and the
+// device kernels (ew_kernels.hip) of libew.  Not installed; not part of the
+// C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ew {
+
+enum OpId : int {
+    kOpAddF32 = 0,
+    kOpAddF16,
+    kOpAddBF16,
+    kOpSaxpyF32,
+    kOpReluF32,
+    kOpCopyF32,
+    kOpGatherF32,
+    kOpCount
+};
+
+// Everything a streaming kernel needs, computed on the host.  Element
+// indices: [0, head) scalar head, then `vectors` 16-byte vectors starting at
+// element `head`, then `tail` scalar elements.
+struct StreamArgs {
+    const void *in0;     // first input (x for saxpy / relu / copy)
+    const void *in1;     // second input (y for saxpy), nullptr if unused
+    void *out;           // output (y for saxpy)
+    uint64_t head;
+    uint64_t vectors;
+    uint64_t tail;
+    uint64_t tiles;      // ceil(vectors / (blockDim * unroll))
+    float alpha;         // saxpy only
+};
+
+// The gather additionally walks its input index (stride * i) mod n
+// incrementally; the steps are reduced mod n on the host.
+struct GatherArgs {
+    const uint32_t *in;
+    uint32_t *out;
+    uint64_t n;
+    uint64_t stride;     // stride mod n
+    uint64_t head;
+    uint64_t vectors;
+    uint64_t tail;
+    uint64_t tiles;
+    uint64_t step_vec;   // stride * 4 * blockDim            (mod n): next unrolled vector
+    uint64_t step_tile;  // stride * 4 * blockDim * unroll * gridDim (mod n): next tile
+    int wide;            // 1 if stride * (n - 1) can exceed 2^64 - 1
+};
+
+struct Launch {
+    int block;
+    int grid;
+    int unroll;
+};
+
+// Launch one streaming kernel.  co0 / co1: whether input 0 / 1 is 16-byte
+// aligned at its body start.  Returns the launch status.
+hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
+                         const Launch &launch, hipStream_t stream);
+
+hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
+                         hipStream_t stream);
+
+}  // namespace ew

@@ -1,0 +1,388 @@
+// ew_kernels.hip -- streaming elementwise kernels for CDNA4 (gfx950).
+//
+// One skeleton serves every operation; only the per-element operator changes
+// ([EwOps] section 二, template code: index, bounds check and operator form a
+// fixed frame around a replaceable middle).  The skeleton:
+//
+//   * a scalar head (elements before the output is 16-byte aligned) and a
+//     scalar tail (fewer than one vector at the end), handled by the first
+//     lanes of block 0;
+//   * a body of 16-byte vectors (4 fp32 or 8 fp16/bf16 lanes), each wave
+//     instruction moving 64 lanes x 16 B = 1 KiB of contiguous memory with
+//     global_load_dwordx4 / global_store_dwordx4 ([HyperAI] "Version 2" and
+//     "Version 6": one 128-bit access per lane instead of four 32-bit ones);
+//   * tiles of blockDim * U vectors, walked with a grid stride by a grid of a
+//     few blocks per compute unit ([EwOps] optimisation point 2), with all U
+//     loads of a tile issued before the first store so that enough bytes are
+//     in flight to cover HBM latency ([EwOps] point 2 on overlapping
+//     requests; [PerfNotes] section 2.2, hide latency rather than reduce it);
+//   * non-temporal stores: nothing written is read again by this kernel.
+//
+// No LDS and no matrix cores: every byte is used once and nothing is
+// contracted.  Inputs whose body start is not 16-byte aligned relative to the
+// output are read with element-aligned 16-byte loads (the hardware splits
+// them across cache lines); the output is always aligned.
+//
+// Numerics: IEEE binary32 arithmetic in round-to-nearest-even with
+// subnormals preserved (the code object's float denorm modes are "preserve";
+// this file must not be built with fast-math or FTZ flags).
+
+#include "ew_internal.h"
+
+#include <stdint.h>
+
+#ifndef EW_LOAD_NT
+#define EW_LOAD_NT 0
+#endif
+#ifndef EW_STORE_NT
+#define EW_STORE_NT 1
+#endif
+
+namespace ew {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_a2 __attribute__((ext_vector_type(4), aligned(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// 16-byte accesses
+// ---------------------------------------------------------------------------
+
+// Load the 16 bytes at p.  Co: p is 16-byte aligned.  Otherwise p is only
+// element aligned (4 or 2 bytes) and the load must not assume more.
+template <bool Co, int ElemSize>
+__device__ __forceinline__ u32x4 load16(const char *p)
+{
+    if constexpr (Co) {
+        const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+        if constexpr (EW_LOAD_NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    } else if constexpr (ElemSize >= 4) {
+        const u32x4_a4 *q = reinterpret_cast<const u32x4_a4 *>(p);
+        if constexpr (EW_LOAD_NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    } else {
+        const u32x4_a2 *q = reinterpret_cast<const u32x4_a2 *>(p);
+        if constexpr (EW_LOAD_NT) return __builtin_nontemporal_load(q);
+        else return *q;
+    }
+}
+
+__device__ __forceinline__ void store16(char *p, u32x4 v)
+{
+    u32x4 *q = reinterpret_cast<u32x4 *>(p);
+    if constexpr (EW_STORE_NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
+// ---------------------------------------------------------------------------
+// Per-element operators.  `vec` works on one 16-byte vector, `one` on one
+// element; both see raw bit patterns so that the skeleton is type-agnostic.
+// ---------------------------------------------------------------------------
+
+// c = a + b, binary32.
+struct OpAddF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 2;
+    __device__ static u32x4 vec(u32x4 a, u32x4 b, float)
+    {
+        f32x4 r = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b);
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem a, Elem b, float)
+    {
+        return __builtin_bit_cast(Elem, __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b));
+    }
+};
+
+// c = rne16(widen(a) + widen(b)).  The compiler may lower this to a native
+// binary16 add: the binary32 detour rounds twice, and 24 >= 2*11 + 2 makes
+// that double rounding innocuous, so both give the correctly rounded sum.
+struct OpAddF16 {
+    using Elem = uint16_t;
+    static constexpr int kInputs = 2;
+    __device__ static u32x4 vec(u32x4 a, u32x4 b, float)
+    {
+        f32x8 s = __builtin_convertvector(__builtin_bit_cast(f16x8, a), f32x8) +
+                  __builtin_convertvector(__builtin_bit_cast(f16x8, b), f32x8);
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(s, f16x8));
+    }
+    __device__ static Elem one(Elem a, Elem b, float)
+    {
+        float s = (float)__builtin_bit_cast(_Float16, a) + (float)__builtin_bit_cast(_Float16, b);
+        return __builtin_bit_cast(Elem, (_Float16)s);
+    }
+};
+
+// c = rnebf(widen(a) + widen(b)); the narrowing is gfx950's hardware
+// round-to-nearest-even binary32 -> bfloat16 conversion.
+struct OpAddBF16 {
+    using Elem = uint16_t;
+    static constexpr int kInputs = 2;
+    __device__ static u32x4 vec(u32x4 a, u32x4 b, float)
+    {
+        f32x8 s = __builtin_convertvector(__builtin_bit_cast(bf16x8, a), f32x8) +
+                  __builtin_convertvector(__builtin_bit_cast(bf16x8, b), f32x8);
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(s, bf16x8));
+    }
+    __device__ static Elem one(Elem a, Elem b, float)
+    {
+        float s = (float)__builtin_bit_cast(__bf16, a) + (float)__builtin_bit_cast(__bf16, b);
+        return __builtin_bit_cast(Elem, (__bf16)s);
+    }
+};
+
+// y = fma(alpha, x, y): an explicit fused multiply-add, one rounding, never
+// left to floating-point contraction.  Input 0 is x, input 1 is y.
+struct OpSaxpyF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 2;
+    __device__ static u32x4 vec(u32x4 x, u32x4 y, float alpha)
+    {
+        f32x4 xf = __builtin_bit_cast(f32x4, x), yf = __builtin_bit_cast(f32x4, y), r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = __builtin_fmaf(alpha, xf[j], yf[j]);
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem x, Elem y, float alpha)
+    {
+        return __builtin_bit_cast(Elem, __builtin_fmaf(alpha, __builtin_bit_cast(float, x),
+                                                       __builtin_bit_cast(float, y)));
+    }
+};
+
+// y = maximum(x, +0): keep x when x > 0 or x is NaN, else +0.  Written as a
+// compare and select rather than the hardware max, whose NaN rule returns the
+// other operand.
+struct OpReluF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 1;
+    __device__ static float relu(float v) { return (v > 0.0f || v != v) ? v : 0.0f; }
+    __device__ static u32x4 vec(u32x4 x, u32x4, float)
+    {
+        f32x4 xf = __builtin_bit_cast(f32x4, x), r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = relu(xf[j]);
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem x, Elem, float)
+    {
+        return __builtin_bit_cast(Elem, relu(__builtin_bit_cast(float, x)));
+    }
+};
+
+// out = in, bits unchanged.
+struct OpCopyF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 1;
+    __device__ static u32x4 vec(u32x4 x, u32x4, float) { return x; }
+    __device__ static Elem one(Elem x, Elem, float) { return x; }
+};
+
+// ---------------------------------------------------------------------------
+// The streaming skeleton
+// ---------------------------------------------------------------------------
+
+template <class Op, int U, bool Co0, bool Co1>
+__global__ void __launch_bounds__(1024) ew_stream_kernel(StreamArgs args)
+{
+    using E = typename Op::Elem;
+    constexpr uint64_t kElem = sizeof(E);
+    constexpr uint64_t kVec = 16 / kElem;
+    constexpr bool kTwo = Op::kInputs == 2;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nthr = blockDim.x;
+
+    // Scalar head and tail: at most 2 * (kVec - 1) elements, one per lane.
+    if (blockIdx.x == 0 && tid < args.head + args.tail) {
+        const uint64_t e = tid < args.head
+                               ? (uint64_t)tid
+                               : args.head + args.vectors * kVec + (tid - args.head);
+        const E a = static_cast<const E *>(args.in0)[e];
+        const E b = kTwo ? static_cast<const E *>(args.in1)[e] : E(0);
+        static_cast<E *>(args.out)[e] = Op::one(a, b, args.alpha);
+    }
+
+    const char *in0 = static_cast<const char *>(args.in0) + args.head * kElem;
+    const char *in1 = kTwo ? static_cast<const char *>(args.in1) + args.head * kElem : nullptr;
+    char *out = static_cast<char *>(args.out) + args.head * kElem;
+    const uint64_t tile_vecs = nthr * U;
+    const float alpha = args.alpha;
+
+    for (uint64_t t = blockIdx.x; t < args.tiles; t += gridDim.x) {
+        const uint64_t v0 = t * tile_vecs + tid;
+        if (v0 + (U - 1) * nthr < args.vectors) {
+            // Whole tile for this lane: issue every load, then every store.
+            u32x4 x[U], y[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = load16<Co0, kElem>(in0 + (v0 + u * nthr) * 16);
+            if constexpr (kTwo) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) y[u] = load16<Co1, kElem>(in1 + (v0 + u * nthr) * 16);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const u32x4 b = kTwo ? y[u] : u32x4{0, 0, 0, 0};
+                store16(out + (v0 + u * nthr) * 16, Op::vec(x[u], b, alpha));
+            }
+        } else {
+            // Last, partial tile.
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint64_t v = v0 + u * nthr;
+                if (v < args.vectors) {
+                    const u32x4 a = load16<Co0, kElem>(in0 + v * 16);
+                    const u32x4 b = kTwo ? load16<Co1, kElem>(in1 + v * 16) : u32x4{0, 0, 0, 0};
+                    store16(out + v * 16, Op::vec(a, b, alpha));
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Strided gather: out[i] = in[(s * i) mod n]
+// ---------------------------------------------------------------------------
+
+// (a + b) mod n for a, b < n < 2^62.
+__device__ __forceinline__ uint64_t add_mod(uint64_t a, uint64_t b, uint64_t n)
+{
+    const uint64_t r = a + b;
+    return r >= n ? r - n : r;
+}
+
+// (a * b) mod n for a, b < n.  Narrow: the product fits in 64 bits.  Wide:
+// double-and-add, exact for any n < 2^62 (used once per lane).
+__device__ __forceinline__ uint64_t mul_mod(uint64_t a, uint64_t b, uint64_t n, int wide)
+{
+    if (!wide) return (a * b) % n;
+    uint64_t r = 0;
+    while (b) {
+        if (b & 1u) r = add_mod(r, a, n);
+        a = add_mod(a, a, n);
+        b >>= 1;
+    }
+    return r;
+}
+
+template <int U>
+__global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nthr = blockDim.x;
+
+    if (blockIdx.x == 0 && tid < g.head + g.tail) {
+        const uint64_t e = tid < g.head ? (uint64_t)tid : g.head + g.vectors * 4 + (tid - g.head);
+        g.out[e] = g.in[mul_mod(g.stride, e, g.n, g.wide)];
+    }
+
+    uint64_t t = blockIdx.x;
+    if (t >= g.tiles) return;
+    char *out = reinterpret_cast<char *>(g.out + g.head);
+    const uint64_t tile_vecs = nthr * U;
+    // Input index of this lane's first element in its first tile.
+    uint64_t jt = mul_mod(g.stride, g.head + 4 * (t * tile_vecs + tid), g.n, g.wide);
+
+    for (; t < g.tiles; t += gridDim.x) {
+        const uint64_t v0 = t * tile_vecs + tid;
+        uint32_t r[U][4];
+        uint64_t j = jt;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool live = v0 + u * nthr < g.vectors;
+            uint64_t jj = j;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[u][k] = live ? g.in[jj] : 0u;
+                jj = add_mod(jj, g.stride, g.n);
+            }
+            j = add_mod(j, g.step_vec, g.n);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t v = v0 + u * nthr;
+            if (v < g.vectors) store16(out + v * 16, u32x4{r[u][0], r[u][1], r[u][2], r[u][3]});
+        }
+        jt = add_mod(jt, g.step_tile, g.n);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+
+namespace {
+
+template <class Op, int U, bool Co0, bool Co1>
+hipError_t launch_typed(const StreamArgs &args, const Launch &l, hipStream_t s)
+{
+    StreamArgs a = args;
+    void *kargs[] = {&a};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&ew_stream_kernel<Op, U, Co0, Co1>),
+                           dim3(l.grid), dim3(l.block), kargs, 0, s);
+}
+
+template <class Op, int U>
+hipError_t launch_aligned(const StreamArgs &args, bool co0, bool co1, const Launch &l,
+                          hipStream_t s)
+{
+    if constexpr (Op::kInputs == 2) {
+        if (co0 && co1) return launch_typed<Op, U, true, true>(args, l, s);
+        if (co0) return launch_typed<Op, U, true, false>(args, l, s);
+        if (co1) return launch_typed<Op, U, false, true>(args, l, s);
+        return launch_typed<Op, U, false, false>(args, l, s);
+    } else {
+        (void)co1;
+        if (co0) return launch_typed<Op, U, true, true>(args, l, s);
+        return launch_typed<Op, U, false, true>(args, l, s);
+    }
+}
+
+template <class Op>
+hipError_t launch_op(const StreamArgs &args, bool co0, bool co1, const Launch &l, hipStream_t s)
+{
+    switch (l.unroll) {
+    case 1: return launch_aligned<Op, 1>(args, co0, co1, l, s);
+    case 2: return launch_aligned<Op, 2>(args, co0, co1, l, s);
+    case 4: return launch_aligned<Op, 4>(args, co0, co1, l, s);
+    case 8: return launch_aligned<Op, 8>(args, co0, co1, l, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
+                         const Launch &launch, hipStream_t stream)
+{
+    switch (op) {
+    case kOpAddF32: return launch_op<OpAddF32>(args, co0, co1, launch, stream);
+    case kOpAddF16: return launch_op<OpAddF16>(args, co0, co1, launch, stream);
+    case kOpAddBF16: return launch_op<OpAddBF16>(args, co0, co1, launch, stream);
+    case kOpSaxpyF32: return launch_op<OpSaxpyF32>(args, co0, co1, launch, stream);
+    case kOpReluF32: return launch_op<OpReluF32>(args, co0, co1, launch, stream);
+    case kOpCopyF32: return launch_op<OpCopyF32>(args, co0, co1, launch, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
+{
+    GatherArgs a = args;
+    void *kargs[] = {&a};
+    const void *fn = nullptr;
+    switch (l.unroll) {
+    case 1: fn = reinterpret_cast<const void *>(&ew_gather_kernel<1>); break;
+    case 2: fn = reinterpret_cast<const void *>(&ew_gather_kernel<2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&ew_gather_kernel<4>); break;
+    case 8: fn = reinterpret_cast<const void *>(&ew_gather_kernel<8>); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
+}
+
+}  // namespace ew

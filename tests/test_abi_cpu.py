@@ -1,0 +1,189 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call.
+
+No test here launches a kernel.  Every call with made-up addresses fails
+validation first; the one test that passes validation runs only when no GPU
+is visible (it then gets EW_ERR_NO_DEVICE).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_bound_elementwise_amd as ew
+from tests.conftest import ROOT, _gpu_visible
+
+HEADER = os.path.join(ROOT, "include", "ew.h")
+
+EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP, EW_ERR_NO_DEVICE, EW_ERR_HIP = (
+    0, -1, -2, -3, -4, -5)
+
+BASE = 0x7F0000000000          # a made-up, 256-byte aligned device address
+MiB = 1 << 20
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ew_[a-z0-9_]+)\s*\(", text)))
+
+
+def _raw():
+    return ctypes.CDLL(ew.library_path())
+
+
+def test_header_declares_the_operations():
+    names = _declared_functions()
+    for op in ("ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
+               "ew_copy_f32", "ew_gather_f32"):
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _raw()
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_names_match_the_c_abi():
+    for name in _declared_functions():
+        assert hasattr(ew, name), name
+
+
+def test_abi_version_and_status_strings():
+    assert ew.ew_abi_version() == 1
+    for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
+                 EW_ERR_NO_DEVICE, EW_ERR_HIP):
+        s = ew.ew_status_string(code)
+        assert s.startswith("EW_")
+    assert ew.ew_status_string(12345) == "EW_ERR_UNKNOWN"
+    assert ew.ew_last_hip_error() == 0
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except ew.EwError as e:
+        return e.status
+    return EW_OK
+
+
+def test_n_zero_is_a_no_op_even_with_null_pointers():
+    assert _status(ew.ew_add_f32, 0, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_add_f16, 0, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_add_bf16, 0, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_saxpy_f32, 2.5, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_relu_f32, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_copy_f32, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_gather_f32, 0, 0, 2, 0, 0) == EW_OK
+
+
+def test_null_pointers_are_invalid():
+    n = 16
+    assert _status(ew.ew_add_f32, 0, BASE, BASE + MiB, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_add_f32, BASE, 0, BASE + MiB, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_add_f32, BASE, BASE + MiB, 0, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_saxpy_f32, 1.0, 0, BASE, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_relu_f32, BASE, 0, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_copy_f32, 0, BASE, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_gather_f32, 0, BASE, 2, n, 0) == EW_ERR_INVALID_ARG
+
+
+def test_zero_stride_and_size_overflow_are_invalid():
+    assert _status(ew.ew_gather_f32, BASE, BASE + MiB, 0, 16, 0) == EW_ERR_INVALID_ARG
+    # n * 4 overflows size_t
+    assert _status(ew.ew_add_f32, BASE, BASE + MiB, BASE + 2 * MiB, (1 << 63), 0) == \
+        EW_ERR_INVALID_ARG
+    # n at or above 2^62 elements
+    assert _status(ew.ew_add_f16, BASE, BASE + MiB, BASE + 2 * MiB, (1 << 62), 0) == \
+        EW_ERR_INVALID_ARG
+    # the range would wrap around the address space
+    top = (1 << 64) - 64
+    assert _status(ew.ew_relu_f32, top, BASE, 1024, 0) == EW_ERR_INVALID_ARG
+
+
+def test_element_misalignment_is_rejected():
+    n = 16
+    assert _status(ew.ew_add_f32, BASE + 2, BASE + MiB, BASE + 2 * MiB, n, 0) == \
+        EW_ERR_MISALIGNED
+    assert _status(ew.ew_add_f32, BASE, BASE + MiB, BASE + 2 * MiB + 1, n, 0) == \
+        EW_ERR_MISALIGNED
+    assert _status(ew.ew_add_f16, BASE + 1, BASE + MiB, BASE + 2 * MiB, n, 0) == \
+        EW_ERR_MISALIGNED
+    assert _status(ew.ew_add_bf16, BASE, BASE + MiB + 3, BASE + 2 * MiB, n, 0) == \
+        EW_ERR_MISALIGNED
+    assert _status(ew.ew_saxpy_f32, 2.5, BASE + 6, BASE + MiB, n, 0) == EW_ERR_MISALIGNED
+    assert _status(ew.ew_gather_f32, BASE + 2, BASE + MiB, 2, n, 0) == EW_ERR_MISALIGNED
+
+
+def test_partial_overlap_is_rejected():
+    n = 1024
+    # output starts one element into input a
+    assert _status(ew.ew_add_f32, BASE, BASE + MiB, BASE + 4, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_add_f32, BASE + 4, BASE + MiB, BASE, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_add_f16, BASE + MiB, BASE, BASE + 2, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_saxpy_f32, 2.5, BASE, BASE + 8, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_relu_f32, BASE, BASE + 4 * n - 4, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_copy_f32, BASE + 4, BASE, n, 0) == EW_ERR_OVERLAP
+    # the gather forbids any overlap, exact aliasing included
+    assert _status(ew.ew_gather_f32, BASE, BASE, 2, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_gather_f32, BASE, BASE + 4 * n - 4, 2, n, 0) == EW_ERR_OVERLAP
+
+
+def test_adjacent_ranges_do_not_overlap_and_copy_onto_itself_is_a_no_op():
+    n = 1024
+    # [BASE, BASE+4n) and [BASE+4n, ...) touch but do not overlap: validation
+    # passes, so check through the planner (which launches nothing).
+    p = ew.ew_make_plan("copy_f32", BASE + 4 * n, BASE, 0, n, 256)
+    assert p.vectors == n // 4
+    # copy with out == in returns EW_OK without a launch or a device
+    assert _status(ew.ew_copy_f32, BASE, BASE, n, 0) == EW_OK
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no GPU is visible")
+def test_valid_call_without_a_device_reports_no_device():
+    assert _status(ew.ew_add_f32, BASE, BASE + MiB, BASE + 2 * MiB, 1000, 0) == EW_ERR_NO_DEVICE
+    assert _status(ew.ew_gather_f32, BASE, BASE + MiB, 2, 1000, 0) == EW_ERR_NO_DEVICE
+    # exact aliasing is allowed for add, so it also gets as far as the device check
+    assert _status(ew.ew_add_f32, BASE, BASE + MiB, BASE, 1000, 0) == EW_ERR_NO_DEVICE
+    assert _status(ew.ew_saxpy_f32, 2.5, BASE, BASE, 1000, 0) == EW_ERR_NO_DEVICE
+
+
+def test_launch_config_table_set_get_reset_and_load(tmp_path):
+    try:
+        ew.ew_reset_launch_config()
+        default = ew.ew_get_launch_config("add_f32", 1 << 28)
+        ew.ew_set_launch_config("add_f32", 1 << 26, 512, 4, 4)
+        assert ew.ew_get_launch_config("add_f32", 1 << 28) == (512, 4, 4)
+        assert ew.ew_get_launch_config("add_f32", (1 << 26) - 1) != (512, 4, 4)
+        # replacing a row
+        ew.ew_set_launch_config("add_f32", 1 << 26, 1024, 2, 8)
+        assert ew.ew_get_launch_config("add_f32", 1 << 26) == (1024, 2, 8)
+        # invalid values
+        for bad in ((100, 8, 1), (0, 8, 1), (2048, 8, 1), (256, 0, 1), (256, 8, 3)):
+            with pytest.raises(ew.EwError):
+                ew.ew_set_launch_config("add_f32", 0, *bad)
+        with pytest.raises(ew.EwError):
+            ew.ew_set_launch_config("no_such_op", 0, 256, 8, 1)
+        with pytest.raises(ew.EwError):
+            ew.ew_get_launch_config("no_such_op", 0)
+        ew.ew_reset_launch_config()
+        assert ew.ew_get_launch_config("add_f32", 1 << 28) == default
+        # table file
+        f = tmp_path / "table.txt"
+        f.write_text("# op min_n block bpc unroll\n\nrelu_f32 0 128 16 1  # small\n"
+                     "relu_f32 1048576 512 2 4\n")
+        ew.ew_load_launch_table(str(f))
+        assert ew.ew_get_launch_config("relu_f32", 10) == (128, 16, 1)
+        assert ew.ew_get_launch_config("relu_f32", 1 << 21) == (512, 2, 4)
+        bad = tmp_path / "bad.txt"
+        bad.write_text("relu_f32 0 128\n")
+        with pytest.raises(ew.EwError):
+            ew.ew_load_launch_table(str(bad))
+        with pytest.raises(ew.EwError):
+            ew.ew_load_launch_table(str(tmp_path / "missing.txt"))
+    finally:
+        ew.ew_reset_launch_config()
+        if os.path.exists(ew.LAUNCH_TABLE):
+            ew.ew_load_launch_table(ew.LAUNCH_TABLE)

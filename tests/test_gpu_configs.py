@@ -1,0 +1,86 @@
+"""The five workload configurations at full size, HIP path vs the oracle on
+every element, in the default launch configuration (the one the bench
+times).  Bit-exact for add / ReLU / copy / gather; SAXPY is held to the
+stated tolerance of 1 ulp and is expected to be exact (fused multiply-add on
+both sides).
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_elementwise_amd as ew
+import oracle
+import synth
+from tests.gpu_util import ELEM, download, mismatches, ulp_f32, upload
+
+pytestmark = pytest.mark.gpu
+
+SAXPY_MAX_ULP = 1
+
+
+def _run(w: synth.Workload):
+    print(f"[configs] {w.name} n={w.n}", flush=True)
+    inp = synth.workload_inputs(w)
+    es = ELEM[w.op]
+    offs = w.offsets
+    s = torch.cuda.current_stream().cuda_stream
+    if w.op in ("add_f32", "add_f16", "add_bf16"):
+        a, _ka = upload(inp["a"], offs.get("a", 0))
+        b, _kb = upload(inp["b"], offs.get("b", 0))
+        c, _kc = upload(np.zeros(w.n, inp["a"].dtype), offs.get("c", 0))
+        getattr(ew, "ew_" + w.op)(a, b, c, stream=s)
+        torch.cuda.synchronize()
+        got = download(c, es)
+        del a, b, c, _ka, _kb, _kc
+        ref = getattr(oracle, w.op)(inp["a"], inp["b"])
+    elif w.op == "saxpy_f32":
+        x, _kx = upload(inp["x"], offs.get("x", 0))
+        y, _ky = upload(inp["y"], offs.get("y", 0))
+        ew.ew_saxpy_f32(w.alpha, x, y, stream=s)
+        torch.cuda.synchronize()
+        got = download(y, es)
+        ref = oracle.saxpy_f32(w.alpha, inp["x"], inp["y"])
+    else:
+        x, _kx = upload(inp["x"], offs.get("x", 0))
+        y, _ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
+        if w.op == "relu_f32":
+            ew.ew_relu_f32(x, y, stream=s)
+        elif w.op == "copy_f32":
+            ew.ew_copy_f32(x, y, stream=s)
+        else:
+            ew.ew_gather_f32(x, y, w.stride, stream=s)
+        torch.cuda.synchronize()
+        got = download(y, es)
+        ref = getattr(oracle, w.op)(inp["x"], w.stride) if w.op == "gather_f32" else \
+            getattr(oracle, w.op)(inp["x"])
+    torch.cuda.empty_cache()
+    return got, ref
+
+
+@pytest.mark.parametrize("name", [k for k in synth.WORKLOADS if k != "cfg3_saxpy_f32_32M"])
+def test_config_bit_exact(name):
+    w = synth.WORKLOADS[name]
+    got, ref = _run(w)
+    bad = mismatches(w.op, got, ref)
+    assert bad.size == 0, f"{name}: {bad.size} mismatches, first at {bad[:5]}"
+
+
+def test_config_saxpy_within_one_ulp_and_exact():
+    w = synth.WORKLOADS["cfg3_saxpy_f32_32M"]
+    got, ref = _run(w)
+    ulps = ulp_f32(got, ref)
+    assert int(ulps.max()) <= SAXPY_MAX_ULP
+    # fused multiply-add on both sides: no element may differ at all
+    assert np.count_nonzero(ulps) == 0
+
+
+def test_config_relu_zero_fraction_is_about_half():
+    """Sanity on the normal(0,1) ReLU input: about half the outputs are +0."""
+    w = synth.WORKLOADS["cfg4c_relu_f32_2e28"]
+    inp = synth.make_inputs("relu_f32", 1 << 22, w.seed, w.dist)
+    x, _kx = upload(inp["x"], 0)
+    y = torch.empty_like(x)
+    ew.ew_relu_f32(x, y)
+    torch.cuda.synchronize()
+    frac = float((y == 0).float().mean())
+    assert 0.49 < frac < 0.51

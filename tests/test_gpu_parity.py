@@ -1,0 +1,295 @@
+"""HIP path against the CPU oracle through the C ABI, element by element.
+
+* brute force: every n in 0..17 plus ragged sizes, every pointer offset class,
+  every op; inputs mix special values (NaN, +-inf, +-0, subnormals, extremes)
+  with random bit patterns and the config distributions; every output region
+  sits in one arena whose untouched bytes must keep their sentinel (guard
+  bands catch any out-of-bounds head / tail / body write);
+* every kernel instantiation: each op under block sizes 64..1024, unroll
+  1..8 and co-aligned / misaligned inputs, at a size spanning several tiles
+  with a ragged tail;
+* exact aliasing where the ABI allows it.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_elementwise_amd as ew
+import oracle
+import synth
+from tests.gpu_util import DEV, ELEM, NP_DTYPE, download, mismatches, upload
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64
+SENTINEL = 0xA5
+SIZES = list(range(0, 18)) + [31, 32, 33, 63, 64, 65, 127, 129, 1000, 4099]
+
+SPECIAL_F32 = np.array(
+    [0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, -np.nan, 1e-45, -1e-45, 1e-40, -3e-39,
+     1.1754944e-38, -1.1754942e-38, 3.4028235e38, -3.4028235e38, 0.5, 2.5, -2.5, 65504.0,
+     1e30, -1e-30, 16777217.0, 0.1],
+    dtype=np.float32)
+
+
+def _f32_pool(length, seed):
+    g = synth.rng(seed)
+    parts = [SPECIAL_F32,
+             synth.uniform_pm1(g, length // 3),
+             synth.normal01(g, length // 3),
+             g.integers(0, 1 << 32, size=length, dtype=np.uint64).astype(np.uint32)
+             .view(np.float32)]
+    pool = np.concatenate(parts)[:length]
+    g.shuffle(pool)
+    return np.ascontiguousarray(pool, dtype=np.float32)
+
+
+def _u16_pool(length, seed):
+    g = synth.rng(seed)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x03FF, 0x0400, 0x3C00, 0x7BFF,
+                        0x7C00, 0xFC00, 0x7E00, 0x7C01, 0x7F80, 0xFF80, 0x7FC0, 0x7F81,
+                        0x0080, 0x007F, 0x3F80, 0xBF80], dtype=np.uint16)
+    rnd = g.integers(0, 1 << 16, size=length, dtype=np.uint32).astype(np.uint16)
+    pool = np.concatenate([special, rnd])[:length]
+    g.shuffle(pool)
+    return pool
+
+
+def _pool(op, length, seed):
+    return _u16_pool(length, seed) if ELEM[op] == 2 else _f32_pool(length, seed)
+
+
+def _oracle(op, ins, n, alpha=2.5, stride=2):
+    if op in ("add_f32", "add_f16", "add_bf16"):
+        return getattr(oracle, op)(ins[0], ins[1])
+    if op == "saxpy_f32":
+        return oracle.saxpy_f32(alpha, ins[0], ins[1])
+    if op == "relu_f32":
+        return oracle.relu_f32(ins[0])
+    if op == "copy_f32":
+        return oracle.copy_f32(ins[0])
+    return oracle.gather_f32(ins[0], stride)
+
+
+def _call(op, out_ptr, in_ptrs, n, alpha=2.5, stride=2):
+    s = torch.cuda.current_stream().cuda_stream
+    if op in ("add_f32", "add_f16", "add_bf16"):
+        getattr(ew, "ew_" + op)(in_ptrs[0], in_ptrs[1], out_ptr, n=n, stream=s)
+    elif op == "saxpy_f32":
+        ew.ew_saxpy_f32(alpha, in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op == "relu_f32":
+        ew.ew_relu_f32(in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op == "copy_f32":
+        ew.ew_copy_f32(in_ptrs[0], out_ptr, n=n, stream=s)
+    else:
+        ew.ew_gather_f32(in_ptrs[0], out_ptr, stride, n=n, stream=s)
+
+
+def _run_cases(op, cases, seed):
+    """cases: list of (n, off_out, [off_in...], stride).  All outputs live in
+    one sentinel-filled arena; returns a list of failure descriptions."""
+    es = ELEM[op]
+    dt = NP_DTYPE[es]
+    n_in = 1 if op in ("relu_f32", "copy_f32", "gather_f32") else 2
+    max_n = max(c[0] for c in cases)
+    pool_len = max_n + 32
+    pools = [_pool(op, pool_len, seed + k) for k in range(n_in)]
+    dev_pools = [upload(p)[1] for p in pools]          # base tensors, offset 0
+    for d in dev_pools:
+        assert d.data_ptr() % 256 == 0
+
+    layout, cursor = [], 0
+    for (n, off_out, offs_in, stride) in cases:
+        start = -(-(cursor + GUARD) // 256) * 256
+        out_byte = start + off_out * es
+        layout.append(out_byte)
+        cursor = out_byte + n * es + GUARD
+    total = -(-(cursor + 256) // 256) * 256
+    host = np.full(total, SENTINEL, np.uint8)
+    if op == "saxpy_f32":   # y is updated in place: seed each output span with y
+        for (n, off_out, offs_in, stride), ob in zip(cases, layout):
+            host[ob:ob + n * es] = pools[1][offs_in[1]:offs_in[1] + n].view(np.uint8)
+    arena = torch.from_numpy(host).to(DEV)
+    base = arena.data_ptr()
+    assert base % 256 == 0
+
+    for (n, off_out, offs_in, stride), ob in zip(cases, layout):
+        assert ob + n * es <= total
+        in_ptrs = []
+        for k in range(n_in):
+            assert offs_in[k] + n <= pool_len
+            in_ptrs.append(dev_pools[k].data_ptr() + offs_in[k] * es)
+        _call(op, base + ob, in_ptrs, n, stride=stride)
+    torch.cuda.synchronize()
+    res = arena.cpu().numpy()
+
+    failures = []
+    written = np.zeros(total, bool)
+    for (n, off_out, offs_in, stride), ob in zip(cases, layout):
+        written[ob:ob + n * es] = True
+        got = res[ob:ob + n * es].view(dt)
+        ins = [pools[k][offs_in[k]:offs_in[k] + n] for k in range(n_in)]
+        ref = _oracle(op, ins, n, stride=stride)
+        bad = mismatches(op, got, ref)
+        if bad.size:
+            failures.append(f"{op} n={n} off_out={off_out} offs_in={offs_in} stride={stride}: "
+                            f"{bad.size} mismatches, first at {bad[0]}")
+    outside = res[~written]
+    if np.any(outside != SENTINEL):
+        failures.append(f"{op}: {np.count_nonzero(outside != SENTINEL)} bytes written outside "
+                        "the output ranges (guard band)")
+    return failures
+
+
+def _offset_cases(op):
+    es = ELEM[op]
+    vec = 16 // es
+    cases = []
+    for n in SIZES:
+        if op in ("add_f32", "add_f16", "add_bf16", "saxpy_f32"):
+            offs_b = range(vec) if es == 4 else (0, 3, 7)
+            for oo in range(vec):
+                for oa in range(vec):
+                    for ob in offs_b:
+                        if op == "saxpy_f32":
+                            ob = oo          # y is the output itself
+                        cases.append((n, oo, [oa, ob], 0))
+                    if op == "saxpy_f32":
+                        pass
+        else:
+            for oo in range(vec):
+                for oa in range(vec):
+                    cases.append((n, oo, [oa], 2))
+    # saxpy produced duplicates (ob forced to oo); drop them
+    seen, uniq = set(), []
+    for c in cases:
+        key = (c[0], c[1], tuple(c[2]), c[3])
+        if key not in seen:
+            seen.add(key)
+            uniq.append(c)
+    return uniq
+
+
+@pytest.mark.parametrize("op", ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32",
+                                "copy_f32", "gather_f32"])
+def test_brute_force_small_all_offsets(op):
+    print(f"[parity] brute force {op}", flush=True)
+    failures = _run_cases(op, _offset_cases(op), seed=300)
+    assert not failures, failures[:10]
+
+
+def test_gather_brute_force_strides():
+    print("[parity] gather strides", flush=True)
+    cases = []
+    for n in range(1, 18):
+        for stride in sorted({1, 2, 3, max(n - 1, 1), n, n + 1, 2 * n + 5, (1 << 63) + 5,
+                              (1 << 64) - 1}):
+            for oo in range(4):
+                cases.append((n, oo, [(oo + 1) % 4], stride))
+    for n in (1000, 4099, 65537):
+        for stride in (1, 2, 3, 7, n - 1, n + 1, 1 << 40):
+            cases.append((n, 1, [2], stride))
+    failures = _run_cases("gather_f32", cases, seed=310)
+    assert not failures, failures[:10]
+
+
+LAUNCHES = [(64, 1, 1), (64, 3, 8), (256, 8, 1), (256, 8, 2), (256, 2, 4), (512, 4, 4),
+            (1024, 1, 2), (1024, 2, 8), (128, 64, 1)]
+
+
+@pytest.mark.parametrize("op", ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32",
+                                "copy_f32", "gather_f32"])
+def test_every_kernel_variant_several_tiles_ragged(op):
+    """Each (block, unroll) and alignment variant, at a size of a few tiles
+    plus a ragged tail, with a grid smaller than the tile count so the
+    grid-stride loop runs several rounds."""
+    print(f"[parity] kernel variants {op}", flush=True)
+    es = ELEM[op]
+    vec = 16 // es
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        for (block, bpc, unroll) in LAUNCHES:
+            ew.ew_set_launch_config(op, 0, block, bpc, unroll)
+            # 2 * grid + 1 tiles: the grid-stride loop runs three rounds and
+            # the last tile is partial
+            n = (2 * bpc * cus + 1) * block * unroll * vec - 3 * vec + 13
+            plan = ew.ew_make_plan(op, 1 << 40, 1 << 41, (1 << 42) if op in (
+                "add_f32", "add_f16", "add_bf16") else (1 << 40 if op == "saxpy_f32" else 0),
+                n, cus)
+            assert plan.tiles > 2 * plan.grid, (plan.tiles, plan.grid)
+            if op in ("relu_f32", "copy_f32", "gather_f32"):
+                offs = [(1, [1]), (1, [0]), (0, [3])]
+            elif op == "saxpy_f32":
+                offs = [(1, [2, 1]), (0, [0, 0]), (3, [1, 3])]
+            else:
+                offs = [(1, [1, 1]), (1, [0, 1]), (1, [1, 2]), (0, [3, 5 % vec])]
+            cases = [(n, oo, oi, 2) for (oo, oi) in offs]
+            failures = _run_cases(op, cases, seed=320 + block + unroll)
+            assert not failures, (block, bpc, unroll, failures[:5])
+    finally:
+        ew.ew_reset_launch_config()
+        ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+def test_exact_aliasing_in_place():
+    print("[parity] aliasing", flush=True)
+    n = 100003
+    s = torch.cuda.current_stream().cuda_stream
+    g = synth.rng(330)
+    a = _f32_pool(n, 331)
+    b = synth.uniform_pm1(g, n)
+    # c == a
+    ta, _ka = upload(a, 1)
+    tb, _kb = upload(b, 0)
+    ew.ew_add_f32(ta, tb, ta, stream=s)
+    torch.cuda.synchronize()
+    assert mismatches("add_f32", download(ta, 4), oracle.add_f32(a, b)).size == 0
+    # c == b, 16-bit
+    a16 = _u16_pool(n, 332)
+    b16 = _u16_pool(n, 333)
+    ta, _ka = upload(a16, 3)
+    tb, _kb = upload(b16, 5)
+    ew.ew_add_bf16(ta, tb, tb, stream=s)
+    torch.cuda.synchronize()
+    assert mismatches("add_bf16", download(tb, 2), oracle.add_bf16(a16, b16)).size == 0
+    # relu in place
+    x = _f32_pool(n, 334)
+    tx, _kx = upload(x, 2)
+    ew.ew_relu_f32(tx, tx, stream=s)
+    torch.cuda.synchronize()
+    assert mismatches("relu_f32", download(tx, 4), oracle.relu_f32(x)).size == 0
+    # saxpy with x == y: y = fma(alpha, y, y)
+    y = synth.normal01(g, n)
+    ty, _ky = upload(y, 1)
+    ew.ew_saxpy_f32(2.5, ty, ty, stream=s)
+    torch.cuda.synchronize()
+    assert mismatches("saxpy_f32", download(ty, 4), oracle.saxpy_f32(2.5, y, y)).size == 0
+    # copy onto itself leaves the data unchanged
+    tz, _kz = upload(x, 0)
+    ew.ew_copy_f32(tz, tz, stream=s)
+    torch.cuda.synchronize()
+    assert np.array_equal(download(tz, 4).view(np.uint32), x.view(np.uint32))
+
+
+def test_errors_surface_as_exceptions_on_device():
+    t = torch.zeros(1024, device=DEV)
+    with pytest.raises(ew.EwError) as e:
+        ew.ew_add_f32(t[1:], t, t[:-1])
+    assert e.value.status == -3
+    with pytest.raises(ew.EwError):
+        ew.ew_gather_f32(t, t, 2)
+
+
+def test_non_default_stream_orders_with_the_stream():
+    """Work on a user stream is ordered after earlier work on that stream."""
+    n = 1 << 22
+    s = torch.cuda.Stream()
+    x = torch.arange(n, dtype=torch.float32, device=DEV)
+    y = torch.empty_like(x)
+    z = torch.empty_like(x)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ew.ew_copy_f32(x, y)            # defaults to the current (user) stream
+        ew.ew_relu_f32(y, z)
+    s.synchronize()
+    assert torch.equal(z, x)

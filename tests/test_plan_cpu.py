@@ -1,0 +1,129 @@
+"""Host-side planning: the head / body / tail split and the launch shape.
+
+``ew_make_plan`` is pure arithmetic on pointer values, so these tests need no
+GPU.  They pin the split against the pages' worked examples
+(``tests/golden/worked_examples.json``) and against brute force.
+"""
+import json
+import os
+
+import pytest
+
+import memory_bound_elementwise_amd as ew
+from tests.conftest import ROOT
+
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "worked_examples.json")))
+BASE = 0x7F0000000000
+MiB = 1 << 20
+CUS = 256
+
+ELEM = {"add_f32": 4, "add_f16": 2, "add_bf16": 2, "saxpy_f32": 4, "relu_f32": 4,
+        "copy_f32": 4, "gather_f32": 4}
+TWO_INPUTS = {"add_f32", "add_f16", "add_bf16", "saxpy_f32"}
+
+
+@pytest.fixture(autouse=True)
+def _fresh_table():
+    ew.ew_reset_launch_config()
+    yield
+    ew.ew_reset_launch_config()
+    if os.path.exists(ew.LAUNCH_TABLE):
+        ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+def _plan(op, out, in0, in1, n, cus=CUS):
+    if op == "saxpy_f32":
+        in1 = out
+    return ew.ew_make_plan(op, out, in0, in1 if op in TWO_INPUTS else 0, n, cus)
+
+
+def test_worked_example_vector_body_plus_scalar_tail():
+    """N = 10 with 4-wide vectors from an aligned base: 8 elements in the
+    vector body, 2 in the scalar tail."""
+    ex = GOLDEN["split_examples"][0]
+    p = _plan("add_f32", BASE + 2 * MiB, BASE, BASE + MiB, ex["n"])
+    assert p.vec_elems == ex["vec_elems"]
+    assert p.head == 0
+    assert p.vectors * p.vec_elems == ex["body_elems"]
+    assert p.tail == ex["tail"]
+
+
+def test_worked_example_ceil_division_of_blocks():
+    """N = 1000 work items at 256 per block need 4 blocks (1024 lanes), 24 of
+    them masked.  Here a work item is one 16-byte vector (4000 fp32 values),
+    and a tile is block * unroll vectors."""
+    ex = GOLDEN["split_examples"][1]
+    ew.ew_set_launch_config("relu_f32", 0, ex["threads_per_block"], 64, 1)
+    p = _plan("relu_f32", BASE + MiB, BASE, 0, 4 * ex["n"])
+    assert p.vectors == ex["n"]
+    assert p.tiles == ex["blocks"]
+    assert p.tiles * p.block == ex["threads"]
+    assert p.tiles * p.block - p.vectors == ex["masked"]
+    assert p.grid == ex["blocks"]          # fewer tiles than blocks_per_cu * CUs
+
+
+@pytest.mark.parametrize("op", sorted(ELEM))
+def test_split_brute_force(op):
+    es = ELEM[op]
+    vec = 16 // es
+    for n in range(0, 41):
+        for ko in range(vec):
+            for k0 in range(vec):
+                out = BASE + 4 * MiB + ko * es
+                in0 = BASE + k0 * es
+                in1 = BASE + MiB + ((ko + 1) % vec) * es
+                p = _plan(op, out, in0, in1, n)
+                assert p.head + p.vectors * p.vec_elems + p.tail == n
+                assert p.vec_elems == vec and p.elem_size == es
+                if n == 0:
+                    assert (p.head, p.vectors, p.tail, p.grid) == (0, 0, 0, 0)
+                    continue
+                assert p.head == min(((16 - out % 16) % 16) // es, n)
+                assert p.tail < vec
+                if p.vectors:
+                    assert (out + p.head * es) % 16 == 0
+                expect_co0 = 1 if op == "gather_f32" else int((in0 + p.head * es) % 16 == 0)
+                assert p.in_coaligned[0] == expect_co0
+                if op in ("add_f32", "add_f16", "add_bf16"):
+                    assert p.in_coaligned[1] == int((in1 + p.head * es) % 16 == 0)
+                assert p.grid >= 1
+                assert p.tiles == -(-p.vectors // (p.block * p.unroll))
+
+
+def test_misaligned_a_config_split():
+    """fp32 add, n = 2^28 + 3, A one element past an aligned allocation, B and
+    C aligned: no head, 2^26 vectors, a 3-element tail, A relatively
+    misaligned."""
+    n = (1 << 28) + 3
+    a, b, c = BASE + 4, BASE + (2 << 30), BASE + (4 << 30)
+    p = ew.ew_make_plan("add_f32", c, a, b, n, CUS)
+    assert (p.head, p.vectors, p.tail) == (0, 1 << 26, 3)
+    assert tuple(p.in_coaligned) == (0, 1)
+
+
+@pytest.mark.parametrize("n,vectors", [((1 << 20), 1 << 18), ((1 << 28), 1 << 26)])
+def test_grid_is_capped_by_cus_and_tiles(n, vectors):
+    p = _plan("add_f32", BASE + (8 << 30), BASE, BASE + (4 << 30), n)
+    assert p.vectors == vectors
+    tiles = -(-vectors // (p.block * p.unroll))
+    assert p.tiles == tiles
+    assert p.grid == min(p.blocks_per_cu * CUS, tiles)
+
+
+def test_sixteen_bit_ops_use_eight_lanes_per_vector():
+    n = (1 << 28)
+    p = _plan("add_f16", BASE + (8 << 30), BASE, BASE + (4 << 30), n)
+    assert (p.vec_elems, p.vectors, p.tail) == (8, 1 << 25, 0)
+    p = _plan("add_bf16", BASE + (8 << 30) + 6, BASE + 6, BASE + (4 << 30), n)
+    assert p.head == 5 and tuple(p.in_coaligned) == (1, 0)
+
+
+def test_plan_rejects_what_the_operation_rejects():
+    with pytest.raises(ew.EwError):
+        ew.ew_make_plan("add_f32", BASE + 4, BASE, BASE + MiB, 1024, CUS)   # overlap
+    with pytest.raises(ew.EwError):
+        ew.ew_make_plan("add_f32", BASE + 2, BASE, BASE + MiB, 16, CUS)     # misaligned
+    with pytest.raises(ew.EwError):
+        ew.ew_make_plan("nope", BASE, BASE, BASE, 16, CUS)
+    with pytest.raises(ew.EwError):
+        ew.ew_make_plan("add_f32", BASE + 2 * MiB, BASE, BASE + MiB, 16, 0)  # no CUs
