@@ -34,6 +34,14 @@ if not os.path.exists(_LIB_PATH):
         f"{_LIB_PATH} is not built; run `python memory_bound_elementwise_amd/build.py` "
         "or __graft_entry__.build() first")
 
+# torch ships its own HIP runtime under the same soname as ROCm's.  Load it
+# first so that libew binds to that one runtime: streams and device pointers
+# handed over by torch are only meaningful inside the runtime that made them.
+try:
+    import torch  # noqa: F401
+except ImportError:     # plain C-ABI use without torch: raw pointers only
+    torch = None
+
 _lib = ctypes.CDLL(_LIB_PATH)
 
 _vp, _sz, _int = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
@@ -120,7 +128,6 @@ def _stream(x, stream):
     if stream is None:
         if isinstance(x, int):
             return None
-        import torch
         return torch.cuda.current_stream(x.device).cuda_stream
     if isinstance(stream, int):
         return stream

@@ -17,7 +17,9 @@ def upload(arr: np.ndarray, off: int = 0, pad: int = 16):
     host = arr.view(np.int16) if es == 2 else arr
     base = torch.empty(arr.size + off + pad, dtype=TORCH_DTYPE[es], device=DEV)
     view = base[off:off + arr.size]
-    view.copy_(torch.from_numpy(np.ascontiguousarray(host)))
+    if not (host.flags.writeable and host.flags.c_contiguous):
+        host = np.array(host, copy=True, order="C")
+    view.copy_(torch.from_numpy(host))
     return view, base
 
 
