@@ -31,7 +31,6 @@ import argparse
 import hashlib
 import json
 import os
-import platform
 import sys
 import time
 
@@ -344,7 +343,7 @@ def main(argv=None):
                    "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                    "numpy": np.__version__, "kernel_source_sha256_16": kernel_source_hash()}
     print(json.dumps(line), flush=True)
-    return 0 if res["parity"] == "PASS" else 1
+    return 1 if res["parity"] == "FAIL" else 0
 
 
 if __name__ == "__main__":

@@ -56,20 +56,28 @@ struct Row {
     int unroll;
 };
 
-// Compiled-in defaults, measured on MI355X (256 CUs, 8 TB/s HBM3E) with the
-// tuner in this package; a row covers n >= min_n up to the next row.
+// Compiled-in defaults: the table written by tune.py on MI355X (256 CUs,
+// 8 TB/s HBM3E); a row covers n >= min_n up to the next row.  blocks_per_cu
+// 1024 means one block per tile at every size used in practice.
 struct DefaultRow {
     int op;
     Row row;
 };
 constexpr DefaultRow kDefaults[] = {
-    {kOpAddF32, {0, 256, 8, 1}},    {kOpAddF32, {size_t(1) << 22, 256, 8, 2}},
-    {kOpAddF16, {0, 256, 8, 1}},    {kOpAddF16, {size_t(1) << 22, 256, 8, 2}},
-    {kOpAddBF16, {0, 256, 8, 1}},   {kOpAddBF16, {size_t(1) << 22, 256, 8, 2}},
-    {kOpSaxpyF32, {0, 256, 8, 1}},  {kOpSaxpyF32, {size_t(1) << 22, 256, 8, 2}},
-    {kOpReluF32, {0, 256, 8, 1}},   {kOpReluF32, {size_t(1) << 22, 256, 8, 2}},
-    {kOpCopyF32, {0, 256, 8, 1}},   {kOpCopyF32, {size_t(1) << 22, 256, 8, 2}},
-    {kOpGatherF32, {0, 256, 8, 1}}, {kOpGatherF32, {size_t(1) << 22, 256, 8, 2}},
+    {kOpAddF32, {0, 128, 4, 4}},
+    {kOpAddF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpAddF16, {0, 1024, 4, 1}},
+    {kOpAddF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddBF16, {0, 128, 4, 2}},
+    {kOpAddBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSaxpyF32, {0, 64, 4, 2}},
+    {kOpSaxpyF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpReluF32, {0, 512, 8, 2}},
+    {kOpReluF32, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpCopyF32, {0, 256, 4, 1}},
+    {kOpCopyF32, {size_t(1) << 22, 64, 1024, 1}},
+    {kOpGatherF32, {0, 512, 1024, 1}},
+    {kOpGatherF32, {size_t(1) << 22, 512, 1, 1}},
 };
 
 constexpr int kMaxRows = 16;

@@ -31,8 +31,12 @@
 
 #include <stdint.h>
 
+// Cache policy of the 16-byte body accesses: non-temporal ("streaming")
+// loads and stores.  Every byte is touched once, so nothing is worth keeping
+// in L2 or the Infinity Cache; on MI355X the nt forms measured 5-8% faster
+// than the default policy for these kernels.
 #ifndef EW_LOAD_NT
-#define EW_LOAD_NT 0
+#define EW_LOAD_NT 1
 #endif
 #ifndef EW_STORE_NT
 #define EW_STORE_NT 1

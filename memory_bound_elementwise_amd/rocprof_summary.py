@@ -1,0 +1,177 @@
+"""Summarise rocprofv3 CSV output of bench.py runs into short text records.
+
+Kernel durations (from ``rocprofv3 --kernel-trace --stats -f csv``):
+
+    python -m memory_bound_elementwise_amd.rocprof_summary trace \\
+        --stats DIR/NAME_kernel_stats.csv --kernel REGEX --bytes B \\
+        --command "the rocprofv3 command line" --out profiles/FILE.txt
+
+HBM traffic (from two ``rocprofv3 --pmc`` runs per kernel, FETCH_SIZE then
+WRITE_SIZE, each in KiB per dispatch).  The counters are calibrated on the
+plain copy kernel of known size: scale = algorithmic bytes / counted bytes,
+per counter.  The result is written as text and merged into
+profiles/traffic.json, which bench.py reads (keyed by workload, kernel
+source hash and launch shape):
+
+    python -m memory_bound_elementwise_amd.rocprof_summary traffic \\
+        --workload NAME --kernel REGEX --bytes B \\
+        --fetch DIR/..._counter_collection.csv --write DIR/..._counter_collection.csv \\
+        --calib-kernel REGEX --calib-bytes-read R --calib-bytes-written W \\
+        --calib-fetch CSV --calib-write CSV --launch '{"block": .., "grid": .., "unroll": ..}' \\
+        --command "..." --out profiles/FILE.txt
+"""
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "memory_bound_elementwise_amd", "csrc", "ew_kernels.hip")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _rows(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def kernel_stats(path, kernel_re):
+    """(name, calls, average ns, min ns, max ns) of the kernel matching the regex."""
+    rx = re.compile(kernel_re)
+    for r in _rows(path):
+        if rx.search(r["Name"]):
+            return (r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                    float(r["MaxNs"]))
+    raise SystemExit(f"no kernel matching {kernel_re!r} in {path}")
+
+
+def counter_per_dispatch(path, kernel_re, counter):
+    """Median over dispatches of the counter summed within each dispatch."""
+    rx = re.compile(kernel_re)
+    per = {}
+    for r in _rows(path):
+        if r.get("Counter_Name") != counter or not rx.search(r.get("Kernel_Name", "")):
+            continue
+        per.setdefault(r.get("Dispatch_Id") or r.get("Correlation_Id"), 0.0)
+        per[r.get("Dispatch_Id") or r.get("Correlation_Id")] += float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernel {kernel_re!r} in {path}")
+    return statistics.median(per.values()), len(per)
+
+
+def cmd_trace(a):
+    name, calls, avg, mn, mx = kernel_stats(a.stats, a.kernel)
+    gbs = a.bytes / avg
+    text = [
+        f"# {a.title}",
+        "",
+        f"command: {a.command}",
+        f"source:  rocprofv3 kernel_stats.csv ({os.path.basename(a.stats)})",
+        "",
+        f"kernel:          {name}",
+        f"dispatches:      {calls}",
+        f"average:         {avg / 1000:.3f} us   (min {mn / 1000:.3f}, max {mx / 1000:.3f})",
+        f"algorithmic:     {a.bytes} bytes per launch",
+        f"achieved:        {gbs:.1f} GB/s = {100 * gbs / 8000:.2f} % of 8000 GB/s",
+        f"kernel source:   ew_kernels.hip sha256[:16] {kernel_source_hash()}",
+    ]
+    if a.bench_ms:
+        text.append(f"bench.py events: {a.bench_ms:.5f} ms per step "
+                    f"({100 * (a.bench_ms * 1e6 - avg) / avg:+.2f} % vs the trace average)")
+    with open(a.out, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def cmd_traffic(a):
+    fetch_kib, nd_f = counter_per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
+    write_kib, nd_w = counter_per_dispatch(a.write, a.kernel, "WRITE_SIZE")
+    cal_f, _ = counter_per_dispatch(a.calib_fetch, a.calib_kernel, "FETCH_SIZE")
+    cal_w, _ = counter_per_dispatch(a.calib_write, a.calib_kernel, "WRITE_SIZE")
+    scale_f = a.calib_bytes_read / (cal_f * 1024)
+    scale_w = a.calib_bytes_written / (cal_w * 1024)
+    fetch_b = fetch_kib * 1024 * scale_f
+    write_b = write_kib * 1024 * scale_w
+    total = fetch_b + write_b
+    launch = json.loads(a.launch)
+    text = [
+        f"# HBM traffic: {a.workload}",
+        "",
+        f"fetch command: {a.command_fetch}",
+        f"write command: {a.command_write}",
+        f"calibration:   {a.command_calib}",
+        "",
+        f"kernel:            {a.kernel}  launch {launch}",
+        f"FETCH_SIZE:        {fetch_kib:.0f} KiB per dispatch (median of {nd_f})",
+        f"WRITE_SIZE:        {write_kib:.0f} KiB per dispatch (median of {nd_w})",
+        f"calibration copy:  FETCH {cal_f:.0f} KiB for {a.calib_bytes_read} B read -> scale "
+        f"{scale_f:.4f};  WRITE {cal_w:.0f} KiB for {a.calib_bytes_written} B written -> scale "
+        f"{scale_w:.4f}",
+        f"HBM bytes/launch:  fetch {fetch_b:.0f} + write {write_b:.0f} = {total:.0f}",
+        f"algorithmic bytes: {a.bytes}  (traffic / algorithmic = {total / a.bytes:.4f})",
+        f"kernel source:     ew_kernels.hip sha256[:16] {kernel_source_hash()}",
+    ]
+    with open(a.out, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+    try:
+        with open(TRAFFIC_JSON) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                         "scaled by the copy-kernel calibration; see the .txt summaries",
+                "workloads": {}}
+    data["workloads"][a.workload] = {
+        "kernel": a.kernel, "launch": launch, "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_kib": fetch_kib, "write_kib": write_kib, "scale_fetch": scale_f,
+        "scale_write": scale_w, "hbm_bytes_per_launch": round(total),
+        "algorithmic_bytes": a.bytes, "summary": os.path.basename(a.out)}
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("--stats", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--bytes", type=int, required=True)
+    t.add_argument("--command", required=True)
+    t.add_argument("--title", default="Kernel duration")
+    t.add_argument("--bench-ms", type=float)
+    t.add_argument("--out", required=True)
+    r = sub.add_parser("traffic")
+    r.add_argument("--workload", required=True)
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--bytes", type=int, required=True)
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--calib-kernel", required=True)
+    r.add_argument("--calib-bytes-read", type=int, required=True)
+    r.add_argument("--calib-bytes-written", type=int, required=True)
+    r.add_argument("--calib-fetch", required=True)
+    r.add_argument("--calib-write", required=True)
+    r.add_argument("--launch", required=True)
+    r.add_argument("--command-fetch", required=True)
+    r.add_argument("--command-write", required=True)
+    r.add_argument("--command-calib", required=True)
+    r.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    (cmd_trace if a.cmd == "trace" else cmd_traffic)(a)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
