@@ -172,7 +172,8 @@ ew_status_t ew_load_launch_table(const char *path);
  *              (then it is read with aligned 16-byte loads; otherwise with
  *              4- or 2-byte aligned 16-byte loads); unused inputs report 1
  *   tiles      ceil(vectors / (block * unroll))
- *   grid       min(blocks_per_cu * cu_count, tiles)  (0 when tiles == 0)
+ *   grid       min(blocks_per_cu * cu_count, tiles), at least 1 when n > 0
+ *   segment, reps   n and 1, except for the gather (ew_make_gather_plan)
  * Validation is the same as the operation's (in1 is ignored for one-input
  * ops; for saxpy in0 = x and out = y). */
 typedef struct ew_plan {
@@ -188,11 +189,25 @@ typedef struct ew_plan {
     int blocks_per_cu;
     int unroll;
     int grid;
+    size_t segment;
+    int reps;
 } ew_plan_t;
 
 ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
                          const void *in1, size_t n, int cu_count,
                          ew_plan_t *plan);
+
+/* The gather's plan.  With g = gcd(stride mod n, n), output elements i and
+ * i + n/g read the same input element, so the output consists of g equal
+ * segments of n/g elements.  When 2 <= g <= 8 and n/g is a multiple of 4,
+ * the kernel computes one segment (head / vectors / tail describe it,
+ * segment = n/g) and stores each value reps = g times, so each input line is
+ * fetched once rather than g times; otherwise segment = n and reps = 1.
+ * (ew_gather_f32 runs the copy kernel when stride mod n == 1, and a kernel
+ * that reads the input with contiguous 16-byte loads when stride mod n == 2
+ * and reps == 2.)  Same validation as ew_gather_f32. */
+ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
+                                size_t stride, int cu_count, ew_plan_t *plan);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,7 @@ __all__ = [
     "ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
     "ew_copy_f32", "ew_gather_f32", "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
-    "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan",
+    "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan", "ew_make_gather_plan",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,7 @@ class EwPlan(ctypes.Structure):
         ("n", _sz), ("head", _sz), ("vectors", _sz), ("tail", _sz), ("tiles", _sz),
         ("vec_elems", _int), ("elem_size", _int), ("in_coaligned", _int * 2),
         ("block", _int), ("blocks_per_cu", _int), ("unroll", _int), ("grid", _int),
+        ("segment", _sz), ("reps", _int),
     ]
 
     def as_dict(self):
@@ -88,6 +89,8 @@ _c = {
     "ew_load_launch_table": _proto("ew_load_launch_table", _int, ctypes.c_char_p),
     "ew_make_plan": _proto("ew_make_plan", _int, ctypes.c_char_p, _vp, _vp, _vp, _sz, _int,
                            ctypes.POINTER(EwPlan)),
+    "ew_make_gather_plan": _proto("ew_make_gather_plan", _int, _vp, _vp, _sz, _sz, _int,
+                                  ctypes.POINTER(EwPlan)),
 }
 
 
@@ -214,6 +217,14 @@ def ew_make_plan(op, out, in0, in1, n, cu_count) -> EwPlan:
     plan = EwPlan()
     _check(_c["ew_make_plan"](op.encode(), out, in0, in1, int(n), int(cu_count),
                               ctypes.byref(plan)), "ew_make_plan")
+    return plan
+
+
+def ew_make_gather_plan(out, src, n, stride, cu_count) -> EwPlan:
+    """The gather's plan (segments and replicas) for integer addresses."""
+    plan = EwPlan()
+    _check(_c["ew_make_gather_plan"](out, src, int(n), int(stride), int(cu_count),
+                                     ctypes.byref(plan)), "ew_make_gather_plan")
     return plan
 
 

@@ -13,12 +13,13 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <numeric>
 #include <vector>
 
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 struct OpInfo {
     const char *name;
@@ -64,20 +65,20 @@ struct DefaultRow {
     Row row;
 };
 constexpr DefaultRow kDefaults[] = {
-    {kOpAddF32, {0, 128, 4, 4}},
+    {kOpAddF32, {0, 512, 1, 2}},
     {kOpAddF32, {size_t(1) << 22, 1024, 1024, 1}},
-    {kOpAddF16, {0, 1024, 4, 1}},
+    {kOpAddF16, {0, 128, 2, 2}},
     {kOpAddF16, {size_t(1) << 22, 128, 1024, 1}},
-    {kOpAddBF16, {0, 128, 4, 2}},
+    {kOpAddBF16, {0, 256, 2, 2}},
     {kOpAddBF16, {size_t(1) << 22, 128, 1024, 1}},
-    {kOpSaxpyF32, {0, 64, 4, 2}},
+    {kOpSaxpyF32, {0, 512, 1, 1}},
     {kOpSaxpyF32, {size_t(1) << 22, 1024, 1024, 1}},
-    {kOpReluF32, {0, 512, 8, 2}},
+    {kOpReluF32, {0, 64, 1024, 1}},
     {kOpReluF32, {size_t(1) << 22, 512, 1024, 1}},
-    {kOpCopyF32, {0, 256, 4, 1}},
-    {kOpCopyF32, {size_t(1) << 22, 64, 1024, 1}},
-    {kOpGatherF32, {0, 512, 1024, 1}},
-    {kOpGatherF32, {size_t(1) << 22, 512, 1, 1}},
+    {kOpCopyF32, {0, 1024, 2, 2}},
+    {kOpCopyF32, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpGatherF32, {0, 128, 4, 1}},
+    {kOpGatherF32, {size_t(1) << 22, 128, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
@@ -305,6 +306,42 @@ uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
     return (uint64_t)(((unsigned __int128)a * (unsigned __int128)b) % (unsigned __int128)m);
 }
 
+// The gather's plan.  With g = gcd(stride mod n, n), output i and output
+// i + n/g read the same input element ((stride * n/g) mod n == 0), so the
+// output is g copies of its first n/g elements.  For 2 <= g <= 8 with n/g a
+// multiple of 4 (so every copy has the same 16-byte alignment) the kernel
+// computes one segment and stores each vector g times: every input line is
+// then fetched once instead of g times.  Otherwise one segment of n.
+void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, GatherArgs *g,
+                 Launch *l)
+{
+    const uint64_t s = stride % n;
+    const uint64_t gcd = std::gcd(s, (uint64_t)n);  // gcd(0, n) == n
+    uint64_t reps = 1, seg = n;
+    if (gcd >= 2 && gcd <= 8 && (n / gcd) % 4 == 0) {
+        reps = gcd;
+        seg = n / gcd;
+    }
+    const Plan p = make_plan(kOpGatherF32, out, in, nullptr, seg, cus);
+    *g = GatherArgs{};
+    g->in = reinterpret_cast<const uint32_t *>(in);
+    g->out = reinterpret_cast<uint32_t *>(out);
+    g->n = n;
+    g->stride = s;
+    g->seg = seg;
+    g->reps = reps;
+    g->head = p.head;
+    g->vectors = p.vectors;
+    g->tail = p.tail;
+    g->tiles = p.tiles;
+    const uint64_t nthr = (uint64_t)p.launch.block;
+    g->step_vec = mulmod_host(s, (4 * nthr) % n, n);
+    const uint64_t tile_elems = (4 * nthr * (uint64_t)p.launch.unroll) % n;
+    g->step_tile = mulmod_host(mulmod_host(s, tile_elems, n), (uint64_t)p.launch.grid % n, n);
+    g->wide = (s != 0 && (n - 1) > UINT64_MAX / s) ? 1 : 0;
+    *l = p.launch;
+}
+
 }  // namespace
 }  // namespace ew
 
@@ -353,25 +390,17 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride, 
     if (stride == 0) return EW_ERR_INVALID_ARG;
     ew_status_t st = validate(kOpGatherF32, out, in, nullptr, n);
     if (st != EW_OK) return st;
+    if (n == 1 || stride % n == 1) {
+        // out[i] = in[i mod n] = in[i]: the contiguous copy
+        return run_stream(kOpCopyF32, out, in, nullptr, n, 0.0f, s);
+    }
     int cus = 0;
     st = current_device(&cus);
     if (st != EW_OK) return st;
-    const Plan p = make_plan(kOpGatherF32, out, in, nullptr, n, cus);
     GatherArgs g{};
-    g.in = reinterpret_cast<const uint32_t *>(in);
-    g.out = reinterpret_cast<uint32_t *>(out);
-    g.n = n;
-    g.stride = stride % n;
-    g.head = p.head;
-    g.vectors = p.vectors;
-    g.tail = p.tail;
-    g.tiles = p.tiles;
-    const uint64_t nthr = (uint64_t)p.launch.block;
-    g.step_vec = mulmod_host(g.stride, (4 * nthr) % n, n);
-    const uint64_t tile_elems = (4 * nthr * (uint64_t)p.launch.unroll) % n;
-    g.step_tile = mulmod_host(mulmod_host(g.stride, tile_elems, n), (uint64_t)p.launch.grid % n, n);
-    g.wide = (g.stride != 0 && (n - 1) > UINT64_MAX / g.stride) ? 1 : 0;
-    const hipError_t e = launch_gather(g, p.launch, s);
+    Launch l{};
+    gather_plan(in, out, n, stride, cus, &g, &l);
+    const hipError_t e = launch_gather(g, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
@@ -460,6 +489,7 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const
     plan->elem_size = info.elem_size;
     plan->vec_elems = 16 / info.elem_size;
     plan->in_coaligned[0] = plan->in_coaligned[1] = 1;
+    plan->reps = 1;
     const Row r = get_row(id, n);
     plan->block = r.block;
     plan->blocks_per_cu = r.blocks_per_cu;
@@ -473,6 +503,39 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const
     plan->in_coaligned[0] = p.co[0] ? 1 : 0;
     plan->in_coaligned[1] = p.co[1] ? 1 : 0;
     plan->grid = p.launch.grid;
+    plan->segment = n;
+    plan->reps = 1;
+    return EW_OK;
+}
+
+ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_t stride,
+                                int cu_count, ew_plan_t *plan)
+{
+    if (!plan || cu_count <= 0) return EW_ERR_INVALID_ARG;
+    std::memset(plan, 0, sizeof *plan);
+    if (n == 0) return EW_OK;
+    if (stride == 0) return EW_ERR_INVALID_ARG;
+    const ew_status_t st = validate(kOpGatherF32, out, in, nullptr, n);
+    if (st != EW_OK) return st;
+    GatherArgs g{};
+    Launch l{};
+    gather_plan(static_cast<const float *>(in), static_cast<float *>(const_cast<void *>(out)), n,
+                stride, cu_count, &g, &l);
+    const Row r = get_row(kOpGatherF32, (size_t)g.seg);
+    plan->n = n;
+    plan->head = g.head;
+    plan->vectors = g.vectors;
+    plan->tail = g.tail;
+    plan->tiles = g.tiles;
+    plan->vec_elems = 4;
+    plan->elem_size = 4;
+    plan->in_coaligned[0] = plan->in_coaligned[1] = 1;
+    plan->block = l.block;
+    plan->blocks_per_cu = r.blocks_per_cu;
+    plan->unroll = l.unroll;
+    plan->grid = l.grid;
+    plan->segment = g.seg;
+    plan->reps = (int)g.reps;
     return EW_OK;
 }
 

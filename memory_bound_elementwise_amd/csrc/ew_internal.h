@@ -34,12 +34,18 @@ struct StreamArgs {
 };
 
 // The gather additionally walks its input index (stride * i) mod n
-// incrementally; the steps are reduced mod n on the host.
+// incrementally; the steps are reduced mod n on the host.  When
+// g = gcd(stride, n) > 1 the output is g copies of one segment of n / g
+// elements (out[i + k*n/g] = out[i]); then head / vectors / tail describe one
+// segment and every value is stored `reps` times, `seg` elements apart, so
+// each input element is fetched once instead of g times.
 struct GatherArgs {
     const uint32_t *in;
     uint32_t *out;
     uint64_t n;
     uint64_t stride;     // stride mod n
+    uint64_t seg;        // elements per output segment (n when reps == 1)
+    uint64_t reps;       // number of identical segments (1..8)
     uint64_t head;
     uint64_t vectors;
     uint64_t tail;

@@ -278,10 +278,12 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 {
     const uint32_t tid = threadIdx.x;
     const uint64_t nthr = blockDim.x;
+    const uint64_t seg_bytes = g.seg * 4;
 
     if (blockIdx.x == 0 && tid < g.head + g.tail) {
         const uint64_t e = tid < g.head ? (uint64_t)tid : g.head + g.vectors * 4 + (tid - g.head);
-        g.out[e] = g.in[mul_mod(g.stride, e, g.n, g.wide)];
+        const uint32_t x = g.in[mul_mod(g.stride, e, g.n, g.wide)];
+        for (uint64_t k = 0; k < g.reps; ++k) g.out[e + k * g.seg] = x;
     }
 
     uint64_t t = blockIdx.x;
@@ -309,9 +311,69 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t v = v0 + u * nthr;
-            if (v < g.vectors) store16(out + v * 16, u32x4{r[u][0], r[u][1], r[u][2], r[u][3]});
+            if (v < g.vectors) {
+                const u32x4 x = u32x4{r[u][0], r[u][1], r[u][2], r[u][3]};
+                for (uint64_t k = 0; k < g.reps; ++k) store16(out + k * seg_bytes + v * 16, x);
+            }
         }
         jt = add_mod(jt, g.step_tile, g.n);
+    }
+}
+
+// Stride 2 with two equal segments (n even, n/2 a multiple of 4): output i of
+// the first segment reads in[2i] and never wraps.  Instead of four scalar
+// loads per vector, each wave reads its 2 KiB input span with two contiguous
+// 16-byte-per-lane loads (1 KiB per instruction) and keeps elements 0 and 2
+// of each: lane l of a wave covering outputs [o, o + 256) produces outputs
+// o + 2l, o + 2l + 1 from the first load and o + 128 + 2l, o + 129 + 2l from
+// the second, stored as 8-byte pairs (512 contiguous bytes per instruction),
+// once per segment.  A tile is blockDim * U vectors of 4 outputs, so the
+// launch shape means the same as for the general gather.
+template <int U, bool Co>
+__global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = tid >> 6;
+    const uint64_t nthr = blockDim.x;
+    const uint64_t seg_bytes = g.seg * 4;
+
+    if (blockIdx.x == 0 && tid < g.head + g.tail) {
+        const uint64_t e = tid < g.head ? (uint64_t)tid : g.head + g.vectors * 4 + (tid - g.head);
+        const uint32_t x = g.in[2 * e];
+        for (uint64_t k = 0; k < g.reps; ++k) g.out[e + k * g.seg] = x;
+    }
+
+    const char *in = reinterpret_cast<const char *>(g.in);
+    char *out = reinterpret_cast<char *>(g.out);
+    const uint64_t body_end = g.head + g.vectors * 4;
+    for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
+        const uint64_t o0 = g.head + 4 * t * nthr * U;
+        u32x4 x[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t o = o0 + ((uint64_t)wave * U + u) * 256;
+            const uint64_t i1 = o + 2 * lane, i2 = o + 128 + 2 * lane;
+            x[u][0] = i1 < body_end ? load16<Co, 4>(in + 8 * i1) : u32x4{0, 0, 0, 0};
+            x[u][1] = i2 < body_end ? load16<Co, 4>(in + 8 * i2) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t o = o0 + ((uint64_t)wave * U + u) * 256;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint64_t i = o + 128 * h + 2 * lane;
+                if (i < body_end) {
+                    const u32x2 pair = u32x2{x[u][h].x, x[u][h].z};
+                    for (uint64_t k = 0; k < g.reps; ++k) {
+                        u32x2 *q = reinterpret_cast<u32x2 *>(out + k * seg_bytes + 4 * i);
+                        if constexpr (EW_STORE_NT) __builtin_nontemporal_store(pair, q);
+                        else *q = pair;
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -374,17 +436,39 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
     }
 }
 
+namespace {
+
+template <int U, bool Co>
+const void *gather2_fn()
+{
+    return reinterpret_cast<const void *>(&ew_gather2_kernel<U, Co>);
+}
+
+}  // namespace
+
 hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
 {
     GatherArgs a = args;
     void *kargs[] = {&a};
     const void *fn = nullptr;
-    switch (l.unroll) {
-    case 1: fn = reinterpret_cast<const void *>(&ew_gather_kernel<1>); break;
-    case 2: fn = reinterpret_cast<const void *>(&ew_gather_kernel<2>); break;
-    case 4: fn = reinterpret_cast<const void *>(&ew_gather_kernel<4>); break;
-    case 8: fn = reinterpret_cast<const void *>(&ew_gather_kernel<8>); break;
-    default: return hipErrorInvalidValue;
+    if (args.stride == 2 && args.reps == 2) {
+        // co-alignment of the input's body start: in + 8 * head
+        const bool co = ((reinterpret_cast<uintptr_t>(args.in) + 8 * args.head) & 15u) == 0;
+        switch (l.unroll) {
+        case 1: fn = co ? gather2_fn<1, true>() : gather2_fn<1, false>(); break;
+        case 2: fn = co ? gather2_fn<2, true>() : gather2_fn<2, false>(); break;
+        case 4: fn = co ? gather2_fn<4, true>() : gather2_fn<4, false>(); break;
+        case 8: fn = co ? gather2_fn<8, true>() : gather2_fn<8, false>(); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (l.unroll) {
+        case 1: fn = reinterpret_cast<const void *>(&ew_gather_kernel<1>); break;
+        case 2: fn = reinterpret_cast<const void *>(&ew_gather_kernel<2>); break;
+        case 4: fn = reinterpret_cast<const void *>(&ew_gather_kernel<4>); break;
+        case 8: fn = reinterpret_cast<const void *>(&ew_gather_kernel<8>); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
 }

@@ -105,6 +105,10 @@ WORKLOADS = {
     "cfg5b_gather_f32_2e26_s2": _w(
         "cfg5b_gather_f32_2e26_s2", "gather_f32", 1 << 26, 107, "uniform", stride=2,
         description="fp32 strided gather out[i]=in[(2*i) mod n], n=2^26, in uniform[-1,1)"),
+    "gather_f32_2e26_s3": _w(
+        "gather_f32_2e26_s3", "gather_f32", 1 << 26, 107, "uniform", stride=3,
+        description="fp32 strided gather out[i]=in[(3*i) mod n], n=2^26 (gcd 1: a permutation "
+                    "read with stride 3)"),
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),

@@ -204,6 +204,12 @@ def test_gather_brute_force_strides():
     for n in (1000, 4099, 65537):
         for stride in (1, 2, 3, 7, n - 1, n + 1, 1 << 40):
             cases.append((n, 1, [2], stride))
+    # replicated-segment plans (gcd(stride, n) in 2..8) and their neighbours
+    for n, stride in (((1 << 20), 2), ((1 << 20) + 4, 2), (3 << 18, 6), ((1 << 20), 8),
+                      ((1 << 20), 4), (3 << 18, 3), (5 * 4096, 5), ((1 << 20) + 1, 2),
+                      ((1 << 20), (1 << 20) + 2)):
+        for oo in (0, 1, 3):
+            cases.append((n, oo, [0], stride))
     failures = _run_cases("gather_f32", cases, seed=310)
     assert not failures, failures[:10]
 
@@ -255,6 +261,12 @@ def test_every_kernel_variant_several_tiles_ragged(op):
             else:
                 offs = [(1, [1, 1]), (1, [0, 1]), (1, [1, 2]), (0, [3, 5 % vec])]
             cases = [(n, oo, oi, 2) for (oo, oi) in offs]
+            if op == "gather_f32":
+                # stride 2 with two equal segments: the contiguous-load kernel
+                m = (2 * bpc * cus + 1) * block * unroll * 4
+                gp = ew.ew_make_gather_plan(1 << 40, 1 << 41, 2 * m, 2, cus)
+                assert gp.reps == 2 and gp.tiles > 2 * gp.grid, (gp.reps, gp.tiles, gp.grid)
+                cases += [(2 * m, 1, [1], 2), (2 * m, 0, [3], 2), (2 * m, 2, [0], 2)]
             failures = _run_cases(op, cases, seed=320)
             assert not failures, (block, bpc, unroll, failures[:5])
     finally:

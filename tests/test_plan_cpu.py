@@ -127,3 +127,48 @@ def test_plan_rejects_what_the_operation_rejects():
         ew.ew_make_plan("nope", BASE, BASE, BASE, 16, CUS)
     with pytest.raises(ew.EwError):
         ew.ew_make_plan("add_f32", BASE + 2 * MiB, BASE, BASE + MiB, 16, 0)  # no CUs
+
+
+@pytest.mark.parametrize("n,stride,reps,segment", [
+    (1 << 26, 2, 2, 1 << 25),        # the stride-2 workload: two equal halves
+    ((1 << 26) + 1, 2, 1, (1 << 26) + 1),   # odd n: gcd 1, one segment
+    (1024, 4, 4, 256),
+    (1200, 6, 6, 200),
+    (1200, 12, 1, 1200),             # gcd 12 > 8: no replication
+    (1002, 2, 1, 1002),              # n/2 = 501 not a multiple of 4
+    (1024, 1026, 2, 512),            # stride reduced mod n first
+    (1 << 20, 3, 1, 1 << 20),        # odd stride, power-of-two n: a permutation
+    (16, 16, 1, 16),                 # stride == n: gcd(0, n) = n > 8
+    (8, 8, 1, 8),                    # gcd 8 but n/8 = 1 is not a multiple of 4
+])
+def test_gather_plan_segments(n, stride, reps, segment):
+    p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
+    assert (p.reps, p.segment) == (reps, segment)
+    assert p.head + p.vectors * 4 + p.tail == segment
+    assert p.head == 0 and p.tail == segment % 4
+
+
+def test_gather_replicated_segments_match_the_definition():
+    """Whenever the planner replicates, the oracle's output really consists of
+    `reps` equal segments (a property of the definition, checked on the CPU)."""
+    import numpy as np
+    import oracle
+    x = np.arange(1, 257, dtype=np.uint32).view(np.float32)
+    for n in range(4, 257, 4):
+        for stride in range(1, 2 * n + 3):
+            p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
+            assert p.reps * p.segment == n
+            if p.reps > 1:
+                out = oracle.gather_f32(x[:n], stride).view(np.uint32)
+                first = out[:p.segment]
+                for k in range(1, p.reps):
+                    assert np.array_equal(out[k * p.segment:(k + 1) * p.segment], first)
+
+
+def test_gather_plan_validation():
+    with pytest.raises(ew.EwError):
+        ew.ew_make_gather_plan(BASE + MiB, BASE, 16, 0, CUS)
+    with pytest.raises(ew.EwError):
+        ew.ew_make_gather_plan(BASE, BASE, 16, 2, CUS)
+    p = ew.ew_make_gather_plan(0, 0, 0, 2, CUS)
+    assert p.vectors == 0 and p.reps == 0
