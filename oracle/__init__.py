@@ -14,6 +14,7 @@ Each function wraps the plain scalar C loop of the same name in ``oracle.c``
 * ``relu_f32(x)``              IEEE maximum(x, +0)
 * ``copy_f32(x)``              bitwise copy
 * ``gather_f32(x, stride)``    out[i] = x[(stride*i) mod n], bitwise
+* ``gather_index(n, stride, i)``  the input index of one gather output
 
 plus the scalar conversions and the binary32 ulp distance.  Parity status:
 all functions pinned (see ``tests/test_oracle.py``); none unpinned.
@@ -63,6 +64,8 @@ def _load():
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_ulp_distance_f32.argtypes = [ctypes.c_float, ctypes.c_float]
     lib.oracle_ulp_distance_f32.restype = ctypes.c_uint64
+    lib.oracle_gather_index.argtypes = [sz, sz, sz]
+    lib.oracle_gather_index.restype = sz
     lib.oracle_fpenv_ok.argtypes = []
     lib.oracle_fpenv_ok.restype = ctypes.c_int
     _lib = lib
@@ -156,6 +159,11 @@ def gather_f32(x, stride):
     if x.size:
         lib.oracle_gather_f32(_ptr(x), _ptr(y), x.size, int(stride))
     return y
+
+
+def gather_index(n, stride, i) -> int:
+    """(stride * i) mod n, exact: the input index of gather output i."""
+    return int(_load().oracle_gather_index(int(n), int(stride), int(i)))
 
 
 def f32_to_f16(x):

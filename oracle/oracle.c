@@ -18,7 +18,7 @@
  *   [PerfNotes] GPU-performance lecture notes (cyqw.cn/news/898472)
  *
  * Parity status: every function here is pinned by tests against library
- * routines (numpy, torch CPU, x86 F16C via numpy), exact rational arithmetic,
+ * routines (numpy, torch CPU, the x86 F16C instructions), exact rational arithmetic,
  * closed forms and brute force.  None is "parity unpinned".
  */
 #include <stddef.h>
@@ -233,6 +233,15 @@ void oracle_gather_f32(const float *in, float *out, size_t n, size_t stride)
         size_t j = (size_t)(p % (unsigned __int128)n);
         d[i] = s[j];
     }
+}
+
+/* The input index the gather reads for output i: (stride * i) mod n, exact
+ * for every 64-bit stride and i (one element of oracle_gather_f32, for
+ * checking sampled outputs of arrays too large to gather on the host). */
+size_t oracle_gather_index(size_t n, size_t stride, size_t i)
+{
+    unsigned __int128 p = (unsigned __int128)stride * (unsigned __int128)i;
+    return (size_t)(p % (unsigned __int128)n);
 }
 
 /* ------------------------------------------------------------------------ */

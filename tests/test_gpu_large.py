@@ -1,0 +1,180 @@
+"""Maximum sizes: arrays past 2^32 elements.
+
+Element indices, byte offsets and the gather's index products must all be
+64-bit (the pages' kernels use 32-bit `int` indices).  Inputs are
+deterministic integer patterns generated on the GPU; results are checked two
+ways:
+
+* properties that hold at any size, on every element, on the device, chunk
+  by chunk (A + (-0) == A bitwise; copy == input; the stride-2 gather's two
+  halves are equal);
+* sampled elements (first, last, around the 2^31 and 2^32 element
+  boundaries, and random positions) against the oracle computed one by one
+  on the host.
+"""
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_elementwise_amd as ew
+import oracle
+from tests.gpu_util import DEV, mismatches
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 27
+GiB = 1 << 30
+
+
+def _need(nbytes):
+    free, _ = torch.cuda.mem_get_info()
+    if free < nbytes + 4 * GiB:
+        pytest.skip(f"needs {nbytes / GiB:.0f} GiB of free device memory")
+
+
+def _fill_f32(t, mul, mod, scale):
+    """t[i] = ((i * mul) mod mod) * scale, exact in binary32 (mod <= 2^24)."""
+    n = t.numel()
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        i = torch.arange(s, e, device=DEV, dtype=torch.int64)
+        t[s:e] = ((i * mul) % mod).to(torch.float32) * scale
+
+
+def _fill_bits(t, mul, bits):
+    """Integer view of t gets ((i * mul) >> 7) mod 2^bits, as signed ints."""
+    n = t.numel()
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        i = torch.arange(s, e, device=DEV, dtype=torch.int64)
+        v = ((i * mul) >> 7) & ((1 << bits) - 1)
+        v = torch.where(v >= (1 << (bits - 1)), v - (1 << bits), v)
+        t[s:e] = v.to(t.dtype)
+
+
+def _samples(n, seed=5):
+    g = np.random.Generator(np.random.PCG64(seed))
+    edges = [0, 1, 2, 3, n - 4, n - 3, n - 2, n - 1]
+    for b in (1 << 31, 1 << 32):
+        if b < n:
+            edges += list(range(max(0, b - 5), min(n, b + 5)))
+    idx = np.concatenate([np.array(edges, np.int64), g.integers(0, n, size=1 << 18)])
+    return np.unique(idx)
+
+
+def _take(t, idx):
+    return t[torch.from_numpy(idx).to(DEV)].cpu().numpy()
+
+
+def _chunked_equal(x, y):
+    n = x.numel()
+    for s in range(0, n, CHUNK):
+        e = min(n, s + CHUNK)
+        if not torch.equal(x[s:e], y[s:e]):
+            return False
+    return True
+
+
+def test_add_f32_past_2_pow_32_elements():
+    n = (1 << 32) + 5
+    _need(3 * 4 * n)
+    print(f"[large] add_f32 n={n}", flush=True)
+    a = torch.empty(n, dtype=torch.float32, device=DEV)
+    b = torch.empty(n, dtype=torch.float32, device=DEV)
+    c = torch.empty(n, dtype=torch.float32, device=DEV)
+    _fill_f32(a, 40503, 65521, 2.0 ** -8)
+    b.fill_(-0.0)
+    ew.ew_add_f32(a, b, c)
+    torch.cuda.synchronize()
+    assert _chunked_equal(c.view(torch.int32), a.view(torch.int32))   # A + (-0) == A
+    _fill_f32(b, 7919, 1021, 2.0 ** -10)
+    ew.ew_add_f32(a, b, c)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    ref = oracle.add_f32(_take(a, idx), _take(b, idx))
+    assert mismatches("add_f32", _take(c, idx), ref).size == 0
+    del a, b, c
+    torch.cuda.empty_cache()
+
+
+def test_add_bf16_past_2_pow_32_elements_misaligned():
+    n = (1 << 32) + 9
+    _need(3 * 2 * (n + 8))
+    print(f"[large] add_bf16 n={n}", flush=True)
+    abase = torch.empty(n + 8, dtype=torch.int16, device=DEV)
+    b = torch.empty(n, dtype=torch.int16, device=DEV)
+    cbase = torch.empty(n + 8, dtype=torch.int16, device=DEV)
+    a, c = abase[3:3 + n], cbase[1:1 + n]
+    _fill_bits(a, 2654435761, 16)
+    _fill_bits(b, 40503 * 65537, 16)
+    ew.ew_add_bf16(a, b, c)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    got = _take(c, idx).view(np.uint16)
+    ref = oracle.add_bf16(_take(a, idx).view(np.uint16), _take(b, idx).view(np.uint16))
+    assert mismatches("add_bf16", got, ref).size == 0
+    del abase, b, cbase, a, c
+    torch.cuda.empty_cache()
+
+
+def test_copy_and_saxpy_past_2_pow_32_elements():
+    n = (1 << 32) + 7
+    _need(2 * 4 * (n + 4))
+    print(f"[large] copy / saxpy n={n}", flush=True)
+    xbase = torch.empty(n + 4, dtype=torch.float32, device=DEV)
+    y = torch.empty(n, dtype=torch.float32, device=DEV)
+    x = xbase[1:1 + n]
+    _fill_f32(x, 40503, 65521, 2.0 ** -8)
+    ew.ew_copy_f32(x, y)
+    torch.cuda.synchronize()
+    assert _chunked_equal(y.view(torch.int32), x.view(torch.int32))
+    _fill_f32(y, 7919, 1021, 2.0 ** -10)
+    idx = _samples(n)
+    y0 = _take(y, idx)
+    ew.ew_saxpy_f32(2.5, x, y)
+    torch.cuda.synchronize()
+    ref = oracle.saxpy_f32(2.5, _take(x, idx), y0)
+    assert mismatches("saxpy_f32", _take(y, idx), ref).size == 0
+    del xbase, x, y
+    torch.cuda.empty_cache()
+
+
+def test_gather_wide_index_products():
+    """stride = n - 1 with n > 2^32: stride * (n - 1) exceeds 2^64, so each
+    lane's first index takes the exact double-and-add path."""
+    n = (1 << 32) + 8
+    _need(2 * 4 * n)
+    print(f"[large] gather stride n-1, n={n}", flush=True)
+    src = torch.empty(n, dtype=torch.int32, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    plan = ew.ew_make_gather_plan(out.data_ptr(), src.data_ptr(), n, n - 1,
+                                  torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan.reps == 1
+    ew.ew_gather_f32(src.data_ptr(), out.data_ptr(), n - 1, n=n)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    j = np.array([oracle.gather_index(n, n - 1, int(i)) for i in idx], np.int64)
+    assert np.array_equal(_take(out, idx), _take(src, j))
+    del src, out
+    torch.cuda.empty_cache()
+
+
+def test_gather_stride_2_replicated_segments_past_2_pow_32():
+    n = (1 << 33) + 16          # two segments of 2^32 + 8 elements
+    _need(2 * 4 * n)
+    print(f"[large] gather stride 2, n={n}", flush=True)
+    src = torch.empty(n, dtype=torch.int32, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    plan = ew.ew_make_gather_plan(out.data_ptr(), src.data_ptr(), n, 2,
+                                  torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan.reps == 2 and plan.segment == n // 2
+    ew.ew_gather_f32(src.data_ptr(), out.data_ptr(), 2, n=n)
+    torch.cuda.synchronize()
+    assert _chunked_equal(out[: n // 2], out[n // 2:])
+    idx = _samples(n)
+    j = np.array([oracle.gather_index(n, 2, int(i)) for i in idx], np.int64)
+    assert np.array_equal(_take(out, idx), _take(src, j))
+    del src, out
+    torch.cuda.empty_cache()

@@ -458,6 +458,25 @@ def test_gather_large_index_products_exact():
         assert o[i] == (stride * i) % n
 
 
+def test_gather_index_matches_python_integers():
+    g = np.random.Generator(np.random.PCG64(73))
+    for _ in range(2000):
+        n = int(g.integers(1, 1 << 62))
+        stride = int(g.integers(0, 1 << 63)) * 2 + int(g.integers(0, 2))
+        i = int(g.integers(0, n))
+        assert oracle.gather_index(n, stride, i) == (stride * i) % n
+    n = (1 << 32) + 8
+    assert oracle.gather_index(n, n - 1, 5) == n - 5
+    assert oracle.gather_index(n, n - 1, 0) == 0
+
+
+def test_gather_index_agrees_with_the_array_gather():
+    x = np.arange(997, dtype=np.uint32).view(np.float32)
+    for stride in (1, 2, 5, 996, 997, (1 << 64) - 1):
+        o = oracle.gather_f32(x, stride).view(np.uint32)
+        assert all(int(o[i]) == oracle.gather_index(997, stride, i) for i in range(997))
+
+
 # --------------------------------------------------------------------------
 # ulp distance
 # --------------------------------------------------------------------------
