@@ -12,6 +12,9 @@ Each function wraps the plain scalar C loop of the same name in ``oracle.c``
 * ``add_bf16(a, b)``           bfloat16 bits in, bfloat16 bits out (uint16)
 * ``saxpy_f32(alpha, x, y)``   returns fmaf(alpha, x, y) (y is not modified)
 * ``relu_f32(x)``              IEEE maximum(x, +0)
+* ``add_relu_f32(a, b)``       maximum(a + b, +0)
+* ``saxpy_relu_f32(alpha, x, y)``  maximum(fmaf(alpha, x, y), +0)
+* ``bias_relu_f32(x, bias, rows, cols)``  maximum(x[r, c] + bias[c], +0)
 * ``copy_f32(x)``              bitwise copy
 * ``gather_f32(x, stride)``    out[i] = x[(stride*i) mod n], bitwise
 * ``gather_index(n, stride, i)``  the input index of one gather output
@@ -44,6 +47,12 @@ def _load():
         getattr(lib, name).restype = None
     lib.oracle_saxpy_f32.argtypes = [ctypes.c_float, vp, vp, sz]
     lib.oracle_saxpy_f32.restype = None
+    lib.oracle_add_relu_f32.argtypes = [vp, vp, vp, sz]
+    lib.oracle_add_relu_f32.restype = None
+    lib.oracle_saxpy_relu_f32.argtypes = [ctypes.c_float, vp, vp, sz]
+    lib.oracle_saxpy_relu_f32.restype = None
+    lib.oracle_bias_relu_f32.argtypes = [vp, vp, vp, sz, sz]
+    lib.oracle_bias_relu_f32.restype = None
     for name in ("oracle_relu_f32", "oracle_copy_f32",
                  "oracle_f32_to_f16_array", "oracle_f16_to_f32_array",
                  "oracle_f32_to_bf16_array", "oracle_bf16_to_f32_array"):
@@ -130,6 +139,36 @@ def saxpy_f32(alpha, x, y):
         raise ValueError("shape mismatch")
     lib.oracle_saxpy_f32(float(np.float32(alpha)), _ptr(x), _ptr(out), x.size)
     return out
+
+
+def add_relu_f32(a, b):
+    """maximum(a + b, +0), the sum rounded once to binary32."""
+    return _binary("oracle_add_relu_f32", a, b, np.float32)
+
+
+def saxpy_relu_f32(alpha, x, y):
+    """maximum(fmaf(alpha, x, y), +0) per element; ``y`` is left unchanged."""
+    lib = _load()
+    _check_env(lib)
+    x = _as(x, np.float32)
+    out = np.array(_as(y, np.float32), copy=True)
+    if x.shape != out.shape:
+        raise ValueError("shape mismatch")
+    lib.oracle_saxpy_relu_f32(float(np.float32(alpha)), _ptr(x), _ptr(out), x.size)
+    return out
+
+
+def bias_relu_f32(x, bias, rows, cols):
+    """maximum(x[r, c] + bias[c], +0) for a row-major rows x cols x."""
+    lib = _load()
+    _check_env(lib)
+    x = _as(x, np.float32)
+    bias = _as(bias, np.float32)
+    if x.size != rows * cols or bias.size != cols:
+        raise ValueError("shape mismatch")
+    y = np.empty_like(x)
+    lib.oracle_bias_relu_f32(_ptr(x), _ptr(bias), _ptr(y), int(rows), int(cols))
+    return y
 
 
 def relu_f32(x):

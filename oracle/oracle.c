@@ -16,6 +16,7 @@
  *   [Puzzle31]  Mojo GPU Puzzles, "Puzzle 31: occupancy optimisation"
  *               (puzzles.modular.com)
  *   [PerfNotes] GPU-performance lecture notes (cyqw.cn/news/898472)
+ *   [GEMM-9.3]  "9.3 project: GEMM optimisation step by step" (amittech.dev)
  *
  * Parity status: every function here is pinned by tests against library
  * routines (numpy, torch CPU, the x86 F16C instructions), exact rational arithmetic,
@@ -209,6 +210,39 @@ void oracle_relu_f32(const float *x, float *y, size_t n)
         else if (v != v)   y[i] = v;
         else               y[i] = 0.0f;
     }
+}
+
+/* ReLU of one binary32 value in the IEEE maximum(v, +0) sense (see above). */
+static float relu1(float v)
+{
+    if (v > 0.0f) return v;
+    if (v != v) return v;
+    return 0.0f;
+}
+
+/* Fused add and ReLU: c[i] = maximum(a[i] + b[i], +0), the sum rounded once
+ * to binary32 before the maximum.  An epilogue that saves the second pass
+ * over memory ([GEMM-9.3] "what comes next": fuse bias and ReLU into the
+ * producing kernel; [PerfNotes] 5.3: fusion raises the intensity of
+ * memory-bound operations). */
+void oracle_add_relu_f32(const float *a, const float *b, float *c, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) c[i] = relu1(a[i] + b[i]);
+}
+
+/* Fused SAXPY and ReLU in place: y[i] = maximum(fmaf(alpha, x[i], y[i]), +0). */
+void oracle_saxpy_relu_f32(float alpha, const float *x, float *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = relu1(fmaf(alpha, x[i], y[i]));
+}
+
+/* Bias and ReLU over a row-major rows x cols matrix: the bias vector is
+ * broadcast along rows, y[r*cols + c] = maximum(x[r*cols + c] + bias[c], +0). */
+void oracle_bias_relu_f32(const float *x, const float *bias, float *y, size_t rows, size_t cols)
+{
+    for (size_t r = 0; r < rows; ++r)
+        for (size_t c = 0; c < cols; ++c)
+            y[r * cols + c] = relu1(x[r * cols + c] + bias[c]);
 }
 
 /* Contiguous copy out[i] = in[i], moved as bit patterns so NaN payloads and

@@ -406,6 +406,53 @@ def test_relu_invariants():
     assert np.all(np.isnan(n)) and (n.view(np.uint32)[1] >> 31) == 1
 
 
+def test_add_relu_vs_numpy():
+    """maximum(a + b, 0) with numpy's own add and maximum, bitwise."""
+    g = synth.rng(55)
+    a = np.concatenate([synth.uniform_pm1(g, 1 << 18), _random_f32_bits(1 << 18, 56, False),
+                        F32_SPECIALS, np.array([-0.0, 1.0, np.nan], np.float32)])
+    b = np.concatenate([synth.uniform_pm1(g, 1 << 18), _random_f32_bits(1 << 18, 57, False),
+                        F32_SPECIALS[::-1], np.array([-0.0, -1.0, 1.0], np.float32)])
+    with np.errstate(all="ignore"):
+        ref = np.maximum(a + b, np.float32(0))
+    got = oracle.add_relu_f32(a, b)
+    assert np.array_equal(got.view(np.uint32)[~np.isnan(ref)], ref.view(np.uint32)[~np.isnan(ref)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    # -0 + -0 = -0, whose ReLU is +0; 1 + -1 = +0
+    assert got.view(np.uint32)[-3] == 0 and got.view(np.uint32)[-2] == 0
+
+
+def test_saxpy_relu_exact_rational():
+    g = synth.rng(58)
+    x = np.concatenate([synth.normal01(g, 1500), _random_f32_bits(500, 59)])
+    y = np.concatenate([synth.normal01(g, 1500), _random_f32_bits(500, 60)])
+    y[:200] = -(np.float32(2.5) * x[:200])          # results near zero, both signs
+    got = oracle.saxpy_relu_f32(2.5, x, y)
+    for xi, yi, r in zip(x, y, got):
+        q = exact.f32_to_fraction(np.float32(2.5)) * exact.f32_to_fraction(xi) + \
+            exact.f32_to_fraction(yi)
+        v = exact.round_rne(q, exact.BINARY32)
+        ref = v if v > 0 else 0.0
+        if math.isinf(ref):
+            assert math.isinf(float(r)) and float(r) > 0
+            continue
+        assert exact.f32_bits(ref) == exact.f32_bits(float(r)), (xi, yi)
+
+
+def test_bias_relu_vs_numpy_broadcast():
+    g = synth.rng(61)
+    for rows, cols in ((1, 1), (3, 7), (64, 129), (1000, 4), (17, 1)):
+        x = synth.normal01(g, rows * cols)
+        bias = synth.normal01(g, cols)
+        ref = np.maximum(x.reshape(rows, cols) + bias[None, :], np.float32(0)).reshape(-1)
+        got = oracle.bias_relu_f32(x, bias, rows, cols)
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    # bias of zeros reduces to the plain ReLU (x + 0 keeps x except -0 -> +0)
+    x = synth.normal01(g, 4096)
+    assert np.array_equal(oracle.bias_relu_f32(x, np.zeros(64, np.float32), 64, 64),
+                          oracle.relu_f32(x))
+
+
 def test_copy_bitwise_including_nan_payloads():
     g = np.random.Generator(np.random.PCG64(61))
     bits = g.integers(0, 1 << 32, size=1 << 16, dtype=np.uint64).astype(np.uint32)
