@@ -15,6 +15,8 @@ Each function wraps the plain scalar C loop of the same name in ``oracle.c``
 * ``add_relu_f32(a, b)``       maximum(a + b, +0)
 * ``saxpy_relu_f32(alpha, x, y)``  maximum(fmaf(alpha, x, y), +0)
 * ``bias_relu_f32(x, bias, rows, cols)``  maximum(x[r, c] + bias[c], +0)
+* ``saxpy_f16 / saxpy_bf16(alpha, x, y)``  16-bit SAXPY via one binary32 fma
+* ``relu_f16 / relu_bf16(x)``  16-bit IEEE maximum(x, +0)
 * ``copy_f32(x)``              bitwise copy
 * ``gather_f32(x, stride)``    out[i] = x[(stride*i) mod n], bitwise
 * ``gather_index(n, stride, i)``  the input index of one gather output
@@ -53,6 +55,12 @@ def _load():
     lib.oracle_saxpy_relu_f32.restype = None
     lib.oracle_bias_relu_f32.argtypes = [vp, vp, vp, sz, sz]
     lib.oracle_bias_relu_f32.restype = None
+    for name in ("oracle_saxpy_f16", "oracle_saxpy_bf16"):
+        getattr(lib, name).argtypes = [ctypes.c_float, vp, vp, sz]
+        getattr(lib, name).restype = None
+    for name in ("oracle_relu_f16", "oracle_relu_bf16"):
+        getattr(lib, name).argtypes = [vp, vp, sz]
+        getattr(lib, name).restype = None
     for name in ("oracle_relu_f32", "oracle_copy_f32",
                  "oracle_f32_to_f16_array", "oracle_f16_to_f32_array",
                  "oracle_f32_to_bf16_array", "oracle_bf16_to_f32_array"):
@@ -169,6 +177,45 @@ def bias_relu_f32(x, bias, rows, cols):
     y = np.empty_like(x)
     lib.oracle_bias_relu_f32(_ptr(x), _ptr(bias), _ptr(y), int(rows), int(cols))
     return y
+
+
+def _saxpy16(name, alpha, x, y):
+    lib = _load()
+    _check_env(lib)
+    x = _as(x, np.uint16)
+    out = np.array(_as(y, np.uint16), copy=True)
+    if x.shape != out.shape:
+        raise ValueError("shape mismatch")
+    getattr(lib, name)(float(np.float32(alpha)), _ptr(x), _ptr(out), x.size)
+    return out
+
+
+def saxpy_f16(alpha, x, y):
+    """rne16(fmaf(alpha, widen(x), widen(y))) on binary16 bit patterns."""
+    return _saxpy16("oracle_saxpy_f16", alpha, x, y)
+
+
+def saxpy_bf16(alpha, x, y):
+    """rnebf(fmaf(alpha, widen(x), widen(y))) on bfloat16 bit patterns."""
+    return _saxpy16("oracle_saxpy_bf16", alpha, x, y)
+
+
+def _relu16(name, x):
+    lib = _load()
+    x = _as(x, np.uint16)
+    y = np.empty_like(x)
+    getattr(lib, name)(_ptr(x), _ptr(y), x.size)
+    return y
+
+
+def relu_f16(x):
+    """IEEE maximum(x, +0) on binary16 bit patterns."""
+    return _relu16("oracle_relu_f16", x)
+
+
+def relu_bf16(x):
+    """IEEE maximum(x, +0) on bfloat16 bit patterns."""
+    return _relu16("oracle_relu_bf16", x)
 
 
 def relu_f32(x):

@@ -245,6 +245,39 @@ void oracle_bias_relu_f32(const float *x, const float *bias, float *y, size_t ro
             y[r * cols + c] = relu1(x[r * cols + c] + bias[c]);
 }
 
+/* SAXPY in place on binary16 / bfloat16 data: widen x and y exactly, one
+ * fused multiply-add in binary32 with a binary32 alpha, round the result to
+ * the 16-bit format nearest-even (the same rule as the 16-bit add). */
+void oracle_saxpy_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        y[i] = oracle_f32_to_f16(fmaf(alpha, oracle_f16_to_f32(x[i]), oracle_f16_to_f32(y[i])));
+}
+
+void oracle_saxpy_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i)
+        y[i] = oracle_f32_to_bf16(fmaf(alpha, oracle_bf16_to_f32(x[i]), oracle_bf16_to_f32(y[i])));
+}
+
+/* ReLU on binary16 / bfloat16 data: IEEE maximum(x, +0) is x itself (a
+ * positive value or a NaN, bits unchanged) or +0; no rounding is involved. */
+void oracle_relu_f16(const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) {
+        float v = oracle_f16_to_f32(x[i]);
+        y[i] = (v > 0.0f || v != v) ? x[i] : (uint16_t)0;
+    }
+}
+
+void oracle_relu_bf16(const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) {
+        float v = oracle_bf16_to_f32(x[i]);
+        y[i] = (v > 0.0f || v != v) ? x[i] : (uint16_t)0;
+    }
+}
+
 /* Contiguous copy out[i] = in[i], moved as bit patterns so NaN payloads and
  * signalling NaNs survive.  [PerfNotes] section 3.2, coalesced copy kernel. */
 void oracle_copy_f32(const float *in, float *out, size_t n)

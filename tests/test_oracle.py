@@ -453,6 +453,67 @@ def test_bias_relu_vs_numpy_broadcast():
                           oracle.relu_f32(x))
 
 
+def _bf16_value(bits):
+    return float((np.uint32(bits) << np.uint32(16)).view(np.float32))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_saxpy16_exact_rational(fmt):
+    """One binary32 fma of the widened operands, then one rounding to the
+    16-bit format: the exact rational alpha*x + y rounded twice."""
+    g = np.random.Generator(np.random.PCG64(81 if fmt == "f16" else 82))
+    x = g.integers(0, 1 << 16, size=2500, dtype=np.uint16)
+    y = g.integers(0, 1 << 16, size=2500, dtype=np.uint16)
+    if fmt == "f16":
+        fin = ((x & 0x7C00) != 0x7C00) & ((y & 0x7C00) != 0x7C00)
+        val = lambda b: float(np.uint16(b).view(np.float16))
+        to_bits, fmt16 = exact.f16_bits, exact.BINARY16
+        fn = oracle.saxpy_f16
+    else:
+        fin = ((x & 0x7F80) != 0x7F80) & ((y & 0x7F80) != 0x7F80)
+        val = _bf16_value
+        to_bits = lambda v: exact.f32_bits(v) >> 16
+        fmt16 = exact.BFLOAT16
+        fn = oracle.saxpy_bf16
+    x, y = x[fin], y[fin]
+    for alpha in (np.float32(2.5), np.float32(-0.3), np.float32(1.0)):
+        got = fn(alpha, x, y)
+        for xi, yi, r in zip(x, y, got):
+            q = exact.f32_to_fraction(alpha) * exact.f32_to_fraction(val(xi)) + \
+                exact.f32_to_fraction(val(yi))
+            prod_neg = (math.copysign(1, float(alpha)) * math.copysign(1, val(xi))) < 0
+            both_neg = prod_neg and math.copysign(1, val(yi)) < 0
+            v32 = exact.round_rne(q, exact.BINARY32, zero_sign_negative=both_neg)
+            if math.isinf(v32):
+                ref = v32
+            else:
+                ref = exact.round_rne(exact.f32_to_fraction(v32), fmt16,
+                                      zero_sign_negative=math.copysign(1, v32) < 0)
+            assert to_bits(ref) == int(r), (fmt, alpha, hex(xi), hex(yi))
+
+
+def test_relu16_vs_library_maximum():
+    """numpy float16 and torch bfloat16 maximum agree on every input except
+    the zeros (both return -0 for maximum(-0, +0), where IEEE 754-2019 gives
+    +0) and NaN payloads (torch returns a canonical NaN): those are pinned by
+    closed forms."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    zero = (h & 0x7FFF) == 0
+    f16_nan = ((h & 0x7C00) == 0x7C00) & ((h & 0x03FF) != 0)
+    got = oracle.relu_f16(h)
+    ref = np.maximum(h.view(np.float16), np.float16(0)).view(np.uint16)
+    ok = ~zero & ~f16_nan
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.all(got[zero] == 0) and np.array_equal(got[f16_nan], h[f16_nan])
+    bf_nan = ((h & 0x7F80) == 0x7F80) & ((h & 0x007F) != 0)
+    got = oracle.relu_bf16(h)
+    t = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16)
+    ref = torch.maximum(t, torch.zeros_like(t)).view(torch.int16).numpy().view(np.uint16)
+    ok = ~zero & ~bf_nan
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.all(got[zero] == 0) and np.array_equal(got[bf_nan], h[bf_nan])
+
+
 def test_copy_bitwise_including_nan_payloads():
     g = np.random.Generator(np.random.PCG64(61))
     bits = g.integers(0, 1 << 32, size=1 << 16, dtype=np.uint64).astype(np.uint32)
