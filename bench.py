@@ -44,15 +44,23 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 
 # Algorithmic bytes per element: each input element read once, each output
 # element written once.  The gather counts logical bytes (read 4 + write 4).
+# The fused chains count what they move: add+ReLU and SAXPY+ReLU 12, bias+ReLU
+# 8 (x read, y written) plus the bias row once.
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
-                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8}
+                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
+                  "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
+                  "relu_f16": 4, "relu_bf16": 4}
 DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f32",
-         "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32"}
+         "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32", "add_relu_f32": "f32",
+         "saxpy_relu_f32": "f32", "bias_relu_f32": "f32", "saxpy_f16": "f16",
+         "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16"}
+# The unfused sequence each fused chain replaces, timed beside it.
+UNFUSED = {"add_relu_f32": ("add_f32", "relu_f32"), "saxpy_relu_f32": ("saxpy_f32", "relu_f32")}
 MALL_BYTES = 256 * 2 ** 20
 
 
-def algorithmic_bytes(op: str, n: int) -> int:
-    return BYTES_PER_ELEM[op] * n
+def algorithmic_bytes(op: str, n: int, cols: int = 0) -> int:
+    return BYTES_PER_ELEM[op] * n + (4 * cols if op == "bias_relu_f32" else 0)
 
 
 def kernel_source_hash() -> str:
@@ -75,7 +83,16 @@ class Prepared:
         offs = w.offsets
         s = stream.cuda_stream
         self.stream = s
-        if w.op in ("add_f32", "add_f16", "add_bf16"):
+        self.unfused = None
+        if w.op == "bias_relu_f32":
+            x, kx = upload(self.inp["x"], offs.get("x", 0))
+            bias, kb = upload(self.inp["bias"], 0)
+            y, ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
+            self.keep += [kx, kb, ky]
+            rows = w.n // w.cols
+            self.launch = lambda: ew.ew_bias_relu_f32(x, bias, y, rows, w.cols, stream=s)
+            self.out, self.ptrs = y, (y, x, None)
+        elif w.op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
             a, ka = upload(self.inp["a"], offs.get("a", 0))
             b, kb = upload(self.inp["b"], offs.get("b", 0))
             c, kc = upload(np.zeros(w.n, self.inp["a"].dtype), offs.get("c", 0))
@@ -83,18 +100,30 @@ class Prepared:
             fn = getattr(ew, "ew_" + w.op)
             self.launch = lambda: fn(a, b, c, stream=s)
             self.out, self.ptrs = c, (c, a, b)
-        elif w.op == "saxpy_f32":
+            if w.op == "add_relu_f32":
+                def unfused():
+                    ew.ew_add_f32(a, b, c, stream=s)
+                    ew.ew_relu_f32(c, c, stream=s)
+                self.unfused = unfused
+        elif w.op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
             x, kx = upload(self.inp["x"], offs.get("x", 0))
             y, ky = upload(self.inp["y"], offs.get("y", 0))
             self.keep += [kx, ky]
-            self.launch = lambda: ew.ew_saxpy_f32(w.alpha, x, y, stream=s)
+            fn = getattr(ew, "ew_" + w.op)
+            self.launch = lambda: fn(w.alpha, x, y, stream=s)
             self.out, self.ptrs = y, (y, x, y)
+            if w.op == "saxpy_relu_f32":
+                def unfused():
+                    ew.ew_saxpy_f32(w.alpha, x, y, stream=s)
+                    ew.ew_relu_f32(y, y, stream=s)
+                self.unfused = unfused
         else:
             x, kx = upload(self.inp["x"], offs.get("x", 0))
-            y, ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
+            y, ky = upload(np.zeros(w.n, self.inp["x"].dtype), offs.get("y", 0))
             self.keep += [kx, ky]
-            if w.op == "relu_f32":
-                self.launch = lambda: ew.ew_relu_f32(x, y, stream=s)
+            if w.op in ("relu_f32", "relu_f16", "relu_bf16"):
+                fn = getattr(ew, "ew_" + w.op)
+                self.launch = lambda: fn(x, y, stream=s)
             elif w.op == "copy_f32":
                 self.launch = lambda: ew.ew_copy_f32(x, y, stream=s)
             else:
@@ -159,10 +188,12 @@ def cpu_baseline_leg(w, inp, got, target_s):
     from tests.gpu_util import mismatches
 
     def run(d):
-        if w.op in ("add_f32", "add_f16", "add_bf16"):
+        if w.op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
             return getattr(oracle, w.op)(d["a"], d["b"])
-        if w.op == "saxpy_f32":
-            return oracle.saxpy_f32(w.alpha, d["x"], d["y"])
+        if w.op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
+            return getattr(oracle, w.op)(w.alpha, d["x"], d["y"])
+        if w.op == "bias_relu_f32":
+            return oracle.bias_relu_f32(d["x"], d["bias"], d["x"].size // w.cols, w.cols)
         if w.op == "gather_f32":
             return oracle.gather_f32(d["x"], w.stride)
         return getattr(oracle, w.op)(d["x"])
@@ -177,7 +208,7 @@ def cpu_baseline_leg(w, inp, got, target_s):
         sample = f"one full pass over all {w.n} elements ({full_s:.2f} s)"
     else:
         m = min(w.n, 1 << 26)
-        small = synth.make_inputs(w.op, m, w.seed, w.dist)
+        small = synth.make_inputs(w.op, m, w.seed, w.dist, w.cols)
         run(small)                                   # warm-up, first touch
         reps, t0 = 0, time.perf_counter()
         while True:
@@ -240,7 +271,7 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     del got
     if bad:
         return res, prep, None
-    nbytes = algorithmic_bytes(w.op, w.n)
+    nbytes = algorithmic_bytes(w.op, w.n, w.cols)
     footprint = nbytes if w.op != "gather_f32" else 8 * w.n
     cold = footprint <= 2 * MALL_BYTES
     flush = (lambda: flush_buf.fill_(1)) if cold else None
@@ -252,6 +283,10 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     if cold:
         warm_ms = time_launches(torch, prep.launch, stream, steps, 2)
         res["warm_gbs"] = round(nbytes / (warm_ms / 1e3) / 1e9, 1)
+    if prep.unfused is not None:
+        un_ms = time_launches(torch, prep.unfused, stream, steps, warmup, flush=flush)
+        res["unfused"] = {"ops": list(UNFUSED[w.op]), "ms": round(un_ms, 5),
+                          "speedup_of_fused": round(un_ms / ms, 3)}
     return res, prep, ms
 
 

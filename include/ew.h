@@ -13,6 +13,7 @@
  *   [Puzzle31]  Mojo GPU Puzzles, "Puzzle 31: occupancy optimisation"
  *               (puzzles.modular.com)
  *   [PerfNotes] GPU-performance lecture notes (cyqw.cn/news/898472)
+ *   [GEMM-9.3]  "9.3 project: GEMM optimisation step by step" (amittech.dev)
  *
  * Conventions shared by every operation
  * -------------------------------------
@@ -122,6 +123,55 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* SAXPY and ReLU on 16-bit data                                             */
+/* ------------------------------------------------------------------------ */
+/* The operator template of [EwOps] section 二 (only the middle operation
+ * changes) applied to the 16-bit formats of [HyperAI] Stage 2.  Data are raw
+ * uint16_t bit patterns, pointers 2-byte aligned, 8 lanes per 16-byte vector. */
+
+/* In place: y[i] = rne16(fma(alpha, widen(x[i]), widen(y[i]))): x and y are
+ * widened exactly, one binary32 fused multiply-add with the binary32 alpha,
+ * then one round-to-nearest-even to binary16.  x may equal y. */
+ew_status_t ew_saxpy_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                         hipStream_t stream);
+
+/* The same for bfloat16. */
+ew_status_t ew_saxpy_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                          hipStream_t stream);
+
+/* y[i] = maximum(x[i], +0) on binary16 / bfloat16: x's bits when x > 0 or x
+ * is a NaN, else +0 (no rounding).  y may equal x. */
+ew_status_t ew_relu_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
+ew_status_t ew_relu_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Fused chains: one pass over memory instead of two                         */
+/* ------------------------------------------------------------------------ */
+/* An epilogue fused into the producing kernel saves a full pass through HBM
+ * ([GEMM-9.3] "what comes next": bias and ReLU inside the same kernel;
+ * [PerfNotes] 5.3: fusion raises the arithmetic intensity of memory-bound
+ * work).  Each result is rounded exactly as the unfused sequence would round
+ * it, so the fused and unfused paths agree bit for bit. */
+
+/* c[i] = maximum(a[i] + b[i], +0): the binary32 sum, then the ReLU of
+ * ew_relu_f32.  12 bytes per element, where ew_add_f32 followed by
+ * ew_relu_f32 moves 20.  Pointers 4-byte aligned; c may equal a or b. */
+ew_status_t ew_add_relu_f32(const float *a, const float *b, float *c, size_t n,
+                            hipStream_t stream);
+
+/* In place: y[i] = maximum(fma(alpha, x[i], y[i]), +0).  x may equal y. */
+ew_status_t ew_saxpy_relu_f32(float alpha, const float *x, float *y, size_t n,
+                              hipStream_t stream);
+
+/* y[r*cols + c] = maximum(x[r*cols + c] + bias[c], +0) for a row-major
+ * rows x cols matrix: the bias row is broadcast down the rows (a bias-and-
+ * activation epilogue).  x, y: rows*cols elements (y may equal x); bias: cols
+ * elements, must not overlap y.  rows or cols 0 -> EW_OK.  Errors as for the
+ * other operations; the bias pointer is checked after x and y. */
+ew_status_t ew_bias_relu_f32(const float *x, const float *bias, float *y,
+                             size_t rows, size_t cols, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Status, launch configuration and planning                                */
 /* ------------------------------------------------------------------------ */
 
@@ -136,7 +186,9 @@ int ew_last_hip_error(void);
 int ew_abi_version(void);
 
 /* Launch configuration, per operation name ("add_f32", "add_f16",
- * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32") and size
+ * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
+ * "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16",
+ * "saxpy_bf16", "relu_f16", "relu_bf16") and size
  * class: a row applies to every n >= min_n up to the next row's min_n.  The
  * grid is min(blocks_per_cu * CU count, number of tiles), where a tile is
  * block * unroll 16-byte vectors; each block walks tiles with a grid stride

@@ -18,7 +18,9 @@ import os
 __all__ = [
     "EwError", "EwPlan", "OPS", "library_path",
     "ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
-    "ew_copy_f32", "ew_gather_f32", "ew_status_string", "ew_last_hip_error",
+    "ew_copy_f32", "ew_gather_f32", "ew_add_relu_f32", "ew_saxpy_relu_f32",
+    "ew_bias_relu_f32", "ew_saxpy_f16", "ew_saxpy_bf16", "ew_relu_f16", "ew_relu_bf16",
+    "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
     "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan", "ew_make_gather_plan",
 ]
@@ -27,7 +29,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libew.so")
 LAUNCH_TABLE = os.path.join(_PKG, "launch_table.txt")
 
-OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32")
+OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
+       "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16", "saxpy_bf16",
+       "relu_f16", "relu_bf16")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -77,6 +81,13 @@ _c = {
     "ew_relu_f32": _proto("ew_relu_f32", _int, _vp, _vp, _sz, _vp),
     "ew_copy_f32": _proto("ew_copy_f32", _int, _vp, _vp, _sz, _vp),
     "ew_gather_f32": _proto("ew_gather_f32", _int, _vp, _vp, _sz, _sz, _vp),
+    "ew_add_relu_f32": _proto("ew_add_relu_f32", _int, _vp, _vp, _vp, _sz, _vp),
+    "ew_saxpy_relu_f32": _proto("ew_saxpy_relu_f32", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
+    "ew_bias_relu_f32": _proto("ew_bias_relu_f32", _int, _vp, _vp, _vp, _sz, _sz, _vp),
+    "ew_saxpy_f16": _proto("ew_saxpy_f16", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
+    "ew_saxpy_bf16": _proto("ew_saxpy_bf16", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
+    "ew_relu_f16": _proto("ew_relu_f16", _int, _vp, _vp, _sz, _vp),
+    "ew_relu_bf16": _proto("ew_relu_bf16", _int, _vp, _vp, _sz, _vp),
     "ew_status_string": _proto("ew_status_string", ctypes.c_char_p, _int),
     "ew_last_hip_error": _proto("ew_last_hip_error", _int),
     "ew_abi_version": _proto("ew_abi_version", _int),
@@ -177,6 +188,52 @@ def ew_gather_f32(src, out, stride, n=None, stream=None):
     """out[i] = src[(stride * i) mod n], bitwise."""
     _check(_c["ew_gather_f32"](_addr(src), _addr(out), _numel(out, n), int(stride),
                                _stream(out, stream)), "ew_gather_f32")
+
+
+def ew_add_relu_f32(a, b, c, n=None, stream=None):
+    """c = maximum(a + b, +0) in one pass."""
+    _check(_c["ew_add_relu_f32"](_addr(a), _addr(b), _addr(c), _numel(c, n),
+                                 _stream(c, stream)), "ew_add_relu_f32")
+
+
+def ew_saxpy_relu_f32(alpha, x, y, n=None, stream=None):
+    """y = maximum(fma(alpha, x, y), +0) in place."""
+    _check(_c["ew_saxpy_relu_f32"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+                                   _stream(y, stream)), "ew_saxpy_relu_f32")
+
+
+def ew_bias_relu_f32(x, bias, y, rows=None, cols=None, stream=None):
+    """y[r, c] = maximum(x[r, c] + bias[c], +0); rows/cols default to y's 2-D shape."""
+    if rows is None or cols is None:
+        if isinstance(y, int):
+            raise ValueError("rows and cols are required when buffers are raw pointers")
+        rows, cols = y.shape
+    _check(_c["ew_bias_relu_f32"](_addr(x), _addr(bias), _addr(y), int(rows), int(cols),
+                                  _stream(y, stream)), "ew_bias_relu_f32")
+
+
+def ew_saxpy_f16(alpha, x, y, n=None, stream=None):
+    """y = rne16(fma(alpha, x, y)) in place on binary16 data."""
+    _check(_c["ew_saxpy_f16"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+                              _stream(y, stream)), "ew_saxpy_f16")
+
+
+def ew_saxpy_bf16(alpha, x, y, n=None, stream=None):
+    """y = rnebf(fma(alpha, x, y)) in place on bfloat16 data."""
+    _check(_c["ew_saxpy_bf16"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+                               _stream(y, stream)), "ew_saxpy_bf16")
+
+
+def ew_relu_f16(x, y, n=None, stream=None):
+    """y = maximum(x, +0) on binary16 data."""
+    _check(_c["ew_relu_f16"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
+           "ew_relu_f16")
+
+
+def ew_relu_bf16(x, y, n=None, stream=None):
+    """y = maximum(x, +0) on bfloat16 data."""
+    _check(_c["ew_relu_bf16"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
+           "ew_relu_bf16")
 
 
 def ew_status_string(status: int) -> str:

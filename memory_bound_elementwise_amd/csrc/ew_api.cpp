@@ -19,7 +19,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 4;
 
 struct OpInfo {
     const char *name;
@@ -36,6 +36,13 @@ constexpr OpInfo kOps[kOpCount] = {
     {"relu_f32", 4, 1, true},
     {"copy_f32", 4, 1, true},
     {"gather_f32", 4, 1, false},
+    {"add_relu_f32", 4, 2, true},
+    {"saxpy_relu_f32", 4, 2, true},
+    {"bias_relu_f32", 4, 1, true},
+    {"saxpy_f16", 2, 2, true},
+    {"saxpy_bf16", 2, 2, true},
+    {"relu_f16", 2, 1, true},
+    {"relu_bf16", 2, 1, true},
 };
 
 int op_from_name(const char *name)
@@ -79,6 +86,20 @@ constexpr DefaultRow kDefaults[] = {
     {kOpCopyF32, {size_t(1) << 22, 512, 1024, 1}},
     {kOpGatherF32, {0, 128, 4, 1}},
     {kOpGatherF32, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddReluF32, {0, 512, 1024, 2}},
+    {kOpAddReluF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpSaxpyReluF32, {0, 512, 4, 2}},
+    {kOpSaxpyReluF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpBiasReluF32, {0, 1024, 4, 2}},
+    {kOpBiasReluF32, {size_t(1) << 22, 128, 1024, 2}},
+    {kOpSaxpyF16, {0, 256, 1024, 4}},
+    {kOpSaxpyF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSaxpyBF16, {0, 128, 2, 2}},
+    {kOpSaxpyBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpReluF16, {0, 1024, 2, 1}},
+    {kOpReluF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpReluBF16, {0, 512, 8, 2}},
+    {kOpReluBF16, {size_t(1) << 22, 512, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
@@ -401,6 +422,70 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride, 
     Launch l{};
     gather_plan(in, out, n, stride, cus, &g, &l);
     const hipError_t e = launch_gather(g, l, s);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
+}
+
+ew_status_t ew_add_relu_f32(const float *a, const float *b, float *c, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAddReluF32, c, a, b, n, 0.0f, s);
+}
+
+ew_status_t ew_saxpy_relu_f32(float alpha, const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSaxpyReluF32, y, x, y, n, alpha, s);
+}
+
+ew_status_t ew_saxpy_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSaxpyF16, y, x, y, n, alpha, s);
+}
+
+ew_status_t ew_saxpy_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSaxpyBF16, y, x, y, n, alpha, s);
+}
+
+ew_status_t ew_relu_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpReluF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_relu_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpReluBF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_bias_relu_f32(const float *x, const float *bias, float *y, size_t rows,
+                             size_t cols, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return EW_OK;
+    if (!bias || rows > SIZE_MAX / cols) return EW_ERR_INVALID_ARG;
+    const size_t n = rows * cols;
+    ew_status_t st = validate(kOpBiasReluF32, y, x, nullptr, n);
+    if (st != EW_OK) return st;
+    const uintptr_t bp = reinterpret_cast<uintptr_t>(bias);
+    if (cols > SIZE_MAX / 4 || bp > UINTPTR_MAX - cols * 4) return EW_ERR_INVALID_ARG;
+    if (bp % 4 != 0) return EW_ERR_MISALIGNED;
+    const uintptr_t yp = reinterpret_cast<uintptr_t>(y);
+    if (bp < yp + n * 4 && yp < bp + cols * 4) return EW_ERR_OVERLAP;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    const Plan p = make_plan(kOpBiasReluF32, y, x, nullptr, n, cus);
+    BiasArgs a{};
+    a.x = x;
+    a.bias = bias;
+    a.y = y;
+    a.cols = cols;
+    a.head = p.head;
+    a.vectors = p.vectors;
+    a.tail = p.tail;
+    a.tiles = p.tiles;
+    const uint64_t nthr = (uint64_t)p.launch.block;
+    a.step_vec = (4 * nthr) % cols;
+    a.step_tile = mulmod_host((4 * nthr * (uint64_t)p.launch.unroll) % cols,
+                              (uint64_t)p.launch.grid % cols, cols);
+    const hipError_t e = launch_bias_relu(a, p.co[0], p.launch, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 

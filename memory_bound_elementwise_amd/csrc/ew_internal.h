@@ -16,6 +16,13 @@ enum OpId : int {
     kOpReluF32,
     kOpCopyF32,
     kOpGatherF32,
+    kOpAddReluF32,
+    kOpSaxpyReluF32,
+    kOpBiasReluF32,
+    kOpSaxpyF16,
+    kOpSaxpyBF16,
+    kOpReluF16,
+    kOpReluBF16,
     kOpCount
 };
 
@@ -55,6 +62,21 @@ struct GatherArgs {
     int wide;            // 1 if stride * (n - 1) can exceed 2^64 - 1
 };
 
+// Bias + ReLU over a row-major rows x cols matrix (n = rows * cols): the
+// column index of element i is i mod cols, walked incrementally per lane.
+struct BiasArgs {
+    const float *x;
+    const float *bias;
+    float *y;
+    uint64_t cols;
+    uint64_t head;
+    uint64_t vectors;
+    uint64_t tail;
+    uint64_t tiles;
+    uint64_t step_vec;   // (4 * blockDim) mod cols: next unrolled vector
+    uint64_t step_tile;  // (4 * blockDim * unroll * gridDim) mod cols: next tile
+};
+
 struct Launch {
     int block;
     int grid;
@@ -68,5 +90,9 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
                          hipStream_t stream);
+
+// co: x's body start is 16-byte aligned (it is read with aligned loads).
+hipError_t launch_bias_relu(const BiasArgs &args, bool co, const Launch &launch,
+                            hipStream_t stream);
 
 }  // namespace ew

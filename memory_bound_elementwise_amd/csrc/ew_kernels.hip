@@ -179,6 +179,105 @@ struct OpReluF32 {
     }
 };
 
+// c = maximum(a + b, +0): the add and the ReLU fused into one pass over
+// memory (12 bytes per element instead of 12 + 8 for two kernels).
+struct OpAddReluF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 2;
+    __device__ static u32x4 vec(u32x4 a, u32x4 b, float)
+    {
+        f32x4 s = __builtin_bit_cast(f32x4, a) + __builtin_bit_cast(f32x4, b), r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = OpReluF32::relu(s[j]);
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem a, Elem b, float)
+    {
+        return __builtin_bit_cast(
+            Elem, OpReluF32::relu(__builtin_bit_cast(float, a) + __builtin_bit_cast(float, b)));
+    }
+};
+
+// y = maximum(fma(alpha, x, y), +0), in place.
+struct OpSaxpyReluF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 2;
+    __device__ static u32x4 vec(u32x4 x, u32x4 y, float alpha)
+    {
+        f32x4 xf = __builtin_bit_cast(f32x4, x), yf = __builtin_bit_cast(f32x4, y), r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = OpReluF32::relu(__builtin_fmaf(alpha, xf[j], yf[j]));
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem x, Elem y, float alpha)
+    {
+        return __builtin_bit_cast(Elem, OpReluF32::relu(__builtin_fmaf(
+                                            alpha, __builtin_bit_cast(float, x),
+                                            __builtin_bit_cast(float, y))));
+    }
+};
+
+// SAXPY on 16-bit data: widen x and y exactly, one binary32 fused
+// multiply-add with the binary32 alpha, round to the 16-bit format RNE.
+// The binary32 result is pinned in a register before the narrowing: left
+// alone, the compiler fuses fma + narrow into v_fma_mixlo_f16, which rounds
+// the exact product-sum once, straight to binary16 -- a different result
+// whenever the binary32 rounding step changes the binary16 tie decision.
+template <typename H>
+struct OpSaxpy16 {
+    using Elem = uint16_t;
+    static constexpr int kInputs = 2;
+    typedef H h8 __attribute__((ext_vector_type(8)));
+    __device__ static float fma32(float alpha, float x, float y)
+    {
+        float r = __builtin_fmaf(alpha, x, y);
+        asm("" : "+v"(r));
+        return r;
+    }
+    __device__ static u32x4 vec(u32x4 x, u32x4 y, float alpha)
+    {
+        const f32x8 xf = __builtin_convertvector(__builtin_bit_cast(h8, x), f32x8);
+        const f32x8 yf = __builtin_convertvector(__builtin_bit_cast(h8, y), f32x8);
+        f32x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = fma32(alpha, xf[j], yf[j]);
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(r, h8));
+    }
+    __device__ static Elem one(Elem x, Elem y, float alpha)
+    {
+        const float r = fma32(alpha, (float)__builtin_bit_cast(H, x), (float)__builtin_bit_cast(H, y));
+        return __builtin_bit_cast(Elem, (H)r);
+    }
+};
+using OpSaxpyF16 = OpSaxpy16<_Float16>;
+using OpSaxpyBF16 = OpSaxpy16<__bf16>;
+
+// ReLU on 16-bit data: keep x's bits when x > 0 or x is NaN, else +0.  The
+// comparison is made on the exactly widened value; no rounding happens.
+template <typename H>
+struct OpRelu16 {
+    using Elem = uint16_t;
+    static constexpr int kInputs = 1;
+    typedef H h8 __attribute__((ext_vector_type(8)));
+    typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+    __device__ static u32x4 vec(u32x4 x, u32x4, float)
+    {
+        const f32x8 xf = __builtin_convertvector(__builtin_bit_cast(h8, x), f32x8);
+        const u16x8 xb = __builtin_bit_cast(u16x8, x);
+        u16x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = (xf[j] > 0.0f || xf[j] != xf[j]) ? xb[j] : (uint16_t)0;
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem x, Elem, float)
+    {
+        const float v = (float)__builtin_bit_cast(H, x);
+        return (v > 0.0f || v != v) ? x : (Elem)0;
+    }
+};
+using OpReluF16 = OpRelu16<_Float16>;
+using OpReluBF16 = OpRelu16<__bf16>;
+
 // out = in, bits unchanged.
 struct OpCopyF32 {
     using Elem = uint32_t;
@@ -378,6 +477,74 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 }
 
 // ---------------------------------------------------------------------------
+// Bias + ReLU: y[i] = maximum(x[i] + bias[i mod cols], +0)
+// ---------------------------------------------------------------------------
+
+// The streaming skeleton with a broadcast second operand: x and y stream
+// through 16-byte vectors; each lane walks the column of its vector's first
+// element incrementally (one 64-bit remainder per lane, then
+// compare-and-subtract steps precomputed on the host).  VecBias: cols is a
+// multiple of 4 and the body starts at a row start's alignment (head == 0),
+// so a vector's four columns are contiguous and never wrap; the bias is then
+// read as one 16-byte load.  Otherwise four 4-byte loads.  Bias loads use
+// the default cache policy: the bias row is reused by every row.
+template <int U, bool Co, bool VecBias>
+__global__ void __launch_bounds__(1024) ew_bias_relu_kernel(BiasArgs a)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nthr = blockDim.x;
+    const uint64_t cols = a.cols;
+
+    if (blockIdx.x == 0 && tid < a.head + a.tail) {
+        const uint64_t e = tid < a.head ? (uint64_t)tid : a.head + a.vectors * 4 + (tid - a.head);
+        a.y[e] = OpReluF32::relu(a.x[e] + a.bias[e % cols]);
+    }
+
+    uint64_t t = blockIdx.x;
+    if (t >= a.tiles) return;
+    const char *x = reinterpret_cast<const char *>(a.x + a.head);
+    char *y = reinterpret_cast<char *>(a.y + a.head);
+    const uint64_t tile_vecs = nthr * U;
+    uint64_t ct = (a.head + 4 * (t * tile_vecs + tid)) % cols;   // column of the first element
+
+    for (; t < a.tiles; t += gridDim.x) {
+        const uint64_t v0 = t * tile_vecs + tid;
+        u32x4 xv[U];
+        f32x4 bv[U];
+        uint64_t c = ct;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool live = v0 + u * nthr < a.vectors;
+            xv[u] = live ? load16<Co, 4>(x + (v0 + u * nthr) * 16) : u32x4{0, 0, 0, 0};
+            if constexpr (VecBias) {
+                bv[u] = live ? __builtin_bit_cast(
+                                   f32x4, *reinterpret_cast<const u32x4_a4 *>(a.bias + c))
+                             : f32x4{0, 0, 0, 0};
+            } else {
+                uint64_t cc = c;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    bv[u][k] = live ? a.bias[cc] : 0.0f;
+                    cc = cc + 1 == cols ? 0 : cc + 1;
+                }
+            }
+            c = add_mod(c, a.step_vec, cols);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t v = v0 + u * nthr;
+            if (v < a.vectors) {
+                f32x4 s = __builtin_bit_cast(f32x4, xv[u]) + bv[u], r;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) r[k] = OpReluF32::relu(s[k]);
+                store16(y + v * 16, __builtin_bit_cast(u32x4, r));
+            }
+        }
+        ct = add_mod(ct, a.step_tile, cols);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
 
@@ -432,6 +599,12 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
     case kOpSaxpyF32: return launch_op<OpSaxpyF32>(args, co0, co1, launch, stream);
     case kOpReluF32: return launch_op<OpReluF32>(args, co0, co1, launch, stream);
     case kOpCopyF32: return launch_op<OpCopyF32>(args, co0, co1, launch, stream);
+    case kOpAddReluF32: return launch_op<OpAddReluF32>(args, co0, co1, launch, stream);
+    case kOpSaxpyReluF32: return launch_op<OpSaxpyReluF32>(args, co0, co1, launch, stream);
+    case kOpSaxpyF16: return launch_op<OpSaxpyF16>(args, co0, co1, launch, stream);
+    case kOpSaxpyBF16: return launch_op<OpSaxpyBF16>(args, co0, co1, launch, stream);
+    case kOpReluF16: return launch_op<OpReluF16>(args, co0, co1, launch, stream);
+    case kOpReluBF16: return launch_op<OpReluBF16>(args, co0, co1, launch, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -445,6 +618,28 @@ const void *gather2_fn()
 }
 
 }  // namespace
+
+hipError_t launch_bias_relu(const BiasArgs &args, bool co, const Launch &l, hipStream_t s)
+{
+    BiasArgs a = args;
+    void *kargs[] = {&a};
+    const void *fn = nullptr;
+    const bool vb = args.cols % 4 == 0 && args.head == 0;
+#define EW_BIAS_FN(U)                                                                      \
+    (vb ? (co ? reinterpret_cast<const void *>(&ew_bias_relu_kernel<U, true, true>)         \
+              : reinterpret_cast<const void *>(&ew_bias_relu_kernel<U, false, true>))       \
+        : (co ? reinterpret_cast<const void *>(&ew_bias_relu_kernel<U, true, false>)        \
+              : reinterpret_cast<const void *>(&ew_bias_relu_kernel<U, false, false>)))
+    switch (l.unroll) {
+    case 1: fn = EW_BIAS_FN(1); break;
+    case 2: fn = EW_BIAS_FN(2); break;
+    case 4: fn = EW_BIAS_FN(4); break;
+    case 8: fn = EW_BIAS_FN(8); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef EW_BIAS_FN
+    return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
+}
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
 {

@@ -34,7 +34,10 @@ UNROLLS = (1, 2, 4)
 LARGE_MIN_N = 1 << 22
 SIZES = {"small": 1 << 20, "large": 1 << 28}
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
-                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8}
+                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
+                  "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
+                  "relu_f16": 4, "relu_bf16": 4}
+BIAS_COLS = 4096
 
 
 # Element offset of input A for the large fp32 add: the misaligned-input
@@ -48,11 +51,18 @@ def _launcher(op, n, bufs, stream, off_a=0):
     a, b, c = bufs
     s = stream.cuda_stream
     pa = a.data_ptr() + 4 * off_a
-    if op in ("add_f32", "add_f16", "add_bf16"):
+    if op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         fn = getattr(ew, "ew_" + op)
         return lambda: fn(pa, b.data_ptr(), c.data_ptr(), n=n, stream=s)
-    if op == "saxpy_f32":
-        return lambda: ew.ew_saxpy_f32(0.5, pa, c.data_ptr(), n=n, stream=s)
+    if op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
+        fn = getattr(ew, "ew_" + op)
+        return lambda: fn(0.5, pa, c.data_ptr(), n=n, stream=s)
+    if op in ("relu_f16", "relu_bf16"):
+        fn = getattr(ew, "ew_" + op)
+        return lambda: fn(pa, c.data_ptr(), n=n, stream=s)
+    if op == "bias_relu_f32":
+        return lambda: ew.ew_bias_relu_f32(pa, b.data_ptr(), c.data_ptr(), n // BIAS_COLS,
+                                           BIAS_COLS, stream=s)
     if op == "relu_f32":
         return lambda: ew.ew_relu_f32(pa, c.data_ptr(), n=n, stream=s)
     if op == "copy_f32":

@@ -70,6 +70,7 @@ class Workload:
     offsets: dict = field(default_factory=dict)
     alpha: float = 0.0    # saxpy only
     stride: int = 0       # gather only
+    cols: int = 0         # bias_relu only: row length (n = rows * cols)
     description: str = ""
 
 
@@ -109,6 +110,29 @@ WORKLOADS = {
         "gather_f32_2e26_s3", "gather_f32", 1 << 26, 107, "uniform", stride=3,
         description="fp32 strided gather out[i]=in[(3*i) mod n], n=2^26 (gcd 1: a permutation "
                     "read with stride 3)"),
+    "fused_add_relu_f32_2e28": _w(
+        "fused_add_relu_f32_2e28", "add_relu_f32", 1 << 28, 108, "normal",
+        description="fp32 C=max(A+B,0) in one pass, n=2^28, A,B normal(0,1)"),
+    "fused_saxpy_relu_f32_2e28": _w(
+        "fused_saxpy_relu_f32_2e28", "saxpy_relu_f32", 1 << 28, 109, "normal", alpha=2.5,
+        description="fp32 y=max(2.5*x+y,0) in place, n=2^28, x,y normal(0,1)"),
+    "fused_bias_relu_f32_65536x4096": _w(
+        "fused_bias_relu_f32_65536x4096", "bias_relu_f32", 1 << 28, 110, "normal", cols=4096,
+        description="fp32 y=max(x+bias[col],0), 65536 x 4096 row-major, x,bias normal(0,1)"),
+    "saxpy_f16_2e28": _w(
+        "saxpy_f16_2e28", "saxpy_f16", 1 << 28, 111, "normal", alpha=2.5,
+        description="fp16 SAXPY in place y = 2.5*x + y (fp32 fma, RNE to fp16), n=2^28, "
+                    "x,y normal(0,1) cast RNE"),
+    "saxpy_bf16_2e28": _w(
+        "saxpy_bf16_2e28", "saxpy_bf16", 1 << 28, 112, "normal", alpha=2.5,
+        description="bf16 SAXPY in place y = 2.5*x + y (fp32 fma, RNE to bf16), n=2^28, "
+                    "x,y normal(0,1) cast RNE"),
+    "relu_f16_2e28": _w(
+        "relu_f16_2e28", "relu_f16", 1 << 28, 113, "normal",
+        description="fp16 ReLU y=max(x,0), n=2^28, x normal(0,1) cast RNE"),
+    "relu_bf16_2e28": _w(
+        "relu_bf16_2e28", "relu_bf16", 1 << 28, 114, "normal",
+        description="bf16 ReLU y=max(x,0), n=2^28, x normal(0,1) cast RNE"),
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),
@@ -118,29 +142,36 @@ WORKLOADS = {
 OP_INPUTS = {
     "add_f32": ("a", "b"), "add_f16": ("a", "b"), "add_bf16": ("a", "b"),
     "saxpy_f32": ("x", "y"), "relu_f32": ("x",), "copy_f32": ("x",),
-    "gather_f32": ("x",),
+    "gather_f32": ("x",), "add_relu_f32": ("a", "b"), "saxpy_relu_f32": ("x", "y"),
+    "bias_relu_f32": ("x", "bias"), "saxpy_f16": ("x", "y"), "saxpy_bf16": ("x", "y"),
+    "relu_f16": ("x",), "relu_bf16": ("x",),
 }
 OP_DTYPE = {
     "add_f32": np.float32, "add_f16": np.uint16, "add_bf16": np.uint16,
     "saxpy_f32": np.float32, "relu_f32": np.float32, "copy_f32": np.float32,
-    "gather_f32": np.float32,
+    "gather_f32": np.float32, "add_relu_f32": np.float32, "saxpy_relu_f32": np.float32,
+    "bias_relu_f32": np.float32, "saxpy_f16": np.uint16, "saxpy_bf16": np.uint16,
+    "relu_f16": np.uint16, "relu_bf16": np.uint16,
 }
+F16_OPS = ("add_f16", "saxpy_f16", "relu_f16")
+BF16_OPS = ("add_bf16", "saxpy_bf16", "relu_bf16")
 
 
-def make_inputs(op: str, n: int, seed: int, dist: str = "uniform") -> dict:
-    """Draw the inputs of ``op`` (numpy arrays keyed by role) for n elements."""
+def make_inputs(op: str, n: int, seed: int, dist: str = "uniform", cols: int = 0) -> dict:
+    """Draw the inputs of ``op`` (numpy arrays keyed by role) for n elements
+    (the bias of bias_relu has `cols` elements)."""
     g = rng(seed)
     draw = uniform_pm1 if dist == "uniform" else normal01
     out = {}
     for role in OP_INPUTS[op]:
-        x = draw(g, n)
-        if op == "add_f16":
+        x = draw(g, cols if role == "bias" else n)
+        if op in F16_OPS:
             x = to_f16_bits(x)
-        elif op == "add_bf16":
+        elif op in BF16_OPS:
             x = to_bf16_bits(x)
         out[role] = x
     return out
 
 
 def workload_inputs(w: Workload) -> dict:
-    return make_inputs(w.op, w.n, w.seed, w.dist)
+    return make_inputs(w.op, w.n, w.seed, w.dist, w.cols)

@@ -52,7 +52,7 @@ def test_binding_names_match_the_c_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert ew.ew_abi_version() == 2
+    assert ew.ew_abi_version() == 4
     for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
                  EW_ERR_NO_DEVICE, EW_ERR_HIP):
         s = ew.ew_status_string(code)
@@ -129,6 +129,30 @@ def test_partial_overlap_is_rejected():
     # the gather forbids any overlap, exact aliasing included
     assert _status(ew.ew_gather_f32, BASE, BASE, 2, n, 0) == EW_ERR_OVERLAP
     assert _status(ew.ew_gather_f32, BASE, BASE + 4 * n - 4, 2, n, 0) == EW_ERR_OVERLAP
+
+
+def test_fused_ops_validation():
+    n = 1024
+    assert _status(ew.ew_add_relu_f32, 0, 0, 0, 0, 0) == EW_OK
+    assert _status(ew.ew_add_relu_f32, 0, BASE, BASE + MiB, n, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_add_relu_f32, BASE + 2, BASE + MiB, BASE + 2 * MiB, n, 0) == \
+        EW_ERR_MISALIGNED
+    assert _status(ew.ew_add_relu_f32, BASE, BASE + MiB, BASE + 4, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_saxpy_relu_f32, 1.0, BASE, BASE + 8, n, 0) == EW_ERR_OVERLAP
+    assert _status(ew.ew_saxpy_relu_f32, 1.0, 0, BASE, n, 0) == EW_ERR_INVALID_ARG
+    # bias + ReLU: rows or cols 0 is a no-op; null bias; rows*cols overflow;
+    # misaligned bias; bias overlapping y; x partially overlapping y
+    assert _status(ew.ew_bias_relu_f32, 0, 0, 0, 0, 16, 0) == EW_OK
+    assert _status(ew.ew_bias_relu_f32, 0, 0, 0, 16, 0, 0) == EW_OK
+    assert _status(ew.ew_bias_relu_f32, BASE, 0, BASE + MiB, 4, 4, 0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_bias_relu_f32, BASE, BASE + 8 * MiB, BASE + MiB, 1 << 40, 1 << 40,
+                   0) == EW_ERR_INVALID_ARG
+    assert _status(ew.ew_bias_relu_f32, BASE, BASE + 8 * MiB + 2, BASE + MiB, 4, 4, 0) == \
+        EW_ERR_MISALIGNED
+    assert _status(ew.ew_bias_relu_f32, BASE, BASE + MiB + 16, BASE + MiB, 4, 4, 0) == \
+        EW_ERR_OVERLAP
+    assert _status(ew.ew_bias_relu_f32, BASE + 4, BASE + 8 * MiB, BASE, 4, 4, 0) == \
+        EW_ERR_OVERLAP
 
 
 def test_adjacent_ranges_do_not_overlap_and_copy_onto_itself_is_a_no_op():

@@ -24,7 +24,15 @@ def _run(w: synth.Workload):
     es = ELEM[w.op]
     offs = w.offsets
     s = torch.cuda.current_stream().cuda_stream
-    if w.op in ("add_f32", "add_f16", "add_bf16"):
+    if w.op == "bias_relu_f32":
+        x, _kx = upload(inp["x"], offs.get("x", 0))
+        bias, _kb = upload(inp["bias"], 0)
+        y, _ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
+        ew.ew_bias_relu_f32(x, bias, y, w.n // w.cols, w.cols, stream=s)
+        torch.cuda.synchronize()
+        got = download(y, es)
+        ref = oracle.bias_relu_f32(inp["x"], inp["bias"], w.n // w.cols, w.cols)
+    elif w.op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         a, _ka = upload(inp["a"], offs.get("a", 0))
         b, _kb = upload(inp["b"], offs.get("b", 0))
         c, _kc = upload(np.zeros(w.n, inp["a"].dtype), offs.get("c", 0))
@@ -33,18 +41,18 @@ def _run(w: synth.Workload):
         got = download(c, es)
         del a, b, c, _ka, _kb, _kc
         ref = getattr(oracle, w.op)(inp["a"], inp["b"])
-    elif w.op == "saxpy_f32":
+    elif w.op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
         x, _kx = upload(inp["x"], offs.get("x", 0))
         y, _ky = upload(inp["y"], offs.get("y", 0))
-        ew.ew_saxpy_f32(w.alpha, x, y, stream=s)
+        getattr(ew, "ew_" + w.op)(w.alpha, x, y, stream=s)
         torch.cuda.synchronize()
         got = download(y, es)
-        ref = oracle.saxpy_f32(w.alpha, inp["x"], inp["y"])
+        ref = getattr(oracle, w.op)(w.alpha, inp["x"], inp["y"])
     else:
         x, _kx = upload(inp["x"], offs.get("x", 0))
-        y, _ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
-        if w.op == "relu_f32":
-            ew.ew_relu_f32(x, y, stream=s)
+        y, _ky = upload(np.zeros(w.n, inp["x"].dtype), offs.get("y", 0))
+        if w.op in ("relu_f32", "relu_f16", "relu_bf16"):
+            getattr(ew, "ew_" + w.op)(x, y, stream=s)
         elif w.op == "copy_f32":
             ew.ew_copy_f32(x, y, stream=s)
         else:

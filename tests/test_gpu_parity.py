@@ -77,12 +77,12 @@ def _pool(op, length, seed):
 
 
 def _oracle(op, ins, n, alpha=2.5, stride=2):
-    if op in ("add_f32", "add_f16", "add_bf16"):
+    if op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         return getattr(oracle, op)(ins[0], ins[1])
-    if op == "saxpy_f32":
-        return oracle.saxpy_f32(alpha, ins[0], ins[1])
-    if op == "relu_f32":
-        return oracle.relu_f32(ins[0])
+    if op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
+        return getattr(oracle, op)(alpha, ins[0], ins[1])
+    if op in ("relu_f32", "relu_f16", "relu_bf16"):
+        return getattr(oracle, op)(ins[0])
     if op == "copy_f32":
         return oracle.copy_f32(ins[0])
     return oracle.gather_f32(ins[0], stride)
@@ -90,12 +90,12 @@ def _oracle(op, ins, n, alpha=2.5, stride=2):
 
 def _call(op, out_ptr, in_ptrs, n, alpha=2.5, stride=2):
     s = torch.cuda.current_stream().cuda_stream
-    if op in ("add_f32", "add_f16", "add_bf16"):
+    if op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         getattr(ew, "ew_" + op)(in_ptrs[0], in_ptrs[1], out_ptr, n=n, stream=s)
-    elif op == "saxpy_f32":
-        ew.ew_saxpy_f32(alpha, in_ptrs[0], out_ptr, n=n, stream=s)
-    elif op == "relu_f32":
-        ew.ew_relu_f32(in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
+        getattr(ew, "ew_" + op)(alpha, in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op in ("relu_f32", "relu_f16", "relu_bf16"):
+        getattr(ew, "ew_" + op)(in_ptrs[0], out_ptr, n=n, stream=s)
     elif op == "copy_f32":
         ew.ew_copy_f32(in_ptrs[0], out_ptr, n=n, stream=s)
     else:
@@ -107,7 +107,7 @@ def _run_cases(op, cases, seed):
     one sentinel-filled arena; returns a list of failure descriptions."""
     es = ELEM[op]
     dt = NP_DTYPE[es]
-    n_in = 1 if op in ("relu_f32", "copy_f32", "gather_f32") else 2
+    n_in = 1 if op in ("relu_f32", "copy_f32", "gather_f32", "relu_f16", "relu_bf16") else 2
     max_n = max(c[0] for c in cases)
     pool_len = max_n + 32
     pools = [_pool(op, pool_len, seed + k) for k in range(n_in)]
@@ -123,7 +123,7 @@ def _run_cases(op, cases, seed):
         cursor = out_byte + n * es + GUARD
     total = -(-(cursor + 256) // 256) * 256
     host = np.full(total, SENTINEL, np.uint8)
-    if op == "saxpy_f32":   # y is updated in place: seed each output span with y
+    if op in IN_PLACE:   # y is updated in place: seed each output span with y
         for (n, off_out, offs_in, stride), ob in zip(cases, layout):
             host[ob:ob + n * es] = pools[1][offs_in[1]:offs_in[1] + n].view(np.uint8)
     arena = torch.from_numpy(host).to(DEV)
@@ -158,17 +158,21 @@ def _run_cases(op, cases, seed):
     return failures
 
 
+IN_PLACE = ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16")
+TWO_INPUT = ("add_f32", "add_f16", "add_bf16", "add_relu_f32") + IN_PLACE
+
+
 def _offset_cases(op):
     es = ELEM[op]
     vec = 16 // es
     cases = []
     for n in SIZES:
-        if op in ("add_f32", "add_f16", "add_bf16", "saxpy_f32"):
+        if op in TWO_INPUT:
             offs_b = range(vec) if es == 4 else (0, 3, 7)
             for oo in range(vec):
                 for oa in range(vec):
                     for ob in offs_b:
-                        if op == "saxpy_f32":
+                        if op in IN_PLACE:
                             ob = oo          # y is the output itself
                         cases.append((n, oo, [oa, ob], 0))
         else:
@@ -185,8 +189,12 @@ def _offset_cases(op):
     return uniq
 
 
-@pytest.mark.parametrize("op", ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32",
-                                "copy_f32", "gather_f32"])
+ALL_STREAM_OPS = ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32",
+                  "gather_f32", "add_relu_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16",
+                  "relu_f16", "relu_bf16"]
+
+
+@pytest.mark.parametrize("op", ALL_STREAM_OPS)
 def test_brute_force_small_all_offsets(op):
     print(f"[parity] brute force {op}", flush=True)
     failures = _run_cases(op, _offset_cases(op), seed=300)
@@ -234,8 +242,7 @@ LAUNCHES = [(64, 1, 1), (64, 3, 8), (256, 8, 1), (256, 8, 2), (256, 2, 4), (512,
             (1024, 1, 2), (1024, 1, 8), (128, 16, 1)]
 
 
-@pytest.mark.parametrize("op", ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32",
-                                "copy_f32", "gather_f32"])
+@pytest.mark.parametrize("op", ALL_STREAM_OPS)
 def test_every_kernel_variant_several_tiles_ragged(op):
     """Each (block, unroll) and alignment variant, at a size of a few tiles
     plus a ragged tail, with a grid smaller than the tile count so the
@@ -251,12 +258,12 @@ def test_every_kernel_variant_several_tiles_ragged(op):
             # the last tile is partial
             n = (2 * bpc * cus + 1) * block * unroll * vec - 3 * vec + 13
             plan = ew.ew_make_plan(op, 1 << 40, 1 << 41, (1 << 42) if op in (
-                "add_f32", "add_f16", "add_bf16") else (1 << 40 if op == "saxpy_f32" else 0),
-                n, cus)
+                "add_f32", "add_f16", "add_bf16", "add_relu_f32") else (
+                1 << 40 if op in IN_PLACE else 0), n, cus)
             assert plan.tiles > 2 * plan.grid, (plan.tiles, plan.grid)
-            if op in ("relu_f32", "copy_f32", "gather_f32"):
+            if op not in TWO_INPUT:
                 offs = [(1, [1]), (1, [0]), (0, [3])]
-            elif op == "saxpy_f32":
+            elif op in IN_PLACE:
                 offs = [(1, [2, 1]), (0, [0, 0]), (3, [1, 3])]
             else:
                 offs = [(1, [1, 1]), (1, [0, 1]), (1, [1, 2]), (0, [3, 5 % vec])]
@@ -269,6 +276,62 @@ def test_every_kernel_variant_several_tiles_ragged(op):
                 cases += [(2 * m, 1, [1], 2), (2 * m, 0, [3], 2), (2 * m, 2, [0], 2)]
             failures = _run_cases(op, cases, seed=320)
             assert not failures, (block, bpc, unroll, failures[:5])
+    finally:
+        ew.ew_reset_launch_config()
+        if os.path.exists(ew.LAUNCH_TABLE):
+            ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+def _bias_case(rows, cols, off_x, off_y, off_b, seed, in_place=False):
+    """One bias+ReLU launch with guard bands around y; returns failures."""
+    n = rows * cols
+    x = _f32_pool(n + 8, seed)[:n]
+    bias = _f32_pool(cols + 8, seed + 1)[:cols]
+    tx, _kx = upload(x, off_x)
+    tb, _kb = upload(bias, off_b)
+    if in_place:
+        ty = tx
+    else:
+        base = torch.full((n + off_y + 32,), -7.0, device=DEV)
+        ty = base[off_y:off_y + n]
+    ew.ew_bias_relu_f32(tx, tb, ty, rows, cols)
+    torch.cuda.synchronize()
+    got = download(ty, 4)
+    ref = oracle.bias_relu_f32(x, bias, rows, cols)
+    bad = mismatches("bias_relu_f32", got, ref)
+    out = [f"rows={rows} cols={cols} offs=({off_x},{off_y},{off_b}): {bad.size} mismatches"] \
+        if bad.size else []
+    if not in_place:
+        guard = base.cpu().numpy()
+        if np.any(guard[:off_y] != -7.0) or np.any(guard[off_y + n:] != -7.0):
+            out.append(f"rows={rows} cols={cols}: guard band written")
+    return out
+
+
+def test_bias_relu_shapes_and_offsets():
+    print("[parity] bias_relu", flush=True)
+    failures = []
+    shapes = [(1, 1), (1, 3), (2, 5), (3, 7), (5, 4), (4, 16), (7, 33), (1, 1000), (1000, 1),
+              (33, 127), (64, 129), (129, 64), (256, 1024), (3, 100003)]
+    for k, (rows, cols) in enumerate(shapes):
+        for off_x, off_y, off_b in ((0, 0, 0), (1, 0, 3), (0, 3, 1), (2, 1, 0), (3, 3, 2)):
+            failures += _bias_case(rows, cols, off_x, off_y, off_b, 340 + k)
+    failures += _bias_case(64, 129, 1, 1, 0, 360, in_place=True)
+    assert not failures, failures[:10]
+
+
+def test_bias_relu_every_kernel_variant():
+    print("[parity] bias_relu variants", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        for (block, bpc, unroll) in LAUNCHES:
+            _force_launch("bias_relu_f32", block, bpc, unroll)
+            vecs = (2 * bpc * cus + 1) * block * unroll
+            for cols in (4096, 3):
+                rows = -(-4 * vecs // cols) + 1
+                failures = _bias_case(rows, cols, 1, 0, 1, 370) + \
+                    _bias_case(rows, cols, 0, 0, 0, 371)
+                assert not failures, (block, bpc, unroll, cols, failures[:3])
     finally:
         ew.ew_reset_launch_config()
         if os.path.exists(ew.LAUNCH_TABLE):

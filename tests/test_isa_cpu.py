@@ -1,0 +1,79 @@
+"""Static checks on the gfx950 assembly of every kernel (no GPU needed).
+
+The library's numerics rest on instruction choices the compiler could change
+silently; these checks fail the build's tests if it does:
+
+* no LDS and no scratch (register spills) in any kernel;
+* float denormal modes "preserve" for binary32 and binary16/64;
+* no packed-fp32 instructions (the library is built without them);
+* no single-rounding mixed-precision fma into a 16-bit result
+  (v_fma_mixlo/mixhi_f16): the 16-bit SAXPY is defined as a binary32 fma
+  followed by a separate round-to-nearest-even;
+* no round-toward-zero conversions (v_cvt_pkrtz_*);
+* the ReLU kernels select with a compare (no v_max_*, whose NaN rule returns
+  the other operand);
+* the streaming kernels move 16 bytes per lane (global_load_dwordx4 /
+  global_store_dwordx4) and store non-temporally.
+"""
+import importlib.util
+import os
+import re
+
+import pytest
+
+from tests.conftest import ROOT
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    spec = importlib.util.spec_from_file_location(
+        "_ew_build", os.path.join(ROOT, "memory_bound_elementwise_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    path = mod.device_asm(str(tmp_path_factory.mktemp("asm")))
+    return open(path).read()
+
+
+def _kernels(text):
+    """{mangled name: (body, metadata)} for every kernel in the assembly."""
+    bodies = dict(re.findall(r"\n(_ZN2ew\w+):[^\n]*\n(.*?)\n\.Lfunc_end", text, re.S))
+    meta = dict(re.findall(r"\.amdhsa_kernel (\w+)(.*?)\.end_amdhsa_kernel", text, re.S))
+    assert bodies and set(bodies) == set(meta), "could not split the assembly into kernels"
+    return {k: (bodies[k], meta[k]) for k in bodies}
+
+
+def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
+    ks = _kernels(asm)
+    assert len(ks) > 100
+    for name, (_, meta) in ks.items():
+        d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
+        assert d["group_segment_fixed_size"] == "0", name
+        assert d["private_segment_fixed_size"] == "0", name
+        assert d["float_denorm_mode_32"] == "3", name
+        assert d["float_denorm_mode_16_64"] == "3", name
+
+
+def test_no_forbidden_instructions(asm):
+    for pat in (r"\bv_pk_(add|mul|fma)_f32\b", r"\bv_fma_mix(lo|hi)_f16\b",
+                r"\bv_mad_mix(lo|hi)_f16\b", r"\bv_cvt_pkrtz"):
+        assert not re.search(pat, asm), pat
+
+
+def test_relu_kernels_select_rather_than_max(asm):
+    for name, (body, _) in _kernels(asm).items():
+        if "Relu" in name:
+            assert not re.search(r"\bv_(pk_)?max_(f32|f16|num_f32|num_f16|bf16)", body), name
+
+
+def test_saxpy_kernels_use_a_fused_multiply_add(asm):
+    for name, (body, _) in _kernels(asm).items():
+        if "Saxpy" in name:
+            assert re.search(r"\bv_fma(c)?_(mix_)?f32", body), name
+            assert not re.search(r"\bv_mul_f32\b", body), name
+
+
+def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
+    for name, (body, _) in _kernels(asm).items():
+        if "ew_stream_kernel" in name:
+            assert re.search(r"global_load_dwordx4 .* nt\b", body), name
+            assert re.search(r"global_store_dwordx4 .* nt\b", body), name
