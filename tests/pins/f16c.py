@@ -33,6 +33,9 @@ def _load():
         lib.pin_f16c_range.restype = None
         lib.pin_f16c_widen.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t]
         lib.pin_f16c_widen.restype = None
+        lib.pin_f16c_count_mismatches.argtypes = [ctypes.c_void_p, ctypes.c_uint64,
+                                                  ctypes.c_uint64]
+        lib.pin_f16c_count_mismatches.restype = ctypes.c_uint64
         _lib = lib
     return _lib
 
@@ -41,6 +44,13 @@ def range_to_f16(start: int, count: int) -> np.ndarray:
     y = np.empty(count, np.uint16)
     _load().pin_f16c_range(start, count, y.ctypes.data_as(ctypes.c_void_p))
     return y
+
+
+def count_mismatches(fn_address: int, start: int, count: int) -> int:
+    """Patterns in [start, start+count) where the binary32 -> binary16
+    function at `fn_address` disagrees with VCVTPS2PH (NaNs by class and
+    sign)."""
+    return int(_load().pin_f16c_count_mismatches(fn_address, start, count))
 
 
 def widen(h: np.ndarray) -> np.ndarray:
