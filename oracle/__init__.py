@@ -20,6 +20,8 @@ Each function wraps the plain scalar C loop of the same name in ``oracle.c``
 * ``copy_f32(x)``              bitwise copy
 * ``gather_f32(x, stride)``    out[i] = x[(stride*i) mod n], bitwise
 * ``gather_index(n, stride, i)``  the input index of one gather output
+* ``copy2d_f32(base, offset, stride_r, stride_c, rows, cols)``  strided view
+  copied to a contiguous array
 
 plus the scalar conversions and the binary32 ulp distance.  Parity status:
 all functions pinned (see ``tests/test_oracle.py``); none unpinned.
@@ -66,6 +68,8 @@ def _load():
                  "oracle_f32_to_bf16_array", "oracle_bf16_to_f32_array"):
         getattr(lib, name).argtypes = [vp, vp, sz]
         getattr(lib, name).restype = None
+    lib.oracle_copy2d_f32.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, sz, sz]
+    lib.oracle_copy2d_f32.restype = None
     lib.oracle_gather_f32.argtypes = [vp, vp, sz, sz]
     lib.oracle_gather_f32.restype = None
     for name in ("oracle_f32_range_to_f16", "oracle_f32_range_to_bf16"):
@@ -245,6 +249,24 @@ def gather_f32(x, stride):
     if x.size:
         lib.oracle_gather_f32(_ptr(x), _ptr(y), x.size, int(stride))
     return y
+
+
+def copy2d_f32(base, offset, stride_r, stride_c, rows, cols):
+    """out[r, c] = base[offset + r*stride_r + c*stride_c], bitwise, as a
+    contiguous rows x cols array (strides in elements, may be negative).
+    Every index touched must lie inside `base`."""
+    lib = _load()
+    base = _as(base, np.float32)
+    lo = offset + min(0, (rows - 1) * stride_r) + min(0, (cols - 1) * stride_c)
+    hi = offset + max(0, (rows - 1) * stride_r) + max(0, (cols - 1) * stride_c)
+    if rows and cols and (lo < 0 or hi >= base.size):
+        raise ValueError("view outside the base array")
+    out = np.empty(rows * cols, np.float32)
+    if rows and cols:
+        ptr = base.ctypes.data + 4 * offset
+        lib.oracle_copy2d_f32(ctypes.c_void_p(ptr), int(stride_r), int(stride_c), _ptr(out),
+                              int(rows), int(cols))
+    return out
 
 
 def gather_index(n, stride, i) -> int:

@@ -278,6 +278,21 @@ void oracle_relu_bf16(const uint16_t *x, uint16_t *y, size_t n)
     }
 }
 
+/* Strided view copied to a contiguous row-major array, bit patterns
+ * unchanged: out[r*cols + c] = in[r*stride_r + c*stride_c], strides in
+ * elements and signed (a transposed view has stride_r = 1; x[::2] is the
+ * rows = 1, stride_c = 2 case).  [PerfNotes] 3.4: non-contiguous access in
+ * PyTorch appears as a stride; 3.1-3.2: coalesced versus strided reads. */
+void oracle_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, float *out,
+                       size_t rows, size_t cols)
+{
+    const uint32_t *s = (const uint32_t *)in;
+    uint32_t *d = (uint32_t *)out;
+    for (size_t r = 0; r < rows; ++r)
+        for (size_t c = 0; c < cols; ++c)
+            d[r * cols + c] = s[(int64_t)r * stride_r + (int64_t)c * stride_c];
+}
+
 /* Contiguous copy out[i] = in[i], moved as bit patterns so NaN payloads and
  * signalling NaNs survive.  [PerfNotes] section 3.2, coalesced copy kernel. */
 void oracle_copy_f32(const float *in, float *out, size_t n)

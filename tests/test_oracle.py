@@ -579,6 +579,48 @@ def test_gather_index_agrees_with_the_array_gather():
         assert all(int(o[i]) == oracle.gather_index(997, stride, i) for i in range(997))
 
 
+def _as_strided_ref(base, offset, sr, sc, rows, cols):
+    """numpy's own strided view of the same memory, copied (bitwise)."""
+    from numpy.lib.stride_tricks import as_strided
+    b = base.view(np.uint32)
+    v = as_strided(b[offset:], shape=(rows, cols), strides=(4 * sr, 4 * sc)) if sr >= 0 and \
+        sc >= 0 else None
+    if v is None:
+        # negative strides: index explicitly (a different code path from the oracle's loop)
+        r = np.arange(rows)[:, None]
+        c = np.arange(cols)[None, :]
+        v = b[offset + r * sr + c * sc]
+    return np.ascontiguousarray(v).reshape(-1)
+
+
+def test_copy2d_vs_numpy_strided_views():
+    g = np.random.Generator(np.random.PCG64(91))
+    base = g.integers(0, 1 << 32, size=1 << 16, dtype=np.uint32).view(np.float32)
+    cases = [(0, 1, 1, 1, 1), (5, 7, 1, 3, 7), (0, 1, 2, 1, 1000),      # 1-D x[::2]
+             (3, 64, 1, 10, 50),                                         # submatrix
+             (0, 1, 128, 128, 96), (1, 1, 200, 150, 199),                # transposed views
+             (17, 300, 3, 20, 40), (0, 0, 1, 5, 9),                      # broadcast rows
+             (8000, -64, 1, 100, 64), (9000, 1, -3, 7, 500), (40000, -129, -1, 33, 64)]
+    for off, sr, sc, rows, cols in cases:
+        got = oracle.copy2d_f32(base, off, sr, sc, rows, cols).view(np.uint32)
+        ref = _as_strided_ref(base, off, sr, sc, rows, cols)
+        assert np.array_equal(got, ref), (off, sr, sc, rows, cols)
+
+
+def test_copy2d_closed_forms():
+    x = synth.uniform_pm1(synth.rng(92), 96 * 80)
+    # contiguous strides are a plain copy
+    assert np.array_equal(oracle.copy2d_f32(x, 0, 80, 1, 96, 80), x)
+    # transposing twice gives the original back
+    t = oracle.copy2d_f32(x, 0, 1, 80, 80, 96)            # (80 x 96) = x^T
+    assert np.array_equal(oracle.copy2d_f32(t, 0, 1, 96, 96, 80), x)
+    assert np.array_equal(t.reshape(80, 96), x.reshape(96, 80).T)
+    # rows = 1 with stride 2 is x[::2]
+    assert np.array_equal(oracle.copy2d_f32(x, 0, 0, 2, 1, x.size // 2), x[::2])
+    with pytest.raises(ValueError):
+        oracle.copy2d_f32(x, 0, 80, 1, 97, 80)
+
+
 # --------------------------------------------------------------------------
 # ulp distance
 # --------------------------------------------------------------------------
