@@ -49,11 +49,11 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                   "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
-                  "relu_f16": 4, "relu_bf16": 4}
+                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8}
 DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f32",
          "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32", "add_relu_f32": "f32",
          "saxpy_relu_f32": "f32", "bias_relu_f32": "f32", "saxpy_f16": "f16",
-         "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16"}
+         "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16", "copy2d_f32": "f32"}
 # The unfused sequence each fused chain replaces, timed beside it.
 UNFUSED = {"add_relu_f32": ("add_f32", "relu_f32"), "saxpy_relu_f32": ("saxpy_f32", "relu_f32")}
 MALL_BYTES = 256 * 2 ** 20
@@ -84,7 +84,16 @@ class Prepared:
         s = stream.cuda_stream
         self.stream = s
         self.unfused = None
-        if w.op == "bias_relu_f32":
+        if w.op == "copy2d_f32":
+            sr, sc, _, offset = w.view
+            base, kb = upload(self.inp["base"], 0)
+            out, ko = upload(np.zeros(w.n, np.float32), 0)
+            self.keep += [kb, ko]
+            rows = w.n // w.cols
+            src = base.data_ptr() + 4 * offset
+            self.launch = lambda: ew.ew_copy2d_f32(src, sr, sc, out, rows, w.cols, stream=s)
+            self.out, self.ptrs = out, (out, base, None)
+        elif w.op == "bias_relu_f32":
             x, kx = upload(self.inp["x"], offs.get("x", 0))
             bias, kb = upload(self.inp["bias"], 0)
             y, ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))
@@ -194,6 +203,9 @@ def cpu_baseline_leg(w, inp, got, target_s):
             return getattr(oracle, w.op)(w.alpha, d["x"], d["y"])
         if w.op == "bias_relu_f32":
             return oracle.bias_relu_f32(d["x"], d["bias"], d["x"].size // w.cols, w.cols)
+        if w.op == "copy2d_f32":       # always the full view (see below)
+            sr, sc, _, offset = w.view
+            return oracle.copy2d_f32(d["base"], offset, sr, sc, w.n // w.cols, w.cols)
         if w.op == "gather_f32":
             return oracle.gather_f32(d["x"], w.stride)
         return getattr(oracle, w.op)(d["x"])
@@ -203,8 +215,8 @@ def cpu_baseline_leg(w, inp, got, target_s):
     full_s = time.perf_counter() - t0
     bad = int(mismatches(w.op, got, ref).size)
     del ref
-    if target_s <= 0:
-        gbs = algorithmic_bytes(w.op, w.n) / full_s / 1e9
+    if target_s <= 0 or w.op == "copy2d_f32":
+        gbs = algorithmic_bytes(w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0) / full_s / 1e9
         sample = f"one full pass over all {w.n} elements ({full_s:.2f} s)"
     else:
         m = min(w.n, 1 << 26)
@@ -257,6 +269,13 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     prep = Prepared(w, torch, np, ew, synth, stream)
     plan = prep.plan(ew, cus)
     launch_desc = {"block": plan.block, "grid": plan.grid, "unroll": plan.unroll}
+    if w.op == "copy2d_f32":
+        sr, sc = w.view[0], w.view[1]
+        launch_desc["path"] = ("contiguous 16-byte loads, even elements kept (stride-2 gather "
+                               "kernel)" if (w.n == w.cols and sc == 2) else
+                               "rows contiguous" if sc == 1 else
+                               "LDS-tiled transpose (64 x 64 tiles, 256 threads)" if sr == 1 else
+                               "generic (one 4-byte load per element)")
     res = {"workload": w.name, "op": w.op, "n": w.n, "launch": launch_desc,
            "split": {"head": plan.head, "vectors": plan.vectors, "tail": plan.tail,
                      "in_coaligned": list(plan.in_coaligned)}}
@@ -271,7 +290,7 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     del got
     if bad:
         return res, prep, None
-    nbytes = algorithmic_bytes(w.op, w.n, w.cols)
+    nbytes = algorithmic_bytes(w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0)
     footprint = nbytes if w.op != "gather_f32" else 8 * w.n
     cold = footprint <= 2 * MALL_BYTES
     flush = (lambda: flush_buf.fill_(1)) if cold else None

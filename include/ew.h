@@ -123,6 +123,30 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Strided views                                                            */
+/* ------------------------------------------------------------------------ */
+
+/* A strided 2-D view copied to a contiguous row-major array, bit patterns
+ * unchanged: out[r*cols + c] = in[r*stride_r + c*stride_c] for r < rows,
+ * c < cols.  Strides are in elements and signed (zero and negative strides
+ * are allowed); `in` points at element (0, 0) of the view.  A 1-D strided
+ * view (PyTorch x[::s]) is rows = 1, stride_c = s; a submatrix has
+ * stride_c = 1; a transposed view has stride_r = 1.
+ * [PerfNotes] 3.4 (non-contiguous tensors show up as strides) and 3.1-3.2
+ * (coalesced versus strided reads).
+ * Paths: rows == 1 with stride_c == 2 reads contiguous 16-byte spans and
+ * keeps the even elements; stride_c == 1 reads whole 16-byte row segments;
+ * stride_r == 1 moves 64 x 64 tiles through LDS so that both reads and
+ * writes are coalesced; otherwise one 4-byte load per element.  out is written with 16-byte
+ * stores after a scalar head.
+ * Errors: rows or cols 0 -> EW_OK; null pointers, rows*cols overflow, or a
+ * view reaching outside the address space -> EW_ERR_INVALID_ARG; in or out
+ * not 4-byte aligned -> EW_ERR_MISALIGNED; any overlap between out and the
+ * span of elements the view touches -> EW_ERR_OVERLAP. */
+ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c,
+                          float *out, size_t rows, size_t cols, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* SAXPY and ReLU on 16-bit data                                             */
 /* ------------------------------------------------------------------------ */
 /* The operator template of [EwOps] section 二 (only the middle operation
@@ -188,7 +212,7 @@ int ew_abi_version(void);
 /* Launch configuration, per operation name ("add_f32", "add_f16",
  * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
  * "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16",
- * "saxpy_bf16", "relu_f16", "relu_bf16") and size
+ * "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32") and size
  * class: a row applies to every n >= min_n up to the next row's min_n.  The
  * grid is min(blocks_per_cu * CU count, number of tiles), where a tile is
  * block * unroll 16-byte vectors; each block walks tiles with a grid stride

@@ -20,7 +20,7 @@ __all__ = [
     "ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
     "ew_copy_f32", "ew_gather_f32", "ew_add_relu_f32", "ew_saxpy_relu_f32",
     "ew_bias_relu_f32", "ew_saxpy_f16", "ew_saxpy_bf16", "ew_relu_f16", "ew_relu_bf16",
-    "ew_status_string", "ew_last_hip_error",
+    "ew_copy2d_f32", "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
     "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan", "ew_make_gather_plan",
 ]
@@ -31,7 +31,7 @@ LAUNCH_TABLE = os.path.join(_PKG, "launch_table.txt")
 
 OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
        "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16", "saxpy_bf16",
-       "relu_f16", "relu_bf16")
+       "relu_f16", "relu_bf16", "copy2d_f32")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -88,6 +88,8 @@ _c = {
     "ew_saxpy_bf16": _proto("ew_saxpy_bf16", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
     "ew_relu_f16": _proto("ew_relu_f16", _int, _vp, _vp, _sz, _vp),
     "ew_relu_bf16": _proto("ew_relu_bf16", _int, _vp, _vp, _sz, _vp),
+    "ew_copy2d_f32": _proto("ew_copy2d_f32", _int, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
+                            _sz, _sz, _vp),
     "ew_status_string": _proto("ew_status_string", ctypes.c_char_p, _int),
     "ew_last_hip_error": _proto("ew_last_hip_error", _int),
     "ew_abi_version": _proto("ew_abi_version", _int),
@@ -234,6 +236,18 @@ def ew_relu_bf16(x, y, n=None, stream=None):
     """y = maximum(x, +0) on bfloat16 data."""
     _check(_c["ew_relu_bf16"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
            "ew_relu_bf16")
+
+
+def ew_copy2d_f32(src, stride_r, stride_c, out, rows=None, cols=None, stream=None):
+    """out[r, c] = src[r*stride_r + c*stride_c] into a contiguous rows x cols
+    array; `src` is the address (or tensor) of element (0, 0) of the view.
+    rows/cols default to out's 2-D shape."""
+    if rows is None or cols is None:
+        if isinstance(out, int):
+            raise ValueError("rows and cols are required when buffers are raw pointers")
+        rows, cols = out.shape
+    _check(_c["ew_copy2d_f32"](_addr(src), int(stride_r), int(stride_c), _addr(out), int(rows),
+                               int(cols), _stream(out, stream)), "ew_copy2d_f32")
 
 
 def ew_status_string(status: int) -> str:

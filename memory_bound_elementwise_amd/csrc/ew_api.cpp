@@ -19,7 +19,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 
 struct OpInfo {
     const char *name;
@@ -43,6 +43,7 @@ constexpr OpInfo kOps[kOpCount] = {
     {"saxpy_bf16", 2, 2, true},
     {"relu_f16", 2, 1, true},
     {"relu_bf16", 2, 1, true},
+    {"copy2d_f32", 4, 1, false},
 };
 
 int op_from_name(const char *name)
@@ -100,6 +101,8 @@ constexpr DefaultRow kDefaults[] = {
     {kOpReluF16, {size_t(1) << 22, 512, 1024, 1}},
     {kOpReluBF16, {0, 512, 8, 2}},
     {kOpReluBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpCopy2dF32, {0, 1024, 1024, 2}},
+    {kOpCopy2dF32, {size_t(1) << 22, 128, 1024, 2}},
 };
 
 constexpr int kMaxRows = 16;
@@ -453,6 +456,88 @@ ew_status_t ew_relu_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 ew_status_t ew_relu_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 {
     return run_stream(kOpReluBF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, float *out,
+                          size_t rows, size_t cols, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return EW_OK;
+    if (!in || !out || rows > SIZE_MAX / cols) return EW_ERR_INVALID_ARG;
+    const size_t n = rows * cols;
+    if (n >= (size_t(1) << 62) || n > SIZE_MAX / 4) return EW_ERR_INVALID_ARG;
+    // Element offsets touched in the input: [lo, hi], exact in 128 bits.
+    const __int128 er = (__int128)(rows - 1) * stride_r, ec = (__int128)(cols - 1) * stride_c;
+    const __int128 lo = (er < 0 ? er : 0) + (ec < 0 ? ec : 0);
+    const __int128 hi = (er > 0 ? er : 0) + (ec > 0 ? ec : 0);
+    const __int128 ip = (__int128)reinterpret_cast<uintptr_t>(in);
+    const __int128 in_lo = ip + 4 * lo, in_hi = ip + 4 * (hi + 1);   // byte range [in_lo, in_hi)
+    if (in_lo < 0 || in_hi > (__int128)UINTPTR_MAX) return EW_ERR_INVALID_ARG;
+    const uintptr_t op = reinterpret_cast<uintptr_t>(out);
+    if (op > UINTPTR_MAX - n * 4) return EW_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(in) % 4 != 0 || op % 4 != 0) return EW_ERR_MISALIGNED;
+    if (in_lo < (__int128)op + (__int128)(n * 4) && (__int128)op < in_hi) return EW_ERR_OVERLAP;
+    int cus = 0;
+    ew_status_t st = current_device(&cus);
+    if (st != EW_OK) return st;
+    const Plan p = make_plan(kOpCopy2dF32, out, out, nullptr, n, cus);
+    Copy2dArgs a{};
+    a.in = reinterpret_cast<const uint32_t *>(in);
+    a.out = reinterpret_cast<uint32_t *>(out);
+    a.sr = stride_r;
+    a.sc = stride_c;
+    a.rows = rows;
+    a.cols = cols;
+    a.head = p.head;
+    a.vectors = p.vectors;
+    a.tail = p.tail;
+    a.tiles = p.tiles;
+    const uint64_t sv = 4 * (uint64_t)p.launch.block;
+    const unsigned __int128 st_t = (unsigned __int128)sv * (uint64_t)p.launch.unroll *
+                                   (uint64_t)p.launch.grid;
+    a.step_vec_r = sv / cols;
+    a.step_vec_c = sv % cols;
+    a.step_tile_r = (uint64_t)(st_t / cols);
+    a.step_tile_c = (uint64_t)(st_t % cols);
+    // Path: a 1-D view with stride 2 (x[::2]) reads contiguous 16-byte spans
+    // and keeps the even elements (the stride-2 gather kernel, one segment,
+    // no wrap); rows contiguous; a transposed view (tiles through LDS);
+    // generic.
+    if (rows == 1 && stride_c == 2) {
+        GatherArgs g{};
+        g.in = a.in;
+        g.out = a.out;
+        g.n = 2 * n;
+        g.stride = 2;
+        g.seg = n;
+        g.reps = 1;
+        const Plan pg = make_plan(kOpGatherF32, out, in, nullptr, n, cus);
+        // The kernel reads 16 bytes per output pair (input elements 2i ..
+        // 2i + 3); the view ends at element 2(n - 1), so the body must stop
+        // one output early (head + 4 * vectors <= n - 1) and the scalar tail,
+        // which reads only in[2e], finishes the rest (1 to 4 elements).
+        g.head = pg.head;
+        g.vectors = n - 1 >= pg.head ? (n - 1 - pg.head) / 4 : 0;
+        g.tail = n - g.head - 4 * g.vectors;
+        const uint64_t tile_vecs = (uint64_t)pg.launch.block * (uint64_t)pg.launch.unroll;
+        g.tiles = (g.vectors + tile_vecs - 1) / tile_vecs;
+        Launch lg = pg.launch;
+        const uint64_t cap = (uint64_t)pg.blocks_per_cu * (uint64_t)cus;
+        lg.grid = (int)(g.tiles == 0 ? 1 : (g.tiles < cap ? g.tiles : cap));
+        const hipError_t e = launch_gather(g, lg, s);
+        return e == hipSuccess ? EW_OK : fail_hip(e);
+    }
+    int mode = 0;
+    Launch l = p.launch;
+    if (stride_c == 1) {
+        mode = 1;
+    } else if (stride_r == 1 && rows >= 2 && cols >= 2) {
+        mode = 2;
+        const uint64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64);
+        const uint64_t cap = (uint64_t)cus * 8;   // 8 blocks of 256 per CU resident
+        l.grid = (int)(tiles < cap * 64 ? tiles : cap * 64);
+    }
+    const hipError_t e = launch_copy2d(a, mode, l, s);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
 ew_status_t ew_bias_relu_f32(const float *x, const float *bias, float *y, size_t rows,

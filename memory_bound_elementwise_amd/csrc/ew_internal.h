@@ -23,6 +23,7 @@ enum OpId : int {
     kOpSaxpyBF16,
     kOpReluF16,
     kOpReluBF16,
+    kOpCopy2dF32,
     kOpCount
 };
 
@@ -77,6 +78,19 @@ struct BiasArgs {
     uint64_t step_tile;  // (4 * blockDim * unroll * gridDim) mod cols: next tile
 };
 
+// Strided 2-D view copied to a contiguous row-major array:
+// out[r*cols + c] = in[r*sr + c*sc].  head / vectors / tail split the
+// contiguous output (n = rows * cols) as for the streaming kernels.
+struct Copy2dArgs {
+    const uint32_t *in;  // element (0, 0) of the view
+    uint32_t *out;
+    int64_t sr, sc;      // strides in elements
+    uint64_t rows, cols;
+    uint64_t head, vectors, tail, tiles;
+    uint64_t step_vec_r, step_vec_c;    // (4 * blockDim) as (rows, cols) of the output
+    uint64_t step_tile_r, step_tile_c;  // (4 * blockDim * unroll * gridDim) likewise
+};
+
 struct Launch {
     int block;
     int grid;
@@ -89,6 +103,11 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
                          const Launch &launch, hipStream_t stream);
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
+                         hipStream_t stream);
+
+// mode 0: generic (one 4-byte load per element), 1: rows contiguous
+// (sc == 1, 16-byte loads inside a row), 2: LDS-tiled transpose (sr == 1).
+hipError_t launch_copy2d(const Copy2dArgs &args, int mode, const Launch &launch,
                          hipStream_t stream);
 
 // co: x's body start is 16-byte aligned (it is read with aligned loads).

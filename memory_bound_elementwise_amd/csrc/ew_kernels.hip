@@ -545,6 +545,133 @@ __global__ void __launch_bounds__(1024) ew_bias_relu_kernel(BiasArgs a)
 }
 
 // ---------------------------------------------------------------------------
+// Strided 2-D views: out[r*cols + c] = in[r*sr + c*sc], out contiguous
+// ---------------------------------------------------------------------------
+
+// Output-ordered kernel: the streaming skeleton over the contiguous output,
+// each lane walking the (row, column) of its vector incrementally (one
+// 64-bit division per lane, then host-precomputed steps with a carry).
+// RowContig (sc == 1): a vector whose four columns lie in one row is read
+// with one element-aligned 16-byte load; otherwise four 4-byte loads.
+template <int U, bool RowContig>
+__global__ void __launch_bounds__(1024) ew_copy2d_kernel(Copy2dArgs a)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nthr = blockDim.x;
+    const uint64_t cols = a.cols;
+
+    if (blockIdx.x == 0 && tid < a.head + a.tail) {
+        const uint64_t e = tid < a.head ? (uint64_t)tid : a.head + a.vectors * 4 + (tid - a.head);
+        const int64_t r = (int64_t)(e / cols), c = (int64_t)(e % cols);
+        a.out[e] = a.in[r * a.sr + c * a.sc];
+    }
+
+    uint64_t t = blockIdx.x;
+    if (t >= a.tiles) return;
+    char *out = reinterpret_cast<char *>(a.out + a.head);
+    const uint64_t tile_vecs = nthr * U;
+    const uint64_t e0 = a.head + 4 * (t * tile_vecs + tid);
+    uint64_t rt = e0 / cols, ct = e0 % cols;    // (row, column) of this lane's first element
+
+    for (; t < a.tiles; t += gridDim.x) {
+        const uint64_t v0 = t * tile_vecs + tid;
+        u32x4 x[U];
+        uint64_t r = rt, c = ct;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool live = v0 + u * nthr < a.vectors;
+            if (RowContig && c + 3 < cols) {
+                x[u] = live ? load16<false, 4>(reinterpret_cast<const char *>(
+                                  a.in + (int64_t)r * a.sr + (int64_t)c))
+                            : u32x4{0, 0, 0, 0};
+            } else {
+                uint64_t rr = r, cc = c;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    x[u][k] = live ? a.in[(int64_t)rr * a.sr + (int64_t)cc * a.sc] : 0u;
+                    if (++cc == cols) { cc = 0; ++rr; }
+                }
+            }
+            c += a.step_vec_c;
+            r += a.step_vec_r;
+            if (c >= cols) { c -= cols; ++r; }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t v = v0 + u * nthr;
+            if (v < a.vectors) store16(out + v * 16, x[u]);
+        }
+        ct += a.step_tile_c;
+        rt += a.step_tile_r;
+        if (ct >= cols) { ct -= cols; ++rt; }
+    }
+}
+
+// Transposed views (sr == 1: the input is contiguous along the output's
+// rows).  Reading in output order would touch one cache line per element;
+// instead each 256-thread block moves a 64 x 64 tile through LDS: it reads
+// the tile column by column (64 consecutive input elements = 256 B, 16 bytes
+// per lane), writes it into LDS, and writes the output row by row (64
+// consecutive output elements, 16 bytes per lane), so both HBM streams are
+// coalesced.  Rows of the LDS tile are padded to 68 floats.  Partial edge
+// tiles fall back to 4-byte accesses with bounds checks.  Tiles are walked
+// with a grid stride; one 64-bit division per tile.
+constexpr int kT = 64;
+constexpr int kPitch = kT + 4;
+
+__global__ void __launch_bounds__(256) ew_transpose_kernel(Copy2dArgs a)
+{
+    __shared__ uint32_t tile[kT * kPitch];
+    const uint32_t tid = threadIdx.x;
+    const uint64_t tiles_c = (a.cols + kT - 1) / kT;
+    const uint64_t tiles = tiles_c * ((a.rows + kT - 1) / kT);
+    const uint32_t sub = tid >> 4;          // 0..15
+    const uint32_t q4 = (tid & 15u) * 4;    // 0, 4, ..., 60
+
+    for (uint64_t t = blockIdx.x; t < tiles; t += gridDim.x) {
+        const uint64_t r0 = (t / tiles_c) * kT, c0 = (t % tiles_c) * kT;
+        const bool full_r = r0 + kT <= a.rows, full_c = c0 + kT <= a.cols;
+        // Load: column c0 + c of the tile is kT consecutive input elements.
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t c = p * 16 + sub;
+            const int64_t base = (int64_t)(c0 + c) * a.sc + (int64_t)(r0 + q4);
+            u32x4 v;
+            if (full_r && full_c) {
+                v = load16<false, 4>(reinterpret_cast<const char *>(a.in + base));
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const bool ok = c0 + c < a.cols && r0 + q4 + k < a.rows;
+                    v[k] = ok ? a.in[base + k] : 0u;
+                }
+            }
+            *reinterpret_cast<u32x4 *>(&tile[c * kPitch + q4]) = v;
+        }
+        __syncthreads();
+        // Store: output row r0 + r of the tile is kT consecutive elements.
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t r = p * 16 + sub;
+            u32x4 w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = tile[(q4 + k) * kPitch + r];
+            uint32_t *dst = a.out + (r0 + r) * a.cols + c0 + q4;
+            if (full_r && full_c) {
+                u32x4_a4 *q = reinterpret_cast<u32x4_a4 *>(dst);
+                if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, q);
+                else *q = w;
+            } else if (r0 + r < a.rows) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (c0 + q4 + k < a.cols) dst[k] = w[k];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
 
@@ -619,6 +746,28 @@ const void *gather2_fn()
 
 }  // namespace
 
+hipError_t launch_copy2d(const Copy2dArgs &args, int mode, const Launch &l, hipStream_t s)
+{
+    Copy2dArgs a = args;
+    void *kargs[] = {&a};
+    const void *fn = nullptr;
+    if (mode == 2) {
+        fn = reinterpret_cast<const void *>(&ew_transpose_kernel);
+        return hipLaunchKernel(fn, dim3(l.grid), dim3(256), kargs, 0, s);
+    }
+#define EW_C2D_FN(U) (mode == 1 ? reinterpret_cast<const void *>(&ew_copy2d_kernel<U, true>) \
+                                : reinterpret_cast<const void *>(&ew_copy2d_kernel<U, false>))
+    switch (l.unroll) {
+    case 1: fn = EW_C2D_FN(1); break;
+    case 2: fn = EW_C2D_FN(2); break;
+    case 4: fn = EW_C2D_FN(4); break;
+    case 8: fn = EW_C2D_FN(8); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef EW_C2D_FN
+    return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
+}
+
 hipError_t launch_bias_relu(const BiasArgs &args, bool co, const Launch &l, hipStream_t s)
 {
     BiasArgs a = args;
@@ -646,7 +795,7 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
     GatherArgs a = args;
     void *kargs[] = {&a};
     const void *fn = nullptr;
-    if (args.stride == 2 && args.reps == 2) {
+    if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {
         // co-alignment of the input's body start: in + 8 * head
         const bool co = ((reinterpret_cast<uintptr_t>(args.in) + 8 * args.head) & 15u) == 0;
         switch (l.unroll) {

@@ -36,8 +36,11 @@ SIZES = {"small": 1 << 20, "large": 1 << 28}
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                   "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
-                  "relu_f16": 4, "relu_bf16": 4}
+                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8}
 BIAS_COLS = 4096
+# copy2d is tuned on a submatrix view: 16384 rows of 16380 columns out of
+# 16384-wide rows (the row-contiguous path, which uses the table).
+C2D_ROWS, C2D_COLS, C2D_PITCH = 16384, 16380, 16384
 
 
 # Element offset of input A for the large fp32 add: the misaligned-input
@@ -60,6 +63,9 @@ def _launcher(op, n, bufs, stream, off_a=0):
     if op in ("relu_f16", "relu_bf16"):
         fn = getattr(ew, "ew_" + op)
         return lambda: fn(pa, c.data_ptr(), n=n, stream=s)
+    if op == "copy2d_f32":
+        return lambda: ew.ew_copy2d_f32(pa + 4, C2D_PITCH, 1, c.data_ptr(), C2D_ROWS, C2D_COLS,
+                                        stream=s)
     if op == "bias_relu_f32":
         return lambda: ew.ew_bias_relu_f32(pa, b.data_ptr(), c.data_ptr(), n // BIAS_COLS,
                                            BIAS_COLS, stream=s)
@@ -111,6 +117,14 @@ def tune(ops=ew.OPS, repeats=3, finalists=6, rounds=7, log=None):
             launch = _launcher(op, n, bufs, stream, off_a)
             launches = 20 if n >= (1 << 24) else 200
             nbytes = BYTES_PER_ELEM[op] * n
+            if op == "copy2d_f32":
+                if cls == "small":
+                    launch = lambda: ew.ew_copy2d_f32(bufs[0].data_ptr() + 4, 1024, 1,
+                                                      bufs[2].data_ptr(), 1024, 1020,
+                                                      stream=stream.cuda_stream)
+                    nbytes = 8 * 1024 * 1020
+                else:
+                    nbytes = 8 * C2D_ROWS * C2D_COLS
             results = []
             for block, bpc, unroll in itertools.product(BLOCKS, BPC, UNROLLS):
                 _set(op, block, bpc, unroll)

@@ -70,7 +70,8 @@ class Workload:
     offsets: dict = field(default_factory=dict)
     alpha: float = 0.0    # saxpy only
     stride: int = 0       # gather only
-    cols: int = 0         # bias_relu only: row length (n = rows * cols)
+    cols: int = 0         # bias_relu / copy2d: row length (n = rows * cols)
+    view: tuple = ()      # copy2d: (stride_r, stride_c, base elements, offset)
     description: str = ""
 
 
@@ -133,6 +134,21 @@ WORKLOADS = {
     "relu_bf16_2e28": _w(
         "relu_bf16_2e28", "relu_bf16", 1 << 28, 114, "normal",
         description="bf16 ReLU y=max(x,0), n=2^28, x normal(0,1) cast RNE"),
+    "transpose_f32_16384x16384": _w(
+        "transpose_f32_16384x16384", "copy2d_f32", 1 << 28, 115, "uniform", cols=16384,
+        view=(1, 16384, 1 << 28, 0),
+        description="fp32 transposed view copied to contiguous: out[r,c] = in[c*16384 + r], "
+                    "16384 x 16384 (LDS-tiled path)"),
+    "strided_view_f32_2e26_s2": _w(
+        "strided_view_f32_2e26_s2", "copy2d_f32", 1 << 26, 116, "uniform", cols=1 << 26,
+        view=(0, 2, 1 << 27, 0),
+        description="fp32 1-D strided view x[::2] copied to contiguous, 2^26 outputs from a "
+                    "2^27-element array"),
+    "submatrix_f32_16384x16000": _w(
+        "submatrix_f32_16384x16000", "copy2d_f32", 16384 * 16000, 117, "uniform", cols=16000,
+        view=(16384, 1, 16384 * 16384, 3),
+        description="fp32 submatrix view (16384 x 16000 out of 16384-wide rows, starting 3 "
+                    "elements in) copied to contiguous"),
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),
@@ -144,14 +160,14 @@ OP_INPUTS = {
     "saxpy_f32": ("x", "y"), "relu_f32": ("x",), "copy_f32": ("x",),
     "gather_f32": ("x",), "add_relu_f32": ("a", "b"), "saxpy_relu_f32": ("x", "y"),
     "bias_relu_f32": ("x", "bias"), "saxpy_f16": ("x", "y"), "saxpy_bf16": ("x", "y"),
-    "relu_f16": ("x",), "relu_bf16": ("x",),
+    "relu_f16": ("x",), "relu_bf16": ("x",), "copy2d_f32": ("base",),
 }
 OP_DTYPE = {
     "add_f32": np.float32, "add_f16": np.uint16, "add_bf16": np.uint16,
     "saxpy_f32": np.float32, "relu_f32": np.float32, "copy_f32": np.float32,
     "gather_f32": np.float32, "add_relu_f32": np.float32, "saxpy_relu_f32": np.float32,
     "bias_relu_f32": np.float32, "saxpy_f16": np.uint16, "saxpy_bf16": np.uint16,
-    "relu_f16": np.uint16, "relu_bf16": np.uint16,
+    "relu_f16": np.uint16, "relu_bf16": np.uint16, "copy2d_f32": np.float32,
 }
 F16_OPS = ("add_f16", "saxpy_f16", "relu_f16")
 BF16_OPS = ("add_bf16", "saxpy_bf16", "relu_bf16")
@@ -174,4 +190,8 @@ def make_inputs(op: str, n: int, seed: int, dist: str = "uniform", cols: int = 0
 
 
 def workload_inputs(w: Workload) -> dict:
+    if w.op == "copy2d_f32":      # the base array the view looks into
+        g = rng(w.seed)
+        draw = uniform_pm1 if w.dist == "uniform" else normal01
+        return {"base": draw(g, w.view[2])}
     return make_inputs(w.op, w.n, w.seed, w.dist, w.cols)

@@ -52,7 +52,7 @@ def test_binding_names_match_the_c_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert ew.ew_abi_version() == 4
+    assert ew.ew_abi_version() == 5
     for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
                  EW_ERR_NO_DEVICE, EW_ERR_HIP):
         s = ew.ew_status_string(code)
@@ -155,6 +155,24 @@ def test_fused_ops_validation():
         EW_ERR_OVERLAP
 
 
+def test_copy2d_validation():
+    c2 = ew.ew_copy2d_f32
+    assert _status(c2, 0, 1, 1, 0, 0, 5, 0) == EW_OK                      # rows 0
+    assert _status(c2, BASE, 1, 1, BASE + MiB, 5, 0, 0) == EW_OK           # cols 0
+    assert _status(c2, 0, 1, 1, BASE, 4, 4, 0) == EW_ERR_INVALID_ARG
+    assert _status(c2, BASE, 1, 1, 0, 4, 4, 0) == EW_ERR_INVALID_ARG
+    assert _status(c2, BASE, 1, 1, BASE + MiB, 1 << 40, 1 << 40, 0) == EW_ERR_INVALID_ARG
+    # a view reaching below address 0 or past the top of the address space
+    assert _status(c2, 0x1000, -4096, 1, BASE, 4, 4, 0) == EW_ERR_INVALID_ARG
+    assert _status(c2, (1 << 64) - 4096, 1 << 20, 1, BASE, 4, 4, 0) == EW_ERR_INVALID_ARG
+    assert _status(c2, BASE + 2, 1, 4, BASE + MiB, 4, 4, 0) == EW_ERR_MISALIGNED
+    assert _status(c2, BASE, 1, 4, BASE + MiB + 1, 4, 4, 0) == EW_ERR_MISALIGNED
+    # out overlapping the touched span, including through a negative stride
+    assert _status(c2, BASE, 4, 1, BASE + 4 * 15, 4, 4, 0) == EW_ERR_OVERLAP
+    assert _status(c2, BASE + 4096, -256, 1, BASE + 4096 - 256 * 3 * 4, 4, 4, 0) == \
+        EW_ERR_OVERLAP
+
+
 def test_adjacent_ranges_do_not_overlap_and_copy_onto_itself_is_a_no_op():
     n = 1024
     # [BASE, BASE+4n) and [BASE+4n, ...) touch but do not overlap: validation
@@ -211,3 +229,20 @@ def test_launch_config_table_set_get_reset_and_load(tmp_path):
         ew.ew_reset_launch_config()
         if os.path.exists(ew.LAUNCH_TABLE):
             ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+def test_compiled_defaults_match_the_shipped_table():
+    """The library's built-in rows are the tuned table it ships with, so a
+    caller that never loads the file gets the same launches."""
+    rows = []
+    for line in open(ew.LAUNCH_TABLE):
+        f = line.split("#")[0].split()
+        if f:
+            rows.append((f[0], int(f[1]), tuple(int(v) for v in f[2:5])))
+    assert {r[0] for r in rows} == set(ew.OPS)
+    try:
+        ew.ew_reset_launch_config()
+        for op, min_n, cfg in rows:
+            assert ew.ew_get_launch_config(op, min_n) == cfg, (op, min_n)
+    finally:
+        ew.ew_load_launch_table(ew.LAUNCH_TABLE)

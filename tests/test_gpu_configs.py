@@ -24,7 +24,17 @@ def _run(w: synth.Workload):
     es = ELEM[w.op]
     offs = w.offsets
     s = torch.cuda.current_stream().cuda_stream
-    if w.op == "bias_relu_f32":
+    if w.op == "copy2d_f32":
+        sr, sc, _, offset = w.view
+        rows = w.n // w.cols
+        base, _kb = upload(inp["base"], 0)
+        out, _ko = upload(np.zeros(w.n, np.float32), 0)
+        ew.ew_copy2d_f32(base.data_ptr() + 4 * offset, sr, sc, out, rows, w.cols, stream=s)
+        torch.cuda.synchronize()
+        got = download(out, es)
+        del base, _kb, out, _ko
+        ref = oracle.copy2d_f32(inp["base"], offset, sr, sc, rows, w.cols)
+    elif w.op == "bias_relu_f32":
         x, _kx = upload(inp["x"], offs.get("x", 0))
         bias, _kb = upload(inp["bias"], 0)
         y, _ky = upload(np.zeros(w.n, np.float32), offs.get("y", 0))

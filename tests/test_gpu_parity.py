@@ -338,6 +338,74 @@ def test_bias_relu_every_kernel_variant():
             ew.ew_load_launch_table(ew.LAUNCH_TABLE)
 
 
+def _copy2d_case(rows, cols, sr, sc, seed, off_out=0):
+    """One strided-view copy with guard bands around the output; the view
+    starts inside a base buffer so that every touched element exists."""
+    lo = min(0, (rows - 1) * sr) + min(0, (cols - 1) * sc)
+    hi = max(0, (rows - 1) * sr) + max(0, (cols - 1) * sc)
+    offset = -lo + 3
+    base_len = offset + hi + 8
+    base = _f32_pool(base_len, seed)
+    tb, _kb = upload(base)
+    n = rows * cols
+    obuf = torch.full((n + off_out + 32,), -5.0, device=DEV)
+    out = obuf[off_out:off_out + n]
+    ew.ew_copy2d_f32(tb.data_ptr() + 4 * offset, sr, sc, out.data_ptr(), rows, cols)
+    torch.cuda.synchronize()
+    got = download(out, 4)
+    ref = oracle.copy2d_f32(base, offset, sr, sc, rows, cols)
+    bad = mismatches("copy_f32", got, ref)
+    fails = [f"copy2d rows={rows} cols={cols} sr={sr} sc={sc} off={off_out}: "
+             f"{bad.size} mismatches"] if bad.size else []
+    g = obuf.cpu().numpy()
+    if np.any(g[:off_out] != -5.0) or np.any(g[off_out + n:] != -5.0):
+        fails.append(f"copy2d rows={rows} cols={cols} sr={sr} sc={sc}: guard band written")
+    return fails
+
+
+def test_copy2d_paths_shapes_and_strides():
+    print("[parity] copy2d", flush=True)
+    failures = []
+    k = 0
+    for rows, cols in ((1, 1), (1, 7), (3, 5), (64, 64), (65, 63), (1, 1000), (130, 129),
+                       (200, 7), (7, 300), (513, 257)):
+        for sr, sc in ((cols, 1), (cols + 5, 1), (1, rows), (1, rows + 3), (1, -rows),
+                       (-cols, 1), (2 * cols, 2), (3, 7 * rows), (0, 1), (cols, 0), (1, 1)):
+            for off_out in (0, 1):
+                k += 1
+                failures += _copy2d_case(rows, cols, sr, sc, 400 + k, off_out)
+    # 1-D stride-2 views (x[::2]): every length up to 40 and every output
+    # alignment, so the head, the shortened body and the 1-4 element tail
+    # all occur
+    for cols in range(1, 41):
+        for off_out in range(4):
+            k += 1
+            failures += _copy2d_case(1, cols, 0, 2, 400 + k, off_out)
+    assert not failures, failures[:10]
+
+
+def test_copy2d_large_tiles_and_variants():
+    """Several grid-stride rounds for the output-ordered kernel and edge tiles
+    for the transpose, at moderate sizes."""
+    print("[parity] copy2d variants", flush=True)
+    failures = []
+    failures += _copy2d_case(2050, 3001, 1, 2050, 450)          # transpose, ragged tiles
+    failures += _copy2d_case(3001, 2050, 1, 3001 + 64, 451, 1)  # transpose of a padded matrix
+    failures += _copy2d_case(1, 1 << 22, 0, 2, 452, 1)          # x[::2]
+    failures += _copy2d_case(1500, 1999, 2111, 1, 453, 3)       # submatrix, misaligned rows
+    failures += _copy2d_case(999, 1001, -1001, 1, 454)          # rows in reverse order
+    try:
+        for (block, bpc, unroll) in LAUNCHES:
+            _force_launch("copy2d_f32", block, bpc, unroll)
+            failures += _copy2d_case(333, 4097, 4099, 1, 460 + unroll, 1)
+            failures += _copy2d_case(2, 3 * 4096 + 5, 5 * 4096, 3, 470 + unroll)
+    finally:
+        ew.ew_reset_launch_config()
+        if os.path.exists(ew.LAUNCH_TABLE):
+            ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+    assert not failures, failures[:10]
+
+
 def test_exact_aliasing_in_place():
     print("[parity] aliasing", flush=True)
     n = 100003
