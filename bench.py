@@ -49,18 +49,35 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                   "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
-                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8}
+                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8, "relu_inplace_f32": 8}
 DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f32",
          "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32", "add_relu_f32": "f32",
          "saxpy_relu_f32": "f32", "bias_relu_f32": "f32", "saxpy_f16": "f16",
-         "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16", "copy2d_f32": "f32"}
+         "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16", "copy2d_f32": "f32",
+         "relu_inplace_f32": "f32"}
 # The unfused sequence each fused chain replaces, timed beside it.
 UNFUSED = {"add_relu_f32": ("add_f32", "relu_f32"), "saxpy_relu_f32": ("saxpy_f32", "relu_f32")}
 MALL_BYTES = 256 * 2 ** 20
 
 
-def algorithmic_bytes(op: str, n: int, cols: int = 0) -> int:
+def algorithmic_bytes(op: str, n: int, cols: int = 0, changed: int = 0) -> int:
+    """Read + write bytes of one launch.  The in-place ReLU reads every
+    element and writes only the `changed` ones ([PerfNotes] 5.2: an element
+    already >= 0 needs no store)."""
+    if op == "relu_inplace_f32":
+        return 4 * n + 4 * changed
     return BYTES_PER_ELEM[op] * n + (4 * cols if op == "bias_relu_f32" else 0)
+
+
+def relu_store_counts(x, np):
+    """(elements the ReLU changes, 64-byte spans holding one) for a float32
+    input whose first element starts a span: an element changes when its
+    sign bit is set and it is not a NaN."""
+    ch = np.signbit(x) & ~np.isnan(x)
+    n = x.size
+    pad = (-n) % 16
+    spans = np.concatenate([ch, np.zeros(pad, bool)]).reshape(-1, 16).any(axis=1)
+    return int(np.count_nonzero(ch)), int(np.count_nonzero(spans))
 
 
 def kernel_source_hash() -> str:
@@ -84,7 +101,19 @@ class Prepared:
         s = stream.cuda_stream
         self.stream = s
         self.unfused = None
-        if w.op == "copy2d_f32":
+        self.pre = None          # run before every timed launch (in-place ReLU: restore x)
+        self.changed = 0
+        if w.op == "relu_inplace_f32":
+            x, kx = upload(self.inp["x"], offs.get("x", 0))
+            pristine = x.clone()
+            self.keep += [kx, pristine]
+            self.launch = lambda: ew.ew_relu_inplace_f32(x, stream=s)
+            self.pre = lambda: x.copy_(pristine)
+            # the same in-place ReLU storing every element, for comparison
+            self.unfused = lambda: ew.ew_relu_f32(x, x, stream=s)
+            self.changed, self.spans_changed = relu_store_counts(self.inp["x"], np)
+            self.out, self.ptrs = x, (x, x, None)
+        elif w.op == "copy2d_f32":
             sr, sc, _, offset = w.view
             base, kb = upload(self.inp["base"], 0)
             out, ko = upload(np.zeros(w.n, np.float32), 0)
@@ -152,12 +181,16 @@ class Prepared:
         return download(self.out, ELEM[self.w.op])
 
 
-def time_launches(torch, launch, stream, steps, warmup, flush=None):
+def time_launches(torch, launch, stream, steps, warmup, flush=None, pre=None):
     """Average launch time in ms.  Without flush: `steps` back-to-back
     launches between two events on `stream`.  With flush: each launch is
-    bracketed by its own events after a cache-flush write."""
-    for _ in range(warmup):
-        launch()
+    bracketed by its own events after a cache-flush write (and after pre(),
+    which restores an in-place input), median."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            if pre is not None:
+                pre()
+            launch()
     torch.cuda.synchronize()
     if flush is None:
         e0 = torch.cuda.Event(enable_timing=True)
@@ -171,6 +204,8 @@ def time_launches(torch, launch, stream, steps, warmup, flush=None):
     evs = []
     with torch.cuda.stream(stream):
         for _ in range(steps):
+            if pre is not None:
+                pre()
             flush()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
@@ -181,6 +216,36 @@ def time_launches(torch, launch, stream, steps, warmup, flush=None):
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in evs)
     return ts[len(ts) // 2]
+
+
+GRAPH_LAUNCHES = 100
+GRAPH_MAX_N = 1 << 22
+
+
+def time_graph(torch, launch, stream, steps):
+    """Mean time per launch, in ms, of GRAPH_LAUNCHES launches captured into
+    one HIP graph and replayed back to back on `stream` (the launch-bound
+    regime of small arrays: the graph removes the per-call host work and most
+    of the gap between dependent launches)."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(GRAPH_LAUNCHES):
+            launch()
+    replays = max(1, steps // GRAPH_LAUNCHES) * 4
+    with torch.cuda.stream(stream):
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (replays * GRAPH_LAUNCHES)
+    del g
+    return ms
 
 
 def cpu_baseline_leg(w, inp, got, target_s):
@@ -208,7 +273,15 @@ def cpu_baseline_leg(w, inp, got, target_s):
             return oracle.copy2d_f32(d["base"], offset, sr, sc, w.n // w.cols, w.cols)
         if w.op == "gather_f32":
             return oracle.gather_f32(d["x"], w.stride)
+        if w.op == "relu_inplace_f32":     # same result as the out-of-place ReLU
+            return oracle.relu_f32(d["x"])
         return getattr(oracle, w.op)(d["x"])
+
+    def changed(d):
+        if w.op != "relu_inplace_f32":
+            return 0
+        import numpy as np
+        return relu_store_counts(d["x"], np)[0]
 
     t0 = time.perf_counter()
     ref = run(inp)
@@ -216,7 +289,8 @@ def cpu_baseline_leg(w, inp, got, target_s):
     bad = int(mismatches(w.op, got, ref).size)
     del ref
     if target_s <= 0 or w.op == "copy2d_f32":
-        gbs = algorithmic_bytes(w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0) / full_s / 1e9
+        gbs = algorithmic_bytes(w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0,
+                                changed(inp)) / full_s / 1e9
         sample = f"one full pass over all {w.n} elements ({full_s:.2f} s)"
     else:
         m = min(w.n, 1 << 26)
@@ -229,7 +303,7 @@ def cpu_baseline_leg(w, inp, got, target_s):
             el = time.perf_counter() - t0
             if el >= target_s or reps >= 1000:
                 break
-        gbs = algorithmic_bytes(w.op, m) / (el / reps) / 1e9
+        gbs = algorithmic_bytes(w.op, m, 0, changed(small)) / (el / reps) / 1e9
         sample = (f"{w.op} on the first {m} elements of the workload's inputs, {reps} passes "
                   f"in {el:.1f} s")
     rec = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -290,19 +364,42 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     del got
     if bad:
         return res, prep, None
-    nbytes = algorithmic_bytes(w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0)
+    if prep.changed:
+        res["changed"] = prep.changed
+    nbytes = algorithmic_bytes(w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0,
+                               prep.changed)
     footprint = nbytes if w.op != "gather_f32" else 8 * w.n
-    cold = footprint <= 2 * MALL_BYTES
+    # an in-place input must be restored before every launch, so it is
+    # always timed launch by launch, restore and flush outside the events
+    cold = footprint <= 2 * MALL_BYTES or prep.pre is not None
     flush = (lambda: flush_buf.fill_(1)) if cold else None
-    ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush)
+    ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush, pre=prep.pre)
     gbs = nbytes / (ms / 1e3) / 1e9
     res.update({"ms": round(ms, 5), "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
                 "timing": "cold (1 GiB flush before each launch), median" if cold else
                           "back-to-back, mean"})
-    if cold:
+    if cold and prep.pre is None:
         warm_ms = time_launches(torch, prep.launch, stream, steps, 2)
         res["warm_gbs"] = round(nbytes / (warm_ms / 1e3) / 1e9, 1)
-    if prep.unfused is not None:
+    if w.n <= GRAPH_MAX_N and prep.pre is None:
+        eager_ms = warm_ms if cold else ms
+        g_ms = time_graph(torch, prep.launch, stream, steps)
+        res["graph"] = {"launches_per_graph": GRAPH_LAUNCHES, "us_per_launch": round(g_ms * 1e3, 3),
+                        "gbs": round(nbytes / (g_ms / 1e3) / 1e9, 1),
+                        "eager_us_per_launch": round(eager_ms * 1e3, 3),
+                        "timing": "warm: back-to-back replays of one captured graph"}
+    if w.op == "relu_inplace_f32":
+        all_ms = time_launches(torch, prep.unfused, stream, steps, warmup, flush=flush,
+                               pre=prep.pre)
+        n_spans = -(-w.n // 16)
+        span_bytes = 4 * w.n + 64 * prep.spans_changed
+        res["stores"] = {"elements_changed": prep.changed,
+                         "spans_64B_changed_frac": round(prep.spans_changed / n_spans, 4),
+                         "span_bytes_per_launch": span_bytes,
+                         "span_gbs": round(span_bytes / (ms / 1e3) / 1e9, 1)}
+        res["vs_storing_every_element"] = {"op": "ew_relu_f32(x, x)", "ms": round(all_ms, 5),
+                                           "speedup": round(all_ms / ms, 3)}
+    elif prep.unfused is not None:
         un_ms = time_launches(torch, prep.unfused, stream, steps, warmup, flush=flush)
         res["unfused"] = {"ops": list(UNFUSED[w.op]), "ms": round(un_ms, 5),
                           "speedup_of_fused": round(un_ms / ms, 3)}
@@ -371,7 +468,9 @@ def main(argv=None):
                             "unit": "GB/s", "frac": round(res["gbs"] / PEAK_GBS, 4),
                             "traffic": traffic,
                             "kernel": f"ew_stream_kernel<{w.op}, U={res['launch']['unroll']}>",
-                            "algorithmic_bytes_per_launch": algorithmic_bytes(w.op, w.n),
+                            "algorithmic_bytes_per_launch": algorithmic_bytes(
+                                w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0,
+                                res.get("changed", 0)),
                             "avg_launch_ms": res["ms"]}
     del prep
     torch.cuda.empty_cache()

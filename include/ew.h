@@ -108,6 +108,18 @@ ew_status_t ew_saxpy_f32(float alpha, const float *x, float *y, size_t n,
  * x: input, y: output (4-byte aligned); y may equal x exactly. */
 ew_status_t ew_relu_f32(const float *x, float *y, size_t n, hipStream_t stream);
 
+/* x[i] = maximum(x[i], +0) in place, with the result of ew_relu_f32, but
+ * storing only what changes: an element that is already >= 0 (or a NaN)
+ * costs a read and no write ([PerfNotes] section 5.2, the ReLU intensity
+ * example, its second case).  Stores are decided per aligned 64-byte span:
+ * a span holding at least one element to clear is written whole, any other
+ * span is left untouched (a partial span is never written: on MI355X that
+ * costs more than writing it whole).  The body is aligned to 64 bytes by a
+ * scalar head of up to 15 elements.  x: 4-byte aligned.  Errors as for
+ * ew_relu_f32.  On data whose every element is already >= 0 it moves half
+ * the bytes of ew_relu_f32(x, x). */
+ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t stream);
+
 /* out[i] = in[i], bit patterns unchanged (NaN payloads included).
  * [PerfNotes] section 3.2, the coalesced copy kernel.
  * out == in is allowed and launches nothing. */
@@ -212,7 +224,8 @@ int ew_abi_version(void);
 /* Launch configuration, per operation name ("add_f32", "add_f16",
  * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
  * "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16",
- * "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32") and size
+ * "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32")
+ * and size
  * class: a row applies to every n >= min_n up to the next row's min_n.  The
  * grid is min(blocks_per_cu * CU count, number of tiles), where a tile is
  * block * unroll 16-byte vectors; each block walks tiles with a grid stride
@@ -242,6 +255,7 @@ ew_status_t ew_load_launch_table(const char *path);
  * no device is needed (pass cu_count explicitly).
  *   head       elements before the output reaches 16-byte alignment
  *              ((16 - out mod 16) mod 16) / element size, capped at n
+ *              (64-byte alignment, 64 in place of 16, for relu_inplace_f32)
  *   vectors    16-byte vectors in the body, floor((n - head) / vec_elems)
  *   tail       n - head - vectors * vec_elems  (< vec_elems)
  *   in_coaligned[k]  1 if input k's body start is 16-byte aligned too

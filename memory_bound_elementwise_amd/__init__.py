@@ -31,7 +31,7 @@ LAUNCH_TABLE = os.path.join(_PKG, "launch_table.txt")
 
 OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
        "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16", "saxpy_bf16",
-       "relu_f16", "relu_bf16", "copy2d_f32")
+       "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -79,6 +79,7 @@ _c = {
     "ew_add_bf16": _proto("ew_add_bf16", _int, _vp, _vp, _vp, _sz, _vp),
     "ew_saxpy_f32": _proto("ew_saxpy_f32", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
     "ew_relu_f32": _proto("ew_relu_f32", _int, _vp, _vp, _sz, _vp),
+    "ew_relu_inplace_f32": _proto("ew_relu_inplace_f32", _int, _vp, _sz, _vp),
     "ew_copy_f32": _proto("ew_copy_f32", _int, _vp, _vp, _sz, _vp),
     "ew_gather_f32": _proto("ew_gather_f32", _int, _vp, _vp, _sz, _sz, _vp),
     "ew_add_relu_f32": _proto("ew_add_relu_f32", _int, _vp, _vp, _vp, _sz, _vp),
@@ -178,6 +179,12 @@ def ew_relu_f32(x, y, n=None, stream=None):
     """y = maximum(x, +0)."""
     _check(_c["ew_relu_f32"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
            "ew_relu_f32")
+
+
+def ew_relu_inplace_f32(x, n=None, stream=None):
+    """x = maximum(x, +0) in place, storing only the 64-byte spans that change."""
+    _check(_c["ew_relu_inplace_f32"](_addr(x), _numel(x, n), _stream(x, stream)),
+           "ew_relu_inplace_f32")
 
 
 def ew_copy_f32(src, out, n=None, stream=None):

@@ -19,31 +19,33 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 
 struct OpInfo {
     const char *name;
     int elem_size;
     int inputs;          // 1 or 2
     bool alias_ok;       // output may be exactly an input
+    int align;           // the planned head aligns the output body to this many bytes
 };
 
 constexpr OpInfo kOps[kOpCount] = {
-    {"add_f32", 4, 2, true},
-    {"add_f16", 2, 2, true},
-    {"add_bf16", 2, 2, true},
-    {"saxpy_f32", 4, 2, true},
-    {"relu_f32", 4, 1, true},
-    {"copy_f32", 4, 1, true},
-    {"gather_f32", 4, 1, false},
-    {"add_relu_f32", 4, 2, true},
-    {"saxpy_relu_f32", 4, 2, true},
-    {"bias_relu_f32", 4, 1, true},
-    {"saxpy_f16", 2, 2, true},
-    {"saxpy_bf16", 2, 2, true},
-    {"relu_f16", 2, 1, true},
-    {"relu_bf16", 2, 1, true},
-    {"copy2d_f32", 4, 1, false},
+    {"add_f32", 4, 2, true, 16},
+    {"add_f16", 2, 2, true, 16},
+    {"add_bf16", 2, 2, true, 16},
+    {"saxpy_f32", 4, 2, true, 16},
+    {"relu_f32", 4, 1, true, 16},
+    {"copy_f32", 4, 1, true, 16},
+    {"gather_f32", 4, 1, false, 16},
+    {"add_relu_f32", 4, 2, true, 16},
+    {"saxpy_relu_f32", 4, 2, true, 16},
+    {"bias_relu_f32", 4, 1, true, 16},
+    {"saxpy_f16", 2, 2, true, 16},
+    {"saxpy_bf16", 2, 2, true, 16},
+    {"relu_f16", 2, 1, true, 16},
+    {"relu_bf16", 2, 1, true, 16},
+    {"copy2d_f32", 4, 1, false, 16},
+    {"relu_inplace_f32", 4, 1, true, 64},
 };
 
 int op_from_name(const char *name)
@@ -103,6 +105,8 @@ constexpr DefaultRow kDefaults[] = {
     {kOpReluBF16, {size_t(1) << 22, 512, 1024, 1}},
     {kOpCopy2dF32, {0, 1024, 1024, 2}},
     {kOpCopy2dF32, {size_t(1) << 22, 128, 1024, 2}},
+    {kOpReluInplaceF32, {0, 1024, 1, 4}},
+    {kOpReluInplaceF32, {size_t(1) << 22, 128, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
@@ -273,7 +277,8 @@ Plan make_plan(int op, const void *out, const void *in0, const void *in1, size_t
     const size_t vec = 16 / es;
     Plan p{};
     const uintptr_t o = reinterpret_cast<uintptr_t>(out);
-    size_t head = ((16 - (o % 16)) % 16) / es;
+    const size_t al = (size_t)info.align;
+    size_t head = ((al - (o % al)) % al) / es;
     if (head > n) head = n;
     p.head = head;
     p.vectors = (n - head) / vec;
@@ -456,6 +461,26 @@ ew_status_t ew_relu_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 ew_status_t ew_relu_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 {
     return run_stream(kOpReluBF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)
+{
+    if (n == 0) return EW_OK;
+    ew_status_t st = validate(kOpReluInplaceF32, x, x, nullptr, n);
+    if (st != EW_OK) return st;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    const Plan p = make_plan(kOpReluInplaceF32, x, x, nullptr, n, cus);
+    StreamArgs a{};
+    a.in0 = x;
+    a.out = x;
+    a.head = p.head;
+    a.vectors = p.vectors;
+    a.tail = p.tail;
+    a.tiles = p.tiles;
+    const hipError_t e = launch_relu_inplace(a, p.launch, s);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
 ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, float *out,

@@ -24,6 +24,7 @@ enum OpId : int {
     kOpReluF16,
     kOpReluBF16,
     kOpCopy2dF32,
+    kOpReluInplaceF32,
     kOpCount
 };
 
@@ -109,6 +110,11 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
 // (sc == 1, 16-byte loads inside a row), 2: LDS-tiled transpose (sr == 1).
 hipError_t launch_copy2d(const Copy2dArgs &args, int mode, const Launch &launch,
                          hipStream_t stream);
+
+// In-place ReLU on args.out (in0 == out); the body must start 64-byte
+// aligned.
+hipError_t launch_relu_inplace(const StreamArgs &args, const Launch &launch,
+                               hipStream_t stream);
 
 // co: x's body start is 16-byte aligned (it is read with aligned loads).
 hipError_t launch_bias_relu(const BiasArgs &args, bool co, const Launch &launch,

@@ -36,7 +36,9 @@ SIZES = {"small": 1 << 20, "large": 1 << 28}
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                   "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
-                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8}
+                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8,
+                  # in place on normal(0, 1) data: every 64-byte span changes
+                  "relu_inplace_f32": 8}
 BIAS_COLS = 4096
 # copy2d is tuned on a submatrix view: 16384 rows of 16380 columns out of
 # 16384-wide rows (the row-contiguous path, which uses the table).
@@ -76,11 +78,31 @@ def _launcher(op, n, bufs, stream, off_a=0):
     return lambda: ew.ew_gather_f32(pa, c.data_ptr(), 2, n=n, stream=s)
 
 
-def _time(launch, stream, launches, repeats):
+def _time(launch, stream, launches, repeats, restore=None):
+    """Median over `repeats` of the mean launch time in ms.  With `restore`
+    (an in-place op's input must be put back before each launch) every launch
+    is timed by its own events, the restore outside them."""
     for _ in range(3):
+        if restore is not None:
+            restore()
         launch()
     torch.cuda.synchronize()
     out = []
+    if restore is not None:
+        with torch.cuda.stream(stream):
+            for _ in range(repeats):
+                evs = []
+                for _ in range(launches):
+                    restore()
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    launch()
+                    e1.record(stream)
+                    evs.append((e0, e1))
+                torch.cuda.synchronize()
+                out.append(sum(a.elapsed_time(b) for a, b in evs) / launches)
+        return statistics.median(out)
     for _ in range(repeats):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -125,10 +147,17 @@ def tune(ops=ew.OPS, repeats=3, finalists=6, rounds=7, log=None):
                     nbytes = 8 * 1024 * 1020
                 else:
                     nbytes = 8 * C2D_ROWS * C2D_COLS
+            restore = None
+            if op == "relu_inplace_f32":
+                # mixed signs (normal data), put back before every launch
+                x = bufs[2][:n]
+                pristine = torch.randn(n, device=dev)
+                launch = lambda: ew.ew_relu_inplace_f32(x, n=n, stream=stream.cuda_stream)
+                restore = lambda: x.copy_(pristine)
             results = []
             for block, bpc, unroll in itertools.product(BLOCKS, BPC, UNROLLS):
                 _set(op, block, bpc, unroll)
-                ms = _time(launch, stream, launches, repeats)
+                ms = _time(launch, stream, launches, repeats, restore)
                 results.append((nbytes / (ms / 1e3) / 1e9, block, bpc, unroll))
                 if log:
                     log.write(json.dumps({"op": op, "class": cls, "n": n, "stage": 1,
@@ -140,7 +169,7 @@ def tune(ops=ew.OPS, repeats=3, finalists=6, rounds=7, log=None):
             for _ in range(rounds):
                 for sh in shapes:
                     _set(op, *sh)
-                    times[sh].append(_time(launch, stream, launches, 1))
+                    times[sh].append(_time(launch, stream, launches, 1, restore))
             final = sorted(((nbytes / (statistics.median(t) / 1e3) / 1e9,) + sh
                             for sh, t in times.items()), reverse=True)
             if log:

@@ -10,6 +10,8 @@ Recipe (the pages use unseeded ``torch.randn``; every draw here is seeded):
   float32.  Every value is a multiple of 2^-23 in [-1, 1); -0.0, subnormals
   and 1.0 cannot occur (both steps are exact in binary32).
 * normal(0, 1):    ``rng.standard_normal(n, dtype=float32)``.
+* |normal(0, 1)|:  the normal draw with every sign bit cleared (``np.abs``),
+  for the in-place ReLU whose input is already non-negative.
 * binary16 / bfloat16 inputs "cast from fp32": the float32 draw above cast
   round-to-nearest-even by numpy (``astype(float16)``) or torch CPU
   (``.to(bfloat16)``), kept as uint16 bit patterns.
@@ -66,7 +68,7 @@ class Workload:
     op: str               # add_f32 | add_f16 | add_bf16 | saxpy_f32 | relu_f32 | copy_f32 | gather_f32
     n: int
     seed: int
-    dist: str             # "uniform" | "normal"
+    dist: str             # "uniform" | "normal" | "absnormal"
     offsets: dict = field(default_factory=dict)
     alpha: float = 0.0    # saxpy only
     stride: int = 0       # gather only
@@ -149,6 +151,14 @@ WORKLOADS = {
         view=(16384, 1, 16384 * 16384, 3),
         description="fp32 submatrix view (16384 x 16000 out of 16384-wide rows, starting 3 "
                     "elements in) copied to contiguous"),
+    "relu_inplace_f32_2e28": _w(
+        "relu_inplace_f32_2e28", "relu_inplace_f32", 1 << 28, 106, "normal",
+        description="fp32 ReLU in place x=max(x,0), storing only 64-byte spans that change, "
+                    "n=2^28, x normal(0,1) (the ReLU workload's input: signs mixed)"),
+    "relu_inplace_f32_2e28_nonneg": _w(
+        "relu_inplace_f32_2e28_nonneg", "relu_inplace_f32", 1 << 28, 118, "absnormal",
+        description="fp32 ReLU in place, n=2^28, x = |normal(0,1)| (every element already "
+                    ">= 0: nothing to store)"),
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),
@@ -161,6 +171,7 @@ OP_INPUTS = {
     "gather_f32": ("x",), "add_relu_f32": ("a", "b"), "saxpy_relu_f32": ("x", "y"),
     "bias_relu_f32": ("x", "bias"), "saxpy_f16": ("x", "y"), "saxpy_bf16": ("x", "y"),
     "relu_f16": ("x",), "relu_bf16": ("x",), "copy2d_f32": ("base",),
+    "relu_inplace_f32": ("x",),
 }
 OP_DTYPE = {
     "add_f32": np.float32, "add_f16": np.uint16, "add_bf16": np.uint16,
@@ -168,16 +179,25 @@ OP_DTYPE = {
     "gather_f32": np.float32, "add_relu_f32": np.float32, "saxpy_relu_f32": np.float32,
     "bias_relu_f32": np.float32, "saxpy_f16": np.uint16, "saxpy_bf16": np.uint16,
     "relu_f16": np.uint16, "relu_bf16": np.uint16, "copy2d_f32": np.float32,
+    "relu_inplace_f32": np.float32,
 }
 F16_OPS = ("add_f16", "saxpy_f16", "relu_f16")
 BF16_OPS = ("add_bf16", "saxpy_bf16", "relu_bf16")
+
+
+def absnormal(g: np.random.Generator, n: int) -> np.ndarray:
+    """|normal(0, 1)|: the normal draw with its sign bit cleared (exact)."""
+    return np.abs(normal01(g, n))
+
+
+_DRAW = {"uniform": uniform_pm1, "normal": normal01, "absnormal": absnormal}
 
 
 def make_inputs(op: str, n: int, seed: int, dist: str = "uniform", cols: int = 0) -> dict:
     """Draw the inputs of ``op`` (numpy arrays keyed by role) for n elements
     (the bias of bias_relu has `cols` elements)."""
     g = rng(seed)
-    draw = uniform_pm1 if dist == "uniform" else normal01
+    draw = _DRAW[dist]
     out = {}
     for role in OP_INPUTS[op]:
         x = draw(g, cols if role == "bias" else n)
@@ -191,7 +211,5 @@ def make_inputs(op: str, n: int, seed: int, dist: str = "uniform", cols: int = 0
 
 def workload_inputs(w: Workload) -> dict:
     if w.op == "copy2d_f32":      # the base array the view looks into
-        g = rng(w.seed)
-        draw = uniform_pm1 if w.dist == "uniform" else normal01
-        return {"base": draw(g, w.view[2])}
+        return {"base": _DRAW[w.dist](rng(w.seed), w.view[2])}
     return make_inputs(w.op, w.n, w.seed, w.dist, w.cols)

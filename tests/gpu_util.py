@@ -7,7 +7,7 @@ DEV = torch.device("cuda:0")
 ELEM = {"add_f32": 4, "add_f16": 2, "add_bf16": 2, "saxpy_f32": 4, "relu_f32": 4,
         "copy_f32": 4, "gather_f32": 4, "add_relu_f32": 4, "saxpy_relu_f32": 4,
         "bias_relu_f32": 4, "saxpy_f16": 2, "saxpy_bf16": 2, "relu_f16": 2, "relu_bf16": 2,
-        "copy2d_f32": 4}
+        "copy2d_f32": 4, "relu_inplace_f32": 4}
 NP_DTYPE = {4: np.float32, 2: np.uint16}
 TORCH_DTYPE = {4: torch.float32, 2: torch.int16}
 
@@ -50,7 +50,7 @@ def mismatches(op: str, got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     arithmetic ops (fused ones included) a NaN matches any NaN (payloads are
     not part of the contract).  Copy, gather and ReLU compare bitwise
     throughout."""
-    if op in ("copy_f32", "gather_f32", "relu_f32", "copy2d_f32"):
+    if op in ("copy_f32", "gather_f32", "relu_f32", "copy2d_f32", "relu_inplace_f32"):
         g, r = got.view(np.uint32), ref.view(np.uint32)
         return np.nonzero(g != r)[0]
     if op in ("relu_f16", "relu_bf16"):

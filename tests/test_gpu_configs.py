@@ -34,6 +34,12 @@ def _run(w: synth.Workload):
         got = download(out, es)
         del base, _kb, out, _ko
         ref = oracle.copy2d_f32(inp["base"], offset, sr, sc, rows, w.cols)
+    elif w.op == "relu_inplace_f32":
+        x, _kx = upload(inp["x"], offs.get("x", 0))
+        ew.ew_relu_inplace_f32(x, stream=s)
+        torch.cuda.synchronize()
+        got = download(x, es)
+        ref = oracle.relu_f32(inp["x"])
     elif w.op == "bias_relu_f32":
         x, _kx = upload(inp["x"], offs.get("x", 0))
         bias, _kb = upload(inp["bias"], 0)

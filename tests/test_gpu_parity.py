@@ -72,7 +72,31 @@ def _u16_pool(length, seed):
     return pool
 
 
+# Bit patterns at the in-place ReLU's decision boundary: -0, -inf and the
+# most negative finite change; negative NaNs and +0 do not.
+RELU_EDGE_BITS = np.array([0x80000000, 0xFF800000, 0xFF800001, 0xFFC00000, 0xFFFFFFFF,
+                           0x7F800000, 0x00000000, 0x80000001, 0xFF7FFFFF, 0x7FFFFFFF],
+                          dtype=np.uint32)
+
+
+@functools.lru_cache(maxsize=8)
+def _sparse_negative_pool(length, seed):
+    """The f32 pool with every sign cleared, then about one element in 40
+    negated (so most 64-byte spans hold no element to clear and many hold
+    exactly one), with the decision-boundary bit patterns at the start."""
+    pool = np.abs(_f32_pool(length, seed))
+    g = synth.rng(seed + 17)
+    pos = g.integers(0, length, size=max(length // 40, 1))
+    pool[pos] = -pool[pos]
+    k = min(length, RELU_EDGE_BITS.size)
+    pool[:k] = RELU_EDGE_BITS[:k].view(np.float32)
+    pool.setflags(write=False)
+    return pool
+
+
 def _pool(op, length, seed):
+    if op == "relu_inplace_f32":
+        return _sparse_negative_pool(length, seed)
     return _u16_pool(length, seed) if ELEM[op] == 2 else _f32_pool(length, seed)
 
 
@@ -83,6 +107,8 @@ def _oracle(op, ins, n, alpha=2.5, stride=2):
         return getattr(oracle, op)(alpha, ins[0], ins[1])
     if op in ("relu_f32", "relu_f16", "relu_bf16"):
         return getattr(oracle, op)(ins[0])
+    if op == "relu_inplace_f32":
+        return oracle.relu_f32(ins[0])
     if op == "copy_f32":
         return oracle.copy_f32(ins[0])
     return oracle.gather_f32(ins[0], stride)
@@ -96,6 +122,8 @@ def _call(op, out_ptr, in_ptrs, n, alpha=2.5, stride=2):
         getattr(ew, "ew_" + op)(alpha, in_ptrs[0], out_ptr, n=n, stream=s)
     elif op in ("relu_f32", "relu_f16", "relu_bf16"):
         getattr(ew, "ew_" + op)(in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op == "relu_inplace_f32":
+        ew.ew_relu_inplace_f32(out_ptr, n=n, stream=s)
     elif op == "copy_f32":
         ew.ew_copy_f32(in_ptrs[0], out_ptr, n=n, stream=s)
     else:
@@ -107,7 +135,7 @@ def _run_cases(op, cases, seed):
     one sentinel-filled arena; returns a list of failure descriptions."""
     es = ELEM[op]
     dt = NP_DTYPE[es]
-    n_in = 1 if op in ("relu_f32", "copy_f32", "gather_f32", "relu_f16", "relu_bf16") else 2
+    n_in = 1 if op in ONE_INPUT else 2
     max_n = max(c[0] for c in cases)
     pool_len = max_n + 32
     pools = [_pool(op, pool_len, seed + k) for k in range(n_in)]
@@ -126,6 +154,9 @@ def _run_cases(op, cases, seed):
     if op in IN_PLACE:   # y is updated in place: seed each output span with y
         for (n, off_out, offs_in, stride), ob in zip(cases, layout):
             host[ob:ob + n * es] = pools[1][offs_in[1]:offs_in[1] + n].view(np.uint8)
+    if op == "relu_inplace_f32":   # x is the output span itself
+        for (n, off_out, offs_in, stride), ob in zip(cases, layout):
+            host[ob:ob + n * es] = pools[0][offs_in[0]:offs_in[0] + n].view(np.uint8)
     arena = torch.from_numpy(host).to(DEV)
     base = arena.data_ptr()
     assert base % 256 == 0
@@ -159,6 +190,7 @@ def _run_cases(op, cases, seed):
 
 
 IN_PLACE = ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16")
+ONE_INPUT = ("relu_f32", "copy_f32", "gather_f32", "relu_f16", "relu_bf16", "relu_inplace_f32")
 TWO_INPUT = ("add_f32", "add_f16", "add_bf16", "add_relu_f32") + IN_PLACE
 
 
@@ -175,6 +207,9 @@ def _offset_cases(op):
                         if op in IN_PLACE:
                             ob = oo          # y is the output itself
                         cases.append((n, oo, [oa, ob], 0))
+        elif op == "relu_inplace_f32":
+            for oo in range(32):        # every head length of the 64-byte alignment, twice
+                cases.append((n, oo, [(5 * oo) % 29], 2))
         else:
             for oo in range(vec):
                 for oa in range(vec):
@@ -191,7 +226,7 @@ def _offset_cases(op):
 
 ALL_STREAM_OPS = ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32",
                   "gather_f32", "add_relu_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16",
-                  "relu_f16", "relu_bf16"]
+                  "relu_f16", "relu_bf16", "relu_inplace_f32"]
 
 
 @pytest.mark.parametrize("op", ALL_STREAM_OPS)
@@ -261,7 +296,9 @@ def test_every_kernel_variant_several_tiles_ragged(op):
                 "add_f32", "add_f16", "add_bf16", "add_relu_f32") else (
                 1 << 40 if op in IN_PLACE else 0), n, cus)
             assert plan.tiles > 2 * plan.grid, (plan.tiles, plan.grid)
-            if op not in TWO_INPUT:
+            if op == "relu_inplace_f32":
+                offs = [(0, [0]), (1, [1]), (17, [3]), (31, [2])]
+            elif op not in TWO_INPUT:
                 offs = [(1, [1]), (1, [0]), (0, [3])]
             elif op in IN_PLACE:
                 offs = [(1, [2, 1]), (0, [0, 0]), (3, [1, 3])]

@@ -76,7 +76,7 @@ def test_saxpy_kernels_use_a_fused_multiply_add(asm):
 
 def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
     for name, (body, _) in _kernels(asm).items():
-        if "ew_stream_kernel" in name:
+        if "ew_stream_kernel" in name or "relu_inplace" in name:
             assert re.search(r"global_load_dwordx4 .* nt\b", body), name
             assert re.search(r"global_store_dwordx4 .* nt\b", body), name
 
@@ -90,3 +90,14 @@ def test_transpose_moves_16_bytes_per_lane_through_lds(asm):
     assert re.search(r"global_load_dwordx4 .* nt\b", body)
     assert re.search(r"\bds_write_b128\b", body)
     assert re.search(r"global_store_dwordx4 .* nt\b", body)
+
+
+def test_inplace_relu_decides_stores_with_a_wave_vote(asm):
+    """The in-place ReLU stores a 64-byte span whole or not at all: each lane's
+    decision combines the wave's compare mask (a vote) with a 4-lane group
+    mask shifted by the lane index."""
+    ks = [v for k, v in _kernels(asm).items() if "relu_inplace" in k]
+    assert len(ks) == 4
+    for body, _ in ks:
+        assert re.search(r"\bv_mbcnt_(lo|hi)_u32_b32\b", body)     # lane index
+        assert re.search(r"\bv_lshlrev_b64\b", body)               # group mask << lane group
