@@ -102,6 +102,7 @@ class Prepared:
         self.stream = s
         self.unfused = None
         self.pre = None          # run before every timed launch (in-place ReLU: restore x)
+        self.torch_context = None  # (label, launcher) of PyTorch's kernel for the same op
         self.changed = 0
         if w.op == "relu_inplace_f32":
             x, kx = upload(self.inp["x"], offs.get("x", 0))
@@ -138,6 +139,15 @@ class Prepared:
             fn = getattr(ew, "ew_" + w.op)
             self.launch = lambda: fn(a, b, c, stream=s)
             self.out, self.ptrs = c, (c, a, b)
+            tdt = {"add_f32": torch.float32, "add_f16": torch.float16,
+                   "add_bf16": torch.bfloat16}.get(w.op)
+            if tdt is not None:
+                ta, tb, tc = (t.view(tdt) for t in (a, b, c))
+
+                def t_add():
+                    with torch.cuda.stream(stream):
+                        torch.add(ta, tb, out=tc)
+                self.torch_context = ("torch.add(a, b, out=c)", t_add)
             if w.op == "add_relu_f32":
                 def unfused():
                     ew.ew_add_f32(a, b, c, stream=s)
@@ -150,6 +160,11 @@ class Prepared:
             fn = getattr(ew, "ew_" + w.op)
             self.launch = lambda: fn(w.alpha, x, y, stream=s)
             self.out, self.ptrs = y, (y, x, y)
+            if w.op == "saxpy_f32":
+                def t_saxpy():
+                    with torch.cuda.stream(stream):
+                        y.add_(x, alpha=w.alpha)
+                self.torch_context = ("y.add_(x, alpha=2.5)", t_saxpy)
             if w.op == "saxpy_relu_f32":
                 def unfused():
                     ew.ew_saxpy_f32(w.alpha, x, y, stream=s)
@@ -162,8 +177,18 @@ class Prepared:
             if w.op in ("relu_f32", "relu_f16", "relu_bf16"):
                 fn = getattr(ew, "ew_" + w.op)
                 self.launch = lambda: fn(x, y, stream=s)
+                if w.op == "relu_f32":
+                    def t_relu():
+                        with torch.cuda.stream(stream):
+                            torch.relu(x)
+                    self.torch_context = ("torch.relu(x)", t_relu)
             elif w.op == "copy_f32":
                 self.launch = lambda: ew.ew_copy_f32(x, y, stream=s)
+
+                def t_copy():
+                    with torch.cuda.stream(stream):
+                        y.copy_(x)
+                self.torch_context = ("y.copy_(x)", t_copy)
             else:
                 self.launch = lambda: ew.ew_gather_f32(x, y, w.stride, stream=s)
             self.out, self.ptrs = y, (y, x, None)
@@ -179,6 +204,9 @@ class Prepared:
         self.launch()
         torch.cuda.synchronize()
         return download(self.out, ELEM[self.w.op])
+
+
+LAST_DIST = {}     # p10 / p90 of the last per-launch (flushed) timing, in ms
 
 
 def time_launches(torch, launch, stream, steps, warmup, flush=None, pre=None):
@@ -215,6 +243,8 @@ def time_launches(torch, launch, stream, steps, warmup, flush=None, pre=None):
             evs.append((a, b))
     torch.cuda.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in evs)
+    LAST_DIST["p10"] = ts[len(ts) // 10]
+    LAST_DIST["p90"] = ts[(9 * len(ts)) // 10]
     return ts[len(ts) // 2]
 
 
@@ -308,7 +338,51 @@ def cpu_baseline_leg(w, inp, got, target_s):
                   f"in {el:.1f} s")
     rec = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": sample + " (scalar C loop, one thread)", "cpu": _cpu_model()}
+    if target_s > 0 and w.op not in ("copy2d_f32", "gather_f32"):
+        rec["all_cores"] = _all_cores(w, run, changed, small, m, target_s / 2)
     return bad, rec
+
+
+def _all_cores(w, run, changed, small, m, target_s):
+    """The same oracle loop, unchanged, on static contiguous chunks of the
+    sample, one chunk per core of this process's affinity set, run from a
+    thread pool (the C call releases the GIL).  Context for the one-thread
+    figure; the outputs are discarded."""
+    from concurrent.futures import ThreadPoolExecutor
+    cores = len(os.sched_getaffinity(0))
+    unit = w.cols if w.op == "bias_relu_f32" else 16
+    step = -(-m // cores)
+    step = -(-step // unit) * unit
+    parts = []
+    for lo in range(0, m, step):
+        hi = min(m, lo + step)
+        parts.append({k: (v if k == "bias" else v[lo:hi]) for k, v in small.items()})
+    with ThreadPoolExecutor(max_workers=len(parts)) as ex:
+        list(ex.map(run, parts))                       # warm-up, first touch
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            list(ex.map(run, parts))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= target_s or reps >= 1000:
+                break
+    gbs = algorithmic_bytes(w.op, m, 0, changed(small)) / (el / reps) / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": len(parts),
+            "sample": f"the same {m} elements in {len(parts)} contiguous chunks, one thread "
+                      f"each, {reps} passes in {el:.1f} s"}
+
+
+def _clocks():
+    """Current GPU clocks as rocm-smi reports them (None if it is unavailable)."""
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        data = json.loads(out.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
+    return {k: v for k, v in card.items() if "clock" in k.lower()} or None
 
 
 def _cpu_model():
@@ -348,7 +422,7 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
         launch_desc["path"] = ("contiguous 16-byte loads, even elements kept (stride-2 gather "
                                "kernel)" if (w.n == w.cols and sc == 2) else
                                "rows contiguous" if sc == 1 else
-                               "LDS-tiled transpose (64 x 64 tiles, 256 threads)" if sr == 1 else
+                               "LDS-tiled transpose (128 x 128 tiles, 1024 threads)" if sr == 1 else
                                "generic (one 4-byte load per element)")
     res = {"workload": w.name, "op": w.op, "n": w.n, "launch": launch_desc,
            "split": {"head": plan.head, "vectors": plan.vectors, "tail": plan.tail,
@@ -378,6 +452,15 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     res.update({"ms": round(ms, 5), "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
                 "timing": "cold (1 GiB flush before each launch), median" if cold else
                           "back-to-back, mean"})
+    if cold:
+        res["p10_ms"], res["p90_ms"] = round(LAST_DIST["p10"], 5), round(LAST_DIST["p90"], 5)
+    ctx = prep.torch_context
+    if ctx is not None:
+        t_ms = time_launches(torch, ctx[1], stream, steps, warmup, flush=flush)
+        res["torch_context"] = {"op": ctx[0], "ms": round(t_ms, 5),
+                                "gbs": round(nbytes / (t_ms / 1e3) / 1e9, 1),
+                                "note": "PyTorch's own kernel on the same buffers, same timing; "
+                                        "context, not a target"}
     if cold and prep.pre is None:
         warm_ms = time_launches(torch, prep.launch, stream, steps, 2)
         res["warm_gbs"] = round(nbytes / (warm_ms / 1e3) / 1e9, 1)
@@ -439,6 +522,7 @@ def main(argv=None):
 
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.description}")
+    input_sha = {k: synth.sha256(v)[:16] for k, v in synth.workload_inputs(w).items()}
     res, prep, ms = measure(w, torch, np, ew, synth, stream, args.steps, args.warmup, cus,
                             flush_buf, args.cpu_seconds, check=not args.no_cpu_baseline)
     log(f"parity {res['parity']}; {res.get('gbs')} GB/s")
@@ -462,6 +546,9 @@ def main(argv=None):
         "parity": res["parity"],
         "pct_of_peak": round(100 * res["gbs"] / PEAK_GBS, 2) if res.get("gbs") else None,
     }
+    for k in ("p10_ms", "p90_ms", "torch_context", "graph"):
+        if k in res:
+            line[k] = res[k]
     if ms is not None:
         traffic = traffic_for(w.name, res["launch"])
         line["roofline"] = {"bound": "hbm", "achieved": res["gbs"], "peak": PEAK_GBS,
@@ -477,6 +564,8 @@ def main(argv=None):
 
     if "cpu_baseline" in res:
         line["cpu_baseline"] = res.pop("cpu_baseline")
+        if "all_cores" in line["cpu_baseline"]:
+            line["cpu_baseline_all_cores"] = line["cpu_baseline"].pop("all_cores")
 
     if not args.no_others:
         others = []
@@ -492,9 +581,12 @@ def main(argv=None):
             torch.cuda.empty_cache()
         line["other_configs"] = others
 
-    line["env"] = {"device": torch.cuda.get_device_name(0), "cus": cus,
+    line["env"] = {"device": torch.cuda.get_device_name(0),
+                   "arch": getattr(dev_props, "gcnArchName", None), "cus": cus,
+                   "hbm_bytes": dev_props.total_memory, "clocks": _clocks(),
                    "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
-                   "numpy": np.__version__, "kernel_source_sha256_16": kernel_source_hash()}
+                   "numpy": np.__version__, "kernel_source_sha256_16": kernel_source_hash(),
+                   "input_sha256": input_sha}
     print(json.dumps(line), flush=True)
     return 1 if res["parity"] == "FAIL" else 0
 

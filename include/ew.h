@@ -148,7 +148,7 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
  * (coalesced versus strided reads).
  * Paths: rows == 1 with stride_c == 2 reads contiguous 16-byte spans and
  * keeps the even elements; stride_c == 1 reads whole 16-byte row segments;
- * stride_r == 1 moves 64 x 64 tiles through LDS so that both reads and
+ * stride_r == 1 moves 128 x 128 tiles through LDS so that both reads and
  * writes are coalesced; otherwise one 4-byte load per element.  out is written with 16-byte
  * stores after a scalar head.
  * Errors: rows or cols 0 -> EW_OK; null pointers, rows*cols overflow, or a

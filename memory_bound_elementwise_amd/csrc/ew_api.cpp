@@ -106,7 +106,7 @@ constexpr DefaultRow kDefaults[] = {
     {kOpCopy2dF32, {0, 1024, 1024, 2}},
     {kOpCopy2dF32, {size_t(1) << 22, 128, 1024, 2}},
     {kOpReluInplaceF32, {0, 1024, 1, 4}},
-    {kOpReluInplaceF32, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpReluInplaceF32, {size_t(1) << 22, 512, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
@@ -557,9 +557,11 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         mode = 1;
     } else if (stride_r == 1 && rows >= 2 && cols >= 2) {
         mode = 2;
-        const uint64_t tiles = ((rows + 63) / 64) * ((cols + 63) / 64);
-        const uint64_t cap = (uint64_t)cus * 8;   // 8 blocks of 256 per CU resident
-        l.grid = (int)(tiles < cap * 64 ? tiles : cap * 64);
+        // 128 x 128 tiles; the grid is capped at blocks_per_cu blocks per CU
+        // (the table's row for this size), beyond which blocks stride
+        const uint64_t tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
+        const uint64_t cap = (uint64_t)cus * (uint64_t)p.blocks_per_cu;
+        l.grid = (int)(tiles < cap ? tiles : cap);
     }
     const hipError_t e = launch_copy2d(a, mode, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);

@@ -405,7 +405,7 @@ def test_copy2d_paths_shapes_and_strides():
     failures = []
     k = 0
     for rows, cols in ((1, 1), (1, 7), (3, 5), (64, 64), (65, 63), (1, 1000), (130, 129),
-                       (200, 7), (7, 300), (513, 257)):
+                       (200, 7), (7, 300), (513, 257), (128, 128), (127, 129), (256, 385)):
         for sr, sc in ((cols, 1), (cols + 5, 1), (1, rows), (1, rows + 3), (1, -rows),
                        (-cols, 1), (2 * cols, 2), (3, 7 * rows), (0, 1), (cols, 0), (1, 1)):
             for off_out in (0, 1):
@@ -422,8 +422,8 @@ def test_copy2d_paths_shapes_and_strides():
 
 
 def test_copy2d_large_tiles_and_variants():
-    """Several grid-stride rounds for the output-ordered kernel and edge tiles
-    for the transpose, at moderate sizes."""
+    """Several grid-stride rounds for the output-ordered kernel and for the
+    transpose, and edge tiles for the transpose, at moderate sizes."""
     print("[parity] copy2d variants", flush=True)
     failures = []
     failures += _copy2d_case(2050, 3001, 1, 2050, 450)          # transpose, ragged tiles
@@ -436,6 +436,9 @@ def test_copy2d_large_tiles_and_variants():
             _force_launch("copy2d_f32", block, bpc, unroll)
             failures += _copy2d_case(333, 4097, 4099, 1, 460 + unroll, 1)
             failures += _copy2d_case(2, 3 * 4096 + 5, 5 * 4096, 3, 470 + unroll)
+            # transpose: 17 x 24 tiles of 128, more than one block per CU's
+            # worth when blocks_per_cu is 1, so blocks stride over tiles
+            failures += _copy2d_case(2050, 3001, 1, 2050, 480 + unroll, 1)
     finally:
         ew.ew_reset_launch_config()
         if os.path.exists(ew.LAUNCH_TABLE):

@@ -43,12 +43,12 @@ def _kernels(text):
 
 
 def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
-    """Only the transpose kernel stages data in LDS (one 64 x 68 fp32 tile)."""
+    """Only the transpose kernel stages data in LDS (one 128 x 132 fp32 tile)."""
     ks = _kernels(asm)
     assert len(ks) > 100
     for name, (_, meta) in ks.items():
         d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
-        lds = "17408" if "transpose" in name else "0"
+        lds = "67584" if "transpose" in name else "0"
         assert d["group_segment_fixed_size"] == lds, name
         assert d["private_segment_fixed_size"] == "0", name
         assert d["float_denorm_mode_32"] == "3", name
