@@ -195,6 +195,9 @@ class Prepared:
 
     def plan(self, ew, cus):
         out, in0, in1 = self.ptrs
+        if self.w.op == "gather_f32":
+            return ew.ew_make_gather_plan(out.data_ptr(), in0.data_ptr(), self.w.n,
+                                          self.w.stride, cus)
         return ew.ew_make_plan(self.w.op, out.data_ptr(), in0.data_ptr(),
                                in1.data_ptr() if in1 is not None else 0, self.w.n, cus)
 
@@ -417,6 +420,13 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     prep = Prepared(w, torch, np, ew, synth, stream)
     plan = prep.plan(ew, cus)
     launch_desc = {"block": plan.block, "grid": plan.grid, "unroll": plan.unroll}
+    if w.op == "gather_f32":
+        launch_desc["path"] = ("copy kernel" if w.stride % w.n == 1 else
+                               f"{plan.passes} passes, input staged through LDS"
+                               if plan.passes > 1 else
+                               "contiguous 16-byte loads, even elements kept" if
+                               (plan.reps == 2 and w.stride % w.n == 2) else
+                               f"per-output index walk, {plan.reps} segment(s)")
     if w.op == "copy2d_f32":
         sr, sc = w.view[0], w.view[1]
         launch_desc["path"] = ("contiguous 16-byte loads, even elements kept (stride-2 gather "

@@ -263,7 +263,8 @@ ew_status_t ew_load_launch_table(const char *path);
  *              4- or 2-byte aligned 16-byte loads); unused inputs report 1
  *   tiles      ceil(vectors / (block * unroll))
  *   grid       min(blocks_per_cu * cu_count, tiles), at least 1 when n > 0
- *   segment, reps   n and 1, except for the gather (ew_make_gather_plan)
+ *   segment, reps, passes   n, 1 and 1, except for the gather
+ *              (ew_make_gather_plan)
  * Validation is the same as the operation's (in1 is ignored for one-input
  * ops; for saxpy in0 = x and out = y). */
 typedef struct ew_plan {
@@ -281,6 +282,7 @@ typedef struct ew_plan {
     int grid;
     size_t segment;
     int reps;
+    int passes;
 } ew_plan_t;
 
 ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
@@ -295,7 +297,17 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * fetched once rather than g times; otherwise segment = n and reps = 1.
  * (ew_gather_f32 runs the copy kernel when stride mod n == 1, and a kernel
  * that reads the input with contiguous 16-byte loads when stride mod n == 2
- * and reps == 2.)  Same validation as ew_gather_f32. */
+ * and reps == 2.)
+ * When g == 1 and 2 <= s <= 8 (s = stride mod n) the output splits into
+ * passes = s contiguous runs: run k holds the i with floor(s*i / n) == k and
+ * reads every s-th input element from a residue that differs per run, so
+ * slot m of all s runs reads the s consecutive elements s*m .. s*m + s - 1.
+ * The kernel reads the input once, contiguously (staged through LDS), and
+ * writes the s runs; segment = ceil(n / s) (the longest run), vectors =
+ * groups of four slots, head = tail = 0, block = 256 and unroll = 1 whatever
+ * the table says (its blocks_per_cu still caps the grid).  Otherwise
+ * passes = 1.
+ * Same validation as ew_gather_f32. */
 ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
                                 size_t stride, int cu_count, ew_plan_t *plan);
 

@@ -57,7 +57,7 @@ class EwPlan(ctypes.Structure):
         ("n", _sz), ("head", _sz), ("vectors", _sz), ("tail", _sz), ("tiles", _sz),
         ("vec_elems", _int), ("elem_size", _int), ("in_coaligned", _int * 2),
         ("block", _int), ("blocks_per_cu", _int), ("unroll", _int), ("grid", _int),
-        ("segment", _sz), ("reps", _int),
+        ("segment", _sz), ("reps", _int), ("passes", _int),
     ]
 
     def as_dict(self):

@@ -19,7 +19,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 
 struct OpInfo {
     const char *name;
@@ -340,12 +340,44 @@ uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
 // output is g copies of its first n/g elements.  For 2 <= g <= 8 with n/g a
 // multiple of 4 (so every copy has the same 16-byte alignment) the kernel
 // computes one segment and stores each vector g times: every input line is
-// then fetched once instead of g times.  Otherwise one segment of n.
+// then fetched once instead of g times.  For g == 1 and a stride of 2 to 8
+// the output splits into `stride` passes that together read the input
+// contiguously (see GatherArgs).  Otherwise one segment of n.
 void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, GatherArgs *g,
                  Launch *l)
 {
     const uint64_t s = stride % n;
     const uint64_t gcd = std::gcd(s, (uint64_t)n);  // gcd(0, n) == n
+    if (gcd == 1 && s >= 2 && s <= 8) {
+        // Pass decomposition: output pass k (floor(s*i/n) == k) starts at
+        // i_k = ceil(k*n/s) and reads in[s*m + r_k], r_k = s*i_k - k*n; the
+        // r_k are distinct because gcd(s, n) == 1.
+        *g = GatherArgs{};
+        g->in = reinterpret_cast<const uint32_t *>(in);
+        g->out = reinterpret_cast<uint32_t *>(out);
+        g->n = n;
+        g->stride = s;
+        g->passes = (int)s;
+        for (uint64_t k = 0; k < s; ++k) {
+            const unsigned __int128 kn = (unsigned __int128)k * n;
+            const uint64_t ik = (uint64_t)((kn + s - 1) / s);
+            const uint64_t r = (uint64_t)((unsigned __int128)s * ik - kn);
+            g->dest[r] = ik;
+        }
+        g->seg = (n + s - 1) / s;
+        g->reps = 1;
+        g->vectors = (g->seg + 3) / 4;
+        // fixed block shape (one group per thread); the table's
+        // blocks_per_cu still caps the grid
+        const Row r = get_row(kOpGatherF32, n);
+        const uint64_t tile = (uint64_t)gather_passes_threads();
+        g->tiles = (g->vectors + tile - 1) / tile;
+        uint64_t grid = (uint64_t)r.blocks_per_cu * (uint64_t)(cus > 0 ? cus : 1);
+        if (grid > g->tiles) grid = g->tiles;
+        if (grid == 0) grid = 1;
+        *l = Launch{gather_passes_threads(), (int)grid, 1};
+        return;
+    }
     uint64_t reps = 1, seg = n;
     if (gcd >= 2 && gcd <= 8 && (n / gcd) % 4 == 0) {
         reps = gcd;
@@ -687,6 +719,7 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const
     plan->vec_elems = 16 / info.elem_size;
     plan->in_coaligned[0] = plan->in_coaligned[1] = 1;
     plan->reps = 1;
+    plan->passes = 1;
     const Row r = get_row(id, n);
     plan->block = r.block;
     plan->blocks_per_cu = r.blocks_per_cu;
@@ -702,6 +735,7 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const
     plan->grid = p.launch.grid;
     plan->segment = n;
     plan->reps = 1;
+    plan->passes = 1;
     return EW_OK;
 }
 
@@ -718,7 +752,7 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     Launch l{};
     gather_plan(static_cast<const float *>(in), static_cast<float *>(const_cast<void *>(out)), n,
                 stride, cu_count, &g, &l);
-    const Row r = get_row(kOpGatherF32, (size_t)g.seg);
+    const Row r = get_row(kOpGatherF32, g.passes ? n : (size_t)g.seg);
     plan->n = n;
     plan->head = g.head;
     plan->vectors = g.vectors;
@@ -733,6 +767,7 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     plan->grid = l.grid;
     plan->segment = g.seg;
     plan->reps = (int)g.reps;
+    plan->passes = g.passes ? g.passes : 1;
     return EW_OK;
 }
 

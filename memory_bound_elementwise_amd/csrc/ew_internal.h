@@ -62,6 +62,15 @@ struct GatherArgs {
     uint64_t step_vec;   // stride * 4 * blockDim            (mod n): next unrolled vector
     uint64_t step_tile;  // stride * 4 * blockDim * unroll * gridDim (mod n): next tile
     int wide;            // 1 if stride * (n - 1) can exceed 2^64 - 1
+    // Pass decomposition (gcd(stride, n) == 1, 2 <= stride <= 8): passes ==
+    // stride, otherwise 0.  Output pass k is the run of i with
+    // floor(stride * i / n) == k; it reads in[stride * m + r] for m = 0, 1,
+    // ... where the residue r = (-k * n) mod stride differs from pass to pass.
+    // dest[r] is the first output index of the pass with residue r; seg is
+    // ceil(n / stride) (the longest pass) and vectors counts groups of four
+    // slots m.
+    int passes;
+    uint64_t dest[8];
 };
 
 // Bias + ReLU over a row-major rows x cols matrix (n = rows * cols): the
@@ -105,6 +114,10 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
                          hipStream_t stream);
+
+// Threads per block of the pass-decomposed gather (one group of four slots
+// per thread, one tile per block and round).
+int gather_passes_threads();
 
 // mode 0: generic (one 4-byte load per element), 1: rows contiguous
 // (sc == 1, 16-byte loads inside a row), 2: LDS-tiled transpose (sr == 1).

@@ -419,6 +419,79 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
     }
 }
 
+// Small strides coprime with n (2 <= s <= 8, gcd(s, n) == 1): read every
+// input element once.  Output index i reads in[s*i - k*n] where
+// k = floor(s*i / n), so the output is s contiguous passes (k = 0 .. s-1),
+// pass k reading every s-th input element from a residue r_k = (-k*n) mod s,
+// and the s residues are all different.  Slot m of all s passes together
+// therefore reads the s consecutive elements in[s*m .. s*m + s - 1].
+//
+// Each lane takes four slots (a group); a wave takes 64 groups, i.e. 1024 * s
+// consecutive input bytes.  The wave reads them with s contiguous 16-byte-
+// per-lane loads (1 KiB per instruction), parks them in its own part of LDS,
+// and each lane reads back its 16 * s bytes; then, for each residue r, it
+// writes the four values in[s*(m+q) + r] (q = 0..3) as one 16-byte store to
+// its pass's output run at dest[r] + m.  Letting each lane load its own 16 * s
+// bytes directly instead (s loads 16 * s bytes apart across the lanes) ran
+// 14 % (s = 3) to 70 % (s = 7) slower on MI355X.  The register permutation is
+// fixed at compile time (S is a template parameter); only the destinations
+// are runtime values.  Blocks are 256 threads; a tile is 256 groups.
+constexpr int kPassThreads = 256;
+
+template <int S>
+__global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
+{
+    __shared__ u32x4 buf[kPassThreads / 64][64 * S];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
+        const uint64_t grp0 = t * kPassThreads + wv * 64;     // first group of this wave
+        const uint64_t wbase = (uint64_t)S * 4 * grp0;        // its first input element
+        const bool wfull = (grp0 + 64) * 4 * S <= g.n;       // the wave's span is in range
+        if (wfull) {
+#pragma unroll
+            for (int v = 0; v < S; ++v)
+                buf[wv][64 * v + lane] = load16<false, 4>(
+                    reinterpret_cast<const char *>(g.in + wbase + 4 * (64 * v + lane)));
+        }
+        __syncthreads();
+        const uint64_t grp = grp0 + lane;
+        if (grp < g.vectors) {
+            const uint64_t base = (uint64_t)S * 4 * grp;
+            u32x4 e[S];
+            if (wfull) {
+#pragma unroll
+                for (int v = 0; v < S; ++v) e[v] = buf[wv][S * lane + v];
+            } else {
+#pragma unroll
+                for (int v = 0; v < S; ++v)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint64_t x = base + 4 * v + q;
+                        e[v][q] = x < g.n ? g.in[x] : 0u;
+                    }
+            }
+            const bool full = base + 4 * S <= g.n;
+#pragma unroll
+            for (int r = 0; r < S; ++r) {
+                u32x4 w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = e[(S * q + r) / 4][(S * q + r) % 4];
+                uint32_t *dst = g.out + g.dest[r] + 4 * grp;
+                if (full) {
+                    u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(dst);
+                    if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
+                    else *p = w;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (base + (uint64_t)S * q + r < g.n) dst[q] = w[q];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Stride 2 with two equal segments (n even, n/2 a multiple of 4): output i of
 // the first segment reads in[2i] and never wraps.  Instead of four scalar
 // loads per vector, each wave reads its 2 KiB input span with two contiguous
@@ -891,11 +964,26 @@ hipError_t launch_bias_relu(const BiasArgs &args, bool co, const Launch &l, hipS
     return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
 }
 
+int gather_passes_threads() { return kPassThreads; }
+
 hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
 {
     GatherArgs a = args;
     void *kargs[] = {&a};
     const void *fn = nullptr;
+    if (args.passes >= 2) {
+        switch (args.passes) {
+        case 2: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<2>); break;
+        case 3: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<3>); break;
+        case 4: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<4>); break;
+        case 5: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<5>); break;
+        case 6: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<6>); break;
+        case 7: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<7>); break;
+        case 8: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<8>); break;
+        default: return hipErrorInvalidValue;
+        }
+        return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, 0, s);
+    }
     if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {
         // co-alignment of the input's body start: in + 8 * head
         const bool co = ((reinterpret_cast<uintptr_t>(args.in) + 8 * args.head) & 15u) == 0;

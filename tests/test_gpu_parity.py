@@ -11,6 +11,7 @@
 * exact aliasing where the ABI allows it.
 """
 import functools
+import math
 import os
 
 import numpy as np
@@ -255,6 +256,50 @@ def test_gather_brute_force_strides():
             cases.append((n, oo, [0], stride))
     failures = _run_cases("gather_f32", cases, seed=310)
     assert not failures, failures[:10]
+
+
+def test_gather_pass_decomposition_small_strides():
+    """Strides 2..8 coprime with n take the pass-decomposed kernel: every
+    such stride at every n up to 80 and at ragged larger n, with aligned and
+    misaligned input and output."""
+    import math
+    print("[parity] gather passes", flush=True)
+    cases = []
+    for n in list(range(3, 81)) + [1000, 4099, 65537, (1 << 20) + 1, 3 * 5 * 7 * 4096 + 1]:
+        for s in range(2, 9):
+            if s >= n or math.gcd(s, n) != 1:
+                continue
+            for oo, oi in ((0, 0), (1, 0), (0, 3), (3, 2)):
+                cases.append((n, oo, [oi], s))
+    failures = _run_cases("gather_f32", cases, seed=315)
+    assert not failures, failures[:10]
+
+
+def test_gather_pass_decomposition_launch_variants():
+    """The pass-decomposed gather under forced grid caps (its block shape is
+    fixed), at sizes where the grid-stride loop runs three rounds and the
+    last tile is partial."""
+    print("[parity] gather passes variants", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        for (block, bpc, unroll) in LAUNCHES:
+            _force_launch("gather_f32", block, bpc, unroll)
+            cases = []
+            if bpc > 8:
+                continue      # the kernel's block shape is fixed: only the grid cap varies
+            for s in (3, 5, 8):
+                n = (2 * bpc * cus + 1) * 256 * 4 * s - 7
+                while math.gcd(n, s) != 1:
+                    n += 1
+                p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
+                assert p.passes == s and p.tiles > 2 * p.grid, (s, p.tiles, p.grid)
+                cases += [(n, 1, [2], s), (n, 0, [0], s)]
+            failures = _run_cases("gather_f32", cases, seed=330)
+            assert not failures, (block, bpc, unroll, failures[:5])
+    finally:
+        ew.ew_reset_launch_config()
+        if os.path.exists(ew.LAUNCH_TABLE):
+            ew.ew_load_launch_table(ew.LAUNCH_TABLE)
 
 
 def _table_min_ns(op):

@@ -3,7 +3,8 @@
 The library's numerics rest on instruction choices the compiler could change
 silently; these checks fail the build's tests if it does:
 
-* no LDS (except the transpose's one tile) and no scratch (register spills);
+* no LDS (except the transpose's tile and the pass gather's staging) and no
+  scratch (register spills);
 * float denormal modes "preserve" for binary32 and binary16/64;
 * no packed-fp32 instructions (the library is built without them);
 * no single-rounding mixed-precision fma into a 16-bit result
@@ -43,12 +44,15 @@ def _kernels(text):
 
 
 def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
-    """Only the transpose kernel stages data in LDS (one 128 x 132 fp32 tile)."""
+    """Only the transpose (one 128 x 132 fp32 tile) and the pass-decomposed
+    gather (16 * stride bytes per lane) stage data in LDS."""
     ks = _kernels(asm)
     assert len(ks) > 100
     for name, (_, meta) in ks.items():
         d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
-        lds = "67584" if "transpose" in name else "0"
+        lds = "67584" if "transpose" in name else (
+            str(4096 * int(re.search(r"passes_kernelILi(\d)E", name).group(1)))
+            if "gather_passes" in name else "0")
         assert d["group_segment_fixed_size"] == lds, name
         assert d["private_segment_fixed_size"] == "0", name
         assert d["float_denorm_mode_32"] == "3", name

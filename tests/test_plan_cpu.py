@@ -129,23 +129,65 @@ def test_plan_rejects_what_the_operation_rejects():
         ew.ew_make_plan("add_f32", BASE + 2 * MiB, BASE, BASE + MiB, 16, 0)  # no CUs
 
 
-@pytest.mark.parametrize("n,stride,reps,segment", [
-    (1 << 26, 2, 2, 1 << 25),        # the stride-2 workload: two equal halves
-    ((1 << 26) + 1, 2, 1, (1 << 26) + 1),   # odd n: gcd 1, one segment
-    (1024, 4, 4, 256),
-    (1200, 6, 6, 200),
-    (1200, 12, 1, 1200),             # gcd 12 > 8: no replication
-    (1002, 2, 1, 1002),              # n/2 = 501 not a multiple of 4
-    (1024, 1026, 2, 512),            # stride reduced mod n first
-    (1 << 20, 3, 1, 1 << 20),        # odd stride, power-of-two n: a permutation
-    (16, 16, 1, 16),                 # stride == n: gcd(0, n) = n > 8
-    (8, 8, 1, 8),                    # gcd 8 but n/8 = 1 is not a multiple of 4
+@pytest.mark.parametrize("n,stride,reps,segment,passes", [
+    (1 << 26, 2, 2, 1 << 25, 1),     # the stride-2 workload: two equal halves
+    ((1 << 26) + 1, 2, 1, (1 << 25) + 1, 2),   # odd n: gcd 1, two passes
+    (1024, 4, 4, 256, 1),
+    (1200, 6, 6, 200, 1),
+    (1200, 12, 1, 1200, 1),          # gcd 12 > 8: no replication
+    (1002, 2, 1, 1002, 1),           # n/2 = 501 not a multiple of 4
+    (1024, 1026, 2, 512, 1),         # stride reduced mod n first
+    (1 << 20, 3, 1, 349526, 3),      # stride 3, power-of-two n: three passes
+    ((1 << 20) + 1, 9, 1, (1 << 20) + 1, 1),   # gcd 1 but stride 9 > 8: per output
+    (16, 16, 1, 16, 1),              # stride == n: gcd(0, n) = n > 8
+    (8, 8, 1, 8, 1),                 # gcd 8 but n/8 = 1 is not a multiple of 4
 ])
-def test_gather_plan_segments(n, stride, reps, segment):
+def test_gather_plan_segments(n, stride, reps, segment, passes):
     p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
-    assert (p.reps, p.segment) == (reps, segment)
-    assert p.head + p.vectors * 4 + p.tail == segment
-    assert p.head == 0 and p.tail == segment % 4
+    assert (p.reps, p.segment, p.passes) == (reps, segment, passes)
+    if passes == 1:
+        assert p.head + p.vectors * 4 + p.tail == segment
+        assert p.head == 0 and p.tail == segment % 4
+    else:
+        assert p.head == 0 and p.tail == 0 and p.vectors == -(-segment // 4)
+        assert (p.block, p.unroll) == (256, 1)
+        assert p.tiles == -(-p.vectors // 256)
+        assert p.grid == min(p.tiles, p.blocks_per_cu * CUS)
+
+
+def _passes(n, s):
+    """(first output index, residue) of each pass k = 0 .. s-1."""
+    out = []
+    for k in range(s):
+        ik = -(-k * n // s)
+        out.append((ik, s * ik - k * n))
+    return out
+
+
+def test_gather_pass_decomposition_matches_the_definition():
+    """For gcd(s, n) == 1 the outputs with floor(s*i/n) == k form a run that
+    reads in[s*m + r_k], m = 0, 1, ..., from residues r_k that are all
+    different; checked against the oracle's output (a property of the
+    definition, on the CPU), with the planner's pass count and run length."""
+    import math
+    import numpy as np
+    import oracle
+    x = np.arange(1, 1001, dtype=np.uint32).view(np.float32)
+    for n in list(range(3, 120)) + [997, 1000]:
+        for s in range(2, 9):
+            if s >= n or math.gcd(s, n) != 1:
+                continue
+            p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, s, CUS)
+            assert p.passes == s and p.segment == -(-n // s)
+            runs = _passes(n, s)
+            assert sorted(r for _, r in runs) == list(range(s))
+            out = oracle.gather_f32(x[:n], s).view(np.uint32)
+            xs = x[:n].view(np.uint32)
+            ends = [ik for ik, _ in runs[1:]] + [n]
+            for (ik, r), end in zip(runs, ends):
+                m = np.arange(end - ik)
+                assert np.array_equal(out[ik:end], xs[s * m + r]), (n, s, ik, r)
+                assert s * (end - ik) + r >= n > s * (end - ik - 1) + r
 
 
 def test_gather_replicated_segments_match_the_definition():
@@ -157,6 +199,8 @@ def test_gather_replicated_segments_match_the_definition():
     for n in range(4, 257, 4):
         for stride in range(1, 2 * n + 3):
             p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
+            if p.passes > 1:
+                continue
             assert p.reps * p.segment == n
             if p.reps > 1:
                 out = oracle.gather_f32(x[:n], stride).view(np.uint32)
