@@ -431,6 +431,8 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
         sr, sc = w.view[0], w.view[1]
         launch_desc["path"] = ("contiguous 16-byte loads, even elements kept (stride-2 gather "
                                "kernel)" if (w.n == w.cols and sc == 2) else
+                               f"span read contiguously through LDS, one element in {sc} kept"
+                               if (w.n == w.cols and 3 <= sc <= 8) else
                                "rows contiguous" if sc == 1 else
                                "LDS-tiled transpose (128 x 128 tiles, 1024 threads)" if sr == 1 else
                                "generic (one 4-byte load per element)")

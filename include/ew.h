@@ -147,7 +147,9 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
  * [PerfNotes] 3.4 (non-contiguous tensors show up as strides) and 3.1-3.2
  * (coalesced versus strided reads).
  * Paths: rows == 1 with stride_c == 2 reads contiguous 16-byte spans and
- * keeps the even elements; stride_c == 1 reads whole 16-byte row segments;
+ * keeps the even elements; rows == 1 with 3 <= stride_c <= 8 reads the
+ * view's span contiguously (staged through LDS) and keeps one element in
+ * stride_c; stride_c == 1 reads whole 16-byte row segments;
  * stride_r == 1 moves 128 x 128 tiles through LDS so that both reads and
  * writes are coalesced; otherwise one 4-byte load per element.  out is written with 16-byte
  * stores after a scalar head.

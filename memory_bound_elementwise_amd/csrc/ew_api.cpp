@@ -557,8 +557,9 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
     a.step_tile_c = (uint64_t)(st_t % cols);
     // Path: a 1-D view with stride 2 (x[::2]) reads contiguous 16-byte spans
     // and keeps the even elements (the stride-2 gather kernel, one segment,
-    // no wrap); rows contiguous; a transposed view (tiles through LDS);
-    // generic.
+    // no wrap); a 1-D view with stride 3..8 keeps one element in s of
+    // contiguously read spans; rows contiguous; a transposed view (tiles
+    // through LDS); generic.
     if (rows == 1 && stride_c == 2) {
         GatherArgs g{};
         g.in = a.in;
@@ -580,6 +581,29 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         Launch lg = pg.launch;
         const uint64_t cap = (uint64_t)pg.blocks_per_cu * (uint64_t)cus;
         lg.grid = (int)(g.tiles == 0 ? 1 : (g.tiles < cap ? g.tiles : cap));
+        const hipError_t e = launch_gather(g, lg, s);
+        return e == hipSuccess ? EW_OK : fail_hip(e);
+    }
+    if (rows == 1 && stride_c >= 3 && stride_c <= 8) {
+        // x[::s]: the residue-0 pass of the pass-decomposed gather; each wave
+        // reads its 1 KiB * s input span contiguously and keeps every s-th
+        // element.  n (the kernel's input length) is the view's extent.
+        GatherArgs g{};
+        g.in = a.in;
+        g.out = a.out;
+        g.stride = (uint64_t)stride_c;
+        g.n = (uint64_t)stride_c * (n - 1) + 1;
+        g.passes = (int)stride_c;
+        g.first_only = 1;
+        g.dest[0] = 0;
+        g.seg = n;
+        g.reps = 1;
+        g.vectors = (n + 3) / 4;
+        const uint64_t tile = (uint64_t)gather_passes_threads();
+        g.tiles = (g.vectors + tile - 1) / tile;
+        const uint64_t cap = (uint64_t)p.blocks_per_cu * (uint64_t)cus;
+        Launch lg{gather_passes_threads(), (int)(g.tiles < cap ? g.tiles : cap), 1};
+        if (lg.grid == 0) lg.grid = 1;
         const hipError_t e = launch_gather(g, lg, s);
         return e == hipSuccess ? EW_OK : fail_hip(e);
     }

@@ -71,6 +71,9 @@ struct GatherArgs {
     // slots m.
     int passes;
     uint64_t dest[8];
+    // 1: store only the residue-0 pass (a 1-D strided view x[::stride]: n is
+    // then the view's input extent stride * (count - 1) + 1 and dest[0] = 0).
+    int first_only;
 };
 
 // Bias + ReLU over a row-major rows x cols matrix (n = rows * cols): the

@@ -436,9 +436,11 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // 14 % (s = 3) to 70 % (s = 7) slower on MI355X.  The register permutation is
 // fixed at compile time (S is a template parameter); only the destinations
 // are runtime values.  Blocks are 256 threads; a tile is 256 groups.
+// FirstOnly keeps only the residue-0 pass: that is the strided view
+// x[::S] (out[m] = in[S*m]), read as contiguous spans of which 1/S is kept.
 constexpr int kPassThreads = 256;
 
-template <int S>
+template <int S, bool FirstOnly>
 __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
 {
     __shared__ u32x4 buf[kPassThreads / 64][64 * S];
@@ -472,7 +474,7 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
             }
             const bool full = base + 4 * S <= g.n;
 #pragma unroll
-            for (int r = 0; r < S; ++r) {
+            for (int r = 0; r < (FirstOnly ? 1 : S); ++r) {
                 u32x4 w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = e[(S * q + r) / 4][(S * q + r) % 4];
@@ -972,16 +974,20 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
     void *kargs[] = {&a};
     const void *fn = nullptr;
     if (args.passes >= 2) {
+#define EW_PASS_FN(S) (args.first_only                                                        \
+                           ? reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, true>)   \
+                           : reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, false>))
         switch (args.passes) {
-        case 2: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<2>); break;
-        case 3: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<3>); break;
-        case 4: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<4>); break;
-        case 5: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<5>); break;
-        case 6: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<6>); break;
-        case 7: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<7>); break;
-        case 8: fn = reinterpret_cast<const void *>(&ew_gather_passes_kernel<8>); break;
+        case 2: fn = EW_PASS_FN(2); break;
+        case 3: fn = EW_PASS_FN(3); break;
+        case 4: fn = EW_PASS_FN(4); break;
+        case 5: fn = EW_PASS_FN(5); break;
+        case 6: fn = EW_PASS_FN(6); break;
+        case 7: fn = EW_PASS_FN(7); break;
+        case 8: fn = EW_PASS_FN(8); break;
         default: return hipErrorInvalidValue;
         }
+#undef EW_PASS_FN
         return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, 0, s);
     }
     if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {

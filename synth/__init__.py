@@ -146,6 +146,16 @@ WORKLOADS = {
         view=(0, 2, 1 << 27, 0),
         description="fp32 1-D strided view x[::2] copied to contiguous, 2^26 outputs from a "
                     "2^27-element array"),
+    "strided_view_f32_2e24_s3": _w(
+        "strided_view_f32_2e24_s3", "copy2d_f32", 1 << 24, 119, "uniform", cols=1 << 24,
+        view=(0, 3, 3 << 24, 0),
+        description="fp32 1-D strided view x[::3] copied to contiguous, 2^24 outputs from a "
+                    "3*2^24-element array"),
+    "strided_view_f32_2e24_s8": _w(
+        "strided_view_f32_2e24_s8", "copy2d_f32", 1 << 24, 120, "uniform", cols=1 << 24,
+        view=(0, 8, 1 << 27, 0),
+        description="fp32 1-D strided view x[::8] copied to contiguous, 2^24 outputs from a "
+                    "2^27-element array"),
     "submatrix_f32_16384x16000": _w(
         "submatrix_f32_16384x16000", "copy2d_f32", 16384 * 16000, 117, "uniform", cols=16000,
         view=(16384, 1, 16384 * 16384, 3),

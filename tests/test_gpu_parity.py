@@ -463,6 +463,13 @@ def test_copy2d_paths_shapes_and_strides():
         for off_out in range(4):
             k += 1
             failures += _copy2d_case(1, cols, 0, 2, 400 + k, off_out)
+    # 1-D views x[::s], s = 3..8 (one element kept per s of a contiguously
+    # read span): short and ragged lengths, every output alignment
+    for sc in range(3, 9):
+        for cols in list(range(1, 21)) + [255, 256, 257, 1000, 4099]:
+            for off_out in (0, 1, 3):
+                k += 1
+                failures += _copy2d_case(1, cols, 0, sc, 400 + k, off_out)
     assert not failures, failures[:10]
 
 
@@ -474,6 +481,8 @@ def test_copy2d_large_tiles_and_variants():
     failures += _copy2d_case(2050, 3001, 1, 2050, 450)          # transpose, ragged tiles
     failures += _copy2d_case(3001, 2050, 1, 3001 + 64, 451, 1)  # transpose of a padded matrix
     failures += _copy2d_case(1, 1 << 22, 0, 2, 452, 1)          # x[::2]
+    failures += _copy2d_case(1, (1 << 21) + 5, 0, 3, 455, 2)    # x[::3], many tiles
+    failures += _copy2d_case(1, (1 << 20) + 3, 0, 8, 456)       # x[::8]
     failures += _copy2d_case(1500, 1999, 2111, 1, 453, 3)       # submatrix, misaligned rows
     failures += _copy2d_case(999, 1001, -1001, 1, 454)          # rows in reverse order
     try:
