@@ -18,10 +18,19 @@
 //     requests; [PerfNotes] section 2.2, hide latency rather than reduce it);
 //   * non-temporal stores: nothing written is read again by this kernel.
 //
-// No LDS and no matrix cores: every byte is used once and nothing is
-// contracted.  Inputs whose body start is not 16-byte aligned relative to the
-// output are read with element-aligned 16-byte loads (the hardware splits
-// them across cache lines); the output is always aligned.
+// No matrix cores: nothing is contracted.  The streaming kernels use no LDS
+// either (every byte is used once); LDS only reorders data where the access
+// order of the input and the output differ -- the transpose's tiles and the
+// pass-decomposed gather's staging.  Inputs whose body start is not 16-byte
+// aligned relative to the output are read with element-aligned 16-byte loads
+// (the hardware splits them across cache lines); the streaming kernels'
+// output is always aligned.
+//
+// Kernels in this file: ew_stream_kernel (every one-pass operation and the
+// fused chains), ew_gather_kernel / ew_gather_passes_kernel /
+// ew_gather2_kernel (the strided gather), ew_bias_relu_kernel,
+// ew_copy2d_kernel and ew_transpose_kernel (strided views), and
+// ew_relu_inplace_kernel.
 //
 // Numerics: IEEE binary32 arithmetic in round-to-nearest-even with
 // subnormals preserved (the code object's float denorm modes are "preserve";
