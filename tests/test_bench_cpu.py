@@ -1,0 +1,68 @@
+"""bench.py's host-side bookkeeping, without a GPU: byte formulas, the
+in-place ReLU's store counts, the traffic record lookup and the one-GPU
+contract."""
+import json
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from tests.conftest import ROOT
+
+
+def test_algorithmic_bytes_follow_the_read_plus_write_rule():
+    n = (1 << 28) + 3
+    assert bench.algorithmic_bytes("add_f32", n) == 12 * n         # headline: 3221225508
+    assert bench.algorithmic_bytes("add_f32", n) == 3221225508
+    assert bench.algorithmic_bytes("add_f16", 10) == 60
+    assert bench.algorithmic_bytes("relu_f32", 10) == 80
+    assert bench.algorithmic_bytes("bias_relu_f32", 4096 * 3, 4096) == 8 * 4096 * 3 + 4 * 4096
+    # in place: every element read, only the changed ones written
+    assert bench.algorithmic_bytes("relu_inplace_f32", 100, 0, 0) == 400
+    assert bench.algorithmic_bytes("relu_inplace_f32", 100, 0, 37) == 400 + 4 * 37
+
+
+def test_relu_store_counts_follow_the_reading_of_the_relu():
+    """Changed: sign bit set and not a NaN (so -0 and -inf count, negative
+    NaNs do not); spans are 16 elements (64 bytes)."""
+    bits = np.zeros(40, np.uint32)                      # +0: unchanged
+    bits[3] = 0x80000000                                # -0 -> +0
+    bits[17] = 0xFF800000                               # -inf
+    bits[20] = 0xFFC00000                               # negative NaN: kept
+    bits[39] = 0xBF800000                               # -1
+    changed, spans = bench.relu_store_counts(bits.view(np.float32), np)
+    assert changed == 3
+    assert spans == 3                                   # spans 0, 1 and 2 (elements 32..39)
+    assert bench.relu_store_counts(np.abs(np.arange(-5, 5, dtype=np.float32)), np) == (0, 0)
+
+
+def test_traffic_is_reported_only_for_the_current_kernel_source(tmp_path, monkeypatch):
+    rec = {"workloads": {"w": {"kernel_source_sha256_16": bench.kernel_source_hash(),
+                               "launch": {"block": 1024, "grid": 7, "unroll": 1},
+                               "hbm_bytes_per_launch": 123}}}
+    f = tmp_path / "traffic.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "TRAFFIC_JSON", str(f))
+    assert bench.traffic_for("w", {"block": 1024, "grid": 7, "unroll": 1}) == 123
+    assert bench.traffic_for("w", {"block": 512, "grid": 7, "unroll": 1}) is None
+    assert bench.traffic_for("other", {"block": 1024, "grid": 7, "unroll": 1}) is None
+    rec["workloads"]["w"]["kernel_source_sha256_16"] = "0" * 16
+    f.write_text(json.dumps(rec))
+    assert bench.traffic_for("w", {"block": 1024, "grid": 7, "unroll": 1}) is None
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_committed_traffic_records_name_existing_summaries():
+    import os
+    with open(bench.TRAFFIC_JSON) as fh:
+        data = json.load(fh)
+    for name, rec in data["workloads"].items():
+        assert os.path.exists(os.path.join(ROOT, "profiles", rec["summary"])), name
+        assert rec["hbm_bytes_per_launch"] > 0
