@@ -24,8 +24,8 @@ Also reported, in the same line:
   ``profiles/traffic.json`` (else null);
 * ``cpu_baseline``: the CPU oracle timed on the host on a bounded sample;
 * ``other_configs``: the remaining workloads (each parity-gated); working
-  sets that fit in the 256 MB Infinity Cache are timed cold, with a 1 GiB
-  flush write before each timed launch.
+  sets up to 1 GiB (4 x the 256 MB Infinity Cache) are timed cold, with a
+  1 GiB flush write before each timed launch.
 """
 import argparse
 import hashlib
@@ -58,6 +58,11 @@ DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f
 # The unfused sequence each fused chain replaces, timed beside it.
 UNFUSED = {"add_relu_f32": ("add_f32", "relu_f32"), "saxpy_relu_f32": ("saxpy_f32", "relu_f32")}
 MALL_BYTES = 256 * 2 ** 20
+# Working sets up to 4 x the Infinity Cache are timed cold (a 1 GiB flush
+# before each launch): back to back, a 600 MB stream still found part of its
+# data in the cache (the 10^8 + 1 fp16 add read 86 % of peak that way, 84 %
+# at 2^28).  Larger working sets are timed back to back.
+COLD_MAX_BYTES = 4 * MALL_BYTES
 
 
 def algorithmic_bytes(op: str, n: int, cols: int = 0, changed: int = 0) -> int:
@@ -457,7 +462,7 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     footprint = nbytes if w.op != "gather_f32" else 8 * w.n
     # an in-place input must be restored before every launch, so it is
     # always timed launch by launch, restore and flush outside the events
-    cold = footprint <= 2 * MALL_BYTES or prep.pre is not None
+    cold = footprint <= COLD_MAX_BYTES or prep.pre is not None
     flush = (lambda: flush_buf.fill_(1)) if cold else None
     ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush, pre=prep.pre)
     gbs = nbytes / (ms / 1e3) / 1e9
@@ -501,6 +506,42 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     return res, prep, ms
 
 
+# The roofline curve: each op of the five configurations, its config's input
+# distribution, N = 2^20 .. 2^28 and one odd N per decade; seed 200 + log2 N
+# (300 + floor(log2 N) for the odd sizes).
+SWEEP_OPS = (("add_f32", "uniform"), ("add_f16", "uniform"), ("add_bf16", "uniform"),
+             ("saxpy_f32", "normal"), ("relu_f32", "normal"), ("copy_f32", "uniform"),
+             ("gather_f32", "uniform"))
+SWEEP_SIZES = [1 << k for k in range(20, 29)] + [10 ** 6 + 1, 10 ** 7 + 1, 10 ** 8 + 1]
+
+
+def run_sweep(torch, np, ew, synth, stream, cus, flush_buf):
+    """One JSON line per (op, N): parity against the oracle on every element
+    (the CPU leg, one full pass), then the timing of measure()."""
+    import math
+    rc = 0
+    for op, dist in SWEEP_OPS:
+        for n in sorted(SWEEP_SIZES):
+            lg = math.floor(math.log2(n))
+            seed = 200 + lg if n == 1 << lg else 300 + lg
+            w = synth.Workload(f"sweep_{op}_{n}", op, n, seed, dist,
+                               alpha=2.5 if op == "saxpy_f32" else 0.0,
+                               stride=2 if op == "gather_f32" else 0,
+                               description=f"{op}, n={n}, {dist}, seed {seed}")
+            log(f"sweep {op} n={n}")
+            steps = 200 if n >= (1 << 25) else 1000
+            res, prep, _ = measure(w, torch, np, ew, synth, stream, steps, 10, cus, flush_buf,
+                                   0.0)
+            del prep
+            torch.cuda.empty_cache()
+            res.pop("cpu_baseline", None)
+            res.pop("split", None)
+            print(json.dumps(res), flush=True)
+            if res["parity"] != "PASS":
+                rc = 1
+    return rc
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -510,6 +551,9 @@ def main(argv=None):
     ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the bench line: each op of the five configurations over "
+                         "N = 2^20 .. 2^28 plus odd N, one parity-gated JSON line per point")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -531,6 +575,9 @@ def main(argv=None):
     cus = dev_props.multi_processor_count
     stream = torch.cuda.Stream()          # default priority
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+
+    if args.sweep:
+        return run_sweep(torch, np, ew, synth, stream, cus, flush_buf)
 
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.description}")
