@@ -37,6 +37,10 @@
  *             (EW_ERR_MISALIGNED), overlap (EW_ERR_OVERLAP).  Then: no HIP
  *             device (EW_ERR_NO_DEVICE), a failed launch (EW_ERR_HIP; the
  *             hipError_t is kept for ew_last_hip_error()).  Nothing aborts.
+ * Logging     With the environment variable EW_LOG set (to anything but ""
+ *             or "0") every launch prints its plan -- op, n, head, vectors,
+ *             tail, grid, block, unroll and the kernel path -- as one line on
+ *             stderr.  Read once per process.
  * Numerics    IEEE-754 round-to-nearest-even, subnormals preserved (no
  *             flush-to-zero).  NaN results are NaN; their payload is not part
  *             of the contract for arithmetic operations.  Copy and gather

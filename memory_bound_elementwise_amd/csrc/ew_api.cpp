@@ -306,6 +306,28 @@ ew_status_t fail_hip(hipError_t e)
     return EW_ERR_HIP;
 }
 
+// EW_LOG set to anything but "" or "0": every launch prints its plan to
+// stderr (read once per process).
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char *v = std::getenv("EW_LOG");
+        return v != nullptr && *v != '\0' && std::strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_launch(const char *op, size_t n, uint64_t head, uint64_t vectors, uint64_t tail,
+                const Launch &l, const char *path)
+{
+    if (!log_enabled()) return;
+    std::fprintf(stderr,
+                 "[ew] %s n=%zu head=%llu vectors=%llu tail=%llu grid=%d block=%d unroll=%d "
+                 "path=%s\n",
+                 op, n, (unsigned long long)head, (unsigned long long)vectors,
+                 (unsigned long long)tail, l.grid, l.block, l.unroll, path);
+}
+
 ew_status_t run_stream(int op, const void *out, const void *in0, const void *in1, size_t n,
                        float alpha, hipStream_t stream)
 {
@@ -325,6 +347,8 @@ ew_status_t run_stream(int op, const void *out, const void *in0, const void *in1
     a.tail = p.tail;
     a.tiles = p.tiles;
     a.alpha = alpha;
+    log_launch(kOps[op].name, n, p.head, p.vectors, p.tail, p.launch,
+               p.co[0] && p.co[1] ? "stream, inputs co-aligned" : "stream, an input misaligned");
     const hipError_t e = launch_stream(static_cast<OpId>(op), a, p.co[0], p.co[1], p.launch, stream);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
@@ -461,6 +485,8 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride, 
     GatherArgs g{};
     Launch l{};
     gather_plan(in, out, n, stride, cus, &g, &l);
+    log_launch("gather_f32", n, g.head, g.vectors, g.tail, l,
+               g.passes ? "passes" : g.reps > 1 ? "replicated segments" : "index walk");
     const hipError_t e = launch_gather(g, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
@@ -511,6 +537,7 @@ ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)
     a.vectors = p.vectors;
     a.tail = p.tail;
     a.tiles = p.tiles;
+    log_launch("relu_inplace_f32", n, p.head, p.vectors, p.tail, p.launch, "64-byte spans");
     const hipError_t e = launch_relu_inplace(a, p.launch, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
@@ -581,6 +608,7 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         Launch lg = pg.launch;
         const uint64_t cap = (uint64_t)pg.blocks_per_cu * (uint64_t)cus;
         lg.grid = (int)(g.tiles == 0 ? 1 : (g.tiles < cap ? g.tiles : cap));
+        log_launch("copy2d_f32", n, g.head, g.vectors, g.tail, lg, "view x[::2]");
         const hipError_t e = launch_gather(g, lg, s);
         return e == hipSuccess ? EW_OK : fail_hip(e);
     }
@@ -604,6 +632,7 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         const uint64_t cap = (uint64_t)p.blocks_per_cu * (uint64_t)cus;
         Launch lg{gather_passes_threads(), (int)(g.tiles < cap ? g.tiles : cap), 1};
         if (lg.grid == 0) lg.grid = 1;
+        log_launch("copy2d_f32", n, 0, g.vectors, 0, lg, "view x[::s], s = 3..8");
         const hipError_t e = launch_gather(g, lg, s);
         return e == hipSuccess ? EW_OK : fail_hip(e);
     }
@@ -619,6 +648,8 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         const uint64_t cap = (uint64_t)cus * (uint64_t)p.blocks_per_cu;
         l.grid = (int)(tiles < cap ? tiles : cap);
     }
+    log_launch("copy2d_f32", n, a.head, a.vectors, a.tail, l,
+               mode == 1 ? "rows contiguous" : mode == 2 ? "transpose tiles" : "generic");
     const hipError_t e = launch_copy2d(a, mode, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
@@ -653,6 +684,7 @@ ew_status_t ew_bias_relu_f32(const float *x, const float *bias, float *y, size_t
     a.step_vec = (4 * nthr) % cols;
     a.step_tile = mulmod_host((4 * nthr * (uint64_t)p.launch.unroll) % cols,
                               (uint64_t)p.launch.grid % cols, cols);
+    log_launch("bias_relu_f32", n, p.head, p.vectors, p.tail, p.launch, "bias row broadcast");
     const hipError_t e = launch_bias_relu(a, p.co[0], p.launch, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }

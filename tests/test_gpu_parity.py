@@ -570,3 +570,27 @@ def test_non_default_stream_orders_with_the_stream():
         ew.ew_relu_f32(y, z)
     s.synchronize()
     assert torch.equal(z, x)
+
+
+def test_launch_log_names_each_plan():
+    """EW_LOG=1 prints one line per launch with the plan and the chosen path
+    (a child process: the setting is read once per process)."""
+    import subprocess
+    import sys
+    code = (
+        "import torch, memory_bound_elementwise_amd as ew\n"
+        "a = torch.zeros(1003, device='cuda'); b = torch.zeros(1003, device='cuda')\n"
+        "c = torch.zeros(1003, device='cuda')\n"
+        "ew.ew_add_f32(a[1:], b[1:], c[1:])\n"
+        "ew.ew_gather_f32(a, c, 3)\n"
+        "ew.ew_copy2d_f32(a, 1, 17, c, 17, 59)\n"
+        "torch.cuda.synchronize()\n")
+    env = dict(os.environ, EW_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=os.path.dirname(os.path.dirname(
+        os.path.abspath(__file__))), env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[ew] ")]
+    assert len(lines) == 3, r.stderr[-2000:]
+    assert lines[0].startswith("[ew] add_f32 n=1002 ") and "path=stream" in lines[0]
+    assert lines[1].startswith("[ew] gather_f32 n=1003 ") and "path=passes" in lines[1]
+    assert lines[2].startswith("[ew] copy2d_f32 n=1003 ") and "path=transpose tiles" in lines[2]
