@@ -639,6 +639,14 @@ def main(argv=None):
             del p
             torch.cuda.empty_cache()
         line["other_configs"] = others
+        by = {r["workload"]: r for r in others + [res]}
+        sg, cg = by.get("cfg5b_gather_f32_2e26_s2"), by.get("cfg5a_copy_f32_2e26")
+        if sg and cg and sg.get("gbs") and cg.get("gbs"):
+            # the fifth configuration's comparison: strided gather vs coalesced copy
+            line["strided_over_coalesced"] = {
+                "gather_s2_gbs": sg["gbs"], "copy_gbs": cg["gbs"],
+                "ratio": round(sg["gbs"] / cg["gbs"], 4),
+                "traffic_note": "logical bytes for both; the gather reads each input line once"}
 
     line["env"] = {"device": torch.cuda.get_device_name(0),
                    "arch": getattr(dev_props, "gcnArchName", None), "cus": cus,
