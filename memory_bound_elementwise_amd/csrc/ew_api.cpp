@@ -368,7 +368,7 @@ uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
 // the output splits into `stride` passes that together read the input
 // contiguously (see GatherArgs).  Otherwise one segment of n.
 void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, GatherArgs *g,
-                 Launch *l)
+                 Launch *l, int *blocks_per_cu = nullptr)
 {
     const uint64_t s = stride % n;
     const uint64_t gcd = std::gcd(s, (uint64_t)n);  // gcd(0, n) == n
@@ -400,6 +400,7 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
         if (grid > g->tiles) grid = g->tiles;
         if (grid == 0) grid = 1;
         *l = Launch{gather_passes_threads(), (int)grid, 1};
+        if (blocks_per_cu) *blocks_per_cu = r.blocks_per_cu;
         return;
     }
     uint64_t reps = 1, seg = n;
@@ -425,6 +426,7 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
     g->step_tile = mulmod_host(mulmod_host(s, tile_elems, n), (uint64_t)p.launch.grid % n, n);
     g->wide = (s != 0 && (n - 1) > UINT64_MAX / s) ? 1 : 0;
     *l = p.launch;
+    if (blocks_per_cu) *blocks_per_cu = p.blocks_per_cu;
 }
 
 }  // namespace
@@ -781,7 +783,12 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const
     plan->blocks_per_cu = r.blocks_per_cu;
     plan->unroll = r.unroll;
     if (n == 0) return EW_OK;
+    // one table read for everything reported (another thread may be
+    // rewriting the table)
     const Plan p = make_plan(id, out, in0, in1, n, cu_count);
+    plan->block = p.launch.block;
+    plan->blocks_per_cu = p.blocks_per_cu;
+    plan->unroll = p.launch.unroll;
     plan->head = p.head;
     plan->vectors = p.vectors;
     plan->tail = p.tail;
@@ -806,9 +813,9 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     if (st != EW_OK) return st;
     GatherArgs g{};
     Launch l{};
+    int bpc = 0;
     gather_plan(static_cast<const float *>(in), static_cast<float *>(const_cast<void *>(out)), n,
-                stride, cu_count, &g, &l);
-    const Row r = get_row(kOpGatherF32, g.passes ? n : (size_t)g.seg);
+                stride, cu_count, &g, &l, &bpc);
     plan->n = n;
     plan->head = g.head;
     plan->vectors = g.vectors;
@@ -818,7 +825,7 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     plan->elem_size = 4;
     plan->in_coaligned[0] = plan->in_coaligned[1] = 1;
     plan->block = l.block;
-    plan->blocks_per_cu = r.blocks_per_cu;
+    plan->blocks_per_cu = bpc;
     plan->unroll = l.unroll;
     plan->grid = l.grid;
     plan->segment = g.seg;

@@ -246,3 +246,46 @@ def test_compiled_defaults_match_the_shipped_table():
             assert ew.ew_get_launch_config(op, min_n) == cfg, (op, min_n)
     finally:
         ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+def test_planning_and_the_table_are_thread_safe():
+    """Several threads plan, read and rewrite the launch table at once (the
+    ctypes calls release the GIL); every plan stays self-consistent and the
+    process survives.  Rows are rewritten with values every row can take."""
+    import threading
+    errors = []
+
+    def planner(seed):
+        try:
+            for k in range(400):
+                n = (seed * 7919 + k * 104729) % (1 << 24) + 1
+                p = ew.ew_make_plan("add_f32", BASE + 4 * (k % 4), BASE + 2 * MiB * 64,
+                                    BASE + 4 * MiB * 64, n, 256)
+                assert p.head + 4 * p.vectors + p.tail == n
+                assert p.tiles == -(-p.vectors // (p.block * p.unroll))
+                g = ew.ew_make_gather_plan(BASE + 8 * MiB * 64, BASE, n, 3, 256)
+                assert g.n == n
+        except Exception as e:   # noqa: BLE001 - reported below
+            errors.append(repr(e))
+
+    def writer():
+        try:
+            for k in range(400):
+                ew.ew_set_launch_config("add_f32", 1 << 22, (64, 256, 1024)[k % 3], 1024, 1)
+                ew.ew_get_launch_config("add_f32", 1 << 23)
+                if k % 50 == 0:
+                    ew.ew_reset_launch_config()
+        except Exception as e:   # noqa: BLE001
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=planner, args=(s,)) for s in range(6)]
+    threads.append(threading.Thread(target=writer))
+    try:
+        for t in threads:
+            t.start()
+        for t in threads:
+            t.join()
+    finally:
+        ew.ew_reset_launch_config()
+        ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+    assert not errors, errors[:3]
