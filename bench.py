@@ -515,13 +515,29 @@ SWEEP_OPS = (("add_f32", "uniform"), ("add_f16", "uniform"), ("add_bf16", "unifo
 SWEEP_SIZES = [1 << k for k in range(20, 29)] + [10 ** 6 + 1, 10 ** 7 + 1, 10 ** 8 + 1]
 
 
-def run_sweep(torch, np, ew, synth, stream, cus, flush_buf):
+def run_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):
     """One JSON line per (op, N): parity against the oracle on every element
-    (the CPU leg, one full pass), then the timing of measure()."""
+    (the CPU leg, one full pass), then the timing of measure().  With
+    out_path, each record is also appended to that JSONL file as soon as it
+    is measured, and points already recorded there with parity PASS are
+    skipped (an interrupted sweep resumes where it stopped)."""
     import math
     rc = 0
+    done = set()
+    if out_path and os.path.exists(out_path):
+        with open(out_path) as f:
+            for line in f:
+                try:
+                    r = json.loads(line)
+                except ValueError:
+                    continue
+                if r.get("parity") == "PASS":
+                    done.add((r["op"], r["n"]))
     for op, dist in SWEEP_OPS:
         for n in sorted(SWEEP_SIZES):
+            if (op, n) in done:
+                log(f"sweep {op} n={n}: already recorded")
+                continue
             lg = math.floor(math.log2(n))
             seed = 200 + lg if n == 1 << lg else 300 + lg
             w = synth.Workload(f"sweep_{op}_{n}", op, n, seed, dist,
@@ -537,6 +553,9 @@ def run_sweep(torch, np, ew, synth, stream, cus, flush_buf):
             res.pop("cpu_baseline", None)
             res.pop("split", None)
             print(json.dumps(res), flush=True)
+            if out_path:
+                with open(out_path, "a") as f:
+                    f.write(json.dumps(res) + "\n")
             if res["parity"] != "PASS":
                 rc = 1
     return rc
@@ -554,6 +573,8 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: each op of the five configurations over "
                          "N = 2^20 .. 2^28 plus odd N, one parity-gated JSON line per point")
+    ap.add_argument("--sweep-out", help="with --sweep: append each point to this JSONL file "
+                                        "and skip points it already holds with parity PASS")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -577,7 +598,7 @@ def main(argv=None):
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
 
     if args.sweep:
-        return run_sweep(torch, np, ew, synth, stream, cus, flush_buf)
+        return run_sweep(torch, np, ew, synth, stream, cus, flush_buf, args.sweep_out)
 
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.description}")

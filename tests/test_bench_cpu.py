@@ -66,3 +66,34 @@ def test_committed_traffic_records_name_existing_summaries():
     for name, rec in data["workloads"].items():
         assert os.path.exists(os.path.join(ROOT, "profiles", rec["summary"])), name
         assert rec["hbm_bytes_per_launch"] > 0
+
+
+def test_sweep_resume_skips_recorded_points(tmp_path, monkeypatch):
+    """An interrupted sweep resumes: points already in the output file with
+    parity PASS are skipped, the rest are measured and appended."""
+    out = tmp_path / "sweep.jsonl"
+    out.write_text(json.dumps({"op": "add_f32", "n": 5, "parity": "PASS"}) + "\n"
+                   + json.dumps({"op": "add_f32", "n": 7, "parity": "FAIL"}) + "\n")
+    monkeypatch.setattr(bench, "SWEEP_OPS", (("add_f32", "uniform"),))
+    monkeypatch.setattr(bench, "SWEEP_SIZES", [5, 7, 9])
+    measured = []
+
+    def fake_measure(w, *a, **k):
+        measured.append(w.n)
+        return {"op": w.op, "n": w.n, "parity": "PASS"}, None, 1.0
+    monkeypatch.setattr(bench, "measure", fake_measure)
+
+    class FakeCuda:
+        @staticmethod
+        def empty_cache():
+            pass
+
+    class FakeTorch:
+        cuda = FakeCuda
+
+    import synth
+    assert bench.run_sweep(FakeTorch, np, None, synth, None, 256, None, str(out)) == 0
+    assert measured == [7, 9]
+    lines = [json.loads(x) for x in out.read_text().splitlines()]
+    assert [(r["n"], r["parity"]) for r in lines] == [(5, "PASS"), (7, "FAIL"), (7, "PASS"),
+                                                      (9, "PASS")]
