@@ -7,7 +7,7 @@ ways:
 
 * properties that hold at any size, on every element, on the device, chunk
   by chunk (A + (-0) == A bitwise; copy == input; the stride-2 gather's two
-  halves are equal);
+  halves are equal; no sign bit left after the in-place ReLU);
 * sampled elements (first, last, around the 2^31 and 2^32 element
   boundaries, and random positions) against the oracle computed one by one
   on the host.
@@ -176,5 +176,71 @@ def test_gather_stride_2_replicated_segments_past_2_pow_32():
     idx = _samples(n)
     j = np.array([oracle.gather_index(n, 2, int(i)) for i in idx], np.int64)
     assert np.array_equal(_take(out, idx), _take(src, j))
+    del src, out
+    torch.cuda.empty_cache()
+
+
+def test_relu_inplace_past_2_pow_32_elements_misaligned():
+    n = (1 << 32) + 21
+    _need(4 * (n + 8))
+    print(f"[large] relu_inplace n={n}", flush=True)
+    base = torch.empty(n + 8, dtype=torch.float32, device=DEV)
+    x = base[5:5 + n]                                   # head of 11 elements to 64 bytes
+    _fill_f32(x, 40503, 65521, 2.0 ** -8)               # non-negative ...
+    xi = x.view(torch.int32)
+    for s in range(0, n, CHUNK):                        # ... then every 7th element negated
+        e = min(n, s + CHUNK)
+        i = torch.arange(s, e, device=DEV, dtype=torch.int64)
+        xi[s:e] = torch.where(i % 7 == 3, xi[s:e] | (-(1 << 31)), xi[s:e])
+    idx = _samples(n)
+    before = _take(x, idx)
+    ew.ew_relu_inplace_f32(x)
+    torch.cuda.synchronize()
+    assert mismatches("relu_f32", _take(x, idx), oracle.relu_f32(before)).size == 0
+    for s in range(0, n, CHUNK):                        # property on every element
+        assert not bool(torch.signbit(x[s:min(n, s + CHUNK)]).any())
+    del base, x, xi
+    torch.cuda.empty_cache()
+
+
+def test_gather_passes_past_2_pow_32_elements():
+    """Stride 3 with gcd(3, n) == 1 and n > 2^32: the pass kernel's slot and
+    destination arithmetic in 64 bits (host planning in 128)."""
+    n = (1 << 32) + 1
+    _need(2 * 4 * n)
+    print(f"[large] gather passes stride 3, n={n}", flush=True)
+    src = torch.empty(n, dtype=torch.int32, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    plan = ew.ew_make_gather_plan(out.data_ptr(), src.data_ptr(), n, 3,
+                                  torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan.passes == 3
+    ew.ew_gather_f32(src.data_ptr(), out.data_ptr(), 3, n=n)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    for k in (1, 2):                                    # around each pass boundary
+        b = -(-k * n // 3)
+        idx = np.unique(np.concatenate([idx, np.arange(b - 6, b + 6)]))
+    j = np.array([oracle.gather_index(n, 3, int(i)) for i in idx], np.int64)
+    assert np.array_equal(_take(out, idx), _take(src, j))
+    del src, out
+    torch.cuda.empty_cache()
+
+
+def test_transpose_past_2_pow_32_elements():
+    """A 65536 x 65540 transposed view (2^32 + 2^18 elements): tile and row
+    offsets past 32 bits, ragged edge tiles on one side."""
+    rows, cols = 65536, 65540
+    n = rows * cols
+    _need(2 * 4 * n)
+    print(f"[large] transpose {rows} x {cols}", flush=True)
+    src = torch.empty(n, dtype=torch.int32, device=DEV)    # (cols x rows) row-major
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    ew.ew_copy2d_f32(src.data_ptr(), 1, rows, out.data_ptr(), rows, cols)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    r, c = idx // cols, idx % cols
+    assert np.array_equal(_take(out, idx), _take(src, c * rows + r))
     del src, out
     torch.cuda.empty_cache()
