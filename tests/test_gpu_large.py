@@ -244,3 +244,47 @@ def test_transpose_past_2_pow_32_elements():
     assert np.array_equal(_take(out, idx), _take(src, c * rows + r))
     del src, out
     torch.cuda.empty_cache()
+
+
+def test_bias_relu_past_2_pow_32_elements():
+    """rows x cols > 2^32 with a column count that is not a multiple of 4
+    (the per-element bias walk) and a misaligned output."""
+    rows, cols = 1048063, 4099
+    n = rows * cols
+    assert n > 1 << 32
+    _need(2 * 4 * (n + 8))
+    print(f"[large] bias_relu {rows} x {cols}", flush=True)
+    x = torch.empty(n, dtype=torch.float32, device=DEV)
+    ybase = torch.empty(n + 8, dtype=torch.float32, device=DEV)
+    y = ybase[3:3 + n]
+    _fill_f32(x, 40503, 65521, 2.0 ** -8)
+    x.sub_(128.0)                                      # mixed signs, exact in binary32
+    bias = ((torch.arange(cols, device=DEV, dtype=torch.float32) % 509) - 254.0) * 0.25
+    ew.ew_bias_relu_f32(x, bias, y, rows, cols)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    hb = bias.cpu().numpy()
+    ref = oracle.relu_f32(oracle.add_f32(_take(x, idx), hb[idx % cols]))
+    assert mismatches("bias_relu_f32", _take(y, idx), ref).size == 0
+    del x, ybase, y
+    torch.cuda.empty_cache()
+
+
+def test_submatrix_view_past_2_pow_32_elements():
+    """A 65537 x 65536 sub-matrix of a 65540-wide array, starting 3 elements
+    in: the rows-contiguous path with row and column walks past 32 bits."""
+    rows, cols, pitch = 65537, 65536, 65540
+    n = rows * cols
+    base_n = (rows - 1) * pitch + cols + 3
+    _need(4 * (n + base_n))
+    print(f"[large] submatrix {rows} x {cols}", flush=True)
+    src = torch.empty(base_n, dtype=torch.int32, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    ew.ew_copy2d_f32(src.data_ptr() + 4 * 3, pitch, 1, out.data_ptr(), rows, cols)
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    r, c = idx // cols, idx % cols
+    assert np.array_equal(_take(out, idx), _take(src, 3 + r * pitch + c))
+    del src, out
+    torch.cuda.empty_cache()
