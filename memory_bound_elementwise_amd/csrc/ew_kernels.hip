@@ -444,10 +444,11 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // bytes directly instead (s loads 16 * s bytes apart across the lanes) ran
 // 14 % (s = 3) to 70 % (s = 7) slower on MI355X.  The register permutation is
 // fixed at compile time (S is a template parameter); only the destinations
-// are runtime values.  Blocks are 256 threads; a tile is 256 groups.
+// are runtime values.  Blocks are 512 threads; a tile is 512 groups (512-
+// thread blocks measured up to 8 % faster than 256 at s = 8, equal elsewhere).
 // FirstOnly keeps only the residue-0 pass: that is the strided view
 // x[::S] (out[m] = in[S*m]), read as contiguous spans of which 1/S is kept.
-constexpr int kPassThreads = 256;
+constexpr int kPassThreads = 512;
 
 template <int S, bool FirstOnly>
 __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)

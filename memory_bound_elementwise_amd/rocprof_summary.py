@@ -4,6 +4,7 @@ Kernel durations (from ``rocprofv3 --kernel-trace --stats -f csv``):
 
     python -m memory_bound_elementwise_amd.rocprof_summary trace \\
         --stats DIR/NAME_kernel_stats.csv --kernel REGEX --bytes B \\
+        --bench-json BENCH_OUTPUT_OF_THE_PROFILED_RUN \\
         --command "the rocprofv3 command line" --out profiles/FILE.txt
 
 HBM traffic (from two ``rocprofv3 --pmc`` runs per kernel, FETCH_SIZE then
@@ -18,11 +19,15 @@ source hash and launch shape):
         --fetch DIR/..._counter_collection.csv --write DIR/..._counter_collection.csv \\
         --calib-kernel REGEX --calib-bytes-read R --calib-bytes-written W \\
         --calib-fetch CSV --calib-write CSV --launch '{"block": .., "grid": .., "unroll": ..}' \\
-        --command "..." --out profiles/FILE.txt
+        --bench-json FETCH_RUN_OUTPUT --bench-json-write WRITE_RUN_OUTPUT \\
+        --command-fetch "..." --command-write "..." --command-calib "..." --out profiles/FILE.txt
+
+The kernel source hash written into every record is the one the profiled
+bench.py run printed (env.kernel_source_sha256_16), never the hash of the
+source as it is when the summary is written.
 """
 import argparse
 import csv
-import hashlib
 import json
 import os
 import re
@@ -31,12 +36,23 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "memory_bound_elementwise_amd", "csrc", "ew_kernels.hip")
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def bench_record(path):
+    """The JSON line bench.py printed in the profiled run (its last line)."""
+    with open(path) as f:
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def profiled_hash(bench_json):
+    """The kernel source hash the profiled run was built from: taken from the
+    bench line it printed, so that a summary written later, after the source
+    has changed, cannot claim the new hash.  Refuses a bench line without one."""
+    rec = bench_record(bench_json)
+    h = rec.get("env", {}).get("kernel_source_sha256_16")
+    if not h:
+        raise SystemExit(f"{bench_json}: no env.kernel_source_sha256_16")
+    return h
 
 
 def _rows(path):
@@ -71,6 +87,8 @@ def counter_per_dispatch(path, kernel_re, counter):
 def cmd_trace(a):
     name, calls, avg, mn, mx = kernel_stats(a.stats, a.kernel)
     gbs = a.bytes / avg
+    src_hash = profiled_hash(a.bench_json)
+    bench_ms = bench_record(a.bench_json).get("ms_per_step")
     text = [
         f"# {a.title}",
         "",
@@ -82,11 +100,11 @@ def cmd_trace(a):
         f"average:         {avg / 1000:.3f} us   (min {mn / 1000:.3f}, max {mx / 1000:.3f})",
         f"algorithmic:     {a.bytes} bytes per launch",
         f"achieved:        {gbs:.1f} GB/s = {100 * gbs / 8000:.2f} % of 8000 GB/s",
-        f"kernel source:   ew_kernels.hip sha256[:16] {kernel_source_hash()}",
+        f"kernel source:   ew_kernels.hip sha256[:16] {src_hash} (of the profiled run)",
     ]
-    if a.bench_ms:
-        text.append(f"bench.py events: {a.bench_ms:.5f} ms per step "
-                    f"({100 * (a.bench_ms * 1e6 - avg) / avg:+.2f} % vs the trace average)")
+    if bench_ms:
+        text.append(f"bench.py events: {bench_ms:.5f} ms per step "
+                    f"({100 * (bench_ms * 1e6 - avg) / avg:+.2f} % vs the trace average)")
     with open(a.out, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
@@ -103,6 +121,9 @@ def cmd_traffic(a):
     write_b = write_kib * 1024 * scale_w
     total = fetch_b + write_b
     launch = json.loads(a.launch)
+    src_hash = profiled_hash(a.bench_json)
+    if profiled_hash(a.bench_json_write) != src_hash:
+        raise SystemExit("the FETCH_SIZE and WRITE_SIZE runs were built from different sources")
     text = [
         f"# HBM traffic: {a.workload}",
         "",
@@ -118,7 +139,7 @@ def cmd_traffic(a):
         f"{scale_w:.4f}",
         f"HBM bytes/launch:  fetch {fetch_b:.0f} + write {write_b:.0f} = {total:.0f}",
         f"algorithmic bytes: {a.bytes}  (traffic / algorithmic = {total / a.bytes:.4f})",
-        f"kernel source:     ew_kernels.hip sha256[:16] {kernel_source_hash()}",
+        f"kernel source:     ew_kernels.hip sha256[:16] {src_hash} (of the profiled runs)",
     ]
     with open(a.out, "w") as f:
         f.write("\n".join(text) + "\n")
@@ -131,7 +152,7 @@ def cmd_traffic(a):
                          "scaled by the copy-kernel calibration; see the .txt summaries",
                 "workloads": {}}
     data["workloads"][a.workload] = {
-        "kernel": a.kernel, "launch": launch, "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel": a.kernel, "launch": launch, "kernel_source_sha256_16": src_hash,
         "fetch_kib": fetch_kib, "write_kib": write_kib, "scale_fetch": scale_f,
         "scale_write": scale_w, "hbm_bytes_per_launch": round(total),
         "algorithmic_bytes": a.bytes, "summary": os.path.basename(a.out)}
@@ -150,7 +171,8 @@ def main(argv=None):
     t.add_argument("--bytes", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="Kernel duration")
-    t.add_argument("--bench-ms", type=float)
+    t.add_argument("--bench-json", required=True,
+                   help="the bench.py output of the profiled run (events and source hash)")
     t.add_argument("--out", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("--workload", required=True)
@@ -167,6 +189,10 @@ def main(argv=None):
     r.add_argument("--command-fetch", required=True)
     r.add_argument("--command-write", required=True)
     r.add_argument("--command-calib", required=True)
+    r.add_argument("--bench-json", required=True,
+                   help="bench.py output of the FETCH_SIZE run (source hash)")
+    r.add_argument("--bench-json-write", required=True,
+                   help="bench.py output of the WRITE_SIZE run")
     r.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     (cmd_trace if a.cmd == "trace" else cmd_traffic)(a)

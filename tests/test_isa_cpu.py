@@ -51,7 +51,7 @@ def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
     for name, (_, meta) in ks.items():
         d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
         lds = "67584" if "transpose" in name else (
-            str(4096 * int(re.search(r"passes_kernelILi(\d)ELb[01]E", name).group(1)))
+            str(8192 * int(re.search(r"passes_kernelILi(\d)ELb[01]E", name).group(1)))
             if "gather_passes" in name else "0")
         assert d["group_segment_fixed_size"] == lds, name
         assert d["private_segment_fixed_size"] == "0", name
