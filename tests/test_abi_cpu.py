@@ -289,3 +289,15 @@ def test_planning_and_the_table_are_thread_safe():
         ew.ew_reset_launch_config()
         ew.ew_load_launch_table(ew.LAUNCH_TABLE)
     assert not errors, errors[:3]
+
+
+def test_header_is_clean_c11_and_a_c_program_links_against_the_library(tmp_path):
+    """A plain C11 program (no C++, no torch) includes ew.h with warnings as
+    errors and links libew.so, the HIP runtime and the oracle."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_c_client_build", os.path.join(ROOT, "tests", "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    exe = mod.build(out=str(tmp_path / "client"))
+    assert os.path.exists(exe)
