@@ -452,7 +452,8 @@ def test_copy2d_paths_shapes_and_strides():
     for rows, cols in ((1, 1), (1, 7), (3, 5), (64, 64), (65, 63), (1, 1000), (130, 129),
                        (200, 7), (7, 300), (513, 257), (128, 128), (127, 129), (256, 385)):
         for sr, sc in ((cols, 1), (cols + 5, 1), (1, rows), (1, rows + 3), (1, -rows),
-                       (-cols, 1), (2 * cols, 2), (3, 7 * rows), (0, 1), (cols, 0), (1, 1)):
+                       (-cols, 1), (2 * cols, 2), (3, 7 * rows), (0, 1), (cols, 0), (1, 1),
+                       (1, 0), (1, 2 * rows), (-1, rows), (1, -2 * rows)):
             for off_out in (0, 1):
                 k += 1
                 failures += _copy2d_case(rows, cols, sr, sc, 400 + k, off_out)
