@@ -763,7 +763,9 @@ __global__ void __launch_bounds__(kTThreads) ew_transpose_kernel(Copy2dArgs a)
                     if (c0 + q4 + k < a.cols) dst[k] = w[k];
             }
         }
-        __syncthreads();
+        // the tile is rewritten only if this block has another round (a
+        // block-uniform condition)
+        if (t + gridDim.x < tiles) __syncthreads();
     }
 }
 
