@@ -24,8 +24,11 @@ Also reported, in the same line:
   ``profiles/traffic.json`` (else null);
 * ``cpu_baseline``: the CPU oracle timed on the host on a bounded sample;
 * ``other_configs``: the remaining workloads (each parity-gated); working
-  sets up to 1 GiB (4 x the 256 MB Infinity Cache) are timed cold, with a
-  1 GiB flush write before each timed launch.
+  sets up to 1 GiB (4 x the 256 MB Infinity Cache) are timed cold: back to
+  back over R copies of the workload's buffers, used in turn, so that at
+  least 1 GiB of other traffic runs between two uses of one copy.  Beside it,
+  ``flushed_per_launch`` gives the median of single launches each bracketed
+  by its own events after a 1 GiB fill.
 """
 import argparse
 import hashlib
@@ -58,11 +61,21 @@ DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f
 # The unfused sequence each fused chain replaces, timed beside it.
 UNFUSED = {"add_relu_f32": ("add_f32", "relu_f32"), "saxpy_relu_f32": ("saxpy_f32", "relu_f32")}
 MALL_BYTES = 256 * 2 ** 20
-# Working sets up to 4 x the Infinity Cache are timed cold (a 1 GiB flush
-# before each launch): back to back, a 600 MB stream still found part of its
-# data in the cache (the 10^8 + 1 fp16 add read 86 % of peak that way, 84 %
-# at 2^28).  Larger working sets are timed back to back.
+# Working sets up to 4 x the Infinity Cache are timed cold: back to back, a
+# 600 MB stream still found part of its data in the cache (the 10^8 + 1 fp16
+# add read 86 % of peak that way, 84 % at 2^28).  Larger working sets are
+# timed back to back on one set of buffers.
 COLD_MAX_BYTES = 4 * MALL_BYTES
+# Cold timing rotates over copies of the buffers so that this much other
+# traffic separates two uses of one copy (4 x the Infinity Cache).
+COLD_GAP_BYTES = 4 * MALL_BYTES
+
+
+def rotation_sets(bytes_per_launch: int) -> int:
+    """Buffer copies for cold back-to-back timing: with R copies used in
+    turn, R - 1 launches of other copies (at least COLD_GAP_BYTES of traffic)
+    run between two uses of one copy."""
+    return max(2, -(-COLD_GAP_BYTES // bytes_per_launch) + 1)
 
 
 def algorithmic_bytes(op: str, n: int, cols: int = 0, changed: int = 0) -> int:
@@ -97,10 +110,10 @@ def log(msg):
 class Prepared:
     """Device buffers of one workload and a launcher bound to a stream."""
 
-    def __init__(self, w, torch, np, ew, synth, stream):
+    def __init__(self, w, torch, np, ew, synth, stream, inp=None):
         from tests.gpu_util import upload
         self.w = w
-        self.inp = synth.workload_inputs(w)
+        self.inp = synth.workload_inputs(w) if inp is None else inp
         self.keep = []
         offs = w.offsets
         s = stream.cuda_stream
@@ -254,6 +267,26 @@ def time_launches(torch, launch, stream, steps, warmup, flush=None, pre=None):
     LAST_DIST["p10"] = ts[len(ts) // 10]
     LAST_DIST["p90"] = ts[(9 * len(ts)) // 10]
     return ts[len(ts) // 2]
+
+
+def time_rotated(torch, launches, stream, steps, warmup):
+    """Mean time per launch in ms of `steps` back-to-back launches between
+    two events on `stream`, launch i calling launches[i mod R]: each copy's
+    data has left the caches by the time it is used again, and no per-launch
+    event or flush sits between the launches."""
+    r = len(launches)
+    with torch.cuda.stream(stream):
+        for i in range(max(warmup, 2 * r)):
+            launches[i % r]()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        launches[i % r]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 GRAPH_LAUNCHES = 100
@@ -464,16 +497,36 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     # always timed launch by launch, restore and flush outside the events
     cold = footprint <= COLD_MAX_BYTES or prep.pre is not None
     flush = (lambda: flush_buf.fill_(1)) if cold else None
-    ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush, pre=prep.pre)
+    sets = [prep]
+    if cold and prep.pre is None:
+        # cold, back to back: R copies of the buffers (same inputs, same
+        # offsets, so the same plan) used in turn
+        sets += [Prepared(w, torch, np, ew, synth, stream, inp=prep.inp)
+                 for _ in range(rotation_sets(footprint) - 1)]
+        ms = time_rotated(torch, [p.launch for p in sets], stream, steps, warmup)
+        fl_ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush)
+        timing = (f"cold: back to back over {len(sets)} copies of the buffers used in turn "
+                  f"(>= 1 GiB of other traffic between two uses of one copy), mean")
+        res["flushed_per_launch"] = {
+            "ms": round(fl_ms, 5), "gbs": round(nbytes / (fl_ms / 1e3) / 1e9, 1),
+            "p10_ms": round(LAST_DIST["p10"], 5), "p90_ms": round(LAST_DIST["p90"], 5),
+            "timing": "each launch between its own events after a 1 GiB fill, median "
+                      "(includes the per-launch event gap and the fill's write-back)"}
+    else:
+        ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush, pre=prep.pre)
+        timing = ("cold (1 GiB flush before each launch), median" if cold else
+                  "back-to-back, mean")
+        if cold:
+            res["p10_ms"], res["p90_ms"] = round(LAST_DIST["p10"], 5), round(LAST_DIST["p90"], 5)
     gbs = nbytes / (ms / 1e3) / 1e9
     res.update({"ms": round(ms, 5), "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                "timing": "cold (1 GiB flush before each launch), median" if cold else
-                          "back-to-back, mean"})
-    if cold:
-        res["p10_ms"], res["p90_ms"] = round(LAST_DIST["p10"], 5), round(LAST_DIST["p90"], 5)
+                "timing": timing})
     ctx = prep.torch_context
     if ctx is not None:
-        t_ms = time_launches(torch, ctx[1], stream, steps, warmup, flush=flush)
+        if len(sets) > 1:
+            t_ms = time_rotated(torch, [p.torch_context[1] for p in sets], stream, steps, warmup)
+        else:
+            t_ms = time_launches(torch, ctx[1], stream, steps, warmup, flush=flush)
         res["torch_context"] = {"op": ctx[0], "ms": round(t_ms, 5),
                                 "gbs": round(nbytes / (t_ms / 1e3) / 1e9, 1),
                                 "note": "PyTorch's own kernel on the same buffers, same timing; "
@@ -500,9 +553,13 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
         res["vs_storing_every_element"] = {"op": "ew_relu_f32(x, x)", "ms": round(all_ms, 5),
                                            "speedup": round(all_ms / ms, 3)}
     elif prep.unfused is not None:
-        un_ms = time_launches(torch, prep.unfused, stream, steps, warmup, flush=flush)
+        if len(sets) > 1:
+            un_ms = time_rotated(torch, [p.unfused for p in sets], stream, steps, warmup)
+        else:
+            un_ms = time_launches(torch, prep.unfused, stream, steps, warmup, flush=flush)
         res["unfused"] = {"ops": list(UNFUSED[w.op]), "ms": round(un_ms, 5),
                           "speedup_of_fused": round(un_ms / ms, 3)}
+    del sets[1:]
     return res, prep, ms
 
 

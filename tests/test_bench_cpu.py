@@ -97,3 +97,18 @@ def test_sweep_resume_skips_recorded_points(tmp_path, monkeypatch):
     lines = [json.loads(x) for x in out.read_text().splitlines()]
     assert [(r["n"], r["parity"]) for r in lines] == [(5, "PASS"), (7, "FAIL"), (7, "PASS"),
                                                       (9, "PASS")]
+
+
+def test_rotation_puts_a_gibibyte_of_other_traffic_between_two_uses():
+    """Cold timing over R buffer copies used in turn: the R - 1 launches
+    between two uses of one copy move at least 1 GiB, and R is the smallest
+    count that does (at least 2)."""
+    gib = 1 << 30
+    for nbytes in (12 << 20, 402653184, 536870912, 805306368, gib, 3 * gib):
+        r = bench.rotation_sets(nbytes)
+        assert r >= 2
+        assert (r - 1) * nbytes >= gib
+        assert r == 2 or (r - 2) * nbytes < gib
+    assert bench.rotation_sets(12 * (1 << 20)) == 87       # the 2^20 fp32 add
+    assert bench.rotation_sets(12 * (1 << 25)) == 4        # SAXPY 2^25
+    assert bench.rotation_sets(8 * (1 << 26)) == 3         # copy and gather 2^26
