@@ -413,17 +413,27 @@ def _all_cores(w, run, changed, small, m, target_s):
                       f"each, {reps} passes in {el:.1f} s"}
 
 
-def _clocks():
-    """Current GPU clocks as rocm-smi reports them (None if it is unavailable)."""
-    import subprocess
+def _clocks(props):
+    """Current clocks of the device torch uses, read from the amdgpu driver's
+    DPM tables in sysfs (the level marked "*"), or None if they are not
+    readable.  Plain file reads: no child process is started from this
+    GPU-initialised process."""
     try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                             text=True, timeout=20)
-        data = json.loads(out.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
+        addr = "%04x:%02x:%02x.0" % (props.pci_domain_id, props.pci_bus_id, props.pci_device_id)
+    except (AttributeError, TypeError):
         return None
-    card = next(iter(data.values()), {}) if isinstance(data, dict) else {}
-    return {k: v for k, v in card.items() if "clock" in k.lower()} or None
+    base = os.path.join("/sys/bus/pci/devices", addr)
+    out = {}
+    for name in ("sclk", "mclk", "fclk", "socclk"):
+        try:
+            with open(os.path.join(base, "pp_dpm_" + name)) as f:
+                for line in f:
+                    line = line.strip()
+                    if line.endswith("*") and ":" in line:
+                        out[name] = line.split(":", 1)[1].rstrip("*").strip()
+        except OSError:
+            continue
+    return out or None
 
 
 def _cpu_model():
@@ -728,7 +738,7 @@ def main(argv=None):
 
     line["env"] = {"device": torch.cuda.get_device_name(0),
                    "arch": getattr(dev_props, "gcnArchName", None), "cus": cus,
-                   "hbm_bytes": dev_props.total_memory, "clocks": _clocks(),
+                   "hbm_bytes": dev_props.total_memory, "clocks": _clocks(dev_props),
                    "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                    "numpy": np.__version__, "kernel_source_sha256_16": kernel_source_hash(),
                    "input_sha256": input_sha}

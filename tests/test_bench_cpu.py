@@ -112,3 +112,26 @@ def test_rotation_puts_a_gibibyte_of_other_traffic_between_two_uses():
     assert bench.rotation_sets(12 * (1 << 20)) == 87       # the 2^20 fp32 add
     assert bench.rotation_sets(12 * (1 << 25)) == 4        # SAXPY 2^25
     assert bench.rotation_sets(8 * (1 << 26)) == 3         # copy and gather 2^26
+
+
+def test_clocks_come_from_sysfs_without_a_child_process(tmp_path, monkeypatch):
+    """The DPM level marked '*' of the device's PCI address is reported; a
+    missing directory gives None.  No process is spawned."""
+    dev = tmp_path / "0000:75:00.0"
+    dev.mkdir()
+    (dev / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 2400Mhz *\n")
+    (dev / "pp_dpm_mclk").write_text("0: 900Mhz\n1: 2000Mhz *\n")
+
+    class Props:
+        pci_domain_id, pci_bus_id, pci_device_id = 0, 0x75, 0
+
+    real_join = bench.os.path.join
+    monkeypatch.setattr(bench.os.path, "join",
+                        lambda a, *b: real_join(str(tmp_path), *b) if a == "/sys/bus/pci/devices"
+                        else real_join(a, *b))
+    monkeypatch.setattr(subprocess, "run", None)
+    assert bench._clocks(Props) == {"sclk": "2400Mhz", "mclk": "2000Mhz"}
+
+    class Other:
+        pci_domain_id, pci_bus_id, pci_device_id = 0, 0x11, 0
+    assert bench._clocks(Other) is None
