@@ -444,63 +444,102 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // bytes directly instead (s loads 16 * s bytes apart across the lanes) ran
 // 14 % (s = 3) to 70 % (s = 7) slower on MI355X.  The register permutation is
 // fixed at compile time (S is a template parameter); only the destinations
-// are runtime values.  Blocks are 512 threads; a tile is 512 groups (512-
-// thread blocks measured up to 8 % faster than 256 at s = 8, equal elsewhere).
+// are runtime values.
+//
+// Each wave keeps 1 KiB * S of loads in flight, S times what a copy wave
+// keeps, and on MI355X the full gather (S writes per wave) ran fastest with
+// about 24-32 KiB of loads in flight per compute unit: at full occupancy
+// (32 waves per CU) it lost 9 % (s = 2) to 17 % (s = 8) against the capped
+// shapes.  Blocks are therefore 256 threads and each reserves enough LDS
+// that at most kPassBlocksPerCu(S) blocks fit in a CU's 160 KiB: 16 waves per
+// CU for s = 2, 8 for s = 3..5, 4 for s = 6..8 (the best of 4..32 waves per
+// CU and blocks of 256 or 512 threads for every s).  The reservation holds
+// the waves' staging slices; the rest of it is unused.  The view (FirstOnly:
+// S KiB read, 1 KiB written per wave) ran fastest uncapped, so it reserves
+// only its staging.  A wave only reads back the slice it wrote itself, so no
+// block barrier is needed: the LDS performs one wave's accesses in issue
+// order, and wavefront-scope fences keep the compiler from moving them (a
+// block barrier there cost up to 5 %).
 // FirstOnly keeps only the residue-0 pass: that is the strided view
 // x[::S] (out[m] = in[S*m]), read as contiguous spans of which 1/S is kept.
-constexpr int kPassThreads = 512;
+constexpr int kPassThreads = 256;
+constexpr int kLdsBytesPerCu = 160 * 1024;
+
+constexpr int kPassBlocksPerCu(int s) { return s == 2 ? 4 : s <= 5 ? 2 : 1; }
+
+// Bytes of LDS each pass block reserves: its staging (16 * S bytes per lane)
+// or, for the full gather if larger, just over 1/(blocks + 1) of the CU's LDS
+// so that no more than kPassBlocksPerCu(S) blocks are resident on one CU.
+constexpr int kPassLdsBytes(int s, bool first_only)
+{
+    return (first_only || kPassThreads * 16 * s > kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024)
+               ? kPassThreads * 16 * s
+               : kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024;
+}
+static_assert(kPassLdsBytes(2, false) * 5 > kLdsBytesPerCu &&
+                  kPassLdsBytes(3, false) * 3 > kLdsBytesPerCu &&
+                  kPassLdsBytes(6, false) * 2 > kLdsBytesPerCu &&
+                  kPassLdsBytes(8, false) <= kLdsBytesPerCu,
+              "the LDS reservation must cap the resident pass blocks per CU");
+
+// Orders this wave's LDS accesses at a point of the program: the LDS
+// performs one wave's accesses in issue order, so only the compiler needs
+// holding back (no instruction is emitted).
+__device__ __forceinline__ void wave_lds_order()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int S, bool FirstOnly>
 __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
 {
-    __shared__ u32x4 buf[kPassThreads / 64][64 * S];
+    __shared__ u32x4 lds[kPassLdsBytes(S, FirstOnly) / 16];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    u32x4 *buf = lds + wv * 64 * S;         // this wave's staging slice
+    constexpr int kRuns = FirstOnly ? 1 : S;
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         const uint64_t grp0 = t * kPassThreads + wv * 64;     // first group of this wave
-        const uint64_t wbase = (uint64_t)S * 4 * grp0;        // its first input element
-        const bool wfull = (grp0 + 64) * 4 * S <= g.n;       // the wave's span is in range
-        if (wfull) {
+        const uint64_t grp = grp0 + lane;
+        if ((grp0 + 64) * 4 * S <= g.n) {
+            // The wave's whole span is in range, so every lane's four slots
+            // exist in every pass.  A path of its own, with no element-wise
+            // fallback merged into its registers: the compiler then has no
+            // reason to wait for one store to complete before the next.
+            const uint64_t wbase = (uint64_t)S * 4 * grp0;    // its first input element
 #pragma unroll
             for (int v = 0; v < S; ++v)
-                buf[wv][64 * v + lane] = load16<false, 4>(
+                buf[64 * v + lane] = load16<false, 4>(
                     reinterpret_cast<const char *>(g.in + wbase + 4 * (64 * v + lane)));
-        }
-        __syncthreads();
-        const uint64_t grp = grp0 + lane;
-        if (grp < g.vectors) {
-            const uint64_t base = (uint64_t)S * 4 * grp;
+            wave_lds_order();
             u32x4 e[S];
-            if (wfull) {
 #pragma unroll
-                for (int v = 0; v < S; ++v) e[v] = buf[wv][S * lane + v];
-            } else {
+            for (int v = 0; v < S; ++v) e[v] = buf[S * lane + v];
+            wave_lds_order();       // read back before the next tile's writes
 #pragma unroll
-                for (int v = 0; v < S; ++v)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint64_t x = base + 4 * v + q;
-                        e[v][q] = x < g.n ? g.in[x] : 0u;
-                    }
-            }
-            const bool full = base + 4 * S <= g.n;
-#pragma unroll
-            for (int r = 0; r < (FirstOnly ? 1 : S); ++r) {
+            for (int r = 0; r < kRuns; ++r) {
                 u32x4 w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = e[(S * q + r) / 4][(S * q + r) % 4];
-                uint32_t *dst = g.out + g.dest[r] + 4 * grp;
-                if (full) {
-                    u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(dst);
-                    if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
-                    else *p = w;
-                } else {
+                u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(g.out + g.dest[r] + 4 * grp);
+                if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
+                else *p = w;
+            }
+        } else if (grp < g.vectors) {
+            // The wave at the end of the input: element by element.
+            const uint64_t base = (uint64_t)S * 4 * grp;
+            uint32_t e[4 * S];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        if (base + (uint64_t)S * q + r < g.n) dst[q] = w[q];
-                }
+            for (int k = 0; k < 4 * S; ++k) e[k] = base + k < g.n ? g.in[base + k] : 0u;
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r) {
+                uint32_t *dst = g.out + g.dest[r] + 4 * grp;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (base + (uint64_t)S * q + r < g.n) dst[q] = e[S * q + r];
             }
         }
-        __syncthreads();
     }
 }
 

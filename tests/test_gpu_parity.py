@@ -288,7 +288,9 @@ def test_gather_pass_decomposition_launch_variants():
             if bpc > 8:
                 continue      # the kernel's block shape is fixed: only the grid cap varies
             for s in (3, 5, 8):
-                n = (2 * bpc * cus + 1) * 512 * 4 * s - 7      # blocks of 512 groups
+                # one group (four outputs per pass) per thread of the fixed block
+                threads = ew.ew_make_gather_plan(1 << 40, 1 << 42, 1000003, s, cus).block
+                n = (2 * bpc * cus + 1) * threads * 4 * s - 7
                 while math.gcd(n, s) != 1:
                     n += 1
                 p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
