@@ -84,6 +84,14 @@ def counter_per_dispatch(path, kernel_re, counter):
     return statistics.median(per.values()), len(per)
 
 
+def dispatch_durations(path, kernel_re):
+    """Per-dispatch durations in ns of the kernel matching the regex, from a
+    rocprofv3 kernel_trace.csv."""
+    rx = re.compile(kernel_re)
+    return [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in _rows(path)
+            if rx.search(r.get("Kernel_Name", ""))]
+
+
 def cmd_trace(a):
     name, calls, avg, mn, mx = kernel_stats(a.stats, a.kernel)
     gbs = a.bytes / avg
@@ -98,6 +106,13 @@ def cmd_trace(a):
         f"kernel:          {name}",
         f"dispatches:      {calls}",
         f"average:         {avg / 1000:.3f} us   (min {mn / 1000:.3f}, max {mx / 1000:.3f})",
+    ]
+    if a.trace:
+        d = sorted(dispatch_durations(a.trace, a.kernel))
+        text.append(f"median:          {statistics.median(d) / 1000:.3f} us   (p10 "
+                    f"{d[len(d) // 10] / 1000:.3f}, p90 {d[(9 * len(d)) // 10] / 1000:.3f}; "
+                    f"{len(d)} dispatches in {os.path.basename(a.trace)})")
+    text += [
         f"algorithmic:     {a.bytes} bytes per launch",
         f"achieved:        {gbs:.1f} GB/s = {100 * gbs / 8000:.2f} % of 8000 GB/s",
         f"kernel source:   ew_kernels.hip sha256[:16] {src_hash} (of the profiled run)",
@@ -171,6 +186,8 @@ def main(argv=None):
     t.add_argument("--bytes", type=int, required=True)
     t.add_argument("--command", required=True)
     t.add_argument("--title", default="Kernel duration")
+    t.add_argument("--trace", help="the run's kernel_trace.csv: also report the per-dispatch "
+                                   "median")
     t.add_argument("--bench-json", required=True,
                    help="the bench.py output of the profiled run (events and source hash)")
     t.add_argument("--out", required=True)
