@@ -150,8 +150,8 @@ def test_gather_plan_segments(n, stride, reps, segment, passes):
         assert p.head == 0 and p.tail == segment % 4
     else:
         assert p.head == 0 and p.tail == 0 and p.vectors == -(-segment // 4)
-        assert (p.block, p.unroll) == (512, 1)
-        assert p.tiles == -(-p.vectors // 512)
+        assert (p.block, p.unroll) == (256, 1)         # one group of 4 slots per thread
+        assert p.tiles == -(-p.vectors // 256)
         assert p.grid == min(p.tiles, p.blocks_per_cu * CUS)
 
 
