@@ -7,6 +7,13 @@ Kernel durations (from ``rocprofv3 --kernel-trace --stats -f csv``):
         --bench-json BENCH_OUTPUT_OF_THE_PROFILED_RUN \\
         --command "the rocprofv3 command line" --out profiles/FILE.txt
 
+Every configuration's kernel durations from the kernel trace of one default
+bench run (per-dispatch median, matched by kernel name, grid and block):
+
+    python -m memory_bound_elementwise_amd.rocprof_summary configs \\
+        --trace DIR/NAME_kernel_trace.csv --bench-json BENCH_OUTPUT \\
+        --command "the rocprofv3 command line" --out profiles/FILE.txt
+
 HBM traffic (from two ``rocprofv3 --pmc`` runs per kernel, FETCH_SIZE then
 WRITE_SIZE, each in KiB per dispatch).  The counters are calibrated on the
 plain copy kernel of known size: scale = algorithmic bytes / counted bytes,
@@ -176,6 +183,70 @@ def cmd_traffic(a):
         f.write("\n")
 
 
+# Kernel of each operation in a kernel trace (template operator name).
+OP_KERNEL = {"add_f32": "OpAddF32", "add_f16": "OpAddF16", "add_bf16": "OpAddBF16",
+             "saxpy_f32": "OpSaxpyF32", "relu_f32": "OpReluF32", "copy_f32": "OpCopyF32"}
+BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12, "relu_f32": 8,
+                  "copy_f32": 8, "gather_f32": 8}
+
+
+def cmd_configs(a):
+    """Per-dispatch durations of every configuration's kernel in one traced
+    default bench run: each record of the bench line (main workload and
+    other_configs) whose op is a streaming op or the gather is matched to the
+    trace by kernel name, grid and block."""
+    line = bench_record(a.bench_json)
+    src_hash = line.get("env", {}).get("kernel_source_sha256_16")
+    main = {"workload": line["config"]["name"], "op": line["config"]["op"],
+            "n": line["config"]["n"], "launch": line["config"]["launch"],
+            "split": line["config"]["split"], "gbs": line["value"], "timing": "back-to-back, mean"}
+    recs = [main] + [r for r in line.get("other_configs", [])
+                     if r.get("op") in BYTES_PER_ELEM and r.get("workload", "").startswith(("cfg", "headline"))]
+    rows = _rows(a.trace)
+    text = [
+        "# Kernel durations of the five configurations and the headline (rocprofv3 kernel trace)",
+        "",
+        f"command: {a.command}",
+        f"source:  per-dispatch durations (End - Start) in {os.path.basename(a.trace)}, each "
+        "configuration's kernel matched by name, grid and block",
+        "note:    for the cold workloads (<= 1 GiB) the dispatches include the rotated launches "
+        "that bench.py times, the flushed per-launch ones and the warm ones; all include the "
+        "parity launch",
+        "         the bench.py column is that profiled run's own figure: the tracer adds host-side "
+        "cost to every launch, which shows only where back-to-back launches are bound by the "
+        "host (the 2^20 add)",
+        f"kernel source: ew_kernels.hip sha256[:16] {src_hash} (of the profiled run)",
+        "",
+        "| workload | kernel | grid x block | dispatches | median us (p10, p90) | GB/s at the median "
+        "| bench.py GB/s (its timing) |",
+        "|---|---|---|---|---|---|---|",
+    ]
+    for r in sorted(recs, key=lambda r: r["workload"]):
+        op, n, lc = r["op"], r["n"], r["launch"]
+        if op == "gather_f32":
+            rx = re.compile(r"ew_gather(2|_passes)?_kernel")
+        else:
+            co = ["true" if c else "false" for c in r["split"]["in_coaligned"]]
+            rx = re.compile(re.escape(f"ew_stream_kernel<ew::{OP_KERNEL[op]}, {lc['unroll']}, "
+                                      f"{co[0]}, {co[1]}>"))
+        d = sorted(int(x["End_Timestamp"]) - int(x["Start_Timestamp"]) for x in rows
+                   if rx.search(x["Kernel_Name"])
+                   and int(x["Workgroup_Size_X"]) == lc["block"]
+                   and int(x["Grid_Size_X"]) == lc["block"] * lc["grid"])
+        if not d:
+            raise SystemExit(f"no dispatch of {r['workload']}'s kernel in {a.trace}")
+        med = statistics.median(d)
+        name = next(x["Kernel_Name"] for x in rows if rx.search(x["Kernel_Name"]))
+        name = name.replace("void ew::", "").split("(")[0]
+        gbs = BYTES_PER_ELEM[op] * n / med
+        text.append(f"| {r['workload']} | {name} | {lc['grid']} x {lc['block']} | {len(d)} | "
+                    f"{med / 1000:.2f} ({d[len(d) // 10] / 1000:.2f}, {d[(9 * len(d)) // 10] / 1000:.2f}) | "
+                    f"{gbs:.1f} | {r['gbs']} ({r['timing']}) |")
+    with open(a.out, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -211,8 +282,13 @@ def main(argv=None):
     r.add_argument("--bench-json-write", required=True,
                    help="bench.py output of the WRITE_SIZE run")
     r.add_argument("--out", required=True)
+    c = sub.add_parser("configs")
+    c.add_argument("--trace", required=True, help="kernel_trace.csv of a default bench run")
+    c.add_argument("--bench-json", required=True, help="that run's bench.py output")
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    (cmd_trace if a.cmd == "trace" else cmd_traffic)(a)
+    {"trace": cmd_trace, "traffic": cmd_traffic, "configs": cmd_configs}[a.cmd](a)
     return 0
 
 
