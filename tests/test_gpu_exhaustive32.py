@@ -1,0 +1,89 @@
+"""Every binary32 bit pattern through the HIP path, against the oracle:
+
+* ew_relu_f32 on all 2^32 patterns, bitwise (ReLU read as IEEE maximum(x, +0):
+  -0 and negatives become +0, NaNs pass through with their payload);
+* ew_add_f32 with every pattern once as the first operand, paired with
+  h(a) = a * 0x9E3779B1 mod 2^32 (odd multiplier, so a bijection: every
+  pattern is also the second operand exactly once), bitwise except that a
+  NaN matches any NaN.
+
+Four launches of 2^30 elements each, the input misaligned by one element.
+The oracle runs on the host, split over the process's cores (at most 16).
+"""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import memory_bound_elementwise_amd as ew
+import oracle
+from tests.gpu_util import download, upload
+
+pytestmark = pytest.mark.gpu
+
+CHUNK = 1 << 30
+MULT = np.uint32(0x9E3779B1)
+
+
+def _parallel(fn, *arrays):
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    n = arrays[0].size
+    step = -(-n // workers)
+    out = np.empty_like(arrays[0])
+
+    def part(lo):
+        out[lo:lo + step] = fn(*(a[lo:lo + step] for a in arrays))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(part, range(0, n, step)))
+    return out
+
+
+def _chunk(k):
+    print(f"[exhaustive32] patterns {k * CHUNK:#010x}..{(k + 1) * CHUNK - 1:#010x}", flush=True)
+    return np.arange(k * CHUNK, (k + 1) * CHUNK, dtype=np.uint32)
+
+
+def test_relu_on_every_f32_pattern():
+    for k in range((1 << 32) // CHUNK):
+        bits = _chunk(k)
+        x = bits.view(np.float32)
+        xd, kx = upload(x, 1)
+        yd, ky = upload(np.zeros(CHUNK, np.float32), 0)
+        ew.ew_relu_f32(xd, yd)
+        torch.cuda.synchronize()
+        got = download(yd, 4).view(np.uint32)
+        del xd, kx, yd, ky
+        torch.cuda.empty_cache()
+        ref = _parallel(oracle.relu_f32, x).view(np.uint32)
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, (f"{bad.size} mismatches, first x={bits[bad[0]]:#010x}: "
+                               f"got {got[bad[0]]:#010x}, want {ref[bad[0]]:#010x}")
+        del bits, x, got, ref
+
+
+def test_add_with_every_f32_pattern_as_each_operand():
+    for k in range((1 << 32) // CHUNK):
+        a_bits = _chunk(k)
+        b_bits = a_bits * MULT                      # wraps mod 2^32
+        a, b = a_bits.view(np.float32), b_bits.view(np.float32)
+        ad, ka = upload(a, 1)
+        bd, kb = upload(b, 0)
+        cd, kc = upload(np.zeros(CHUNK, np.float32), 2)
+        ew.ew_add_f32(ad, bd, cd)
+        torch.cuda.synchronize()
+        got = download(cd, 4).view(np.uint32)
+        del ad, ka, bd, kb, cd, kc
+        torch.cuda.empty_cache()
+        ref = _parallel(oracle.add_f32, a, b).view(np.uint32)
+        bad = np.flatnonzero(got != ref)
+        if bad.size:                                # NaN payloads may differ
+            g, r = got[bad], ref[bad]
+            both_nan = ((g & 0x7FFFFFFF) > 0x7F800000) & ((r & 0x7FFFFFFF) > 0x7F800000)
+            wrong = bad[~both_nan]
+            assert wrong.size == 0, (
+                f"{wrong.size} mismatches, first a={a_bits[wrong[0]]:#010x} "
+                f"b={b_bits[wrong[0]]:#010x}: got {got[wrong[0]]:#010x}, "
+                f"want {ref[wrong[0]]:#010x}")
+        del a_bits, b_bits, a, b, got, ref, bad
