@@ -5,7 +5,11 @@
 * ew_add_f32 with every pattern once as the first operand, paired with
   h(a) = a * 0x9E3779B1 mod 2^32 (odd multiplier, so a bijection: every
   pattern is also the second operand exactly once), bitwise except that a
-  NaN matches any NaN.
+  NaN matches any NaN;
+* ew_saxpy_f32 (alpha = 2.5, the SAXPY workload's) with every pattern once
+  as x and once as y, paired the same way, against the oracle's fmaf:
+  bitwise except that a NaN matches any NaN (the 1-ulp allowance is not
+  used).
 
 Four launches of 2^30 elements each, the input misaligned by one element.
 The oracle runs on the host, split over the process's cores (at most 16).
@@ -63,20 +67,15 @@ def test_relu_on_every_f32_pattern():
         del bits, x, got, ref
 
 
-def test_add_with_every_f32_pattern_as_each_operand():
+def _both_operands(run, ref_fn):
+    """run(a, b) -> the HIP result for one chunk; ref_fn(a, b) -> the oracle's."""
     for k in range((1 << 32) // CHUNK):
         a_bits = _chunk(k)
         b_bits = a_bits * MULT                      # wraps mod 2^32
         a, b = a_bits.view(np.float32), b_bits.view(np.float32)
-        ad, ka = upload(a, 1)
-        bd, kb = upload(b, 0)
-        cd, kc = upload(np.zeros(CHUNK, np.float32), 2)
-        ew.ew_add_f32(ad, bd, cd)
-        torch.cuda.synchronize()
-        got = download(cd, 4).view(np.uint32)
-        del ad, ka, bd, kb, cd, kc
+        got = run(a, b)
         torch.cuda.empty_cache()
-        ref = _parallel(oracle.add_f32, a, b).view(np.uint32)
+        ref = _parallel(ref_fn, a, b).view(np.uint32)
         bad = np.flatnonzero(got != ref)
         if bad.size:                                # NaN payloads may differ
             g, r = got[bad], ref[bad]
@@ -87,3 +86,24 @@ def test_add_with_every_f32_pattern_as_each_operand():
                 f"b={b_bits[wrong[0]]:#010x}: got {got[wrong[0]]:#010x}, "
                 f"want {ref[wrong[0]]:#010x}")
         del a_bits, b_bits, a, b, got, ref, bad
+
+
+def test_add_with_every_f32_pattern_as_each_operand():
+    def run(a, b):
+        ad, ka = upload(a, 1)
+        bd, kb = upload(b, 0)
+        cd, kc = upload(np.zeros(a.size, np.float32), 2)
+        ew.ew_add_f32(ad, bd, cd)
+        torch.cuda.synchronize()
+        return download(cd, 4).view(np.uint32)
+    _both_operands(run, oracle.add_f32)
+
+
+def test_saxpy_with_every_f32_pattern_as_x_and_as_y():
+    def run(x, y):
+        xd, kx = upload(x, 1)
+        yd, ky = upload(y, 0)
+        ew.ew_saxpy_f32(2.5, xd, yd)
+        torch.cuda.synchronize()
+        return download(yd, 4).view(np.uint32)
+    _both_operands(run, lambda x, y: oracle.saxpy_f32(2.5, x, y))
