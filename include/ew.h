@@ -310,9 +310,10 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * slot m of all s runs reads the s consecutive elements s*m .. s*m + s - 1.
  * The kernel reads the input once, contiguously (staged through LDS), and
  * writes the s runs; segment = ceil(n / s) (the longest run), vectors =
- * groups of four slots, head = tail = 0, block = 512 and unroll = 1 whatever
- * the table says (its blocks_per_cu still caps the grid).  Otherwise
- * passes = 1.
+ * groups of four slots, head = tail = 0, block = 256 and unroll = 1 whatever
+ * the table says (its blocks_per_cu still caps the grid; the kernel's own LDS
+ * reservation limits how many of its blocks share a compute unit).
+ * Otherwise passes = 1.
  * Same validation as ew_gather_f32. */
 ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
                                 size_t stride, int cu_count, ew_plan_t *plan);
