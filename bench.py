@@ -721,12 +721,22 @@ def main(argv=None):
                 continue
             log(f"other config {name}")
             steps = 200 if ow.n >= (1 << 25) else 1000
-            r, p, _ = measure(ow, torch, np, ew, synth, stream, steps, 10, cus, flush_buf, 0.0,
-                              check=not args.no_cpu_baseline)
+            try:
+                r, p, _ = measure(ow, torch, np, ew, synth, stream, steps, 10, cus, flush_buf,
+                                  0.0, check=not args.no_cpu_baseline)
+                del p
+            except Exception as exc:
+                # recorded, and nothing more is launched (the error may have left the
+                # device unusable); the headline line below still prints
+                others.append({"workload": name, "op": ow.op, "n": ow.n,
+                               "error": f"{type(exc).__name__}: {exc}"})
+                log(f"other config {name} failed, remaining configs skipped: {exc}")
+                break
             others.append(r)
-            del p
             torch.cuda.empty_cache()
         line["other_configs"] = others
+        if any("error" in r for r in others):
+            line["other_configs_incomplete"] = True
         by = {r["workload"]: r for r in others + [res]}
         sg, cg = by.get("cfg5b_gather_f32_2e26_s2"), by.get("cfg5a_copy_f32_2e26")
         if sg and cg and sg.get("gbs") and cg.get("gbs"):
