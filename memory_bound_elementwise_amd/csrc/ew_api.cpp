@@ -83,10 +83,10 @@ constexpr DefaultRow kDefaults[] = {
     {kOpAddBF16, {size_t(1) << 22, 128, 1024, 1}},
     {kOpSaxpyF32, {0, 512, 1, 1}},
     {kOpSaxpyF32, {size_t(1) << 22, 1024, 1024, 1}},
-    {kOpReluF32, {0, 64, 1024, 1}},
-    {kOpReluF32, {size_t(1) << 22, 512, 1024, 1}},
-    {kOpCopyF32, {0, 1024, 2, 2}},
-    {kOpCopyF32, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpReluF32, {0, 512, 8, 1}},
+    {kOpReluF32, {size_t(1) << 22, 256, 1024, 1}},
+    {kOpCopyF32, {0, 256, 8, 1}},
+    {kOpCopyF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpGatherF32, {0, 128, 4, 1}},
     {kOpGatherF32, {size_t(1) << 22, 128, 1024, 1}},
     {kOpAddReluF32, {0, 512, 1024, 2}},
@@ -99,10 +99,10 @@ constexpr DefaultRow kDefaults[] = {
     {kOpSaxpyF16, {size_t(1) << 22, 128, 1024, 1}},
     {kOpSaxpyBF16, {0, 128, 2, 2}},
     {kOpSaxpyBF16, {size_t(1) << 22, 128, 1024, 1}},
-    {kOpReluF16, {0, 1024, 2, 1}},
-    {kOpReluF16, {size_t(1) << 22, 512, 1024, 1}},
-    {kOpReluBF16, {0, 512, 8, 2}},
-    {kOpReluBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpReluF16, {0, 1024, 8, 1}},
+    {kOpReluF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpReluBF16, {0, 128, 4, 2}},
+    {kOpReluBF16, {size_t(1) << 22, 128, 1024, 1}},
     {kOpCopy2dF32, {0, 1024, 1024, 2}},
     {kOpCopy2dF32, {size_t(1) << 22, 128, 1024, 2}},
     {kOpReluInplaceF32, {0, 1024, 1, 4}},

@@ -16,7 +16,9 @@
 //     loads of a tile issued before the first store so that enough bytes are
 //     in flight to cover HBM latency ([EwOps] point 2 on overlapping
 //     requests; [PerfNotes] section 2.2, hide latency rather than reduce it);
-//   * non-temporal stores: nothing written is read again by this kernel.
+//   * non-temporal stores: nothing written is read again by this kernel
+//     (single-input streams store at device scope as well, see
+//     store16_device).
 //
 // No matrix cores: nothing is contracted.  The streaming kernels use no LDS
 // either (every byte is used once); LDS only reorders data where the access
@@ -90,6 +92,25 @@ __device__ __forceinline__ void store16(char *p, u32x4 v)
     u32x4 *q = reinterpret_cast<u32x4 *>(p);
     if constexpr (EW_STORE_NT) __builtin_nontemporal_store(v, q);
     else *q = v;
+}
+
+// A non-temporal 16-byte store at device scope (the sc1 bit as well as nt).
+// On MI355X a stream that reads one array and writes one (copy, ReLU) ran
+// about 3 % faster with these stores, at 128-256-thread blocks, than with
+// plain non-temporal ones; streams that read two arrays per one written (the
+// adds, SAXPY) ran 1-2 % slower with them, so they keep store16.  No builtin
+// sets sc1 on a global store, so this is a raw buffer store (cache-policy
+// bits 0x12 = sc1 | nt) through a descriptor whose base is the caller's tile
+// start (uniform across the block) and whose range is tile_bytes; the
+// compiler emits it, so it also handles the instruction's hazards (a
+// hand-written store in inline assembly got no wait state before the next
+// write of its data registers and stored stale data).
+__device__ __forceinline__ void store16_device(char *tile, uint32_t tile_bytes, uint32_t off,
+                                               u32x4 v)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(tile, (short)0, (int)tile_bytes, 0x00020000);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0x12);
 }
 
 // ---------------------------------------------------------------------------
@@ -339,7 +360,11 @@ __global__ void __launch_bounds__(1024) ew_stream_kernel(StreamArgs args)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const u32x4 b = kTwo ? y[u] : u32x4{0, 0, 0, 0};
-                store16(out + (v0 + u * nthr) * 16, Op::vec(x[u], b, alpha));
+                if constexpr (kTwo)
+                    store16(out + (v0 + u * nthr) * 16, Op::vec(x[u], b, alpha));
+                else
+                    store16_device(out + t * tile_vecs * 16, (uint32_t)(tile_vecs * 16),
+                                   (uint32_t)((tid + u * nthr) * 16), Op::vec(x[u], b, alpha));
             }
         } else {
             // Last, partial tile.
@@ -349,7 +374,11 @@ __global__ void __launch_bounds__(1024) ew_stream_kernel(StreamArgs args)
                 if (v < args.vectors) {
                     const u32x4 a = load16<Co0, kElem>(in0 + v * 16);
                     const u32x4 b = kTwo ? load16<Co1, kElem>(in1 + v * 16) : u32x4{0, 0, 0, 0};
-                    store16(out + v * 16, Op::vec(a, b, alpha));
+                    if constexpr (kTwo)
+                        store16(out + v * 16, Op::vec(a, b, alpha));
+                    else
+                        store16_device(out + t * tile_vecs * 16, (uint32_t)(tile_vecs * 16),
+                                       (uint32_t)((tid + u * nthr) * 16), Op::vec(a, b, alpha));
                 }
             }
         }

@@ -14,7 +14,10 @@ silently; these checks fail the build's tests if it does:
 * the ReLU kernels select with a compare (no v_max_*, whose NaN rule returns
   the other operand);
 * the streaming kernels move 16 bytes per lane (global_load_dwordx4 /
-  global_store_dwordx4) and store non-temporally.
+  global_store_dwordx4) and store non-temporally; the single-input ones
+  (copy, ReLU) store their body with a compiler-emitted buffer store
+  carrying the device-scope and non-temporal bits (buffer_store_dwordx4 ...
+  nt sc1).
 """
 import importlib.util
 import os
@@ -90,11 +93,28 @@ def test_saxpy_kernels_use_a_fused_multiply_add(asm):
             assert not re.search(r"\bv_mul_f32\b", body), name
 
 
+SINGLE_INPUT_OPS = ("OpReluF32", "OpCopyF32", "OpRelu16")
+
+
 def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
+    n_single = 0
     for name, (body, _) in _kernels(asm).items():
         if "ew_stream_kernel" in name or "relu_inplace" in name:
             assert re.search(r"global_load_dwordx4 .* nt\b", body), name
-            assert re.search(r"global_store_dwordx4 .* nt\b", body), name
+            if "ew_stream_kernel" in name and any(op in name for op in SINGLE_INPUT_OPS):
+                n_single += 1
+                assert re.search(r"buffer_store_dwordx4 .* nt sc1\b", body), name
+                assert not re.search(r"global_store_dwordx4", body), name
+            else:
+                assert re.search(r"global_store_dwordx4 .* nt\b", body), name
+    assert n_single > 0
+
+
+def test_device_scope_stores_come_from_the_compiler(asm):
+    """The sc1 bit is set only through the buffer-store builtin: a global
+    store with sc1 could only come from inline assembly, whose data registers
+    the compiler does not protect after issue (that once stored stale data)."""
+    assert not re.search(r"global_store_dword\S* .*\bsc1\b", asm)
 
 
 def test_transpose_moves_16_bytes_per_lane_through_lds(asm):
