@@ -103,8 +103,8 @@ constexpr DefaultRow kDefaults[] = {
     {kOpReluF16, {size_t(1) << 22, 128, 1024, 1}},
     {kOpReluBF16, {0, 128, 4, 2}},
     {kOpReluBF16, {size_t(1) << 22, 128, 1024, 1}},
-    {kOpCopy2dF32, {0, 1024, 1024, 2}},
-    {kOpCopy2dF32, {size_t(1) << 22, 128, 1024, 2}},
+    {kOpCopy2dF32, {0, 256, 2, 2}},
+    {kOpCopy2dF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpReluInplaceF32, {0, 1024, 1, 4}},
     {kOpReluInplaceF32, {size_t(1) << 22, 512, 1024, 1}},
 };

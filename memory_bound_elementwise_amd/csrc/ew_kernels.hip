@@ -752,7 +752,9 @@ __global__ void __launch_bounds__(1024) ew_copy2d_kernel(Copy2dArgs a)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t v = v0 + u * nthr;
-            if (v < a.vectors) store16(out + v * 16, x[u]);
+            if (v < a.vectors)        // one view read, one array written: device scope
+                store16_device(out + t * tile_vecs * 16, (uint32_t)(tile_vecs * 16),
+                               (uint32_t)((tid + u * nthr) * 16), x[u]);
         }
         ct += a.step_tile_c;
         rt += a.step_tile_r;
