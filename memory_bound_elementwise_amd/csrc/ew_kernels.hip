@@ -885,8 +885,8 @@ __global__ void __launch_bounds__(1024) ew_relu_inplace_kernel(StreamArgs args)
     const uint64_t tile_vecs = nthr * U;
     const uint32_t lane = __lane_id();
 
-    // Store vector v (already loaded as w) if its group needs it.
-    auto finish = [&](uint64_t v, u32x4 w) {
+    // Store vector v of tile t (already loaded as w) if its group needs it.
+    auto finish = [&](uint64_t t, uint64_t v, u32x4 w) {
         bool ch[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) ch[k] = relu_changes(w[k]);
@@ -906,7 +906,9 @@ __global__ void __launch_bounds__(1024) ew_relu_inplace_kernel(StreamArgs args)
                 u32x4 r;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) r[k] = ch[k] ? 0u : w[k];
-                store16(body + v * 16, r);
+                // one array read, (part of) it written: a device-scope store
+                store16_device(body + t * tile_vecs * 16, (uint32_t)(tile_vecs * 16),
+                               (uint32_t)((v - t * tile_vecs) * 16), r);
             }
         }
     };
@@ -918,12 +920,12 @@ __global__ void __launch_bounds__(1024) ew_relu_inplace_kernel(StreamArgs args)
 #pragma unroll
             for (int u = 0; u < U; ++u) w[u] = load16<true, 4>(body + (v0 + u * nthr) * 16);
 #pragma unroll
-            for (int u = 0; u < U; ++u) finish(v0 + u * nthr, w[u]);
+            for (int u = 0; u < U; ++u) finish(t, v0 + u * nthr, w[u]);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const uint64_t v = v0 + u * nthr;
-                if (v < args.vectors) finish(v, load16<true, 4>(body + v * 16));
+                if (v < args.vectors) finish(t, v, load16<true, 4>(body + v * 16));
             }
         }
     }

@@ -15,9 +15,9 @@ silently; these checks fail the build's tests if it does:
   the other operand);
 * the streaming kernels move 16 bytes per lane (global_load_dwordx4 /
   global_store_dwordx4) and store non-temporally; the single-input ones
-  (copy, ReLU) and the strided-view kernel store their body with a
-  compiler-emitted buffer store carrying the device-scope and non-temporal
-  bits (buffer_store_dwordx4 ... nt sc1).
+  (copy, ReLU, in-place ReLU) and the strided-view kernel store their body
+  with a compiler-emitted buffer store carrying the device-scope and
+  non-temporal bits (buffer_store_dwordx4 ... nt sc1).
 """
 import importlib.util
 import os
@@ -101,7 +101,8 @@ def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
     for name, (body, _) in _kernels(asm).items():
         if "ew_stream_kernel" in name or "relu_inplace" in name:
             assert re.search(r"global_load_dwordx4 .* nt\b", body), name
-            if "ew_stream_kernel" in name and any(op in name for op in SINGLE_INPUT_OPS):
+            if ("relu_inplace" in name or
+                    ("ew_stream_kernel" in name and any(op in name for op in SINGLE_INPUT_OPS))):
                 n_single += 1
                 assert re.search(r"buffer_store_dwordx4 .* nt sc1\b", body), name
                 assert not re.search(r"global_store_dwordx4", body), name
