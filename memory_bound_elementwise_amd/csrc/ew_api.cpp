@@ -93,8 +93,8 @@ constexpr DefaultRow kDefaults[] = {
     {kOpAddReluF32, {size_t(1) << 22, 1024, 1024, 1}},
     {kOpSaxpyReluF32, {0, 512, 4, 2}},
     {kOpSaxpyReluF32, {size_t(1) << 22, 1024, 1024, 1}},
-    {kOpBiasReluF32, {0, 1024, 4, 2}},
-    {kOpBiasReluF32, {size_t(1) << 22, 128, 1024, 2}},
+    {kOpBiasReluF32, {0, 1024, 1024, 1}},
+    {kOpBiasReluF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpSaxpyF16, {0, 256, 1024, 4}},
     {kOpSaxpyF16, {size_t(1) << 22, 128, 1024, 1}},
     {kOpSaxpyBF16, {0, 128, 2, 2}},

@@ -690,7 +690,9 @@ __global__ void __launch_bounds__(1024) ew_bias_relu_kernel(BiasArgs a)
                 f32x4 s = __builtin_bit_cast(f32x4, xv[u]) + bv[u], r;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) r[k] = OpReluF32::relu(s[k]);
-                store16(y + v * 16, __builtin_bit_cast(u32x4, r));
+                // one array read (and the small bias row), one written
+                store16_device(y + t * tile_vecs * 16, (uint32_t)(tile_vecs * 16),
+                               (uint32_t)((tid + u * nthr) * 16), __builtin_bit_cast(u32x4, r));
             }
         }
         ct = add_mod(ct, a.step_tile, cols);

@@ -15,7 +15,7 @@ silently; these checks fail the build's tests if it does:
   the other operand);
 * the streaming kernels move 16 bytes per lane (global_load_dwordx4 /
   global_store_dwordx4) and store non-temporally; the single-input ones
-  (copy, ReLU, in-place ReLU) and the strided-view kernel store their body
+  (copy, ReLU, in-place ReLU, bias + ReLU) and the strided-view kernel store their body
   with a compiler-emitted buffer store carrying the device-scope and
   non-temporal bits (buffer_store_dwordx4 ... nt sc1).
 """
@@ -111,8 +111,9 @@ def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
     assert n_single > 0
 
 
-def test_strided_view_kernel_stores_at_device_scope(asm):
-    ks = [v[0] for k, v in _kernels(asm).items() if "ew_copy2d_kernel" in k]
+def test_strided_view_and_bias_relu_kernels_store_at_device_scope(asm):
+    ks = [v[0] for k, v in _kernels(asm).items()
+          if "ew_copy2d_kernel" in k or "ew_bias_relu_kernel" in k]
     assert ks
     for body in ks:
         assert re.search(r"buffer_store_dwordx4 .* nt sc1\b", body)
