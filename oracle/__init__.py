@@ -22,6 +22,11 @@ Each function wraps the plain scalar C loop of the same name in ``oracle.c``
 * ``gather_index(n, stride, i)``  the input index of one gather output
 * ``copy2d_f32(base, offset, stride_r, stride_c, rows, cols)``  strided view
   copied to a contiguous array
+* ``scale_f32 / scale_f16 / scale_bf16(alpha, x)``  alpha * x
+* ``add_scalar_f32 / add_scalar_f16 / add_scalar_bf16(alpha, x)``  x + alpha
+* ``sqrt_f32 / sqrt_f16 / sqrt_bf16(x)``  correctly rounded binary32 sqrt
+  (16-bit: of the widened value, rounded to the 16-bit format)
+* ``abs_f32 / abs_f16 / abs_bf16(x)``  sign bit cleared
 
 plus the scalar conversions and the binary32 ulp distance.  Parity status:
 all functions pinned (see ``tests/test_oracle.py``); none unpinned.
@@ -66,6 +71,14 @@ def _load():
     for name in ("oracle_relu_f32", "oracle_copy_f32",
                  "oracle_f32_to_f16_array", "oracle_f16_to_f32_array",
                  "oracle_f32_to_bf16_array", "oracle_bf16_to_f32_array"):
+        getattr(lib, name).argtypes = [vp, vp, sz]
+        getattr(lib, name).restype = None
+    for name in ("oracle_scale_f32", "oracle_add_scalar_f32", "oracle_scale_f16",
+                 "oracle_scale_bf16", "oracle_add_scalar_f16", "oracle_add_scalar_bf16"):
+        getattr(lib, name).argtypes = [ctypes.c_float, vp, vp, sz]
+        getattr(lib, name).restype = None
+    for name in ("oracle_sqrt_f32", "oracle_abs_f32", "oracle_sqrt_f16", "oracle_sqrt_bf16",
+                 "oracle_abs_16"):
         getattr(lib, name).argtypes = [vp, vp, sz]
         getattr(lib, name).restype = None
     lib.oracle_copy2d_f32.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, sz, sz]
@@ -230,6 +243,78 @@ def relu_f32(x):
     y = np.empty_like(x)
     lib.oracle_relu_f32(_ptr(x), _ptr(y), x.size)
     return y
+
+
+def _map(name, dtype, x, alpha=None):
+    lib = _load()
+    _check_env(lib)
+    x = _as(x, dtype)
+    y = np.empty_like(x)
+    if alpha is None:
+        getattr(lib, name)(_ptr(x), _ptr(y), x.size)
+    else:
+        getattr(lib, name)(float(np.float32(alpha)), _ptr(x), _ptr(y), x.size)
+    return y
+
+
+def scale_f32(alpha, x):
+    """alpha * x in binary32."""
+    return _map("oracle_scale_f32", np.float32, x, alpha)
+
+
+def scale_f16(alpha, x):
+    """rne16(alpha * widen(x)) on binary16 bit patterns."""
+    return _map("oracle_scale_f16", np.uint16, x, alpha)
+
+
+def scale_bf16(alpha, x):
+    """rnebf(alpha * widen(x)) on bfloat16 bit patterns."""
+    return _map("oracle_scale_bf16", np.uint16, x, alpha)
+
+
+def add_scalar_f32(alpha, x):
+    """x + alpha in binary32."""
+    return _map("oracle_add_scalar_f32", np.float32, x, alpha)
+
+
+def add_scalar_f16(alpha, x):
+    """rne16(widen(x) + alpha) on binary16 bit patterns."""
+    return _map("oracle_add_scalar_f16", np.uint16, x, alpha)
+
+
+def add_scalar_bf16(alpha, x):
+    """rnebf(widen(x) + alpha) on bfloat16 bit patterns."""
+    return _map("oracle_add_scalar_bf16", np.uint16, x, alpha)
+
+
+def sqrt_f32(x):
+    """Correctly rounded binary32 square root."""
+    return _map("oracle_sqrt_f32", np.float32, x)
+
+
+def sqrt_f16(x):
+    """rne16(sqrtf(widen(x))) on binary16 bit patterns."""
+    return _map("oracle_sqrt_f16", np.uint16, x)
+
+
+def sqrt_bf16(x):
+    """rnebf(sqrtf(widen(x))) on bfloat16 bit patterns."""
+    return _map("oracle_sqrt_bf16", np.uint16, x)
+
+
+def abs_f32(x):
+    """The sign bit cleared, every other bit kept."""
+    return _map("oracle_abs_f32", np.float32, x)
+
+
+def abs_f16(x):
+    """Bit 15 cleared (binary16)."""
+    return _map("oracle_abs_16", np.uint16, x)
+
+
+def abs_bf16(x):
+    """Bit 15 cleared (bfloat16)."""
+    return _map("oracle_abs_16", np.uint16, x)
 
 
 def copy_f32(x):

@@ -278,6 +278,72 @@ void oracle_relu_bf16(const uint16_t *x, uint16_t *y, size_t n)
     }
 }
 
+/* Scalar-broadcast and unary maps, y[i] = f(x[i]): [EwOps] section 二 (the
+ * template code whose middle operation is the only part that changes).
+ * binary32: f is a single binary32 operation, rounded to nearest-even --
+ * alpha * x, x + alpha, or sqrtf (IEEE 754 requires the square root to be
+ * correctly rounded, and C99 sqrtf is that operation).  |x| clears the sign
+ * bit and keeps every other bit. */
+void oracle_scale_f32(float alpha, const float *x, float *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = alpha * x[i];
+}
+
+void oracle_add_scalar_f32(float alpha, const float *x, float *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = x[i] + alpha;
+}
+
+void oracle_sqrt_f32(const float *x, float *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = sqrtf(x[i]);
+}
+
+void oracle_abs_f32(const float *x, float *y, size_t n)
+{
+    const uint32_t *s = (const uint32_t *)x;
+    uint32_t *d = (uint32_t *)y;
+    for (size_t i = 0; i < n; ++i) d[i] = s[i] & 0x7fffffffu;
+}
+
+/* The same maps on 16-bit data: widen x exactly, apply f once in binary32
+ * (with the binary32 alpha), round the result to the 16-bit format
+ * nearest-even -- the rule of the 16-bit add.  |x| clears bit 15. */
+void oracle_scale_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = oracle_f32_to_f16(alpha * oracle_f16_to_f32(x[i]));
+}
+
+void oracle_scale_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = oracle_f32_to_bf16(alpha * oracle_bf16_to_f32(x[i]));
+}
+
+void oracle_add_scalar_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = oracle_f32_to_f16(oracle_f16_to_f32(x[i]) + alpha);
+}
+
+void oracle_add_scalar_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = oracle_f32_to_bf16(oracle_bf16_to_f32(x[i]) + alpha);
+}
+
+void oracle_sqrt_f16(const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = oracle_f32_to_f16(sqrtf(oracle_f16_to_f32(x[i])));
+}
+
+void oracle_sqrt_bf16(const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = oracle_f32_to_bf16(sqrtf(oracle_bf16_to_f32(x[i])));
+}
+
+void oracle_abs_16(const uint16_t *x, uint16_t *y, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) y[i] = (uint16_t)(x[i] & 0x7fffu);
+}
+
 /* Strided view copied to a contiguous row-major array, bit patterns
  * unchanged: out[r*cols + c] = in[r*stride_r + c*stride_c], strides in
  * elements and signed (a transposed view has stride_r = 1; x[::2] is the
@@ -375,4 +441,4 @@ uint64_t oracle_ulp_distance_f32(float a, float b)
     return (uint64_t)(d < 0 ? -d : d);
 }
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }

@@ -66,3 +66,25 @@ def f32_bits(x: float) -> int:
 
 def f16_bits(x: float) -> int:
     return int(np.array([x], np.float16).view(np.uint16)[0])
+
+
+def sqrt_rne(q: Fraction, fmt) -> float:
+    """The square root of the exact non-negative rational q, rounded once to
+    the format (roundTiesToEven).  With 4^k scaling chosen so that every
+    rounding boundary of the result is an integer multiple of 2^-k, the
+    integer root r = isqrt(floor(q * 4^k)) brackets sqrt(q) * 2^k in
+    [r, r + 1); an inexact root lies strictly inside, where (2r + 1) / 2
+    rounds the same way."""
+    if q < 0:
+        raise ValueError("negative")
+    if q == 0:
+        return 0.0
+    p = fmt[0]
+    k = p + 4 - _floor_log2(q) // 2
+    s = q * Fraction(4) ** k if k >= 0 else q / Fraction(4) ** (-k)
+    t = s.numerator // s.denominator
+    r = math.isqrt(t)
+    exact = s.denominator == 1 and r * r == t
+    root = Fraction(r) if exact else Fraction(2 * r + 1, 2)
+    root = root / Fraction(2) ** k if k >= 0 else root * Fraction(2) ** (-k)
+    return round_rne(root, fmt)

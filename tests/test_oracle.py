@@ -7,6 +7,7 @@ a wrong gather index) fails at least one of them.
 """
 import math
 import struct
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -634,3 +635,158 @@ def test_ulp_distance_closed_forms():
     assert u(np.finfo(np.float32).max, np.float32(np.inf)) == 1
     assert u(one, one) == 0
     assert u(one, np.float32(2.0)) == 1 << 23
+
+
+# --------------------------------------------------------------------------
+# Scalar-broadcast and unary maps
+# --------------------------------------------------------------------------
+
+MAP_ALPHAS = (np.float32(2.5), np.float32(-0.3), np.float32(1.0) / np.float32(3.0),
+              np.float32(1e-30), np.float32(-3e38))
+
+
+def test_scale_and_add_scalar_f32_vs_numpy():
+    g = synth.rng(91)
+    x = np.concatenate([synth.uniform_pm1(g, 1 << 16), _random_f32_bits(1 << 16, 92, False),
+                        F32_SPECIALS])
+    for alpha in MAP_ALPHAS + (np.float32(np.inf), np.float32(np.nan), np.float32(-0.0)):
+        with np.errstate(all="ignore"):
+            for got, ref in ((oracle.scale_f32(alpha, x), alpha * x),
+                             (oracle.add_scalar_f32(alpha, x), x + alpha)):
+                assert _nan_class_equal(got.view(np.uint32), ref.view(np.uint32),
+                                        np.isnan(got), np.isnan(ref)), alpha
+
+
+def test_scale_and_add_scalar_f32_exact_rational():
+    x = np.concatenate([_random_f32_bits(1200, 93), synth.uniform_pm1(synth.rng(94), 800)])
+    for alpha in MAP_ALPHAS:
+        fa = exact.f32_to_fraction(alpha)
+        for xi, r in zip(x, oracle.scale_f32(alpha, x)):
+            neg = (math.copysign(1, float(alpha)) * math.copysign(1, float(xi))) < 0
+            ref = exact.round_rne(fa * exact.f32_to_fraction(xi), exact.BINARY32,
+                                  zero_sign_negative=neg)
+            assert exact.f32_bits(ref) == exact.f32_bits(float(r)), (alpha, xi)
+        for xi, r in zip(x, oracle.add_scalar_f32(alpha, x)):
+            both_neg = math.copysign(1, float(alpha)) < 0 and math.copysign(1, float(xi)) < 0
+            ref = exact.round_rne(fa + exact.f32_to_fraction(xi), exact.BINARY32,
+                                  zero_sign_negative=both_neg)
+            assert exact.f32_bits(ref) == exact.f32_bits(float(r)), (alpha, xi)
+
+
+def test_scalar_map_closed_forms():
+    """scale by 1 is the identity and by -1 flips the sign bit; scale by 2 is
+    the exact doubling x + x; adding -0 is the identity (all non-NaN x)."""
+    x = np.concatenate([_random_f32_bits(1 << 16, 95, False), F32_SPECIALS])
+    x = x[~np.isnan(x)]
+    b = x.view(np.uint32)
+    assert np.array_equal(oracle.scale_f32(1.0, x).view(np.uint32), b)
+    assert np.array_equal(oracle.scale_f32(-1.0, x).view(np.uint32), b ^ np.uint32(0x80000000))
+    assert np.array_equal(oracle.scale_f32(2.0, x).view(np.uint32),
+                          oracle.add_f32(x, x).view(np.uint32))
+    assert np.array_equal(oracle.add_scalar_f32(-0.0, x).view(np.uint32), b)
+
+
+def test_sqrt_f32_vs_numpy_and_exact_root():
+    """numpy's float32 sqrt (correctly rounded, as IEEE 754 requires) on random
+    patterns of every class, and the exact rational root on positive samples
+    including subnormals."""
+    x = np.concatenate([_random_f32_bits(1 << 18, 96, False), F32_SPECIALS,
+                        np.abs(_random_f32_bits(1 << 12, 97))])
+    got = oracle.sqrt_f32(x)
+    with np.errstate(all="ignore"):
+        ref = np.sqrt(x)
+    assert _nan_class_equal(got.view(np.uint32), ref.view(np.uint32), np.isnan(got), np.isnan(ref))
+    pos = np.abs(_random_f32_bits(2000, 98))
+    pos = np.concatenate([pos, (np.arange(1, 200, dtype=np.uint32) * 40503).view(np.float32)])
+    for xi, r in zip(pos, oracle.sqrt_f32(pos)):
+        ref = exact.sqrt_rne(exact.f32_to_fraction(xi), exact.BINARY32)
+        assert exact.f32_bits(ref) == exact.f32_bits(float(r)), xi
+    neg0 = oracle.sqrt_f32(np.array([-0.0, np.inf, -1.0, -np.inf], np.float32))
+    assert neg0.view(np.uint32)[0] == 0x80000000 and neg0[1] == np.inf
+    assert np.isnan(neg0[2]) and np.isnan(neg0[3])
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_sqrt16_every_pattern_is_the_correctly_rounded_root(fmt):
+    """Every 16-bit pattern: a positive finite x gives the exact root rounded
+    once to the 16-bit format (so the binary32 detour never double-rounds
+    wrongly), -0 gives -0, +inf gives +inf, negatives and NaNs give NaN."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if fmt == "f16":
+        got, fmt16, to_bits = oracle.sqrt_f16(h), exact.BINARY16, exact.f16_bits
+        val = lambda b: float(np.uint16(b).view(np.float16))
+        exp_mask, man_mask = 0x7C00, 0x03FF
+    else:
+        got, fmt16 = oracle.sqrt_bf16(h), exact.BFLOAT16
+        to_bits = lambda v: exact.f32_bits(v) >> 16
+        val = _bf16_value
+        exp_mask, man_mask = 0x7F80, 0x007F
+    nan_out = ((got & exp_mask) == exp_mask) & ((got & man_mask) != 0)
+    for b, r, is_nan in zip(h, got, nan_out):
+        v = val(b)
+        if math.isnan(v) or v < 0:
+            assert is_nan, hex(b)
+        elif v == 0 or math.isinf(v):
+            assert r == b, hex(b)
+        else:
+            assert to_bits(exact.sqrt_rne(Fraction(v), fmt16)) == int(r), hex(b)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_scalar_maps16_vs_library_and_exact_rational(fmt):
+    """16-bit scale / add-scalar: against the library's own binary32 op and
+    RNE narrowing (numpy float16; torch bfloat16) on every pattern, and the
+    exact rational result rounded twice on a sample."""
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if fmt == "f16":
+        wide = h.view(np.float16).astype(np.float32)
+        narrow = lambda f: f.astype(np.float16).view(np.uint16)
+        nan = lambda u: ((u & 0x7C00) == 0x7C00) & ((u & 0x03FF) != 0)
+        fns = (oracle.scale_f16, oracle.add_scalar_f16)
+        fmt16, to_bits = exact.BINARY16, exact.f16_bits
+        val = lambda b: float(np.uint16(b).view(np.float16))
+    else:
+        wide = oracle.bf16_to_f32(h)
+        narrow = lambda f: torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy() \
+            .view(np.uint16)
+        nan = lambda u: ((u & 0x7F80) == 0x7F80) & ((u & 0x007F) != 0)
+        fns = (oracle.scale_bf16, oracle.add_scalar_bf16)
+        fmt16 = exact.BFLOAT16
+        to_bits = lambda v: exact.f32_bits(v) >> 16
+        val = _bf16_value
+    for alpha in MAP_ALPHAS:
+        with np.errstate(all="ignore"):
+            refs = (narrow(alpha * wide), narrow(wide + alpha))
+        for fn, ref in zip(fns, refs):
+            got = fn(alpha, h)
+            gn, rn = nan(got), nan(ref)
+            assert np.array_equal(gn, rn) and np.array_equal(got[~gn], ref[~rn]), (fmt, alpha)
+    g = np.random.Generator(np.random.PCG64(99 if fmt == "f16" else 100))
+    sample = g.integers(0, 1 << 16, size=600, dtype=np.uint16)
+    sample = sample[~nan(sample) & np.isfinite([val(b) for b in sample])]
+    for alpha in MAP_ALPHAS[:3]:
+        fa, sa = exact.f32_to_fraction(alpha), math.copysign(1, float(alpha))
+        for fn, is_mul in ((fns[0], True), (fns[1], False)):
+            for b, r in zip(sample, fn(alpha, sample)):
+                v = val(b)
+                sv = math.copysign(1, v)
+                q = fa * Fraction(v) if is_mul else Fraction(v) + fa
+                # sign of an exact zero: product of the signs / both addends negative
+                neg = sa * sv < 0 if is_mul else (sa < 0 and sv < 0)
+                v32 = exact.round_rne(q, exact.BINARY32, zero_sign_negative=neg)
+                ref = v32 if math.isinf(v32) else exact.round_rne(
+                    Fraction(v32), fmt16, zero_sign_negative=math.copysign(1, v32) < 0)
+                assert to_bits(ref) == int(r), (fmt, alpha, hex(b))
+
+
+def test_abs_vs_library_and_bit_identity():
+    x = np.concatenate([_random_f32_bits(1 << 16, 101, False), F32_SPECIALS])
+    got = oracle.abs_f32(x)
+    assert np.array_equal(got.view(np.uint32), np.abs(x).view(np.uint32))   # NaN payloads too
+    assert np.array_equal(got.view(np.uint32) | (x.view(np.uint32) & np.uint32(0x80000000)),
+                          x.view(np.uint32))
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    g16 = oracle.abs_f16(h)
+    assert np.array_equal(g16, np.abs(h.view(np.float16)).view(np.uint16))
+    gbf = oracle.abs_bf16(h)
+    assert np.array_equal(gbf | (h & np.uint16(0x8000)), h) and not np.any(gbf & 0x8000)
