@@ -52,12 +52,18 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                   "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
-                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8, "relu_inplace_f32": 8}
+                  "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8, "relu_inplace_f32": 8,
+                  # scalar-broadcast and unary maps: one input read, one output written
+                  **{f"{m}_{d}": 8 if d == "f32" else 4
+                     for m in ("scale", "add_scalar", "sqrt", "abs")
+                     for d in ("f32", "f16", "bf16")}}
 DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f32",
          "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32", "add_relu_f32": "f32",
          "saxpy_relu_f32": "f32", "bias_relu_f32": "f32", "saxpy_f16": "f16",
          "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16", "copy2d_f32": "f32",
-         "relu_inplace_f32": "f32"}
+         "relu_inplace_f32": "f32",
+         **{f"{m}_{d}": d for m in ("scale", "add_scalar", "sqrt", "abs")
+            for d in ("f32", "f16", "bf16")}}
 # The unfused sequence each fused chain replaces, timed beside it.
 UNFUSED = {"add_relu_f32": ("add_f32", "relu_f32"), "saxpy_relu_f32": ("saxpy_f32", "relu_f32")}
 MALL_BYTES = 256 * 2 ** 20
@@ -207,9 +213,35 @@ class Prepared:
                     with torch.cuda.stream(stream):
                         y.copy_(x)
                 self.torch_context = ("y.copy_(x)", t_copy)
+            elif w.op.rsplit("_", 1)[0] in ew.SCALAR_MAPS + ew.UNARY_MAPS:
+                self._map(w, torch, ew, x, y, stream)
             else:
                 self.launch = lambda: ew.ew_gather_f32(x, y, w.stride, stream=s)
             self.out, self.ptrs = y, (y, x, None)
+
+    def _map(self, w, torch, ew, x, y, stream):
+        """Launcher of a scalar-broadcast or unary map, and PyTorch's kernel for
+        the same map on the same buffers (viewed in the op's dtype)."""
+        s = stream.cuda_stream
+        kind, dt = w.op.rsplit("_", 1)
+        fn = getattr(ew, "ew_" + w.op)
+        if kind in ew.SCALAR_MAPS:
+            self.launch = lambda: fn(w.alpha, x, y, stream=s)
+        else:
+            self.launch = lambda: fn(x, y, stream=s)
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dt]
+        tx, ty = x.view(tdt), y.view(tdt)
+        label, tfn = {
+            "scale": ("torch.mul(x, alpha, out=y)", lambda: torch.mul(tx, w.alpha, out=ty)),
+            "add_scalar": ("torch.add(x, alpha, out=y)", lambda: torch.add(tx, w.alpha, out=ty)),
+            "sqrt": ("torch.sqrt(x, out=y)", lambda: torch.sqrt(tx, out=ty)),
+            "abs": ("torch.abs(x, out=y)", lambda: torch.abs(tx, out=ty)),
+        }[kind]
+
+        def t_map():
+            with torch.cuda.stream(stream):
+                tfn()
+        self.torch_context = (label, t_map)
 
     def plan(self, ew, cus):
         out, in0, in1 = self.ptrs
@@ -346,6 +378,8 @@ def cpu_baseline_leg(w, inp, got, target_s):
             return oracle.gather_f32(d["x"], w.stride)
         if w.op == "relu_inplace_f32":     # same result as the out-of-place ReLU
             return oracle.relu_f32(d["x"])
+        if w.op.rsplit("_", 1)[0] in ("scale", "add_scalar"):
+            return getattr(oracle, w.op)(w.alpha, d["x"])
         return getattr(oracle, w.op)(d["x"])
 
     def changed(d):

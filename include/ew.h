@@ -187,6 +187,49 @@ ew_status_t ew_relu_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t st
 ew_status_t ew_relu_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Scalar-broadcast and unary maps, in every format                          */
+/* ------------------------------------------------------------------------ */
+/* More instances of [EwOps] section 二's template (index, bounds check and
+ * store fixed; only the middle operation replaced): y[i] = f(x[i]), one
+ * input stream and one output stream, 8 bytes per fp32 element and 4 per
+ * 16-bit element.  fp32: f is one binary32 operation rounded to nearest-
+ * even.  _f16 / _bf16: x is widened exactly to binary32, f is applied in
+ * binary32 (with the binary32 alpha), and the result is rounded once to the
+ * 16-bit format, nearest-even -- the rule of the 16-bit add ([HyperAI]
+ * Stage 2).  Data are raw bit patterns for the 16-bit formats; pointers
+ * need element alignment.  y may equal x (in place); any other overlap is
+ * EW_ERR_OVERLAP.  NaN results are NaN (payload not part of the contract)
+ * except for abs, which moves bits. */
+
+/* Scalar broadcast, multiply: y[i] = alpha * x[i]. */
+ew_status_t ew_scale_f32(float alpha, const float *x, float *y, size_t n, hipStream_t stream);
+ew_status_t ew_scale_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                         hipStream_t stream);
+ew_status_t ew_scale_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                          hipStream_t stream);
+
+/* Scalar broadcast, add: y[i] = x[i] + alpha. */
+ew_status_t ew_add_scalar_f32(float alpha, const float *x, float *y, size_t n,
+                              hipStream_t stream);
+ew_status_t ew_add_scalar_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                              hipStream_t stream);
+ew_status_t ew_add_scalar_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                               hipStream_t stream);
+
+/* Unary: y[i] = sqrt(x[i]), correctly rounded in binary32 (sqrt(-0) = -0,
+ * negative inputs give NaN); the 16-bit forms round that binary32 root to
+ * the 16-bit format, which equals the correctly rounded 16-bit root. */
+ew_status_t ew_sqrt_f32(const float *x, float *y, size_t n, hipStream_t stream);
+ew_status_t ew_sqrt_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
+ew_status_t ew_sqrt_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
+
+/* Unary: y[i] = |x[i]|, the sign bit cleared and every other bit (NaN
+ * payloads included) unchanged. */
+ew_status_t ew_abs_f32(const float *x, float *y, size_t n, hipStream_t stream);
+ew_status_t ew_abs_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
+ew_status_t ew_abs_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Fused chains: one pass over memory instead of two                         */
 /* ------------------------------------------------------------------------ */
 /* An epilogue fused into the producing kernel saves a full pass through HBM
@@ -230,8 +273,10 @@ int ew_abi_version(void);
 /* Launch configuration, per operation name ("add_f32", "add_f16",
  * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
  * "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16",
- * "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32")
- * and size
+ * "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32",
+ * "scale_f32", "scale_f16", "scale_bf16", "add_scalar_f32", "add_scalar_f16",
+ * "add_scalar_bf16", "sqrt_f32", "sqrt_f16", "sqrt_bf16", "abs_f32",
+ * "abs_f16", "abs_bf16") and size
  * class: a row applies to every n >= min_n up to the next row's min_n.  The
  * grid is min(blocks_per_cu * CU count, number of tiles), where a tile is
  * block * unroll 16-byte vectors; each block walks tiles with a grid stride

@@ -20,7 +20,9 @@ __all__ = [
     "ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
     "ew_copy_f32", "ew_gather_f32", "ew_add_relu_f32", "ew_saxpy_relu_f32",
     "ew_bias_relu_f32", "ew_saxpy_f16", "ew_saxpy_bf16", "ew_relu_f16", "ew_relu_bf16",
-    "ew_copy2d_f32", "ew_status_string", "ew_last_hip_error",
+    "ew_copy2d_f32", "ew_scale_f32", "ew_scale_f16", "ew_scale_bf16", "ew_add_scalar_f32",
+    "ew_add_scalar_f16", "ew_add_scalar_bf16", "ew_sqrt_f32", "ew_sqrt_f16", "ew_sqrt_bf16",
+    "ew_abs_f32", "ew_abs_f16", "ew_abs_bf16", "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
     "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan", "ew_make_gather_plan",
 ]
@@ -31,7 +33,14 @@ LAUNCH_TABLE = os.path.join(_PKG, "launch_table.txt")
 
 OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
        "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16", "saxpy_bf16",
-       "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32")
+       "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32",
+       "scale_f32", "scale_f16", "scale_bf16", "add_scalar_f32", "add_scalar_f16",
+       "add_scalar_bf16", "sqrt_f32", "sqrt_f16", "sqrt_bf16", "abs_f32", "abs_f16", "abs_bf16")
+
+# The scalar-broadcast maps (alpha, x, y) and the unary maps (x, y).
+SCALAR_MAPS = ("scale", "add_scalar")
+UNARY_MAPS = ("sqrt", "abs")
+MAP_DTYPES = ("f32", "f16", "bf16")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -91,6 +100,10 @@ _c = {
     "ew_relu_bf16": _proto("ew_relu_bf16", _int, _vp, _vp, _sz, _vp),
     "ew_copy2d_f32": _proto("ew_copy2d_f32", _int, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
                             _sz, _sz, _vp),
+    **{f"ew_{m}_{d}": _proto(f"ew_{m}_{d}", _int, ctypes.c_float, _vp, _vp, _sz, _vp)
+       for m in SCALAR_MAPS for d in MAP_DTYPES},
+    **{f"ew_{m}_{d}": _proto(f"ew_{m}_{d}", _int, _vp, _vp, _sz, _vp)
+       for m in UNARY_MAPS for d in MAP_DTYPES},
     "ew_status_string": _proto("ew_status_string", ctypes.c_char_p, _int),
     "ew_last_hip_error": _proto("ew_last_hip_error", _int),
     "ew_abi_version": _proto("ew_abi_version", _int),
@@ -255,6 +268,74 @@ def ew_copy2d_f32(src, stride_r, stride_c, out, rows=None, cols=None, stream=Non
         rows, cols = out.shape
     _check(_c["ew_copy2d_f32"](_addr(src), int(stride_r), int(stride_c), _addr(out), int(rows),
                                int(cols), _stream(out, stream)), "ew_copy2d_f32")
+
+
+def _scalar_map(name, alpha, x, y, n, stream):
+    _check(_c[name](float(alpha), _addr(x), _addr(y), _numel(y, n), _stream(y, stream)), name)
+
+
+def _unary_map(name, x, y, n, stream):
+    _check(_c[name](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)), name)
+
+
+def ew_scale_f32(alpha, x, y, n=None, stream=None):
+    """y = alpha * x (binary32)."""
+    _scalar_map("ew_scale_f32", alpha, x, y, n, stream)
+
+
+def ew_scale_f16(alpha, x, y, n=None, stream=None):
+    """y = rne16(alpha * widen(x)) on binary16 data."""
+    _scalar_map("ew_scale_f16", alpha, x, y, n, stream)
+
+
+def ew_scale_bf16(alpha, x, y, n=None, stream=None):
+    """y = rnebf(alpha * widen(x)) on bfloat16 data."""
+    _scalar_map("ew_scale_bf16", alpha, x, y, n, stream)
+
+
+def ew_add_scalar_f32(alpha, x, y, n=None, stream=None):
+    """y = x + alpha (binary32)."""
+    _scalar_map("ew_add_scalar_f32", alpha, x, y, n, stream)
+
+
+def ew_add_scalar_f16(alpha, x, y, n=None, stream=None):
+    """y = rne16(widen(x) + alpha) on binary16 data."""
+    _scalar_map("ew_add_scalar_f16", alpha, x, y, n, stream)
+
+
+def ew_add_scalar_bf16(alpha, x, y, n=None, stream=None):
+    """y = rnebf(widen(x) + alpha) on bfloat16 data."""
+    _scalar_map("ew_add_scalar_bf16", alpha, x, y, n, stream)
+
+
+def ew_sqrt_f32(x, y, n=None, stream=None):
+    """y = sqrt(x), correctly rounded binary32."""
+    _unary_map("ew_sqrt_f32", x, y, n, stream)
+
+
+def ew_sqrt_f16(x, y, n=None, stream=None):
+    """y = rne16(sqrt(widen(x))) on binary16 data."""
+    _unary_map("ew_sqrt_f16", x, y, n, stream)
+
+
+def ew_sqrt_bf16(x, y, n=None, stream=None):
+    """y = rnebf(sqrt(widen(x))) on bfloat16 data."""
+    _unary_map("ew_sqrt_bf16", x, y, n, stream)
+
+
+def ew_abs_f32(x, y, n=None, stream=None):
+    """y = |x|: the sign bit cleared."""
+    _unary_map("ew_abs_f32", x, y, n, stream)
+
+
+def ew_abs_f16(x, y, n=None, stream=None):
+    """y = |x| on binary16 bit patterns."""
+    _unary_map("ew_abs_f16", x, y, n, stream)
+
+
+def ew_abs_bf16(x, y, n=None, stream=None):
+    """y = |x| on bfloat16 bit patterns."""
+    _unary_map("ew_abs_bf16", x, y, n, stream)
 
 
 def ew_status_string(status: int) -> str:

@@ -19,7 +19,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 
 struct OpInfo {
     const char *name;
@@ -46,6 +46,18 @@ constexpr OpInfo kOps[kOpCount] = {
     {"relu_bf16", 2, 1, true, 16},
     {"copy2d_f32", 4, 1, false, 16},
     {"relu_inplace_f32", 4, 1, true, 64},
+    {"scale_f32", 4, 1, true, 16},
+    {"scale_f16", 2, 1, true, 16},
+    {"scale_bf16", 2, 1, true, 16},
+    {"add_scalar_f32", 4, 1, true, 16},
+    {"add_scalar_f16", 2, 1, true, 16},
+    {"add_scalar_bf16", 2, 1, true, 16},
+    {"sqrt_f32", 4, 1, true, 16},
+    {"sqrt_f16", 2, 1, true, 16},
+    {"sqrt_bf16", 2, 1, true, 16},
+    {"abs_f32", 4, 1, true, 16},
+    {"abs_f16", 2, 1, true, 16},
+    {"abs_bf16", 2, 1, true, 16},
 };
 
 int op_from_name(const char *name)
@@ -107,6 +119,30 @@ constexpr DefaultRow kDefaults[] = {
     {kOpCopy2dF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpReluInplaceF32, {0, 1024, 1, 4}},
     {kOpReluInplaceF32, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpScaleF32, {0, 256, 8, 1}},
+    {kOpScaleF32, {size_t(1) << 22, 256, 1024, 1}},
+    {kOpScaleF16, {0, 1024, 8, 1}},
+    {kOpScaleF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpScaleBF16, {0, 1024, 8, 1}},
+    {kOpScaleBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddScalarF32, {0, 256, 8, 1}},
+    {kOpAddScalarF32, {size_t(1) << 22, 256, 1024, 1}},
+    {kOpAddScalarF16, {0, 1024, 8, 1}},
+    {kOpAddScalarF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddScalarBF16, {0, 1024, 8, 1}},
+    {kOpAddScalarBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSqrtF32, {0, 256, 8, 1}},
+    {kOpSqrtF32, {size_t(1) << 22, 256, 1024, 1}},
+    {kOpSqrtF16, {0, 1024, 8, 1}},
+    {kOpSqrtF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSqrtBF16, {0, 1024, 8, 1}},
+    {kOpSqrtBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAbsF32, {0, 256, 8, 1}},
+    {kOpAbsF32, {size_t(1) << 22, 256, 1024, 1}},
+    {kOpAbsF16, {0, 1024, 8, 1}},
+    {kOpAbsF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAbsBF16, {0, 1024, 8, 1}},
+    {kOpAbsBF16, {size_t(1) << 22, 128, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
@@ -521,6 +557,68 @@ ew_status_t ew_relu_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 ew_status_t ew_relu_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 {
     return run_stream(kOpReluBF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_scale_f32(float alpha, const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpScaleF32, y, x, nullptr, n, alpha, s);
+}
+
+ew_status_t ew_scale_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpScaleF16, y, x, nullptr, n, alpha, s);
+}
+
+ew_status_t ew_scale_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpScaleBF16, y, x, nullptr, n, alpha, s);
+}
+
+ew_status_t ew_add_scalar_f32(float alpha, const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAddScalarF32, y, x, nullptr, n, alpha, s);
+}
+
+ew_status_t ew_add_scalar_f16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                              hipStream_t s)
+{
+    return run_stream(kOpAddScalarF16, y, x, nullptr, n, alpha, s);
+}
+
+ew_status_t ew_add_scalar_bf16(float alpha, const uint16_t *x, uint16_t *y, size_t n,
+                               hipStream_t s)
+{
+    return run_stream(kOpAddScalarBF16, y, x, nullptr, n, alpha, s);
+}
+
+ew_status_t ew_sqrt_f32(const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSqrtF32, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_sqrt_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSqrtF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_sqrt_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpSqrtBF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_abs_f32(const float *x, float *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAbsF32, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_abs_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAbsF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_abs_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
+{
+    return run_stream(kOpAbsBF16, y, x, nullptr, n, 0.0f, s);
 }
 
 ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)

@@ -25,6 +25,18 @@ enum OpId : int {
     kOpReluBF16,
     kOpCopy2dF32,
     kOpReluInplaceF32,
+    kOpScaleF32,
+    kOpScaleF16,
+    kOpScaleBF16,
+    kOpAddScalarF32,
+    kOpAddScalarF16,
+    kOpAddScalarBF16,
+    kOpSqrtF32,
+    kOpSqrtF16,
+    kOpSqrtBF16,
+    kOpAbsF32,
+    kOpAbsF16,
+    kOpAbsBF16,
     kOpCount
 };
 
@@ -39,7 +51,7 @@ struct StreamArgs {
     uint64_t vectors;
     uint64_t tail;
     uint64_t tiles;      // ceil(vectors / (blockDim * unroll))
-    float alpha;         // saxpy only
+    float alpha;         // saxpy, scale and add-scalar only
 };
 
 // The gather additionally walks its input index (stride * i) mod n

@@ -308,6 +308,91 @@ struct OpRelu16 {
 using OpReluF16 = OpRelu16<_Float16>;
 using OpReluBF16 = OpRelu16<__bf16>;
 
+// Scalar-broadcast and unary maps y = f(x): the template's middle operation
+// replaced and nothing else ([EwOps] section 二, template code).  Each f is
+// one IEEE binary32 operation rounded to nearest-even: alpha * x, x + alpha,
+// or the square root (HIP's sqrtf is correctly rounded unless fast-math
+// relaxes it; this file is never built so).
+struct FnScale {
+    __device__ static float f(float v, float alpha) { return alpha * v; }
+};
+struct FnAddScalar {
+    __device__ static float f(float v, float alpha) { return v + alpha; }
+};
+struct FnSqrt {
+    __device__ static float f(float v, float) { return __builtin_sqrtf(v); }
+};
+
+template <class Fn>
+struct OpMapF32 {
+    using Elem = uint32_t;
+    static constexpr int kInputs = 1;
+    __device__ static u32x4 vec(u32x4 x, u32x4, float alpha)
+    {
+        f32x4 xf = __builtin_bit_cast(f32x4, x), r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = Fn::f(xf[j], alpha);
+        return __builtin_bit_cast(u32x4, r);
+    }
+    __device__ static Elem one(Elem x, Elem, float alpha)
+    {
+        return __builtin_bit_cast(Elem, Fn::f(__builtin_bit_cast(float, x), alpha));
+    }
+};
+using OpScaleF32 = OpMapF32<FnScale>;
+using OpAddScalarF32 = OpMapF32<FnAddScalar>;
+using OpSqrtF32 = OpMapF32<FnSqrt>;
+
+// The same maps on 16-bit data: widen x exactly, apply f in binary32, round
+// the result once to the 16-bit format (RNE).  The binary32 result is pinned
+// in a register before the narrowing, as in OpSaxpy16, so that the compiler
+// neither fuses the multiply or add with the narrowing into one mixed-
+// precision instruction nor narrows a square root of a widened value into a
+// native 16-bit one: either would round straight from the exact value.
+template <typename H, class Fn>
+struct OpMap16 {
+    using Elem = uint16_t;
+    static constexpr int kInputs = 1;
+    typedef H h8 __attribute__((ext_vector_type(8)));
+    __device__ static float f32(float v, float alpha)
+    {
+        float r = Fn::f(v, alpha);
+        asm("" : "+v"(r));
+        return r;
+    }
+    __device__ static u32x4 vec(u32x4 x, u32x4, float alpha)
+    {
+        const f32x8 xf = __builtin_convertvector(__builtin_bit_cast(h8, x), f32x8);
+        f32x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = f32(xf[j], alpha);
+        return __builtin_bit_cast(u32x4, __builtin_convertvector(r, h8));
+    }
+    __device__ static Elem one(Elem x, Elem, float alpha)
+    {
+        return __builtin_bit_cast(Elem, (H)f32((float)__builtin_bit_cast(H, x), alpha));
+    }
+};
+using OpScaleF16 = OpMap16<_Float16, FnScale>;
+using OpScaleBF16 = OpMap16<__bf16, FnScale>;
+using OpAddScalarF16 = OpMap16<_Float16, FnAddScalar>;
+using OpAddScalarBF16 = OpMap16<__bf16, FnAddScalar>;
+using OpSqrtF16 = OpMap16<_Float16, FnSqrt>;
+using OpSqrtBF16 = OpMap16<__bf16, FnSqrt>;
+
+// |x|: the sign bit cleared, every other bit kept (IEEE abs is a sign-bit
+// operation, so NaN payloads pass unchanged).  E is the element's width.
+template <typename E>
+struct OpAbs {
+    using Elem = E;
+    static constexpr int kInputs = 1;
+    static constexpr uint32_t kMask = sizeof(E) == 4 ? 0x7fffffffu : 0x7fff7fffu;
+    __device__ static u32x4 vec(u32x4 x, u32x4, float) { return x & kMask; }
+    __device__ static Elem one(Elem x, Elem, float) { return (Elem)(x & (Elem)kMask); }
+};
+using OpAbsF32 = OpAbs<uint32_t>;
+using OpAbs16 = OpAbs<uint16_t>;
+
 // out = in, bits unchanged.
 struct OpCopyF32 {
     using Elem = uint32_t;
@@ -994,6 +1079,19 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
     case kOpSaxpyBF16: return launch_op<OpSaxpyBF16>(args, co0, co1, launch, stream);
     case kOpReluF16: return launch_op<OpReluF16>(args, co0, co1, launch, stream);
     case kOpReluBF16: return launch_op<OpReluBF16>(args, co0, co1, launch, stream);
+    case kOpScaleF32: return launch_op<OpScaleF32>(args, co0, co1, launch, stream);
+    case kOpScaleF16: return launch_op<OpScaleF16>(args, co0, co1, launch, stream);
+    case kOpScaleBF16: return launch_op<OpScaleBF16>(args, co0, co1, launch, stream);
+    case kOpAddScalarF32: return launch_op<OpAddScalarF32>(args, co0, co1, launch, stream);
+    case kOpAddScalarF16: return launch_op<OpAddScalarF16>(args, co0, co1, launch, stream);
+    case kOpAddScalarBF16: return launch_op<OpAddScalarBF16>(args, co0, co1, launch, stream);
+    case kOpSqrtF32: return launch_op<OpSqrtF32>(args, co0, co1, launch, stream);
+    case kOpSqrtF16: return launch_op<OpSqrtF16>(args, co0, co1, launch, stream);
+    case kOpSqrtBF16: return launch_op<OpSqrtBF16>(args, co0, co1, launch, stream);
+    case kOpAbsF32: return launch_op<OpAbsF32>(args, co0, co1, launch, stream);
+    // binary16 and bfloat16 share the sign bit's position: one kernel
+    case kOpAbsF16:
+    case kOpAbsBF16: return launch_op<OpAbs16>(args, co0, co1, launch, stream);
     default: return hipErrorInvalidValue;
     }
 }

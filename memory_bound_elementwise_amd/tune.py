@@ -38,7 +38,9 @@ BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
                   "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8,
                   # in place on normal(0, 1) data: every 64-byte span changes
-                  "relu_inplace_f32": 8}
+                  "relu_inplace_f32": 8,
+                  **{f"{m}_{d}": 8 if d == "f32" else 4
+                     for m in ew.SCALAR_MAPS + ew.UNARY_MAPS for d in ew.MAP_DTYPES}}
 BIAS_COLS = 4096
 # copy2d is tuned on a submatrix view: 16384 rows of 16380 columns out of
 # 16384-wide rows (the row-contiguous path, which uses the table).
@@ -62,9 +64,12 @@ def _launcher(op, n, bufs, stream, off_a=0):
     if op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
         fn = getattr(ew, "ew_" + op)
         return lambda: fn(0.5, pa, c.data_ptr(), n=n, stream=s)
-    if op in ("relu_f16", "relu_bf16"):
+    if op in ("relu_f16", "relu_bf16") or op.rsplit("_", 1)[0] in ew.UNARY_MAPS:
         fn = getattr(ew, "ew_" + op)
         return lambda: fn(pa, c.data_ptr(), n=n, stream=s)
+    if op.rsplit("_", 1)[0] in ew.SCALAR_MAPS:
+        fn = getattr(ew, "ew_" + op)
+        return lambda: fn(2.5, pa, c.data_ptr(), n=n, stream=s)
     if op == "copy2d_f32":
         return lambda: ew.ew_copy2d_f32(pa + 4, C2D_PITCH, 1, c.data_ptr(), C2D_ROWS, C2D_COLS,
                                         stream=s)
@@ -218,12 +223,12 @@ def write_table(best, path, merge_from=None):
         if op in best:
             for cls, min_n in (("small", 0), ("large", LARGE_MIN_N)):
                 block, bpc, unroll, gbs = best[op][cls]
-                lines.append(f"{op:<11s} {min_n:<8d} {block:<5d} {bpc:<5d} {unroll:<2d} "
+                lines.append(f"{op:<15s} {min_n:<8d} {block:<5d} {bpc:<5d} {unroll:<2d} "
                              f"# {gbs} GB/s")
         else:
             for (min_n, block, bpc, unroll, comment) in old.get(op, []):
                 tail = f" # {comment}" if comment else ""
-                lines.append(f"{op:<11s} {min_n:<8d} {block:<5d} {bpc:<5d} {unroll:<2d}{tail}")
+                lines.append(f"{op:<15s} {min_n:<8d} {block:<5d} {bpc:<5d} {unroll:<2d}{tail}")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
 

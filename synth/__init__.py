@@ -65,12 +65,12 @@ class Workload:
     aligned allocation the pointer handed to the library starts.
     """
     name: str
-    op: str               # add_f32 | add_f16 | add_bf16 | saxpy_f32 | relu_f32 | copy_f32 | gather_f32
+    op: str               # a libew operation name (add_f32, saxpy_f32, sqrt_f16, ...)
     n: int
     seed: int
     dist: str             # "uniform" | "normal" | "absnormal"
     offsets: dict = field(default_factory=dict)
-    alpha: float = 0.0    # saxpy only
+    alpha: float = 0.0    # saxpy and the scalar-broadcast maps
     stride: int = 0       # gather only
     cols: int = 0         # bias_relu / copy2d: row length (n = rows * cols)
     view: tuple = ()      # copy2d: (stride_r, stride_c, base elements, offset)
@@ -169,6 +169,22 @@ WORKLOADS = {
         "relu_inplace_f32_2e28_nonneg", "relu_inplace_f32", 1 << 28, 118, "absnormal",
         description="fp32 ReLU in place, n=2^28, x = |normal(0,1)| (every element already "
                     ">= 0: nothing to store)"),
+    "scale_f32_2e28": _w(
+        "scale_f32_2e28", "scale_f32", 1 << 28, 121, "normal", alpha=2.5,
+        description="fp32 scalar-broadcast multiply y = 2.5*x, n=2^28, x normal(0,1)"),
+    "add_scalar_bf16_2e28": _w(
+        "add_scalar_bf16_2e28", "add_scalar_bf16", 1 << 28, 122, "normal", alpha=2.5,
+        description="bf16 scalar-broadcast add y = x + 2.5 (fp32 add, RNE to bf16), n=2^28, "
+                    "x normal(0,1) cast RNE"),
+    "sqrt_f32_2e28": _w(
+        "sqrt_f32_2e28", "sqrt_f32", 1 << 28, 123, "absnormal",
+        description="fp32 square root y = sqrt(x), correctly rounded, n=2^28, x = |normal(0,1)|"),
+    "sqrt_f16_2e28": _w(
+        "sqrt_f16_2e28", "sqrt_f16", 1 << 28, 124, "absnormal",
+        description="fp16 square root y = rne16(sqrt(x)), n=2^28, x = |normal(0,1)| cast RNE"),
+    "abs_f16_2e28": _w(
+        "abs_f16_2e28", "abs_f16", 1 << 28, 125, "normal",
+        description="fp16 y = |x| (sign bit cleared), n=2^28, x normal(0,1) cast RNE"),
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),
@@ -182,6 +198,8 @@ OP_INPUTS = {
     "bias_relu_f32": ("x", "bias"), "saxpy_f16": ("x", "y"), "saxpy_bf16": ("x", "y"),
     "relu_f16": ("x",), "relu_bf16": ("x",), "copy2d_f32": ("base",),
     "relu_inplace_f32": ("x",),
+    **{f"{m}_{d}": ("x",) for m in ("scale", "add_scalar", "sqrt", "abs")
+       for d in ("f32", "f16", "bf16")},
 }
 OP_DTYPE = {
     "add_f32": np.float32, "add_f16": np.uint16, "add_bf16": np.uint16,
@@ -190,9 +208,13 @@ OP_DTYPE = {
     "bias_relu_f32": np.float32, "saxpy_f16": np.uint16, "saxpy_bf16": np.uint16,
     "relu_f16": np.uint16, "relu_bf16": np.uint16, "copy2d_f32": np.float32,
     "relu_inplace_f32": np.float32,
+    **{f"{m}_{d}": np.float32 if d == "f32" else np.uint16
+       for m in ("scale", "add_scalar", "sqrt", "abs") for d in ("f32", "f16", "bf16")},
 }
-F16_OPS = ("add_f16", "saxpy_f16", "relu_f16")
-BF16_OPS = ("add_bf16", "saxpy_bf16", "relu_bf16")
+F16_OPS = ("add_f16", "saxpy_f16", "relu_f16", "scale_f16", "add_scalar_f16", "sqrt_f16",
+           "abs_f16")
+BF16_OPS = ("add_bf16", "saxpy_bf16", "relu_bf16", "scale_bf16", "add_scalar_bf16",
+            "sqrt_bf16", "abs_bf16")
 
 
 def absnormal(g: np.random.Generator, n: int) -> np.ndarray:

@@ -7,7 +7,9 @@ DEV = torch.device("cuda:0")
 ELEM = {"add_f32": 4, "add_f16": 2, "add_bf16": 2, "saxpy_f32": 4, "relu_f32": 4,
         "copy_f32": 4, "gather_f32": 4, "add_relu_f32": 4, "saxpy_relu_f32": 4,
         "bias_relu_f32": 4, "saxpy_f16": 2, "saxpy_bf16": 2, "relu_f16": 2, "relu_bf16": 2,
-        "copy2d_f32": 4, "relu_inplace_f32": 4}
+        "copy2d_f32": 4, "relu_inplace_f32": 4,
+        **{f"{m}_{d}": 4 if d == "f32" else 2
+           for m in ("scale", "add_scalar", "sqrt", "abs") for d in ("f32", "f16", "bf16")}}
 NP_DTYPE = {4: np.float32, 2: np.uint16}
 TORCH_DTYPE = {4: torch.float32, 2: torch.int16}
 
@@ -48,20 +50,21 @@ def bf16_nan(bits):
 def mismatches(op: str, got: np.ndarray, ref: np.ndarray) -> np.ndarray:
     """Indices where got differs from ref: bitwise, except that for the
     arithmetic ops (fused ones included) a NaN matches any NaN (payloads are
-    not part of the contract).  Copy, gather and ReLU compare bitwise
+    not part of the contract).  Copy, gather, ReLU and abs compare bitwise
     throughout."""
-    if op in ("copy_f32", "gather_f32", "relu_f32", "copy2d_f32", "relu_inplace_f32"):
+    if op in ("copy_f32", "gather_f32", "relu_f32", "copy2d_f32", "relu_inplace_f32",
+              "abs_f32"):
         g, r = got.view(np.uint32), ref.view(np.uint32)
         return np.nonzero(g != r)[0]
-    if op in ("relu_f16", "relu_bf16"):
+    if op in ("relu_f16", "relu_bf16", "abs_f16", "abs_bf16"):
         return np.nonzero(got.view(np.uint16) != ref.view(np.uint16))[0]
-    if op in ("add_f32", "saxpy_f32", "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32"):
+    if op.endswith("_f32"):
         g, r = got.view(np.uint32), ref.view(np.uint32)
         gn = (g & 0x7FFFFFFF) > 0x7F800000
         rn = (r & 0x7FFFFFFF) > 0x7F800000
     else:
         g, r = got.view(np.uint16), ref.view(np.uint16)
-        isnan = f16_nan if op in ("add_f16", "saxpy_f16") else bf16_nan
+        isnan = f16_nan if op.endswith("_f16") else bf16_nan
         gn, rn = isnan(g), isnan(r)
     bad = ((g != r) & ~(gn & rn)) | (gn != rn)
     return np.nonzero(bad)[0]

@@ -4,10 +4,12 @@
 * ew_saxpy_f16 / ew_saxpy_bf16 on all 2^32 (x, y) pairs, for alpha = 2.5
   (the SAXPY workload's) and alpha = fl32(1/3) (inexact, so the binary32 fma
   rounds on almost every pair before the 16-bit rounding);
-* ew_relu_f16 / ew_relu_bf16 on all 65,536 patterns.
+* ew_relu_f16 / ew_relu_bf16 on all 65,536 patterns;
+* the scalar-broadcast and unary maps (scale, add-scalar with several
+  alphas; sqrt; abs) on all 65,536 patterns of each 16-bit format.
 
 Bitwise, except that a NaN matches any NaN for the arithmetic operations
-(ReLU passes NaNs through bitwise).  The pairs go through in four launches
+(ReLU and abs pass NaNs through bitwise).  The pairs go through in four launches
 of 2^30 elements (the first operand = the high half-word of the pair index,
 the second = the low one), with the first operand misaligned, so the body
 runs the element-aligned load path.  The oracle runs on the host, split over
@@ -107,3 +109,33 @@ def test_relu_on_every_16bit_pattern(op):
     got = download(yd, 2)
     ref = getattr(oracle, op)(x)
     assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+
+
+MAP_ALPHAS = (2.5, THIRD, -1.0e-5, 65504.0, float(np.float32(3.0e38)))
+
+
+@pytest.mark.parametrize("op", ["scale_f16", "scale_bf16", "add_scalar_f16", "add_scalar_bf16",
+                                "sqrt_f16", "sqrt_bf16", "abs_f16", "abs_bf16"])
+def test_maps_on_every_16bit_pattern(op):
+    """Every pattern, misaligned by one element; the scalar maps under
+    several alphas (inexact, tiny, at the binary16 maximum, near the
+    binary32 one)."""
+    x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    scalar = op.rsplit("_", 1)[0] in ew.SCALAR_MAPS
+    exp, man = (0x7C00, 0x03FF) if op.endswith("_f16") else (0x7F80, 0x007F)
+    for alpha in MAP_ALPHAS if scalar else (None,):
+        xd, kx = upload(x, 1)
+        yd, ky = upload(np.zeros(x.size, np.uint16), 0)
+        fn = getattr(ew, "ew_" + op)
+        fn(alpha, xd, yd) if scalar else fn(xd, yd)
+        torch.cuda.synchronize()
+        got = download(yd, 2)
+        ref = getattr(oracle, op)(alpha, x) if scalar else getattr(oracle, op)(x)
+        if op.startswith("abs"):
+            assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+            continue
+        gn = ((got & exp) == exp) & ((got & man) != 0)
+        rn = ((ref & exp) == exp) & ((ref & man) != 0)
+        bad = np.flatnonzero((gn != rn) | (~gn & (got != ref)))
+        assert bad.size == 0, (op, alpha, [hex(v) for v in x[bad[:5]]],
+                               [hex(v) for v in got[bad[:5]]], [hex(v) for v in ref[bad[:5]]])

@@ -9,7 +9,10 @@
 * ew_saxpy_f32 (alpha = 2.5, the SAXPY workload's) with every pattern once
   as x and once as y, paired the same way, against the oracle's fmaf:
   bitwise except that a NaN matches any NaN (the 1-ulp allowance is not
-  used).
+  used);
+* ew_sqrt_f32 on all 2^32 patterns against the correctly rounded root, and
+  ew_scale_f32 / ew_add_scalar_f32 with alpha = fl32(1/3) on all 2^32
+  patterns: bitwise except that a NaN matches any NaN.
 
 Four launches of 2^30 elements each, the input misaligned by one element.
 The oracle runs on the host, split over the process's cores (at most 16).
@@ -107,3 +110,40 @@ def test_saxpy_with_every_f32_pattern_as_x_and_as_y():
         torch.cuda.synchronize()
         return download(yd, 4).view(np.uint32)
     _both_operands(run, lambda x, y: oracle.saxpy_f32(2.5, x, y))
+
+
+THIRD = float(np.float32(1.0) / np.float32(3.0))
+
+
+def _every_pattern_map(launch, ref_fn):
+    """launch(x_view, y_view) runs the HIP map; ref_fn(x) is the oracle's."""
+    for k in range((1 << 32) // CHUNK):
+        bits = _chunk(k)
+        x = bits.view(np.float32)
+        xd, kx = upload(x, 1)
+        yd, ky = upload(np.zeros(CHUNK, np.float32), 0)
+        launch(xd, yd)
+        torch.cuda.synchronize()
+        got = download(yd, 4).view(np.uint32)
+        del xd, kx, yd, ky
+        torch.cuda.empty_cache()
+        ref = _parallel(ref_fn, x).view(np.uint32)
+        bad = np.flatnonzero(got != ref)
+        if bad.size:
+            g, r = got[bad], ref[bad]
+            both_nan = ((g & 0x7FFFFFFF) > 0x7F800000) & ((r & 0x7FFFFFFF) > 0x7F800000)
+            wrong = bad[~both_nan]
+            assert wrong.size == 0, (f"{wrong.size} mismatches, first x={bits[wrong[0]]:#010x}: "
+                                     f"got {got[wrong[0]]:#010x}, want {ref[wrong[0]]:#010x}")
+        del bits, x, got, ref
+
+
+def test_sqrt_on_every_f32_pattern():
+    _every_pattern_map(ew.ew_sqrt_f32, oracle.sqrt_f32)
+
+
+def test_scale_and_add_scalar_on_every_f32_pattern():
+    _every_pattern_map(lambda x, y: ew.ew_scale_f32(THIRD, x, y),
+                       lambda x: oracle.scale_f32(THIRD, x))
+    _every_pattern_map(lambda x, y: ew.ew_add_scalar_f32(THIRD, x, y),
+                       lambda x: oracle.add_scalar_f32(THIRD, x))

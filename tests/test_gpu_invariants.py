@@ -14,7 +14,9 @@ in a kernel shows here even if the oracle shared it.
   1 or n + 1 is the copy, with stride 2 and even n its halves are equal, and
   with a stride coprime with n it is a permutation;
 * a transposed view of a transposed view is the identity, and a view with
-  contiguous strides is the copy.
+  contiguous strides is the copy;
+* the scalar and unary maps: scale by 1, -1 and 2, adding -0, abs as a
+  sign-bit clear, the roots of exact squares.
 
 Sizes span several tiles with a ragged tail; pointers are misaligned.
 """
@@ -192,3 +194,30 @@ def test_double_transpose_is_the_identity_and_contiguous_strides_copy():
     assert np.all(_bits(download(c, 4)) == _bits(x))
     tt = download(t, 4).reshape(cols, rows)
     assert np.all(_bits(tt) == _bits(x.reshape(rows, cols).T))
+
+
+def test_scalar_and_unary_map_closed_forms():
+    """scale by 1 is the identity, by -1 flips the sign bit and by 2 equals
+    the add of x and x; adding -0 is the identity; abs clears exactly the sign
+    bit; the root of an exact square k^2 (k < 2^12) is k, and of 4^j is 2^j."""
+    x = _pool_f32(N, 413)
+    x = x[~_nan32(x)]
+    n = x.size
+    z = np.zeros(n, np.float32)
+    _, s1 = _run(lambda xv, yv: ew.ew_scale_f32(1.0, xv, yv), x, z)
+    assert np.all(_bits(s1) == _bits(x))
+    _, sm = _run(lambda xv, yv: ew.ew_scale_f32(-1.0, xv, yv), x, z)
+    assert np.all(_bits(sm) == (_bits(x) ^ np.uint32(0x80000000)))
+    _, s2 = _run(lambda xv, yv: ew.ew_scale_f32(2.0, xv, yv), x, z)
+    _, _, xx = _run(ew.ew_add_f32, x, x, np.zeros(n, np.float32))
+    assert np.all(_bits(s2) == _bits(xx))
+    _, a0 = _run(lambda xv, yv: ew.ew_add_scalar_f32(-0.0, xv, yv), x, z)
+    assert np.all(_bits(a0) == _bits(x))
+    _, ab = _run(ew.ew_abs_f32, x, z)
+    assert np.all((_bits(ab) | (_bits(x) & np.uint32(0x80000000))) == _bits(x))
+    assert not np.any(_bits(ab) & np.uint32(0x80000000))
+    k = np.arange(1, 4096, dtype=np.float32)
+    sq = np.concatenate([k * k, np.ldexp(np.float32(1), np.arange(-74, 64, 2)).astype(np.float32)])
+    _, r = _run(ew.ew_sqrt_f32, sq, np.zeros(sq.size, np.float32))
+    want = np.concatenate([k, np.ldexp(np.float32(1), np.arange(-37, 32)).astype(np.float32)])
+    assert np.all(_bits(r) == _bits(want))

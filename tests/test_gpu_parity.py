@@ -101,7 +101,15 @@ def _pool(op, length, seed):
     return _u16_pool(length, seed) if ELEM[op] == 2 else _f32_pool(length, seed)
 
 
+SCALAR_MAPS = tuple(f"{m}_{d}" for m in ew.SCALAR_MAPS for d in ew.MAP_DTYPES)
+UNARY_MAPS = tuple(f"{m}_{d}" for m in ew.UNARY_MAPS for d in ew.MAP_DTYPES)
+
+
 def _oracle(op, ins, n, alpha=2.5, stride=2):
+    if op in SCALAR_MAPS:
+        return getattr(oracle, op)(alpha, ins[0])
+    if op in UNARY_MAPS:
+        return getattr(oracle, op)(ins[0])
     if op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         return getattr(oracle, op)(ins[0], ins[1])
     if op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
@@ -117,7 +125,11 @@ def _oracle(op, ins, n, alpha=2.5, stride=2):
 
 def _call(op, out_ptr, in_ptrs, n, alpha=2.5, stride=2):
     s = torch.cuda.current_stream().cuda_stream
-    if op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
+    if op in SCALAR_MAPS:
+        getattr(ew, "ew_" + op)(alpha, in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op in UNARY_MAPS:
+        getattr(ew, "ew_" + op)(in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         getattr(ew, "ew_" + op)(in_ptrs[0], in_ptrs[1], out_ptr, n=n, stream=s)
     elif op in ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16"):
         getattr(ew, "ew_" + op)(alpha, in_ptrs[0], out_ptr, n=n, stream=s)
@@ -131,7 +143,7 @@ def _call(op, out_ptr, in_ptrs, n, alpha=2.5, stride=2):
         ew.ew_gather_f32(in_ptrs[0], out_ptr, stride, n=n, stream=s)
 
 
-def _run_cases(op, cases, seed):
+def _run_cases(op, cases, seed, alpha=2.5):
     """cases: list of (n, off_out, [off_in...], stride).  All outputs live in
     one sentinel-filled arena; returns a list of failure descriptions."""
     es = ELEM[op]
@@ -168,7 +180,7 @@ def _run_cases(op, cases, seed):
         for k in range(n_in):
             assert offs_in[k] + n <= pool_len
             in_ptrs.append(dev_pools[k].data_ptr() + offs_in[k] * es)
-        _call(op, base + ob, in_ptrs, n, stride=stride)
+        _call(op, base + ob, in_ptrs, n, alpha=alpha, stride=stride)
     torch.cuda.synchronize()
     res = arena.cpu().numpy()
 
@@ -178,7 +190,7 @@ def _run_cases(op, cases, seed):
         written[ob:ob + n * es] = True
         got = res[ob:ob + n * es].view(dt)
         ins = [pools[k][offs_in[k]:offs_in[k] + n] for k in range(n_in)]
-        ref = _oracle(op, ins, n, stride=stride)
+        ref = _oracle(op, ins, n, alpha=alpha, stride=stride)
         bad = mismatches(op, got, ref)
         if bad.size:
             failures.append(f"{op} n={n} off_out={off_out} offs_in={offs_in} stride={stride}: "
@@ -191,7 +203,8 @@ def _run_cases(op, cases, seed):
 
 
 IN_PLACE = ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16")
-ONE_INPUT = ("relu_f32", "copy_f32", "gather_f32", "relu_f16", "relu_bf16", "relu_inplace_f32")
+ONE_INPUT = ("relu_f32", "copy_f32", "gather_f32", "relu_f16", "relu_bf16",
+             "relu_inplace_f32") + SCALAR_MAPS + UNARY_MAPS
 TWO_INPUT = ("add_f32", "add_f16", "add_bf16", "add_relu_f32") + IN_PLACE
 
 
@@ -227,7 +240,22 @@ def _offset_cases(op):
 
 ALL_STREAM_OPS = ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32",
                   "gather_f32", "add_relu_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16",
-                  "relu_f16", "relu_bf16", "relu_inplace_f32"]
+                  "relu_f16", "relu_bf16", "relu_inplace_f32"] + list(SCALAR_MAPS + UNARY_MAPS)
+
+
+@pytest.mark.parametrize("alpha", [np.float32(1.0) / np.float32(3.0), -7.5e-39, np.inf, np.nan,
+                                   -0.0, 3e38])
+def test_scalar_maps_other_alphas(alpha):
+    """The scalar-broadcast maps with an inexact alpha, a subnormal one, inf,
+    NaN, -0 and one that overflows most products, over ragged sizes and
+    offsets (the brute-force test covers alpha = 2.5)."""
+    print(f"[parity] scalar maps alpha={alpha}", flush=True)
+    for op in SCALAR_MAPS:
+        vec = 16 // ELEM[op]
+        cases = [(n, oo, [(oo + k) % vec], 0) for n in (1, 7, 33, 1000, 4099, 65537)
+                 for k, oo in enumerate(range(vec))]
+        failures = _run_cases(op, cases, seed=305, alpha=float(np.float32(alpha)))
+        assert not failures, failures[:5]
 
 
 @pytest.mark.parametrize("op", ALL_STREAM_OPS)
@@ -536,6 +564,15 @@ def test_exact_aliasing_in_place():
     ew.ew_saxpy_f32(2.5, ty, ty, stream=s)
     torch.cuda.synchronize()
     assert mismatches("saxpy_f32", download(ty, 4), oracle.saxpy_f32(2.5, y, y)).size == 0
+    # the maps in place, y == x
+    for op, pool, es in (("sqrt_f32", x, 4), ("scale_bf16", a16, 2), ("add_scalar_f16", b16, 2),
+                         ("abs_f32", x, 4)):
+        tm, _km = upload(pool, 1)
+        args = (2.5, tm, tm) if op in SCALAR_MAPS else (tm, tm)
+        getattr(ew, "ew_" + op)(*args, stream=s)
+        torch.cuda.synchronize()
+        ref = _oracle(op, [pool], n)
+        assert mismatches(op, download(tm, es), ref).size == 0, op
     # copy onto itself leaves the data unchanged
     tz, _kz = upload(x, 0)
     ew.ew_copy_f32(tz, tz, stream=s)

@@ -13,9 +13,13 @@ silently; these checks fail the build's tests if it does:
 * no round-toward-zero conversions (v_cvt_pkrtz_*);
 * the ReLU kernels select with a compare (no v_max_*, whose NaN rule returns
   the other operand);
+* the square-root kernels take a refined binary32 root (the hardware
+  estimate followed by fma residual corrections), never a native 16-bit
+  root, and the scalar maps multiply / add in binary32;
 * the streaming kernels move 16 bytes per lane (global_load_dwordx4 /
   global_store_dwordx4) and store non-temporally; the single-input ones
-  (copy, ReLU, in-place ReLU, bias + ReLU) and the strided-view kernel store their body
+  (copy, ReLU, in-place ReLU, bias + ReLU, the scalar and unary maps) and the
+  strided-view kernel store their body
   with a compiler-emitted buffer store carrying the device-scope and
   non-temporal bits (buffer_store_dwordx4 ... nt sc1).
 """
@@ -93,7 +97,7 @@ def test_saxpy_kernels_use_a_fused_multiply_add(asm):
             assert not re.search(r"\bv_mul_f32\b", body), name
 
 
-SINGLE_INPUT_OPS = ("OpReluF32", "OpCopyF32", "OpRelu16")
+SINGLE_INPUT_OPS = ("OpReluF32", "OpCopyF32", "OpRelu16", "OpMapF32", "OpMap16", "OpAbs")
 
 
 def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
@@ -148,3 +152,25 @@ def test_inplace_relu_decides_stores_with_a_wave_vote(asm):
     for body, _ in ks:
         assert re.search(r"\bv_mbcnt_(lo|hi)_u32_b32\b", body)     # lane index
         assert re.search(r"\bv_lshlrev_b64\b", body)               # group mask << lane group
+
+
+def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
+    """Neither hardware estimate (v_sqrt_f32, v_rsq_f32) is correctly rounded
+    alone: the compiler refines it with fma residuals (for fp32 data the
+    root's neighbours are tested and one is selected; for widened 16-bit data
+    it emits a reciprocal-root Newton step).  The 16-bit forms must take such
+    a binary32 root and narrow it, never a native 16-bit root."""
+    ks = {k: v[0] for k, v in _kernels(asm).items() if "FnSqrt" in k}
+    assert len(ks) == 3 * 4 * 2            # 3 formats x 4 unrolls x 2 alignments
+    for name, body in ks.items():
+        assert re.search(r"\bv_(sqrt|rsq)_f32", body), name
+        assert re.search(r"\bv_fma_f32\b.*-v", body), name
+        assert not re.search(r"\bv_(sqrt|rsq|rcp)_f16", body), name
+
+
+def test_scalar_maps_compute_in_binary32(asm):
+    ks = {k: v[0] for k, v in _kernels(asm).items() if "FnScale" in k or "FnAddScalar" in k}
+    assert len(ks) == 2 * 3 * 4 * 2
+    for name, body in ks.items():
+        op = "v_mul_f32" if "FnScale" in name else "v_add_f32"
+        assert re.search(r"\b" + op, body), name
