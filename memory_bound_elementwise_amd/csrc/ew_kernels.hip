@@ -323,6 +323,29 @@ struct FnSqrt {
     __device__ static float f(float v, float) { return __builtin_sqrtf(v); }
 };
 
+// The square root of a widened binary16 value, which is never subnormal in
+// binary32, so the hardware root needs no input scaling.  v_sqrt_f32 is
+// within one ulp; of it and its two neighbours the correctly rounded root is
+// selected by the sign of the exact residuals x - n * s (one fma each): the
+// lower neighbour is taken when x <= n_lo * s, the upper when x > n_hi * s.
+// Zeros, infinities and NaNs come out of v_sqrt_f32 already right and the
+// residual tests leave them (their neighbours give NaN or a zero residual).
+// About half the vector work of the general binary32 sequence, which for
+// widened data refines a reciprocal root; only the binary16 map uses it.
+struct FnSqrtWidenedF16 {
+    __device__ static float f(float v, float)
+    {
+        const float s = __builtin_amdgcn_sqrtf(v);
+        const uint32_t si = __builtin_bit_cast(uint32_t, s);
+        const float lo = __builtin_bit_cast(float, si - 1u);
+        const float hi = __builtin_bit_cast(float, si + 1u);
+        float r = s;
+        if (__builtin_fmaf(-lo, s, v) <= 0.0f) r = lo;
+        if (__builtin_fmaf(-hi, s, v) > 0.0f) r = hi;
+        return r;
+    }
+};
+
 template <class Fn>
 struct OpMapF32 {
     using Elem = uint32_t;
@@ -377,7 +400,7 @@ using OpScaleF16 = OpMap16<_Float16, FnScale>;
 using OpScaleBF16 = OpMap16<__bf16, FnScale>;
 using OpAddScalarF16 = OpMap16<_Float16, FnAddScalar>;
 using OpAddScalarBF16 = OpMap16<__bf16, FnAddScalar>;
-using OpSqrtF16 = OpMap16<_Float16, FnSqrt>;
+using OpSqrtF16 = OpMap16<_Float16, FnSqrtWidenedF16>;
 using OpSqrtBF16 = OpMap16<__bf16, FnSqrt>;
 
 // |x|: the sign bit cleared, every other bit kept (IEEE abs is a sign-bit

@@ -156,15 +156,17 @@ def test_inplace_relu_decides_stores_with_a_wave_vote(asm):
 
 def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
     """Neither hardware estimate (v_sqrt_f32, v_rsq_f32) is correctly rounded
-    alone: the compiler refines it with fma residuals (for fp32 data the
-    root's neighbours are tested and one is selected; for widened 16-bit data
-    it emits a reciprocal-root Newton step).  The 16-bit forms must take such
-    a binary32 root and narrow it, never a native 16-bit root."""
+    alone: each is refined with fma residuals (for fp32 data and the binary16
+    map the root's neighbours are tested and one is selected; for widened
+    bfloat16 data the compiler emits a reciprocal-root Newton step).  The
+    16-bit forms must take such a binary32 root and narrow it, never a native
+    16-bit root."""
     ks = {k: v[0] for k, v in _kernels(asm).items() if "FnSqrt" in k}
     assert len(ks) == 3 * 4 * 2            # 3 formats x 4 unrolls x 2 alignments
+    assert sum("FnSqrtWidenedF16" in k for k in ks) == 8
     for name, body in ks.items():
         assert re.search(r"\bv_(sqrt|rsq)_f32", body), name
-        assert re.search(r"\bv_fma_f32\b.*-v", body), name
+        assert re.search(r"\bv_fma(_mix)?_f32\b.*-v", body), name
         assert not re.search(r"\bv_(sqrt|rsq|rcp)_f16", body), name
 
 
