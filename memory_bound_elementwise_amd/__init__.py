@@ -10,7 +10,12 @@ Buffers may be torch tensors (their ``data_ptr()``; pass sliced tensors to
 get offset pointers) or plain integers holding device addresses.  ``n``
 defaults to the output tensor's ``numel()``; ``stream`` defaults to torch's
 current stream on the output's device (an integer ``hipStream_t`` is also
-accepted).  Calls are asynchronous, like the C functions.
+accepted).  Calls are asynchronous, like the C functions.  A tensor argument
+must hold elements of the operation's width, be contiguous, hold at least the
+n elements the call covers and live on a GPU (a strided view's source: every
+element the view touches must lie in its storage); otherwise TypeError or
+ValueError is raised before the library is called.  Raw integer addresses are
+the caller's responsibility.
 """
 import ctypes
 import os
@@ -146,6 +151,25 @@ def _addr(x):
     return x.data_ptr()
 
 
+def _buf(x, es, n, role):
+    """Device address of one buffer argument.  The C ABI sees only a pointer
+    and n, so a tensor is checked here first: elements of the operation's
+    width (es bytes), contiguous, at least n elements (a shorter tensor would
+    be read or written past its end), on a GPU.  Integers pass unchecked."""
+    if x is None or isinstance(x, int):
+        return x
+    if x.element_size() != es:
+        raise TypeError(f"{role}: {x.dtype} has {x.element_size()}-byte elements, "
+                        f"the operation takes {es}-byte elements")
+    if not x.is_contiguous():
+        raise ValueError(f"{role}: the tensor is not contiguous")
+    if x.numel() < n:
+        raise ValueError(f"{role}: {x.numel()} elements, the call covers {n}")
+    if x.device.type != "cuda":
+        raise ValueError(f"{role}: the tensor is on {x.device}, not on a GPU")
+    return x.data_ptr()
+
+
 def _numel(x, n):
     if n is not None:
         return int(n)
@@ -166,61 +190,71 @@ def _stream(x, stream):
 
 def ew_add_f32(a, b, c, n=None, stream=None):
     """c = a + b (binary32)."""
-    _check(_c["ew_add_f32"](_addr(a), _addr(b), _addr(c), _numel(c, n), _stream(c, stream)),
-           "ew_add_f32")
+    n = _numel(c, n)
+    _check(_c["ew_add_f32"](_buf(a, 4, n, "a"), _buf(b, 4, n, "b"), _buf(c, 4, n, "c"), n,
+                            _stream(c, stream)), "ew_add_f32")
 
 
 def ew_add_f16(a, b, c, n=None, stream=None):
     """c = a + b on binary16 data (widen, add in binary32, round RNE)."""
-    _check(_c["ew_add_f16"](_addr(a), _addr(b), _addr(c), _numel(c, n), _stream(c, stream)),
-           "ew_add_f16")
+    n = _numel(c, n)
+    _check(_c["ew_add_f16"](_buf(a, 2, n, "a"), _buf(b, 2, n, "b"), _buf(c, 2, n, "c"), n,
+                            _stream(c, stream)), "ew_add_f16")
 
 
 def ew_add_bf16(a, b, c, n=None, stream=None):
     """c = a + b on bfloat16 data (widen, add in binary32, round RNE)."""
-    _check(_c["ew_add_bf16"](_addr(a), _addr(b), _addr(c), _numel(c, n), _stream(c, stream)),
-           "ew_add_bf16")
+    n = _numel(c, n)
+    _check(_c["ew_add_bf16"](_buf(a, 2, n, "a"), _buf(b, 2, n, "b"), _buf(c, 2, n, "c"), n,
+                             _stream(c, stream)), "ew_add_bf16")
 
 
 def ew_saxpy_f32(alpha, x, y, n=None, stream=None):
     """y = fma(alpha, x, y) in place."""
-    _check(_c["ew_saxpy_f32"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+    n = _numel(y, n)
+    _check(_c["ew_saxpy_f32"](float(alpha), _buf(x, 4, n, "x"), _buf(y, 4, n, "y"), n,
                               _stream(y, stream)), "ew_saxpy_f32")
 
 
 def ew_relu_f32(x, y, n=None, stream=None):
     """y = maximum(x, +0)."""
-    _check(_c["ew_relu_f32"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
+    n = _numel(y, n)
+    _check(_c["ew_relu_f32"](_buf(x, 4, n, "x"), _buf(y, 4, n, "y"), n, _stream(y, stream)),
            "ew_relu_f32")
 
 
 def ew_relu_inplace_f32(x, n=None, stream=None):
     """x = maximum(x, +0) in place, storing only the 64-byte spans that change."""
-    _check(_c["ew_relu_inplace_f32"](_addr(x), _numel(x, n), _stream(x, stream)),
+    n = _numel(x, n)
+    _check(_c["ew_relu_inplace_f32"](_buf(x, 4, n, "x"), n, _stream(x, stream)),
            "ew_relu_inplace_f32")
 
 
 def ew_copy_f32(src, out, n=None, stream=None):
     """out = src, bitwise."""
-    _check(_c["ew_copy_f32"](_addr(src), _addr(out), _numel(out, n), _stream(out, stream)),
-           "ew_copy_f32")
+    n = _numel(out, n)
+    _check(_c["ew_copy_f32"](_buf(src, 4, n, "src"), _buf(out, 4, n, "out"), n,
+                             _stream(out, stream)), "ew_copy_f32")
 
 
 def ew_gather_f32(src, out, stride, n=None, stream=None):
     """out[i] = src[(stride * i) mod n], bitwise."""
-    _check(_c["ew_gather_f32"](_addr(src), _addr(out), _numel(out, n), int(stride),
+    n = _numel(out, n)
+    _check(_c["ew_gather_f32"](_buf(src, 4, n, "src"), _buf(out, 4, n, "out"), n, int(stride),
                                _stream(out, stream)), "ew_gather_f32")
 
 
 def ew_add_relu_f32(a, b, c, n=None, stream=None):
     """c = maximum(a + b, +0) in one pass."""
-    _check(_c["ew_add_relu_f32"](_addr(a), _addr(b), _addr(c), _numel(c, n),
+    n = _numel(c, n)
+    _check(_c["ew_add_relu_f32"](_buf(a, 4, n, "a"), _buf(b, 4, n, "b"), _buf(c, 4, n, "c"), n,
                                  _stream(c, stream)), "ew_add_relu_f32")
 
 
 def ew_saxpy_relu_f32(alpha, x, y, n=None, stream=None):
     """y = maximum(fma(alpha, x, y), +0) in place."""
-    _check(_c["ew_saxpy_relu_f32"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+    n = _numel(y, n)
+    _check(_c["ew_saxpy_relu_f32"](float(alpha), _buf(x, 4, n, "x"), _buf(y, 4, n, "y"), n,
                                    _stream(y, stream)), "ew_saxpy_relu_f32")
 
 
@@ -230,31 +264,38 @@ def ew_bias_relu_f32(x, bias, y, rows=None, cols=None, stream=None):
         if isinstance(y, int):
             raise ValueError("rows and cols are required when buffers are raw pointers")
         rows, cols = y.shape
-    _check(_c["ew_bias_relu_f32"](_addr(x), _addr(bias), _addr(y), int(rows), int(cols),
-                                  _stream(y, stream)), "ew_bias_relu_f32")
+    rows, cols = int(rows), int(cols)
+    n = rows * cols
+    _check(_c["ew_bias_relu_f32"](_buf(x, 4, n, "x"), _buf(bias, 4, cols, "bias"),
+                                  _buf(y, 4, n, "y"), rows, cols, _stream(y, stream)),
+           "ew_bias_relu_f32")
 
 
 def ew_saxpy_f16(alpha, x, y, n=None, stream=None):
     """y = rne16(fma(alpha, x, y)) in place on binary16 data."""
-    _check(_c["ew_saxpy_f16"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+    n = _numel(y, n)
+    _check(_c["ew_saxpy_f16"](float(alpha), _buf(x, 2, n, "x"), _buf(y, 2, n, "y"), n,
                               _stream(y, stream)), "ew_saxpy_f16")
 
 
 def ew_saxpy_bf16(alpha, x, y, n=None, stream=None):
     """y = rnebf(fma(alpha, x, y)) in place on bfloat16 data."""
-    _check(_c["ew_saxpy_bf16"](float(alpha), _addr(x), _addr(y), _numel(y, n),
+    n = _numel(y, n)
+    _check(_c["ew_saxpy_bf16"](float(alpha), _buf(x, 2, n, "x"), _buf(y, 2, n, "y"), n,
                                _stream(y, stream)), "ew_saxpy_bf16")
 
 
 def ew_relu_f16(x, y, n=None, stream=None):
     """y = maximum(x, +0) on binary16 data."""
-    _check(_c["ew_relu_f16"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
+    n = _numel(y, n)
+    _check(_c["ew_relu_f16"](_buf(x, 2, n, "x"), _buf(y, 2, n, "y"), n, _stream(y, stream)),
            "ew_relu_f16")
 
 
 def ew_relu_bf16(x, y, n=None, stream=None):
     """y = maximum(x, +0) on bfloat16 data."""
-    _check(_c["ew_relu_bf16"](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)),
+    n = _numel(y, n)
+    _check(_c["ew_relu_bf16"](_buf(x, 2, n, "x"), _buf(y, 2, n, "y"), n, _stream(y, stream)),
            "ew_relu_bf16")
 
 
@@ -266,16 +307,46 @@ def ew_copy2d_f32(src, stride_r, stride_c, out, rows=None, cols=None, stream=Non
         if isinstance(out, int):
             raise ValueError("rows and cols are required when buffers are raw pointers")
         rows, cols = out.shape
-    _check(_c["ew_copy2d_f32"](_addr(src), int(stride_r), int(stride_c), _addr(out), int(rows),
-                               int(cols), _stream(out, stream)), "ew_copy2d_f32")
+    rows, cols, stride_r, stride_c = int(rows), int(cols), int(stride_r), int(stride_c)
+    _check(_c["ew_copy2d_f32"](_view_src(src, stride_r, stride_c, rows, cols), stride_r,
+                               stride_c, _buf(out, 4, rows * cols, "out"), rows, cols,
+                               _stream(out, stream)), "ew_copy2d_f32")
+
+
+def _view_src(x, sr, sc, rows, cols):
+    """Address of a strided view's element (0, 0).  For a tensor, every
+    element the view touches must lie inside the tensor's storage."""
+    if isinstance(x, int) or not rows or not cols:
+        return _addr(x)
+    if x.element_size() != 4:
+        raise TypeError(f"src: {x.dtype} has {x.element_size()}-byte elements, the view "
+                        "takes 4-byte elements")
+    lo = min(0, (rows - 1) * sr) + min(0, (cols - 1) * sc)
+    hi = max(0, (rows - 1) * sr) + max(0, (cols - 1) * sc)
+    start = x.storage_offset()
+    size = x.untyped_storage().nbytes() // 4
+    if start + lo < 0 or start + hi >= size:
+        raise ValueError(f"src: the view reaches elements {start + lo}..{start + hi} of a "
+                         f"storage of {size}")
+    if x.device.type != "cuda":
+        raise ValueError(f"src: the tensor is on {x.device}, not on a GPU")
+    return x.data_ptr()
+
+
+def _es(name):
+    return 4 if name.endswith("_f32") else 2
 
 
 def _scalar_map(name, alpha, x, y, n, stream):
-    _check(_c[name](float(alpha), _addr(x), _addr(y), _numel(y, n), _stream(y, stream)), name)
+    n = _numel(y, n)
+    _check(_c[name](float(alpha), _buf(x, _es(name), n, "x"), _buf(y, _es(name), n, "y"), n,
+                    _stream(y, stream)), name)
 
 
 def _unary_map(name, x, y, n, stream):
-    _check(_c[name](_addr(x), _addr(y), _numel(y, n), _stream(y, stream)), name)
+    n = _numel(y, n)
+    _check(_c[name](_buf(x, _es(name), n, "x"), _buf(y, _es(name), n, "y"), n,
+                    _stream(y, stream)), name)
 
 
 def ew_scale_f32(alpha, x, y, n=None, stream=None):

@@ -634,3 +634,22 @@ def test_launch_log_names_each_plan():
     assert lines[0].startswith("[ew] add_f32 n=1002 ") and "path=stream" in lines[0]
     assert lines[1].startswith("[ew] gather_f32 n=1003 ") and "path=passes" in lines[1]
     assert lines[2].startswith("[ew] copy2d_f32 n=1003 ") and "path=transpose tiles" in lines[2]
+
+
+def test_binding_checks_gpu_tensors_before_the_call():
+    """GPU tensors of the right width and length pass; a shorter input, a
+    wrong width or a non-contiguous view is refused before any launch, and
+    the output is left untouched."""
+    x = torch.randn(1000, device=DEV)
+    y = torch.full((1000,), 7.0, device=DEV)
+    with pytest.raises(ValueError, match="999 elements"):
+        ew.ew_relu_f32(x[:999], y)
+    with pytest.raises(TypeError):
+        ew.ew_scale_f16(2.0, x, y)
+    with pytest.raises(ValueError, match="not contiguous"):
+        ew.ew_abs_f32(x[::2], y[:500])
+    torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+    ew.ew_relu_f32(x, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y, torch.clamp(x, min=0.0))
