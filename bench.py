@@ -125,6 +125,7 @@ class Prepared:
         s = stream.cuda_stream
         self.stream = s
         self.unfused = None
+        self.unfused_label = None   # what `unfused` runs, when not the op's UNFUSED pair
         self.pre = None          # run before every timed launch (in-place ReLU: restore x)
         self.torch_context = None  # (label, launcher) of PyTorch's kernel for the same op
         self.changed = 0
@@ -155,6 +156,33 @@ class Prepared:
             rows = w.n // w.cols
             self.launch = lambda: ew.ew_bias_relu_f32(x, bias, y, rows, w.cols, stream=s)
             self.out, self.ptrs = y, (y, x, None)
+        elif w.batch:
+            # consecutive equal items of three arrays: the batched call's result
+            # over all items is the single operation's result over the arrays
+            a, ka = upload(self.inp["a"], offs.get("a", 0))
+            b, kb = upload(self.inp["b"], offs.get("b", 0))
+            c, kc = upload(np.zeros(w.n, self.inp["a"].dtype), offs.get("c", 0))
+            self.keep += [ka, kb, kc]
+            m = w.n // w.batch
+            parts = [(c[k * m:(k + 1) * m], a[k * m:(k + 1) * m], b[k * m:(k + 1) * m])
+                     for k in range(w.batch)]
+            batch = ew.EwBatch(w.op, [(o, x, y, m) for o, x, y in parts])
+            self.launch = lambda: batch(stream=s)
+            fn = getattr(ew, "ew_" + w.op)
+
+            def separate():
+                for o, x, y in parts:
+                    fn(x, y, o, stream=s)
+            self.unfused = separate
+            self.unfused_label = [f"{w.batch} x ew_{w.op}, one launch each"]
+            la, lb, lc = ([p[i] for p in parts] for i in (1, 2, 0))
+
+            def t_foreach():
+                with torch.cuda.stream(stream):
+                    torch._foreach_add(la, lb)
+            self.torch_context = ("torch._foreach_add(a_list, b_list) (allocates its outputs)",
+                                  t_foreach)
+            self.out, self.ptrs = c, (c, a, b)
         elif w.op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
             a, ka = upload(self.inp["a"], offs.get("a", 0))
             b, kb = upload(self.inp["b"], offs.get("b", 0))
@@ -502,6 +530,18 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     prep = Prepared(w, torch, np, ew, synth, stream)
     plan = prep.plan(ew, cus)
     launch_desc = {"block": plan.block, "grid": plan.grid, "unroll": plan.unroll}
+    if w.batch:
+        # one launch shape for the whole call: the table's row for the total n
+        block, bpc, unroll = ew.ew_get_launch_config(w.op, w.n)
+        m = w.n // w.batch
+        vec = 16 // (4 if w.op.endswith("_f32") else 2)
+        tiles = max(1, -(-(m // vec) // (block * min(unroll, 4))))     # per item
+        launch_desc = {"block": block, "unroll": min(unroll, 4), "items": w.batch,
+                       "items_per_launch": ew.BATCH_MAX,
+                       "launches": -(-w.batch // ew.BATCH_MAX),
+                       "grid_per_launch": min(bpc * cus, tiles * min(w.batch, ew.BATCH_MAX)),
+                       "path": "batched: items' tiles numbered consecutively, one kernel"}
+        steps = min(steps, 200)
     if w.op == "gather_f32":
         launch_desc["path"] = ("copy kernel" if w.stride % w.n == 1 else
                                f"{plan.passes} passes, input staged through LDS"
@@ -521,6 +561,9 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     res = {"workload": w.name, "op": w.op, "n": w.n, "launch": launch_desc,
            "split": {"head": plan.head, "vectors": plan.vectors, "tail": plan.tail,
                      "in_coaligned": list(plan.in_coaligned)}}
+    if w.batch:
+        res["split"] = {"items": w.batch, "elements_per_item": w.n // w.batch,
+                        "note": "consecutive slices of three arrays, every item 16-byte aligned"}
     got = prep.result(torch)
     if check:
         bad, cpu = cpu_baseline_leg(w, prep.inp, got, cpu_target_s)
@@ -601,8 +644,13 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
             un_ms = time_rotated(torch, [p.unfused for p in sets], stream, steps, warmup)
         else:
             un_ms = time_launches(torch, prep.unfused, stream, steps, warmup, flush=flush)
-        res["unfused"] = {"ops": list(UNFUSED[w.op]), "ms": round(un_ms, 5),
-                          "speedup_of_fused": round(un_ms / ms, 3)}
+        if prep.unfused_label is not None:
+            res["separate_calls"] = {"ops": prep.unfused_label, "ms": round(un_ms, 5),
+                                     "gbs": round(nbytes / (un_ms / 1e3) / 1e9, 1),
+                                     "speedup_of_batch": round(un_ms / ms, 3)}
+        else:
+            res["unfused"] = {"ops": list(UNFUSED[w.op]), "ms": round(un_ms, 5),
+                              "speedup_of_fused": round(un_ms / ms, 3)}
     del sets[1:]
     return res, prep, ms
 
@@ -727,7 +775,8 @@ def main(argv=None):
         "parity": res["parity"],
         "pct_of_peak": round(100 * res["gbs"] / PEAK_GBS, 2) if res.get("gbs") else None,
     }
-    for k in ("p10_ms", "p90_ms", "torch_context", "graph"):
+    for k in ("p10_ms", "p90_ms", "timing", "warm_gbs", "flushed_per_launch", "torch_context",
+              "graph", "unfused", "separate_calls"):
         if k in res:
             line[k] = res[k]
     if ms is not None:

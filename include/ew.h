@@ -230,6 +230,45 @@ ew_status_t ew_abs_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t str
 ew_status_t ew_abs_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Batched calls: many small arrays, one launch                              */
+/* ------------------------------------------------------------------------ */
+/* [HyperAI] Stage 3: at the smallest size every kernel version takes the
+ * same few microseconds -- the launch, not the memory.  Many small arrays
+ * each cost that floor through the single-array entry points; a batched call
+ * runs up to EW_BATCH_MAX of them per kernel launch. */
+
+#define EW_BATCH_MAX 96
+
+/* One operand set: the pointers of the single call, in ew_make_plan's
+ * order.  out = c (add), y (saxpy, in place), y (ReLU, maps), out (copy).
+ * in0 = a (add) or x.  in1 = b (add); ignored for the one-input operations
+ * and for SAXPY, whose second input is out itself. */
+typedef struct ew_batch_item {
+    void *out;
+    const void *in0;
+    const void *in1;
+    size_t n;
+} ew_batch_item_t;
+
+/* Runs count independent instances of one streaming operation -- any of
+ * "add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32",
+ * "add_relu_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16", "relu_f16",
+ * "relu_bf16" and the scale / add_scalar / sqrt / abs maps -- each with the
+ * result its single call would give, in ceil(items / EW_BATCH_MAX) kernel
+ * launches on `stream` (items with n == 0 are skipped).  alpha is used by
+ * the SAXPY, scale and add-scalar operations and ignored otherwise.  items:
+ * a host array, read during the call only.
+ * Errors: an unknown or non-batchable op name, or items == NULL with count >
+ * 0, -> EW_ERR_INVALID_ARG; each item is validated like its single call
+ * (first failing item's status); an item's output range intersecting any
+ * range of another item -> EW_ERR_OVERLAP (the items run concurrently; reads
+ * of shared inputs are fine).  count == 0 or all n == 0 -> EW_OK, no launch.
+ * The launch shape is the table's row of the operation for the total element
+ * count (unroll at most 4). */
+ew_status_t ew_batch(const char *op, float alpha, const ew_batch_item_t *items,
+                     size_t count, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
 /* Fused chains: one pass over memory instead of two                         */
 /* ------------------------------------------------------------------------ */
 /* An epilogue fused into the producing kernel saves a full pass through HBM

@@ -30,6 +30,7 @@ __all__ = [
     "ew_abs_f32", "ew_abs_f16", "ew_abs_bf16", "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
     "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan", "ew_make_gather_plan",
+    "ew_batch", "EwBatch", "EwBatchItem", "BATCH_MAX",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -80,6 +81,14 @@ class EwPlan(ctypes.Structure):
         return d
 
 
+class EwBatchItem(ctypes.Structure):
+    """Mirror of ``ew_batch_item_t``."""
+    _fields_ = [("out", _vp), ("in0", _vp), ("in1", _vp), ("n", _sz)]
+
+
+BATCH_MAX = 96          # EW_BATCH_MAX: items per kernel launch
+
+
 def _proto(name, restype, *argtypes):
     fn = getattr(_lib, name)
     fn.restype = restype
@@ -109,6 +118,8 @@ _c = {
        for m in SCALAR_MAPS for d in MAP_DTYPES},
     **{f"ew_{m}_{d}": _proto(f"ew_{m}_{d}", _int, _vp, _vp, _sz, _vp)
        for m in UNARY_MAPS for d in MAP_DTYPES},
+    "ew_batch": _proto("ew_batch", _int, ctypes.c_char_p, ctypes.c_float,
+                       ctypes.POINTER(EwBatchItem), _sz, _vp),
     "ew_status_string": _proto("ew_status_string", ctypes.c_char_p, _int),
     "ew_last_hip_error": _proto("ew_last_hip_error", _int),
     "ew_abi_version": _proto("ew_abi_version", _int),
@@ -407,6 +418,44 @@ def ew_abs_f16(x, y, n=None, stream=None):
 def ew_abs_bf16(x, y, n=None, stream=None):
     """y = |x| on bfloat16 bit patterns."""
     _unary_map("ew_abs_bf16", x, y, n, stream)
+
+
+class EwBatch:
+    """A batched call prepared once: the tensors are checked and the C item
+    array is built at construction, so each call -- ``batch(alpha, stream)``
+    -- goes straight to ``ew_batch`` (which still validates every item).
+    items: a sequence of (out, in0, in1, n) with the single call's pointers
+    (in1 None for one-input operations and SAXPY; n None for out's numel()).
+    The tensors must stay alive while the batch is used."""
+
+    def __init__(self, op, items):
+        es = 4 if op.endswith("_f32") else 2
+        self.op = op
+        self._op = op.encode()
+        self.count = len(items)
+        self._arr = (EwBatchItem * max(self.count, 1))()
+        self._first = None
+        for k, (out, in0, in1, n) in enumerate(items):
+            n = _numel(out, n)
+            self._arr[k] = EwBatchItem(
+                _buf(out, es, n, f"items[{k}].out"), _buf(in0, es, n, f"items[{k}].in0"),
+                _buf(in1, es, n, f"items[{k}].in1") if in1 is not None else None, n)
+            if self._first is None and not isinstance(out, int):
+                self._first = out
+
+    def __call__(self, alpha=0.0, stream=None):
+        s = _stream(self._first, stream) if self._first is not None else stream
+        if s is not None and not isinstance(s, int):
+            s = s.cuda_stream
+        _check(_c["ew_batch"](self._op, float(alpha), self._arr, self.count, s), "ew_batch")
+
+
+def ew_batch(op, items, alpha=0.0, stream=None):
+    """Independent instances of one streaming operation in ceil(len(items) /
+    BATCH_MAX) launches (see EwBatch for items; prepare an EwBatch once to
+    call the same batch repeatedly without re-marshalling).  stream defaults
+    to torch's current stream on the first tensor's device."""
+    EwBatch(op, items)(alpha, stream)
 
 
 def ew_status_string(status: int) -> str:

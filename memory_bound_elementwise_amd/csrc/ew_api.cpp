@@ -7,6 +7,7 @@
 #include "ew.h"
 #include "ew_internal.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cerrno>
 #include <cstdio>
@@ -19,7 +20,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 
 struct OpInfo {
     const char *name;
@@ -389,6 +390,68 @@ ew_status_t run_stream(int op, const void *out, const void *in0, const void *in1
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
+// Operations the batched entry point runs: every one-pass streaming
+// operation of ew_stream_kernel.
+bool batchable(int op)
+{
+    switch (op) {
+    case kOpGatherF32:
+    case kOpBiasReluF32:
+    case kOpCopy2dF32:
+    case kOpReluInplaceF32: return false;
+    default: return op >= 0 && op < kOpCount;
+    }
+}
+
+// Operations whose single call passes y as both the second input and the
+// output (y <- f(x, y) in place).
+bool in_place_second(int op)
+{
+    return op == kOpSaxpyF32 || op == kOpSaxpyReluF32 || op == kOpSaxpyF16 ||
+           op == kOpSaxpyBF16;
+}
+
+// Items of one batched call must not race: an item's output range may not
+// intersect any range (input or output) of another item.  Ranges sorted by
+// start; each is compared with the earlier ones that are still open.
+ew_status_t batch_overlap(int op, const ew_batch_item_t *items, size_t count)
+{
+    struct R {
+        uintptr_t lo, hi;
+        size_t item;
+        bool write;
+    };
+    const size_t es = (size_t)kOps[op].elem_size;
+    std::vector<R> rs;
+    rs.reserve(3 * count);
+    for (size_t i = 0; i < count; ++i) {
+        const ew_batch_item_t &it = items[i];
+        if (it.n == 0) continue;
+        const uintptr_t bytes = (uintptr_t)(it.n * es);
+        const uintptr_t o = reinterpret_cast<uintptr_t>(it.out);
+        rs.push_back(R{o, o + bytes, i, true});
+        const uintptr_t a = reinterpret_cast<uintptr_t>(it.in0);
+        rs.push_back(R{a, a + bytes, i, false});
+        if (kOps[op].inputs == 2 && !in_place_second(op)) {
+            const uintptr_t b = reinterpret_cast<uintptr_t>(it.in1);
+            rs.push_back(R{b, b + bytes, i, false});
+        }
+    }
+    std::sort(rs.begin(), rs.end(), [](const R &x, const R &y) { return x.lo < y.lo; });
+    std::vector<R> open;
+    for (const R &r : rs) {
+        size_t keep = 0;
+        for (const R &q : open) {
+            if (q.hi <= r.lo) continue;              // closed before r starts
+            if (q.item != r.item && (q.write || r.write)) return EW_ERR_OVERLAP;
+            open[keep++] = q;
+        }
+        open.resize(keep);
+        open.push_back(r);
+    }
+    return EW_OK;
+}
+
 // (a * b) mod m without overflow (host: 128-bit arithmetic).
 uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
 {
@@ -619,6 +682,66 @@ ew_status_t ew_abs_f16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 ew_status_t ew_abs_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
 {
     return run_stream(kOpAbsBF16, y, x, nullptr, n, 0.0f, s);
+}
+
+ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *items,
+                     size_t count, hipStream_t s)
+{
+    const int op = op_from_name(op_name);
+    if (op < 0 || !batchable(op)) return EW_ERR_INVALID_ARG;
+    if (count == 0) return EW_OK;
+    if (!items) return EW_ERR_INVALID_ARG;
+    size_t total = 0;
+    for (size_t i = 0; i < count; ++i) {
+        const ew_batch_item_t &it = items[i];
+        if (it.n == 0) continue;
+        const void *in1 = in_place_second(op) ? it.out : it.in1;
+        const ew_status_t st = validate(op, it.out, it.in0, in1, it.n);
+        if (st != EW_OK) return st;
+        if (it.n > (size_t(1) << 62) - total) return EW_ERR_INVALID_ARG;
+        total += it.n;
+    }
+    ew_status_t st = batch_overlap(op, items, count);
+    if (st != EW_OK) return st;
+    if (total == 0) return EW_OK;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    // One launch shape for the whole call: the table's row for the total
+    // element count (unroll at most 4).
+    const Row r = get_row(op, total);
+    const int unroll = r.unroll > 4 ? 4 : r.unroll;
+    const uint64_t tile_vecs = (uint64_t)r.block * (uint64_t)unroll;
+    BatchArgs a{};
+    a.alpha = alpha;
+    size_t i = 0;
+    while (i < count) {
+        a.count = 0;
+        a.tiles = 0;
+        for (; i < count && a.count < (uint32_t)kBatchMax; ++i) {
+            const ew_batch_item_t &it = items[i];
+            if (it.n == 0) continue;
+            const void *in1 = kOps[op].inputs == 2 ? (in_place_second(op) ? it.out : it.in1)
+                                                   : nullptr;
+            // the kernel recomputes this split from the same pointers and n
+            const Plan p = make_plan(op, it.out, it.in0, in1, it.n, cus);
+            a.item[a.count] = BatchItem{it.in0, in1, it.out, (uint64_t)it.n};
+            uint64_t tiles = (p.vectors + tile_vecs - 1) / tile_vecs;
+            if (tiles == 0) tiles = 1;        // the head and tail still need a block
+            a.tiles += tiles;
+            a.tile_end[a.count] = a.tiles;
+            ++a.count;
+        }
+        if (a.count == 0) break;
+        uint64_t grid = (uint64_t)r.blocks_per_cu * (uint64_t)(cus > 0 ? cus : 1);
+        if (grid > a.tiles) grid = a.tiles;
+        const Launch l{r.block, (int)grid, unroll};
+        log_launch(kOps[op].name, (size_t)a.count, 0, a.tiles, 0, l,
+                   "batch (n = items, vectors = tiles)");
+        const hipError_t e = launch_batch(static_cast<OpId>(op), a, l, s);
+        if (e != hipSuccess) return fail_hip(e);
+    }
+    return EW_OK;
 }
 
 ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)

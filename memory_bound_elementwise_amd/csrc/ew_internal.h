@@ -54,6 +54,29 @@ struct StreamArgs {
     float alpha;         // saxpy, scale and add-scalar only
 };
 
+// A batched call: up to kBatchMax independent operand sets of one streaming
+// operation in one launch.  Item k owns the global tiles [tile_end[k - 1],
+// tile_end[k]) -- at least one, so that its scalar head and tail have a block.
+// Each block recomputes its item's head / vectors / tail split and input
+// alignment from the pointers and n, exactly as the host plans a single
+// call, so an item travels as four words.  The whole struct is the kernel
+// argument (3856 bytes, under the 4 KiB kernel-argument limit).
+constexpr int kBatchMax = 96;
+struct BatchItem {
+    const void *in0;
+    const void *in1;     // nullptr for one-input operations
+    void *out;
+    uint64_t n;
+};
+struct BatchArgs {
+    uint64_t tiles;      // tiles of all items together
+    uint32_t count;      // items in this launch, 1..kBatchMax
+    float alpha;         // saxpy, scale and add-scalar only
+    uint64_t tile_end[kBatchMax];
+    BatchItem item[kBatchMax];
+};
+static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
 // The gather additionally walks its input index (stride * i) mod n
 // incrementally; the steps are reduced mod n on the host.  When
 // g = gcd(stride, n) > 1 the output is g copies of one segment of n / g
@@ -126,6 +149,11 @@ struct Launch {
 // aligned at its body start.  Returns the launch status.
 hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
                          const Launch &launch, hipStream_t stream);
+
+// Launch one batched streaming kernel (block and unroll from `launch`; the
+// unroll must be 1, 2 or 4).
+hipError_t launch_batch(OpId op, const BatchArgs &args, const Launch &launch,
+                        hipStream_t stream);
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
                          hipStream_t stream);

@@ -494,6 +494,114 @@ __global__ void __launch_bounds__(1024) ew_stream_kernel(StreamArgs args)
 }
 
 // ---------------------------------------------------------------------------
+// Batched streaming: independent operand sets of one operation, one launch
+// ---------------------------------------------------------------------------
+
+// One tile of one batch item: the body of ew_stream_kernel for local tile lt.
+template <class Op, int U, bool Co0, bool Co1>
+__device__ __forceinline__ void batch_tile(const char *in0, const char *in1, char *out,
+                                           uint64_t vectors, uint64_t lt, uint32_t tid,
+                                           uint64_t nthr, float alpha)
+{
+    using E = typename Op::Elem;
+    constexpr uint64_t kElem = sizeof(E);
+    constexpr bool kTwo = Op::kInputs == 2;
+    const uint64_t tile_vecs = nthr * U;
+    const uint64_t v0 = lt * tile_vecs + tid;
+    char *tile = out + lt * tile_vecs * 16;
+    const uint32_t tile_bytes = (uint32_t)(tile_vecs * 16);
+    if (v0 + (U - 1) * nthr < vectors) {
+        u32x4 x[U], y[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) x[u] = load16<Co0, kElem>(in0 + (v0 + u * nthr) * 16);
+        if constexpr (kTwo) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) y[u] = load16<Co1, kElem>(in1 + (v0 + u * nthr) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const u32x4 b = kTwo ? y[u] : u32x4{0, 0, 0, 0};
+            if constexpr (kTwo)
+                store16(out + (v0 + u * nthr) * 16, Op::vec(x[u], b, alpha));
+            else
+                store16_device(tile, tile_bytes, (uint32_t)((tid + u * nthr) * 16),
+                               Op::vec(x[u], b, alpha));
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t v = v0 + u * nthr;
+            if (v < vectors) {
+                const u32x4 a = load16<Co0, kElem>(in0 + v * 16);
+                const u32x4 b = kTwo ? load16<Co1, kElem>(in1 + v * 16) : u32x4{0, 0, 0, 0};
+                if constexpr (kTwo)
+                    store16(out + v * 16, Op::vec(a, b, alpha));
+                else
+                    store16_device(tile, tile_bytes, (uint32_t)((tid + u * nthr) * 16),
+                                   Op::vec(a, b, alpha));
+            }
+        }
+    }
+}
+
+// Many small arrays cost one launch each through the single-array entry
+// points, and below about 2^21 elements the launch, not HBM, sets the time
+// ([HyperAI] Stage 3: the smallest size runs at the same few microseconds in
+// every version).  Here the tiles of all items are numbered consecutively and
+// walked with a grid stride; a block finds the item that owns its tile by a
+// binary search over tile_end (block-uniform, kernel-argument loads),
+// recomputes the item's head / body / tail split and input alignment (scalar
+// arithmetic on its pointers and n, the same as the host's plan of a single
+// call), does the scalar head and tail if the tile is the item's first, and
+// streams the tile's vectors with the item's own alignment path.
+template <class Op, int U>
+__global__ void __launch_bounds__(1024) ew_batch_kernel(BatchArgs args)
+{
+    using E = typename Op::Elem;
+    constexpr uint64_t kVec = 16 / sizeof(E);
+    constexpr bool kTwo = Op::kInputs == 2;
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nthr = blockDim.x;
+    for (uint64_t t = blockIdx.x; t < args.tiles; t += gridDim.x) {
+        uint32_t lo = 0, hi = args.count - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) / 2;
+            if (args.tile_end[mid] > t) hi = mid;
+            else lo = mid + 1;
+        }
+        const BatchItem &it = args.item[lo];
+        const uint64_t lt = t - (lo ? args.tile_end[lo - 1] : 0);
+        // the single call's split: the head aligns the output to 16 bytes
+        const uint64_t n = it.n;
+        uint64_t head = ((16u - (reinterpret_cast<uintptr_t>(it.out) & 15u)) & 15u) / sizeof(E);
+        if (head > n) head = n;
+        const uint64_t vectors = (n - head) / kVec;
+        const uint64_t tail = n - head - vectors * kVec;
+        if (lt == 0 && tid < head + tail) {
+            const uint64_t e = tid < head ? (uint64_t)tid : head + vectors * kVec + (tid - head);
+            const E a = static_cast<const E *>(it.in0)[e];
+            const E b = kTwo ? static_cast<const E *>(it.in1)[e] : E(0);
+            static_cast<E *>(it.out)[e] = Op::one(a, b, args.alpha);
+        }
+        const char *in0 = static_cast<const char *>(it.in0) + head * sizeof(E);
+        const char *in1 = kTwo ? static_cast<const char *>(it.in1) + head * sizeof(E) : nullptr;
+        char *out = static_cast<char *>(it.out) + head * sizeof(E);
+        const bool co0 = (reinterpret_cast<uintptr_t>(in0) & 15u) == 0;
+        const bool co1 = !kTwo || (reinterpret_cast<uintptr_t>(in1) & 15u) == 0;
+        const float al = args.alpha;
+        if constexpr (kTwo) {
+            if (co0 && co1) batch_tile<Op, U, true, true>(in0, in1, out, vectors, lt, tid, nthr, al);
+            else if (co0) batch_tile<Op, U, true, false>(in0, in1, out, vectors, lt, tid, nthr, al);
+            else if (co1) batch_tile<Op, U, false, true>(in0, in1, out, vectors, lt, tid, nthr, al);
+            else batch_tile<Op, U, false, false>(in0, in1, out, vectors, lt, tid, nthr, al);
+        } else {
+            if (co0) batch_tile<Op, U, true, true>(in0, in1, out, vectors, lt, tid, nthr, al);
+            else batch_tile<Op, U, false, true>(in0, in1, out, vectors, lt, tid, nthr, al);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Strided gather: out[i] = in[(s * i) mod n]
 // ---------------------------------------------------------------------------
 
@@ -1084,7 +1192,53 @@ hipError_t launch_op(const StreamArgs &args, bool co0, bool co1, const Launch &l
     }
 }
 
+template <class Op>
+hipError_t launch_batch_op(const BatchArgs &args, const Launch &l, hipStream_t s)
+{
+    BatchArgs a = args;
+    void *kargs[] = {&a};
+    const void *fn = nullptr;
+    switch (l.unroll) {
+    case 1: fn = reinterpret_cast<const void *>(&ew_batch_kernel<Op, 1>); break;
+    case 2: fn = reinterpret_cast<const void *>(&ew_batch_kernel<Op, 2>); break;
+    case 4: fn = reinterpret_cast<const void *>(&ew_batch_kernel<Op, 4>); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
+}
+
 }  // namespace
+
+hipError_t launch_batch(OpId op, const BatchArgs &args, const Launch &l, hipStream_t s)
+{
+    switch (op) {
+    case kOpAddF32: return launch_batch_op<OpAddF32>(args, l, s);
+    case kOpAddF16: return launch_batch_op<OpAddF16>(args, l, s);
+    case kOpAddBF16: return launch_batch_op<OpAddBF16>(args, l, s);
+    case kOpSaxpyF32: return launch_batch_op<OpSaxpyF32>(args, l, s);
+    case kOpReluF32: return launch_batch_op<OpReluF32>(args, l, s);
+    case kOpCopyF32: return launch_batch_op<OpCopyF32>(args, l, s);
+    case kOpAddReluF32: return launch_batch_op<OpAddReluF32>(args, l, s);
+    case kOpSaxpyReluF32: return launch_batch_op<OpSaxpyReluF32>(args, l, s);
+    case kOpSaxpyF16: return launch_batch_op<OpSaxpyF16>(args, l, s);
+    case kOpSaxpyBF16: return launch_batch_op<OpSaxpyBF16>(args, l, s);
+    case kOpReluF16: return launch_batch_op<OpReluF16>(args, l, s);
+    case kOpReluBF16: return launch_batch_op<OpReluBF16>(args, l, s);
+    case kOpScaleF32: return launch_batch_op<OpScaleF32>(args, l, s);
+    case kOpScaleF16: return launch_batch_op<OpScaleF16>(args, l, s);
+    case kOpScaleBF16: return launch_batch_op<OpScaleBF16>(args, l, s);
+    case kOpAddScalarF32: return launch_batch_op<OpAddScalarF32>(args, l, s);
+    case kOpAddScalarF16: return launch_batch_op<OpAddScalarF16>(args, l, s);
+    case kOpAddScalarBF16: return launch_batch_op<OpAddScalarBF16>(args, l, s);
+    case kOpSqrtF32: return launch_batch_op<OpSqrtF32>(args, l, s);
+    case kOpSqrtF16: return launch_batch_op<OpSqrtF16>(args, l, s);
+    case kOpSqrtBF16: return launch_batch_op<OpSqrtBF16>(args, l, s);
+    case kOpAbsF32: return launch_batch_op<OpAbsF32>(args, l, s);
+    case kOpAbsF16:
+    case kOpAbsBF16: return launch_batch_op<OpAbs16>(args, l, s);
+    default: return hipErrorInvalidValue;
+    }
+}
 
 hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
                          const Launch &launch, hipStream_t stream)

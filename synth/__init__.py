@@ -74,6 +74,7 @@ class Workload:
     stride: int = 0       # gather only
     cols: int = 0         # bias_relu / copy2d: row length (n = rows * cols)
     view: tuple = ()      # copy2d: (stride_r, stride_c, base elements, offset)
+    batch: int = 0        # batched call: n is split into this many equal consecutive items
     description: str = ""
 
 
@@ -185,6 +186,14 @@ WORKLOADS = {
     "abs_f16_2e28": _w(
         "abs_f16_2e28", "abs_f16", 1 << 28, 125, "normal",
         description="fp16 y = |x| (sign bit cleared), n=2^28, x normal(0,1) cast RNE"),
+    "batch_add_f32_64x16384": _w(
+        "batch_add_f32_64x16384", "add_f32", 1 << 20, 126, "uniform", batch=64,
+        description="fp32 C=A+B on 64 arrays of 16384 elements (2^20 in all, the small "
+                    "configuration's bytes) in one batched call, A,B uniform[-1,1)"),
+    "batch_add_f32_1024x1024": _w(
+        "batch_add_f32_1024x1024", "add_f32", 1 << 20, 127, "uniform", batch=1024,
+        description="fp32 C=A+B on 1024 arrays of 1024 elements (2^20 in all) in one batched "
+                    "call, A,B uniform[-1,1)"),
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),

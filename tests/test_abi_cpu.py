@@ -52,7 +52,7 @@ def test_binding_names_match_the_c_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert ew.ew_abi_version() == 8
+    assert ew.ew_abi_version() == 9
     for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
                  EW_ERR_NO_DEVICE, EW_ERR_HIP):
         s = ew.ew_status_string(code)
@@ -301,3 +301,41 @@ def test_header_is_clean_c11_and_a_c_program_links_against_the_library(tmp_path)
     spec.loader.exec_module(mod)
     exe = mod.build(out=str(tmp_path / "client"))
     assert os.path.exists(exe)
+
+
+def _batch(op, items, alpha=0.0):
+    """ew_batch on raw (out, in0, in1, n) tuples; returns the status."""
+    arr = (ew.EwBatchItem * max(len(items), 1))(*[ew.EwBatchItem(*it) for it in items])
+    return ew._c["ew_batch"](op.encode(), alpha, arr, len(items), None)
+
+
+def test_batch_validation():
+    n = 1024
+    a, b, c = BASE, BASE + MiB, BASE + 2 * MiB
+    assert _batch("add_f32", []) == EW_OK
+    assert _batch("add_f32", [(c, a, b, 0), (0, 0, 0, 0)]) == EW_OK          # all n == 0
+    assert ew._c["ew_batch"](b"add_f32", 0.0, None, 3, None) == EW_ERR_INVALID_ARG
+    for op in ("gather_f32", "bias_relu_f32", "copy2d_f32", "relu_inplace_f32", "nope"):
+        assert _batch(op, [(c, a, b, n)]) == EW_ERR_INVALID_ARG, op
+    # each item is validated like its single call
+    assert _batch("add_f32", [(c, a, b, n), (c + 4 * MiB, 0, b, n)]) == EW_ERR_INVALID_ARG
+    assert _batch("add_f16", [(c, a + 1, b, n)]) == EW_ERR_MISALIGNED
+    assert _batch("relu_f32", [(a + 4, a, None, n)]) == EW_ERR_OVERLAP
+    # across items: an output may not meet another item's input or output
+    assert _batch("add_f32", [(c, a, b, n), (c + 4 * n - 4, a, b, n)]) == EW_ERR_OVERLAP
+    assert _batch("add_f32", [(c, a, b, n), (a + 8, c + 8 * MiB, b, 4)]) == EW_ERR_OVERLAP
+    assert _batch("saxpy_f32", [(b, a, None, n), (a, b, None, n)]) == EW_ERR_OVERLAP
+    # exact aliasing inside one item stays allowed, as for the single call
+    assert _batch("relu_f32", [(a, a, None, n), (b, b, None, n)]) in (EW_OK, EW_ERR_NO_DEVICE,
+                                                                      EW_ERR_HIP)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no GPU is visible")
+def test_valid_batch_without_a_device_reports_no_device():
+    n = 1024
+    a, b = BASE, BASE + MiB
+    outs = [BASE + (2 + k) * MiB for k in range(100)]
+    # 100 items reading the same two inputs (shared reads are fine)
+    items = [(o, a, b, n + k) for k, o in enumerate(outs)]
+    assert _batch("add_f32", items) == EW_ERR_NO_DEVICE
+    assert _batch("scale_bf16", [(o, a, None, n) for o in outs], 2.5) == EW_ERR_NO_DEVICE

@@ -48,6 +48,18 @@ def _run(w: synth.Workload):
         torch.cuda.synchronize()
         got = download(y, es)
         ref = oracle.bias_relu_f32(inp["x"], inp["bias"], w.n // w.cols, w.cols)
+    elif w.batch:
+        # the bench's batched call: consecutive equal items of three arrays
+        a, _ka = upload(inp["a"], offs.get("a", 0))
+        b, _kb = upload(inp["b"], offs.get("b", 0))
+        c, _kc = upload(np.zeros(w.n, inp["a"].dtype), offs.get("c", 0))
+        m = w.n // w.batch
+        ew.ew_batch(w.op, [(c[k * m:(k + 1) * m], a[k * m:(k + 1) * m], b[k * m:(k + 1) * m], m)
+                           for k in range(w.batch)], stream=s)
+        torch.cuda.synchronize()
+        got = download(c, es)
+        del a, b, c, _ka, _kb, _kc
+        ref = getattr(oracle, w.op)(inp["a"], inp["b"])
     elif w.op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
         a, _ka = upload(inp["a"], offs.get("a", 0))
         b, _kb = upload(inp["b"], offs.get("b", 0))

@@ -101,18 +101,20 @@ SINGLE_INPUT_OPS = ("OpReluF32", "OpCopyF32", "OpRelu16", "OpMapF32", "OpMap16",
 
 
 def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
-    n_single = 0
+    """The batched kernels follow the same store policy as the single ones."""
+    n_single = n_batch = 0
     for name, (body, _) in _kernels(asm).items():
-        if "ew_stream_kernel" in name or "relu_inplace" in name:
+        n_batch += "ew_batch_kernel" in name
+        if "ew_stream_kernel" in name or "relu_inplace" in name or "ew_batch_kernel" in name:
             assert re.search(r"global_load_dwordx4 .* nt\b", body), name
-            if ("relu_inplace" in name or
-                    ("ew_stream_kernel" in name and any(op in name for op in SINGLE_INPUT_OPS))):
+            if ("relu_inplace" in name or any(op in name for op in SINGLE_INPUT_OPS)):
                 n_single += 1
                 assert re.search(r"buffer_store_dwordx4 .* nt sc1\b", body), name
                 assert not re.search(r"global_store_dwordx4", body), name
             else:
                 assert re.search(r"global_store_dwordx4 .* nt\b", body), name
     assert n_single > 0
+    assert n_batch == 23 * 3           # every batchable operator kernel x unroll 1, 2, 4
 
 
 def test_strided_view_and_bias_relu_kernels_store_at_device_scope(asm):
@@ -162,8 +164,9 @@ def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
     16-bit forms must take such a binary32 root and narrow it, never a native
     16-bit root."""
     ks = {k: v[0] for k, v in _kernels(asm).items() if "FnSqrt" in k}
-    assert len(ks) == 3 * 4 * 2            # 3 formats x 4 unrolls x 2 alignments
-    assert sum("FnSqrtWidenedF16" in k for k in ks) == 8
+    # 3 formats x (4 unrolls x 2 alignments of the single kernel + 3 batched unrolls)
+    assert len(ks) == 3 * (4 * 2 + 3)
+    assert sum("FnSqrtWidenedF16" in k for k in ks) == 8 + 3
     for name, body in ks.items():
         assert re.search(r"\bv_(sqrt|rsq)_f32", body), name
         assert re.search(r"\bv_fma(_mix)?_f32\b.*-v", body), name
@@ -172,7 +175,7 @@ def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
 
 def test_scalar_maps_compute_in_binary32(asm):
     ks = {k: v[0] for k, v in _kernels(asm).items() if "FnScale" in k or "FnAddScalar" in k}
-    assert len(ks) == 2 * 3 * 4 * 2
+    assert len(ks) == 2 * 3 * (4 * 2 + 3)
     for name, body in ks.items():
         op = "v_mul_f32" if "FnScale" in name else "v_add_f32"
         assert re.search(r"\b" + op, body), name
