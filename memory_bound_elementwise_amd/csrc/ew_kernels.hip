@@ -346,6 +346,22 @@ struct FnSqrtWidenedF16 {
     }
 };
 
+// The square root of a widened bfloat16 value, to be rounded to bfloat16.
+// Every positive bfloat16 root lies at least 32 binary32 ulps from a
+// bfloat16 rounding boundary, so any binary32 root within a few ulps -- the
+// hardware's is within one -- rounds to the same bfloat16 as the exact root;
+// no refinement is needed.  Inputs below 2^-96 (bfloat16 subnormals are
+// binary32 subnormals, which the hardware root is not specified for) are
+// scaled by 2^32 first and the root by 2^-16 after, both exactly.
+struct FnSqrtWidenedBF16 {
+    __device__ static float f(float v, float)
+    {
+        const bool tiny = v < 0x1p-96f;
+        const float s = __builtin_amdgcn_sqrtf(tiny ? v * 0x1p32f : v);
+        return tiny ? s * 0x1p-16f : s;
+    }
+};
+
 template <class Fn>
 struct OpMapF32 {
     using Elem = uint32_t;
@@ -401,7 +417,7 @@ using OpScaleBF16 = OpMap16<__bf16, FnScale>;
 using OpAddScalarF16 = OpMap16<_Float16, FnAddScalar>;
 using OpAddScalarBF16 = OpMap16<__bf16, FnAddScalar>;
 using OpSqrtF16 = OpMap16<_Float16, FnSqrtWidenedF16>;
-using OpSqrtBF16 = OpMap16<__bf16, FnSqrt>;
+using OpSqrtBF16 = OpMap16<__bf16, FnSqrtWidenedBF16>;
 
 // |x|: the sign bit cleared, every other bit kept (IEEE abs is a sign-bit
 // operation, so NaN payloads pass unchanged).  E is the element's width.

@@ -183,6 +183,9 @@ WORKLOADS = {
     "sqrt_f16_2e28": _w(
         "sqrt_f16_2e28", "sqrt_f16", 1 << 28, 124, "absnormal",
         description="fp16 square root y = rne16(sqrt(x)), n=2^28, x = |normal(0,1)| cast RNE"),
+    "sqrt_bf16_2e28": _w(
+        "sqrt_bf16_2e28", "sqrt_bf16", 1 << 28, 128, "absnormal",
+        description="bf16 square root y = rnebf(sqrt(x)), n=2^28, x = |normal(0,1)| cast RNE"),
     "abs_f16_2e28": _w(
         "abs_f16_2e28", "abs_f16", 1 << 28, 125, "normal",
         description="fp16 y = |x| (sign bit cleared), n=2^28, x normal(0,1) cast RNE"),

@@ -158,19 +158,27 @@ def test_inplace_relu_decides_stores_with_a_wave_vote(asm):
 
 def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
     """Neither hardware estimate (v_sqrt_f32, v_rsq_f32) is correctly rounded
-    alone: each is refined with fma residuals (for fp32 data and the binary16
-    map the root's neighbours are tested and one is selected; for widened
-    bfloat16 data the compiler emits a reciprocal-root Newton step).  The
-    16-bit forms must take such a binary32 root and narrow it, never a native
-    16-bit root."""
+    alone: for fp32 data and the binary16 map it is refined with fma
+    residuals (the root's neighbours are tested and one is selected).  The
+    bfloat16 map needs no refinement (every bfloat16 root is at least 32
+    binary32 ulps from a bfloat16 rounding boundary; pinned in
+    test_rounding_margins_cpu.py).  No form may use a native 16-bit root."""
     ks = {k: v[0] for k, v in _kernels(asm).items() if "FnSqrt" in k}
     # 3 formats x (4 unrolls x 2 alignments of the single kernel + 3 batched unrolls)
     assert len(ks) == 3 * (4 * 2 + 3)
     assert sum("FnSqrtWidenedF16" in k for k in ks) == 8 + 3
+    assert sum("FnSqrtWidenedBF16" in k for k in ks) == 8 + 3
     for name, body in ks.items():
+        assert not re.search(r"\bv_(sqrt|rsq|rcp)_f16", body), name
+        if "FnSqrtWidenedBF16" in name:
+            # no refinement needed (rounding margin >= 32 ulps): the hardware
+            # root, tiny inputs scaled by 2^32 (0x4f800000) and back by 2^-16
+            assert re.search(r"\bv_sqrt_f32", body), name
+            assert re.search(r"0x4f800000", body) and re.search(r"0x37800000", body), name
+            assert not re.search(r"\bv_rsq_f32", body), name
+            continue
         assert re.search(r"\bv_(sqrt|rsq)_f32", body), name
         assert re.search(r"\bv_fma(_mix)?_f32\b.*-v", body), name
-        assert not re.search(r"\bv_(sqrt|rsq|rcp)_f16", body), name
 
 
 def test_scalar_maps_compute_in_binary32(asm):
