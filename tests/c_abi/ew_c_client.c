@@ -21,6 +21,8 @@ void oracle_relu_f32(const float *x, float *y, size_t n);
 void oracle_gather_f32(const float *in, float *out, size_t n, size_t stride);
 void oracle_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, float *out,
                        size_t rows, size_t cols);
+void oracle_sqrt_f32(const float *x, float *y, size_t n);
+void oracle_scale_f32(float alpha, const float *x, float *y, size_t n);
 
 static int failures = 0, checks = 0;
 
@@ -115,6 +117,48 @@ int main(void)
     HIP_OK(hipMemcpy(got, db, n * sizeof *got, hipMemcpyDeviceToHost));
     oracle_relu_f32(hb, ref, n);
     expect_equal("ew_relu_inplace_f32", got, ref, n);
+
+    /* a unary map: sqrt of |a| (abs first, in place on c) */
+    expect_status("ew_abs_f32", ew_abs_f32(da + 1, dc, n, s), EW_OK);
+    expect_status("ew_sqrt_f32", ew_sqrt_f32(dc, dc, n, s), EW_OK);
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(got, dc, n * sizeof *got, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < n; ++i) ref[i] = ha[i + 1] < 0 ? -ha[i + 1] : ha[i + 1];
+    oracle_sqrt_f32(ref, ref, n);
+    expect_equal("ew_abs_f32 + ew_sqrt_f32", got, ref, n);
+
+    /* a batched call: 130 items (two launches) of a scale by 2.5, item k
+     * covering k * 7 + 1 elements of a at offset k, written to c */
+    {
+        enum { ITEMS = 130 };
+        ew_batch_item_t items[ITEMS];
+        size_t at = 0;
+        for (int k = 0; k < ITEMS; ++k) {
+            const size_t m = (size_t)k * 7 + 1;
+            items[k].out = dc + at;
+            items[k].in0 = da + at + (size_t)(k % 4);
+            items[k].in1 = NULL;
+            items[k].n = m;
+            at += m + 5;
+        }
+        HIP_OK(hipMemset(dc, 0, n * sizeof *dc));
+        expect_status("ew_batch scale_f32", ew_batch("scale_f32", 2.5f, items, ITEMS, s), EW_OK);
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(got, dc, at * sizeof *got, hipMemcpyDeviceToHost));
+        memset(ref, 0, at * sizeof *ref);
+        at = 0;
+        for (int k = 0; k < ITEMS; ++k) {
+            const size_t m = (size_t)k * 7 + 1;
+            oracle_scale_f32(2.5f, ha + at + (size_t)(k % 4), ref + at, m);
+            at += m + 5;
+        }
+        expect_equal("ew_batch scale_f32", got, ref, at);
+        items[1].out = dc;                         /* meets item 0's output */
+        expect_status("ew_batch overlap", ew_batch("scale_f32", 2.5f, items, ITEMS, s),
+                      EW_ERR_OVERLAP);
+        expect_status("ew_batch op", ew_batch("gather_f32", 0.0f, items, ITEMS, s),
+                      EW_ERR_INVALID_ARG);
+    }
 
     /* errors are status codes, checked before any HIP call */
     expect_status("null pointer", ew_add_f32(NULL, db, dc, n, s), EW_ERR_INVALID_ARG);
