@@ -82,20 +82,27 @@ struct Row {
 
 // Compiled-in defaults: the table written by tune.py on MI355X (256 CUs,
 // 8 TB/s HBM3E); a row covers n >= min_n up to the next row.  blocks_per_cu
-// 1024 means one block per tile at every size used in practice.
+// 1024 means one block per tile at every size used in practice.  The
+// two-input operations have a third, mid-size row (2^22 <= n < 2^25) from a
+// sweep timed cold, where 512-thread tiles of two vectors per lane beat the
+// large shapes by 2-14 %.
 struct DefaultRow {
     int op;
     Row row;
 };
 constexpr DefaultRow kDefaults[] = {
     {kOpAddF32, {0, 512, 1, 2}},
-    {kOpAddF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpAddF32, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpAddF32, {size_t(1) << 25, 1024, 1024, 1}},
     {kOpAddF16, {0, 128, 2, 2}},
-    {kOpAddF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddF16, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpAddF16, {size_t(1) << 25, 128, 1024, 1}},
     {kOpAddBF16, {0, 256, 2, 2}},
-    {kOpAddBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddBF16, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpAddBF16, {size_t(1) << 25, 128, 1024, 1}},
     {kOpSaxpyF32, {0, 512, 1, 1}},
-    {kOpSaxpyF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpSaxpyF32, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpSaxpyF32, {size_t(1) << 25, 1024, 1024, 1}},
     {kOpReluF32, {0, 512, 8, 1}},
     {kOpReluF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpCopyF32, {0, 256, 8, 1}},
@@ -103,15 +110,19 @@ constexpr DefaultRow kDefaults[] = {
     {kOpGatherF32, {0, 128, 4, 1}},
     {kOpGatherF32, {size_t(1) << 22, 128, 1024, 1}},
     {kOpAddReluF32, {0, 512, 1024, 2}},
-    {kOpAddReluF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpAddReluF32, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpAddReluF32, {size_t(1) << 25, 1024, 1024, 1}},
     {kOpSaxpyReluF32, {0, 512, 4, 2}},
-    {kOpSaxpyReluF32, {size_t(1) << 22, 1024, 1024, 1}},
+    {kOpSaxpyReluF32, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpSaxpyReluF32, {size_t(1) << 25, 1024, 1024, 1}},
     {kOpBiasReluF32, {0, 1024, 1024, 1}},
     {kOpBiasReluF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpSaxpyF16, {0, 256, 1024, 4}},
-    {kOpSaxpyF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSaxpyF16, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpSaxpyF16, {size_t(1) << 25, 128, 1024, 1}},
     {kOpSaxpyBF16, {0, 128, 2, 2}},
-    {kOpSaxpyBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSaxpyBF16, {size_t(1) << 22, 512, 1024, 2}},
+    {kOpSaxpyBF16, {size_t(1) << 25, 128, 1024, 1}},
     {kOpReluF16, {0, 1024, 8, 1}},
     {kOpReluF16, {size_t(1) << 22, 128, 1024, 1}},
     {kOpReluBF16, {0, 128, 4, 2}},

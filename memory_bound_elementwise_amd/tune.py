@@ -121,7 +121,10 @@ def _time(launch, stream, launches, repeats, restore=None):
 
 
 def _set(op, block, bpc, unroll):
-    for m in (0, LARGE_MIN_N):
+    """Force one shape on every size class of op (every min_n of the loaded
+    table's rows, plus 0 and LARGE_MIN_N), so the timed size uses it."""
+    mins = {0, LARGE_MIN_N} | {r[0] for r in _read_rows(ew.LAUNCH_TABLE).get(op, [])}
+    for m in sorted(mins):
         ew.ew_set_launch_config(op, m, block, bpc, unroll)
 
 
@@ -207,7 +210,11 @@ def _read_rows(path):
 
 
 def write_table(best, path, merge_from=None):
-    """Write the table; ops not in `best` keep their rows from `merge_from`."""
+    """Write the table.  Ops not in `best` keep their rows from `merge_from`.
+    A tuned op gets its small row (min_n 0) and its large row, which replaces
+    the op's last existing row at or above LARGE_MIN_N (so a large row that
+    starts at 2^25, above a mid-size row, stays there); any other existing row
+    of the op -- a mid-size row measured cold by a separate sweep -- is kept."""
     dev = torch.cuda.get_device_name(0)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     old = _read_rows(merge_from) if merge_from else {}
@@ -221,10 +228,15 @@ def write_table(best, path, merge_from=None):
     ]
     for op in ew.OPS:
         if op in best:
-            for cls, min_n in (("small", 0), ("large", LARGE_MIN_N)):
+            kept = {r[0]: r for r in old.get(op, [])}
+            large_min = max((m for m in kept if m >= LARGE_MIN_N), default=LARGE_MIN_N)
+            rows = {m: r for m, r in kept.items() if m not in (0, large_min)}
+            for cls, min_n in (("small", 0), ("large", large_min)):
                 block, bpc, unroll, gbs = best[op][cls]
-                lines.append(f"{op:<15s} {min_n:<8d} {block:<5d} {bpc:<5d} {unroll:<2d} "
-                             f"# {gbs} GB/s")
+                rows[min_n] = (min_n, block, bpc, unroll, f"{gbs} GB/s")
+            for (min_n, block, bpc, unroll, comment) in (rows[m] for m in sorted(rows)):
+                tail = f" # {comment}" if comment else ""
+                lines.append(f"{op:<15s} {min_n:<8d} {block:<5d} {bpc:<5d} {unroll:<2d}{tail}")
         else:
             for (min_n, block, bpc, unroll, comment) in old.get(op, []):
                 tail = f" # {comment}" if comment else ""
