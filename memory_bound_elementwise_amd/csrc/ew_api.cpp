@@ -85,7 +85,9 @@ struct Row {
 // 1024 means one block per tile at every size used in practice.  The
 // two-input operations have a third, mid-size row (2^22 <= n < 2^25) from a
 // sweep timed cold, where 512-thread tiles of two vectors per lane beat the
-// large shapes by 2-14 %.
+// large shapes by 2-14 %.  The gather's rows apply to the length of the
+// segment its kernel computes (n / 2 for stride 2 and even n): 512-thread
+// tiles from 2^21, the large row from 2^25.
 struct DefaultRow {
     int op;
     Row row;
@@ -108,7 +110,8 @@ constexpr DefaultRow kDefaults[] = {
     {kOpCopyF32, {0, 256, 8, 1}},
     {kOpCopyF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpGatherF32, {0, 128, 4, 1}},
-    {kOpGatherF32, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpGatherF32, {size_t(1) << 21, 512, 1024, 1}},
+    {kOpGatherF32, {size_t(1) << 25, 128, 1024, 1}},
     {kOpAddReluF32, {0, 512, 1024, 2}},
     {kOpAddReluF32, {size_t(1) << 22, 512, 1024, 2}},
     {kOpAddReluF32, {size_t(1) << 25, 1024, 1024, 1}},
