@@ -426,42 +426,45 @@ bool in_place_second(int op)
 }
 
 // Items of one batched call must not race: an item's output range may not
-// intersect any range (input or output) of another item.  Ranges sorted by
-// start; each is compared with the earlier ones that are still open.
+// intersect any range (input or output) of another item.  Outputs and
+// inputs are each ordered by start -- already in order for the usual list of
+// consecutive arrays, then without sorting -- the outputs must be disjoint,
+// and one merge pass compares every input with the outputs that start
+// before it ends.
 ew_status_t batch_overlap(int op, const ew_batch_item_t *items, size_t count)
 {
     struct R {
         uintptr_t lo, hi;
         size_t item;
-        bool write;
     };
+    const auto by_lo = [](const R &x, const R &y) { return x.lo < y.lo; };
     const size_t es = (size_t)kOps[op].elem_size;
-    std::vector<R> rs;
-    rs.reserve(3 * count);
+    const bool two = kOps[op].inputs == 2 && !in_place_second(op);
+    std::vector<R> w, r;
+    w.reserve(count);
+    r.reserve(two ? 2 * count : count);
     for (size_t i = 0; i < count; ++i) {
         const ew_batch_item_t &it = items[i];
         if (it.n == 0) continue;
         const uintptr_t bytes = (uintptr_t)(it.n * es);
         const uintptr_t o = reinterpret_cast<uintptr_t>(it.out);
-        rs.push_back(R{o, o + bytes, i, true});
+        w.push_back(R{o, o + bytes, i});
         const uintptr_t a = reinterpret_cast<uintptr_t>(it.in0);
-        rs.push_back(R{a, a + bytes, i, false});
-        if (kOps[op].inputs == 2 && !in_place_second(op)) {
+        r.push_back(R{a, a + bytes, i});
+        if (two) {
             const uintptr_t b = reinterpret_cast<uintptr_t>(it.in1);
-            rs.push_back(R{b, b + bytes, i, false});
+            r.push_back(R{b, b + bytes, i});
         }
     }
-    std::sort(rs.begin(), rs.end(), [](const R &x, const R &y) { return x.lo < y.lo; });
-    std::vector<R> open;
-    for (const R &r : rs) {
-        size_t keep = 0;
-        for (const R &q : open) {
-            if (q.hi <= r.lo) continue;              // closed before r starts
-            if (q.item != r.item && (q.write || r.write)) return EW_ERR_OVERLAP;
-            open[keep++] = q;
-        }
-        open.resize(keep);
-        open.push_back(r);
+    if (!std::is_sorted(w.begin(), w.end(), by_lo)) std::sort(w.begin(), w.end(), by_lo);
+    if (!std::is_sorted(r.begin(), r.end(), by_lo)) std::sort(r.begin(), r.end(), by_lo);
+    for (size_t k = 1; k < w.size(); ++k)
+        if (w[k - 1].hi > w[k].lo) return EW_ERR_OVERLAP;
+    size_t j = 0;                                   // first output that may still meet an input
+    for (const R &in : r) {
+        while (j < w.size() && w[j].hi <= in.lo) ++j;   // ends before this (and every later) input
+        for (size_t k = j; k < w.size() && w[k].lo < in.hi; ++k)
+            if (w[k].item != in.item) return EW_ERR_OVERLAP;
     }
     return EW_OK;
 }
@@ -737,10 +740,15 @@ ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *it
             if (it.n == 0) continue;
             const void *in1 = kOps[op].inputs == 2 ? (in_place_second(op) ? it.out : it.in1)
                                                    : nullptr;
-            // the kernel recomputes this split from the same pointers and n
-            const Plan p = make_plan(op, it.out, it.in0, in1, it.n, cus);
+            // the single call's split (the kernel recomputes it from the same
+            // pointers and n): only the vector count decides the tiles
+            const size_t es = (size_t)kOps[op].elem_size;
+            const uintptr_t o = reinterpret_cast<uintptr_t>(it.out);
+            size_t head = ((16 - (o % 16)) % 16) / es;
+            if (head > it.n) head = it.n;
+            const uint64_t vectors = (it.n - head) / (16 / es);
             a.item[a.count] = BatchItem{it.in0, in1, it.out, (uint64_t)it.n};
-            uint64_t tiles = (p.vectors + tile_vecs - 1) / tile_vecs;
+            uint64_t tiles = (vectors + tile_vecs - 1) / tile_vecs;
             if (tiles == 0) tiles = 1;        // the head and tail still need a block
             a.tiles += tiles;
             a.tile_end[a.count] = a.tiles;
