@@ -20,7 +20,6 @@ persistent grid of that many blocks per compute unit.
 import argparse
 import itertools
 import json
-import os
 import statistics
 import sys
 

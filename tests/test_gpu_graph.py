@@ -7,7 +7,6 @@ The graph fixes the pointers, sizes and launch shapes at capture time; the
 data may change between replays.  Each replay here follows eager work that
 rewrites the inputs, and every replay is checked against the oracle.
 """
-import numpy as np
 import pytest
 import torch
 

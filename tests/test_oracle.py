@@ -6,7 +6,6 @@ rounding rule, an unfused SAXPY, a dropped NaN case, a signed-zero mistake,
 a wrong gather index) fails at least one of them.
 """
 import math
-import struct
 from fractions import Fraction
 
 import numpy as np
