@@ -4,7 +4,8 @@
  *
  * Plain C: no C++ or torch types.  Every operation takes device pointers, an
  * element count n and a HIP stream, validates its arguments on the host,
- * launches one kernel asynchronously on that stream and returns a status.
+ * launches one kernel asynchronously on that stream (a batched call: one per
+ * EW_BATCH_MAX items) and returns a status.
  *
  * Pages cited (by title and section):
  *   [HyperAI]   HyperAI article on optimising the Elementwise operator
