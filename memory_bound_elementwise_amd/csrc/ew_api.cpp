@@ -162,10 +162,18 @@ constexpr DefaultRow kDefaults[] = {
 
 constexpr int kMaxRows = 16;
 
+// Fixed capacity, so that no table operation allocates (or can throw).
+struct Rows {
+    Row row[kMaxRows];
+    int count = 0;
+    Row *begin() { return row; }
+    Row *end() { return row + count; }
+};
+
 struct Table {
     std::mutex mu;
     bool loaded = false;
-    std::vector<Row> rows[kOpCount];
+    Rows rows[kOpCount];
 };
 
 Table &table()
@@ -176,8 +184,11 @@ Table &table()
 
 void reset_locked(Table &t)
 {
-    for (auto &r : t.rows) r.clear();
-    for (const auto &d : kDefaults) t.rows[d.op].push_back(d.row);
+    for (auto &r : t.rows) r.count = 0;
+    for (const auto &d : kDefaults) {
+        Rows &r = t.rows[d.op];
+        if (r.count < kMaxRows) r.row[r.count++] = d.row;
+    }
     t.loaded = true;
 }
 
@@ -206,10 +217,12 @@ ew_status_t set_row(int op, size_t min_n, int block, int bpc, int unroll)
             return EW_OK;
         }
     }
-    if ((int)rows.size() >= kMaxRows) return EW_ERR_INVALID_ARG;
-    size_t pos = 0;
-    while (pos < rows.size() && rows[pos].min_n < min_n) ++pos;
-    rows.insert(rows.begin() + pos, Row{min_n, block, bpc, unroll});
+    if (rows.count >= kMaxRows) return EW_ERR_INVALID_ARG;
+    int pos = 0;
+    while (pos < rows.count && rows.row[pos].min_n < min_n) ++pos;
+    for (int k = rows.count; k > pos; --k) rows.row[k] = rows.row[k - 1];
+    rows.row[pos] = Row{min_n, block, bpc, unroll};
+    ++rows.count;
     return EW_OK;
 }
 
@@ -718,7 +731,12 @@ ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *it
         if (it.n > (size_t(1) << 62) - total) return EW_ERR_INVALID_ARG;
         total += it.n;
     }
-    ew_status_t st = batch_overlap(op, items, count);
+    ew_status_t st;
+    try {
+        st = batch_overlap(op, items, count);
+    } catch (...) {      // no exception crosses the C ABI (the check's vectors: 3 x count)
+        return EW_ERR_INVALID_ARG;
+    }
     if (st != EW_OK) return st;
     if (total == 0) return EW_OK;
     int cus = 0;
