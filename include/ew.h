@@ -259,8 +259,9 @@ typedef struct ew_batch_item {
  * launches on `stream` (items with n == 0 are skipped).  alpha is used by
  * the SAXPY, scale and add-scalar operations and ignored otherwise.  items:
  * a host array, read during the call only.
- * Errors: an unknown or non-batchable op name, or items == NULL with count >
- * 0, -> EW_ERR_INVALID_ARG; each item is validated like its single call
+ * Errors: an unknown or non-batchable op name, items == NULL with count >
+ * 0, or host memory for the overlap check (about 72 bytes per item) not
+ * available -> EW_ERR_INVALID_ARG; each item is validated like its single call
  * (first failing item's status); an item's output range intersecting any
  * range of another item -> EW_ERR_OVERLAP (the items run concurrently; reads
  * of shared inputs are fine).  count == 0 or all n == 0 -> EW_OK, no launch.
