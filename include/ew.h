@@ -19,8 +19,9 @@
  * Conventions shared by every operation
  * -------------------------------------
  * Memory      The caller owns every buffer (device memory, e.g. allocated by
- *             torch).  The library never allocates, frees or keeps a pointer
- *             after the call returns.
+ *             torch).  The library never allocates or frees device memory
+ *             and keeps no pointer after the call returns (ew_batch alone
+ *             takes transient host memory for its overlap check).
  * Layout      One-dimensional, contiguous, n elements.  Pointers need only
  *             element alignment (4 bytes for fp32, 2 bytes for 16-bit data);
  *             16-byte alignment is NOT required: the library peels a scalar
