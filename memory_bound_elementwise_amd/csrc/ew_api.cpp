@@ -85,7 +85,8 @@ struct Row {
 // 1024 means one block per tile at every size used in practice.  The
 // two-input operations have a third, mid-size row (2^22 <= n < 2^25) from a
 // sweep timed cold, where 512-thread tiles of two vectors per lane beat the
-// large shapes by 2-14 %.  The gather's rows apply to the length of the
+// large shapes by 2-14 %; the 16-bit one-input operations likewise take
+// 512-thread tiles from 2^22 to 2^26 (3-19 %).  The gather's rows apply to the length of the
 // segment its kernel computes (n / 2 for stride 2 and even n): 512-thread
 // tiles from 2^21, the large row from 2^25.
 struct DefaultRow {
@@ -127,9 +128,11 @@ constexpr DefaultRow kDefaults[] = {
     {kOpSaxpyBF16, {size_t(1) << 22, 512, 1024, 2}},
     {kOpSaxpyBF16, {size_t(1) << 25, 128, 1024, 1}},
     {kOpReluF16, {0, 1024, 8, 1}},
-    {kOpReluF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpReluF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpReluF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpReluBF16, {0, 128, 4, 2}},
-    {kOpReluBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpReluBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpReluBF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpCopy2dF32, {0, 256, 2, 2}},
     {kOpCopy2dF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpReluInplaceF32, {0, 1024, 1, 4}},
@@ -137,27 +140,35 @@ constexpr DefaultRow kDefaults[] = {
     {kOpScaleF32, {0, 256, 8, 1}},
     {kOpScaleF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpScaleF16, {0, 1024, 8, 1}},
-    {kOpScaleF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpScaleF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpScaleF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpScaleBF16, {0, 1024, 8, 1}},
-    {kOpScaleBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpScaleBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpScaleBF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpAddScalarF32, {0, 256, 8, 1}},
     {kOpAddScalarF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpAddScalarF16, {0, 1024, 8, 1}},
-    {kOpAddScalarF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddScalarF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpAddScalarF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpAddScalarBF16, {0, 1024, 8, 1}},
-    {kOpAddScalarBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAddScalarBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpAddScalarBF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpSqrtF32, {0, 256, 8, 1}},
     {kOpSqrtF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpSqrtF16, {0, 1024, 8, 1}},
-    {kOpSqrtF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSqrtF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpSqrtF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpSqrtBF16, {0, 1024, 8, 1}},
-    {kOpSqrtBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpSqrtBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpSqrtBF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpAbsF32, {0, 256, 8, 1}},
     {kOpAbsF32, {size_t(1) << 22, 256, 1024, 1}},
     {kOpAbsF16, {0, 1024, 8, 1}},
-    {kOpAbsF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAbsF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpAbsF16, {size_t(1) << 26, 128, 1024, 1}},
     {kOpAbsBF16, {0, 1024, 8, 1}},
-    {kOpAbsBF16, {size_t(1) << 22, 128, 1024, 1}},
+    {kOpAbsBF16, {size_t(1) << 22, 512, 1024, 1}},
+    {kOpAbsBF16, {size_t(1) << 26, 128, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
