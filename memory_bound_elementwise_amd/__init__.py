@@ -166,8 +166,14 @@ def _buf(x, es, n, role):
     """Device address of one buffer argument.  The C ABI sees only a pointer
     and n, so a tensor is checked here first: elements of the operation's
     width (es bytes), contiguous, at least n elements (a shorter tensor would
-    be read or written past its end), on a GPU.  Integers pass unchecked."""
-    if x is None or isinstance(x, int):
+    be read or written past its end), on a GPU.  Integers pass unchecked.
+    One condition on the fast path (this runs on every call, where the host
+    cost of a small launch is a few microseconds)."""
+    if x is None or type(x) is int:
+        return x
+    if x.is_cuda and x.element_size() == es and x.is_contiguous() and x.numel() >= n:
+        return x.data_ptr()
+    if isinstance(x, int):
         return x
     if x.element_size() != es:
         raise TypeError(f"{role}: {x.dtype} has {x.element_size()}-byte elements, "
@@ -176,9 +182,7 @@ def _buf(x, es, n, role):
         raise ValueError(f"{role}: the tensor is not contiguous")
     if x.numel() < n:
         raise ValueError(f"{role}: {x.numel()} elements, the call covers {n}")
-    if x.device.type != "cuda":
-        raise ValueError(f"{role}: the tensor is on {x.device}, not on a GPU")
-    return x.data_ptr()
+    raise ValueError(f"{role}: the tensor is on {x.device}, not on a GPU")
 
 
 def _numel(x, n):
@@ -339,7 +343,7 @@ def _view_src(x, sr, sc, rows, cols):
     if start + lo < 0 or start + hi >= size:
         raise ValueError(f"src: the view reaches elements {start + lo}..{start + hi} of a "
                          f"storage of {size}")
-    if x.device.type != "cuda":
+    if not x.is_cuda:
         raise ValueError(f"src: the tensor is on {x.device}, not on a GPU")
     return x.data_ptr()
 
