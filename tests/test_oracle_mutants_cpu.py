@@ -3,7 +3,9 @@ oracle/oracle.c with one deliberate slip (a wrong rounding tie rule, an
 unfused SAXPY, a ReLU that keeps -0, a gather index that wraps at 2^64, an
 approximate square root, an abs that rewrites NaN payloads, an add-scalar
 that rounds alpha to bfloat16 first, a bfloat16 narrowing that does not
-quiet NaNs), builds it with the oracle's own flags, points the oracle at the
+quiet NaNs, a binary16 overflow threshold at 65504, a widening that keeps
+signalling NaNs, a bias indexed by row, a view that ignores negative
+strides), builds it with the oracle's own flags, points the oracle at the
 copy and runs the pins that should notice: every one must fail.  The real
 oracle is restored afterwards.  CPU only; nothing here touches a GPU."""
 import os
@@ -46,6 +48,25 @@ MUTANTS = {
         "y[i] = oracle_f32_to_bf16(oracle_bf16_to_f32(x[i]) + "
         "oracle_bf16_to_f32(oracle_f32_to_bf16(alpha)));",
         [lambda: pins.test_scalar_maps16_vs_library_and_exact_rational("bf16")]),
+    # (moving the threshold by one ulp is no mistake: at exactly 65520 the
+    # normal path's rounding carries into the exponent and also gives inf)
+    "f16_overflow_threshold_at_65504": (
+        "if (a >= 0x477ff000u) {",
+        "if (a >= 0x477fe000u) {",
+        [pins.test_add_f16_overflow_threshold, pins.test_f16_rounding_closed_forms]),
+    "f16_widening_keeps_signalling_nans": (
+        "        if (m != 0) out |= 0x00400000u;",
+        "",
+        [pins.test_f16_widen_all_patterns]),
+    "bias_indexed_by_row": (
+        "y[r * cols + c] = relu1(x[r * cols + c] + bias[c]);",
+        "y[r * cols + c] = relu1(x[r * cols + c] + bias[r % cols]);",
+        [pins.test_bias_relu_vs_numpy_broadcast]),
+    "view_ignores_negative_strides": (
+        "d[r * cols + c] = s[(int64_t)r * stride_r + (int64_t)c * stride_c];",
+        "d[r * cols + c] = s[(int64_t)r * (stride_r < 0 ? -stride_r : stride_r) + "
+        "(int64_t)c * (stride_c < 0 ? -stride_c : stride_c)];",
+        [pins.test_copy2d_vs_numpy_strided_views]),
     "bf16_nan_not_quieted": (
         "return (uint16_t)((u >> 16) | 0x0040u);",
         "return (uint16_t)(u >> 16);",
