@@ -219,6 +219,7 @@ def saxpy_bf16(alpha, x, y):
 
 def _relu16(name, x):
     lib = _load()
+    _check_env(lib)     # the decision compares the widened value with 0 in binary32
     x = _as(x, np.uint16)
     y = np.empty_like(x)
     getattr(lib, name)(_ptr(x), _ptr(y), x.size)

@@ -508,6 +508,18 @@ def test_relu16_vs_library_maximum():
     assert np.all(got[zero] == 0) and np.array_equal(got[bf_nan], h[bf_nan])
 
 
+def test_relu16_keeps_positive_subnormals():
+    """Closed form at the edge a flushing environment would break: every
+    positive subnormal of both 16-bit formats (bfloat16 subnormals are
+    binary32 subnormals once widened) is kept bit for bit, every negative
+    one becomes +0."""
+    for fn, mant in ((oracle.relu_f16, 0x03FF), (oracle.relu_bf16, 0x007F)):
+        pos = np.arange(1, mant + 1, dtype=np.uint16)
+        neg = pos | np.uint16(0x8000)
+        assert np.array_equal(fn(pos), pos)
+        assert not np.any(fn(neg))
+
+
 def test_copy_bitwise_including_nan_payloads():
     g = np.random.Generator(np.random.PCG64(61))
     bits = g.integers(0, 1 << 32, size=1 << 16, dtype=np.uint64).astype(np.uint32)
