@@ -4,8 +4,9 @@
  *
  * Plain C: no C++ or torch types.  Every operation takes device pointers, an
  * element count n and a HIP stream, validates its arguments on the host,
- * launches one kernel asynchronously on that stream (a batched call: one per
- * EW_BATCH_MAX items) and returns a status.
+ * launches one kernel asynchronously on that stream (ew_batch: one per
+ * EW_BATCH_MAX items; ew_batch_run: one for any number) and returns a
+ * status.
  *
  * Pages cited (by title and section):
  *   [HyperAI]   HyperAI article on optimising the Elementwise operator
@@ -20,8 +21,9 @@
  * -------------------------------------
  * Memory      The caller owns every buffer (device memory, e.g. allocated by
  *             torch).  The library never allocates or frees device memory
- *             and keeps no pointer after the call returns (ew_batch alone
- *             takes transient host memory for its overlap check).
+ *             and keeps no pointer after the call returns (ew_batch and
+ *             ew_batch_build alone take transient host memory for their
+ *             overlap check).
  * Layout      One-dimensional, contiguous, n elements.  Pointers need only
  *             element alignment (4 bytes for fp32, 2 bytes for 16-bit data);
  *             16-byte alignment is NOT required: the library peels a scalar
@@ -123,7 +125,11 @@ ew_status_t ew_relu_f32(const float *x, float *y, size_t n, hipStream_t stream);
  * costs more than writing it whole).  The body is aligned to 64 bytes by a
  * scalar head of up to 15 elements.  x: 4-byte aligned.  Errors as for
  * ew_relu_f32.  On data whose every element is already >= 0 it moves half
- * the bytes of ew_relu_f32(x, x). */
+ * the bytes of ew_relu_f32(x, x).  When to prefer ew_relu_f32(x, x): data
+ * with mixed signs.  On normal(0, 1) data almost every 64-byte span holds a
+ * negative element, so nearly every span is written and the call moves the
+ * same bytes as ew_relu_f32(x, x) (measured on MI355X: 1.33 x the bytes it
+ * must move, and a few per cent slower than ew_relu_f32(x, x)). */
 ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t stream);
 
 /* out[i] = in[i], bit patterns unchanged (NaN payloads included).
@@ -139,6 +145,19 @@ ew_status_t ew_copy_f32(const float *in, float *out, size_t n,
  * in and out must not overlap at all. */
 ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
                           hipStream_t stream);
+
+/* The same result as ew_gather_f32 -- out[i] = in[(stride * i) mod n], bits
+ * unchanged -- computed the way the non-coalesced copy kernel of [PerfNotes]
+ * section 3.2 computes it: every output element loads its own input element
+ * (4-byte loads, index stepped per lane), whatever the stride, with none of
+ * ew_gather_f32's reuse (no replicated segments, no pass decomposition, no
+ * contiguous-span path).  For stride 2 on even n it reads the input twice
+ * (outputs i and i + n/2 read the same element).  It is the baseline against
+ * which the cost of strided reads is measured ([PerfNotes] 3.3).  Arguments,
+ * errors and launch rows ("gather_walk_f32") as for ew_gather_f32; stride 1
+ * also walks (no redirection to the copy). */
+ew_status_t ew_gather_walk_f32(const float *in, float *out, size_t n, size_t stride,
+                               hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Strided views                                                            */
@@ -271,6 +290,54 @@ typedef struct ew_batch_item {
 ew_status_t ew_batch(const char *op, float alpha, const ew_batch_item_t *items,
                      size_t count, hipStream_t stream);
 
+/* Batched calls with the item table in device memory: one kernel launch for
+ * any number of items.  The library builds the table image on the host
+ * (ew_batch_build, into memory the caller provides), the caller places it in
+ * device memory (any copy; it may be reused for every call on the same
+ * items), and ew_batch_run launches one kernel that reads it.  This is the
+ * form to use for many items and for repeated calls on the same arrays; it
+ * also suits graph capture (ew_batch_run makes no copy and allocates
+ * nothing).
+ *
+ * ew_batch_plan_t describes a built table; fill it only through
+ * ew_batch_build.  The launch shape is the table's row of the operation for
+ * the total element count (unroll at most 4); the grid is min(blocks_per_cu
+ * * CU count, tiles). */
+typedef struct ew_batch_plan {
+    int32_t op;             /* operation (library-internal number) */
+    int32_t block;          /* threads per block */
+    int32_t unroll;         /* 16-byte vectors per lane per tile */
+    int32_t blocks_per_cu;  /* grid cap per compute unit */
+    uint64_t items;         /* records in the table: the items with n > 0 */
+    uint64_t tiles;         /* tiles of all items together (one block each) */
+    uint64_t bytes;         /* size of the table image, a multiple of 8 */
+    uint64_t total_n;       /* elements of all items together */
+} ew_batch_plan_t;
+
+/* Validates items exactly as ew_batch does (same operations, same errors)
+ * and fills *plan.  With table == NULL it only sizes the image (plan->bytes)
+ * and returns EW_OK; otherwise it writes the image -- plan->items records of
+ * 40 bytes (in0, in1, out, n, first tile), then one 32-bit item index per
+ * tile, zero padded to plan->bytes -- into `table` (host memory, 8-byte
+ * aligned, table_bytes >= plan->bytes; EW_ERR_INVALID_ARG if smaller,
+ * EW_ERR_MISALIGNED if not 8-byte aligned).  No device is needed.  The
+ * image holds the items' device pointers: it stays valid while those
+ * buffers do. */
+ew_status_t ew_batch_build(const char *op, const ew_batch_item_t *items, size_t count,
+                           void *table, size_t table_bytes, ew_batch_plan_t *plan);
+
+/* Runs a built table in one kernel launch on `stream`: the result of
+ * ew_batch on the same items and alpha.  table: device memory (8-byte
+ * aligned) holding exactly the plan->bytes bytes that ew_batch_build wrote
+ * for this plan; the kernel trusts its pointers as every entry point trusts
+ * its buffers, so a table that was changed or built for other buffers is
+ * undefined behaviour.  The plan's fields are checked for consistency
+ * (EW_ERR_INVALID_ARG).  plan->tiles == 0 (no item with n > 0) -> EW_OK, no
+ * launch.  Calls on different streams may share one table (it is only
+ * read). */
+ew_status_t ew_batch_run(const ew_batch_plan_t *plan, float alpha, const void *table,
+                         hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Fused chains: one pass over memory instead of two                         */
 /* ------------------------------------------------------------------------ */
@@ -314,30 +381,50 @@ int ew_abi_version(void);
 
 /* Launch configuration, per operation name ("add_f32", "add_f16",
  * "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
- * "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16",
- * "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32",
- * "scale_f32", "scale_f16", "scale_bf16", "add_scalar_f32", "add_scalar_f16",
- * "add_scalar_bf16", "sqrt_f32", "sqrt_f16", "sqrt_bf16", "abs_f32",
- * "abs_f16", "abs_bf16") and size
- * class: a row applies to every n >= min_n up to the next row's min_n.  The
- * grid is min(blocks_per_cu * CU count, number of tiles), where a tile is
- * block * unroll 16-byte vectors; each block walks tiles with a grid stride
- * ([EwOps] optimisation point 2: a grid sized to the processor count).
- * block: a multiple of 64 in [64, 1024]; blocks_per_cu in [1, 1024];
- * unroll in {1, 2, 4, 8}.  Setting a row with an existing min_n replaces it.
- * Returns EW_ERR_INVALID_ARG for an unknown op or a value out of range. */
-ew_status_t ew_set_launch_config(const char *op, size_t min_n, int block,
-                                 int blocks_per_cu, int unroll);
+ * "gather_walk_f32", "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32",
+ * "saxpy_f16", "saxpy_bf16", "relu_f16", "relu_bf16", "copy2d_f32",
+ * "relu_inplace_f32", "scale_f32", "scale_f16", "scale_bf16",
+ * "add_scalar_f32", "add_scalar_f16", "add_scalar_bf16", "sqrt_f32",
+ * "sqrt_f16", "sqrt_bf16", "abs_f32", "abs_f16", "abs_bf16").
+ * A launch is `grid` blocks of `block` threads; each block walks tiles of
+ * block * unroll 16-byte vectors with a grid stride, and the grid is
+ * min(blocks_per_cu * CU count, number of tiles) ([EwOps] section 二,
+ * optimisation point 2: a grid sized to the processor count times a small
+ * factor).  block: a multiple of 64 in [64, 1024]; blocks_per_cu in
+ * [1, 1024]; unroll in {1, 2, 4, 8}.  Out of range or unknown op ->
+ * EW_ERR_INVALID_ARG.
+ *
+ * The table holds, per operation, rows for size classes (see
+ * ew_set_launch_row); the compiled-in rows were tuned on MI355X. */
+
+/* One launch configuration for every size of `op`: replaces all of op's
+ * rows with one row applying to every n. */
+ew_status_t ew_set_launch_config(const char *op, int block, int blocks_per_cu, int unroll);
+
+/* The launch the next call of `op` with n elements would make on the
+ * current device, for pointers 16-byte aligned (as device allocations are):
+ * threads per block, grid (0 when n == 0: no launch) and unroll.  For the
+ * gather this is the index walk's grid (ew_gather_walk_f32, or
+ * ew_gather_f32 at a stride > 8 coprime with n); ew_make_gather_plan gives
+ * the grid for a given stride.  Needs a device: EW_ERR_NO_DEVICE without
+ * one. */
+ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *grid, int *unroll);
+
+/* Size classes: a row applies to every n >= min_n up to the next row's
+ * min_n; setting a row with an existing min_n replaces it (at most 16 rows
+ * per operation, else EW_ERR_INVALID_ARG). */
+ew_status_t ew_set_launch_row(const char *op, size_t min_n, int block, int blocks_per_cu,
+                              int unroll);
 
 /* The row that applies to n (no device needed). */
-ew_status_t ew_get_launch_config(const char *op, size_t n, int *block,
-                                 int *blocks_per_cu, int *unroll);
+ew_status_t ew_get_launch_row(const char *op, size_t n, int *block, int *blocks_per_cu,
+                              int *unroll);
 
 /* Restore the compiled-in table (tuned on MI355X). */
 void ew_reset_launch_config(void);
 
 /* Read rows "op min_n block blocks_per_cu unroll" (one per line, '#'
- * comments) from a text file and apply them with ew_set_launch_config.
+ * comments) from a text file and apply them with ew_set_launch_row.
  * EW_ERR_INVALID_ARG on an unreadable file or a malformed row (rows before
  * it stay applied). */
 ew_status_t ew_load_launch_table(const char *path);

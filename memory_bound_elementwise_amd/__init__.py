@@ -23,14 +23,15 @@ import os
 __all__ = [
     "EwError", "EwPlan", "OPS", "library_path",
     "ew_add_f32", "ew_add_f16", "ew_add_bf16", "ew_saxpy_f32", "ew_relu_f32",
-    "ew_copy_f32", "ew_gather_f32", "ew_add_relu_f32", "ew_saxpy_relu_f32",
+    "ew_copy_f32", "ew_gather_f32", "ew_gather_walk_f32", "ew_add_relu_f32", "ew_saxpy_relu_f32",
     "ew_bias_relu_f32", "ew_saxpy_f16", "ew_saxpy_bf16", "ew_relu_f16", "ew_relu_bf16",
     "ew_copy2d_f32", "ew_scale_f32", "ew_scale_f16", "ew_scale_bf16", "ew_add_scalar_f32",
     "ew_add_scalar_f16", "ew_add_scalar_bf16", "ew_sqrt_f32", "ew_sqrt_f16", "ew_sqrt_bf16",
     "ew_abs_f32", "ew_abs_f16", "ew_abs_bf16", "ew_status_string", "ew_last_hip_error",
-    "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config",
-    "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan", "ew_make_gather_plan",
-    "ew_batch", "EwBatch", "EwBatchItem", "BATCH_MAX",
+    "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config", "ew_set_launch_row",
+    "ew_get_launch_row", "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan",
+    "ew_make_gather_plan", "ew_batch", "ew_batch_build", "ew_batch_run", "EwBatch",
+    "EwBatchItem", "EwBatchPlan", "BATCH_MAX",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -38,7 +39,7 @@ _LIB_PATH = os.path.join(_PKG, "libew.so")
 LAUNCH_TABLE = os.path.join(_PKG, "launch_table.txt")
 
 OPS = ("add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32", "gather_f32",
-       "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16", "saxpy_bf16",
+       "gather_walk_f32", "add_relu_f32", "saxpy_relu_f32", "bias_relu_f32", "saxpy_f16", "saxpy_bf16",
        "relu_f16", "relu_bf16", "copy2d_f32", "relu_inplace_f32",
        "scale_f32", "scale_f16", "scale_bf16", "add_scalar_f32", "add_scalar_f16",
        "add_scalar_bf16", "sqrt_f32", "sqrt_f16", "sqrt_bf16", "abs_f32", "abs_f16", "abs_bf16")
@@ -86,7 +87,15 @@ class EwBatchItem(ctypes.Structure):
     _fields_ = [("out", _vp), ("in0", _vp), ("in1", _vp), ("n", _sz)]
 
 
-BATCH_MAX = 96          # EW_BATCH_MAX: items per kernel launch
+class EwBatchPlan(ctypes.Structure):
+    """Mirror of ``ew_batch_plan_t``."""
+    _fields_ = [("op", ctypes.c_int32), ("block", ctypes.c_int32), ("unroll", ctypes.c_int32),
+                ("blocks_per_cu", ctypes.c_int32), ("items", ctypes.c_uint64),
+                ("tiles", ctypes.c_uint64), ("bytes", ctypes.c_uint64),
+                ("total_n", ctypes.c_uint64)]
+
+
+BATCH_MAX = 96          # EW_BATCH_MAX: items per kernel launch of ew_batch
 
 
 def _proto(name, restype, *argtypes):
@@ -105,6 +114,7 @@ _c = {
     "ew_relu_inplace_f32": _proto("ew_relu_inplace_f32", _int, _vp, _sz, _vp),
     "ew_copy_f32": _proto("ew_copy_f32", _int, _vp, _vp, _sz, _vp),
     "ew_gather_f32": _proto("ew_gather_f32", _int, _vp, _vp, _sz, _sz, _vp),
+    "ew_gather_walk_f32": _proto("ew_gather_walk_f32", _int, _vp, _vp, _sz, _sz, _vp),
     "ew_add_relu_f32": _proto("ew_add_relu_f32", _int, _vp, _vp, _vp, _sz, _vp),
     "ew_saxpy_relu_f32": _proto("ew_saxpy_relu_f32", _int, ctypes.c_float, _vp, _vp, _sz, _vp),
     "ew_bias_relu_f32": _proto("ew_bias_relu_f32", _int, _vp, _vp, _vp, _sz, _sz, _vp),
@@ -123,11 +133,21 @@ _c = {
     "ew_status_string": _proto("ew_status_string", ctypes.c_char_p, _int),
     "ew_last_hip_error": _proto("ew_last_hip_error", _int),
     "ew_abi_version": _proto("ew_abi_version", _int),
-    "ew_set_launch_config": _proto("ew_set_launch_config", _int, ctypes.c_char_p, _sz,
-                                   _int, _int, _int),
+    "ew_batch_build": _proto("ew_batch_build", _int, ctypes.c_char_p,
+                             ctypes.POINTER(EwBatchItem), _sz, _vp, _sz,
+                             ctypes.POINTER(EwBatchPlan)),
+    "ew_batch_run": _proto("ew_batch_run", _int, ctypes.POINTER(EwBatchPlan), ctypes.c_float,
+                           _vp, _vp),
+    "ew_set_launch_config": _proto("ew_set_launch_config", _int, ctypes.c_char_p, _int, _int,
+                                   _int),
     "ew_get_launch_config": _proto("ew_get_launch_config", _int, ctypes.c_char_p, _sz,
                                    ctypes.POINTER(_int), ctypes.POINTER(_int),
                                    ctypes.POINTER(_int)),
+    "ew_set_launch_row": _proto("ew_set_launch_row", _int, ctypes.c_char_p, _sz, _int, _int,
+                                _int),
+    "ew_get_launch_row": _proto("ew_get_launch_row", _int, ctypes.c_char_p, _sz,
+                                ctypes.POINTER(_int), ctypes.POINTER(_int),
+                                ctypes.POINTER(_int)),
     "ew_reset_launch_config": _proto("ew_reset_launch_config", None),
     "ew_load_launch_table": _proto("ew_load_launch_table", _int, ctypes.c_char_p),
     "ew_make_plan": _proto("ew_make_plan", _int, ctypes.c_char_p, _vp, _vp, _vp, _sz, _int,
@@ -257,6 +277,14 @@ def ew_gather_f32(src, out, stride, n=None, stream=None):
     n = _numel(out, n)
     _check(_c["ew_gather_f32"](_buf(src, 4, n, "src"), _buf(out, 4, n, "out"), n, int(stride),
                                _stream(out, stream)), "ew_gather_f32")
+
+
+def ew_gather_walk_f32(src, out, stride, n=None, stream=None):
+    """out[i] = src[(stride * i) mod n], bitwise, one input load per output
+    element (the per-output index walk, no reuse)."""
+    n = _numel(out, n)
+    _check(_c["ew_gather_walk_f32"](_buf(src, 4, n, "src"), _buf(out, 4, n, "out"), n,
+                                    int(stride), _stream(out, stream)), "ew_gather_walk_f32")
 
 
 def ew_add_relu_f32(a, b, c, n=None, stream=None):
@@ -424,42 +452,93 @@ def ew_abs_bf16(x, y, n=None, stream=None):
     _unary_map("ew_abs_bf16", x, y, n, stream)
 
 
-class EwBatch:
-    """A batched call prepared once: the tensors are checked and the C item
-    array is built at construction, so each call -- ``batch(alpha, stream)``
-    -- goes straight to ``ew_batch`` (which still validates every item).
-    items: a sequence of (out, in0, in1, n) with the single call's pointers
-    (in1 None for one-input operations and SAXPY; n None for out's numel()).
-    The tensors must stay alive while the batch is used."""
+def _batch_items(op, items):
+    """The C item array of a batch (tensors checked), and the first tensor
+    given as an output (for the default stream and device)."""
+    es = 4 if op.endswith("_f32") else 2
+    arr = (EwBatchItem * max(len(items), 1))()
+    first = None
+    for k, (out, in0, in1, n) in enumerate(items):
+        n = _numel(out, n)
+        arr[k] = EwBatchItem(
+            _buf(out, es, n, f"items[{k}].out"), _buf(in0, es, n, f"items[{k}].in0"),
+            _buf(in1, es, n, f"items[{k}].in1") if in1 is not None else None, n)
+        if first is None and not isinstance(out, int):
+            first = out
+    return arr, first
 
-    def __init__(self, op, items):
-        es = 4 if op.endswith("_f32") else 2
+
+def ew_batch_build(op, items):
+    """Validate a batch and build its table image on the host: returns
+    (EwBatchPlan, image) with the image as a ctypes array of plan.bytes
+    bytes (8-byte aligned).  items as for EwBatch."""
+    arr, _ = _batch_items(op, items)
+    plan = EwBatchPlan()
+    _check(_c["ew_batch_build"](op.encode(), arr, len(items), None, 0, ctypes.byref(plan)),
+           "ew_batch_build")
+    image = (ctypes.c_uint64 * max(1, plan.bytes // 8))()
+    _check(_c["ew_batch_build"](op.encode(), arr, len(items), ctypes.addressof(image),
+                                ctypes.sizeof(image), ctypes.byref(plan)), "ew_batch_build")
+    return plan, image
+
+
+def ew_batch_run(plan, alpha, table, stream=None):
+    """One launch of a built batch; table: a device tensor (or address)
+    holding the image ew_batch_build returned."""
+    s = _stream(table, stream) if not isinstance(table, int) else stream
+    if s is not None and not isinstance(s, int):
+        s = s.cuda_stream
+    _check(_c["ew_batch_run"](ctypes.byref(plan), float(alpha), _addr(table), s),
+           "ew_batch_run")
+
+
+class EwBatch:
+    """A batched call prepared once.  items: a sequence of (out, in0, in1, n)
+    with the single call's pointers (in1 None for one-input operations and
+    SAXPY; n None for out's numel()); the tensors must stay alive while the
+    batch is used.
+
+    table=True (default): the library builds the item table once
+    (ew_batch_build), it is copied to a device tensor on the first output's
+    device, and each call -- ``batch(alpha, stream)`` -- is one
+    ``ew_batch_run`` launch, however many items.  table=False: each call
+    passes the host item array to ``ew_batch`` (one launch per BATCH_MAX
+    items; the items are validated on every call)."""
+
+    def __init__(self, op, items, table=True):
         self.op = op
         self._op = op.encode()
         self.count = len(items)
-        self._arr = (EwBatchItem * max(self.count, 1))()
-        self._first = None
-        for k, (out, in0, in1, n) in enumerate(items):
-            n = _numel(out, n)
-            self._arr[k] = EwBatchItem(
-                _buf(out, es, n, f"items[{k}].out"), _buf(in0, es, n, f"items[{k}].in0"),
-                _buf(in1, es, n, f"items[{k}].in1") if in1 is not None else None, n)
-            if self._first is None and not isinstance(out, int):
-                self._first = out
+        self._arr, self._first = _batch_items(op, items)
+        self.plan = self.table = None
+        if table:
+            plan, image = ew_batch_build(op, items)
+            self.plan = plan
+            if plan.tiles:
+                if self._first is None:
+                    raise ValueError("table=True needs tensor outputs (for the table's device)")
+                host = torch.frombuffer(bytearray(image), dtype=torch.uint8)[:plan.bytes]
+                self.table = host.to(self._first.device)
 
     def __call__(self, alpha=0.0, stream=None):
         s = _stream(self._first, stream) if self._first is not None else stream
         if s is not None and not isinstance(s, int):
             s = s.cuda_stream
+        if self.plan is not None:
+            if self.plan.tiles:
+                _check(_c["ew_batch_run"](ctypes.byref(self.plan), float(alpha),
+                                          self.table.data_ptr(), s), "ew_batch_run")
+            return
         _check(_c["ew_batch"](self._op, float(alpha), self._arr, self.count, s), "ew_batch")
 
 
 def ew_batch(op, items, alpha=0.0, stream=None):
-    """Independent instances of one streaming operation in ceil(len(items) /
-    BATCH_MAX) launches (see EwBatch for items; prepare an EwBatch once to
-    call the same batch repeatedly without re-marshalling).  stream defaults
-    to torch's current stream on the first tensor's device."""
-    EwBatch(op, items)(alpha, stream)
+    """Independent instances of one streaming operation through the host-array
+    entry point, in ceil(len(items) / BATCH_MAX) launches (see EwBatch for
+    items; EwBatch(op, items) builds a device table once and runs any number
+    of items in one launch per call).  stream defaults to torch's current
+    stream on the first tensor's device."""
+    EwBatch(op, items, table=False)(alpha, stream)
 
 
 def ew_status_string(status: int) -> str:
@@ -474,16 +553,32 @@ def ew_abi_version() -> int:
     return _c["ew_abi_version"]()
 
 
-def ew_set_launch_config(op, min_n, block, blocks_per_cu, unroll):
-    _check(_c["ew_set_launch_config"](op.encode(), int(min_n), int(block), int(blocks_per_cu),
-                                      int(unroll)), "ew_set_launch_config")
+def ew_set_launch_config(op, block, blocks_per_cu, unroll):
+    """One launch configuration for every size of op (replaces its rows)."""
+    _check(_c["ew_set_launch_config"](op.encode(), int(block), int(blocks_per_cu), int(unroll)),
+           "ew_set_launch_config")
 
 
 def ew_get_launch_config(op, n):
+    """(block, grid, unroll) of the launch the next call of op with n
+    elements makes on the current device (16-byte-aligned pointers)."""
+    b, g, u = _int(), _int(), _int()
+    _check(_c["ew_get_launch_config"](op.encode(), int(n), ctypes.byref(b), ctypes.byref(g),
+                                      ctypes.byref(u)), "ew_get_launch_config")
+    return b.value, g.value, u.value
+
+
+def ew_set_launch_row(op, min_n, block, blocks_per_cu, unroll):
+    """Set the size-class row of op that applies from min_n elements."""
+    _check(_c["ew_set_launch_row"](op.encode(), int(min_n), int(block), int(blocks_per_cu),
+                                   int(unroll)), "ew_set_launch_row")
+
+
+def ew_get_launch_row(op, n):
     """(block, blocks_per_cu, unroll) of the row that applies to n."""
     b, k, u = _int(), _int(), _int()
-    _check(_c["ew_get_launch_config"](op.encode(), int(n), ctypes.byref(b), ctypes.byref(k),
-                                      ctypes.byref(u)), "ew_get_launch_config")
+    _check(_c["ew_get_launch_row"](op.encode(), int(n), ctypes.byref(b), ctypes.byref(k),
+                                   ctypes.byref(u)), "ew_get_launch_row")
     return b.value, k.value, u.value
 
 

@@ -23,7 +23,9 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libew.so")
 ARCH = "gfx950"
 
-SOURCES = [os.path.join(CSRC, "ew_api.cpp"), os.path.join(CSRC, "ew_kernels.hip")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in
+                  ("ew_stream.hip", "ew_batch.hip", "ew_gather.hip", "ew_view.hip")]
+SOURCES = [os.path.join(CSRC, "ew_api.cpp"), *KERNEL_SOURCES]
 
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 COMMON_FLAGS = [
@@ -62,12 +64,20 @@ def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
 
 
 def device_asm(dest_dir: str, verbose: bool = False, extra_flags=()) -> str:
-    """Write the gfx950 assembly of the kernels to ``dest_dir``; returns its path."""
+    """Write the gfx950 assembly of every kernel source to ``dest_dir``, one
+    file per source plus their concatenation; returns the concatenation's path."""
     os.makedirs(dest_dir, exist_ok=True)
+    parts = []
+    for src in KERNEL_SOURCES:
+        stem = os.path.splitext(os.path.basename(src))[0]
+        path = os.path.join(dest_dir, f"{stem}-{ARCH}.s")
+        cmd = [hipcc(), *COMMON_FLAGS, *extra_flags, "--cuda-device-only", "-S", "-o", path, src]
+        _run(cmd, verbose)
+        with open(path) as f:
+            parts.append(f.read())
     path = os.path.join(dest_dir, f"ew_kernels-{ARCH}.s")
-    cmd = [hipcc(), *COMMON_FLAGS, *extra_flags, "--cuda-device-only", "-S", "-o", path,
-           os.path.join(CSRC, "ew_kernels.hip")]
-    _run(cmd, verbose)
+    with open(path, "w") as f:
+        f.write("\n".join(parts))
     return path
 
 

@@ -20,7 +20,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 
 struct OpInfo {
     const char *name;
@@ -59,6 +59,7 @@ constexpr OpInfo kOps[kOpCount] = {
     {"abs_f32", 4, 1, true, 16},
     {"abs_f16", 2, 1, true, 16},
     {"abs_bf16", 2, 1, true, 16},
+    {"gather_walk_f32", 4, 1, false, 16},
 };
 
 int op_from_name(const char *name)
@@ -169,6 +170,9 @@ constexpr DefaultRow kDefaults[] = {
     {kOpAbsBF16, {0, 1024, 8, 1}},
     {kOpAbsBF16, {size_t(1) << 22, 512, 1024, 1}},
     {kOpAbsBF16, {size_t(1) << 26, 128, 1024, 1}},
+    {kOpGatherWalkF32, {0, 128, 4, 1}},
+    {kOpGatherWalkF32, {size_t(1) << 21, 512, 1024, 1}},
+    {kOpGatherWalkF32, {size_t(1) << 25, 128, 1024, 1}},
 };
 
 constexpr int kMaxRows = 16;
@@ -361,7 +365,7 @@ Plan make_plan(int op, const void *out, const void *in0, const void *in1, size_t
     const void *ins[2] = {in0, info.inputs == 2 ? in1 : nullptr};
     for (int k = 0; k < 2; ++k) {
         p.co[k] = true;
-        if (op != kOpGatherF32 && ins[k])
+        if (op != kOpGatherF32 && op != kOpGatherWalkF32 && ins[k])
             p.co[k] = (reinterpret_cast<uintptr_t>(ins[k]) + head * es) % 16 == 0;
     }
     const Row r = get_row(op, n);
@@ -434,6 +438,7 @@ bool batchable(int op)
 {
     switch (op) {
     case kOpGatherF32:
+    case kOpGatherWalkF32:
     case kOpBiasReluF32:
     case kOpCopy2dF32:
     case kOpReluInplaceF32: return false;
@@ -507,12 +512,16 @@ uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
 // then fetched once instead of g times.  For g == 1 and a stride of 2 to 8
 // the output splits into `stride` passes that together read the input
 // contiguously (see GatherArgs).  Otherwise one segment of n.
+//
+// walk: the per-output index walk whatever the stride (no pass decomposition
+// and no replicated segments: every output element loads its own input
+// element), with the launch rows of gather_walk_f32.
 void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, GatherArgs *g,
-                 Launch *l, int *blocks_per_cu = nullptr)
+                 Launch *l, int *blocks_per_cu = nullptr, bool walk = false)
 {
     const uint64_t s = stride % n;
     const uint64_t gcd = std::gcd(s, (uint64_t)n);  // gcd(0, n) == n
-    if (gcd == 1 && s >= 2 && s <= 8) {
+    if (!walk && gcd == 1 && s >= 2 && s <= 8) {
         // Pass decomposition: output pass k (floor(s*i/n) == k) starts at
         // i_k = ceil(k*n/s) and reads in[s*m + r_k], r_k = s*i_k - k*n; the
         // r_k are distinct because gcd(s, n) == 1.
@@ -544,11 +553,11 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
         return;
     }
     uint64_t reps = 1, seg = n;
-    if (gcd >= 2 && gcd <= 8 && (n / gcd) % 4 == 0) {
+    if (!walk && gcd >= 2 && gcd <= 8 && (n / gcd) % 4 == 0) {
         reps = gcd;
         seg = n / gcd;
     }
-    const Plan p = make_plan(kOpGatherF32, out, in, nullptr, seg, cus);
+    const Plan p = make_plan(walk ? kOpGatherWalkF32 : kOpGatherF32, out, in, nullptr, seg, cus);
     *g = GatherArgs{};
     g->in = reinterpret_cast<const uint32_t *>(in);
     g->out = reinterpret_cast<uint32_t *>(out);
@@ -629,6 +638,24 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride, 
     gather_plan(in, out, n, stride, cus, &g, &l);
     log_launch("gather_f32", n, g.head, g.vectors, g.tail, l,
                g.passes ? "passes" : g.reps > 1 ? "replicated segments" : "index walk");
+    const hipError_t e = launch_gather(g, l, s);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
+}
+
+ew_status_t ew_gather_walk_f32(const float *in, float *out, size_t n, size_t stride,
+                               hipStream_t s)
+{
+    if (n == 0) return EW_OK;
+    if (stride == 0) return EW_ERR_INVALID_ARG;
+    ew_status_t st = validate(kOpGatherWalkF32, out, in, nullptr, n);
+    if (st != EW_OK) return st;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    GatherArgs g{};
+    Launch l{};
+    gather_plan(in, out, n, stride, cus, &g, &l, nullptr, true);
+    log_launch("gather_walk_f32", n, g.head, g.vectors, g.tail, l, "index walk");
     const hipError_t e = launch_gather(g, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
@@ -725,6 +752,75 @@ ew_status_t ew_abs_bf16(const uint16_t *x, uint16_t *y, size_t n, hipStream_t s)
     return run_stream(kOpAbsBF16, y, x, nullptr, n, 0.0f, s);
 }
 
+}  // extern "C"
+
+namespace ew {
+namespace {
+
+// Validation shared by the batched entry points: every item (n > 0) as its
+// single call, the sum of n below 2^62, and no output range intersecting a
+// range of another item.  *total = the sum of n.
+ew_status_t batch_validate(int op, const ew_batch_item_t *items, size_t count, size_t *total)
+{
+    size_t sum = 0;
+    for (size_t i = 0; i < count; ++i) {
+        const ew_batch_item_t &it = items[i];
+        if (it.n == 0) continue;
+        const void *in1 = in_place_second(op) ? it.out : it.in1;
+        const ew_status_t st = validate(op, it.out, it.in0, in1, it.n);
+        if (st != EW_OK) return st;
+        if (it.n > (size_t(1) << 62) - sum) return EW_ERR_INVALID_ARG;
+        sum += it.n;
+    }
+    ew_status_t st;
+    try {
+        st = batch_overlap(op, items, count);
+    } catch (...) {      // no exception crosses the C ABI (the check's vectors: 3 x count)
+        return EW_ERR_INVALID_ARG;
+    }
+    *total = sum;
+    return st;
+}
+
+// The launch row of a batched call: the table's row for the total element
+// count, unroll at most 4.
+Row batch_row(int op, size_t total)
+{
+    Row r = get_row(op, total);
+    if (r.unroll > 4) r.unroll = 4;
+    return r;
+}
+
+// Tiles of one item (n > 0) under tiles of tile_vecs vectors: the single
+// call's vector count decides them (the kernel recomputes the split from the
+// same pointer and n); at least one, for the scalar head and tail.
+uint64_t item_tiles(int op, const ew_batch_item_t &it, uint64_t tile_vecs)
+{
+    const size_t es = (size_t)kOps[op].elem_size;
+    const uintptr_t o = reinterpret_cast<uintptr_t>(it.out);
+    size_t head = ((16 - (o % 16)) % 16) / es;
+    if (head > it.n) head = it.n;
+    const uint64_t vectors = (it.n - head) / (16 / es);
+    const uint64_t tiles = (vectors + tile_vecs - 1) / tile_vecs;
+    return tiles ? tiles : 1;
+}
+
+// Bytes of a table image with `items` records and `tiles` tile entries
+// (8-byte multiple), or 0 if that does not fit in size_t.
+size_t table_image_bytes(uint64_t items, uint64_t tiles)
+{
+    const uint64_t rec = (uint64_t)sizeof(BatchTableItem);
+    if (items > (SIZE_MAX / 2) / rec) return 0;
+    const uint64_t head = items * rec;
+    if (tiles > (SIZE_MAX / 2 - head) / 4) return 0;
+    return (size_t)((head + 4 * tiles + 7) & ~uint64_t(7));
+}
+
+}  // namespace
+}  // namespace ew
+
+extern "C" {
+
 ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *items,
                      size_t count, hipStream_t s)
 {
@@ -733,31 +829,15 @@ ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *it
     if (count == 0) return EW_OK;
     if (!items) return EW_ERR_INVALID_ARG;
     size_t total = 0;
-    for (size_t i = 0; i < count; ++i) {
-        const ew_batch_item_t &it = items[i];
-        if (it.n == 0) continue;
-        const void *in1 = in_place_second(op) ? it.out : it.in1;
-        const ew_status_t st = validate(op, it.out, it.in0, in1, it.n);
-        if (st != EW_OK) return st;
-        if (it.n > (size_t(1) << 62) - total) return EW_ERR_INVALID_ARG;
-        total += it.n;
-    }
-    ew_status_t st;
-    try {
-        st = batch_overlap(op, items, count);
-    } catch (...) {      // no exception crosses the C ABI (the check's vectors: 3 x count)
-        return EW_ERR_INVALID_ARG;
-    }
+    ew_status_t st = batch_validate(op, items, count, &total);
     if (st != EW_OK) return st;
     if (total == 0) return EW_OK;
     int cus = 0;
     st = current_device(&cus);
     if (st != EW_OK) return st;
-    // One launch shape for the whole call: the table's row for the total
-    // element count (unroll at most 4).
-    const Row r = get_row(op, total);
-    const int unroll = r.unroll > 4 ? 4 : r.unroll;
-    const uint64_t tile_vecs = (uint64_t)r.block * (uint64_t)unroll;
+    // One launch shape for the whole call.
+    const Row r = batch_row(op, total);
+    const uint64_t tile_vecs = (uint64_t)r.block * (uint64_t)r.unroll;
     BatchArgs a{};
     a.alpha = alpha;
     size_t i = 0;
@@ -769,30 +849,106 @@ ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *it
             if (it.n == 0) continue;
             const void *in1 = kOps[op].inputs == 2 ? (in_place_second(op) ? it.out : it.in1)
                                                    : nullptr;
-            // the single call's split (the kernel recomputes it from the same
-            // pointers and n): only the vector count decides the tiles
-            const size_t es = (size_t)kOps[op].elem_size;
-            const uintptr_t o = reinterpret_cast<uintptr_t>(it.out);
-            size_t head = ((16 - (o % 16)) % 16) / es;
-            if (head > it.n) head = it.n;
-            const uint64_t vectors = (it.n - head) / (16 / es);
             a.item[a.count] = BatchItem{it.in0, in1, it.out, (uint64_t)it.n};
-            uint64_t tiles = (vectors + tile_vecs - 1) / tile_vecs;
-            if (tiles == 0) tiles = 1;        // the head and tail still need a block
-            a.tiles += tiles;
+            a.tiles += item_tiles(op, it, tile_vecs);
             a.tile_end[a.count] = a.tiles;
             ++a.count;
         }
         if (a.count == 0) break;
         uint64_t grid = (uint64_t)r.blocks_per_cu * (uint64_t)(cus > 0 ? cus : 1);
         if (grid > a.tiles) grid = a.tiles;
-        const Launch l{r.block, (int)grid, unroll};
+        const Launch l{r.block, (int)grid, r.unroll};
         log_launch(kOps[op].name, (size_t)a.count, 0, a.tiles, 0, l,
                    "batch (n = items, vectors = tiles)");
         const hipError_t e = launch_batch(static_cast<OpId>(op), a, l, s);
         if (e != hipSuccess) return fail_hip(e);
     }
     return EW_OK;
+}
+
+ew_status_t ew_batch_build(const char *op_name, const ew_batch_item_t *items, size_t count,
+                           void *table, size_t table_bytes, ew_batch_plan_t *plan)
+{
+    if (!plan) return EW_ERR_INVALID_ARG;
+    std::memset(plan, 0, sizeof *plan);
+    const int op = op_from_name(op_name);
+    if (op < 0 || !batchable(op)) return EW_ERR_INVALID_ARG;
+    if (count > 0 && !items) return EW_ERR_INVALID_ARG;
+    size_t total = 0;
+    ew_status_t st = batch_validate(op, items, count, &total);
+    if (st != EW_OK) return st;
+    const Row r = batch_row(op, total);
+    const uint64_t tile_vecs = (uint64_t)r.block * (uint64_t)r.unroll;
+    uint64_t live = 0, tiles = 0;
+    for (size_t i = 0; i < count; ++i) {
+        if (items[i].n == 0) continue;
+        ++live;
+        tiles += item_tiles(op, items[i], tile_vecs);
+    }
+    if (live > UINT32_MAX) return EW_ERR_INVALID_ARG;   // item indices are 32-bit
+    const size_t bytes = table_image_bytes(live, tiles);
+    if (live > 0 && bytes == 0) return EW_ERR_INVALID_ARG;
+    plan->op = op;
+    plan->block = r.block;
+    plan->unroll = r.unroll;
+    plan->blocks_per_cu = r.blocks_per_cu;
+    plan->items = live;
+    plan->tiles = tiles;
+    plan->bytes = bytes;
+    plan->total_n = total;
+    if (!table) return EW_OK;                           // size query
+    if (table_bytes < bytes) return EW_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(table) % 8 != 0) return EW_ERR_MISALIGNED;
+    BatchTableItem *rec = static_cast<BatchTableItem *>(table);
+    uint32_t *tile_item = reinterpret_cast<uint32_t *>(static_cast<char *>(table) +
+                                                       live * sizeof(BatchTableItem));
+    uint64_t k = 0, t = 0;
+    for (size_t i = 0; i < count; ++i) {
+        const ew_batch_item_t &it = items[i];
+        if (it.n == 0) continue;
+        const void *in1 = kOps[op].inputs == 2 ? (in_place_second(op) ? it.out : it.in1)
+                                               : nullptr;
+        const uint64_t nt = item_tiles(op, it, tile_vecs);
+        rec[k] = BatchTableItem{it.in0, in1, it.out, (uint64_t)it.n, t};
+        for (uint64_t q = 0; q < nt; ++q) tile_item[t + q] = (uint32_t)k;
+        t += nt;
+        ++k;
+    }
+    // the padding word, if any, is defined too
+    const size_t used = live * sizeof(BatchTableItem) + 4 * tiles;
+    if (bytes > used) std::memset(static_cast<char *>(table) + used, 0, bytes - used);
+    return EW_OK;
+}
+
+ew_status_t ew_batch_run(const ew_batch_plan_t *plan, float alpha, const void *table,
+                         hipStream_t s)
+{
+    if (!plan) return EW_ERR_INVALID_ARG;
+    if (plan->tiles == 0) return EW_OK;
+    if (!table) return EW_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(table) % 8 != 0) return EW_ERR_MISALIGNED;
+    const int op = plan->op;
+    if (op < 0 || op >= kOpCount || !batchable(op) ||
+        !valid_row(plan->block, plan->blocks_per_cu, plan->unroll) || plan->unroll > 4 ||
+        plan->items == 0 || plan->items > UINT32_MAX || plan->tiles < plan->items ||
+        plan->bytes != table_image_bytes(plan->items, plan->tiles))
+        return EW_ERR_INVALID_ARG;
+    int cus = 0;
+    const ew_status_t st = current_device(&cus);
+    if (st != EW_OK) return st;
+    uint64_t grid = (uint64_t)plan->blocks_per_cu * (uint64_t)cus;
+    if (grid > plan->tiles) grid = plan->tiles;
+    const Launch l{plan->block, (int)grid, plan->unroll};
+    BatchTableArgs a{};
+    a.item = static_cast<const BatchTableItem *>(table);
+    a.tile_item = reinterpret_cast<const uint32_t *>(static_cast<const char *>(table) +
+                                                     plan->items * sizeof(BatchTableItem));
+    a.tiles = plan->tiles;
+    a.alpha = alpha;
+    log_launch(kOps[op].name, (size_t)plan->items, 0, plan->tiles, 0, l,
+               "batch table (n = items, vectors = tiles)");
+    const hipError_t e = launch_batch_table(static_cast<OpId>(op), a, l, s);
+    return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
 ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)
@@ -980,14 +1136,49 @@ int ew_last_hip_error(void) { return g_last_hip_error; }
 
 int ew_abi_version(void) { return kAbiVersion; }
 
-ew_status_t ew_set_launch_config(const char *op, size_t min_n, int block, int blocks_per_cu,
-                                 int unroll)
+ew_status_t ew_set_launch_config(const char *op, int block, int blocks_per_cu, int unroll)
+{
+    const int id = op_from_name(op);
+    if (id < 0 || !valid_row(block, blocks_per_cu, unroll)) return EW_ERR_INVALID_ARG;
+    Table &t = table();
+    std::lock_guard<std::mutex> g(t.mu);
+    ensure_loaded_locked(t);
+    Rows &rows = t.rows[id];
+    rows.count = 1;
+    rows.row[0] = Row{0, block, blocks_per_cu, unroll};
+    return EW_OK;
+}
+
+ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *grid, int *unroll)
+{
+    const int id = op_from_name(op);
+    if (id < 0 || !block || !grid || !unroll) return EW_ERR_INVALID_ARG;
+    int cus = 0;
+    const ew_status_t st = current_device(&cus);
+    if (st != EW_OK) return st;
+    // the plan of a call whose pointers are all 256-byte aligned (what a
+    // device allocation returns): no head, so only n decides the grid
+    const Row r = get_row(id, n);
+    const size_t es = (size_t)kOps[id].elem_size;
+    const size_t tile_vecs = (size_t)r.block * (size_t)r.unroll;
+    const size_t tiles = (n / (16 / es) + tile_vecs - 1) / tile_vecs;
+    size_t g = (size_t)r.blocks_per_cu * (size_t)cus;
+    if (g > tiles) g = tiles;
+    if (g == 0 && n > 0) g = 1;  // a head or tail still needs one block
+    *block = r.block;
+    *grid = (int)g;
+    *unroll = r.unroll;
+    return EW_OK;
+}
+
+ew_status_t ew_set_launch_row(const char *op, size_t min_n, int block, int blocks_per_cu,
+                              int unroll)
 {
     return set_row(op_from_name(op), min_n, block, blocks_per_cu, unroll);
 }
 
-ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *blocks_per_cu,
-                                 int *unroll)
+ew_status_t ew_get_launch_row(const char *op, size_t n, int *block, int *blocks_per_cu,
+                              int *unroll)
 {
     const int id = op_from_name(op);
     if (id < 0 || !block || !blocks_per_cu || !unroll) return EW_ERR_INVALID_ARG;

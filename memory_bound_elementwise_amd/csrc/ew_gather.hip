@@ -1,0 +1,304 @@
+// ew_gather.hip -- the strided gather out[i] = in[(s * i) mod n] for CDNA4
+// (gfx950): a per-output index walk, replicated segments, a pass
+// decomposition for small strides coprime with n (input staged through LDS)
+// and a stride-2 kernel reading contiguous spans.
+
+#include "ew_device.h"
+
+namespace ew {
+
+// ---------------------------------------------------------------------------
+// Strided gather: out[i] = in[(s * i) mod n]
+// ---------------------------------------------------------------------------
+
+// (a * b) mod n for a, b < n.  Narrow: the product fits in 64 bits.  Wide:
+// double-and-add, exact for any n < 2^62 (used once per lane).
+__device__ __forceinline__ uint64_t mul_mod(uint64_t a, uint64_t b, uint64_t n, int wide)
+{
+    if (!wide) return (a * b) % n;
+    uint64_t r = 0;
+    while (b) {
+        if (b & 1u) r = add_mod(r, a, n);
+        a = add_mod(a, a, n);
+        b >>= 1;
+    }
+    return r;
+}
+
+template <int U>
+__global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint64_t nthr = blockDim.x;
+    const uint64_t seg_bytes = g.seg * 4;
+
+    if (blockIdx.x == 0 && tid < g.head + g.tail) {
+        const uint64_t e = tid < g.head ? (uint64_t)tid : g.head + g.vectors * 4 + (tid - g.head);
+        const uint32_t x = g.in[mul_mod(g.stride, e, g.n, g.wide)];
+        for (uint64_t k = 0; k < g.reps; ++k) g.out[e + k * g.seg] = x;
+    }
+
+    uint64_t t = blockIdx.x;
+    if (t >= g.tiles) return;
+    char *out = reinterpret_cast<char *>(g.out + g.head);
+    const uint64_t tile_vecs = nthr * U;
+    // Input index of this lane's first element in its first tile.
+    uint64_t jt = mul_mod(g.stride, g.head + 4 * (t * tile_vecs + tid), g.n, g.wide);
+
+    for (; t < g.tiles; t += gridDim.x) {
+        const uint64_t v0 = t * tile_vecs + tid;
+        uint32_t r[U][4];
+        uint64_t j = jt;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool live = v0 + u * nthr < g.vectors;
+            uint64_t jj = j;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r[u][k] = live ? g.in[jj] : 0u;
+                jj = add_mod(jj, g.stride, g.n);
+            }
+            j = add_mod(j, g.step_vec, g.n);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t v = v0 + u * nthr;
+            if (v < g.vectors) {
+                const u32x4 x = u32x4{r[u][0], r[u][1], r[u][2], r[u][3]};
+                for (uint64_t k = 0; k < g.reps; ++k) store16(out + k * seg_bytes + v * 16, x);
+            }
+        }
+        jt = add_mod(jt, g.step_tile, g.n);
+    }
+}
+
+// Small strides coprime with n (2 <= s <= 8, gcd(s, n) == 1): read every
+// input element once.  Output index i reads in[s*i - k*n] where
+// k = floor(s*i / n), so the output is s contiguous passes (k = 0 .. s-1),
+// pass k reading every s-th input element from a residue r_k = (-k*n) mod s,
+// and the s residues are all different.  Slot m of all s passes together
+// therefore reads the s consecutive elements in[s*m .. s*m + s - 1].
+//
+// Each lane takes four slots (a group); a wave takes 64 groups, i.e. 1024 * s
+// consecutive input bytes.  The wave reads them with s contiguous 16-byte-
+// per-lane loads (1 KiB per instruction), parks them in its own part of LDS,
+// and each lane reads back its 16 * s bytes; then, for each residue r, it
+// writes the four values in[s*(m+q) + r] (q = 0..3) as one 16-byte store to
+// its pass's output run at dest[r] + m.  Letting each lane load its own 16 * s
+// bytes directly instead (s loads 16 * s bytes apart across the lanes) ran
+// 14 % (s = 3) to 70 % (s = 7) slower on MI355X.  The register permutation is
+// fixed at compile time (S is a template parameter); only the destinations
+// are runtime values.
+//
+// Each wave keeps 1 KiB * S of loads in flight, S times what a copy wave
+// keeps, and on MI355X the full gather (S writes per wave) ran fastest with
+// about 24-32 KiB of loads in flight per compute unit: at full occupancy
+// (32 waves per CU) it lost 9 % (s = 2) to 17 % (s = 8) against the capped
+// shapes.  Blocks are therefore 256 threads and each reserves enough LDS
+// that at most kPassBlocksPerCu(S) blocks fit in a CU's 160 KiB: 16 waves per
+// CU for s = 2, 8 for s = 3..5, 4 for s = 6..8 (the best of 4..32 waves per
+// CU and blocks of 256 or 512 threads for every s).  The reservation holds
+// the waves' staging slices; the rest of it is unused.  The view (FirstOnly:
+// S KiB read, 1 KiB written per wave) ran fastest uncapped, so it reserves
+// only its staging.  A wave only reads back the slice it wrote itself, so no
+// block barrier is needed: the LDS performs one wave's accesses in issue
+// order, and wavefront-scope fences keep the compiler from moving them (a
+// block barrier there cost up to 5 %).
+// FirstOnly keeps only the residue-0 pass: that is the strided view
+// x[::S] (out[m] = in[S*m]), read as contiguous spans of which 1/S is kept.
+constexpr int kPassThreads = 256;
+constexpr int kLdsBytesPerCu = 160 * 1024;
+
+constexpr int kPassBlocksPerCu(int s) { return s == 2 ? 4 : s <= 5 ? 2 : 1; }
+
+// Bytes of LDS each pass block reserves: its staging (16 * S bytes per lane)
+// or, for the full gather if larger, just over 1/(blocks + 1) of the CU's LDS
+// so that no more than kPassBlocksPerCu(S) blocks are resident on one CU.
+constexpr int kPassLdsBytes(int s, bool first_only)
+{
+    return (first_only || kPassThreads * 16 * s > kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024)
+               ? kPassThreads * 16 * s
+               : kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024;
+}
+static_assert(kPassLdsBytes(2, false) * 5 > kLdsBytesPerCu &&
+                  kPassLdsBytes(3, false) * 3 > kLdsBytesPerCu &&
+                  kPassLdsBytes(6, false) * 2 > kLdsBytesPerCu &&
+                  kPassLdsBytes(8, false) <= kLdsBytesPerCu,
+              "the LDS reservation must cap the resident pass blocks per CU");
+
+// Orders this wave's LDS accesses at a point of the program: the LDS
+// performs one wave's accesses in issue order, so only the compiler needs
+// holding back (no instruction is emitted).
+__device__ __forceinline__ void wave_lds_order()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int S, bool FirstOnly>
+__global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
+{
+    __shared__ u32x4 lds[kPassLdsBytes(S, FirstOnly) / 16];
+    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    u32x4 *buf = lds + wv * 64 * S;         // this wave's staging slice
+    constexpr int kRuns = FirstOnly ? 1 : S;
+    for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
+        const uint64_t grp0 = t * kPassThreads + wv * 64;     // first group of this wave
+        const uint64_t grp = grp0 + lane;
+        if ((grp0 + 64) * 4 * S <= g.n) {
+            // The wave's whole span is in range, so every lane's four slots
+            // exist in every pass.  A path of its own, with no element-wise
+            // fallback merged into its registers: the compiler then has no
+            // reason to wait for one store to complete before the next.
+            const uint64_t wbase = (uint64_t)S * 4 * grp0;    // its first input element
+#pragma unroll
+            for (int v = 0; v < S; ++v)
+                buf[64 * v + lane] = load16<false, 4>(
+                    reinterpret_cast<const char *>(g.in + wbase + 4 * (64 * v + lane)));
+            wave_lds_order();
+            u32x4 e[S];
+#pragma unroll
+            for (int v = 0; v < S; ++v) e[v] = buf[S * lane + v];
+            wave_lds_order();       // read back before the next tile's writes
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r) {
+                u32x4 w;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w[q] = e[(S * q + r) / 4][(S * q + r) % 4];
+                u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(g.out + g.dest[r] + 4 * grp);
+                if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
+                else *p = w;
+            }
+        } else if (grp < g.vectors) {
+            // The wave at the end of the input: element by element.
+            const uint64_t base = (uint64_t)S * 4 * grp;
+            uint32_t e[4 * S];
+#pragma unroll
+            for (int k = 0; k < 4 * S; ++k) e[k] = base + k < g.n ? g.in[base + k] : 0u;
+#pragma unroll
+            for (int r = 0; r < kRuns; ++r) {
+                uint32_t *dst = g.out + g.dest[r] + 4 * grp;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (base + (uint64_t)S * q + r < g.n) dst[q] = e[S * q + r];
+            }
+        }
+    }
+}
+
+// Stride 2 with two equal segments (n even, n/2 a multiple of 4): output i of
+// the first segment reads in[2i] and never wraps.  Instead of four scalar
+// loads per vector, each wave reads its 2 KiB input span with two contiguous
+// 16-byte-per-lane loads (1 KiB per instruction) and keeps elements 0 and 2
+// of each: lane l of a wave covering outputs [o, o + 256) produces outputs
+// o + 2l, o + 2l + 1 from the first load and o + 128 + 2l, o + 129 + 2l from
+// the second, stored as 8-byte pairs (512 contiguous bytes per instruction),
+// once per segment.  A tile is blockDim * U vectors of 4 outputs, so the
+// launch shape means the same as for the general gather.
+template <int U, bool Co>
+__global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
+{
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & 63u;
+    const uint32_t wave = tid >> 6;
+    const uint64_t nthr = blockDim.x;
+    const uint64_t seg_bytes = g.seg * 4;
+
+    if (blockIdx.x == 0 && tid < g.head + g.tail) {
+        const uint64_t e = tid < g.head ? (uint64_t)tid : g.head + g.vectors * 4 + (tid - g.head);
+        const uint32_t x = g.in[2 * e];
+        for (uint64_t k = 0; k < g.reps; ++k) g.out[e + k * g.seg] = x;
+    }
+
+    const char *in = reinterpret_cast<const char *>(g.in);
+    char *out = reinterpret_cast<char *>(g.out);
+    const uint64_t body_end = g.head + g.vectors * 4;
+    for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
+        const uint64_t o0 = g.head + 4 * t * nthr * U;
+        u32x4 x[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t o = o0 + ((uint64_t)wave * U + u) * 256;
+            const uint64_t i1 = o + 2 * lane, i2 = o + 128 + 2 * lane;
+            x[u][0] = i1 < body_end ? load16<Co, 4>(in + 8 * i1) : u32x4{0, 0, 0, 0};
+            x[u][1] = i2 < body_end ? load16<Co, 4>(in + 8 * i2) : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint64_t o = o0 + ((uint64_t)wave * U + u) * 256;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint64_t i = o + 128 * h + 2 * lane;
+                if (i < body_end) {
+                    const u32x2 pair = u32x2{x[u][h].x, x[u][h].z};
+                    for (uint64_t k = 0; k < g.reps; ++k) {
+                        u32x2 *q = reinterpret_cast<u32x2 *>(out + k * seg_bytes + 4 * i);
+                        if constexpr (EW_STORE_NT) __builtin_nontemporal_store(pair, q);
+                        else *q = pair;
+                    }
+                }
+            }
+        }
+    }
+}
+// ---------------------------------------------------------------------------
+// Dispatch
+// ---------------------------------------------------------------------------
+
+namespace {
+
+template <int U, bool Co>
+const void *gather2_fn()
+{
+    return reinterpret_cast<const void *>(&ew_gather2_kernel<U, Co>);
+}
+}  // namespace
+
+int gather_passes_threads() { return kPassThreads; }
+
+hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
+{
+    GatherArgs a = args;
+    void *kargs[] = {&a};
+    const void *fn = nullptr;
+    if (args.passes >= 2) {
+#define EW_PASS_FN(S) (args.first_only                                                        \
+                           ? reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, true>)   \
+                           : reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, false>))
+        switch (args.passes) {
+        case 2: fn = EW_PASS_FN(2); break;
+        case 3: fn = EW_PASS_FN(3); break;
+        case 4: fn = EW_PASS_FN(4); break;
+        case 5: fn = EW_PASS_FN(5); break;
+        case 6: fn = EW_PASS_FN(6); break;
+        case 7: fn = EW_PASS_FN(7); break;
+        case 8: fn = EW_PASS_FN(8); break;
+        default: return hipErrorInvalidValue;
+        }
+#undef EW_PASS_FN
+        return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, 0, s);
+    }
+    if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {
+        // co-alignment of the input's body start: in + 8 * head
+        const bool co = ((reinterpret_cast<uintptr_t>(args.in) + 8 * args.head) & 15u) == 0;
+        switch (l.unroll) {
+        case 1: fn = co ? gather2_fn<1, true>() : gather2_fn<1, false>(); break;
+        case 2: fn = co ? gather2_fn<2, true>() : gather2_fn<2, false>(); break;
+        case 4: fn = co ? gather2_fn<4, true>() : gather2_fn<4, false>(); break;
+        case 8: fn = co ? gather2_fn<8, true>() : gather2_fn<8, false>(); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (l.unroll) {
+        case 1: fn = reinterpret_cast<const void *>(&ew_gather_kernel<1>); break;
+        case 2: fn = reinterpret_cast<const void *>(&ew_gather_kernel<2>); break;
+        case 4: fn = reinterpret_cast<const void *>(&ew_gather_kernel<4>); break;
+        case 8: fn = reinterpret_cast<const void *>(&ew_gather_kernel<8>); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
+    return hipLaunchKernel(fn, dim3(l.grid), dim3(l.block), kargs, 0, s);
+}
+}  // namespace ew

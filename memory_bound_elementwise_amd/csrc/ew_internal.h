@@ -1,5 +1,6 @@
 // ew_internal.h -- declarations shared by the host API (ew_api.cpp) and the
-// device kernels (ew_kernels.hip) of libew.  Not installed; not part of the
+// device kernels (ew_stream.hip, ew_batch.hip, ew_gather.hip, ew_view.hip)
+// of libew.  Not installed; not part of the
 // C ABI.
 #pragma once
 
@@ -37,6 +38,7 @@ enum OpId : int {
     kOpAbsF32,
     kOpAbsF16,
     kOpAbsBF16,
+    kOpGatherWalkF32,
     kOpCount
 };
 
@@ -76,6 +78,26 @@ struct BatchArgs {
     BatchItem item[kBatchMax];
 };
 static_assert(sizeof(BatchArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
+// A batched call whose item table lives in device memory (any number of
+// items per launch).  Table image, 8-byte aligned: `count` BatchTableItem
+// records, then one uint32_t per global tile naming the item that owns it.
+// Item k owns the tiles [first_tile, first_tile + its tile count), at least
+// one per item so that its scalar head and tail have a block.
+struct BatchTableItem {
+    const void *in0;
+    const void *in1;     // nullptr for one-input operations
+    void *out;
+    uint64_t n;
+    uint64_t first_tile;
+};
+static_assert(sizeof(BatchTableItem) == 40, "table record layout");
+struct BatchTableArgs {
+    const BatchTableItem *item;
+    const uint32_t *tile_item;
+    uint64_t tiles;      // tiles of all items together
+    float alpha;         // saxpy, scale and add-scalar only
+};
 
 // The gather additionally walks its input index (stride * i) mod n
 // incrementally; the steps are reduced mod n on the host.  When
@@ -154,6 +176,11 @@ hipError_t launch_stream(OpId op, const StreamArgs &args, bool co0, bool co1,
 // unroll must be 1, 2 or 4).
 hipError_t launch_batch(OpId op, const BatchArgs &args, const Launch &launch,
                         hipStream_t stream);
+
+// Launch one batched kernel reading its item table from device memory
+// (unroll 1, 2 or 4).
+hipError_t launch_batch_table(OpId op, const BatchTableArgs &args, const Launch &launch,
+                              hipStream_t stream);
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
                          hipStream_t stream);

@@ -124,7 +124,7 @@ def _set(op, block, bpc, unroll):
     table's rows, plus 0 and LARGE_MIN_N), so the timed size uses it."""
     mins = {0, LARGE_MIN_N} | {r[0] for r in _read_rows(ew.LAUNCH_TABLE).get(op, [])}
     for m in sorted(mins):
-        ew.ew_set_launch_config(op, m, block, bpc, unroll)
+        ew.ew_set_launch_row(op, m, block, bpc, unroll)
 
 
 def tune(ops=ew.OPS, repeats=3, finalists=6, rounds=7, log=None):

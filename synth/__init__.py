@@ -200,13 +200,26 @@ WORKLOADS = {
     "headline_add_f32_2e28": _w(
         "headline_add_f32_2e28", "add_f32", 1 << 28, 100, "uniform",
         description="fp32 C=A+B, n=2^28, all buffers aligned"),
+    # the per-output index walk of the fifth configuration's gather: every
+    # output element loads its own input element (the input read twice)
+    "gather_walk_f32_2e26_s2": _w(
+        "gather_walk_f32_2e26_s2", "gather_walk_f32", 1 << 26, 107, "uniform", stride=2,
+        description="fp32 strided gather out[i]=in[(2*i) mod n] as a per-output index walk "
+                    "(one 4-byte load per output), n=2^26, in uniform[-1,1)"),
+    # the one-read-one-write stream at the headline's size: with the pure
+    # read stream (relu_inplace_f32_2e28_nonneg) it brackets what a stream
+    # mixing reads and writes attains on the part
+    "copy_f32_2e28": _w(
+        "copy_f32_2e28", "copy_f32", 1 << 28, 129, "uniform",
+        description="fp32 contiguous copy out[i]=in[i], n=2^28, in uniform[-1,1)"),
 }
 
 # Number of inputs each operation reads, and its element type.
 OP_INPUTS = {
     "add_f32": ("a", "b"), "add_f16": ("a", "b"), "add_bf16": ("a", "b"),
     "saxpy_f32": ("x", "y"), "relu_f32": ("x",), "copy_f32": ("x",),
-    "gather_f32": ("x",), "add_relu_f32": ("a", "b"), "saxpy_relu_f32": ("x", "y"),
+    "gather_f32": ("x",), "gather_walk_f32": ("x",), "add_relu_f32": ("a", "b"),
+    "saxpy_relu_f32": ("x", "y"),
     "bias_relu_f32": ("x", "bias"), "saxpy_f16": ("x", "y"), "saxpy_bf16": ("x", "y"),
     "relu_f16": ("x",), "relu_bf16": ("x",), "copy2d_f32": ("base",),
     "relu_inplace_f32": ("x",),
@@ -216,7 +229,8 @@ OP_INPUTS = {
 OP_DTYPE = {
     "add_f32": np.float32, "add_f16": np.uint16, "add_bf16": np.uint16,
     "saxpy_f32": np.float32, "relu_f32": np.float32, "copy_f32": np.float32,
-    "gather_f32": np.float32, "add_relu_f32": np.float32, "saxpy_relu_f32": np.float32,
+    "gather_f32": np.float32, "gather_walk_f32": np.float32, "add_relu_f32": np.float32,
+    "saxpy_relu_f32": np.float32,
     "bias_relu_f32": np.float32, "saxpy_f16": np.uint16, "saxpy_bf16": np.uint16,
     "relu_f16": np.uint16, "relu_bf16": np.uint16, "copy2d_f32": np.float32,
     "relu_inplace_f32": np.float32,

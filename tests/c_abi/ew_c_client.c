@@ -160,6 +160,81 @@ int main(void)
                       EW_ERR_INVALID_ARG);
     }
 
+    /* the same batch through a device item table: one launch */
+    {
+        enum { ITEMS = 130 };
+        ew_batch_item_t items[ITEMS];
+        size_t at = 0;
+        for (int k = 0; k < ITEMS; ++k) {
+            const size_t m = (size_t)k * 7 + 1;
+            items[k].out = dc + at;
+            items[k].in0 = da + at + (size_t)(k % 4);
+            items[k].in1 = NULL;
+            items[k].n = m;
+            at += m + 5;
+        }
+        ew_batch_plan_t plan;
+        expect_status("ew_batch_build size", ew_batch_build("scale_f32", items, ITEMS, NULL, 0,
+                                                            &plan), EW_OK);
+        uint64_t *image = malloc(plan.bytes);
+        void *table = NULL;
+        if (!image) return 2;
+        expect_status("ew_batch_build", ew_batch_build("scale_f32", items, ITEMS, image,
+                                                       plan.bytes, &plan), EW_OK);
+        HIP_OK(hipMalloc(&table, plan.bytes));
+        HIP_OK(hipMemcpy(table, image, plan.bytes, hipMemcpyHostToDevice));
+        HIP_OK(hipMemset(dc, 0, n * sizeof *dc));
+        expect_status("ew_batch_run", ew_batch_run(&plan, 2.5f, table, s), EW_OK);
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(got, dc, at * sizeof *got, hipMemcpyDeviceToHost));
+        memset(ref, 0, at * sizeof *ref);
+        at = 0;
+        for (int k = 0; k < ITEMS; ++k) {
+            const size_t m = (size_t)k * 7 + 1;
+            oracle_scale_f32(2.5f, ha + at + (size_t)(k % 4), ref + at, m);
+            at += m + 5;
+        }
+        expect_equal("ew_batch_run scale_f32", got, ref, at);
+        expect_status("ew_batch_run misaligned table",
+                      ew_batch_run(&plan, 2.5f, (const char *)table + 4, s), EW_ERR_MISALIGNED);
+        HIP_OK(hipFree(table));
+        free(image);
+    }
+
+    /* the per-output index walk of the strided gather, stride 2 */
+    expect_status("ew_gather_walk_f32", ew_gather_walk_f32(da, dc, n, 2, s), EW_OK);
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(got, dc, n * sizeof *got, hipMemcpyDeviceToHost));
+    oracle_gather_f32(ha, ref, n, 2);
+    expect_equal("ew_gather_walk_f32 stride 2", got, ref, n);
+
+    /* one launch configuration for every size: what get reports is what the
+     * next call launches (block, unroll; grid = min(4 * CUs, tiles)) */
+    {
+        int dev = 0, cus = 0, block = 0, grid = 0, unroll = 0;
+        HIP_OK(hipGetDevice(&dev));
+        HIP_OK(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+        expect_status("ew_set_launch_config", ew_set_launch_config("copy_f32", 256, 4, 2), EW_OK);
+        expect_status("ew_get_launch_config",
+                      ew_get_launch_config("copy_f32", n, &block, &grid, &unroll), EW_OK);
+        const size_t tiles = (n / 4 + 511) / 512;
+        const int want = (size_t)(4 * cus) < tiles ? 4 * cus : (int)tiles;
+        checks++;
+        if (block != 256 || unroll != 2 || grid != want) {
+            printf("FAIL ew_get_launch_config: block %d grid %d unroll %d, expected 256 %d 2\n",
+                   block, grid, unroll, want);
+            failures++;
+        }
+        expect_status("ew_set_launch_config range", ew_set_launch_config("copy_f32", 96, 4, 2),
+                      EW_ERR_INVALID_ARG);
+        expect_status("ew_copy_f32", ew_copy_f32(db, dc, n, s), EW_OK);
+        HIP_OK(hipStreamSynchronize(s));
+        HIP_OK(hipMemcpy(got, dc, n * sizeof *got, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(ref, db, n * sizeof *ref, hipMemcpyDeviceToHost));
+        expect_equal("ew_copy_f32 under the set configuration", got, ref, n);
+        ew_reset_launch_config();
+    }
+
     /* errors are status codes, checked before any HIP call */
     expect_status("null pointer", ew_add_f32(NULL, db, dc, n, s), EW_ERR_INVALID_ARG);
     expect_status("misaligned", ew_add_f32((const float *)((const char *)da + 2), db, dc, n, s),

@@ -52,7 +52,7 @@ def test_binding_names_match_the_c_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert ew.ew_abi_version() == 9
+    assert ew.ew_abi_version() == 10
     for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
                  EW_ERR_NO_DEVICE, EW_ERR_HIP):
         s = ew.ew_status_string(code)
@@ -192,33 +192,34 @@ def test_valid_call_without_a_device_reports_no_device():
     assert _status(ew.ew_saxpy_f32, 2.5, BASE, BASE, 1000, 0) == EW_ERR_NO_DEVICE
 
 
-def test_launch_config_table_set_get_reset_and_load(tmp_path):
+def test_launch_rows_set_get_reset_and_load(tmp_path):
+    """Size-class rows: ew_set_launch_row / ew_get_launch_row."""
     try:
         ew.ew_reset_launch_config()
-        default = ew.ew_get_launch_config("add_f32", 1 << 28)
-        ew.ew_set_launch_config("add_f32", 1 << 26, 512, 4, 4)
-        assert ew.ew_get_launch_config("add_f32", 1 << 28) == (512, 4, 4)
-        assert ew.ew_get_launch_config("add_f32", (1 << 26) - 1) != (512, 4, 4)
+        default = ew.ew_get_launch_row("add_f32", 1 << 28)
+        ew.ew_set_launch_row("add_f32", 1 << 26, 512, 4, 4)
+        assert ew.ew_get_launch_row("add_f32", 1 << 28) == (512, 4, 4)
+        assert ew.ew_get_launch_row("add_f32", (1 << 26) - 1) != (512, 4, 4)
         # replacing a row
-        ew.ew_set_launch_config("add_f32", 1 << 26, 1024, 2, 8)
-        assert ew.ew_get_launch_config("add_f32", 1 << 26) == (1024, 2, 8)
+        ew.ew_set_launch_row("add_f32", 1 << 26, 1024, 2, 8)
+        assert ew.ew_get_launch_row("add_f32", 1 << 26) == (1024, 2, 8)
         # invalid values
         for bad in ((100, 8, 1), (0, 8, 1), (2048, 8, 1), (256, 0, 1), (256, 8, 3)):
             with pytest.raises(ew.EwError):
-                ew.ew_set_launch_config("add_f32", 0, *bad)
+                ew.ew_set_launch_row("add_f32", 0, *bad)
         with pytest.raises(ew.EwError):
-            ew.ew_set_launch_config("no_such_op", 0, 256, 8, 1)
+            ew.ew_set_launch_row("no_such_op", 0, 256, 8, 1)
         with pytest.raises(ew.EwError):
-            ew.ew_get_launch_config("no_such_op", 0)
+            ew.ew_get_launch_row("no_such_op", 0)
         ew.ew_reset_launch_config()
-        assert ew.ew_get_launch_config("add_f32", 1 << 28) == default
+        assert ew.ew_get_launch_row("add_f32", 1 << 28) == default
         # table file
         f = tmp_path / "table.txt"
         f.write_text("# op min_n block bpc unroll\n\nrelu_f32 0 128 16 1  # small\n"
                      "relu_f32 1048576 512 2 4\n")
         ew.ew_load_launch_table(str(f))
-        assert ew.ew_get_launch_config("relu_f32", 10) == (128, 16, 1)
-        assert ew.ew_get_launch_config("relu_f32", 1 << 21) == (512, 2, 4)
+        assert ew.ew_get_launch_row("relu_f32", 10) == (128, 16, 1)
+        assert ew.ew_get_launch_row("relu_f32", 1 << 21) == (512, 2, 4)
         bad = tmp_path / "bad.txt"
         bad.write_text("relu_f32 0 128\n")
         with pytest.raises(ew.EwError):
@@ -229,6 +230,40 @@ def test_launch_config_table_set_get_reset_and_load(tmp_path):
         ew.ew_reset_launch_config()
         if os.path.exists(ew.LAUNCH_TABLE):
             ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+def test_set_launch_config_replaces_every_size_class():
+    """ew_set_launch_config(op, block, blocks_per_cu, unroll): one row for
+    every n of that operation; other operations keep their rows."""
+    try:
+        ew.ew_reset_launch_config()
+        relu = [ew.ew_get_launch_row("relu_f32", n) for n in (1, 1 << 22, 1 << 28)]
+        ew.ew_set_launch_config("add_f32", 256, 4, 2)
+        for n in (0, 1, 1 << 20, 1 << 22, 1 << 25, 1 << 28, (1 << 62) - 1):
+            assert ew.ew_get_launch_row("add_f32", n) == (256, 4, 2), n
+        assert [ew.ew_get_launch_row("relu_f32", n) for n in (1, 1 << 22, 1 << 28)] == relu
+        p = ew.ew_make_plan("add_f32", BASE, BASE + 8 * MiB, BASE + 16 * MiB, 1 << 20, 256)
+        assert (p.block, p.blocks_per_cu, p.unroll) == (256, 4, 2)
+        assert p.grid == min(4 * 256, -(-(1 << 18) // 512))
+        for bad in ((100, 8, 1), (0, 8, 1), (2048, 8, 1), (256, 0, 1), (256, 1025, 1),
+                    (256, 8, 3)):
+            with pytest.raises(ew.EwError):
+                ew.ew_set_launch_config("add_f32", *bad)
+        with pytest.raises(ew.EwError):
+            ew.ew_set_launch_config("no_such_op", 256, 8, 1)
+        with pytest.raises(ew.EwError):
+            ew.ew_get_launch_config("no_such_op", 1)
+    finally:
+        ew.ew_reset_launch_config()
+        ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="only meaningful where no GPU is visible")
+def test_get_launch_config_needs_a_device():
+    """The grid depends on the current device's compute-unit count."""
+    with pytest.raises(ew.EwError) as e:
+        ew.ew_get_launch_config("add_f32", 1 << 28)
+    assert e.value.status == EW_ERR_NO_DEVICE
 
 
 def test_compiled_defaults_match_the_shipped_table():
@@ -243,7 +278,7 @@ def test_compiled_defaults_match_the_shipped_table():
     try:
         ew.ew_reset_launch_config()
         for op, min_n, cfg in rows:
-            assert ew.ew_get_launch_config(op, min_n) == cfg, (op, min_n)
+            assert ew.ew_get_launch_row(op, min_n) == cfg, (op, min_n)
     finally:
         ew.ew_load_launch_table(ew.LAUNCH_TABLE)
 
@@ -271,8 +306,8 @@ def test_planning_and_the_table_are_thread_safe():
     def writer():
         try:
             for k in range(400):
-                ew.ew_set_launch_config("add_f32", 1 << 22, (64, 256, 1024)[k % 3], 1024, 1)
-                ew.ew_get_launch_config("add_f32", 1 << 23)
+                ew.ew_set_launch_row("add_f32", 1 << 22, (64, 256, 1024)[k % 3], 1024, 1)
+                ew.ew_get_launch_row("add_f32", 1 << 23)
                 if k % 50 == 0:
                     ew.ew_reset_launch_config()
         except Exception as e:   # noqa: BLE001
@@ -339,3 +374,123 @@ def test_valid_batch_without_a_device_reports_no_device():
     items = [(o, a, b, n + k) for k, o in enumerate(outs)]
     assert _batch("add_f32", items) == EW_ERR_NO_DEVICE
     assert _batch("scale_bf16", [(o, a, None, n) for o in outs], 2.5) == EW_ERR_NO_DEVICE
+
+
+def _build(op, items, table=None, table_bytes=0):
+    """ew_batch_build on raw (out, in0, in1, n) tuples; returns (status, plan)."""
+    arr = (ew.EwBatchItem * max(len(items), 1))(*[ew.EwBatchItem(*it) for it in items])
+    plan = ew.EwBatchPlan()
+    st = ew._c["ew_batch_build"](op.encode(), arr, len(items), table, table_bytes,
+                                 ctypes.byref(plan))
+    return st, plan
+
+
+def test_batch_build_validates_like_the_host_array_call():
+    """Every item list that ew_batch rejects, ew_batch_build rejects with the
+    same status (the two share their validation)."""
+    n = 1024
+    a, b, c = BASE, BASE + MiB, BASE + 2 * MiB
+    cases = [("add_f32", [(c, a, b, n), (c + 4 * MiB, 0, b, n)]),
+             ("add_f16", [(c, a + 1, b, n)]),
+             ("relu_f32", [(a + 4, a, None, n)]),
+             ("add_f32", [(c, a, b, n), (c + 4 * n - 4, a, b, n)]),
+             ("add_f32", [(c, a, b, n), (a + 8, c + 8 * MiB, b, 4)]),
+             ("saxpy_f32", [(b, a, None, n), (a, b, None, n)])]
+    cases += [(op, [(c, a, b, n)]) for op in ("gather_f32", "gather_walk_f32", "bias_relu_f32",
+                                               "copy2d_f32", "relu_inplace_f32", "nope")]
+    for op, items in cases:
+        want = _batch(op, items)
+        assert want != EW_OK
+        assert _build(op, items)[0] == want, (op, items)
+    st = ew._c["ew_batch_build"](b"add_f32", None, 3, None, 0, ctypes.byref(ew.EwBatchPlan()))
+    assert st == EW_ERR_INVALID_ARG
+    assert ew._c["ew_batch_build"](b"add_f32", None, 0, None, 0, None) == EW_ERR_INVALID_ARG
+
+
+def _expected_tiles(out, n, es, block, unroll):
+    head = min(((16 - out % 16) % 16) // es, n)
+    vectors = (n - head) // (16 // es)
+    return max(1, -(-vectors // (block * unroll)))
+
+
+@pytest.mark.parametrize("op,es", [("add_f32", 4), ("add_bf16", 2), ("saxpy_f32", 4),
+                                   ("relu_f16", 2), ("sqrt_f32", 4)])
+def test_batch_build_writes_the_documented_image(op, es):
+    """The image holds one 40-byte record per item with n > 0 (in0, in1, out,
+    n, first tile) and one 32-bit item index per tile; the tile counts are the
+    single call's (head aligning the output to 16 bytes), at least one per
+    item; a size query (no table) gives the same plan."""
+    import random
+    rnd = random.Random(7 + es)
+    items = []
+    for k in range(300):
+        n = rnd.choice([0, 1, 3, 7, 8, 15, 1000, 4096, 65536 + 5, rnd.randrange(1, 200000)])
+        base = BASE + k * 4 * MiB
+        out = base + es * rnd.randrange(0, 8)
+        in0 = base + MiB + es * rnd.randrange(0, 8)
+        in1 = base + 2 * MiB + es * rnd.randrange(0, 8)
+        if op == "saxpy_f32":
+            in1 = None                       # the second input is out itself
+        elif op in ("relu_f16", "sqrt_f32"):
+            in1 = None
+        items.append((out, in0, in1, n))
+    st, plan = _build(op, items)
+    assert st == EW_OK
+    total = sum(it[3] for it in items)
+    block, bpc, unroll = ew.ew_get_launch_row(op, total)
+    unroll = min(unroll, 4)
+    assert (plan.block, plan.unroll, plan.blocks_per_cu) == (block, unroll, bpc)
+    live = [it for it in items if it[3] > 0]
+    tiles = [_expected_tiles(it[0], it[3], es, block, unroll) for it in live]
+    assert plan.items == len(live) and plan.tiles == sum(tiles) and plan.total_n == total
+    assert plan.bytes == -(-(40 * len(live) + 4 * sum(tiles)) // 8) * 8
+    img = (ctypes.c_uint64 * (plan.bytes // 8))()
+    st, plan2 = _build(op, items, ctypes.addressof(img), plan.bytes)
+    assert st == EW_OK and bytes(plan2) == bytes(plan)
+    raw = bytes(img)
+    import struct
+    first = 0
+    for k, (it, nt) in enumerate(zip(live, tiles)):
+        in0, in1, out, n, ft = struct.unpack_from("<5Q", raw, 40 * k)
+        second = it[0] if op == "saxpy_f32" else (it[2] or 0)
+        assert (in0, in1, out, n, ft) == (it[1], second, it[0], it[3], first), k
+        idx = struct.unpack_from(f"<{nt}I", raw, 40 * len(live) + 4 * first)
+        assert set(idx) == {k}
+        first += nt
+    assert raw[40 * len(live) + 4 * first:] == b"\0" * (plan.bytes - 40 * len(live) - 4 * first)
+    # too small a table, or a misaligned one
+    assert _build(op, items, ctypes.addressof(img), plan.bytes - 8)[0] == EW_ERR_INVALID_ARG
+    big = (ctypes.c_uint64 * (plan.bytes // 8 + 1))()
+    assert _build(op, items, ctypes.addressof(big) + 4, plan.bytes)[0] == EW_ERR_MISALIGNED
+
+
+def test_batch_build_of_nothing_and_run_checks_the_plan():
+    st, plan = _build("add_f32", [(BASE, BASE + MiB, BASE + 2 * MiB, 0)])
+    assert st == EW_OK and plan.items == 0 and plan.tiles == 0 and plan.bytes == 0
+    run = ew._c["ew_batch_run"]
+    assert run(ctypes.byref(plan), 0.0, None, None) == EW_OK          # nothing to launch
+    assert run(None, 0.0, BASE, None) == EW_ERR_INVALID_ARG
+    st, plan = _build("add_f32", [(BASE + 2 * MiB * k, BASE + 2 * MiB * k + MiB,
+                                   BASE + 2 * MiB * k + MiB + 4096, 1000) for k in range(4)])
+    assert st == EW_OK and plan.items == 4
+    assert run(ctypes.byref(plan), 0.0, None, None) == EW_ERR_INVALID_ARG
+    assert run(ctypes.byref(plan), 0.0, BASE + 4, None) == EW_ERR_MISALIGNED
+    for field, value in (("op", 999), ("op", 6), ("block", 100), ("unroll", 8), ("items", 0),
+                         ("tiles", 3), ("bytes", 8), ("blocks_per_cu", 0)):
+        bad = ew.EwBatchPlan.from_buffer_copy(plan)
+        setattr(bad, field, value)
+        assert run(ctypes.byref(bad), 0.0, BASE, None) == EW_ERR_INVALID_ARG, field
+    if not _gpu_visible():
+        assert run(ctypes.byref(plan), 0.0, BASE, None) == EW_ERR_NO_DEVICE
+
+
+def test_gather_walk_validation():
+    walk = ew._c["ew_gather_walk_f32"]
+    assert walk(None, None, 0, 0, None) == EW_OK                        # n == 0
+    assert walk(BASE, BASE + MiB, 1000, 0, None) == EW_ERR_INVALID_ARG   # stride 0
+    assert walk(None, BASE + MiB, 1000, 2, None) == EW_ERR_INVALID_ARG
+    assert walk(BASE + 2, BASE + MiB, 1000, 2, None) == EW_ERR_MISALIGNED
+    assert walk(BASE, BASE + 3996, 1000, 2, None) == EW_ERR_OVERLAP
+    assert walk(BASE, BASE, 1000, 1, None) == EW_ERR_OVERLAP             # no exact alias either
+    if not _gpu_visible():
+        assert walk(BASE, BASE + MiB, 1000, 2, None) == EW_ERR_NO_DEVICE

@@ -139,6 +139,8 @@ def _call(op, out_ptr, in_ptrs, n, alpha=2.5, stride=2):
         ew.ew_relu_inplace_f32(out_ptr, n=n, stream=s)
     elif op == "copy_f32":
         ew.ew_copy_f32(in_ptrs[0], out_ptr, n=n, stream=s)
+    elif op == "gather_walk_f32":
+        ew.ew_gather_walk_f32(in_ptrs[0], out_ptr, stride, n=n, stream=s)
     else:
         ew.ew_gather_f32(in_ptrs[0], out_ptr, stride, n=n, stream=s)
 
@@ -203,7 +205,7 @@ def _run_cases(op, cases, seed, alpha=2.5):
 
 
 IN_PLACE = ("saxpy_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16")
-ONE_INPUT = ("relu_f32", "copy_f32", "gather_f32", "relu_f16", "relu_bf16",
+ONE_INPUT = ("relu_f32", "copy_f32", "gather_f32", "gather_walk_f32", "relu_f16", "relu_bf16",
              "relu_inplace_f32") + SCALAR_MAPS + UNARY_MAPS
 TWO_INPUT = ("add_f32", "add_f16", "add_bf16", "add_relu_f32") + IN_PLACE
 
@@ -239,7 +241,7 @@ def _offset_cases(op):
 
 
 ALL_STREAM_OPS = ["add_f32", "add_f16", "add_bf16", "saxpy_f32", "relu_f32", "copy_f32",
-                  "gather_f32", "add_relu_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16",
+                  "gather_f32", "gather_walk_f32", "add_relu_f32", "saxpy_relu_f32", "saxpy_f16", "saxpy_bf16",
                   "relu_f16", "relu_bf16", "relu_inplace_f32"] + list(SCALAR_MAPS + UNARY_MAPS)
 
 
@@ -265,8 +267,12 @@ def test_brute_force_small_all_offsets(op):
     assert not failures, failures[:10]
 
 
-def test_gather_brute_force_strides():
-    print("[parity] gather strides", flush=True)
+@pytest.mark.parametrize("op", ["gather_f32", "gather_walk_f32"])
+def test_gather_brute_force_strides(op):
+    """Both gathers (the library's, with its segment / pass / contiguous-span
+    plans, and the per-output index walk) on every small n with strides up
+    to 2^64 - 1, and the plans' boundary cases."""
+    print(f"[parity] gather strides {op}", flush=True)
     cases = []
     for n in range(1, 18):
         for stride in sorted({1, 2, 3, max(n - 1, 1), n, n + 1, 2 * n + 5, (1 << 63) + 5,
@@ -282,7 +288,7 @@ def test_gather_brute_force_strides():
                       ((1 << 20), (1 << 20) + 2)):
         for oo in (0, 1, 3):
             cases.append((n, oo, [0], stride))
-    failures = _run_cases("gather_f32", cases, seed=310)
+    failures = _run_cases(op, cases, seed=310)
     assert not failures, failures[:10]
 
 
@@ -345,7 +351,7 @@ def _table_min_ns(op):
 
 def _force_launch(op, block, bpc, unroll):
     for m in _table_min_ns(op):
-        ew.ew_set_launch_config(op, m, block, bpc, unroll)
+        ew.ew_set_launch_row(op, m, block, bpc, unroll)
 
 
 LAUNCHES = [(64, 1, 1), (64, 3, 8), (256, 8, 1), (256, 8, 2), (256, 2, 4), (512, 2, 4),

@@ -101,11 +101,14 @@ SINGLE_INPUT_OPS = ("OpReluF32", "OpCopyF32", "OpRelu16", "OpMapF32", "OpMap16",
 
 
 def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
-    """The batched kernels follow the same store policy as the single ones."""
-    n_single = n_batch = 0
+    """The batched kernels (item table in the kernel arguments or in device
+    memory) follow the same store policy as the single ones."""
+    n_single = n_batch = n_table = 0
     for name, (body, _) in _kernels(asm).items():
         n_batch += "ew_batch_kernel" in name
-        if "ew_stream_kernel" in name or "relu_inplace" in name or "ew_batch_kernel" in name:
+        n_table += "ew_batch_table_kernel" in name
+        if ("ew_stream_kernel" in name or "relu_inplace" in name or "ew_batch_kernel" in name
+                or "ew_batch_table_kernel" in name):
             assert re.search(r"global_load_dwordx4 .* nt\b", body), name
             if ("relu_inplace" in name or any(op in name for op in SINGLE_INPUT_OPS)):
                 n_single += 1
@@ -115,6 +118,7 @@ def test_stream_kernels_move_16_bytes_per_lane_with_nt_stores(asm):
                 assert re.search(r"global_store_dwordx4 .* nt\b", body), name
     assert n_single > 0
     assert n_batch == 23 * 3           # every batchable operator kernel x unroll 1, 2, 4
+    assert n_table == 23 * 3
 
 
 def test_strided_view_and_bias_relu_kernels_store_at_device_scope(asm):
@@ -164,10 +168,11 @@ def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
     binary32 ulps from a bfloat16 rounding boundary; pinned in
     test_rounding_margins_cpu.py).  No form may use a native 16-bit root."""
     ks = {k: v[0] for k, v in _kernels(asm).items() if "FnSqrt" in k}
-    # 3 formats x (4 unrolls x 2 alignments of the single kernel + 3 batched unrolls)
-    assert len(ks) == 3 * (4 * 2 + 3)
-    assert sum("FnSqrtWidenedF16" in k for k in ks) == 8 + 3
-    assert sum("FnSqrtWidenedBF16" in k for k in ks) == 8 + 3
+    # 3 formats x (4 unrolls x 2 alignments of the single kernel + 3 unrolls
+    # of each batched kernel)
+    assert len(ks) == 3 * (4 * 2 + 3 + 3)
+    assert sum("FnSqrtWidenedF16" in k for k in ks) == 8 + 3 + 3
+    assert sum("FnSqrtWidenedBF16" in k for k in ks) == 8 + 3 + 3
     for name, body in ks.items():
         assert not re.search(r"\bv_(sqrt|rsq|rcp)_f16", body), name
         if "FnSqrtWidenedBF16" in name:
@@ -183,7 +188,7 @@ def test_sqrt_kernels_round_the_binary32_root_correctly(asm):
 
 def test_scalar_maps_compute_in_binary32(asm):
     ks = {k: v[0] for k, v in _kernels(asm).items() if "FnScale" in k or "FnAddScalar" in k}
-    assert len(ks) == 2 * 3 * (4 * 2 + 3)
+    assert len(ks) == 2 * 3 * (4 * 2 + 3 + 3)
     for name, body in ks.items():
         op = "v_mul_f32" if "FnScale" in name else "v_add_f32"
         assert re.search(r"\b" + op, body), name

@@ -53,7 +53,7 @@ def test_worked_example_ceil_division_of_blocks():
     them masked.  Here a work item is one 16-byte vector (4000 fp32 values),
     and a tile is block * unroll vectors."""
     ex = GOLDEN["split_examples"][1]
-    ew.ew_set_launch_config("relu_f32", 0, ex["threads_per_block"], 64, 1)
+    ew.ew_set_launch_row("relu_f32", 0, ex["threads_per_block"], 64, 1)
     p = _plan("relu_f32", BASE + MiB, BASE, 0, 4 * ex["n"])
     assert p.vectors == ex["n"]
     assert p.tiles == ex["blocks"]
