@@ -2,12 +2,12 @@
 """Achieved HBM bandwidth of the elementwise kernels on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-others] [--no-cpu-baseline]
+                    [--no-others] [--no-cpu-baseline] [--details FILE]
 
 A step is one call of the library on the workload (validation, plan, launch
 of the vectorised grid-stride kernel with its scalar head and tail).  The
-default workload is fp32 C = A + B on n = 2^28 + 3 elements with A one
-element (4 bytes) past an aligned allocation.
+default workload is the headline: fp32 C = A + B on n = 2^28 elements, every
+buffer aligned, A and B uniform on [-1, 1) (seed 100).
 
 Procedure: inputs are generated on the host, copied to the GPU once, and a
 parity gate compares one launch with the CPU oracle on every element (a
@@ -15,20 +15,26 @@ workload that fails reports no speed).  The oracle runs only inside the CPU
 leg (``cpu_baseline_leg``), which also times it.  Then W untimed launches, then K
 launches bracketed by HIP events recorded on the stream the kernels run on.
 GB/s = algorithmic bytes (read + write, 10^9 bytes per GB) / average launch
-time.  Prints one JSON line.
+time ([HyperAI] Stage 3 benchmark script: bytes = 3 * numel * element size
+for the add).
 
-Also reported, in the same line:
-* ``roofline``: the dominant kernel's achieved GB/s against the 8 TB/s HBM
-  peak, and (``traffic``) the HBM bytes per launch measured by rocprofv3
-  counters when a summary for the current kernel source is in
-  ``profiles/traffic.json`` (else null);
-* ``cpu_baseline``: the CPU oracle timed on the host on a bounded sample;
-* ``other_configs``: the remaining workloads (each parity-gated); working
-  sets up to 1 GiB (4 x the 256 MB Infinity Cache) are timed cold: back to
-  back over R copies of the workload's buffers, used in turn, so that at
-  least 1 GiB of other traffic runs between two uses of one copy.  Beside it,
-  ``flushed_per_launch`` gives the median of single launches each bracketed
-  by its own events after a 1 GiB fill.
+Output, on stdout:
+* one JSON line per other workload (``--no-others`` skips them), each
+  parity-gated; working sets up to 1 GiB (4 x the 256 MB Infinity Cache) are
+  timed cold: back to back over R copies of the workload's buffers, used in
+  turn, so that at least 1 GiB of other traffic runs between two uses of one
+  copy.  Beside it, ``flushed_per_launch`` gives the median of single
+  launches each bracketed by its own events after a 1 GiB fill;
+* then the final line, a compact record of the main workload (a few KB):
+  metric, value, ``roofline`` -- the dominant kernel's achieved GB/s against
+  the 8 TB/s HBM peak, its HBM bytes per launch from the committed rocprofv3
+  counter summary (``traffic``, when taken on the current kernel sources and
+  launch shape), the committed kernel-trace duration (``profiled``, likewise)
+  and ``attainable``: what two library kernels measured in the same run move
+  at the same size, the pure read stream (in-place ReLU on non-negative data,
+  which stores nothing) and the one-read-one-write copy -- and
+  ``cpu_baseline``, the CPU oracle timed on the host on a bounded sample.
+``--details FILE`` also writes every record in full, one JSON line each.
 """
 import argparse
 import hashlib
@@ -41,16 +47,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0          # MI355X HBM3E, published
-DEFAULT_WORKLOAD = "cfg2_add_f32_2e28p3_offA1"
-KERNEL_SRC = os.path.join(ROOT, "memory_bound_elementwise_amd", "csrc", "ew_kernels.hip")
+METRIC = "achieved HBM GB/s (read+write bytes/time) and % of MI355X peak, N=2^28"
+DEFAULT_WORKLOAD = "headline_add_f32_2e28"
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_TRACE_JSON = os.path.join(ROOT, "profiles", "kernel_trace.json")
+# The two library streams that bracket a mixed read/write stream's attainable
+# rate at the headline's size: a pure read stream and a copy.
+ATTAINABLE = {"read": "relu_inplace_f32_2e28_nonneg", "copy": "copy_f32_2e28"}
+# The fifth configuration's comparison: the coalesced copy, the library's
+# gather and the per-output index walk, all at n = 2^26.
+STRIDED = {"copy": "cfg5a_copy_f32_2e26", "gather": "cfg5b_gather_f32_2e26_s2",
+           "walk": "gather_walk_f32_2e26_s2"}
+FINAL_LINE_MAX_BYTES = 4096
 
 # Algorithmic bytes per element: each input element read once, each output
 # element written once.  The gather counts logical bytes (read 4 + write 4).
 # The fused chains count what they move: add+ReLU and SAXPY+ReLU 12, bias+ReLU
 # 8 (x read, y written) plus the bias row once.
 BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
-                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "add_relu_f32": 12,
+                  "relu_f32": 8, "copy_f32": 8, "gather_f32": 8, "gather_walk_f32": 8,
+                  "add_relu_f32": 12,
                   "saxpy_relu_f32": 12, "bias_relu_f32": 8, "saxpy_f16": 6, "saxpy_bf16": 6,
                   "relu_f16": 4, "relu_bf16": 4, "copy2d_f32": 8, "relu_inplace_f32": 8,
                   # scalar-broadcast and unary maps: one input read, one output written
@@ -58,7 +74,8 @@ BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12,
                      for m in ("scale", "add_scalar", "sqrt", "abs")
                      for d in ("f32", "f16", "bf16")}}
 DTYPE = {"add_f32": "f32", "add_f16": "f16", "add_bf16": "bf16", "saxpy_f32": "f32",
-         "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32", "add_relu_f32": "f32",
+         "relu_f32": "f32", "copy_f32": "f32", "gather_f32": "f32", "gather_walk_f32": "f32",
+         "add_relu_f32": "f32",
          "saxpy_relu_f32": "f32", "bias_relu_f32": "f32", "saxpy_f16": "f16",
          "saxpy_bf16": "bf16", "relu_f16": "f16", "relu_bf16": "bf16", "copy2d_f32": "f32",
          "relu_inplace_f32": "f32",
@@ -104,9 +121,59 @@ def relu_store_counts(x, np):
     return int(np.count_nonzero(ch)), int(np.count_nonzero(spans))
 
 
-def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(op: str = "add_f32", batch: bool = False) -> str:
+    """Hash of the kernel sources the workload's kernels are built from."""
+    from memory_bound_elementwise_amd import sources
+    return sources.source_hash(sources.family(op, batch))
+
+
+# Operator class of each streaming operation, as rocprofv3 prints the kernel
+# instance (template arguments demangled).
+OP_CLASS = {"add_f32": "OpAddF32", "add_f16": "OpAddF16", "add_bf16": "OpAddBF16",
+            "saxpy_f32": "OpSaxpyF32", "relu_f32": "OpReluF32", "copy_f32": "OpCopyF32",
+            "add_relu_f32": "OpAddReluF32", "saxpy_relu_f32": "OpSaxpyReluF32",
+            "saxpy_f16": "OpSaxpy16<_Float16>", "saxpy_bf16": "OpSaxpy16<__bf16>",
+            "relu_f16": "OpRelu16<_Float16>", "relu_bf16": "OpRelu16<__bf16>",
+            "abs_f32": "OpAbs<unsigned int>", "abs_f16": "OpAbs<unsigned short>",
+            "abs_bf16": "OpAbs<unsigned short>",
+            **{f"{m}_f32": f"OpMapF32<ew::{fn}>" for m, fn in
+               (("scale", "FnScale"), ("add_scalar", "FnAddScalar"), ("sqrt", "FnSqrt"))},
+            **{f"{m}_{d}": f"OpMap16<{h}, ew::{fn}>" for d, h in
+               (("f16", "_Float16"), ("bf16", "__bf16")) for m, fn in
+               (("scale", "FnScale"), ("add_scalar", "FnAddScalar"))},
+            "sqrt_f16": "OpMap16<_Float16, ew::FnSqrtWidenedF16>",
+            "sqrt_bf16": "OpMap16<__bf16, ew::FnSqrtWidenedBF16>"}
+
+
+def _b(v) -> str:
+    return "true" if v else "false"
+
+
+def kernel_instance(w, launch: dict, split: dict):
+    """The kernel instance one launch of the workload runs (the name
+    rocprofv3 reports, without 'void ew::' and the argument list), or None
+    where the record does not determine it."""
+    u = launch.get("unroll")
+    if w.batch:
+        return f"ew_batch_table_kernel<ew::{OP_CLASS[w.op]}, {u}>"
+    if w.op in OP_CLASS:
+        co = split.get("in_coaligned", [1, 1])
+        return f"ew_stream_kernel<ew::{OP_CLASS[w.op]}, {u}, {_b(co[0])}, {_b(co[1])}>"
+    if w.op == "relu_inplace_f32":
+        return f"ew_relu_inplace_kernel<{u}>"
+    if w.op == "gather_walk_f32":
+        return f"ew_gather_kernel<{u}>"
+    path = launch.get("path", "")
+    if w.op == "gather_f32":
+        if path.startswith("contiguous 16-byte loads"):
+            return f"ew_gather2_kernel<{u}, true>"
+        if "passes" in path:
+            return f"ew_gather_passes_kernel<{w.stride % w.n}, false>"
+        if path.startswith("per-output"):
+            return f"ew_gather_kernel<{u}>"
+    if w.op == "copy2d_f32" and path.startswith("LDS-tiled transpose"):
+        return "ew_transpose_kernel"
+    return None
 
 
 def log(msg):
@@ -117,7 +184,7 @@ class Prepared:
     """Device buffers of one workload and a launcher bound to a stream."""
 
     def __init__(self, w, torch, np, ew, synth, stream, inp=None):
-        from tests.gpu_util import upload
+        from harness import upload
         self.w = w
         self.inp = synth.workload_inputs(w) if inp is None else inp
         self.keep = []
@@ -129,15 +196,18 @@ class Prepared:
         self.pre = None          # run before every timed launch (in-place ReLU: restore x)
         self.torch_context = None  # (label, launcher) of PyTorch's kernel for the same op
         self.changed = 0
+        self.batch_plan = self.host_form = None
         if w.op == "relu_inplace_f32":
             x, kx = upload(self.inp["x"], offs.get("x", 0))
             pristine = x.clone()
             self.keep += [kx, pristine]
             self.launch = lambda: ew.ew_relu_inplace_f32(x, stream=s)
-            self.pre = lambda: x.copy_(pristine)
             # the same in-place ReLU storing every element, for comparison
             self.unfused = lambda: ew.ew_relu_f32(x, x, stream=s)
             self.changed, self.spans_changed = relu_store_counts(self.inp["x"], np)
+            # restore x before every timed launch -- unless no element
+            # changes, when every launch does the same work on the same data
+            self.pre = (lambda: x.copy_(pristine)) if self.changed else None
             self.out, self.ptrs = x, (x, x, None)
         elif w.op == "copy2d_f32":
             sr, sc, _, offset = w.view
@@ -166,8 +236,13 @@ class Prepared:
             m = w.n // w.batch
             parts = [(c[k * m:(k + 1) * m], a[k * m:(k + 1) * m], b[k * m:(k + 1) * m])
                      for k in range(w.batch)]
+            # the device item table: one launch for all items
             batch = ew.EwBatch(w.op, [(o, x, y, m) for o, x, y in parts])
+            self.batch_plan = batch.plan
             self.launch = lambda: batch(stream=s)
+            # the host-array form: one launch per BATCH_MAX items
+            host_form = ew.EwBatch(w.op, [(o, x, y, m) for o, x, y in parts], table=False)
+            self.host_form = lambda: host_form(stream=s)
             fn = getattr(ew, "ew_" + w.op)
 
             def separate():
@@ -243,6 +318,8 @@ class Prepared:
                 self.torch_context = ("y.copy_(x)", t_copy)
             elif w.op.rsplit("_", 1)[0] in ew.SCALAR_MAPS + ew.UNARY_MAPS:
                 self._map(w, torch, ew, x, y, stream)
+            elif w.op == "gather_walk_f32":
+                self.launch = lambda: ew.ew_gather_walk_f32(x, y, w.stride, stream=s)
             else:
                 self.launch = lambda: ew.ew_gather_f32(x, y, w.stride, stream=s)
             self.out, self.ptrs = y, (y, x, None)
@@ -281,7 +358,7 @@ class Prepared:
 
     def result(self, torch):
         """One launch on fresh buffers; returns the output copied to the host."""
-        from tests.gpu_util import ELEM, download
+        from harness import ELEM, download
         self.launch()
         torch.cuda.synchronize()
         return download(self.out, ELEM[self.w.op])
@@ -390,7 +467,7 @@ def cpu_baseline_leg(w, inp, got, target_s):
     Returns (number of mismatching elements, cpu_baseline record)."""
     import oracle
     import synth
-    from tests.gpu_util import mismatches
+    from harness import mismatches
 
     def run(d):
         if w.op in ("add_f32", "add_f16", "add_bf16", "add_relu_f32"):
@@ -402,7 +479,7 @@ def cpu_baseline_leg(w, inp, got, target_s):
         if w.op == "copy2d_f32":       # always the full view (see below)
             sr, sc, _, offset = w.view
             return oracle.copy2d_f32(d["base"], offset, sr, sc, w.n // w.cols, w.cols)
-        if w.op == "gather_f32":
+        if w.op in ("gather_f32", "gather_walk_f32"):    # one definition, two kernels
             return oracle.gather_f32(d["x"], w.stride)
         if w.op == "relu_inplace_f32":     # same result as the out-of-place ReLU
             return oracle.relu_f32(d["x"])
@@ -441,7 +518,7 @@ def cpu_baseline_leg(w, inp, got, target_s):
                   f"in {el:.1f} s")
     rec = {"value": round(gbs, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
            "sample": sample + " (scalar C loop, one thread)", "cpu": _cpu_model()}
-    if target_s > 0 and w.op not in ("copy2d_f32", "gather_f32"):
+    if target_s > 0 and w.op not in ("copy2d_f32", "gather_f32", "gather_walk_f32"):
         rec["all_cores"] = _all_cores(w, run, changed, small, m, target_s / 2)
     return bad, rec
 
@@ -509,20 +586,35 @@ def _cpu_model():
     return "unknown"
 
 
-def traffic_for(workload: str, launch_desc: dict):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel source and launch shape; else None."""
+def _committed(path, workload, src_hash, launch_desc):
+    """The record of `workload` in a committed profile index, if it was taken
+    on the given kernel source hash and launch shape; else None."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(path) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     rec = data.get("workloads", {}).get(workload)
-    if not rec or rec.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not rec or rec.get("kernel_source_sha256_16") != src_hash:
         return None
     if rec.get("launch") != launch_desc:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def traffic_for(workload: str, launch_desc: dict, src_hash: str = None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources and launch shape; else None."""
+    rec = _committed(TRAFFIC_JSON, workload, src_hash or kernel_source_hash(), launch_desc)
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def profiled_for(workload: str, launch_desc: dict, src_hash: str = None):
+    """The committed rocprofv3 kernel-trace record of the workload's kernel
+    (average and median duration per dispatch), if it was taken on the current
+    kernel sources and launch shape; else None."""
+    return _committed(KERNEL_TRACE_JSON, workload, src_hash or kernel_source_hash(),
+                      launch_desc)
 
 
 def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_target_s,
@@ -531,17 +623,15 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     plan = prep.plan(ew, cus)
     launch_desc = {"block": plan.block, "grid": plan.grid, "unroll": plan.unroll}
     if w.batch:
-        # one launch shape for the whole call: the table's row for the total n
-        block, bpc, unroll = ew.ew_get_launch_config(w.op, w.n)
-        m = w.n // w.batch
-        vec = 16 // (4 if w.op.endswith("_f32") else 2)
-        tiles = max(1, -(-(m // vec) // (block * min(unroll, 4))))     # per item
-        launch_desc = {"block": block, "unroll": min(unroll, 4), "items": w.batch,
-                       "items_per_launch": ew.BATCH_MAX,
-                       "launches": -(-w.batch // ew.BATCH_MAX),
-                       "grid_per_launch": min(bpc * cus, tiles * min(w.batch, ew.BATCH_MAX)),
-                       "path": "batched: items' tiles numbered consecutively, one kernel"}
+        # one launch for the whole call: the table's row for the total n
+        bp = prep.batch_plan
+        launch_desc = {"block": bp.block, "grid": min(bp.blocks_per_cu * cus, bp.tiles),
+                       "unroll": bp.unroll, "items": bp.items, "tiles": bp.tiles,
+                       "table_bytes": bp.bytes, "launches": 1,
+                       "path": "batched: device item table, one kernel for every item"}
         steps = min(steps, 200)
+    if w.op == "gather_walk_f32":
+        launch_desc["path"] = "per-output index walk (one 4-byte load per output element)"
     if w.op == "gather_f32":
         launch_desc["path"] = ("copy kernel" if w.stride % w.n == 1 else
                                f"{plan.passes} passes, input staged through LDS"
@@ -561,6 +651,8 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     res = {"workload": w.name, "op": w.op, "n": w.n, "launch": launch_desc,
            "split": {"head": plan.head, "vectors": plan.vectors, "tail": plan.tail,
                      "in_coaligned": list(plan.in_coaligned)}}
+    res["kernel"] = kernel_instance(w, launch_desc, res["split"])
+    res["source_sha256_16"] = kernel_source_hash(w.op, bool(w.batch))
     if w.batch:
         res["split"] = {"items": w.batch, "elements_per_item": w.n // w.batch,
                         "note": "consecutive slices of three arrays, every item 16-byte aligned"}
@@ -607,7 +699,11 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
             res["p10_ms"], res["p90_ms"] = round(LAST_DIST["p10"], 5), round(LAST_DIST["p90"], 5)
     gbs = nbytes / (ms / 1e3) / 1e9
     res.update({"ms": round(ms, 5), "gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_GBS, 4),
-                "timing": timing})
+                "timing": timing, "algorithmic_bytes": nbytes})
+    traffic = traffic_for(w.name, launch_desc, res["source_sha256_16"])
+    if traffic is not None:
+        res["traffic_bytes"] = traffic
+        res["traffic_ratio"] = round(traffic / nbytes, 4)
     ctx = prep.torch_context
     if ctx is not None:
         if len(sets) > 1:
@@ -648,6 +744,15 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
             res["separate_calls"] = {"ops": prep.unfused_label, "ms": round(un_ms, 5),
                                      "gbs": round(nbytes / (un_ms / 1e3) / 1e9, 1),
                                      "speedup_of_batch": round(un_ms / ms, 3)}
+            if prep.host_form is not None:
+                hf_ms = (time_rotated(torch, [p.host_form for p in sets], stream, steps, warmup)
+                         if len(sets) > 1 else
+                         time_launches(torch, prep.host_form, stream, steps, warmup, flush=flush))
+                res["host_array_form"] = {
+                    "op": f"ew_batch: the item array in the kernel arguments, "
+                          f"{-(-w.batch // ew.BATCH_MAX)} launches", "ms": round(hf_ms, 5),
+                    "gbs": round(nbytes / (hf_ms / 1e3) / 1e9, 1),
+                    "speedup_of_table": round(hf_ms / ms, 3)}
         else:
             res["unfused"] = {"ops": list(UNFUSED[w.op]), "ms": round(un_ms, 5),
                               "speedup_of_fused": round(un_ms / ms, 3)}
@@ -710,6 +815,97 @@ def run_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):
     return rc
 
 
+def _ratio(a, b):
+    return round(a / b, 4) if a and b else None
+
+
+def attainable(by: dict, value):
+    """The pure read stream and the copy, measured in this run at the
+    headline's size: what the part attains for the two ends of a streaming
+    mix (no write; one write per read) -- the ceiling a two-read-one-write
+    stream is judged against.  None without those records."""
+    rd, cp = by.get(ATTAINABLE["read"]), by.get(ATTAINABLE["copy"])
+    if not (rd and cp and rd.get("gbs") and cp.get("gbs")):
+        return None
+    return {"read_stream_gbs": rd["gbs"], "copy_gbs": cp["gbs"],
+            "value_over_copy": _ratio(value, cp["gbs"]),
+            "value_over_read_stream": _ratio(value, rd["gbs"]),
+            "read_stream": f"{rd['workload']} ({rd.get('kernel')}, stores nothing)",
+            "copy": f"{cp['workload']} ({cp.get('kernel')})"}
+
+
+def strided_over_coalesced(by: dict):
+    """[PerfNotes] 3.2-3.3's experiment at n = 2^26: the strided gather
+    out[i] = in[(2i) mod n] against the coalesced copy, for the per-output
+    index walk (the page's kernel) and the library's gather."""
+    cp = by.get(STRIDED["copy"])
+    if not (cp and cp.get("gbs")):
+        return None
+    out = {"copy_gbs": cp["gbs"]}
+    for key in ("walk", "gather"):
+        r = by.get(STRIDED[key])
+        if r and r.get("gbs"):
+            out[key] = {"gbs": r["gbs"], "over_copy": _ratio(r["gbs"], cp["gbs"]),
+                        "traffic_ratio": r.get("traffic_ratio"), "kernel": r.get("kernel")}
+    out["bytes"] = "logical: 8 per output element for all three"
+    return out
+
+
+def final_line(args, w, res, others, env):
+    """The last stdout line: the main workload's record, compact (the
+    other workloads are printed before it, one line each)."""
+    gbs = res.get("gbs")
+    line = {
+        "metric": METRIC, "value": gbs, "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": res.get("ms"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE[w.op], "data": f"synthetic (seeded {w.dist}, seed {w.seed})",
+        "config": {"workload": w.description, "name": w.name, "op": w.op, "n": w.n,
+                   "launch": res["launch"], "global_batch": w.n, "parallelism": "single GPU"},
+        "parity": res["parity"], "mismatches": res.get("mismatches"),
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2) if gbs else None,
+        "timing": res.get("timing"),
+    }
+    if gbs:
+        alg = res["algorithmic_bytes"]
+        prof = profiled_for(w.name, res["launch"], res["source_sha256_16"])
+        by = {r["workload"]: r for r in others}
+        line["roofline"] = {
+            "bound": "hbm", "achieved": gbs, "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_GBS, 4), "traffic": res.get("traffic_bytes"),
+            "traffic_ratio": res.get("traffic_ratio"), "kernel": res.get("kernel"),
+            "algorithmic_bytes_per_launch": alg,
+            "avg_launch_us": round(res["ms"] * 1e3, 3),
+            "profiled": ({"avg_us": round(prof["avg_ns"] / 1e3, 3),
+                          "median_us": round(prof["median_ns"] / 1e3, 3),
+                          "gbs_at_avg": round(alg / prof["avg_ns"], 1),
+                          "frac_at_avg": round(alg / prof["avg_ns"] / PEAK_GBS, 4),
+                          "summary": "profiles/" + prof["summary"]} if prof else None),
+            "attainable": attainable(by, gbs),
+        }
+        so = strided_over_coalesced(by)
+        if so:
+            line["strided_over_coalesced"] = so
+    if "cpu_baseline" in res:
+        cb = dict(res["cpu_baseline"])
+        allc = cb.pop("all_cores", None)
+        line["cpu_baseline"] = cb
+        if allc:
+            line["cpu_baseline_all_cores"] = {"value": allc["value"], "unit": allc["unit"],
+                                              "cores": allc["cores"]}
+    if "torch_context" in res:
+        line["torch_context_gbs"] = res["torch_context"]["gbs"]
+    if others:
+        line["others"] = {"workloads": len(others),
+                          "parity_pass": sum(r.get("parity") == "PASS" for r in others),
+                          "not_passing": [r["workload"] for r in others
+                                          if r.get("parity") not in ("PASS", None)
+                                          and not r.get("parity", "").startswith("not checked")],
+                          "where": "the JSON lines above this one"}
+    line["env"] = env
+    return line
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -719,6 +915,8 @@ def main(argv=None):
     ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--details", help="also write every record in full to this file, one JSON "
+                                      "line each (the main workload's last)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: each op of the five configurations over "
                          "N = 2^20 .. 2^28 plus odd N, one parity-gated JSON line per point")
@@ -736,6 +934,7 @@ def main(argv=None):
     import torch
 
     import memory_bound_elementwise_amd as ew
+    from memory_bound_elementwise_amd import sources
     import synth
 
     if not torch.cuda.is_available():
@@ -755,50 +954,12 @@ def main(argv=None):
     res, prep, ms = measure(w, torch, np, ew, synth, stream, args.steps, args.warmup, cus,
                             flush_buf, args.cpu_seconds, check=not args.no_cpu_baseline)
     log(f"parity {res['parity']}; {res.get('gbs')} GB/s")
-
-    line = {
-        "metric": "achieved HBM GB/s (read+write bytes/time) and % of MI355X peak, N=2^28",
-        "value": res.get("gbs"),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": res.get("ms"),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": DTYPE[w.op],
-        "data": "synthetic (seeded: " + w.dist + ")",
-        "config": {"workload": w.description, "name": w.name, "op": w.op, "n": w.n,
-                   "offsets_elems": w.offsets, "launch": res["launch"], "split": res["split"],
-                   "global_batch": w.n, "parallelism": "single GPU"},
-        "parity": res["parity"],
-        "pct_of_peak": round(100 * res["gbs"] / PEAK_GBS, 2) if res.get("gbs") else None,
-    }
-    for k in ("p10_ms", "p90_ms", "timing", "warm_gbs", "flushed_per_launch", "torch_context",
-              "graph", "unfused", "separate_calls"):
-        if k in res:
-            line[k] = res[k]
-    if ms is not None:
-        traffic = traffic_for(w.name, res["launch"])
-        line["roofline"] = {"bound": "hbm", "achieved": res["gbs"], "peak": PEAK_GBS,
-                            "unit": "GB/s", "frac": round(res["gbs"] / PEAK_GBS, 4),
-                            "traffic": traffic,
-                            "kernel": f"ew_stream_kernel<{w.op}, U={res['launch']['unroll']}>",
-                            "algorithmic_bytes_per_launch": algorithmic_bytes(
-                                w.op, w.n, w.cols if w.op == "bias_relu_f32" else 0,
-                                res.get("changed", 0)),
-                            "avg_launch_ms": res["ms"]}
     del prep
     torch.cuda.empty_cache()
+    details = open(args.details, "w") if args.details else None
 
-    if "cpu_baseline" in res:
-        line["cpu_baseline"] = res.pop("cpu_baseline")
-        if "all_cores" in line["cpu_baseline"]:
-            line["cpu_baseline_all_cores"] = line["cpu_baseline"].pop("all_cores")
-
+    others = []
     if not args.no_others:
-        others = []
         for name, ow in synth.WORKLOADS.items():
             if name == w.name:
                 continue
@@ -810,32 +971,37 @@ def main(argv=None):
                 del p
             except Exception as exc:
                 # recorded, and nothing more is launched (the error may have left the
-                # device unusable); the headline line below still prints
-                others.append({"workload": name, "op": ow.op, "n": ow.n,
-                               "error": f"{type(exc).__name__}: {exc}"})
+                # device unusable); the final line below still prints
+                r = {"workload": name, "op": ow.op, "n": ow.n,
+                     "error": f"{type(exc).__name__}: {exc}"}
+                others.append(r)
+                print(json.dumps(r), flush=True)
                 log(f"other config {name} failed, remaining configs skipped: {exc}")
                 break
             others.append(r)
+            print(json.dumps(r), flush=True)
+            if details:
+                details.write(json.dumps(r) + "\n")
             torch.cuda.empty_cache()
-        line["other_configs"] = others
-        if any("error" in r for r in others):
-            line["other_configs_incomplete"] = True
-        by = {r["workload"]: r for r in others + [res]}
-        sg, cg = by.get("cfg5b_gather_f32_2e26_s2"), by.get("cfg5a_copy_f32_2e26")
-        if sg and cg and sg.get("gbs") and cg.get("gbs"):
-            # the fifth configuration's comparison: strided gather vs coalesced copy
-            line["strided_over_coalesced"] = {
-                "gather_s2_gbs": sg["gbs"], "copy_gbs": cg["gbs"],
-                "ratio": round(sg["gbs"] / cg["gbs"], 4),
-                "traffic_note": "logical bytes for both; the gather reads each input line once"}
 
-    line["env"] = {"device": torch.cuda.get_device_name(0),
-                   "arch": getattr(dev_props, "gcnArchName", None), "cus": cus,
-                   "hbm_bytes": dev_props.total_memory, "clocks": _clocks(dev_props),
-                   "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
-                   "numpy": np.__version__, "kernel_source_sha256_16": kernel_source_hash(),
-                   "input_sha256": input_sha}
-    print(json.dumps(line), flush=True)
+    env = {"device": torch.cuda.get_device_name(0),
+           "arch": getattr(dev_props, "gcnArchName", None), "cus": cus,
+           "clocks": _clocks(dev_props), "torch": torch.__version__,
+           "hip": getattr(torch.version, "hip", None), "numpy": np.__version__,
+           "kernel_source_sha256_16": res["source_sha256_16"],
+           "sources_sha256_16": sources.all_hashes(), "input_sha256": input_sha}
+    line = final_line(args, w, res, others, env)
+    if details:
+        details.write(json.dumps({**res, "env": env}) + "\n")
+        details.close()
+    text = json.dumps(line, separators=(",", ":"))
+    if len(text) > FINAL_LINE_MAX_BYTES:      # never let the record outgrow the reader
+        for k in ("strided_over_coalesced", "cpu_baseline_all_cores", "others", "env"):
+            line.pop(k, None)
+            text = json.dumps(line, separators=(",", ":"))
+            if len(text) <= FINAL_LINE_MAX_BYTES:
+                break
+    print(text, flush=True)
     return 1 if res["parity"] == "FAIL" else 0
 
 

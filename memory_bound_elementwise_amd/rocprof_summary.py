@@ -1,37 +1,35 @@
 """Summarise rocprofv3 CSV output of bench.py runs into short text records.
 
-Kernel durations (from ``rocprofv3 --kernel-trace --stats -f csv``):
+Kernel durations of every workload in one traced bench run (per-dispatch
+average, median, p10 and p90, each workload's kernel matched by the kernel
+instance its record names, grid and block), written as a text table and
+merged into profiles/kernel_trace.json, which bench.py reads back for the
+main workload's ``roofline.profiled``:
 
-    python -m memory_bound_elementwise_amd.rocprof_summary trace \\
-        --stats DIR/NAME_kernel_stats.csv --kernel REGEX --bytes B \\
-        --bench-json BENCH_OUTPUT_OF_THE_PROFILED_RUN \\
+    rocprofv3 --kernel-trace --stats -f csv -d DIR -o run -- python3 bench.py ... > OUT
+    python -m memory_bound_elementwise_amd.rocprof_summary configs \
+        --trace DIR/run_kernel_trace.csv --bench-json OUT \
         --command "the rocprofv3 command line" --out profiles/FILE.txt
 
-Every configuration's kernel durations from the kernel trace of one default
-bench run (per-dispatch median, matched by kernel name, grid and block):
-
-    python -m memory_bound_elementwise_amd.rocprof_summary configs \\
-        --trace DIR/NAME_kernel_trace.csv --bench-json BENCH_OUTPUT \\
-        --command "the rocprofv3 command line" --out profiles/FILE.txt
-
-HBM traffic (from two ``rocprofv3 --pmc`` runs per kernel, FETCH_SIZE then
+HBM traffic (from two ``rocprofv3 --pmc`` runs per workload, FETCH_SIZE then
 WRITE_SIZE, each in KiB per dispatch).  The counters are calibrated on the
 plain copy kernel of known size: scale = algorithmic bytes / counted bytes,
 per counter.  The result is written as text and merged into
 profiles/traffic.json, which bench.py reads (keyed by workload, kernel
 source hash and launch shape):
 
-    python -m memory_bound_elementwise_amd.rocprof_summary traffic \\
-        --workload NAME --kernel REGEX --bytes B \\
-        --fetch DIR/..._counter_collection.csv --write DIR/..._counter_collection.csv \\
-        --calib-kernel REGEX --calib-bytes-read R --calib-bytes-written W \\
-        --calib-fetch CSV --calib-write CSV --launch '{"block": .., "grid": .., "unroll": ..}' \\
-        --bench-json FETCH_RUN_OUTPUT --bench-json-write WRITE_RUN_OUTPUT \\
+    python -m memory_bound_elementwise_amd.rocprof_summary traffic \
+        --workload NAME --family FAMILY --kernel REGEX \
+        --fetch DIR/..._counter_collection.csv --write DIR/..._counter_collection.csv \
+        --calib-kernel REGEX --calib-bytes-read R --calib-bytes-written W \
+        --calib-fetch CSV --calib-write CSV \
+        --bench-json FETCH_RUN_OUTPUT --bench-json-write WRITE_RUN_OUTPUT \
         --command-fetch "..." --command-write "..." --command-calib "..." --out profiles/FILE.txt
 
-The kernel source hash written into every record is the one the profiled
-bench.py run printed (env.kernel_source_sha256_16), never the hash of the
-source as it is when the summary is written.
+The launch shape, the algorithmic bytes and the kernel source hash written
+into every record are the ones the profiled bench.py run printed for that
+workload (its record's ``source_sha256_16``: the hash of its kernel family's
+sources), never the hash of the source as it is when the summary is written.
 """
 import argparse
 import csv
@@ -43,23 +41,63 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_TRACE_JSON = os.path.join(ROOT, "profiles", "kernel_trace.json")
 
 
-def bench_record(path):
-    """The JSON line bench.py printed in the profiled run (its last line)."""
+def bench_records(path):
+    """Every record a bench.py run printed: the other workloads' lines and
+    the final line (the main workload), as {workload: record}.  The final
+    line's record carries the kernel fields of the main workload under its
+    own keys; it is keyed by config.name."""
+    out = {}
     with open(path) as f:
-        return json.loads(f.read().strip().splitlines()[-1])
+        lines = [ln for ln in f.read().splitlines() if ln.startswith("{")]
+    for ln in lines[:-1]:
+        r = json.loads(ln)
+        if "workload" in r:
+            out[r["workload"]] = r
+    last = json.loads(lines[-1])
+    cfg = last.get("config", {})
+    main = {"workload": cfg.get("name"), "op": cfg.get("op"), "n": cfg.get("n"),
+            "launch": cfg.get("launch"), "gbs": last.get("value"), "ms": last.get("ms_per_step"),
+            "timing": last.get("timing"),
+            "kernel": (last.get("roofline") or {}).get("kernel"),
+            "algorithmic_bytes": (last.get("roofline") or {}).get("algorithmic_bytes_per_launch"),
+            "source_sha256_16": last.get("env", {}).get("kernel_source_sha256_16"),
+            "final_line": True}
+    out[main["workload"]] = main
+    return out
 
 
-def profiled_hash(bench_json):
-    """The kernel source hash the profiled run was built from: taken from the
-    bench line it printed, so that a summary written later, after the source
-    has changed, cannot claim the new hash.  Refuses a bench line without one."""
-    rec = bench_record(bench_json)
-    h = rec.get("env", {}).get("kernel_source_sha256_16")
+def bench_record(path, workload):
+    """The record of one workload in a bench.py output file."""
+    recs = bench_records(path)
+    if workload not in recs:
+        raise SystemExit(f"{path}: no record of workload {workload!r}")
+    return recs[workload]
+
+
+def profiled_hash(bench_json, workload):
+    """The kernel-source hash (of the workload's kernel family) that the
+    profiled run was built from: taken from the record bench.py printed, so
+    that a summary written later, after the source has changed, cannot claim
+    the new hash.  Refuses a record without one."""
+    h = bench_record(bench_json, workload).get("source_sha256_16")
     if not h:
-        raise SystemExit(f"{bench_json}: no env.kernel_source_sha256_16")
+        raise SystemExit(f"{bench_json}: no source hash for {workload}")
     return h
+
+
+def _merge(path, about, workload, rec):
+    try:
+        with open(path) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {"about": about, "workloads": {}}
+    data["workloads"][workload] = rec
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
 
 
 def _rows(path):
@@ -99,39 +137,6 @@ def dispatch_durations(path, kernel_re):
             if rx.search(r.get("Kernel_Name", ""))]
 
 
-def cmd_trace(a):
-    name, calls, avg, mn, mx = kernel_stats(a.stats, a.kernel)
-    gbs = a.bytes / avg
-    src_hash = profiled_hash(a.bench_json)
-    bench_ms = bench_record(a.bench_json).get("ms_per_step")
-    text = [
-        f"# {a.title}",
-        "",
-        f"command: {a.command}",
-        f"source:  rocprofv3 kernel_stats.csv ({os.path.basename(a.stats)})",
-        "",
-        f"kernel:          {name}",
-        f"dispatches:      {calls}",
-        f"average:         {avg / 1000:.3f} us   (min {mn / 1000:.3f}, max {mx / 1000:.3f})",
-    ]
-    if a.trace:
-        d = sorted(dispatch_durations(a.trace, a.kernel))
-        text.append(f"median:          {statistics.median(d) / 1000:.3f} us   (p10 "
-                    f"{d[len(d) // 10] / 1000:.3f}, p90 {d[(9 * len(d)) // 10] / 1000:.3f}; "
-                    f"{len(d)} dispatches in {os.path.basename(a.trace)})")
-    text += [
-        f"algorithmic:     {a.bytes} bytes per launch",
-        f"achieved:        {gbs:.1f} GB/s = {100 * gbs / 8000:.2f} % of 8000 GB/s",
-        f"kernel source:   ew_kernels.hip sha256[:16] {src_hash} (of the profiled run)",
-    ]
-    if bench_ms:
-        text.append(f"bench.py events: {bench_ms:.5f} ms per step "
-                    f"({100 * (bench_ms * 1e6 - avg) / avg:+.2f} % vs the trace average)")
-    with open(a.out, "w") as f:
-        f.write("\n".join(text) + "\n")
-    print("\n".join(text))
-
-
 def cmd_traffic(a):
     fetch_kib, nd_f = counter_per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
     write_kib, nd_w = counter_per_dispatch(a.write, a.kernel, "WRITE_SIZE")
@@ -142,10 +147,12 @@ def cmd_traffic(a):
     fetch_b = fetch_kib * 1024 * scale_f
     write_b = write_kib * 1024 * scale_w
     total = fetch_b + write_b
-    launch = json.loads(a.launch)
-    src_hash = profiled_hash(a.bench_json)
-    if profiled_hash(a.bench_json_write) != src_hash:
+    rec = bench_record(a.bench_json, a.workload)
+    launch = rec["launch"]
+    src_hash = profiled_hash(a.bench_json, a.workload)
+    if profiled_hash(a.bench_json_write, a.workload) != src_hash:
         raise SystemExit("the FETCH_SIZE and WRITE_SIZE runs were built from different sources")
+    alg = rec["algorithmic_bytes"]
     text = [
         f"# HBM traffic: {a.workload}",
         "",
@@ -153,95 +160,78 @@ def cmd_traffic(a):
         f"write command: {a.command_write}",
         f"calibration:   {a.command_calib}",
         "",
-        f"kernel:            {a.kernel}  launch {launch}",
+        f"kernel:            {rec.get('kernel') or a.kernel}  launch {json.dumps(launch)}",
         f"FETCH_SIZE:        {fetch_kib:.0f} KiB per dispatch (median of {nd_f})",
         f"WRITE_SIZE:        {write_kib:.0f} KiB per dispatch (median of {nd_w})",
         f"calibration copy:  FETCH {cal_f:.0f} KiB for {a.calib_bytes_read} B read -> scale "
         f"{scale_f:.4f};  WRITE {cal_w:.0f} KiB for {a.calib_bytes_written} B written -> scale "
         f"{scale_w:.4f}",
         f"HBM bytes/launch:  fetch {fetch_b:.0f} + write {write_b:.0f} = {total:.0f}",
-        f"algorithmic bytes: {a.bytes}  (traffic / algorithmic = {total / a.bytes:.4f})",
-        f"kernel source:     ew_kernels.hip sha256[:16] {src_hash} (of the profiled runs)",
+        f"algorithmic bytes: {alg}  (traffic / algorithmic = {total / alg:.4f})",
+        f"kernel sources:    {a.family} family sha256[:16] {src_hash} (of the profiled runs)",
     ]
     with open(a.out, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
-    try:
-        with open(TRAFFIC_JSON) as f:
-            data = json.load(f)
-    except (OSError, ValueError):
-        data = {"about": "HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
-                         "scaled by the copy-kernel calibration; see the .txt summaries",
-                "workloads": {}}
-    data["workloads"][a.workload] = {
-        "kernel": a.kernel, "launch": launch, "kernel_source_sha256_16": src_hash,
+    _merge(TRAFFIC_JSON, "HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by "
+                         "the copy-kernel calibration; see the .txt summaries", a.workload, {
+        "kernel": rec.get("kernel") or a.kernel, "launch": launch,
+        "kernel_source_sha256_16": src_hash,
         "fetch_kib": fetch_kib, "write_kib": write_kib, "scale_fetch": scale_f,
         "scale_write": scale_w, "hbm_bytes_per_launch": round(total),
-        "algorithmic_bytes": a.bytes, "summary": os.path.basename(a.out)}
-    with open(TRAFFIC_JSON, "w") as f:
-        json.dump(data, f, indent=1, sort_keys=True)
-        f.write("\n")
-
-
-# Kernel of each operation in a kernel trace (template operator name).
-OP_KERNEL = {"add_f32": "OpAddF32", "add_f16": "OpAddF16", "add_bf16": "OpAddBF16",
-             "saxpy_f32": "OpSaxpyF32", "relu_f32": "OpReluF32", "copy_f32": "OpCopyF32"}
-BYTES_PER_ELEM = {"add_f32": 12, "add_f16": 6, "add_bf16": 6, "saxpy_f32": 12, "relu_f32": 8,
-                  "copy_f32": 8, "gather_f32": 8}
+        "algorithmic_bytes": alg, "summary": os.path.basename(a.out)})
 
 
 def cmd_configs(a):
-    """Per-dispatch durations of every configuration's kernel in one traced
-    default bench run: each record of the bench line (main workload and
-    other_configs) whose op is a streaming op or the gather is matched to the
-    trace by kernel name, grid and block."""
-    line = bench_record(a.bench_json)
-    src_hash = line.get("env", {}).get("kernel_source_sha256_16")
-    main = {"workload": line["config"]["name"], "op": line["config"]["op"],
-            "n": line["config"]["n"], "launch": line["config"]["launch"],
-            "split": line["config"]["split"], "gbs": line["value"], "timing": "back-to-back, mean"}
-    recs = [main] + [r for r in line.get("other_configs", [])
-                     if r.get("op") in BYTES_PER_ELEM and r.get("workload", "").startswith(("cfg", "headline"))]
+    """Per-dispatch durations of every workload's kernel in one traced bench
+    run: each record that names its kernel instance is matched to the trace
+    by kernel name, grid and block.  Writes the text table and one record per
+    workload to profiles/kernel_trace.json (keyed by workload, kernel source
+    hash and launch shape, which bench.py reads back)."""
+    recs = bench_records(a.bench_json)
     rows = _rows(a.trace)
     text = [
-        "# Kernel durations of the five configurations and the headline (rocprofv3 kernel trace)",
+        "# Kernel durations per workload (rocprofv3 kernel trace of one bench.py run)",
         "",
         f"command: {a.command}",
         f"source:  per-dispatch durations (End - Start) in {os.path.basename(a.trace)}, each "
-        "configuration's kernel matched by name, grid and block",
+        "workload's kernel matched by name, grid and block",
         "note:    for the cold workloads (<= 1 GiB) the dispatches include the rotated launches "
         "that bench.py times, the flushed per-launch ones and the warm ones; all include the "
         "parity launch",
-        "         the bench.py column is that profiled run's own figure: the tracer adds host-side "
-        "cost to every launch, which shows only where back-to-back launches are bound by the "
-        "host (the 2^20 add)",
-        f"kernel source: ew_kernels.hip sha256[:16] {src_hash} (of the profiled run)",
+        "         the bench.py column is that profiled run's own figure (its timing method in "
+        "the record): the tracer adds host-side cost to every launch, which shows only where "
+        "back-to-back launches are bound by the host (small arrays)",
         "",
-        "| workload | kernel | grid x block | dispatches | median us (p10, p90) | GB/s at the median "
-        "| bench.py GB/s (its timing) |",
-        "|---|---|---|---|---|---|---|",
+        "| workload | kernel | grid x block | dispatches | average us | median us (p10, p90) "
+        "| GB/s at the average | bench.py GB/s | sources sha256[:16] |",
+        "|---|---|---|---|---|---|---|---|---|",
     ]
-    for r in sorted(recs, key=lambda r: r["workload"]):
-        op, n, lc = r["op"], r["n"], r["launch"]
-        if op == "gather_f32":
-            rx = re.compile(r"ew_gather(2|_passes)?_kernel")
-        else:
-            co = ["true" if c else "false" for c in r["split"]["in_coaligned"]]
-            rx = re.compile(re.escape(f"ew_stream_kernel<ew::{OP_KERNEL[op]}, {lc['unroll']}, "
-                                      f"{co[0]}, {co[1]}>"))
+    wanted = [w for w in a.workloads.split(",")] if a.workloads else sorted(recs)
+    for name in wanted:
+        r = recs.get(name)
+        if not r or not r.get("kernel") or not r.get("gbs"):
+            continue
+        lc = r["launch"]
+        kname = "ew::" + r["kernel"]
         d = sorted(int(x["End_Timestamp"]) - int(x["Start_Timestamp"]) for x in rows
-                   if rx.search(x["Kernel_Name"])
+                   if kname + "(" in x["Kernel_Name"].replace("void ", "")
                    and int(x["Workgroup_Size_X"]) == lc["block"]
                    and int(x["Grid_Size_X"]) == lc["block"] * lc["grid"])
         if not d:
-            raise SystemExit(f"no dispatch of {r['workload']}'s kernel in {a.trace}")
-        med = statistics.median(d)
-        name = next(x["Kernel_Name"] for x in rows if rx.search(x["Kernel_Name"]))
-        name = name.replace("void ew::", "").split("(")[0]
-        gbs = BYTES_PER_ELEM[op] * n / med
-        text.append(f"| {r['workload']} | {name} | {lc['grid']} x {lc['block']} | {len(d)} | "
-                    f"{med / 1000:.2f} ({d[len(d) // 10] / 1000:.2f}, {d[(9 * len(d)) // 10] / 1000:.2f}) | "
-                    f"{gbs:.1f} | {r['gbs']} ({r['timing']}) |")
+            print(f"no dispatch of {name}'s kernel {kname} in {a.trace}", file=sys.stderr)
+            continue
+        avg, med = statistics.fmean(d), statistics.median(d)
+        p10, p90 = d[len(d) // 10], d[(9 * len(d)) // 10]
+        alg = r["algorithmic_bytes"]
+        text.append(f"| {name} | {r['kernel']} | {lc['grid']} x {lc['block']} | {len(d)} | "
+                    f"{avg / 1000:.2f} | {med / 1000:.2f} ({p10 / 1000:.2f}, {p90 / 1000:.2f}) | "
+                    f"{alg / avg:.1f} | {r['gbs']} | {r['source_sha256_16']} |")
+        _merge(KERNEL_TRACE_JSON, "rocprofv3 kernel-trace durations per workload, from the "
+                                  "summary named in each record", name, {
+            "kernel": r["kernel"], "launch": lc, "kernel_source_sha256_16": r["source_sha256_16"],
+            "dispatches": len(d), "avg_ns": round(avg, 1), "median_ns": med, "p10_ns": p10,
+            "p90_ns": p90, "algorithmic_bytes": alg, "summary": os.path.basename(a.out)})
     with open(a.out, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
@@ -251,21 +241,9 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
-    t = sub.add_parser("trace")
-    t.add_argument("--stats", required=True)
-    t.add_argument("--kernel", required=True)
-    t.add_argument("--bytes", type=int, required=True)
-    t.add_argument("--command", required=True)
-    t.add_argument("--title", default="Kernel duration")
-    t.add_argument("--trace", help="the run's kernel_trace.csv: also report the per-dispatch "
-                                   "median")
-    t.add_argument("--bench-json", required=True,
-                   help="the bench.py output of the profiled run (events and source hash)")
-    t.add_argument("--out", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("--workload", required=True)
     r.add_argument("--kernel", required=True)
-    r.add_argument("--bytes", type=int, required=True)
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
     r.add_argument("--calib-kernel", required=True)
@@ -273,7 +251,8 @@ def main(argv=None):
     r.add_argument("--calib-bytes-written", type=int, required=True)
     r.add_argument("--calib-fetch", required=True)
     r.add_argument("--calib-write", required=True)
-    r.add_argument("--launch", required=True)
+    r.add_argument("--family", required=True, help="kernel family of the workload "
+                                                   "(stream, batch, gather, view)")
     r.add_argument("--command-fetch", required=True)
     r.add_argument("--command-write", required=True)
     r.add_argument("--command-calib", required=True)
@@ -286,9 +265,11 @@ def main(argv=None):
     c.add_argument("--trace", required=True, help="kernel_trace.csv of a default bench run")
     c.add_argument("--bench-json", required=True, help="that run's bench.py output")
     c.add_argument("--command", required=True)
+    c.add_argument("--workloads", help="comma-separated workloads (default: every record "
+                                       "naming its kernel)")
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"trace": cmd_trace, "traffic": cmd_traffic, "configs": cmd_configs}[a.cmd](a)
+    {"traffic": cmd_traffic, "configs": cmd_configs}[a.cmd](a)
     return 0
 
 

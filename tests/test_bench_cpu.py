@@ -2,6 +2,7 @@
 in-place ReLU's store counts, the traffic record lookup and the one-GPU
 contract."""
 import json
+import os
 import subprocess
 import sys
 
@@ -38,7 +39,7 @@ def test_relu_store_counts_follow_the_reading_of_the_relu():
 
 
 def test_traffic_is_reported_only_for_the_current_kernel_source(tmp_path, monkeypatch):
-    rec = {"workloads": {"w": {"kernel_source_sha256_16": bench.kernel_source_hash(),
+    rec = {"workloads": {"w": {"kernel_source_sha256_16": bench.kernel_source_hash("add_f32"),
                                "launch": {"block": 1024, "grid": 7, "unroll": 1},
                                "hbm_bytes_per_launch": 123}}}
     f = tmp_path / "traffic.json"
@@ -47,9 +48,125 @@ def test_traffic_is_reported_only_for_the_current_kernel_source(tmp_path, monkey
     assert bench.traffic_for("w", {"block": 1024, "grid": 7, "unroll": 1}) == 123
     assert bench.traffic_for("w", {"block": 512, "grid": 7, "unroll": 1}) is None
     assert bench.traffic_for("other", {"block": 1024, "grid": 7, "unroll": 1}) is None
+    # a record taken on another family's sources does not apply
+    assert bench.traffic_for("w", {"block": 1024, "grid": 7, "unroll": 1},
+                             bench.kernel_source_hash("gather_f32")) is None
     rec["workloads"]["w"]["kernel_source_sha256_16"] = "0" * 16
     f.write_text(json.dumps(rec))
     assert bench.traffic_for("w", {"block": 1024, "grid": 7, "unroll": 1}) is None
+
+
+def test_source_hashes_cover_each_family_and_the_shared_headers(tmp_path, monkeypatch):
+    """A family's hash changes with its own file and with the shared device
+    headers, and not with another family's file."""
+    import shutil
+    from memory_bound_elementwise_amd import sources
+    for name in os.listdir(sources.CSRC):
+        shutil.copy(os.path.join(sources.CSRC, name), tmp_path / name)
+    monkeypatch.setattr(sources, "CSRC", str(tmp_path))
+    before = sources.all_hashes()
+    assert len(set(before.values())) == len(before)
+    with open(tmp_path / "ew_view.hip", "a") as f:
+        f.write("\n// edit\n")
+    after = sources.all_hashes()
+    assert after["view"] != before["view"]
+    assert all(after[k] == before[k] for k in ("stream", "batch", "gather"))
+    with open(tmp_path / "ew_gather.hip", "a") as f:
+        f.write("\n// edit\n")
+    again = sources.all_hashes()
+    assert again["gather"] != after["gather"] and again["view"] != after["view"]
+    with open(tmp_path / "ew_device.h", "a") as f:
+        f.write("\n// edit\n")
+    last = sources.all_hashes()
+    assert all(last[k] != again[k] for k in last)
+    assert sources.family("gather_walk_f32") == "gather"
+    assert sources.family("copy2d_f32") == "view"
+    assert sources.family("add_f32", batch=True) == "batch"
+    assert sources.family("sqrt_bf16") == "stream"
+
+
+def test_kernel_instance_names_match_the_profiler_s_demangled_names():
+    import synth
+    W = synth.WORKLOADS
+    split = {"in_coaligned": [1, 1]}
+    assert (bench.kernel_instance(W["headline_add_f32_2e28"], {"unroll": 1}, split)
+            == "ew_stream_kernel<ew::OpAddF32, 1, true, true>")
+    assert (bench.kernel_instance(W["cfg2_add_f32_2e28p3_offA1"], {"unroll": 1},
+                                  {"in_coaligned": [0, 1]})
+            == "ew_stream_kernel<ew::OpAddF32, 1, false, true>")
+    assert (bench.kernel_instance(W["sqrt_bf16_2e28"], {"unroll": 1}, split)
+            == "ew_stream_kernel<ew::OpMap16<__bf16, ew::FnSqrtWidenedBF16>, 1, true, true>")
+    assert (bench.kernel_instance(W["relu_inplace_f32_2e28_nonneg"], {"unroll": 1}, split)
+            == "ew_relu_inplace_kernel<1>")
+    assert (bench.kernel_instance(W["gather_walk_f32_2e26_s2"], {"unroll": 1}, split)
+            == "ew_gather_kernel<1>")
+    assert (bench.kernel_instance(W["cfg5b_gather_f32_2e26_s2"],
+                                  {"unroll": 1, "path": "contiguous 16-byte loads, even "
+                                                        "elements kept"}, split)
+            == "ew_gather2_kernel<1, true>")
+    assert (bench.kernel_instance(W["batch_add_f32_1024x1024"], {"unroll": 2}, split)
+            == "ew_batch_table_kernel<ew::OpAddF32, 2>")
+
+
+def _fake_record(name, op, n, gbs, **kw):
+    ms = bench.algorithmic_bytes(op, n) / (gbs * 1e9) * 1e3
+    rec = {"workload": name, "op": op, "n": n, "gbs": gbs, "ms": round(ms, 5),
+           "parity": "PASS", "mismatches": 0, "kernel": f"k<{op}>",
+           "launch": {"block": 1024, "grid": 65536, "unroll": 1},
+           "split": {"head": 0, "vectors": n // 4, "tail": 0, "in_coaligned": [1, 1]},
+           "source_sha256_16": "0" * 16, "algorithmic_bytes": bench.algorithmic_bytes(op, n),
+           "timing": "back-to-back, mean"}
+    rec.update(kw)
+    return rec
+
+
+def test_final_line_is_one_compact_json_record_with_roofline_and_cpu_baseline():
+    """The driver reads the last stdout line alone: it must parse on its own,
+    stay well under 4 KB, and carry the metric, roofline (with the attainable
+    streams and the strided comparison) and cpu_baseline."""
+    import argparse
+    import synth
+    w = synth.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    assert (w.op, w.n, w.seed, w.offsets) == ("add_f32", 1 << 28, 100, {})
+    sample = "add_f32 on the first 67108864 elements of the workload's inputs, 9 passes " \
+             "in 12.3 s (scalar C loop, one thread)"
+    res = _fake_record(w.name, "add_f32", w.n, 6500.0, cpu_baseline={
+        "value": 30.1, "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample,
+        "cpu": "AMD EPYC", "all_cores": {"value": 220.0, "unit": "GB/s", "cores": 16,
+                                         "sample": "x" * 200}},
+        torch_context={"op": "torch.add", "gbs": 6000.0})
+    others = [_fake_record(name, synth.WORKLOADS[name].op, synth.WORKLOADS[name].n, 6400.0)
+              for name in synth.WORKLOADS if name != w.name]
+    others[3]["parity"] = "FAIL"
+    args = argparse.Namespace(steps=20, warmup=5)
+    env = {"device": "AMD Instinct MI355X", "arch": "gfx950:sramecc+:xnack-", "cus": 256,
+           "clocks": {"sclk": "2400Mhz", "mclk": "2000Mhz"}, "torch": "2.10", "hip": "7.0",
+           "numpy": "2.2", "kernel_source_sha256_16": "0" * 16,
+           "sources_sha256_16": {k: "0" * 16 for k in ("stream", "batch", "gather", "view")},
+           "input_sha256": {"a": "1" * 16, "b": "2" * 16}}
+    line = bench.final_line(args, w, res, others, env)
+    text = json.dumps(line, separators=(",", ":"))
+    assert len(text) < 3000, len(text)
+    out = "\n".join([json.dumps(r) for r in others] + [text])
+    last = json.loads(out.splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "parity", "roofline", "cpu_baseline", "cpu_baseline_all_cores"):
+        assert key in last, key
+    assert last["metric"] == json.load(open(os.path.join(ROOT, "BASELINE.json")))["metric"]
+    assert last["value"] == 6500.0 and last["unit"] == "GB/s" and last["dtype"] == "f32"
+    rl = last["roofline"]
+    assert rl["bound"] == "hbm" and rl["peak"] == 8000.0 and rl["unit"] == "GB/s"
+    assert rl["frac"] == round(6500.0 / 8000, 4)
+    assert rl["algorithmic_bytes_per_launch"] == 12 * (1 << 28)
+    assert rl["attainable"]["copy_gbs"] == 6400.0
+    assert rl["attainable"]["value_over_copy"] == round(6500 / 6400, 4)
+    so = last["strided_over_coalesced"]
+    assert so["walk"]["over_copy"] == 1.0 and so["gather"]["over_copy"] == 1.0
+    assert last["cpu_baseline"]["kind"] == "oracle" and "all_cores" not in last["cpu_baseline"]
+    assert last["cpu_baseline_all_cores"]["cores"] == 16
+    assert last["others"]["not_passing"] == [others[3]["workload"]]
+    assert last["config"]["name"] == "headline_add_f32_2e28"
 
 
 def test_more_than_one_gpu_exits_with_a_message():
