@@ -71,7 +71,8 @@ typedef enum ew_status {
     EW_ERR_MISALIGNED = -2,  /* pointer not aligned to its element size */
     EW_ERR_OVERLAP = -3,     /* output partially overlaps an input */
     EW_ERR_NO_DEVICE = -4,   /* no HIP device is usable */
-    EW_ERR_HIP = -5          /* a HIP runtime call failed; see ew_last_hip_error() */
+    EW_ERR_HIP = -5,         /* a HIP runtime call failed; see ew_last_hip_error() */
+    EW_ERR_TOO_LARGE = -6    /* a batch table larger than EW_BATCH_SCRATCH_BYTES */
 } ew_status_t;
 
 /* ------------------------------------------------------------------------ */
@@ -337,6 +338,26 @@ ew_status_t ew_batch_build(const char *op, const ew_batch_item_t *items, size_t 
  * read). */
 ew_status_t ew_batch_run(const ew_batch_plan_t *plan, float alpha, const void *table,
                          hipStream_t stream);
+
+/* For callers that cannot allocate device memory (no hipMalloc of their own
+ * for the table: code that must not allocate, allocation-free serving
+ * loops): ew_batch_run with the table image taken from host memory and
+ * placed by the library in a static device array of EW_BATCH_SCRATCH_BYTES
+ * that it holds on each GPU it runs on until the process ends.  The call
+ * allocates nothing.  It waits for `stream` (earlier work may still read
+ * the array), copies the plan->bytes bytes of table_host (the image
+ * ew_batch_build wrote, in host memory) into the array on the current
+ * device, waits for the copy, and launches the kernel asynchronously;
+ * table_host may be reused when the call returns.  Because it waits, it
+ * cannot be captured into a graph (ew_batch_run with a caller-owned device
+ * table can).  Every call on one GPU shares that GPU's array, which keeps
+ * the last call's table: calls that overlap on one GPU -- on different
+ * streams, or from several threads -- race; calls on one stream do not.
+ * plan->bytes > EW_BATCH_SCRATCH_BYTES -> EW_ERR_TOO_LARGE (use
+ * ew_batch_run); other errors as for ew_batch_run. */
+#define EW_BATCH_SCRATCH_BYTES (256 * 1024)
+ew_status_t ew_batch_run_static(const ew_batch_plan_t *plan, float alpha, const void *table_host,
+                                hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Fused chains: one pass over memory instead of two                         */

@@ -30,7 +30,8 @@ __all__ = [
     "ew_abs_f32", "ew_abs_f16", "ew_abs_bf16", "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config", "ew_set_launch_row",
     "ew_get_launch_row", "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan",
-    "ew_make_gather_plan", "ew_batch", "ew_batch_build", "ew_batch_run", "EwBatch",
+    "ew_make_gather_plan", "ew_batch", "ew_batch_build", "ew_batch_run", "ew_batch_run_static",
+    "BATCH_SCRATCH_BYTES", "EwBatch",
     "EwBatchItem", "EwBatchPlan", "BATCH_MAX",
 ]
 
@@ -96,6 +97,7 @@ class EwBatchPlan(ctypes.Structure):
 
 
 BATCH_MAX = 96          # EW_BATCH_MAX: items per kernel launch of ew_batch
+BATCH_SCRATCH_BYTES = 256 * 1024   # EW_BATCH_SCRATCH_BYTES: largest table of ew_batch_run_static
 
 
 def _proto(name, restype, *argtypes):
@@ -138,6 +140,8 @@ _c = {
                              ctypes.POINTER(EwBatchPlan)),
     "ew_batch_run": _proto("ew_batch_run", _int, ctypes.POINTER(EwBatchPlan), ctypes.c_float,
                            _vp, _vp),
+    "ew_batch_run_static": _proto("ew_batch_run_static", _int, ctypes.POINTER(EwBatchPlan),
+                                  ctypes.c_float, _vp, _vp),
     "ew_set_launch_config": _proto("ew_set_launch_config", _int, ctypes.c_char_p, _int, _int,
                                    _int),
     "ew_get_launch_config": _proto("ew_get_launch_config", _int, ctypes.c_char_p, _sz,
@@ -490,6 +494,19 @@ def ew_batch_run(plan, alpha, table, stream=None):
         s = s.cuda_stream
     _check(_c["ew_batch_run"](ctypes.byref(plan), float(alpha), _addr(table), s),
            "ew_batch_run")
+
+
+def ew_batch_run_static(plan, alpha, image, stream=None):
+    """One launch of a built batch whose table the library copies from the
+    host image (as ew_batch_build returned it) into its static device array:
+    no device memory of the caller's.  Waits for the stream before and after
+    the copy; plan.bytes must not exceed BATCH_SCRATCH_BYTES."""
+    if stream is not None and not isinstance(stream, int):
+        stream = stream.cuda_stream
+    if stream is None and torch is not None:
+        stream = torch.cuda.current_stream().cuda_stream
+    _check(_c["ew_batch_run_static"](ctypes.byref(plan), float(alpha), ctypes.addressof(image),
+                                     stream), "ew_batch_run_static")
 
 
 class EwBatch:

@@ -20,7 +20,8 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
+static_assert(kBatchScratchBytes == EW_BATCH_SCRATCH_BYTES, "one scratch size for both sides");
 
 struct OpInfo {
     const char *name;
@@ -920,22 +921,27 @@ ew_status_t ew_batch_build(const char *op_name, const ew_batch_item_t *items, si
     return EW_OK;
 }
 
-ew_status_t ew_batch_run(const ew_batch_plan_t *plan, float alpha, const void *table,
-                         hipStream_t s)
+}  // extern "C"
+
+namespace ew {
+namespace {
+
+// A built plan's fields, checked for consistency (plan->tiles > 0).
+bool plan_consistent(const ew_batch_plan_t *plan)
 {
-    if (!plan) return EW_ERR_INVALID_ARG;
-    if (plan->tiles == 0) return EW_OK;
-    if (!table) return EW_ERR_INVALID_ARG;
-    if (reinterpret_cast<uintptr_t>(table) % 8 != 0) return EW_ERR_MISALIGNED;
     const int op = plan->op;
-    if (op < 0 || op >= kOpCount || !batchable(op) ||
-        !valid_row(plan->block, plan->blocks_per_cu, plan->unroll) || plan->unroll > 4 ||
-        plan->items == 0 || plan->items > UINT32_MAX || plan->tiles < plan->items ||
-        plan->bytes != table_image_bytes(plan->items, plan->tiles))
-        return EW_ERR_INVALID_ARG;
-    int cus = 0;
-    const ew_status_t st = current_device(&cus);
-    if (st != EW_OK) return st;
+    return op >= 0 && op < kOpCount && batchable(op) &&
+           valid_row(plan->block, plan->blocks_per_cu, plan->unroll) && plan->unroll <= 4 &&
+           plan->items > 0 && plan->items <= UINT32_MAX && plan->tiles >= plan->items &&
+           plan->bytes == table_image_bytes(plan->items, plan->tiles);
+}
+
+// One launch of the table kernel over a table image at device address
+// `table` (plan checked, device known).
+ew_status_t launch_table(const ew_batch_plan_t *plan, float alpha, const void *table, int cus,
+                         hipStream_t s, const char *path)
+{
+    const int op = plan->op;
     uint64_t grid = (uint64_t)plan->blocks_per_cu * (uint64_t)cus;
     if (grid > plan->tiles) grid = plan->tiles;
     const Launch l{plan->block, (int)grid, plan->unroll};
@@ -945,10 +951,56 @@ ew_status_t ew_batch_run(const ew_batch_plan_t *plan, float alpha, const void *t
                                                      plan->items * sizeof(BatchTableItem));
     a.tiles = plan->tiles;
     a.alpha = alpha;
-    log_launch(kOps[op].name, (size_t)plan->items, 0, plan->tiles, 0, l,
-               "batch table (n = items, vectors = tiles)");
+    log_launch(kOps[op].name, (size_t)plan->items, 0, plan->tiles, 0, l, path);
     const hipError_t e = launch_batch_table(static_cast<OpId>(op), a, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
+}
+
+}  // namespace
+}  // namespace ew
+
+extern "C" {
+
+ew_status_t ew_batch_run(const ew_batch_plan_t *plan, float alpha, const void *table,
+                         hipStream_t s)
+{
+    if (!plan) return EW_ERR_INVALID_ARG;
+    if (plan->tiles == 0) return EW_OK;
+    if (!table) return EW_ERR_INVALID_ARG;
+    if (reinterpret_cast<uintptr_t>(table) % 8 != 0) return EW_ERR_MISALIGNED;
+    if (!plan_consistent(plan)) return EW_ERR_INVALID_ARG;
+    int cus = 0;
+    const ew_status_t st = current_device(&cus);
+    if (st != EW_OK) return st;
+    return launch_table(plan, alpha, table, cus, s, "batch table (n = items, vectors = tiles)");
+}
+
+ew_status_t ew_batch_run_static(const ew_batch_plan_t *plan, float alpha, const void *table_host,
+                                hipStream_t s)
+{
+    if (!plan) return EW_ERR_INVALID_ARG;
+    if (plan->tiles == 0) return EW_OK;
+    if (!table_host) return EW_ERR_INVALID_ARG;
+    if (!plan_consistent(plan)) return EW_ERR_INVALID_ARG;
+    if (plan->bytes > kBatchScratchBytes) return EW_ERR_TOO_LARGE;
+    int cus = 0;
+    ew_status_t st = current_device(&cus);
+    if (st != EW_OK) return st;
+    void *table = nullptr;
+    hipError_t e = batch_scratch(&table);
+    if (e != hipSuccess) return fail_hip(e);
+    // The array still holds the table of the previous call on this device,
+    // which a kernel on this stream may still be reading: wait for the
+    // stream, copy, and wait for the copy, so that the caller may reuse its
+    // image once the call returns.
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail_hip(e);
+    e = hipMemcpyAsync(table, table_host, plan->bytes, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail_hip(e);
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail_hip(e);
+    return launch_table(plan, alpha, table, cus, s,
+                        "batch table in static scratch (n = items, vectors = tiles)");
 }
 
 ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)
@@ -1128,6 +1180,9 @@ const char *ew_status_string(ew_status_t status)
     case EW_ERR_OVERLAP: return "EW_ERR_OVERLAP: output partially overlaps an input";
     case EW_ERR_NO_DEVICE: return "EW_ERR_NO_DEVICE: no usable HIP device";
     case EW_ERR_HIP: return "EW_ERR_HIP: HIP runtime error (see ew_last_hip_error)";
+    case EW_ERR_TOO_LARGE:
+        return "EW_ERR_TOO_LARGE: the batch table exceeds the static scratch "
+               "(EW_BATCH_SCRATCH_BYTES)";
     }
     return "EW_ERR_UNKNOWN";
 }

@@ -3,6 +3,8 @@
 
 #include "ew_device.h"
 
+#include <mutex>
+
 namespace ew {
 
 // ---------------------------------------------------------------------------
@@ -240,6 +242,33 @@ struct TableLauncher {
 };
 
 }  // namespace
+
+// The batch table of ew_batch_run_static, for callers that cannot allocate:
+// one copy per GPU for the life of the process.  Host code never passes this
+// name to a kernel or a copy (on the host it names a stand-in, not device
+// memory); it uses the address batch_scratch() returns for the current device.
+static __device__ __align__(256) unsigned char scratch[kBatchScratchBytes];
+
+hipError_t batch_scratch(void **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_batch(OpId op, const BatchArgs &args, const Launch &l, hipStream_t s)
 {

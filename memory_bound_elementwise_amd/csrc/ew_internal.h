@@ -182,6 +182,14 @@ hipError_t launch_batch(OpId op, const BatchArgs &args, const Launch &launch,
 hipError_t launch_batch_table(OpId op, const BatchTableArgs &args, const Launch &launch,
                               hipStream_t stream);
 
+// Size of the library's static device array that holds a batch table for
+// the entry point that allocates nothing (ew_batch_run_static).
+constexpr uint64_t kBatchScratchBytes = 256 * 1024;
+
+// Device address of that array on the current device (looked up once per
+// device with hipGetSymbolAddress, then cached).
+hipError_t batch_scratch(void **ptr);
+
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
                          hipStream_t stream);
 

@@ -16,8 +16,8 @@ from tests.conftest import ROOT, _gpu_visible
 
 HEADER = os.path.join(ROOT, "include", "ew.h")
 
-EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP, EW_ERR_NO_DEVICE, EW_ERR_HIP = (
-    0, -1, -2, -3, -4, -5)
+(EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP, EW_ERR_NO_DEVICE, EW_ERR_HIP,
+ EW_ERR_TOO_LARGE) = (0, -1, -2, -3, -4, -5, -6)
 
 BASE = 0x7F0000000000          # a made-up, 256-byte aligned device address
 MiB = 1 << 20
@@ -52,9 +52,9 @@ def test_binding_names_match_the_c_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert ew.ew_abi_version() == 10
+    assert ew.ew_abi_version() == 11
     for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
-                 EW_ERR_NO_DEVICE, EW_ERR_HIP):
+                 EW_ERR_NO_DEVICE, EW_ERR_HIP, EW_ERR_TOO_LARGE):
         s = ew.ew_status_string(code)
         assert s.startswith("EW_")
     assert ew.ew_status_string(12345) == "EW_ERR_UNKNOWN"
@@ -494,3 +494,28 @@ def test_gather_walk_validation():
     assert walk(BASE, BASE, 1000, 1, None) == EW_ERR_OVERLAP             # no exact alias either
     if not _gpu_visible():
         assert walk(BASE, BASE + MiB, 1000, 2, None) == EW_ERR_NO_DEVICE
+
+
+def test_batch_run_static_checks_before_any_hip_call():
+    """The allocation-free run: a table larger than the static array is
+    refused with its own status, before any device is touched; the plan is
+    checked as for ew_batch_run."""
+    run = ew._c["ew_batch_run_static"]
+    img = (ctypes.c_uint64 * 4)()
+    st, empty = _build("add_f32", [(BASE, BASE + MiB, BASE + 2 * MiB, 0)])
+    assert st == EW_OK and run(ctypes.byref(empty), 0.0, None, None) == EW_OK
+    # about 6000 single-tile items: a table over 256 KiB
+    items = [(BASE + 3 * k * 4096, BASE + (3 * k + 1) * 4096, BASE + (3 * k + 2) * 4096, 1000)
+             for k in range(6000)]
+    st, big = _build("add_f32", items)
+    assert st == EW_OK and big.bytes > ew.BATCH_SCRATCH_BYTES
+    assert run(ctypes.byref(big), 0.0, ctypes.addressof(img), None) == EW_ERR_TOO_LARGE
+    st, small = _build("add_f32", items[:100])
+    assert st == EW_OK and small.bytes <= ew.BATCH_SCRATCH_BYTES
+    assert run(None, 0.0, ctypes.addressof(img), None) == EW_ERR_INVALID_ARG
+    assert run(ctypes.byref(small), 0.0, None, None) == EW_ERR_INVALID_ARG
+    bad = ew.EwBatchPlan.from_buffer_copy(small)
+    bad.bytes += 8
+    assert run(ctypes.byref(bad), 0.0, ctypes.addressof(img), None) == EW_ERR_INVALID_ARG
+    if not _gpu_visible():
+        assert run(ctypes.byref(small), 0.0, ctypes.addressof(img), None) == EW_ERR_NO_DEVICE

@@ -44,7 +44,9 @@ def asm(tmp_path_factory):
 
 def _kernels(text):
     """{mangled name: (body, metadata)} for every kernel in the assembly."""
-    bodies = dict(re.findall(r"\n(_ZN2ew\w+):[^\n]*\n(.*?)\n\.Lfunc_end", text, re.S))
+    # a function's label is followed by its first basic block; a data label
+    # (the batch scratch array) is not
+    bodies = dict(re.findall(r"\n(_ZN2ew\w+):[^\n]*\n(; %bb\.0:.*?)\n\.Lfunc_end", text, re.S))
     meta = dict(re.findall(r"\.amdhsa_kernel (\w+)(.*?)\.end_amdhsa_kernel", text, re.S))
     assert bodies and set(bodies) == set(meta), "could not split the assembly into kernels"
     return {k: (bodies[k], meta[k]) for k in bodies}
