@@ -913,6 +913,7 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
+    ap.add_argument("--others", help="comma-separated: run only these other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--details", help="also write every record in full to this file, one JSON "
@@ -959,9 +960,14 @@ def main(argv=None):
     details = open(args.details, "w") if args.details else None
 
     others = []
+    only = set(args.others.split(",")) if args.others else None
+    if only and not only <= set(synth.WORKLOADS):
+        print(f"bench.py: unknown workloads {sorted(only - set(synth.WORKLOADS))}",
+              file=sys.stderr)
+        return 2
     if not args.no_others:
         for name, ow in synth.WORKLOADS.items():
-            if name == w.name:
+            if name == w.name or (only and name not in only):
                 continue
             log(f"other config {name}")
             steps = 200 if ow.n >= (1 << 25) else 1000

@@ -166,9 +166,18 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
                 u32x4 w;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) w[q] = e[(S * q + r) / 4][(S * q + r) % 4];
-                u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(g.out + g.dest[r] + 4 * grp);
-                if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
-                else *p = w;
+                if constexpr (FirstOnly) {
+                    // one array read, one written (the view): a device-scope
+                    // store, the wave's 1 KiB as the buffer (4-byte aligned)
+                    store16_device(reinterpret_cast<char *>(g.out + g.dest[0] + 4 * grp0),
+                                   1024u, 16u * lane, w);
+                } else {
+                    // S runs written at once: plain non-temporal stores (the
+                    // device-scope form ran 19 % slower at stride 3)
+                    u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(g.out + g.dest[r] + 4 * grp);
+                    if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
+                    else *p = w;
+                }
             }
         } else if (grp < g.vectors) {
             // The wave at the end of the input: element by element.
@@ -193,13 +202,16 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
 // 16-byte-per-lane loads (1 KiB per instruction) and keeps elements 0 and 2
 // of each: lane l of a wave covering outputs [o, o + 256) produces outputs
 // o + 2l, o + 2l + 1 from the first load and o + 128 + 2l, o + 129 + 2l from
-// the second, stored as 8-byte pairs (512 contiguous bytes per instruction),
-// once per segment.  A tile is blockDim * U vectors of 4 outputs, so the
-// launch shape means the same as for the general gather.
+// the second, stored as 8-byte pairs (512 contiguous bytes per instruction,
+// at device scope), once per segment.  A tile is blockDim * U vectors of 4
+// outputs, so the launch shape means the same as for the general gather.
+// Measured on MI355X against this shape: lanes loading 32 contiguous bytes
+// each (two adjacent vectors) and storing 16 bytes ran 1-2 % slower (each
+// load instruction then touches twice the cache lines), staging the 2 KiB
+// span through LDS 4 % slower, and two spans per wave 3-5 % slower.
 template <int U, bool Co>
 __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = tid >> 6;
@@ -233,11 +245,11 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
                 const uint64_t i = o + 128 * h + 2 * lane;
                 if (i < body_end) {
                     const u32x2 pair = u32x2{x[u][h].x, x[u][h].z};
-                    for (uint64_t k = 0; k < g.reps; ++k) {
-                        u32x2 *q = reinterpret_cast<u32x2 *>(out + k * seg_bytes + 4 * i);
-                        if constexpr (EW_STORE_NT) __builtin_nontemporal_store(pair, q);
-                        else *q = pair;
-                    }
+                    // one input read, one array written: device-scope stores,
+                    // the wave's 512-byte half-row as the buffer
+                    for (uint64_t k = 0; k < g.reps; ++k)
+                        store8_device(out + k * seg_bytes + 4 * (o + 128 * h), 512u, 8u * lane,
+                                      pair);
                 }
             }
         }
