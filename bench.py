@@ -895,6 +895,8 @@ def final_line(args, w, res, others, env):
                                               "cores": allc["cores"]}
     if "torch_context" in res:
         line["torch_context_gbs"] = res["torch_context"]["gbs"]
+    if "graph" in res:        # small workloads: launches replayed from a captured graph
+        line["graph_gbs"] = res["graph"]["gbs"]
     if others:
         line["others"] = {"workloads": len(others),
                           "parity_pass": sum(r.get("parity") == "PASS" for r in others),

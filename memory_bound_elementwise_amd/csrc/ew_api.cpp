@@ -783,12 +783,35 @@ ew_status_t batch_validate(int op, const ew_batch_item_t *items, size_t count, s
     return st;
 }
 
-// The launch row of a batched call: the table's row for the total element
-// count, unroll at most 4.
-Row batch_row(int op, size_t total)
+// The launch shape of a batched call: the table's row for the total element
+// count (unroll at most 4), with the tile shrunk -- unroll first, then the
+// block, down to 64 threads -- while half of it still covers the items' mean
+// vector count (a tile longer than an item leaves its lanes idle).  A shrunk
+// tile takes one block per tile (blocks_per_cu raised so that the grid
+// covers the tiles).
+Row batch_row(int op, const ew_batch_item_t *items, size_t count, size_t total)
 {
     Row r = get_row(op, total);
     if (r.unroll > 4) r.unroll = 4;
+    const uint64_t vec = 16 / (uint64_t)kOps[op].elem_size;
+    uint64_t live = 0, vectors = 0;
+    for (size_t i = 0; i < count; ++i) {
+        if (items[i].n == 0) continue;
+        ++live;
+        vectors += items[i].n / vec;
+    }
+    if (live == 0) return r;
+    const uint64_t mean = (vectors + live - 1) / live;
+    bool shrunk = false;
+    while (r.unroll > 1 && (uint64_t)r.block * (uint64_t)r.unroll / 2 >= mean) {
+        r.unroll /= 2;
+        shrunk = true;
+    }
+    while (r.block > 64 && (uint64_t)r.block / 2 >= mean) {
+        r.block /= 2;
+        shrunk = true;
+    }
+    if (shrunk) r.blocks_per_cu = 1024;
     return r;
 }
 
@@ -837,7 +860,7 @@ ew_status_t ew_batch(const char *op_name, float alpha, const ew_batch_item_t *it
     st = current_device(&cus);
     if (st != EW_OK) return st;
     // One launch shape for the whole call.
-    const Row r = batch_row(op, total);
+    const Row r = batch_row(op, items, count, total);
     const uint64_t tile_vecs = (uint64_t)r.block * (uint64_t)r.unroll;
     BatchArgs a{};
     a.alpha = alpha;
@@ -878,7 +901,7 @@ ew_status_t ew_batch_build(const char *op_name, const ew_batch_item_t *items, si
     size_t total = 0;
     ew_status_t st = batch_validate(op, items, count, &total);
     if (st != EW_OK) return st;
-    const Row r = batch_row(op, total);
+    const Row r = batch_row(op, items, count, total);
     const uint64_t tile_vecs = (uint64_t)r.block * (uint64_t)r.unroll;
     uint64_t live = 0, tiles = 0;
     for (size_t i = 0; i < count; ++i) {

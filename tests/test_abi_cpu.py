@@ -407,6 +407,43 @@ def test_batch_build_validates_like_the_host_array_call():
     assert ew._c["ew_batch_build"](b"add_f32", None, 0, None, 0, None) == EW_ERR_INVALID_ARG
 
 
+def _batch_shape(op, items, es):
+    """The documented launch shape of a batched call: the row for the total
+    n (unroll at most 4), the tile halved -- unroll first, then the block,
+    down to 64 threads -- while half of it still covers the mean item's
+    vectors, and one block per tile (blocks_per_cu 1024) once shrunk."""
+    total = sum(it[3] for it in items)
+    block, bpc, unroll = ew.ew_get_launch_row(op, total)
+    unroll = min(unroll, 4)
+    live = [it[3] for it in items if it[3] > 0]
+    mean = -(-sum(n // (16 // es) for n in live) // len(live))
+    shrunk = False
+    while unroll > 1 and block * unroll // 2 >= mean:
+        unroll //= 2
+        shrunk = True
+    while block > 64 and block // 2 >= mean:
+        block //= 2
+        shrunk = True
+    return block, 1024 if shrunk else bpc, unroll
+
+
+def test_batch_tiles_shrink_to_small_items():
+    """1024 items of 1024 fp32 elements (256 vectors each): the row for 2^20
+    elements has 1024-vector tiles, so the tile shrinks to 256 vectors, one
+    item per tile and one block per tile; large items keep the row's shape."""
+    small = [(BASE + 3 * k * 8192, BASE + (3 * k + 1) * 8192, BASE + (3 * k + 2) * 8192, 1024)
+             for k in range(1024)]
+    st, plan = _build("add_f32", small)
+    assert st == EW_OK
+    assert plan.block * plan.unroll == 256 and plan.tiles == 1024 and plan.blocks_per_cu == 1024
+    big = [(BASE + 3 * k * (1 << 22), BASE + (3 * k + 1) * (1 << 22),
+            BASE + (3 * k + 2) * (1 << 22), 1 << 20) for k in range(4)]
+    st, plan = _build("add_f32", big)
+    assert st == EW_OK
+    block, bpc, unroll = ew.ew_get_launch_row("add_f32", 1 << 22)
+    assert (plan.block, plan.blocks_per_cu, plan.unroll) == (block, bpc, min(4, unroll))
+
+
 def _expected_tiles(out, n, es, block, unroll):
     head = min(((16 - out % 16) % 16) // es, n)
     vectors = (n - head) // (16 // es)
@@ -437,8 +474,7 @@ def test_batch_build_writes_the_documented_image(op, es):
     st, plan = _build(op, items)
     assert st == EW_OK
     total = sum(it[3] for it in items)
-    block, bpc, unroll = ew.ew_get_launch_row(op, total)
-    unroll = min(unroll, 4)
+    block, bpc, unroll = _batch_shape(op, items, es)
     assert (plan.block, plan.unroll, plan.blocks_per_cu) == (block, unroll, bpc)
     live = [it for it in items if it[3] > 0]
     tiles = [_expected_tiles(it[0], it[3], es, block, unroll) for it in live]
