@@ -173,8 +173,9 @@ def cmd_traffic(a):
     with open(a.out, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
-    _merge(TRAFFIC_JSON, "HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by "
-                         "the copy-kernel calibration; see the .txt summaries", a.workload, {
+    _merge(a.index or TRAFFIC_JSON, "HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                    "scaled by the copy-kernel calibration; see the .txt "
+                                    "summaries", a.workload, {
         "kernel": rec.get("kernel") or a.kernel, "launch": launch,
         "kernel_source_sha256_16": src_hash,
         "fetch_kib": fetch_kib, "write_kib": write_kib, "scale_fetch": scale_f,
@@ -227,11 +228,47 @@ def cmd_configs(a):
         text.append(f"| {name} | {r['kernel']} | {lc['grid']} x {lc['block']} | {len(d)} | "
                     f"{avg / 1000:.2f} | {med / 1000:.2f} ({p10 / 1000:.2f}, {p90 / 1000:.2f}) | "
                     f"{alg / avg:.1f} | {r['gbs']} | {r['source_sha256_16']} |")
-        _merge(KERNEL_TRACE_JSON, "rocprofv3 kernel-trace durations per workload, from the "
-                                  "summary named in each record", name, {
+        _merge(a.index or KERNEL_TRACE_JSON, "rocprofv3 kernel-trace durations per workload, "
+                                             "from the summary named in each record", name, {
             "kernel": r["kernel"], "launch": lc, "kernel_source_sha256_16": r["source_sha256_16"],
             "dispatches": len(d), "avg_ns": round(avg, 1), "median_ns": med, "p10_ns": p10,
             "p90_ns": p90, "algorithmic_bytes": alg, "summary": os.path.basename(a.out)})
+    with open(a.out, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
+def cmd_counters(a):
+    """Per-dispatch medians of the counters of one rocprofv3 --pmc pass for
+    the workload's kernel (e.g. the LDS counters of the kernels that stage
+    data in LDS), with bank-conflict cycles as a share of LDS-active cycles
+    when both were collected."""
+    rec = bench_record(a.bench_json, a.workload)
+    rows = [r for r in _rows(a.csv) if re.search(a.kernel, r.get("Kernel_Name", ""))]
+    if not rows:
+        raise SystemExit(f"no dispatch of {a.kernel!r} in {a.csv}")
+    per = {}
+    for r in rows:
+        key = (r["Counter_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    names = sorted({k[0] for k in per})
+    med = {c: statistics.median(v for (n, _), v in per.items() if n == c) for c in names}
+    dispatches = len({k[1] for k in per})
+    text = [
+        f"# {a.title}",
+        "",
+        f"command: {a.command}",
+        f"source:  {os.path.basename(a.csv)}, kernel {rows[0]['Kernel_Name'].split('(')[0]}, "
+        f"{dispatches} dispatches (median per dispatch; SQ counters summed over the SEs)",
+        f"launch:  {json.dumps(rec.get('launch'))}",
+        "",
+    ]
+    text += [f"{c:22s} {med[c]:.6g}" for c in names]
+    if "SQ_LDS_BANK_CONFLICT" in med and med.get("SQ_LDS_IDX_ACTIVE"):
+        text.append(f"bank-conflict cycles / LDS-active cycles: "
+                    f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.3f}")
+    text.append(f"kernel sources: {a.family} family sha256[:16] "
+                f"{profiled_hash(a.bench_json, a.workload)} (of the profiled run)")
     with open(a.out, "w") as f:
         f.write("\n".join(text) + "\n")
     print("\n".join(text))
@@ -261,6 +298,7 @@ def main(argv=None):
     r.add_argument("--bench-json-write", required=True,
                    help="bench.py output of the WRITE_SIZE run")
     r.add_argument("--out", required=True)
+    r.add_argument("--index", help="profile index to merge into (default profiles/traffic.json)")
     c = sub.add_parser("configs")
     c.add_argument("--trace", required=True, help="kernel_trace.csv of a default bench run")
     c.add_argument("--bench-json", required=True, help="that run's bench.py output")
@@ -268,8 +306,19 @@ def main(argv=None):
     c.add_argument("--workloads", help="comma-separated workloads (default: every record "
                                        "naming its kernel)")
     c.add_argument("--out", required=True)
+    c.add_argument("--index", help="profile index to merge into (default "
+                                   "profiles/kernel_trace.json)")
+    k = sub.add_parser("counters")
+    k.add_argument("--csv", required=True, help="counter_collection.csv of one --pmc pass")
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--workload", required=True)
+    k.add_argument("--family", required=True)
+    k.add_argument("--bench-json", required=True)
+    k.add_argument("--command", required=True)
+    k.add_argument("--title", default="Hardware counters")
+    k.add_argument("--out", required=True)
     a = ap.parse_args(argv)
-    {"traffic": cmd_traffic, "configs": cmd_configs}[a.cmd](a)
+    {"traffic": cmd_traffic, "configs": cmd_configs, "counters": cmd_counters}[a.cmd](a)
     return 0
 
 

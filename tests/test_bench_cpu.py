@@ -252,3 +252,62 @@ def test_clocks_come_from_sysfs_without_a_child_process(tmp_path, monkeypatch):
     class Other:
         pci_domain_id, pci_bus_id, pci_device_id = 0, 0x11, 0
     assert bench._clocks(Other) is None
+
+
+def test_rocprof_summaries_read_the_bench_output_and_the_profiler_csv(tmp_path):
+    """The kernel-trace summary matches each record's kernel instance, grid
+    and block in the trace and writes an index bench.py can read back; the
+    counter summary takes per-dispatch medians."""
+    import argparse
+    import csv
+    import synth
+    from memory_bound_elementwise_amd import rocprof_summary as rs
+    w = synth.WORKLOADS[bench.DEFAULT_WORKLOAD]
+    res = _fake_record(w.name, "add_f32", w.n, 6500.0)
+    res["kernel"] = "ew_stream_kernel<ew::OpAddF32, 1, true, true>"
+    other = _fake_record("copy_f32_2e28", "copy_f32", 1 << 28, 6600.0,
+                         kernel="ew_stream_kernel<ew::OpCopyF32, 1, true, true>",
+                         launch={"block": 256, "grid": 262144, "unroll": 1})
+    env = {"kernel_source_sha256_16": "0" * 16}
+    line = bench.final_line(argparse.Namespace(steps=20, warmup=5), w, res, [other], env)
+    out = tmp_path / "bench.out"
+    out.write_text(json.dumps(other) + "\n" + json.dumps(line) + "\n")
+    trace = tmp_path / "run_kernel_trace.csv"
+    with open(trace, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Kernel_Name", "Workgroup_Size_X", "Grid_Size_X", "Start_Timestamp",
+                     "End_Timestamp"])
+        for k, d in enumerate((490000, 500000, 495000)):
+            wr.writerow(["void ew::ew_stream_kernel<ew::OpAddF32, 1, true, true>(ew::StreamArgs)",
+                         1024, 1024 * 65536, 1000 * k, 1000 * k + d])
+        wr.writerow(["void ew::ew_stream_kernel<ew::OpAddF32, 1, false, true>(ew::StreamArgs)",
+                     1024, 1024 * 65536, 0, 1])          # another instance: not matched
+        for k in range(4):
+            wr.writerow(["void ew::ew_stream_kernel<ew::OpCopyF32, 1, true, true>(ew::StreamArgs)",
+                         256, 256 * 262144, 0, 320000 + k])
+    index = tmp_path / "kernel_trace.json"
+    rs.main(["configs", "--trace", str(trace), "--bench-json", str(out), "--command", "cmd",
+             "--out", str(tmp_path / "kt.txt"), "--index", str(index)])
+    idx = json.loads(index.read_text())["workloads"]
+    assert idx[w.name]["dispatches"] == 3 and idx[w.name]["median_ns"] == 495000
+    assert idx[w.name]["launch"] == res["launch"]
+    assert idx["copy_f32_2e28"]["dispatches"] == 4
+    rec = bench._committed(str(index), w.name, "0" * 16, res["launch"])
+    assert rec and rec["avg_ns"] == 495000.0
+    # counters: two dispatches, a counter summed over its rows per dispatch
+    cc = tmp_path / "run_counter_collection.csv"
+    with open(cc, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for d, (bank, active) in enumerate(((30, 100), (50, 100))):
+            wr.writerow([d, "void ew::ew_transpose_kernel(ew::Copy2dArgs)",
+                         "SQ_LDS_BANK_CONFLICT", bank / 2])
+            wr.writerow([d, "void ew::ew_transpose_kernel(ew::Copy2dArgs)",
+                         "SQ_LDS_BANK_CONFLICT", bank / 2])
+            wr.writerow([d, "void ew::ew_transpose_kernel(ew::Copy2dArgs)",
+                         "SQ_LDS_IDX_ACTIVE", active])
+    rs.main(["counters", "--csv", str(cc), "--kernel", "ew_transpose_kernel", "--workload",
+             w.name, "--family", "view", "--bench-json", str(out), "--command", "cmd",
+             "--out", str(tmp_path / "c.txt")])
+    text = (tmp_path / "c.txt").read_text()
+    assert "SQ_LDS_BANK_CONFLICT   40" in text and "LDS-active cycles: 0.400" in text
