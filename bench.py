@@ -149,10 +149,25 @@ def _b(v) -> str:
     return "true" if v else "false"
 
 
-def kernel_instance(w, launch: dict, split: dict):
+# What each kernel path of ew_plan_t.path does, for the record.
+PATH_TEXT = {
+    "stream": "streaming kernel",
+    "copy": "copy kernel (stride 1 mod n)",
+    "gather_walk": "per-output index walk (one 4-byte load per output element), "
+                   "{reps} segment(s)",
+    "gather_spans": "contiguous 16-byte loads, even elements kept",
+    "gather_passes": "{s} passes, input spans staged through LDS",
+    "view_rows": "rows contiguous",
+    "view_transpose": "LDS-tiled transpose (128 x 128 tiles, 1024 threads)",
+    "view_generic": "generic (one 4-byte load per element)",
+}
+
+
+def kernel_instance(w, launch: dict, split: dict, plan=None, ew=None, prep=None):
     """The kernel instance one launch of the workload runs (the name
     rocprofv3 reports, without 'void ew::' and the argument list), or None
-    where the record does not determine it."""
+    where the record does not determine it.  plan: the workload's ew_plan_t
+    (its path decides the gather's and the views' kernels)."""
     u = launch.get("unroll")
     if w.batch:
         return f"ew_batch_table_kernel<ew::{OP_CLASS[w.op]}, {u}>"
@@ -161,18 +176,27 @@ def kernel_instance(w, launch: dict, split: dict):
         return f"ew_stream_kernel<ew::{OP_CLASS[w.op]}, {u}, {_b(co[0])}, {_b(co[1])}>"
     if w.op == "relu_inplace_f32":
         return f"ew_relu_inplace_kernel<{u}>"
-    if w.op == "gather_walk_f32":
+    if w.op == "bias_relu_f32":
+        co = split.get("in_coaligned", [1, 1])[0]
+        vec_bias = w.cols % 4 == 0 and split.get("head", 0) == 0
+        return f"ew_bias_relu_kernel<{u}, {_b(co)}, {_b(vec_bias)}>"
+    if plan is None or ew is None:
+        return None
+    path = ew.PATHS[plan.path]
+    if path == "copy":
+        return f"ew_stream_kernel<ew::OpCopyF32, {u}, {_b(split['in_coaligned'][0])}, true>"
+    if path == "gather_walk":
         return f"ew_gather_kernel<{u}>"
-    path = launch.get("path", "")
-    if w.op == "gather_f32":
-        if path.startswith("contiguous 16-byte loads"):
-            return f"ew_gather2_kernel<{u}, true>"
-        if "passes" in path:
-            return f"ew_gather_passes_kernel<{w.stride % w.n}, false>"
-        if path.startswith("per-output"):
-            return f"ew_gather_kernel<{u}>"
-    if w.op == "copy2d_f32" and path.startswith("LDS-tiled transpose"):
+    if path == "gather_passes":
+        return f"ew_gather_passes_kernel<{plan.passes}, {_b(w.op == 'copy2d_f32')}>"
+    if path == "gather_spans":
+        # the input's body start co-aligned: in + 8 * head (two inputs per output)
+        src = prep.view_src if w.op == "copy2d_f32" else prep.ptrs[1].data_ptr()
+        return f"ew_gather2_kernel<{u}, {_b((src + 8 * plan.head) % 16 == 0)}>"
+    if path == "view_transpose":
         return "ew_transpose_kernel"
+    if path in ("view_rows", "view_generic"):
+        return f"ew_copy2d_kernel<{u}, {_b(path == 'view_rows')}>"
     return None
 
 
@@ -217,6 +241,7 @@ class Prepared:
             rows = w.n // w.cols
             src = base.data_ptr() + 4 * offset
             self.launch = lambda: ew.ew_copy2d_f32(src, sr, sc, out, rows, w.cols, stream=s)
+            self.view_src = src
             self.out, self.ptrs = out, (out, base, None)
         elif w.op == "bias_relu_f32":
             x, kx = upload(self.inp["x"], offs.get("x", 0))
@@ -353,6 +378,10 @@ class Prepared:
         if self.w.op == "gather_f32":
             return ew.ew_make_gather_plan(out.data_ptr(), in0.data_ptr(), self.w.n,
                                           self.w.stride, cus)
+        if self.w.op == "copy2d_f32":
+            sr, sc = self.w.view[0], self.w.view[1]
+            return ew.ew_make_copy2d_plan(self.view_src, sr, sc, out.data_ptr(),
+                                          self.w.n // self.w.cols, self.w.cols, cus)
         return ew.ew_make_plan(self.w.op, out.data_ptr(), in0.data_ptr(),
                                in1.data_ptr() if in1 is not None else 0, self.w.n, cus)
 
@@ -630,28 +659,13 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
                        "table_bytes": bp.bytes, "launches": 1,
                        "path": "batched: device item table, one kernel for every item"}
         steps = min(steps, 200)
-    if w.op == "gather_walk_f32":
-        launch_desc["path"] = "per-output index walk (one 4-byte load per output element)"
-    if w.op == "gather_f32":
-        launch_desc["path"] = ("copy kernel" if w.stride % w.n == 1 else
-                               f"{plan.passes} passes, input staged through LDS"
-                               if plan.passes > 1 else
-                               "contiguous 16-byte loads, even elements kept" if
-                               (plan.reps == 2 and w.stride % w.n == 2) else
-                               f"per-output index walk, {plan.reps} segment(s)")
-    if w.op == "copy2d_f32":
-        sr, sc = w.view[0], w.view[1]
-        launch_desc["path"] = ("contiguous 16-byte loads, even elements kept (stride-2 gather "
-                               "kernel)" if (w.n == w.cols and sc == 2) else
-                               f"span read contiguously through LDS, one element in {sc} kept"
-                               if (w.n == w.cols and 3 <= sc <= 8) else
-                               "rows contiguous" if sc == 1 else
-                               "LDS-tiled transpose (128 x 128 tiles, 1024 threads)" if sr == 1 else
-                               "generic (one 4-byte load per element)")
+    if not w.batch and w.op in ("gather_f32", "gather_walk_f32", "copy2d_f32"):
+        launch_desc["path"] = PATH_TEXT[ew.PATHS[plan.path]].format(s=plan.passes,
+                                                                   reps=plan.reps)
     res = {"workload": w.name, "op": w.op, "n": w.n, "launch": launch_desc,
            "split": {"head": plan.head, "vectors": plan.vectors, "tail": plan.tail,
                      "in_coaligned": list(plan.in_coaligned)}}
-    res["kernel"] = kernel_instance(w, launch_desc, res["split"])
+    res["kernel"] = kernel_instance(w, launch_desc, res["split"], plan, ew, prep)
     res["source_sha256_16"] = kernel_source_hash(w.op, bool(w.batch))
     if w.batch:
         res["split"] = {"items": w.batch, "elements_per_item": w.n // w.batch,

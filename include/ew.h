@@ -466,8 +466,22 @@ ew_status_t ew_load_launch_table(const char *path);
  *   grid       min(blocks_per_cu * cu_count, tiles), at least 1 when n > 0
  *   segment, reps, passes   n, 1 and 1, except for the gather
  *              (ew_make_gather_plan)
+ *   path       the kernel path (ew_path_t): EW_PATH_STREAM, or
+ *              EW_PATH_GATHER_WALK for "gather_walk_f32"
  * Validation is the same as the operation's (in1 is ignored for one-input
  * ops; for saxpy in0 = x and out = y). */
+/* Which kernel path a plan launches. */
+typedef enum ew_path {
+    EW_PATH_STREAM = 0,          /* the streaming kernel: head / 16-byte body / tail */
+    EW_PATH_COPY = 1,            /* a gather with stride 1 mod n: the contiguous copy */
+    EW_PATH_GATHER_WALK = 2,     /* per-output index walk (reps equal segments) */
+    EW_PATH_GATHER_SPANS = 3,    /* stride 2: contiguous 16-byte loads, even elements kept */
+    EW_PATH_GATHER_PASSES = 4,   /* stride 2..8 coprime with n: spans staged through LDS */
+    EW_PATH_VIEW_ROWS = 5,       /* strided view, rows contiguous */
+    EW_PATH_VIEW_TRANSPOSE = 6,  /* strided view, 128 x 128 tiles through LDS */
+    EW_PATH_VIEW_GENERIC = 7     /* strided view, one 4-byte load per element */
+} ew_path_t;
+
 typedef struct ew_plan {
     size_t n;
     size_t head;
@@ -484,6 +498,7 @@ typedef struct ew_plan {
     size_t segment;
     int reps;
     int passes;
+    int path;               /* an ew_path_t */
 } ew_plan_t;
 
 ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
@@ -508,10 +523,23 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * groups of four slots, head = tail = 0, block = 256 and unroll = 1 whatever
  * the table says (its blocks_per_cu still caps the grid; the kernel's own LDS
  * reservation limits how many of its blocks share a compute unit).
- * Otherwise passes = 1.
+ * Otherwise passes = 1.  path: EW_PATH_COPY (stride 1 mod n, or n == 1:
+ * the copy's plan), EW_PATH_GATHER_PASSES, EW_PATH_GATHER_SPANS (stride 2,
+ * reps 2) or EW_PATH_GATHER_WALK.
  * Same validation as ew_gather_f32. */
 ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
                                 size_t stride, int cu_count, ew_plan_t *plan);
+
+/* The plan of ew_copy2d_f32 with these arguments: its path (x[::2] ->
+ * EW_PATH_GATHER_SPANS, x[::s] with s = 3..8 -> EW_PATH_GATHER_PASSES with
+ * passes = s, stride_c == 1 -> EW_PATH_VIEW_ROWS, stride_r == 1 ->
+ * EW_PATH_VIEW_TRANSPOSE, else EW_PATH_VIEW_GENERIC) and the launch it makes
+ * (block, grid, unroll as launched; a kernel with a fixed block shape reports
+ * that shape; tiles counts 128 x 128 tiles for the transpose).  No device is
+ * needed.  Same validation as ew_copy2d_f32. */
+ew_status_t ew_make_copy2d_plan(const void *in, int64_t stride_r, int64_t stride_c,
+                                const void *out, size_t rows, size_t cols, int cu_count,
+                                ew_plan_t *plan);
 
 #ifdef __cplusplus
 }

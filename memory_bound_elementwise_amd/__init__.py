@@ -30,9 +30,9 @@ __all__ = [
     "ew_abs_f32", "ew_abs_f16", "ew_abs_bf16", "ew_status_string", "ew_last_hip_error",
     "ew_abi_version", "ew_set_launch_config", "ew_get_launch_config", "ew_set_launch_row",
     "ew_get_launch_row", "ew_reset_launch_config", "ew_load_launch_table", "ew_make_plan",
-    "ew_make_gather_plan", "ew_batch", "ew_batch_build", "ew_batch_run", "ew_batch_run_static",
-    "BATCH_SCRATCH_BYTES", "EwBatch",
-    "EwBatchItem", "EwBatchPlan", "BATCH_MAX",
+    "ew_make_gather_plan", "ew_make_copy2d_plan", "PATHS", "ew_batch", "ew_batch_build",
+    "ew_batch_run", "ew_batch_run_static", "BATCH_SCRATCH_BYTES", "EwBatch", "EwBatchItem",
+    "EwBatchPlan", "BATCH_MAX",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -74,7 +74,7 @@ class EwPlan(ctypes.Structure):
         ("n", _sz), ("head", _sz), ("vectors", _sz), ("tail", _sz), ("tiles", _sz),
         ("vec_elems", _int), ("elem_size", _int), ("in_coaligned", _int * 2),
         ("block", _int), ("blocks_per_cu", _int), ("unroll", _int), ("grid", _int),
-        ("segment", _sz), ("reps", _int), ("passes", _int),
+        ("segment", _sz), ("reps", _int), ("passes", _int), ("path", _int),
     ]
 
     def as_dict(self):
@@ -158,6 +158,8 @@ _c = {
                            ctypes.POINTER(EwPlan)),
     "ew_make_gather_plan": _proto("ew_make_gather_plan", _int, _vp, _vp, _sz, _sz, _int,
                                   ctypes.POINTER(EwPlan)),
+    "ew_make_copy2d_plan": _proto("ew_make_copy2d_plan", _int, _vp, ctypes.c_int64,
+                                  ctypes.c_int64, _vp, _sz, _sz, _int, ctypes.POINTER(EwPlan)),
 }
 
 
@@ -621,6 +623,20 @@ def ew_make_gather_plan(out, src, n, stride, cu_count) -> EwPlan:
     _check(_c["ew_make_gather_plan"](out, src, int(n), int(stride), int(cu_count),
                                      ctypes.byref(plan)), "ew_make_gather_plan")
     return plan
+
+
+def ew_make_copy2d_plan(src, stride_r, stride_c, out, rows, cols, cu_count) -> EwPlan:
+    """The plan (path and launch) of ew_copy2d_f32 for integer addresses."""
+    plan = EwPlan()
+    _check(_c["ew_make_copy2d_plan"](src, int(stride_r), int(stride_c), out, int(rows),
+                                     int(cols), int(cu_count), ctypes.byref(plan)),
+           "ew_make_copy2d_plan")
+    return plan
+
+
+# ew_path_t: the kernel path of a plan
+PATHS = ("stream", "copy", "gather_walk", "gather_spans", "gather_passes", "view_rows",
+         "view_transpose", "view_generic")
 
 
 def library_path() -> str:

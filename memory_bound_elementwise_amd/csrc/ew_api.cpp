@@ -20,7 +20,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 11;
+constexpr int kAbiVersion = 12;
 static_assert(kBatchScratchBytes == EW_BATCH_SCRATCH_BYTES, "one scratch size for both sides");
 
 struct OpInfo {
@@ -1047,10 +1047,16 @@ ew_status_t ew_relu_inplace_f32(float *x, size_t n, hipStream_t s)
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
-ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, float *out,
-                          size_t rows, size_t cols, hipStream_t s)
+}  // extern "C"
+
+namespace ew {
+namespace {
+
+// Argument checks of a strided view copy (rows, cols > 0), before any HIP
+// call.
+ew_status_t copy2d_check(const float *in, int64_t stride_r, int64_t stride_c, const float *out,
+                         size_t rows, size_t cols)
 {
-    if (rows == 0 || cols == 0) return EW_OK;
     if (!in || !out || rows > SIZE_MAX / cols) return EW_ERR_INVALID_ARG;
     const size_t n = rows * cols;
     if (n >= (size_t(1) << 62) || n > SIZE_MAX / 4) return EW_ERR_INVALID_ARG;
@@ -1065,11 +1071,31 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
     if (op > UINTPTR_MAX - n * 4) return EW_ERR_INVALID_ARG;
     if (reinterpret_cast<uintptr_t>(in) % 4 != 0 || op % 4 != 0) return EW_ERR_MISALIGNED;
     if (in_lo < (__int128)op + (__int128)(n * 4) && (__int128)op < in_hi) return EW_ERR_OVERLAP;
-    int cus = 0;
-    ew_status_t st = current_device(&cus);
-    if (st != EW_OK) return st;
+    return EW_OK;
+}
+
+// The launch of a strided view copy: its path, kernel arguments and shape.
+struct Copy2dPlan {
+    int path;            // an ew_path_t
+    Launch launch;       // as launched (a kernel with a fixed block reports that block)
+    int blocks_per_cu;
+    Copy2dArgs a;        // EW_PATH_VIEW_*
+    GatherArgs g;        // EW_PATH_GATHER_SPANS / EW_PATH_GATHER_PASSES
+};
+
+// Path: a 1-D view with stride 2 (x[::2]) reads contiguous 16-byte spans and
+// keeps the even elements (the stride-2 gather kernel, one segment, no wrap);
+// a 1-D view with stride 3..8 keeps one element in s of contiguously read
+// spans (the pass kernel's residue-0 run); rows contiguous; a transposed view
+// (tiles through LDS); generic.  Arguments already checked.
+Copy2dPlan copy2d_plan(const float *in, int64_t stride_r, int64_t stride_c, float *out,
+                       size_t rows, size_t cols, int cus)
+{
+    const size_t n = rows * cols;
     const Plan p = make_plan(kOpCopy2dF32, out, out, nullptr, n, cus);
-    Copy2dArgs a{};
+    Copy2dPlan c{};
+    c.blocks_per_cu = p.blocks_per_cu;
+    Copy2dArgs &a = c.a;
     a.in = reinterpret_cast<const uint32_t *>(in);
     a.out = reinterpret_cast<uint32_t *>(out);
     a.sr = stride_r;
@@ -1087,13 +1113,8 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
     a.step_vec_c = sv % cols;
     a.step_tile_r = (uint64_t)(st_t / cols);
     a.step_tile_c = (uint64_t)(st_t % cols);
-    // Path: a 1-D view with stride 2 (x[::2]) reads contiguous 16-byte spans
-    // and keeps the even elements (the stride-2 gather kernel, one segment,
-    // no wrap); a 1-D view with stride 3..8 keeps one element in s of
-    // contiguously read spans; rows contiguous; a transposed view (tiles
-    // through LDS); generic.
     if (rows == 1 && stride_c == 2) {
-        GatherArgs g{};
+        GatherArgs &g = c.g;
         g.in = a.in;
         g.out = a.out;
         g.n = 2 * n;
@@ -1110,18 +1131,18 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         g.tail = n - g.head - 4 * g.vectors;
         const uint64_t tile_vecs = (uint64_t)pg.launch.block * (uint64_t)pg.launch.unroll;
         g.tiles = (g.vectors + tile_vecs - 1) / tile_vecs;
-        Launch lg = pg.launch;
+        c.launch = pg.launch;
+        c.blocks_per_cu = pg.blocks_per_cu;
         const uint64_t cap = (uint64_t)pg.blocks_per_cu * (uint64_t)cus;
-        lg.grid = (int)(g.tiles == 0 ? 1 : (g.tiles < cap ? g.tiles : cap));
-        log_launch("copy2d_f32", n, g.head, g.vectors, g.tail, lg, "view x[::2]");
-        const hipError_t e = launch_gather(g, lg, s);
-        return e == hipSuccess ? EW_OK : fail_hip(e);
+        c.launch.grid = (int)(g.tiles == 0 ? 1 : (g.tiles < cap ? g.tiles : cap));
+        c.path = EW_PATH_GATHER_SPANS;
+        return c;
     }
     if (rows == 1 && stride_c >= 3 && stride_c <= 8) {
-        // x[::s]: the residue-0 pass of the pass-decomposed gather; each wave
-        // reads its 1 KiB * s input span contiguously and keeps every s-th
-        // element.  n (the kernel's input length) is the view's extent.
-        GatherArgs g{};
+        // x[::s]: each wave reads its 1 KiB * s input span contiguously and
+        // keeps every s-th element.  n (the kernel's input length) is the
+        // view's extent.
+        GatherArgs &g = c.g;
         g.in = a.in;
         g.out = a.out;
         g.stride = (uint64_t)stride_c;
@@ -1135,28 +1156,97 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         const uint64_t tile = (uint64_t)gather_passes_threads();
         g.tiles = (g.vectors + tile - 1) / tile;
         const uint64_t cap = (uint64_t)p.blocks_per_cu * (uint64_t)cus;
-        Launch lg{gather_passes_threads(), (int)(g.tiles < cap ? g.tiles : cap), 1};
-        if (lg.grid == 0) lg.grid = 1;
-        log_launch("copy2d_f32", n, 0, g.vectors, 0, lg, "view x[::s], s = 3..8");
-        const hipError_t e = launch_gather(g, lg, s);
-        return e == hipSuccess ? EW_OK : fail_hip(e);
+        c.launch = Launch{gather_passes_threads(), (int)(g.tiles < cap ? g.tiles : cap), 1};
+        if (c.launch.grid == 0) c.launch.grid = 1;
+        c.path = EW_PATH_GATHER_PASSES;
+        return c;
     }
-    int mode = 0;
-    Launch l = p.launch;
+    c.launch = p.launch;
+    c.path = EW_PATH_VIEW_GENERIC;
     if (stride_c == 1) {
-        mode = 1;
+        c.path = EW_PATH_VIEW_ROWS;
     } else if (stride_r == 1 && rows >= 2 && cols >= 2) {
-        mode = 2;
-        // 128 x 128 tiles; the grid is capped at blocks_per_cu blocks per CU
-        // (the table's row for this size), beyond which blocks stride
+        c.path = EW_PATH_VIEW_TRANSPOSE;
+        // 128 x 128 tiles of 1024 threads; the grid is capped at
+        // blocks_per_cu blocks per CU (the table's row for this size), beyond
+        // which blocks stride
         const uint64_t tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
         const uint64_t cap = (uint64_t)cus * (uint64_t)p.blocks_per_cu;
-        l.grid = (int)(tiles < cap ? tiles : cap);
+        c.launch.grid = (int)(tiles < cap ? tiles : cap);
+        c.launch.block = transpose_threads();
+        c.launch.unroll = 1;
     }
-    log_launch("copy2d_f32", n, a.head, a.vectors, a.tail, l,
-               mode == 1 ? "rows contiguous" : mode == 2 ? "transpose tiles" : "generic");
-    const hipError_t e = launch_copy2d(a, mode, l, s);
+    return c;
+}
+
+}  // namespace
+}  // namespace ew
+
+extern "C" {
+
+ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, float *out,
+                          size_t rows, size_t cols, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return EW_OK;
+    ew_status_t st = copy2d_check(in, stride_r, stride_c, out, rows, cols);
+    if (st != EW_OK) return st;
+    int cus = 0;
+    st = current_device(&cus);
+    if (st != EW_OK) return st;
+    const Copy2dPlan c = copy2d_plan(in, stride_r, stride_c, out, rows, cols, cus);
+    const size_t n = rows * cols;
+    hipError_t e;
+    switch (c.path) {
+    case EW_PATH_GATHER_SPANS:
+        log_launch("copy2d_f32", n, c.g.head, c.g.vectors, c.g.tail, c.launch, "view x[::2]");
+        e = launch_gather(c.g, c.launch, s);
+        break;
+    case EW_PATH_GATHER_PASSES:
+        log_launch("copy2d_f32", n, 0, c.g.vectors, 0, c.launch, "view x[::s], s = 3..8");
+        e = launch_gather(c.g, c.launch, s);
+        break;
+    default: {
+        const int mode = c.path == EW_PATH_VIEW_ROWS ? 1 : c.path == EW_PATH_VIEW_TRANSPOSE ? 2 : 0;
+        log_launch("copy2d_f32", n, c.a.head, c.a.vectors, c.a.tail, c.launch,
+                   mode == 1 ? "rows contiguous" : mode == 2 ? "transpose tiles" : "generic");
+        e = launch_copy2d(c.a, mode, c.launch, s);
+    }
+    }
     return e == hipSuccess ? EW_OK : fail_hip(e);
+}
+
+ew_status_t ew_make_copy2d_plan(const void *in, int64_t stride_r, int64_t stride_c,
+                                const void *out, size_t rows, size_t cols, int cu_count,
+                                ew_plan_t *plan)
+{
+    if (!plan || cu_count <= 0) return EW_ERR_INVALID_ARG;
+    std::memset(plan, 0, sizeof *plan);
+    plan->vec_elems = 4;
+    plan->elem_size = 4;
+    plan->in_coaligned[0] = plan->in_coaligned[1] = 1;
+    plan->reps = 1;
+    plan->passes = 1;
+    if (rows == 0 || cols == 0) return EW_OK;
+    const float *inf = static_cast<const float *>(in);
+    float *outf = static_cast<float *>(const_cast<void *>(out));
+    const ew_status_t st = copy2d_check(inf, stride_r, stride_c, outf, rows, cols);
+    if (st != EW_OK) return st;
+    const Copy2dPlan c = copy2d_plan(inf, stride_r, stride_c, outf, rows, cols, cu_count);
+    const bool gather = c.path == EW_PATH_GATHER_SPANS || c.path == EW_PATH_GATHER_PASSES;
+    plan->n = rows * cols;
+    plan->head = gather ? c.g.head : c.a.head;
+    plan->vectors = gather ? c.g.vectors : c.a.vectors;
+    plan->tail = gather ? c.g.tail : c.a.tail;
+    plan->tiles = gather ? c.g.tiles : c.a.tiles;
+    if (c.path == EW_PATH_VIEW_TRANSPOSE) plan->tiles = ((rows + 127) / 128) * ((cols + 127) / 128);
+    plan->block = c.launch.block;
+    plan->grid = c.launch.grid;
+    plan->unroll = c.launch.unroll;
+    plan->blocks_per_cu = c.blocks_per_cu;
+    plan->segment = plan->n;
+    if (c.path == EW_PATH_GATHER_PASSES) plan->passes = c.g.passes;
+    plan->path = c.path;
+    return EW_OK;
 }
 
 ew_status_t ew_bias_relu_f32(const float *x, const float *bias, float *y, size_t rows,
@@ -1340,6 +1430,7 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0, const
     plan->segment = n;
     plan->reps = 1;
     plan->passes = 1;
+    plan->path = id == kOpGatherWalkF32 ? EW_PATH_GATHER_WALK : EW_PATH_STREAM;
     return EW_OK;
 }
 
@@ -1352,11 +1443,20 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     if (stride == 0) return EW_ERR_INVALID_ARG;
     const ew_status_t st = validate(kOpGatherF32, out, in, nullptr, n);
     if (st != EW_OK) return st;
+    if (n == 1 || stride % n == 1) {
+        // out[i] = in[i mod n] = in[i]: ew_gather_f32 runs the contiguous copy
+        const ew_status_t sc = ew_make_plan("copy_f32", out, in, nullptr, n, cu_count, plan);
+        plan->path = EW_PATH_COPY;
+        return sc;
+    }
     GatherArgs g{};
     Launch l{};
     int bpc = 0;
     gather_plan(static_cast<const float *>(in), static_cast<float *>(const_cast<void *>(out)), n,
                 stride, cu_count, &g, &l, &bpc);
+    plan->path = g.passes ? EW_PATH_GATHER_PASSES
+                 : (g.stride == 2 && g.reps == 2) ? EW_PATH_GATHER_SPANS
+                 : EW_PATH_GATHER_WALK;
     plan->n = n;
     plan->head = g.head;
     plan->vectors = g.vectors;

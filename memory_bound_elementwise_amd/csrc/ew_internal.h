@@ -197,6 +197,10 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
 // per thread, one tile per block and round).
 int gather_passes_threads();
 
+// Threads per block of the transpose kernel (one 128 x 128 tile per block
+// and round).
+int transpose_threads();
+
 // mode 0: generic (one 4-byte load per element), 1: rows contiguous
 // (sc == 1, 16-byte loads inside a row), 2: LDS-tiled transpose (sr == 1).
 hipError_t launch_copy2d(const Copy2dArgs &args, int mode, const Launch &launch,

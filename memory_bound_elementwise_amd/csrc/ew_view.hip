@@ -152,6 +152,8 @@ __global__ void __launch_bounds__(kTThreads) ew_transpose_kernel(Copy2dArgs a)
 // Dispatch
 // ---------------------------------------------------------------------------
 
+int transpose_threads() { return kTThreads; }
+
 hipError_t launch_copy2d(const Copy2dArgs &args, int mode, const Launch &l, hipStream_t s)
 {
     Copy2dArgs a = args;

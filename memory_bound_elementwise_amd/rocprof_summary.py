@@ -183,6 +183,34 @@ def cmd_traffic(a):
         "algorithmic_bytes": alg, "summary": os.path.basename(a.out)})
 
 
+def _mangled_pattern(instance):
+    """A regex for the Itanium-mangled name of a kernel instance: rocprofv3
+    leaves names mangled when it cannot demangle them (template arguments of
+    type _Float16 or __bf16).  The identifiers, the 16-bit types and the
+    integer and boolean template arguments must appear in order."""
+    toks = []
+    for t in re.findall(r"[A-Za-z_][A-Za-z_0-9]*|\d+", instance.replace("ew::", "")):
+        if t == "_Float16":
+            toks.append("DF16_")
+        elif t == "__bf16":
+            toks.append("DF16b")
+        elif t in ("true", "false"):
+            toks.append("Lb1E" if t == "true" else "Lb0E")
+        elif t.isdigit():
+            toks.append(f"Li{t}E")
+        else:
+            toks.append(f"{len(t)}{t}")
+    return re.compile("^_ZN2ew" + ".*?".join(map(re.escape, toks)))
+
+
+def kernel_matches(instance, name):
+    """Whether a trace's kernel name is the given instance (demangled, or
+    mangled where the profiler left it so)."""
+    if name.startswith("_Z"):
+        return bool(_mangled_pattern(instance).search(name))
+    return ("ew::" + instance + "(") in name.replace("void ", "")
+
+
 def cmd_configs(a):
     """Per-dispatch durations of every workload's kernel in one traced bench
     run: each record that names its kernel instance is matched to the trace
@@ -209,18 +237,34 @@ def cmd_configs(a):
         "|---|---|---|---|---|---|---|---|---|",
     ]
     wanted = [w for w in a.workloads.split(",")] if a.workloads else sorted(recs)
+    # two workloads with the same kernel instance and launch shape cannot be
+    # told apart in the trace: neither is reported
+    shape = {}
+    for name, r in recs.items():
+        if r.get("kernel") and r.get("launch"):
+            key = (r["kernel"], r["launch"].get("block"), r["launch"].get("grid"))
+            shape.setdefault(key, []).append(name)
+    ambiguous = {n for names in shape.values() if len(names) > 1 for n in names}
+    names_seen = {}
     for name in wanted:
         r = recs.get(name)
         if not r or not r.get("kernel") or not r.get("gbs"):
             continue
+        if name in ambiguous:
+            text.append(f"| {name} | {r['kernel']} | (same kernel and launch as another "
+                        "workload of the run: not separable in the trace) | | | | | | |")
+            continue
         lc = r["launch"]
-        kname = "ew::" + r["kernel"]
+        if r["kernel"] not in names_seen:
+            names_seen[r["kernel"]] = {x["Kernel_Name"] for x in rows
+                                       if kernel_matches(r["kernel"], x["Kernel_Name"])}
+        knames = names_seen[r["kernel"]]
         d = sorted(int(x["End_Timestamp"]) - int(x["Start_Timestamp"]) for x in rows
-                   if kname + "(" in x["Kernel_Name"].replace("void ", "")
+                   if x["Kernel_Name"] in knames
                    and int(x["Workgroup_Size_X"]) == lc["block"]
                    and int(x["Grid_Size_X"]) == lc["block"] * lc["grid"])
         if not d:
-            print(f"no dispatch of {name}'s kernel {kname} in {a.trace}", file=sys.stderr)
+            print(f"no dispatch of {name}'s kernel {r['kernel']} in {a.trace}", file=sys.stderr)
             continue
         avg, med = statistics.fmean(d), statistics.median(d)
         p10, p90 = d[len(d) // 10], d[(9 * len(d)) // 10]

@@ -98,12 +98,34 @@ def test_kernel_instance_names_match_the_profiler_s_demangled_names():
             == "ew_stream_kernel<ew::OpMap16<__bf16, ew::FnSqrtWidenedBF16>, 1, true, true>")
     assert (bench.kernel_instance(W["relu_inplace_f32_2e28_nonneg"], {"unroll": 1}, split)
             == "ew_relu_inplace_kernel<1>")
-    assert (bench.kernel_instance(W["gather_walk_f32_2e26_s2"], {"unroll": 1}, split)
-            == "ew_gather_kernel<1>")
-    assert (bench.kernel_instance(W["cfg5b_gather_f32_2e26_s2"],
-                                  {"unroll": 1, "path": "contiguous 16-byte loads, even "
-                                                        "elements kept"}, split)
-            == "ew_gather2_kernel<1, true>")
+    import memory_bound_elementwise_amd as ew
+
+    class Prep:            # the workload's device buffers, as made-up addresses
+        def __init__(self, src):
+            self.view_src = src
+            self.ptrs = (None, type("T", (), {"data_ptr": lambda self_: src})(), None)
+
+    base, out = 1 << 40, 1 << 42
+    walk = ew.ew_make_plan("gather_walk_f32", out, base, 0, 1 << 26, 256)
+    assert (bench.kernel_instance(W["gather_walk_f32_2e26_s2"], {"unroll": 1}, split, walk, ew,
+                                  Prep(base)) == "ew_gather_kernel<1>")
+    spans = ew.ew_make_gather_plan(out, base, 1 << 26, 2, 256)
+    assert (bench.kernel_instance(W["cfg5b_gather_f32_2e26_s2"], {"unroll": 1}, split, spans,
+                                  ew, Prep(base)) == "ew_gather2_kernel<1, true>")
+    assert (bench.kernel_instance(W["cfg5b_gather_f32_2e26_s2"], {"unroll": 1}, split, spans,
+                                  ew, Prep(base + 4)) == "ew_gather2_kernel<1, false>")
+    passes = ew.ew_make_gather_plan(out, base, 1 << 26, 3, 256)
+    assert (bench.kernel_instance(W["gather_f32_2e26_s3"], {"unroll": 1}, split, passes, ew,
+                                  Prep(base)) == "ew_gather_passes_kernel<3, false>")
+    view = ew.ew_make_copy2d_plan(base, 0, 3, out, 1, 1 << 24, 256)
+    assert (bench.kernel_instance(W["strided_view_f32_2e24_s3"], {"unroll": 1}, split, view, ew,
+                                  Prep(base)) == "ew_gather_passes_kernel<3, true>")
+    tr = ew.ew_make_copy2d_plan(base, 1, 16384, out, 16384, 16384, 256)
+    assert (bench.kernel_instance(W["transpose_f32_16384x16384"], {"unroll": 1}, split, tr, ew,
+                                  Prep(base)) == "ew_transpose_kernel")
+    assert (bench.kernel_instance(W["fused_bias_relu_f32_65536x4096"], {"unroll": 1},
+                                  {"in_coaligned": [1, 1], "head": 0})
+            == "ew_bias_relu_kernel<1, true, true>")
     assert (bench.kernel_instance(W["batch_add_f32_1024x1024"], {"unroll": 2}, split)
             == "ew_batch_table_kernel<ew::OpAddF32, 2>")
 
@@ -311,3 +333,23 @@ def test_rocprof_summaries_read_the_bench_output_and_the_profiler_csv(tmp_path):
              "--out", str(tmp_path / "c.txt")])
     text = (tmp_path / "c.txt").read_text()
     assert "SQ_LDS_BANK_CONFLICT   40" in text and "LDS-active cycles: 0.400" in text
+
+
+def test_kernel_names_match_in_demangled_and_mangled_form():
+    """rocprofv3 leaves kernels with _Float16 / __bf16 template arguments
+    mangled; the summary still finds each instance, and only that one."""
+    from memory_bound_elementwise_amd.rocprof_summary import kernel_matches
+    relu_f16 = "_ZN2ew16ew_stream_kernelINS_8OpRelu16IDF16_EELi1ELb1ELb1EEEvNS_10StreamArgsE"
+    sqrt_bf16 = ("_ZN2ew16ew_stream_kernelINS_7OpMap16IDF16bNS_17FnSqrtWidenedBF16EEELi1ELb1E"
+                 "Lb1EEEvNS_10StreamArgsE")
+    assert kernel_matches("ew_stream_kernel<ew::OpRelu16<_Float16>, 1, true, true>", relu_f16)
+    assert not kernel_matches("ew_stream_kernel<ew::OpRelu16<__bf16>, 1, true, true>", relu_f16)
+    assert not kernel_matches("ew_stream_kernel<ew::OpRelu16<_Float16>, 2, true, true>", relu_f16)
+    assert not kernel_matches("ew_stream_kernel<ew::OpRelu16<_Float16>, 1, false, true>",
+                              relu_f16)
+    assert kernel_matches(
+        "ew_stream_kernel<ew::OpMap16<__bf16, ew::FnSqrtWidenedBF16>, 1, true, true>", sqrt_bf16)
+    name = "void ew::ew_stream_kernel<ew::OpAddF32, 1, true, true>(ew::StreamArgs)"
+    assert kernel_matches("ew_stream_kernel<ew::OpAddF32, 1, true, true>", name)
+    assert not kernel_matches("ew_stream_kernel<ew::OpAddF32, 1, false, true>", name)
+    assert kernel_matches("ew_transpose_kernel", "ew::ew_transpose_kernel(ew::Copy2dArgs)")

@@ -216,3 +216,35 @@ def test_gather_plan_validation():
         ew.ew_make_gather_plan(BASE, BASE, 16, 2, CUS)
     p = ew.ew_make_gather_plan(0, 0, 0, 2, CUS)
     assert p.vectors == 0 and p.reps == 0
+
+
+def test_every_plan_names_its_kernel_path():
+    """ew_plan_t.path says which kernel runs: the stream kernel, the copy
+    that a stride of 1 mod n becomes, the gather's walk / spans / passes, the
+    view paths; ew_make_copy2d_plan reports the launch the view makes (the
+    transpose's fixed 1024-thread block and its 128 x 128 tiles)."""
+    P = {name: k for k, name in enumerate(ew.PATHS)}
+    base, out = 1 << 40, 1 << 42
+    assert ew.ew_make_plan("add_f32", out, base, base + (1 << 30), 1000, 256).path == P["stream"]
+    assert ew.ew_make_plan("gather_walk_f32", out, base, 0, 1000, 256).path == P["gather_walk"]
+    g = ew.ew_make_gather_plan
+    assert g(out, base, 1000, 1, 256).path == P["copy"]
+    assert g(out, base, 1000, 1001, 256).path == P["copy"]
+    assert g(out, base, 1 << 20, 2, 256).path == P["gather_spans"]
+    assert g(out, base, (1 << 20) + 1, 3, 256).path == P["gather_passes"]
+    assert g(out, base, (1 << 20) + 1, 2, 256).path == P["gather_passes"]
+    assert g(out, base, 1 << 20, 9, 256).path == P["gather_walk"]
+    c = ew.ew_make_copy2d_plan
+    p = c(base, 0, 2, out, 1, 1 << 20, 256)
+    assert p.path == P["gather_spans"] and p.head + 4 * p.vectors + p.tail == 1 << 20
+    p = c(base, 0, 5, out, 1, 1 << 20, 256)
+    assert p.path == P["gather_passes"] and p.passes == 5 and p.block == 256
+    assert c(base, 20000, 1, out, 100, 16000, 256).path == P["view_rows"]
+    p = c(base, 1, 300, out, 300, 517, 256)
+    assert p.path == P["view_transpose"] and p.block == 1024 and p.unroll == 1
+    assert p.tiles == 3 * 5 and p.grid == min(15, 256 * p.blocks_per_cu)
+    assert c(base, 7, 3, out, 100, 100, 256).path == P["view_generic"]
+    # the same validation as the call itself
+    with pytest.raises(ew.EwError):
+        c(base, 1, 300, base + 4, 300, 517, 256)
+    assert c(base, 1, 300, out, 0, 517, 256).n == 0
