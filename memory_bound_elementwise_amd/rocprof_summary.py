@@ -19,12 +19,15 @@ profiles/traffic.json, which bench.py reads (keyed by workload, kernel
 source hash and launch shape):
 
     python -m memory_bound_elementwise_amd.rocprof_summary traffic \
-        --workload NAME --family FAMILY --kernel REGEX \
+        --workload NAME --family FAMILY \
         --fetch DIR/..._counter_collection.csv --write DIR/..._counter_collection.csv \
-        --calib-kernel REGEX --calib-bytes-read R --calib-bytes-written W \
-        --calib-fetch CSV --calib-write CSV \
+        --calib-workload COPY_WORKLOAD --calib-fetch CSV --calib-write CSV \
+        --calib-bench-json COPY_FETCH_RUN_OUTPUT \
         --bench-json FETCH_RUN_OUTPUT --bench-json-write WRITE_RUN_OUTPUT \
         --command-fetch "..." --command-write "..." --command-calib "..." --out profiles/FILE.txt
+
+Each run's dispatches are matched by the kernel instance and launch shape
+that its bench.py record names.
 
 The launch shape, the algorithmic bytes and the kernel source hash written
 into every record are the ones the profiled bench.py run printed for that
@@ -115,17 +118,21 @@ def kernel_stats(path, kernel_re):
     raise SystemExit(f"no kernel matching {kernel_re!r} in {path}")
 
 
-def counter_per_dispatch(path, kernel_re, counter):
-    """Median over dispatches of the counter summed within each dispatch."""
-    rx = re.compile(kernel_re)
+def counter_per_dispatch(path, kernel, counter, launch=None):
+    """Median over dispatches of the counter summed within each dispatch, for
+    the dispatches of one kernel instance (see kernel_matches) -- and, given
+    its launch, of that grid and block only."""
     per = {}
     for r in _rows(path):
-        if r.get("Counter_Name") != counter or not rx.search(r.get("Kernel_Name", "")):
+        if r.get("Counter_Name") != counter or not kernel_matches(kernel, r.get("Kernel_Name", "")):
             continue
-        per.setdefault(r.get("Dispatch_Id") or r.get("Correlation_Id"), 0.0)
-        per[r.get("Dispatch_Id") or r.get("Correlation_Id")] += float(r["Counter_Value"])
+        if launch and (int(r["Workgroup_Size"]) != launch["block"]
+                       or int(r["Grid_Size"]) != launch["block"] * launch["grid"]):
+            continue
+        key = r.get("Dispatch_Id") or r.get("Correlation_Id")
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
     if not per:
-        raise SystemExit(f"no {counter} rows for kernel {kernel_re!r} in {path}")
+        raise SystemExit(f"no {counter} rows for kernel {kernel!r} in {path}")
     return statistics.median(per.values()), len(per)
 
 
@@ -138,21 +145,24 @@ def dispatch_durations(path, kernel_re):
 
 
 def cmd_traffic(a):
-    fetch_kib, nd_f = counter_per_dispatch(a.fetch, a.kernel, "FETCH_SIZE")
-    write_kib, nd_w = counter_per_dispatch(a.write, a.kernel, "WRITE_SIZE")
-    cal_f, _ = counter_per_dispatch(a.calib_fetch, a.calib_kernel, "FETCH_SIZE")
-    cal_w, _ = counter_per_dispatch(a.calib_write, a.calib_kernel, "WRITE_SIZE")
-    scale_f = a.calib_bytes_read / (cal_f * 1024)
-    scale_w = a.calib_bytes_written / (cal_w * 1024)
+    rec = bench_record(a.bench_json, a.workload)
+    cal = bench_record(a.calib_bench_json, a.calib_workload)
+    fetch_kib, nd_f = counter_per_dispatch(a.fetch, rec["kernel"], "FETCH_SIZE", rec["launch"])
+    write_kib, nd_w = counter_per_dispatch(a.write, rec["kernel"], "WRITE_SIZE", rec["launch"])
+    cal_f, _ = counter_per_dispatch(a.calib_fetch, cal["kernel"], "FETCH_SIZE", cal["launch"])
+    cal_w, _ = counter_per_dispatch(a.calib_write, cal["kernel"], "WRITE_SIZE", cal["launch"])
+    # the calibration is a copy: half its algorithmic bytes read, half written
+    scale_f = (cal["algorithmic_bytes"] // 2) / (cal_f * 1024)
+    scale_w = (cal["algorithmic_bytes"] // 2) / (cal_w * 1024)
     fetch_b = fetch_kib * 1024 * scale_f
     write_b = write_kib * 1024 * scale_w
     total = fetch_b + write_b
-    rec = bench_record(a.bench_json, a.workload)
     launch = rec["launch"]
     src_hash = profiled_hash(a.bench_json, a.workload)
     if profiled_hash(a.bench_json_write, a.workload) != src_hash:
         raise SystemExit("the FETCH_SIZE and WRITE_SIZE runs were built from different sources")
     alg = rec["algorithmic_bytes"]
+    cal_bytes = cal["algorithmic_bytes"]
     text = [
         f"# HBM traffic: {a.workload}",
         "",
@@ -160,12 +170,12 @@ def cmd_traffic(a):
         f"write command: {a.command_write}",
         f"calibration:   {a.command_calib}",
         "",
-        f"kernel:            {rec.get('kernel') or a.kernel}  launch {json.dumps(launch)}",
+        f"kernel:            {rec['kernel']}  launch {json.dumps(launch)}",
         f"FETCH_SIZE:        {fetch_kib:.0f} KiB per dispatch (median of {nd_f})",
         f"WRITE_SIZE:        {write_kib:.0f} KiB per dispatch (median of {nd_w})",
-        f"calibration copy:  FETCH {cal_f:.0f} KiB for {a.calib_bytes_read} B read -> scale "
-        f"{scale_f:.4f};  WRITE {cal_w:.0f} KiB for {a.calib_bytes_written} B written -> scale "
-        f"{scale_w:.4f}",
+        f"calibration copy:  {a.calib_workload}: FETCH {cal_f:.0f} KiB for {cal_bytes // 2} B "
+        f"read -> scale {scale_f:.4f};  WRITE {cal_w:.0f} KiB for {cal_bytes // 2} B written "
+        f"-> scale {scale_w:.4f}",
         f"HBM bytes/launch:  fetch {fetch_b:.0f} + write {write_b:.0f} = {total:.0f}",
         f"algorithmic bytes: {alg}  (traffic / algorithmic = {total / alg:.4f})",
         f"kernel sources:    {a.family} family sha256[:16] {src_hash} (of the profiled runs)",
@@ -176,7 +186,7 @@ def cmd_traffic(a):
     _merge(a.index or TRAFFIC_JSON, "HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                     "scaled by the copy-kernel calibration; see the .txt "
                                     "summaries", a.workload, {
-        "kernel": rec.get("kernel") or a.kernel, "launch": launch,
+        "kernel": rec["kernel"], "launch": launch,
         "kernel_source_sha256_16": src_hash,
         "fetch_kib": fetch_kib, "write_kib": write_kib, "scale_fetch": scale_f,
         "scale_write": scale_w, "hbm_bytes_per_launch": round(total),
@@ -288,9 +298,10 @@ def cmd_counters(a):
     data in LDS), with bank-conflict cycles as a share of LDS-active cycles
     when both were collected."""
     rec = bench_record(a.bench_json, a.workload)
-    rows = [r for r in _rows(a.csv) if re.search(a.kernel, r.get("Kernel_Name", ""))]
+    kernel = a.kernel or rec["kernel"]
+    rows = [r for r in _rows(a.csv) if kernel_matches(kernel, r.get("Kernel_Name", ""))]
     if not rows:
-        raise SystemExit(f"no dispatch of {a.kernel!r} in {a.csv}")
+        raise SystemExit(f"no dispatch of {kernel!r} in {a.csv}")
     per = {}
     for r in rows:
         key = (r["Counter_Name"], r.get("Dispatch_Id") or r.get("Correlation_Id"))
@@ -324,14 +335,14 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("--workload", required=True)
-    r.add_argument("--kernel", required=True)
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
-    r.add_argument("--calib-kernel", required=True)
-    r.add_argument("--calib-bytes-read", type=int, required=True)
-    r.add_argument("--calib-bytes-written", type=int, required=True)
+    r.add_argument("--calib-workload", required=True,
+                   help="the copy workload whose known bytes calibrate both counters")
     r.add_argument("--calib-fetch", required=True)
     r.add_argument("--calib-write", required=True)
+    r.add_argument("--calib-bench-json", required=True,
+                   help="bench.py output of the calibration's FETCH_SIZE run")
     r.add_argument("--family", required=True, help="kernel family of the workload "
                                                    "(stream, batch, gather, view)")
     r.add_argument("--command-fetch", required=True)
@@ -354,7 +365,7 @@ def main(argv=None):
                                    "profiles/kernel_trace.json)")
     k = sub.add_parser("counters")
     k.add_argument("--csv", required=True, help="counter_collection.csv of one --pmc pass")
-    k.add_argument("--kernel", required=True)
+    k.add_argument("--kernel", help="kernel instance (default: the workload record's)")
     k.add_argument("--workload", required=True)
     k.add_argument("--family", required=True)
     k.add_argument("--bench-json", required=True)
