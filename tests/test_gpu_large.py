@@ -288,3 +288,35 @@ def test_submatrix_view_past_2_pow_32_elements():
     assert np.array_equal(_take(out, idx), _take(src, 3 + r * pitch + c))
     del src, out
     torch.cuda.empty_cache()
+
+
+def test_batch_table_with_an_item_past_2_pow_32_elements():
+    """The device-table batch with one bf16 item of 2^32 + 7 elements (its
+    output one element off alignment) between two small items: 64-bit tile
+    and element arithmetic inside the table kernel, sampled against the
+    oracle, the small items on every element."""
+    n = (1 << 32) + 7
+    _need(3 * 2 * (n + 8))
+    print(f"[large] batch table, bf16 item n={n}", flush=True)
+    abase = torch.empty(n + 8, dtype=torch.int16, device=DEV)
+    b = torch.empty(n, dtype=torch.int16, device=DEV)
+    cbase = torch.empty(n + 8, dtype=torch.int16, device=DEV)
+    a, c = abase[2:2 + n], cbase[1:1 + n]
+    _fill_bits(a, 2654435761, 16)
+    _fill_bits(b, 40503 * 65537, 16)
+    sa, sb = abase[-6:], b[:5]                  # small items reading the big inputs' edges
+    sc1 = torch.empty(5, dtype=torch.int16, device=DEV)
+    sc2 = torch.empty(3, dtype=torch.int16, device=DEV)
+    batch = ew.EwBatch("add_bf16", [(sc1, sa[:5], sb, 5), (c, a, b, n), (sc2, sa[1:4], sb[2:5], 3)])
+    assert batch.plan.items == 3 and batch.plan.tiles > (1 << 16)
+    batch()
+    torch.cuda.synchronize()
+    idx = _samples(n)
+    got = _take(c, idx).view(np.uint16)
+    ref = oracle.add_bf16(_take(a, idx).view(np.uint16), _take(b, idx).view(np.uint16))
+    assert mismatches("add_bf16", got, ref).size == 0
+    h = lambda t: t.cpu().numpy().view(np.uint16)          # noqa: E731
+    assert mismatches("add_bf16", h(sc1), oracle.add_bf16(h(sa[:5]), h(sb))).size == 0
+    assert mismatches("add_bf16", h(sc2), oracle.add_bf16(h(sa[1:4]), h(sb[2:5]))).size == 0
+    del abase, b, cbase, a, c, batch
+    torch.cuda.empty_cache()
