@@ -304,7 +304,7 @@ def test_batch_table_with_an_item_past_2_pow_32_elements():
     a, c = abase[2:2 + n], cbase[1:1 + n]
     _fill_bits(a, 2654435761, 16)
     _fill_bits(b, 40503 * 65537, 16)
-    sa, sb = abase[-6:], b[:5]                  # small items reading the big inputs' edges
+    sa, sb = abase[-6:], b[:5]        # small items: abase past a's end, b's first elements
     sc1 = torch.empty(5, dtype=torch.int16, device=DEV)
     sc2 = torch.empty(3, dtype=torch.int16, device=DEV)
     batch = ew.EwBatch("add_bf16", [(sc1, sa[:5], sb, 5), (c, a, b, n), (sc2, sa[1:4], sb[2:5], 3)])
