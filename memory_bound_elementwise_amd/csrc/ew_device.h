@@ -84,18 +84,6 @@ __device__ __forceinline__ void store16_device(char *tile, uint32_t tile_bytes, 
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0x12);
 }
 
-// The same for an 8-byte store (the stride-2 gather keeps two elements of
-// each 16-byte load).  On MI355X the device-scope form ran 1-2 % faster than
-// plain non-temporal 8-byte stores for the x[::2] view and in a standalone
-// stride-2 gather, and within noise for the library's stride-2 gather.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void store8_device(char *base, uint32_t bytes, uint32_t off, u32x2 v)
-{
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, 0x12);
-}
-
 // ---------------------------------------------------------------------------
 // Per-element operators.  `vec` works on one 16-byte vector, `one` on one
 // element; both see raw bit patterns so that the skeleton is type-agnostic.

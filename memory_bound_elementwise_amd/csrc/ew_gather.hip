@@ -200,21 +200,25 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
 // the first segment reads in[2i] and never wraps.  Instead of four scalar
 // loads per vector, each wave reads its 2 KiB input span with two contiguous
 // 16-byte-per-lane loads (1 KiB per instruction) and keeps elements 0 and 2
-// of each: lane l of a wave covering outputs [o, o + 256) produces outputs
+// of each: lane l of a wave covering outputs [o, o + 256) holds the pair
 // o + 2l, o + 2l + 1 from the first load and o + 128 + 2l, o + 129 + 2l from
-// the second, stored as 8-byte pairs (512 contiguous bytes per instruction,
-// at device scope), once per segment.  A tile is blockDim * U vectors of 4
+// the second.  Neighbouring lanes 2k and 2k + 1 then swap one pair (a DPP
+// lane swap, no LDS): lane 2k holds outputs o + 4k .. o + 4k + 3 and lane
+// 2k + 1 outputs o + 128 + 4k .. o + 131 + 4k, and each stores them as one
+// 16-byte vector at device scope -- one store instruction covers the wave's
+// 1 KiB output run, once per segment.  A tile is blockDim * U vectors of 4
 // outputs, so the launch shape means the same as for the general gather.
-// Measured on MI355X against this shape: lanes loading 32 contiguous bytes
-// each (two adjacent vectors) and storing 16 bytes ran 1-2 % slower (each
-// load instruction then touches twice the cache lines), staging the 2 KiB
-// span through LDS 4 % slower, and two spans per wave 3-5 % slower.
+// Measured on MI355X against 8-byte pair stores: lanes loading 32 contiguous
+// bytes each (two adjacent vectors) ran 1-2 % slower (each load instruction
+// then touches twice the cache lines), staging the 2 KiB span through LDS
+// 4 % slower, and two spans per wave 3-5 % slower.
 template <int U, bool Co>
 __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 {
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & 63u;
     const uint32_t wave = tid >> 6;
+    const bool odd = lane & 1u;
     const uint64_t nthr = blockDim.x;
     const uint64_t seg_bytes = g.seg * 4;
 
@@ -227,6 +231,8 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
     const char *in = reinterpret_cast<const char *>(g.in);
     char *out = reinterpret_cast<char *>(g.out);
     const uint64_t body_end = g.head + g.vectors * 4;
+    // this lane's output vector inside the wave's run of 256 outputs
+    const uint32_t first = odd ? 128 + 4 * (lane >> 1) : 4 * (lane >> 1);
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         const uint64_t o0 = g.head + 4 * t * nthr * U;
         u32x4 x[U][2];
@@ -240,17 +246,20 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const uint64_t o = o0 + ((uint64_t)wave * U + u) * 256;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const uint64_t i = o + 128 * h + 2 * lane;
-                if (i < body_end) {
-                    const u32x2 pair = u32x2{x[u][h].x, x[u][h].z};
-                    // one input read, one array written: device-scope stores,
-                    // the wave's 512-byte half-row as the buffer
-                    for (uint64_t k = 0; k < g.reps; ++k)
-                        store8_device(out + k * seg_bytes + 4 * (o + 128 * h), 512u, 8u * lane,
-                                      pair);
-                }
+            // even lanes pass their second pair, odd lanes their first; the
+            // swap runs in every lane (full wave), the stores are guarded
+            const uint32_t s0 = odd ? x[u][0].x : x[u][1].x;
+            const uint32_t s1 = odd ? x[u][0].z : x[u][1].z;
+            // quad_perm [1, 0, 3, 2]: each lane reads its neighbour's value
+            const uint32_t r0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s0, 0xB1, 0xF, 0xF, false);
+            const uint32_t r1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)s1, 0xB1, 0xF, 0xF, false);
+            const u32x4 v = odd ? u32x4{r0, r1, x[u][1].x, x[u][1].z}
+                                : u32x4{x[u][0].x, x[u][0].z, r0, r1};
+            if (o + first < body_end) {
+                // one input read, one array written: device-scope stores, the
+                // wave's 1 KiB run as the buffer
+                for (uint64_t k = 0; k < g.reps; ++k)
+                    store16_device(out + k * seg_bytes + 4 * o, 1024u, 4u * first, v);
             }
         }
     }
