@@ -2,7 +2,8 @@
 """Achieved HBM bandwidth of the elementwise kernels on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-others] [--no-cpu-baseline] [--details FILE]
+                    [--no-others] [--others LIST] [--no-cpu-baseline] [--no-context]
+                    [--details FILE]
 
 A step is one call of the library on the workload (validation, plan, launch
 of the vectorised grid-stride kernel with its scalar head and tail).  The
@@ -647,7 +648,10 @@ def profiled_for(workload: str, launch_desc: dict, src_hash: str = None):
 
 
 def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_target_s,
-            check=True):
+            check=True, context=True):
+    """Parity gate, then the timing of the workload's launch; with context,
+    also the comparisons beside it (per-launch flushed timing, warm timing,
+    PyTorch's kernel, graph replay, unfused or separate calls)."""
     prep = Prepared(w, torch, np, ew, synth, stream)
     plan = prep.plan(ew, cus)
     launch_desc = {"block": plan.block, "grid": plan.grid, "unroll": plan.unroll}
@@ -697,15 +701,16 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
         sets += [Prepared(w, torch, np, ew, synth, stream, inp=prep.inp)
                  for _ in range(rotation_sets(footprint) - 1)]
         ms = time_rotated(torch, [p.launch for p in sets], stream, steps, warmup)
-        fl_ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush)
         timing = (f"cold: back to back over {len(sets)} copies of the buffers used in turn "
                   f"(>= 1 GiB of other traffic between two uses of one copy), mean")
+    if cold and prep.pre is None and context:
+        fl_ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush)
         res["flushed_per_launch"] = {
             "ms": round(fl_ms, 5), "gbs": round(nbytes / (fl_ms / 1e3) / 1e9, 1),
             "p10_ms": round(LAST_DIST["p10"], 5), "p90_ms": round(LAST_DIST["p90"], 5),
             "timing": "each launch between its own events after a 1 GiB fill, median "
                       "(includes the per-launch event gap and the fill's write-back)"}
-    else:
+    elif not (cold and prep.pre is None):
         ms = time_launches(torch, prep.launch, stream, steps, warmup, flush=flush, pre=prep.pre)
         timing = ("cold (1 GiB flush before each launch), median" if cold else
                   "back-to-back, mean")
@@ -718,6 +723,10 @@ def measure(w, torch, np, ew, synth, stream, steps, warmup, cus, flush_buf, cpu_
     if traffic is not None:
         res["traffic_bytes"] = traffic
         res["traffic_ratio"] = round(traffic / nbytes, 4)
+    if not context:
+        res["context"] = "skipped (--no-context)"
+        del sets[1:]
+        return res, prep, ms
     ctx = prep.torch_context
     if ctx is not None:
         if len(sets) > 1:
@@ -931,6 +940,9 @@ def main(argv=None):
     ap.add_argument("--no-others", action="store_true", help="skip the other configurations")
     ap.add_argument("--others", help="comma-separated: run only these other workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="time only the workload's own launch: no flushed, warm, PyTorch, "
+                         "graph, unfused or separate-call figures (for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--details", help="also write every record in full to this file, one JSON "
                                       "line each (the main workload's last)")
@@ -969,7 +981,8 @@ def main(argv=None):
     log(f"workload {w.name}: {w.description}")
     input_sha = {k: synth.sha256(v)[:16] for k, v in synth.workload_inputs(w).items()}
     res, prep, ms = measure(w, torch, np, ew, synth, stream, args.steps, args.warmup, cus,
-                            flush_buf, args.cpu_seconds, check=not args.no_cpu_baseline)
+                            flush_buf, args.cpu_seconds, check=not args.no_cpu_baseline,
+                            context=not args.no_context)
     log(f"parity {res['parity']}; {res.get('gbs')} GB/s")
     del prep
     torch.cuda.empty_cache()
@@ -989,7 +1002,8 @@ def main(argv=None):
             steps = 200 if ow.n >= (1 << 25) else 1000
             try:
                 r, p, _ = measure(ow, torch, np, ew, synth, stream, steps, 10, cus, flush_buf,
-                                  0.0, check=not args.no_cpu_baseline)
+                                  0.0, check=not args.no_cpu_baseline,
+                                  context=not args.no_context)
                 del p
             except Exception as exc:
                 # recorded, and nothing more is launched (the error may have left the
