@@ -1284,9 +1284,15 @@ ew_status_t ew_bias_relu_f32(const float *x, const float *bias, float *y, size_t
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
 
+static_assert(sizeof(ew_status_t) == sizeof(int), "the status enum is an int in C");
+
 const char *ew_status_string(ew_status_t status)
 {
-    switch (status) {
+    // A C caller may pass any int.  In C++ a value outside the enumerators'
+    // range read as the enum type is undefined, so the bytes are read as int.
+    int v;
+    std::memcpy(&v, &status, sizeof v);
+    switch (v) {
     case EW_OK: return "EW_OK";
     case EW_ERR_INVALID_ARG: return "EW_ERR_INVALID_ARG: null pointer, invalid size, stride or op";
     case EW_ERR_MISALIGNED: return "EW_ERR_MISALIGNED: pointer not aligned to its element size";
