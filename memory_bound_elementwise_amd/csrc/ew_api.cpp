@@ -522,7 +522,7 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
 {
     const uint64_t s = stride % n;
     const uint64_t gcd = std::gcd(s, (uint64_t)n);  // gcd(0, n) == n
-    if (!walk && gcd == 1 && s >= 2 && s <= 8) {
+    if (!walk && gcd == 1 && s >= 2 && s <= (uint64_t)kMaxPasses) {
         // Pass decomposition: output pass k (floor(s*i/n) == k) starts at
         // i_k = ceil(k*n/s) and reads in[s*m + r_k], r_k = s*i_k - k*n; the
         // r_k are distinct because gcd(s, n) == 1.
@@ -1085,7 +1085,7 @@ struct Copy2dPlan {
 
 // Path: a 1-D view with stride 2 (x[::2]) reads contiguous 16-byte spans and
 // keeps the even elements (the stride-2 gather kernel, one segment, no wrap);
-// a 1-D view with stride 3..8 keeps one element in s of contiguously read
+// a 1-D view with stride 3..16 keeps one element in s of contiguously read
 // spans (the pass kernel's residue-0 run); rows contiguous; a transposed view
 // (tiles through LDS); generic.  Arguments already checked.
 Copy2dPlan copy2d_plan(const float *in, int64_t stride_r, int64_t stride_c, float *out,
@@ -1138,7 +1138,7 @@ Copy2dPlan copy2d_plan(const float *in, int64_t stride_r, int64_t stride_c, floa
         c.path = EW_PATH_GATHER_SPANS;
         return c;
     }
-    if (rows == 1 && stride_c >= 3 && stride_c <= 8) {
+    if (rows == 1 && stride_c >= 3 && stride_c <= kMaxPasses) {
         // x[::s]: each wave reads its 1 KiB * s input span contiguously and
         // keeps every s-th element.  n (the kernel's input length) is the
         // view's extent.
@@ -1202,7 +1202,7 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         e = launch_gather(c.g, c.launch, s);
         break;
     case EW_PATH_GATHER_PASSES:
-        log_launch("copy2d_f32", n, 0, c.g.vectors, 0, c.launch, "view x[::s], s = 3..8");
+        log_launch("copy2d_f32", n, 0, c.g.vectors, 0, c.launch, "view x[::s], s = 3..16");
         e = launch_gather(c.g, c.launch, s);
         break;
     default: {

@@ -72,7 +72,7 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
     }
 }
 
-// Small strides coprime with n (2 <= s <= 8, gcd(s, n) == 1): read every
+// Small strides coprime with n (2 <= s <= kMaxPasses = 16, gcd(s, n) == 1): read every
 // input element once.  Output index i reads in[s*i - k*n] where
 // k = floor(s*i / n), so the output is s contiguous passes (k = 0 .. s-1),
 // pass k reading every s-th input element from a residue r_k = (-k*n) mod s,
@@ -97,7 +97,8 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // shapes.  Blocks are therefore 256 threads and each reserves enough LDS
 // that at most kPassBlocksPerCu(S) blocks fit in a CU's 160 KiB: 16 waves per
 // CU for s = 2, 8 for s = 3..5, 4 for s = 6..8 (the best of 4..32 waves per
-// CU and blocks of 256 or 512 threads for every s).  The reservation holds
+// CU and blocks of 256 or 512 threads for every s), and 4 for s = 9..16,
+// whose waves keep 9-16 KiB of loads in flight each.  The reservation holds
 // the waves' staging slices; the rest of it is unused.  The view (FirstOnly:
 // S KiB read, 1 KiB written per wave) ran fastest uncapped, so it reserves
 // only its staging.  A wave only reads back the slice it wrote itself, so no
@@ -123,7 +124,9 @@ constexpr int kPassLdsBytes(int s, bool first_only)
 static_assert(kPassLdsBytes(2, false) * 5 > kLdsBytesPerCu &&
                   kPassLdsBytes(3, false) * 3 > kLdsBytesPerCu &&
                   kPassLdsBytes(6, false) * 2 > kLdsBytesPerCu &&
-                  kPassLdsBytes(8, false) <= kLdsBytesPerCu,
+                  kPassLdsBytes(kMaxPasses, false) * 2 > kLdsBytesPerCu &&
+                  kPassLdsBytes(kMaxPasses, false) <= kLdsBytesPerCu &&
+                  kPassLdsBytes(kMaxPasses, true) <= kLdsBytesPerCu,
               "the LDS reservation must cap the resident pass blocks per CU");
 
 // Orders this wave's LDS accesses at a point of the program: the LDS
@@ -139,6 +142,7 @@ __device__ __forceinline__ void wave_lds_order()
 template <int S, bool FirstOnly>
 __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
 {
+    static_assert(S >= 2 && S <= kMaxPasses, "one pass per residue, dest[] holds kMaxPasses");
     __shared__ u32x4 lds[kPassLdsBytes(S, FirstOnly) / 16];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
     u32x4 *buf = lds + wv * 64 * S;         // this wave's staging slice
@@ -296,6 +300,14 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
         case 6: fn = EW_PASS_FN(6); break;
         case 7: fn = EW_PASS_FN(7); break;
         case 8: fn = EW_PASS_FN(8); break;
+        case 9: fn = EW_PASS_FN(9); break;
+        case 10: fn = EW_PASS_FN(10); break;
+        case 11: fn = EW_PASS_FN(11); break;
+        case 12: fn = EW_PASS_FN(12); break;
+        case 13: fn = EW_PASS_FN(13); break;
+        case 14: fn = EW_PASS_FN(14); break;
+        case 15: fn = EW_PASS_FN(15); break;
+        case 16: fn = EW_PASS_FN(16); break;
         default: return hipErrorInvalidValue;
         }
 #undef EW_PASS_FN

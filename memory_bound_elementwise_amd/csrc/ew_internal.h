@@ -105,6 +105,10 @@ struct BatchTableArgs {
 // elements (out[i + k*n/g] = out[i]); then head / vectors / tail describe one
 // segment and every value is stored `reps` times, `seg` elements apart, so
 // each input element is fetched once instead of g times.
+// Strides up to kMaxPasses that are coprime with n take the pass
+// decomposition below (one kernel instance per stride).
+constexpr int kMaxPasses = 16;
+
 struct GatherArgs {
     const uint32_t *in;
     uint32_t *out;
@@ -119,7 +123,7 @@ struct GatherArgs {
     uint64_t step_vec;   // stride * 4 * blockDim            (mod n): next unrolled vector
     uint64_t step_tile;  // stride * 4 * blockDim * unroll * gridDim (mod n): next tile
     int wide;            // 1 if stride * (n - 1) can exceed 2^64 - 1
-    // Pass decomposition (gcd(stride, n) == 1, 2 <= stride <= 8): passes ==
+    // Pass decomposition (gcd(stride, n) == 1, 2 <= stride <= kMaxPasses): passes ==
     // stride, otherwise 0.  Output pass k is the run of i with
     // floor(stride * i / n) == k; it reads in[stride * m + r] for m = 0, 1,
     // ... where the residue r = (-k * n) mod stride differs from pass to pass.
@@ -127,7 +131,7 @@ struct GatherArgs {
     // ceil(n / stride) (the longest pass) and vectors counts groups of four
     // slots m.
     int passes;
-    uint64_t dest[8];
+    uint64_t dest[kMaxPasses];
     // 1: store only the residue-0 pass (a 1-D strided view x[::stride]: n is
     // then the view's input extent stride * (count - 1) + 1 and dest[0] = 0).
     int first_only;
