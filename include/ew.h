@@ -173,7 +173,7 @@ ew_status_t ew_gather_walk_f32(const float *in, float *out, size_t n, size_t str
  * [PerfNotes] 3.4 (non-contiguous tensors show up as strides) and 3.1-3.2
  * (coalesced versus strided reads).
  * Paths: rows == 1 with stride_c == 2 reads contiguous 16-byte spans and
- * keeps the even elements; rows == 1 with 3 <= stride_c <= 16 reads the
+ * keeps the even elements; rows == 1 with 3 <= stride_c <= 32 reads the
  * view's span contiguously (staged through LDS) and keeps one element in
  * stride_c; stride_c == 1 reads whole 16-byte row segments;
  * stride_r == 1 moves 128 x 128 tiles through LDS so that both reads and
@@ -426,7 +426,7 @@ ew_status_t ew_set_launch_config(const char *op, int block, int blocks_per_cu, i
  * current device, for pointers 16-byte aligned (as device allocations are):
  * threads per block, grid (0 when n == 0: no launch) and unroll.  For the
  * gather this is the index walk's grid (ew_gather_walk_f32, or
- * ew_gather_f32 at a stride > 16 coprime with n); ew_make_gather_plan gives
+ * ew_gather_f32 at a stride > 32 coprime with n); ew_make_gather_plan gives
  * the grid for a given stride.  Needs a device: EW_ERR_NO_DEVICE without
  * one. */
 ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *grid, int *unroll);
@@ -476,7 +476,7 @@ typedef enum ew_path {
     EW_PATH_COPY = 1,            /* a gather with stride 1 mod n: the contiguous copy */
     EW_PATH_GATHER_WALK = 2,     /* per-output index walk (reps equal segments) */
     EW_PATH_GATHER_SPANS = 3,    /* stride 2: contiguous 16-byte loads, even elements kept */
-    EW_PATH_GATHER_PASSES = 4,   /* stride 2..16 coprime with n: spans staged through LDS */
+    EW_PATH_GATHER_PASSES = 4,   /* stride 2..32 coprime with n: spans staged through LDS */
     EW_PATH_VIEW_ROWS = 5,       /* strided view, rows contiguous */
     EW_PATH_VIEW_TRANSPOSE = 6,  /* strided view, 128 x 128 tiles through LDS */
     EW_PATH_VIEW_GENERIC = 7     /* strided view, one 4-byte load per element */
@@ -514,7 +514,7 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * (ew_gather_f32 runs the copy kernel when stride mod n == 1, and a kernel
  * that reads the input with contiguous 16-byte loads when stride mod n == 2
  * and reps == 2.)
- * When g == 1 and 2 <= s <= 16 (s = stride mod n) the output splits into
+ * When g == 1 and 2 <= s <= 32 (s = stride mod n) the output splits into
  * passes = s contiguous runs: run k holds the i with floor(s*i / n) == k and
  * reads every s-th input element from a residue that differs per run, so
  * slot m of all s runs reads the s consecutive elements s*m .. s*m + s - 1.

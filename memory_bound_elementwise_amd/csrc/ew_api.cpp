@@ -1085,7 +1085,7 @@ struct Copy2dPlan {
 
 // Path: a 1-D view with stride 2 (x[::2]) reads contiguous 16-byte spans and
 // keeps the even elements (the stride-2 gather kernel, one segment, no wrap);
-// a 1-D view with stride 3..16 keeps one element in s of contiguously read
+// a 1-D view with stride 3..32 keeps one element in s of contiguously read
 // spans (the pass kernel's residue-0 run); rows contiguous; a transposed view
 // (tiles through LDS); generic.  Arguments already checked.
 Copy2dPlan copy2d_plan(const float *in, int64_t stride_r, int64_t stride_c, float *out,
@@ -1202,7 +1202,7 @@ ew_status_t ew_copy2d_f32(const float *in, int64_t stride_r, int64_t stride_c, f
         e = launch_gather(c.g, c.launch, s);
         break;
     case EW_PATH_GATHER_PASSES:
-        log_launch("copy2d_f32", n, 0, c.g.vectors, 0, c.launch, "view x[::s], s = 3..16");
+        log_launch("copy2d_f32", n, 0, c.g.vectors, 0, c.launch, "view x[::s], s = 3..32");
         e = launch_gather(c.g, c.launch, s);
         break;
     default: {

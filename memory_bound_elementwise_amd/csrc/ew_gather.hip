@@ -5,6 +5,8 @@
 
 #include "ew_device.h"
 
+#include <utility>
+
 namespace ew {
 
 // ---------------------------------------------------------------------------
@@ -72,7 +74,7 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
     }
 }
 
-// Small strides coprime with n (2 <= s <= kMaxPasses = 16, gcd(s, n) == 1): read every
+// Small strides coprime with n (2 <= s <= kMaxPasses = 32, gcd(s, n) == 1): read every
 // input element once.  Output index i reads in[s*i - k*n] where
 // k = floor(s*i / n), so the output is s contiguous passes (k = 0 .. s-1),
 // pass k reading every s-th input element from a residue r_k = (-k*n) mod s,
@@ -97,8 +99,8 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // shapes.  Blocks are therefore 256 threads and each reserves enough LDS
 // that at most kPassBlocksPerCu(S) blocks fit in a CU's 160 KiB: 16 waves per
 // CU for s = 2, 8 for s = 3..5, 4 for s = 6..8 (the best of 4..32 waves per
-// CU and blocks of 256 or 512 threads for every s), and 4 for s = 9..16,
-// whose waves keep 9-16 KiB of loads in flight each.  The reservation holds
+// CU and blocks of 256 or 512 threads for every s), and 4 for s = 9..32,
+// whose waves keep 9-32 KiB of loads in flight each.  The reservation holds
 // the waves' staging slices; the rest of it is unused.  The view (FirstOnly:
 // S KiB read, 1 KiB written per wave) ran fastest uncapped, so it reserves
 // only its staging.  A wave only reads back the slice it wrote itself, so no
@@ -274,6 +276,21 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 
 namespace {
 
+// The pass kernel for s = 2 .. kMaxPasses (S = 2 + I), or null.
+template <int... I>
+const void *pass_fn(int s, bool first_only, std::integer_sequence<int, I...>)
+{
+    const void *fn = nullptr;
+    ((s == I + 2 ? (void)(fn = first_only
+                                   ? reinterpret_cast<const void *>(
+                                         &ew_gather_passes_kernel<I + 2, true>)
+                                   : reinterpret_cast<const void *>(
+                                         &ew_gather_passes_kernel<I + 2, false>))
+                 : (void)0),
+     ...);
+    return fn;
+}
+
 template <int U, bool Co>
 const void *gather2_fn()
 {
@@ -289,28 +306,9 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
     void *kargs[] = {&a};
     const void *fn = nullptr;
     if (args.passes >= 2) {
-#define EW_PASS_FN(S) (args.first_only                                                        \
-                           ? reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, true>)   \
-                           : reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, false>))
-        switch (args.passes) {
-        case 2: fn = EW_PASS_FN(2); break;
-        case 3: fn = EW_PASS_FN(3); break;
-        case 4: fn = EW_PASS_FN(4); break;
-        case 5: fn = EW_PASS_FN(5); break;
-        case 6: fn = EW_PASS_FN(6); break;
-        case 7: fn = EW_PASS_FN(7); break;
-        case 8: fn = EW_PASS_FN(8); break;
-        case 9: fn = EW_PASS_FN(9); break;
-        case 10: fn = EW_PASS_FN(10); break;
-        case 11: fn = EW_PASS_FN(11); break;
-        case 12: fn = EW_PASS_FN(12); break;
-        case 13: fn = EW_PASS_FN(13); break;
-        case 14: fn = EW_PASS_FN(14); break;
-        case 15: fn = EW_PASS_FN(15); break;
-        case 16: fn = EW_PASS_FN(16); break;
-        default: return hipErrorInvalidValue;
-        }
-#undef EW_PASS_FN
+        fn = pass_fn(args.passes, args.first_only != 0,
+                     std::make_integer_sequence<int, kMaxPasses - 1>{});
+        if (!fn) return hipErrorInvalidValue;
         return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, 0, s);
     }
     if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {

@@ -107,7 +107,7 @@ struct BatchTableArgs {
 // each input element is fetched once instead of g times.
 // Strides up to kMaxPasses that are coprime with n take the pass
 // decomposition below (one kernel instance per stride).
-constexpr int kMaxPasses = 16;
+constexpr int kMaxPasses = 32;
 
 struct GatherArgs {
     const uint32_t *in;

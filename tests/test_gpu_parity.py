@@ -293,14 +293,14 @@ def test_gather_brute_force_strides(op):
 
 
 def test_gather_pass_decomposition_small_strides():
-    """Strides 2..16 coprime with n take the pass-decomposed kernel: every
+    """Strides 2..32 coprime with n take the pass-decomposed kernel: every
     such stride at every n up to 80 and at ragged larger n, with aligned and
     misaligned input and output."""
     import math
     print("[parity] gather passes", flush=True)
     cases = []
     for n in list(range(3, 81)) + [1000, 4099, 65537, (1 << 20) + 1, 3 * 5 * 7 * 4096 + 1]:
-        for s in range(2, 17):
+        for s in range(2, 33):
             if s >= n or math.gcd(s, n) != 1:
                 continue
             for oo, oi in ((0, 0), (1, 0), (0, 3), (3, 2)):
@@ -321,7 +321,7 @@ def test_gather_pass_decomposition_launch_variants():
             cases = []
             if bpc > 8:
                 continue      # the kernel's block shape is fixed: only the grid cap varies
-            for s in (3, 5, 8, 11, 16):
+            for s in (3, 5, 8, 11, 16, 29):
                 # one group (four outputs per pass) per thread of the fixed block
                 threads = ew.ew_make_gather_plan(1 << 40, 1 << 42, 1000003, s, cus).block
                 n = (2 * bpc * cus + 1) * threads * 4 * s - 7
@@ -500,9 +500,9 @@ def test_copy2d_paths_shapes_and_strides():
         for off_out in range(4):
             k += 1
             failures += _copy2d_case(1, cols, 0, 2, 400 + k, off_out)
-    # 1-D views x[::s], s = 3..16 (one element kept per s of a contiguously
+    # 1-D views x[::s], s = 3..32 (one element kept per s of a contiguously
     # read span): short and ragged lengths, every output alignment
-    for sc in range(3, 17):
+    for sc in range(3, 33):
         for cols in list(range(1, 21)) + [255, 256, 257, 1000, 4099]:
             for off_out in (0, 1, 3):
                 k += 1
@@ -522,6 +522,7 @@ def test_copy2d_large_tiles_and_variants():
     failures += _copy2d_case(1, (1 << 20) + 3, 0, 8, 456)       # x[::8]
     failures += _copy2d_case(1, (1 << 20) + 7, 0, 13, 457, 1)   # x[::13]
     failures += _copy2d_case(1, (1 << 19) + 1, 0, 16, 458)      # x[::16]
+    failures += _copy2d_case(1, (1 << 18) + 9, 0, 32, 459, 2)   # x[::32]
     failures += _copy2d_case(1500, 1999, 2111, 1, 453, 3)       # submatrix, misaligned rows
     failures += _copy2d_case(999, 1001, -1001, 1, 454)          # rows in reverse order
     try:

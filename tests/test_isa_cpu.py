@@ -66,7 +66,7 @@ def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
     gather stage data in LDS.  A pass block of the full gather (256 threads,
     16 * stride bytes per lane) reserves just over 1/(k + 1) of the CU's
     160 KiB so that at most k blocks share a CU: k = 4 for stride 2, 2 for
-    3..5, 1 for 6..16.  The x[::s] view's block reserves its staging only."""
+    3..5, 1 for 6..32.  The x[::s] view's block reserves its staging only."""
     ks = _kernels(asm)
     assert len(ks) > 100
     for name, (_, meta) in ks.items():

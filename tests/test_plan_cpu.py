@@ -139,8 +139,9 @@ def test_plan_rejects_what_the_operation_rejects():
     (1024, 1026, 2, 512, 1),         # stride reduced mod n first
     (1 << 20, 3, 1, 349526, 3),      # stride 3, power-of-two n: three passes
     ((1 << 20) + 1, 9, 1, 116509, 9),          # stride 9, gcd 1: nine passes
-    ((1 << 20) + 1, 16, 1, 65537, 16),         # the largest pass stride
-    ((1 << 20) + 1, 19, 1, (1 << 20) + 1, 1),  # gcd 1 but stride 19 > 16: per output
+    ((1 << 20) + 1, 16, 1, 65537, 16),
+    ((1 << 20) + 1, 32, 1, 32769, 32),         # the largest pass stride
+    ((1 << 20) + 1, 37, 1, (1 << 20) + 1, 1),  # gcd 1 but stride 37 > 32: per output
     (16, 16, 1, 16, 1),              # stride == n: gcd(0, n) = n > 8
     (8, 8, 1, 8, 1),                 # gcd 8 but n/8 = 1 is not a multiple of 4
 ])
@@ -176,7 +177,7 @@ def test_gather_pass_decomposition_matches_the_definition():
     import oracle
     x = np.arange(1, 1001, dtype=np.uint32).view(np.float32)
     for n in list(range(3, 120)) + [997, 1000]:
-        for s in range(2, 17):
+        for s in range(2, 33):
             if s >= n or math.gcd(s, n) != 1:
                 continue
             p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, s, CUS)
@@ -237,16 +238,17 @@ def test_every_plan_names_its_kernel_path():
     assert g(out, base, (1 << 20) + 1, 2, 256).path == P["gather_passes"]
     assert g(out, base, (1 << 20) + 1, 16, 256).path == P["gather_passes"]
     assert g(out, base, 1 << 20, 9, 256).path == P["gather_passes"]
-    assert g(out, base, 1 << 20, 17, 256).path == P["gather_walk"]
+    assert g(out, base, 1 << 20, 31, 256).path == P["gather_passes"]
+    assert g(out, base, 1 << 20, 33, 256).path == P["gather_walk"]
     assert g(out, base, 1 << 20, 18, 256).path == P["gather_walk"]     # gcd 2, n/2 % 4 == 0: reps
     c = ew.ew_make_copy2d_plan
     p = c(base, 0, 2, out, 1, 1 << 20, 256)
     assert p.path == P["gather_spans"] and p.head + 4 * p.vectors + p.tail == 1 << 20
     p = c(base, 0, 5, out, 1, 1 << 20, 256)
     assert p.path == P["gather_passes"] and p.passes == 5 and p.block == 256
-    p = c(base, 0, 16, out, 1, 1 << 20, 256)
-    assert p.path == P["gather_passes"] and p.passes == 16
-    assert c(base, 0, 17, out, 1, 1 << 20, 256).path == P["view_generic"]
+    p = c(base, 0, 32, out, 1, 1 << 20, 256)
+    assert p.path == P["gather_passes"] and p.passes == 32
+    assert c(base, 0, 33, out, 1, 1 << 20, 256).path == P["view_generic"]
     assert c(base, 20000, 1, out, 100, 16000, 256).path == P["view_rows"]
     p = c(base, 1, 300, out, 300, 517, 256)
     assert p.path == P["view_transpose"] and p.block == 1024 and p.unroll == 1
