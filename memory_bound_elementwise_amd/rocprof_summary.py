@@ -292,6 +292,39 @@ def cmd_configs(a):
     print("\n".join(text))
 
 
+# MI355X: 8 XCDs, 16 L2 (TCC) channels each.  rocprofv3 reports a TCC
+# counter summed over all 128 channels and GRBM_GUI_ACTIVE summed over the
+# XCDs (a 0.49 ms kernel reads about 8 x 0.49 ms x 2.4 GHz).
+XCDS, CHANNELS_PER_XCD = 8, 16
+
+
+def memory_side_lines(med):
+    """Derived figures of the L2-to-memory interface counters, when
+    collected: mean request latency (requests in flight summed per cycle /
+    requests, as the counters' definitions state), the requests in flight
+    per L2 channel, and the share of the channels' busy cycles in which the
+    interface had no DRAM credits left."""
+    out = []
+    busy = med.get("GRBM_GUI_ACTIVE")
+    cycles = busy / XCDS if busy else None          # busy cycles of one XCD
+    channels = XCDS * CHANNELS_PER_XCD
+    for kind, what in (("RD", "read"), ("WR", "write")):
+        level, req = med.get(f"TCC_EA0_{kind}REQ_LEVEL"), med.get(f"TCC_EA0_{kind}REQ")
+        if level and req:
+            out.append(f"mean {what} request latency, L2 to memory: {level / req:.0f} cycles "
+                       f"(TCC_EA0_{kind}REQ_LEVEL / TCC_EA0_{kind}REQ)")
+            if cycles:
+                out.append(f"{what} requests in flight per L2 channel: "
+                           f"{level / cycles / channels:.0f} (TCC_EA0_{kind}REQ_LEVEL / "
+                           f"busy cycles / {channels} channels)")
+    for c, what in (("TCC_EA0_RDREQ_DRAM_CREDIT_STALL", "read"),
+                    ("TCC_EA0_WRREQ_DRAM_CREDIT_STALL", "write")):
+        if c in med and cycles:
+            out.append(f"{what} interface out of DRAM credits: "
+                       f"{med[c] / (cycles * channels):.3f} of the L2 channels' busy cycles")
+    return out
+
+
 def cmd_counters(a):
     """Per-dispatch medians of the counters of one rocprofv3 --pmc pass for
     the workload's kernel (e.g. the LDS counters of the kernels that stage
@@ -314,7 +347,8 @@ def cmd_counters(a):
         "",
         f"command: {a.command}",
         f"source:  {os.path.basename(a.csv)}, kernel {rows[0]['Kernel_Name'].split('(')[0]}, "
-        f"{dispatches} dispatches (median per dispatch; SQ counters summed over the SEs)",
+        f"{dispatches} dispatches (median per dispatch; each counter summed over its "
+        f"hardware instances)",
         f"launch:  {json.dumps(rec.get('launch'))}",
         "",
     ]
@@ -322,6 +356,7 @@ def cmd_counters(a):
     if "SQ_LDS_BANK_CONFLICT" in med and med.get("SQ_LDS_IDX_ACTIVE"):
         text.append(f"bank-conflict cycles / LDS-active cycles: "
                     f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE']:.3f}")
+    text += memory_side_lines(med)
     text.append(f"kernel sources: {a.family} family sha256[:16] "
                 f"{profiled_hash(a.bench_json, a.workload)} (of the profiled run)")
     with open(a.out, "w") as f:

@@ -353,3 +353,19 @@ def test_kernel_names_match_in_demangled_and_mangled_form():
     assert kernel_matches("ew_stream_kernel<ew::OpAddF32, 1, true, true>", name)
     assert not kernel_matches("ew_stream_kernel<ew::OpAddF32, 1, false, true>", name)
     assert kernel_matches("ew_transpose_kernel", "ew::ew_transpose_kernel(ew::Copy2dArgs)")
+
+
+def test_memory_side_counter_figures():
+    """Latency = requests in flight summed per cycle / requests; in flight per
+    channel = that sum / one XCD's busy cycles / 128 channels; credit stalls
+    as a share of the channels' busy cycles (GRBM_GUI_ACTIVE is summed over
+    the 8 XCDs, the TCC counters over the 128 channels)."""
+    from memory_bound_elementwise_amd import rocprof_summary as rs
+    med = {"GRBM_GUI_ACTIVE": 8 * 1000.0, "TCC_EA0_RDREQ": 500.0,
+           "TCC_EA0_RDREQ_LEVEL": 128 * 1000 * 300.0,
+           "TCC_EA0_RDREQ_DRAM_CREDIT_STALL": 128 * 1000 * 0.25}
+    lines = rs.memory_side_lines(med)
+    assert any("latency" in ln and f"{128 * 1000 * 300 / 500:.0f} cycles" in ln for ln in lines)
+    assert any("in flight per L2 channel: 300 " in ln for ln in lines)
+    assert any("read interface out of DRAM credits: 0.250" in ln for ln in lines)
+    assert rs.memory_side_lines({"GRBM_GUI_ACTIVE": 1.0}) == []
