@@ -157,7 +157,7 @@ PATH_TEXT = {
     "gather_walk": "per-output index walk (one 4-byte load per output element), "
                    "{reps} segment(s)",
     "gather_spans": "contiguous 16-byte loads, even elements kept",
-    "gather_passes": "{s} passes, input spans staged through LDS",
+    "gather_passes": "{s} run(s) x {reps} segment(s), input spans staged through LDS",
     "view_rows": "rows contiguous",
     "view_transpose": "LDS-tiled transpose (128 x 128 tiles, 1024 threads)",
     "view_generic": "generic (one 4-byte load per element)",
@@ -189,7 +189,10 @@ def kernel_instance(w, launch: dict, split: dict, plan=None, ew=None, prep=None)
     if path == "gather_walk":
         return f"ew_gather_kernel<{u}>"
     if path == "gather_passes":
-        return f"ew_gather_passes_kernel<{plan.passes}, {_b(w.op == 'copy2d_f32')}>"
+        # span S = stride mod n, step G = gcd (runs * segments); a view x[::s]: S = G = s
+        if w.op == "copy2d_f32":
+            return f"ew_gather_passes_kernel<{w.view[1]}, {w.view[1]}>"
+        return f"ew_gather_passes_kernel<{plan.passes * plan.reps}, {plan.reps}>"
     if path == "gather_spans":
         # the input's body start co-aligned: in + 8 * head (two inputs per output)
         src = prep.view_src if w.op == "copy2d_f32" else prep.ptrs[1].data_ptr()

@@ -426,7 +426,7 @@ ew_status_t ew_set_launch_config(const char *op, int block, int blocks_per_cu, i
  * current device, for pointers 16-byte aligned (as device allocations are):
  * threads per block, grid (0 when n == 0: no launch) and unroll.  For the
  * gather this is the index walk's grid (ew_gather_walk_f32, or
- * ew_gather_f32 at a stride > 32 coprime with n); ew_make_gather_plan gives
+ * ew_gather_f32 at a stride mod n above 32); ew_make_gather_plan gives
  * the grid for a given stride.  Needs a device: EW_ERR_NO_DEVICE without
  * one. */
 ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *grid, int *unroll);
@@ -476,7 +476,7 @@ typedef enum ew_path {
     EW_PATH_COPY = 1,            /* a gather with stride 1 mod n: the contiguous copy */
     EW_PATH_GATHER_WALK = 2,     /* per-output index walk (reps equal segments) */
     EW_PATH_GATHER_SPANS = 3,    /* stride 2: contiguous 16-byte loads, even elements kept */
-    EW_PATH_GATHER_PASSES = 4,   /* stride 2..32 coprime with n: spans staged through LDS */
+    EW_PATH_GATHER_PASSES = 4,   /* stride 2..32: spans staged through LDS, runs written */
     EW_PATH_VIEW_ROWS = 5,       /* strided view, rows contiguous */
     EW_PATH_VIEW_TRANSPOSE = 6,  /* strided view, 128 x 128 tiles through LDS */
     EW_PATH_VIEW_GENERIC = 7     /* strided view, one 4-byte load per element */
@@ -505,27 +505,28 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
                          const void *in1, size_t n, int cu_count,
                          ew_plan_t *plan);
 
-/* The gather's plan.  With g = gcd(stride mod n, n), output elements i and
- * i + n/g read the same input element, so the output consists of g equal
- * segments of n/g elements.  When 2 <= g <= 8 and n/g is a multiple of 4,
- * the kernel computes one segment (head / vectors / tail describe it,
- * segment = n/g) and stores each value reps = g times, so each input line is
- * fetched once rather than g times; otherwise segment = n and reps = 1.
- * (ew_gather_f32 runs the copy kernel when stride mod n == 1, and a kernel
- * that reads the input with contiguous 16-byte loads when stride mod n == 2
- * and reps == 2.)
- * When g == 1 and 2 <= s <= 32 (s = stride mod n) the output splits into
- * passes = s contiguous runs: run k holds the i with floor(s*i / n) == k and
- * reads every s-th input element from a residue that differs per run, so
- * slot m of all s runs reads the s consecutive elements s*m .. s*m + s - 1.
- * The kernel reads the input once, contiguously (staged through LDS), and
- * writes the s runs; segment = ceil(n / s) (the longest run), vectors =
- * groups of four slots, head = tail = 0, block = 256 and unroll = 1 whatever
- * the table says (its blocks_per_cu still caps the grid; the kernel's own LDS
- * reservation limits how many of its blocks share a compute unit).
- * Otherwise passes = 1.  path: EW_PATH_COPY (stride 1 mod n, or n == 1:
- * the copy's plan), EW_PATH_GATHER_PASSES, EW_PATH_GATHER_SPANS (stride 2,
- * reps 2) or EW_PATH_GATHER_WALK.
+/* The gather's plan.  Let s = stride mod n and g = gcd(s, n): output
+ * elements i and i + n/g read the same input element, so the output
+ * consists of reps = g equal segments of segment = n/g elements, and the
+ * kernels compute one segment and store each value g times, so that each
+ * input line is fetched once rather than g times.
+ * s == 1 (or n == 1): the contiguous copy (path EW_PATH_COPY, the copy's
+ * plan).  s == 2 with g == 2 and n/2 a multiple of 4: a kernel that reads the
+ * input with contiguous 16-byte loads (EW_PATH_GATHER_SPANS; head / vectors
+ * / tail describe one segment).
+ * Otherwise 2 <= s <= 32 (EW_PATH_GATHER_PASSES): with s' = s/g, a segment
+ * splits into passes = s' contiguous runs: run k holds the i with
+ * floor(s'*i / segment) == k and reads every s-th input element from an
+ * offset g*r that differs per run (0 <= r < s'), so slot m of all runs reads
+ * from the s consecutive elements s*m .. s*m + s - 1.  The kernel reads the
+ * input once, contiguously (staged through LDS), and writes the runs;
+ * vectors = groups of four slots of the longest run (ceil(segment / s')),
+ * head = tail = 0, block = 256 and unroll = 1 whatever the table says (its
+ * blocks_per_cu still caps the grid; the kernel's own LDS reservation limits
+ * how many of its blocks share a compute unit).
+ * Otherwise (s > 32, or s == 0) the per-output index walk
+ * (EW_PATH_GATHER_WALK), on one segment when 2 <= g <= 8 and n/g is a
+ * multiple of 4 (else segment = n and reps = 1); passes = 1.
  * Same validation as ew_gather_f32. */
 ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
                                 size_t stride, int cu_count, ew_plan_t *plan);

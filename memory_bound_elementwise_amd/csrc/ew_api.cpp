@@ -20,7 +20,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 12;
+constexpr int kAbiVersion = 13;
 static_assert(kBatchScratchBytes == EW_BATCH_SCRATCH_BYTES, "one scratch size for both sides");
 
 struct OpInfo {
@@ -522,25 +522,31 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
 {
     const uint64_t s = stride % n;
     const uint64_t gcd = std::gcd(s, (uint64_t)n);  // gcd(0, n) == n
-    if (!walk && gcd == 1 && s >= 2 && s <= (uint64_t)kMaxPasses) {
-        // Pass decomposition: output pass k (floor(s*i/n) == k) starts at
-        // i_k = ceil(k*n/s) and reads in[s*m + r_k], r_k = s*i_k - k*n; the
-        // r_k are distinct because gcd(s, n) == 1.
+    // stride 2 with two segments whose length is a multiple of 4: the
+    // stride-2 kernel (contiguous loads, no LDS) below
+    const bool spans2 = s == 2 && gcd == 2 && (n / 2) % 4 == 0;
+    if (!walk && s >= 2 && s <= (uint64_t)kMaxPasses && !spans2) {
+        // Pass decomposition of one of the g = gcd(s, n) equal segments of
+        // n' = n/g outputs, with s' = s/g coprime with n': pass k
+        // (floor(s'*i/n') == k) starts at i_k = ceil(k*n'/s') and reads
+        // in[s*m + g*r_k], r_k = s'*i_k - k*n'; the r_k are distinct.
+        const uint64_t sp = s / gcd, np = n / gcd;
         *g = GatherArgs{};
         g->in = reinterpret_cast<const uint32_t *>(in);
         g->out = reinterpret_cast<uint32_t *>(out);
         g->n = n;
         g->stride = s;
         g->passes = (int)s;
-        for (uint64_t k = 0; k < s; ++k) {
-            const unsigned __int128 kn = (unsigned __int128)k * n;
-            const uint64_t ik = (uint64_t)((kn + s - 1) / s);
-            const uint64_t r = (uint64_t)((unsigned __int128)s * ik - kn);
+        g->skip = (int)gcd;
+        for (uint64_t k = 0; k < sp; ++k) {
+            const unsigned __int128 kn = (unsigned __int128)k * np;
+            const uint64_t ik = (uint64_t)((kn + sp - 1) / sp);
+            const uint64_t r = (uint64_t)((unsigned __int128)sp * ik - kn);
             g->dest[r] = ik;
         }
-        g->seg = (n + s - 1) / s;
-        g->reps = 1;
-        g->vectors = (g->seg + 3) / 4;
+        g->seg = np;
+        g->reps = gcd;
+        g->vectors = ((np + sp - 1) / sp + 3) / 4;
         // fixed block shape (one group per thread); the table's
         // blocks_per_cu still caps the grid
         const Row r = get_row(kOpGatherF32, n);
@@ -1148,7 +1154,7 @@ Copy2dPlan copy2d_plan(const float *in, int64_t stride_r, int64_t stride_c, floa
         g.stride = (uint64_t)stride_c;
         g.n = (uint64_t)stride_c * (n - 1) + 1;
         g.passes = (int)stride_c;
-        g.first_only = 1;
+        g.skip = (int)stride_c;
         g.dest[0] = 0;
         g.seg = n;
         g.reps = 1;
@@ -1244,7 +1250,6 @@ ew_status_t ew_make_copy2d_plan(const void *in, int64_t stride_r, int64_t stride
     plan->unroll = c.launch.unroll;
     plan->blocks_per_cu = c.blocks_per_cu;
     plan->segment = plan->n;
-    if (c.path == EW_PATH_GATHER_PASSES) plan->passes = c.g.passes;
     plan->path = c.path;
     return EW_OK;
 }
@@ -1477,7 +1482,7 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     plan->grid = l.grid;
     plan->segment = g.seg;
     plan->reps = (int)g.reps;
-    plan->passes = g.passes ? g.passes : 1;
+    plan->passes = g.passes ? g.passes / g.skip : 1;     // runs per segment
     return EW_OK;
 }
 

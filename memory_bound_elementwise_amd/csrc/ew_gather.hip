@@ -74,23 +74,27 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
     }
 }
 
-// Small strides coprime with n (2 <= s <= kMaxPasses = 32, gcd(s, n) == 1): read every
-// input element once.  Output index i reads in[s*i - k*n] where
-// k = floor(s*i / n), so the output is s contiguous passes (k = 0 .. s-1),
-// pass k reading every s-th input element from a residue r_k = (-k*n) mod s,
-// and the s residues are all different.  Slot m of all s passes together
-// therefore reads the s consecutive elements in[s*m .. s*m + s - 1].
+// Small strides (2 <= s <= kMaxPasses = 32): read every input element once.
+// With g = gcd(s, n), the output is g equal segments of n' = n/g elements
+// (out[i + k*n'] = out[i]), and segment output i reads in[g * ((s'*i) mod
+// n')] with s' = s/g coprime with n'.  So the segment is s' contiguous passes
+// (k = 0 .. s'-1, the i with floor(s'*i / n') == k), pass k reading
+// in[s*m + g*r_k] for m = 0, 1, ... where the residue r_k = (-k*n') mod s'
+// differs from pass to pass.  Slot m of all s' passes together therefore
+// reads elements g*r (r = 0 .. s'-1) of the s consecutive elements in[s*m ..
+// s*m + s - 1]: S = s is the span of a slot, G = g the step within it.
 //
-// Each lane takes four slots (a group); a wave takes 64 groups, i.e. 1024 * s
-// consecutive input bytes.  The wave reads them with s contiguous 16-byte-
+// Each lane takes four slots (a group); a wave takes 64 groups, i.e. 1024 * S
+// consecutive input bytes.  The wave reads them with S contiguous 16-byte-
 // per-lane loads (1 KiB per instruction), parks them in its own part of LDS,
-// and each lane reads back its 16 * s bytes; then, for each residue r, it
-// writes the four values in[s*(m+q) + r] (q = 0..3) as one 16-byte store to
-// its pass's output run at dest[r] + m.  Letting each lane load its own 16 * s
-// bytes directly instead (s loads 16 * s bytes apart across the lanes) ran
-// 14 % (s = 3) to 70 % (s = 7) slower on MI355X.  The register permutation is
-// fixed at compile time (S is a template parameter); only the destinations
-// are runtime values.
+// and each lane reads back its 16 * S bytes; then, for each residue r, it
+// writes the four values in[S*(m+q) + G*r] (q = 0..3) as one 16-byte store to
+// its pass's output run at dest[r] + m, and again `reps` times one segment
+// further on.  Letting each lane load its own 16 * S bytes directly instead
+// (S loads 16 * S bytes apart across the lanes) ran 14 % (s = 3) to 70 %
+// (s = 7) slower on MI355X.  The register permutation is fixed at compile
+// time (S and G are template parameters); only the destinations are runtime
+// values.
 //
 // Each wave keeps 1 KiB * S of loads in flight, S times what a copy wave
 // keeps, and on MI355X the full gather (S writes per wave) ran fastest with
@@ -101,34 +105,33 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // CU for s = 2, 8 for s = 3..5, 4 for s = 6..8 (the best of 4..32 waves per
 // CU and blocks of 256 or 512 threads for every s), and 4 for s = 9..32,
 // whose waves keep 9-32 KiB of loads in flight each.  The reservation holds
-// the waves' staging slices; the rest of it is unused.  The view (FirstOnly:
-// S KiB read, 1 KiB written per wave) ran fastest uncapped, so it reserves
-// only its staging.  A wave only reads back the slice it wrote itself, so no
-// block barrier is needed: the LDS performs one wave's accesses in issue
-// order, and wavefront-scope fences keep the compiler from moving them (a
-// block barrier there cost up to 5 %).
-// FirstOnly keeps only the residue-0 pass: that is the strided view
-// x[::S] (out[m] = in[S*m]), read as contiguous spans of which 1/S is kept.
+// the waves' staging slices; the rest of it is unused.  A single run (G == S:
+// the strided view x[::S], out[m] = in[S*m], when reps == 1; S KiB read, 1
+// KiB written per wave) ran fastest uncapped, so it reserves only its
+// staging.  A wave only reads back the slice it wrote itself, so no block
+// barrier is needed: the LDS performs one wave's accesses in issue order,
+// and wavefront-scope fences keep the compiler from moving them (a block
+// barrier there cost up to 5 %).
 constexpr int kPassThreads = 256;
 constexpr int kLdsBytesPerCu = 160 * 1024;
 
 constexpr int kPassBlocksPerCu(int s) { return s == 2 ? 4 : s <= 5 ? 2 : 1; }
 
 // Bytes of LDS each pass block reserves: its staging (16 * S bytes per lane)
-// or, for the full gather if larger, just over 1/(blocks + 1) of the CU's LDS
-// so that no more than kPassBlocksPerCu(S) blocks are resident on one CU.
-constexpr int kPassLdsBytes(int s, bool first_only)
+// or, with several runs if larger, just over 1/(blocks + 1) of the CU's LDS so
+// that no more than kPassBlocksPerCu(S) blocks are resident on one CU.
+constexpr int kPassLdsBytes(int s, int runs)
 {
-    return (first_only || kPassThreads * 16 * s > kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024)
+    return (runs == 1 || kPassThreads * 16 * s > kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024)
                ? kPassThreads * 16 * s
                : kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024;
 }
-static_assert(kPassLdsBytes(2, false) * 5 > kLdsBytesPerCu &&
-                  kPassLdsBytes(3, false) * 3 > kLdsBytesPerCu &&
-                  kPassLdsBytes(6, false) * 2 > kLdsBytesPerCu &&
-                  kPassLdsBytes(kMaxPasses, false) * 2 > kLdsBytesPerCu &&
-                  kPassLdsBytes(kMaxPasses, false) <= kLdsBytesPerCu &&
-                  kPassLdsBytes(kMaxPasses, true) <= kLdsBytesPerCu,
+static_assert(kPassLdsBytes(2, 2) * 5 > kLdsBytesPerCu &&
+                  kPassLdsBytes(3, 3) * 3 > kLdsBytesPerCu &&
+                  kPassLdsBytes(6, 2) * 2 > kLdsBytesPerCu &&
+                  kPassLdsBytes(kMaxPasses, 2) * 2 > kLdsBytesPerCu &&
+                  kPassLdsBytes(kMaxPasses, 2) <= kLdsBytesPerCu &&
+                  kPassLdsBytes(kMaxPasses, 1) <= kLdsBytesPerCu,
               "the LDS reservation must cap the resident pass blocks per CU");
 
 // Orders this wave's LDS accesses at a point of the program: the LDS
@@ -141,14 +144,16 @@ __device__ __forceinline__ void wave_lds_order()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int S, bool FirstOnly>
+template <int S, int G>
 __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
 {
-    static_assert(S >= 2 && S <= kMaxPasses, "one pass per residue, dest[] holds kMaxPasses");
-    __shared__ u32x4 lds[kPassLdsBytes(S, FirstOnly) / 16];
+    static_assert(S >= 2 && S <= kMaxPasses && G >= 1 && S % G == 0,
+                  "one run per residue, dest[] holds kMaxPasses");
+    constexpr int kRuns = S / G;
+    __shared__ u32x4 lds[kPassLdsBytes(S, kRuns) / 16];
     const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
     u32x4 *buf = lds + wv * 64 * S;         // this wave's staging slice
-    constexpr int kRuns = FirstOnly ? 1 : S;
+    const uint64_t seg = g.seg;             // replica distance (elements)
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         const uint64_t grp0 = t * kPassThreads + wv * 64;     // first group of this wave
         const uint64_t grp = grp0 + lane;
@@ -171,18 +176,22 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
             for (int r = 0; r < kRuns; ++r) {
                 u32x4 w;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) w[q] = e[(S * q + r) / 4][(S * q + r) % 4];
-                if constexpr (FirstOnly) {
+                for (int q = 0; q < 4; ++q) w[q] = e[(S * q + G * r) / 4][(S * q + G * r) % 4];
+                if (kRuns == 1 && g.reps == 1) {
                     // one array read, one written (the view): a device-scope
                     // store, the wave's 1 KiB as the buffer (4-byte aligned)
                     store16_device(reinterpret_cast<char *>(g.out + g.dest[0] + 4 * grp0),
                                    1024u, 16u * lane, w);
                 } else {
-                    // S runs written at once: plain non-temporal stores (the
-                    // device-scope form ran 19 % slower at stride 3)
-                    u32x4_a4 *p = reinterpret_cast<u32x4_a4 *>(g.out + g.dest[r] + 4 * grp);
-                    if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
-                    else *p = w;
+                    // several runs or replicas written at once: plain
+                    // non-temporal stores (the device-scope form ran 19 %
+                    // slower for the three runs of stride 3)
+                    for (uint64_t k = 0; k < g.reps; ++k) {
+                        u32x4_a4 *p =
+                            reinterpret_cast<u32x4_a4 *>(g.out + k * seg + g.dest[r] + 4 * grp);
+                        if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, p);
+                        else *p = w;
+                    }
                 }
             }
         } else if (grp < g.vectors) {
@@ -193,10 +202,12 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
             for (int k = 0; k < 4 * S; ++k) e[k] = base + k < g.n ? g.in[base + k] : 0u;
 #pragma unroll
             for (int r = 0; r < kRuns; ++r) {
-                uint32_t *dst = g.out + g.dest[r] + 4 * grp;
+                for (uint64_t k = 0; k < g.reps; ++k) {
+                    uint32_t *dst = g.out + k * seg + g.dest[r] + 4 * grp;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    if (base + (uint64_t)S * q + r < g.n) dst[q] = e[S * q + r];
+                    for (int q = 0; q < 4; ++q)
+                        if (base + (uint64_t)S * q + G * r < g.n) dst[q] = e[S * q + G * r];
+                }
             }
         }
     }
@@ -276,16 +287,28 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 
 namespace {
 
-// The pass kernel for s = 2 .. kMaxPasses (S = 2 + I), or null.
-template <int... I>
-const void *pass_fn(int s, bool first_only, std::integer_sequence<int, I...>)
+// The pass kernel of span S and step G (S = 2 .. kMaxPasses, G dividing S),
+// or null.
+template <int S, int G>
+const void *pass_ptr()
+{
+    if constexpr (S % G == 0) return reinterpret_cast<const void *>(&ew_gather_passes_kernel<S, G>);
+    else return nullptr;
+}
+
+template <int S, int... I>
+const void *pass_fn_g(int g, std::integer_sequence<int, I...>)
 {
     const void *fn = nullptr;
-    ((s == I + 2 ? (void)(fn = first_only
-                                   ? reinterpret_cast<const void *>(
-                                         &ew_gather_passes_kernel<I + 2, true>)
-                                   : reinterpret_cast<const void *>(
-                                         &ew_gather_passes_kernel<I + 2, false>))
+    ((g == I + 1 ? (void)(fn = pass_ptr<S, I + 1>()) : (void)0), ...);
+    return fn;
+}
+
+template <int... I>
+const void *pass_fn(int s, int g, std::integer_sequence<int, I...>)
+{
+    const void *fn = nullptr;
+    ((s == I + 2 ? (void)(fn = pass_fn_g<I + 2>(g, std::make_integer_sequence<int, I + 2>{}))
                  : (void)0),
      ...);
     return fn;
@@ -306,10 +329,19 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
     void *kargs[] = {&a};
     const void *fn = nullptr;
     if (args.passes >= 2) {
-        fn = pass_fn(args.passes, args.first_only != 0,
-                     std::make_integer_sequence<int, kMaxPasses - 1>{});
+        fn = pass_fn(args.passes, args.skip, std::make_integer_sequence<int, kMaxPasses - 1>{});
         if (!fn) return hipErrorInvalidValue;
-        return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, 0, s);
+        // A single run stored into several segments writes as many streams
+        // as the runs of a full gather: cap its blocks per CU the same way,
+        // with dynamic LDS on top of the staging (the view, one stream,
+        // runs uncapped).
+        size_t extra = 0;
+        if (args.passes == args.skip && args.reps > 1) {
+            const int cap = kLdsBytesPerCu / kPassBlocksPerCu(args.passes) - 1024;
+            const int staging = kPassLdsBytes(args.passes, 1);
+            if (cap > staging) extra = (size_t)(cap - staging);
+        }
+        return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, extra, s);
     }
     if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {
         // co-alignment of the input's body start: in + 8 * head

@@ -115,7 +115,7 @@ struct GatherArgs {
     uint64_t n;
     uint64_t stride;     // stride mod n
     uint64_t seg;        // elements per output segment (n when reps == 1)
-    uint64_t reps;       // number of identical segments (1..8)
+    uint64_t reps;       // number of identical segments (1..kMaxPasses)
     uint64_t head;
     uint64_t vectors;
     uint64_t tail;
@@ -123,18 +123,19 @@ struct GatherArgs {
     uint64_t step_vec;   // stride * 4 * blockDim            (mod n): next unrolled vector
     uint64_t step_tile;  // stride * 4 * blockDim * unroll * gridDim (mod n): next tile
     int wide;            // 1 if stride * (n - 1) can exceed 2^64 - 1
-    // Pass decomposition (gcd(stride, n) == 1, 2 <= stride <= kMaxPasses): passes ==
-    // stride, otherwise 0.  Output pass k is the run of i with
-    // floor(stride * i / n) == k; it reads in[stride * m + r] for m = 0, 1,
-    // ... where the residue r = (-k * n) mod stride differs from pass to pass.
-    // dest[r] is the first output index of the pass with residue r; seg is
-    // ceil(n / stride) (the longest pass) and vectors counts groups of four
-    // slots m.
+    // Pass decomposition (2 <= stride <= kMaxPasses): passes == stride (the
+    // span S of a slot) and skip == g = gcd(stride, n) (the step G within
+    // it), otherwise passes == 0.  The output is reps = g segments of
+    // seg = n / g elements; in one segment, pass k is the run of i with
+    // floor(s' * i / seg) == k (s' = stride / g); it reads in[stride * m +
+    // g * r] for m = 0, 1, ... where the residue r = (-k * seg) mod s' differs
+    // from pass to pass.  dest[r] is the first output index of the pass with
+    // residue r, and vectors counts groups of four slots m of the longest
+    // pass.  A 1-D strided view x[::s] is passes == skip == s with reps == 1:
+    // one run (dest[0] = 0), n the view's input extent s * (count - 1) + 1.
     int passes;
+    int skip;
     uint64_t dest[kMaxPasses];
-    // 1: store only the residue-0 pass (a 1-D strided view x[::stride]: n is
-    // then the view's input extent stride * (count - 1) + 1 and dest[0] = 0).
-    int first_only;
 };
 
 // Bias + ReLU over a row-major rows x cols matrix (n = rows * cols): the

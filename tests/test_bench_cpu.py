@@ -116,10 +116,13 @@ def test_kernel_instance_names_match_the_profiler_s_demangled_names():
                                   ew, Prep(base + 4)) == "ew_gather2_kernel<1, false>")
     passes = ew.ew_make_gather_plan(out, base, 1 << 26, 3, 256)
     assert (bench.kernel_instance(W["gather_f32_2e26_s3"], {"unroll": 1}, split, passes, ew,
-                                  Prep(base)) == "ew_gather_passes_kernel<3, false>")
+                                  Prep(base)) == "ew_gather_passes_kernel<3, 1>")
+    six = ew.ew_make_gather_plan(out, base, 1 << 26, 6, 256)          # gcd 2: span 6, step 2
+    assert (bench.kernel_instance(W["gather_f32_2e26_s3"], {"unroll": 1}, split, six, ew,
+                                  Prep(base)) == "ew_gather_passes_kernel<6, 2>")
     view = ew.ew_make_copy2d_plan(base, 0, 3, out, 1, 1 << 24, 256)
     assert (bench.kernel_instance(W["strided_view_f32_2e24_s3"], {"unroll": 1}, split, view, ew,
-                                  Prep(base)) == "ew_gather_passes_kernel<3, true>")
+                                  Prep(base)) == "ew_gather_passes_kernel<3, 3>")
     tr = ew.ew_make_copy2d_plan(base, 1, 16384, out, 16384, 16384, 256)
     assert (bench.kernel_instance(W["transpose_f32_16384x16384"], {"unroll": 1}, split, tr, ew,
                                   Prep(base)) == "ew_transpose_kernel")

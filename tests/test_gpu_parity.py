@@ -293,15 +293,17 @@ def test_gather_brute_force_strides(op):
 
 
 def test_gather_pass_decomposition_small_strides():
-    """Strides 2..32 coprime with n take the pass-decomposed kernel: every
-    such stride at every n up to 80 and at ragged larger n, with aligned and
-    misaligned input and output."""
-    import math
+    """Strides 2..32 take the pass-decomposed kernel, with g = gcd(s, n) equal
+    segments of s/g runs (stride 2 on n/2 a multiple of 4 aside, which takes
+    the contiguous-span kernel): every such stride at every n up to 80 and at
+    ragged and highly composite larger n, with aligned and misaligned input
+    and output."""
     print("[parity] gather passes", flush=True)
     cases = []
-    for n in list(range(3, 81)) + [1000, 4099, 65537, (1 << 20) + 1, 3 * 5 * 7 * 4096 + 1]:
+    for n in list(range(3, 81)) + [1000, 4099, 65537, (1 << 20) + 1, 3 * 5 * 7 * 4096 + 1,
+                                   (1 << 20), 720720, 3 * (1 << 18) + 24]:
         for s in range(2, 33):
-            if s >= n or math.gcd(s, n) != 1:
+            if s >= n:
                 continue
             for oo, oi in ((0, 0), (1, 0), (0, 3), (3, 2)):
                 cases.append((n, oo, [oi], s))
@@ -321,14 +323,15 @@ def test_gather_pass_decomposition_launch_variants():
             cases = []
             if bpc > 8:
                 continue      # the kernel's block shape is fixed: only the grid cap varies
-            for s in (3, 5, 8, 11, 16, 29):
+            for s, gcd in ((3, 1), (8, 1), (29, 1), (6, 2), (24, 8), (12, 12)):
                 # one group (four outputs per pass) per thread of the fixed block
                 threads = ew.ew_make_gather_plan(1 << 40, 1 << 42, 1000003, s, cus).block
                 n = (2 * bpc * cus + 1) * threads * 4 * s - 7
-                while math.gcd(n, s) != 1:
+                while math.gcd(n, s) != gcd:
                     n += 1
                 p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
-                assert p.passes == s and p.tiles > 2 * p.grid, (s, p.tiles, p.grid)
+                assert (p.passes, p.reps) == (s // gcd, gcd) and p.tiles > 2 * p.grid, \
+                    (s, p.tiles, p.grid)
                 cases += [(n, 1, [2], s), (n, 0, [0], s)]
             failures = _run_cases("gather_f32", cases, seed=330)
             assert not failures, (block, bpc, unroll, failures[:5])

@@ -52,8 +52,8 @@ def _kernels(text):
     return {k: (bodies[k], meta[k]) for k in bodies}
 
 
-def _pass_lds(stride, first_only):
-    if first_only:
+def _pass_lds(stride, step):
+    if step == stride:          # one run: the staging only
         return 256 * 16 * stride
     blocks_per_cu = 4 if stride == 2 else 2 if stride <= 5 else 1
     lds = max(256 * 16 * stride, 160 * 1024 // blocks_per_cu - 1024)
@@ -63,16 +63,17 @@ def _pass_lds(stride, first_only):
 
 def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
     """Only the transpose (one 128 x 132 fp32 tile) and the pass-decomposed
-    gather stage data in LDS.  A pass block of the full gather (256 threads,
-    16 * stride bytes per lane) reserves just over 1/(k + 1) of the CU's
-    160 KiB so that at most k blocks share a CU: k = 4 for stride 2, 2 for
-    3..5, 1 for 6..32.  The x[::s] view's block reserves its staging only."""
+    gather stage data in LDS.  A pass block that writes several runs (256
+    threads, 16 * stride bytes per lane) reserves just over 1/(k + 1) of the
+    CU's 160 KiB so that at most k blocks share a CU: k = 4 for stride 2, 2
+    for 3..5, 1 for 6..32.  A single run (step == span: the x[::s] view, or a
+    gather whose stride divides n) reserves its staging only."""
     ks = _kernels(asm)
     assert len(ks) > 100
     for name, (_, meta) in ks.items():
         d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
         lds = "67584" if "transpose" in name else (
-            str(_pass_lds(*map(int, re.search(r"passes_kernelILi(\d+)ELb([01])E", name).groups())))
+            str(_pass_lds(*map(int, re.search(r"passes_kernelILi(\d+)ELi(\d+)E", name).groups())))
             if "gather_passes" in name else "0")
         assert d["group_segment_fixed_size"] == lds, name
         assert d["private_segment_fixed_size"] == "0", name

@@ -130,29 +130,34 @@ def test_plan_rejects_what_the_operation_rejects():
 
 
 @pytest.mark.parametrize("n,stride,reps,segment,passes", [
-    (1 << 26, 2, 2, 1 << 25, 1),     # the stride-2 workload: two equal halves
-    ((1 << 26) + 1, 2, 1, (1 << 25) + 1, 2),   # odd n: gcd 1, two passes
-    (1024, 4, 4, 256, 1),
+    (1 << 26, 2, 2, 1 << 25, 1),     # the stride-2 workload: two equal halves (spans)
+    ((1 << 26) + 1, 2, 1, (1 << 26) + 1, 2),   # odd n: gcd 1, two runs
+    (1024, 4, 4, 256, 1),            # gcd 4: four segments of one run
     (1200, 6, 6, 200, 1),
-    (1200, 12, 1, 1200, 1),          # gcd 12 > 8: no replication
-    (1002, 2, 1, 1002, 1),           # n/2 = 501 not a multiple of 4
-    (1024, 1026, 2, 512, 1),         # stride reduced mod n first
-    (1 << 20, 3, 1, 349526, 3),      # stride 3, power-of-two n: three passes
-    ((1 << 20) + 1, 9, 1, 116509, 9),          # stride 9, gcd 1: nine passes
-    ((1 << 20) + 1, 16, 1, 65537, 16),
-    ((1 << 20) + 1, 32, 1, 32769, 32),         # the largest pass stride
-    ((1 << 20) + 1, 37, 1, (1 << 20) + 1, 1),  # gcd 1 but stride 37 > 32: per output
-    (16, 16, 1, 16, 1),              # stride == n: gcd(0, n) = n > 8
-    (8, 8, 1, 8, 1),                 # gcd 8 but n/8 = 1 is not a multiple of 4
+    (1200, 12, 12, 100, 1),          # gcd 12: twelve segments
+    (1002, 2, 2, 501, 1),            # n/2 = 501 not a multiple of 4: passes, not spans
+    (1024, 1026, 2, 512, 1),         # stride reduced mod n first (spans)
+    (1 << 20, 3, 1, 1 << 20, 3),     # stride 3, power-of-two n: three runs
+    (1 << 20, 6, 2, 1 << 19, 3),     # gcd 2: two segments of three runs
+    (1000, 30, 10, 100, 3),          # gcd 10, s' = 3
+    (3 << 18, 24, 24, 1 << 15, 1),   # gcd 24 = the stride
+    ((1 << 20) + 1, 9, 1, (1 << 20) + 1, 9),   # stride 9, gcd 1: nine runs
+    ((1 << 20) + 1, 16, 1, (1 << 20) + 1, 16),
+    ((1 << 20) + 1, 32, 1, (1 << 20) + 1, 32), # the largest pass stride
+    ((1 << 20) + 1, 37, 1, (1 << 20) + 1, 1),  # stride 37 > 32: per output
+    ((1 << 20), 40, 8, 1 << 17, 1),  # stride 40 > 32, gcd 8: walk over one segment
+    (16, 16, 1, 16, 1),              # stride == n: s = 0, gcd(0, n) = n > 8: walk
+    (8, 8, 1, 8, 1),                 # s = 0, gcd 8 but n/8 = 1 is not a multiple of 4
 ])
 def test_gather_plan_segments(n, stride, reps, segment, passes):
     p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
     assert (p.reps, p.segment, p.passes) == (reps, segment, passes)
-    if passes == 1:
+    if ew.PATHS[p.path] != "gather_passes":
         assert p.head + p.vectors * 4 + p.tail == segment
         assert p.head == 0 and p.tail == segment % 4
     else:
-        assert p.head == 0 and p.tail == 0 and p.vectors == -(-segment // 4)
+        # groups of four slots of the longest run
+        assert p.head == 0 and p.tail == 0 and p.vectors == -(-(-(-segment // passes)) // 4)
         assert (p.block, p.unroll) == (256, 1)         # one group of 4 slots per thread
         assert p.tiles == -(-p.vectors // 256)
         assert p.grid == min(p.tiles, p.blocks_per_cu * CUS)
@@ -168,29 +173,40 @@ def _passes(n, s):
 
 
 def test_gather_pass_decomposition_matches_the_definition():
-    """For gcd(s, n) == 1 the outputs with floor(s*i/n) == k form a run that
-    reads in[s*m + r_k], m = 0, 1, ..., from residues r_k that are all
-    different; checked against the oracle's output (a property of the
-    definition, on the CPU), with the planner's pass count and run length."""
+    """With g = gcd(s, n), n' = n/g and s' = s/g, the output is g copies of
+    its first n' elements, and within that segment the outputs with
+    floor(s'*i/n') == k form a run that reads in[s*m + g*r_k], m = 0, 1, ...,
+    from residues r_k that are all different; checked against the oracle's
+    output (a property of the definition, on the CPU), with the planner's
+    segment count, segment length and run count."""
     import math
     import numpy as np
     import oracle
     x = np.arange(1, 1001, dtype=np.uint32).view(np.float32)
     for n in list(range(3, 120)) + [997, 1000]:
         for s in range(2, 33):
-            if s >= n or math.gcd(s, n) != 1:
+            if s >= n:
                 continue
+            g = math.gcd(s, n)
+            n1, s1 = n // g, s // g
             p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, s, CUS)
-            assert p.passes == s and p.segment == -(-n // s)
-            runs = _passes(n, s)
-            assert sorted(r for _, r in runs) == list(range(s))
+            if s == 2 and g == 2 and n1 % 4 == 0:
+                assert ew.PATHS[p.path] == "gather_spans"
+                continue
+            assert ew.PATHS[p.path] == "gather_passes"
+            assert (p.reps, p.segment, p.passes) == (g, n1, s1)
+            assert p.vectors == -(-(-(-n1 // s1)) // 4)
             out = oracle.gather_f32(x[:n], s).view(np.uint32)
             xs = x[:n].view(np.uint32)
-            ends = [ik for ik, _ in runs[1:]] + [n]
+            for k in range(1, g):
+                assert np.array_equal(out[k * n1:(k + 1) * n1], out[:n1]), (n, s, k)
+            runs = _passes(n1, s1)
+            assert sorted(r for _, r in runs) == list(range(s1))
+            ends = [ik for ik, _ in runs[1:]] + [n1]
             for (ik, r), end in zip(runs, ends):
                 m = np.arange(end - ik)
-                assert np.array_equal(out[ik:end], xs[s * m + r]), (n, s, ik, r)
-                assert s * (end - ik) + r >= n > s * (end - ik - 1) + r
+                assert np.array_equal(out[ik:end], xs[s * m + g * r]), (n, s, ik, r)
+                assert s1 * (end - ik) + r >= n1 > s1 * (end - ik - 1) + r
 
 
 def test_gather_replicated_segments_match_the_definition():
@@ -202,8 +218,6 @@ def test_gather_replicated_segments_match_the_definition():
     for n in range(4, 257, 4):
         for stride in range(1, 2 * n + 3):
             p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
-            if p.passes > 1:
-                continue
             assert p.reps * p.segment == n
             if p.reps > 1:
                 out = oracle.gather_f32(x[:n], stride).view(np.uint32)
@@ -240,14 +254,15 @@ def test_every_plan_names_its_kernel_path():
     assert g(out, base, 1 << 20, 9, 256).path == P["gather_passes"]
     assert g(out, base, 1 << 20, 31, 256).path == P["gather_passes"]
     assert g(out, base, 1 << 20, 33, 256).path == P["gather_walk"]
-    assert g(out, base, 1 << 20, 18, 256).path == P["gather_walk"]     # gcd 2, n/2 % 4 == 0: reps
+    assert g(out, base, 1 << 20, 18, 256).path == P["gather_passes"]   # gcd 2: two segments
+    assert g(out, base, 1 << 20, 40, 256).path == P["gather_walk"]     # > 32: walk, 8 segments
     c = ew.ew_make_copy2d_plan
     p = c(base, 0, 2, out, 1, 1 << 20, 256)
     assert p.path == P["gather_spans"] and p.head + 4 * p.vectors + p.tail == 1 << 20
     p = c(base, 0, 5, out, 1, 1 << 20, 256)
-    assert p.path == P["gather_passes"] and p.passes == 5 and p.block == 256
+    assert p.path == P["gather_passes"] and p.passes == 1 and p.block == 256    # one run
     p = c(base, 0, 32, out, 1, 1 << 20, 256)
-    assert p.path == P["gather_passes"] and p.passes == 32
+    assert p.path == P["gather_passes"] and p.passes == 1
     assert c(base, 0, 33, out, 1, 1 << 20, 256).path == P["view_generic"]
     assert c(base, 20000, 1, out, 100, 16000, 256).path == P["view_rows"]
     p = c(base, 1, 300, out, 300, 517, 256)
