@@ -5,7 +5,10 @@
 // the same way on a machine without a GPU.
 
 #include "ew.h"
+#include "ew_batch_args.h"
+#include "ew_gather_args.h"
 #include "ew_internal.h"
+#include "ew_view_args.h"
 
 #include <algorithm>
 #include <atomic>

@@ -2,6 +2,7 @@
 // arrays of one operation in one kernel launch.
 
 #include "ew_device.h"
+#include "ew_batch_args.h"
 
 #include <mutex>
 

@@ -4,6 +4,7 @@
 // and a stride-2 kernel reading contiguous spans.
 
 #include "ew_device.h"
+#include "ew_gather_args.h"
 
 #include <utility>
 

@@ -1,0 +1,57 @@
+// ew_gather_args.h -- the gather's arguments and launcher, shared by
+// the host API (ew_api.cpp) and ew_gather.hip (the x[::s] views run the
+// gather's kernels).  Not installed; not part of the
+// C ABI.
+#pragma once
+
+#include "ew_internal.h"
+
+namespace ew {
+
+// The gather additionally walks its input index (stride * i) mod n
+// incrementally; the steps are reduced mod n on the host.  When
+// g = gcd(stride, n) > 1 the output is g copies of one segment of n / g
+// elements (out[i + k*n/g] = out[i]); then head / vectors / tail describe one
+// segment and every value is stored `reps` times, `seg` elements apart, so
+// each input element is fetched once instead of g times.
+// Strides up to kMaxPasses that are coprime with n take the pass
+// decomposition below (one kernel instance per stride).
+constexpr int kMaxPasses = 32;
+
+struct GatherArgs {
+    const uint32_t *in;
+    uint32_t *out;
+    uint64_t n;
+    uint64_t stride;     // stride mod n
+    uint64_t seg;        // elements per output segment (n when reps == 1)
+    uint64_t reps;       // number of identical segments (1..kMaxPasses)
+    uint64_t head;
+    uint64_t vectors;
+    uint64_t tail;
+    uint64_t tiles;
+    uint64_t step_vec;   // stride * 4 * blockDim            (mod n): next unrolled vector
+    uint64_t step_tile;  // stride * 4 * blockDim * unroll * gridDim (mod n): next tile
+    int wide;            // 1 if stride * (n - 1) can exceed 2^64 - 1
+    // Pass decomposition (2 <= stride <= kMaxPasses): passes == stride (the
+    // span S of a slot) and skip == g = gcd(stride, n) (the step G within
+    // it), otherwise passes == 0.  The output is reps = g segments of
+    // seg = n / g elements; in one segment, pass k is the run of i with
+    // floor(s' * i / seg) == k (s' = stride / g); it reads in[stride * m +
+    // g * r] for m = 0, 1, ... where the residue r = (-k * seg) mod s' differs
+    // from pass to pass.  dest[r] is the first output index of the pass with
+    // residue r, and vectors counts groups of four slots m of the longest
+    // pass.  A 1-D strided view x[::s] is passes == skip == s with reps == 1:
+    // one run (dest[0] = 0), n the view's input extent s * (count - 1) + 1.
+    int passes;
+    int skip;
+    uint64_t dest[kMaxPasses];
+};
+
+hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
+                         hipStream_t stream);
+
+// Threads per block of the pass-decomposed gather (one group of four slots
+// per thread, one tile per block and round).
+int gather_passes_threads();
+
+}  // namespace ew

@@ -3,6 +3,7 @@
 // LDS-tiled transpose for views whose rows are the input's columns.
 
 #include "ew_device.h"
+#include "ew_view_args.h"
 
 namespace ew {
 

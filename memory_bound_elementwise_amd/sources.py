@@ -16,10 +16,10 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 COMMON = ("ew_internal.h", "ew_device.h")
 FAMILIES = {
     "stream": ("ew_stream.hip",),
-    "batch": ("ew_batch.hip",),
-    "gather": ("ew_gather.hip",),
+    "batch": ("ew_batch_args.h", "ew_batch.hip"),
+    "gather": ("ew_gather_args.h", "ew_gather.hip"),
     # the x[::s] views run the gather's kernels
-    "view": ("ew_view.hip", "ew_gather.hip"),
+    "view": ("ew_view_args.h", "ew_view.hip", "ew_gather_args.h", "ew_gather.hip"),
 }
 
 
