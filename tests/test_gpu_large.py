@@ -180,6 +180,33 @@ def test_gather_stride_2_replicated_segments_past_2_pow_32():
     torch.cuda.empty_cache()
 
 
+def test_gather_passes_past_2_pow_32_elements():
+    """The pass-decomposed gather with 64-bit slots, runs and segments: stride
+    6 on n = 2^32 + 2^20 (gcd 2: two segments of three runs each) and stride
+    31 (coprime: 31 runs), sampled against the oracle's index, the two
+    segments of stride 6 equal on every element."""
+    n = (1 << 32) + (1 << 20)
+    _need(2 * 4 * n)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.empty(n, dtype=torch.int32, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    for stride, reps, runs in ((6, 2, 3), (31, 1, 31)):
+        print(f"[large] gather stride {stride}, n={n}", flush=True)
+        plan = ew.ew_make_gather_plan(out.data_ptr(), src.data_ptr(), n, stride, cus)
+        assert ew.PATHS[plan.path] == "gather_passes"
+        assert (plan.reps, plan.passes, plan.segment) == (reps, runs, n // reps)
+        ew.ew_gather_f32(src.data_ptr(), out.data_ptr(), stride, n=n)
+        torch.cuda.synchronize()
+        if reps == 2:
+            assert _chunked_equal(out[: n // 2], out[n // 2:])
+        idx = _samples(n)
+        j = np.array([oracle.gather_index(n, stride, int(i)) for i in idx], np.int64)
+        assert np.array_equal(_take(out, idx), _take(src, j)), stride
+    del src, out
+    torch.cuda.empty_cache()
+
+
 def test_relu_inplace_past_2_pow_32_elements_misaligned():
     n = (1 << 32) + 21
     _need(4 * (n + 8))
