@@ -1,7 +1,7 @@
 // ew_gather.hip -- the strided gather out[i] = in[(s * i) mod n] for CDNA4
-// (gfx950): a per-output index walk, replicated segments, a pass
-// decomposition for small strides coprime with n (input staged through LDS)
-// and a stride-2 kernel reading contiguous spans.
+// (gfx950): a per-output index walk, a pass decomposition for strides up to
+// 32 (input staged through LDS, g = gcd(s, n) replicated segments) and a
+// stride-2 kernel reading contiguous spans.
 
 #include "ew_device.h"
 #include "ew_gather_args.h"

@@ -8,14 +8,14 @@
 
 namespace ew {
 
-// The gather additionally walks its input index (stride * i) mod n
+// The gather's index walk steps its input index (stride * i) mod n
 // incrementally; the steps are reduced mod n on the host.  When
 // g = gcd(stride, n) > 1 the output is g copies of one segment of n / g
 // elements (out[i + k*n/g] = out[i]); then head / vectors / tail describe one
 // segment and every value is stored `reps` times, `seg` elements apart, so
-// each input element is fetched once instead of g times.
-// Strides up to kMaxPasses that are coprime with n take the pass
-// decomposition below (one kernel instance per stride).
+// each input element is fetched once instead of g times.  Strides up to
+// kMaxPasses take the pass decomposition described below (one kernel
+// instance per stride and gcd).
 constexpr int kMaxPasses = 32;
 
 struct GatherArgs {
