@@ -219,10 +219,18 @@ def _numel(x, n):
     return x.numel()
 
 
+# torch's current stream of a device as a raw handle, without building a
+# Stream object (which costs about 2 us per call); the public route where the
+# internal one is missing.
+_raw_current_stream = getattr(getattr(torch, "_C", None), "_cuda_getCurrentRawStream", None)
+
+
 def _stream(x, stream):
     if stream is None:
         if isinstance(x, int):
             return None
+        if _raw_current_stream is not None:
+            return _raw_current_stream(x.get_device())
         return torch.cuda.current_stream(x.device).cuda_stream
     if isinstance(stream, int):
         return stream
