@@ -841,6 +841,50 @@ def run_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):
     return rc
 
 
+# The stride curve: the gather and the per-output walk at n = 2^26 (the fifth
+# configuration's size and input) for every stride 1..32 and a few beyond.
+STRIDE_SWEEP = list(range(1, 33)) + [33, 64, 1000, (1 << 26) - 1]
+
+
+def run_stride_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):
+    """One JSON line per (op, stride): parity against the oracle on every
+    element, then the timing of measure(); resumable like run_sweep."""
+    rc = 0
+    done = set()
+    if out_path and os.path.exists(out_path):
+        with open(out_path) as f:
+            for line in f:
+                try:
+                    r = json.loads(line)
+                except ValueError:
+                    continue
+                if r.get("parity") == "PASS":
+                    done.add((r["op"], r["stride"]))
+    n = 1 << 26
+    for op in ("gather_f32", "gather_walk_f32"):
+        for stride in STRIDE_SWEEP:
+            if (op, stride) in done:
+                log(f"stride sweep {op} s={stride}: already recorded")
+                continue
+            w = synth.Workload(f"stride_{op}_{stride}", op, n, 107, "uniform", stride=stride,
+                               description=f"{op}, n=2^26, stride {stride}, seed 107")
+            log(f"stride sweep {op} s={stride}")
+            res, prep, _ = measure(w, torch, np, ew, synth, stream, 100, 5, cus, flush_buf, 0.0,
+                                   context=False)
+            del prep
+            torch.cuda.empty_cache()
+            res.pop("cpu_baseline", None)
+            res.pop("split", None)
+            res["stride"] = stride
+            print(json.dumps(res), flush=True)
+            if out_path:
+                with open(out_path, "a") as f:
+                    f.write(json.dumps(res) + "\n")
+            if res["parity"] != "PASS":
+                rc = 1
+    return rc
+
+
 def _ratio(a, b):
     return round(a / b, 4) if a and b else None
 
@@ -952,7 +996,11 @@ def main(argv=None):
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the bench line: each op of the five configurations over "
                          "N = 2^20 .. 2^28 plus odd N, one parity-gated JSON line per point")
-    ap.add_argument("--sweep-out", help="with --sweep: append each point to this JSONL file "
+    ap.add_argument("--stride-sweep", action="store_true",
+                    help="instead of the bench line: the gather and the per-output walk at "
+                         "n = 2^26 for strides 1..32 and a few beyond, one parity-gated JSON "
+                         "line per point")
+    ap.add_argument("--sweep-out", help="with --sweep or --stride-sweep: append each point to this JSONL file "
                                         "and skip points it already holds with parity PASS")
     args = ap.parse_args(argv)
 
@@ -979,6 +1027,8 @@ def main(argv=None):
 
     if args.sweep:
         return run_sweep(torch, np, ew, synth, stream, cus, flush_buf, args.sweep_out)
+    if args.stride_sweep:
+        return run_stride_sweep(torch, np, ew, synth, stream, cus, flush_buf, args.sweep_out)
 
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: {w.description}")
