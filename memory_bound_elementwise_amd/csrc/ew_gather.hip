@@ -87,15 +87,19 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 //
 // Each lane takes four slots (a group); a wave takes 64 groups, i.e. 1024 * S
 // consecutive input bytes.  The wave reads them with S contiguous 16-byte-
-// per-lane loads (1 KiB per instruction), parks them in its own part of LDS,
-// and each lane reads back its 16 * S bytes; then, for each residue r, it
+// per-lane loads (1 KiB per instruction) that the memory unit writes straight
+// into the wave's own part of LDS, and each lane reads back its 16 * S
+// bytes; then, for each residue r, it
 // writes the four values in[S*(m+q) + G*r] (q = 0..3) as one 16-byte store to
 // its pass's output run at dest[r] + m, and again `reps` times one segment
 // further on.  Letting each lane load its own 16 * S bytes directly instead
 // (S loads 16 * S bytes apart across the lanes) ran 14 % (s = 3) to 70 %
 // (s = 7) slower on MI355X.  The register permutation is fixed at compile
 // time (S and G are template parameters); only the destinations are runtime
-// values.
+// values.  Loading into VGPRs first and writing them to LDS ran as fast for
+// s <= 22, but from s = 23 on (G = 1) the compiler, short of registers,
+// waited for each load before issuing the next: 2.8-2.9 TB/s against 4.8-4.9
+// with the loads into LDS, which need no data registers.
 //
 // Each wave keeps 1 KiB * S of loads in flight, S times what a copy wave
 // keeps, and on MI355X the full gather (S writes per wave) ran fastest with
@@ -109,10 +113,12 @@ __global__ void __launch_bounds__(1024) ew_gather_kernel(GatherArgs g)
 // the waves' staging slices; the rest of it is unused.  A single run (G == S:
 // the strided view x[::S], out[m] = in[S*m], when reps == 1; S KiB read, 1
 // KiB written per wave) ran fastest uncapped, so it reserves only its
-// staging.  A wave only reads back the slice it wrote itself, so no block
-// barrier is needed: the LDS performs one wave's accesses in issue order,
-// and wavefront-scope fences keep the compiler from moving them (a block
-// barrier there cost up to 5 %).
+// staging.  A wave only reads back the slice its own loads filled, so no
+// block barrier is needed (one there cost up to 5 %): the wave waits for its
+// loads to complete before reading, its next tile's loads are issued only
+// after this tile's stores, which need every value read back, and
+// wavefront-scope fences keep the compiler from moving LDS accesses across
+// those points.
 constexpr int kPassThreads = 256;
 constexpr int kLdsBytesPerCu = 160 * 1024;
 
@@ -145,6 +151,29 @@ __device__ __forceinline__ void wave_lds_order()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The wave's S KiB input span, read with S 16-byte-per-lane loads that the
+// memory unit writes straight into LDS (buffer_load_dwordx4 ... lds): load v
+// puts lane i's 16 bytes, span bytes 1024 * v + 16 * i, at LDS dst + 64 * v
+// + i.  No VGPR holds the data on its way, and the only per-lane operand is
+// the offset 16 * i, so all S loads leave back to back at any S.  `span`
+// and `dst` are the same in every lane of the wave.
+template <int S>
+__device__ __forceinline__ void load_span_to_lds(const char *span, u32x4 *dst, uint32_t lane)
+{
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(span), (short)0, 1024 * S, 0x00020000);
+#pragma unroll
+    for (int v = 0; v < S; ++v)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void *)(dst + 64 * v), 16, (int)(16 * lane),
+            1024 * v, 0, EW_LOAD_NT ? 2 : 0);
+}
+
+// Waits until every vector memory access this wave issued has completed, so
+// the LDS holds what load_span_to_lds fetched (s_waitcnt vmcnt(0); the other
+// counters are left alone).
+__device__ __forceinline__ void wait_lds_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int S, int G>
 __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherArgs g)
 {
@@ -152,7 +181,8 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
                   "one run per residue, dest[] holds kMaxPasses");
     constexpr int kRuns = S / G;
     __shared__ u32x4 lds[kPassLdsBytes(S, kRuns) / 16];
-    const uint32_t tid = threadIdx.x, lane = tid & 63u, wv = tid >> 6;
+    const uint32_t tid = threadIdx.x, lane = tid & 63u;
+    const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // the same in every lane
     u32x4 *buf = lds + wv * 64 * S;         // this wave's staging slice
     const uint64_t seg = g.seg;             // replica distance (elements)
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
@@ -164,10 +194,8 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
             // fallback merged into its registers: the compiler then has no
             // reason to wait for one store to complete before the next.
             const uint64_t wbase = (uint64_t)S * 4 * grp0;    // its first input element
-#pragma unroll
-            for (int v = 0; v < S; ++v)
-                buf[64 * v + lane] = load16<false, 4>(
-                    reinterpret_cast<const char *>(g.in + wbase + 4 * (64 * v + lane)));
+            load_span_to_lds<S>(reinterpret_cast<const char *>(g.in + wbase), buf, lane);
+            wait_lds_loads();
             wave_lds_order();
             u32x4 e[S];
 #pragma unroll

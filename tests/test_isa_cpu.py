@@ -16,6 +16,8 @@ silently; these checks fail the build's tests if it does:
 * the square-root kernels take a refined binary32 root (the hardware
   estimate followed by fma residual corrections), never a native 16-bit
   root, and the scalar maps multiply / add in binary32;
+* the pass-decomposed gather loads each wave's input span straight into LDS,
+  all loads in flight together;
 * the streaming kernels move 16 bytes per lane (global_load_dwordx4 /
   global_store_dwordx4) and store non-temporally; the single-input ones
   (copy, ReLU, in-place ReLU, bias + ReLU, the scalar and unary maps) and the
@@ -150,6 +152,30 @@ def test_transpose_moves_16_bytes_per_lane_through_lds(asm):
         assert re.search(r"global_load_dwordx4 .* nt\b", body)
         assert re.search(r"\bds_write_b128\b", body)
         assert re.search(r"global_store_dwordx4 .* nt\b", body)
+
+
+def test_pass_gather_loads_its_span_straight_into_lds(asm):
+    """Regression: staged through VGPRs, the span loads of the pass gather
+    were issued one at a time (each waited for before the next) once the
+    instance ran short of registers (s >= 23), at 0.6 x the speed.  Every
+    instance must issue its S loads into LDS (buffer_load_dwordx4 ... lds)
+    back to back, with no wait on the vector memory counter between them, and
+    wait for them (vmcnt(0)) before its first LDS read."""
+    ks = {k: v[0] for k, v in _kernels(asm).items() if "gather_passes_kernel" in k}
+    assert len(ks) > 31
+    for name, body in ks.items():
+        S = int(re.search(r"passes_kernelILi(\d+)ELi", name).group(1))
+        lines = [l.strip() for l in body.splitlines()
+                 if l.strip() and not l.strip().startswith((";", "."))]
+        loads = [i for i, l in enumerate(lines) if re.match(r"buffer_load_dwordx4 .*\blds$", l)]
+        assert len(loads) == S, name
+        assert loads[-1] - loads[0] < 8 * S, name          # one run of instructions
+        assert not any(l.startswith("s_waitcnt") and "vmcnt" in l
+                       for l in lines[loads[0]:loads[-1]]), name
+        first_read = next(i for i in range(loads[-1], len(lines)) if lines[i].startswith("ds_read"))
+        waits = [l for l in lines[loads[-1]:first_read] if l.startswith("s_waitcnt")]
+        assert any("vmcnt(0)" in l for l in waits), name
+        assert not re.search(r"\bglobal_load_dwordx4\b", body.split("ds_read")[0]), name
 
 
 def test_inplace_relu_decides_stores_with_a_wave_vote(asm):
