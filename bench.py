@@ -158,6 +158,8 @@ PATH_TEXT = {
                    "{reps} segment(s)",
     "gather_spans": "contiguous 16-byte loads, even elements kept",
     "gather_passes": "{s} run(s) x {reps} segment(s), input spans staged through LDS",
+    "gather_tiles": "{s} run(s) x {reps} segment(s), rows of the stride transposed through "
+                    "LDS",
     "view_rows": "rows contiguous",
     "view_transpose": "LDS-tiled transpose (128 x 128 tiles, 1024 threads)",
     "view_generic": "generic (one 4-byte load per element)",
@@ -193,6 +195,9 @@ def kernel_instance(w, launch: dict, split: dict, plan=None, ew=None, prep=None)
         if w.op == "copy2d_f32":
             return f"ew_gather_passes_kernel<{w.view[1]}, {w.view[1]}>"
         return f"ew_gather_passes_kernel<{plan.passes * plan.reps}, {plan.reps}>"
+    if path == "gather_tiles":
+        # narrow tiles (whole rows) below a stride of 128
+        return f"ew_gather_tiles_kernel<{_b(w.stride % w.n < 128)}>"
     if path == "gather_spans":
         # the input's body start co-aligned: in + 8 * head (two inputs per output)
         src = prep.view_src if w.op == "copy2d_f32" else prep.ptrs[1].data_ptr()

@@ -479,7 +479,9 @@ typedef enum ew_path {
     EW_PATH_GATHER_PASSES = 4,   /* stride 2..32: spans staged through LDS, runs written */
     EW_PATH_VIEW_ROWS = 5,       /* strided view, rows contiguous */
     EW_PATH_VIEW_TRANSPOSE = 6,  /* strided view, 128 x 128 tiles through LDS */
-    EW_PATH_VIEW_GENERIC = 7     /* strided view, one 4-byte load per element */
+    EW_PATH_VIEW_GENERIC = 7,    /* strided view, one 4-byte load per element */
+    EW_PATH_GATHER_TILES = 8     /* stride > 32: rows of `stride` elements transposed
+                                    through LDS, each column written as a run */
 } ew_path_t;
 
 typedef struct ew_plan {
@@ -524,15 +526,26 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * head = tail = 0, block = 256 and unroll = 1 whatever the table says (its
  * blocks_per_cu still caps the grid; the kernel's own LDS reservation limits
  * how many of its blocks share a compute unit).
- * Otherwise (s > 32, or s == 0) the per-output index walk
- * (EW_PATH_GATHER_WALK), on one segment when 2 <= g <= 8 and n/g is a
- * multiple of 4 (else segment = n and reps = 1); passes = 1.
+ * Otherwise, for s > 32 with s' = s/g >= 2, g < 32, at least 128 rows
+ * (ceil(n / s) >= 128), s' < 2^32 and s' * (n/g) < 2^64
+ * (EW_PATH_GATHER_TILES): the input viewed as rows of s elements,
+ * A[m][c] = in[s*m + c], is transposed through LDS: column g*r of A is one
+ * run of a segment (passes = s', clamped to INT_MAX; the run of column g*r
+ * is the k-th with k = (-r * (n/g)^-1) mod s'), written from output
+ * ceil(k * segment / s') on.  block = 1024, unroll = 1, one block per tile
+ * (tiles: for s < 128 bands of floor(16384 / s) rounded down to a multiple
+ * of 4 whole rows, else 128 x 128 tiles), the grid capped at the table's
+ * blocks_per_cu per compute unit, vectors = ceil(segment / 4),
+ * head = tail = 0.
+ * Otherwise (s == 0, or a large stride outside those bounds) the per-output
+ * index walk (EW_PATH_GATHER_WALK), on one segment when 2 <= g <= 8 and n/g
+ * is a multiple of 4 (else segment = n and reps = 1); passes = 1.
  * Same validation as ew_gather_f32. */
 ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
                                 size_t stride, int cu_count, ew_plan_t *plan);
 
 /* The plan of ew_copy2d_f32 with these arguments: its path (x[::2] ->
- * EW_PATH_GATHER_SPANS, x[::s] with s = 3..8 -> EW_PATH_GATHER_PASSES with
+ * EW_PATH_GATHER_SPANS, x[::s] with s = 3..32 -> EW_PATH_GATHER_PASSES with
  * passes = s, stride_c == 1 -> EW_PATH_VIEW_ROWS, stride_r == 1 ->
  * EW_PATH_VIEW_TRANSPOSE, else EW_PATH_VIEW_GENERIC) and the launch it makes
  * (block, grid, unroll as launched; a kernel with a fixed block shape reports

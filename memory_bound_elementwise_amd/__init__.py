@@ -644,7 +644,7 @@ def ew_make_copy2d_plan(src, stride_r, stride_c, out, rows, cols, cu_count) -> E
 
 # ew_path_t: the kernel path of a plan
 PATHS = ("stream", "copy", "gather_walk", "gather_spans", "gather_passes", "view_rows",
-         "view_transpose", "view_generic")
+         "view_transpose", "view_generic", "gather_tiles")
 
 
 def library_path() -> str:

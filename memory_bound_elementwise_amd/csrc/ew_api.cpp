@@ -11,6 +11,7 @@
 #include "ew_view_args.h"
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <cerrno>
 #include <cstdio>
@@ -23,7 +24,7 @@
 namespace ew {
 namespace {
 
-constexpr int kAbiVersion = 13;
+constexpr int kAbiVersion = 14;
 static_assert(kBatchScratchBytes == EW_BATCH_SCRATCH_BYTES, "one scratch size for both sides");
 
 struct OpInfo {
@@ -508,14 +509,29 @@ uint64_t mulmod_host(uint64_t a, uint64_t b, uint64_t m)
     return (uint64_t)(((unsigned __int128)a * (unsigned __int128)b) % (unsigned __int128)m);
 }
 
+// a^-1 mod m for gcd(a, m) == 1 and m >= 2 (extended Euclid).
+uint64_t modinv_host(uint64_t a, uint64_t m)
+{
+    __int128 r0 = m, r1 = a % m, t0 = 0, t1 = 1;
+    while (r1 != 0) {
+        const __int128 q = r0 / r1;
+        const __int128 r2 = r0 - q * r1, t2 = t0 - q * t1;
+        r0 = r1; r1 = r2; t0 = t1; t1 = t2;
+    }
+    if (t0 < 0) t0 += m;
+    return (uint64_t)t0;
+}
+
 // The gather's plan.  With g = gcd(stride mod n, n), output i and output
 // i + n/g read the same input element ((stride * n/g) mod n == 0), so the
-// output is g copies of its first n/g elements.  For 2 <= g <= 8 with n/g a
-// multiple of 4 (so every copy has the same 16-byte alignment) the kernel
-// computes one segment and stores each vector g times: every input line is
-// then fetched once instead of g times.  For g == 1 and a stride of 2 to 8
-// the output splits into `stride` passes that together read the input
-// contiguously (see GatherArgs).  Otherwise one segment of n.
+// output is g copies of its first n/g elements, and the kernels compute one
+// segment and store each value g times: every input line is then fetched
+// once instead of g times.  Strides 2..32: the pass decomposition (see
+// GatherArgs).  Larger strides with at least 128 rows of `stride` elements,
+// g < 32, s' = s/g below 2^32 and s' * n/g below 2^64: the tiled
+// transposition.  Otherwise the per-output walk, over one segment when
+// 2 <= g <= 8 and n/g is a multiple of 4 (every copy then has the same
+// 16-byte alignment), else over all n.
 //
 // walk: the per-output index walk whatever the stride (no pass decomposition
 // and no replicated segments: every output element loads its own input
@@ -561,6 +577,38 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
         *l = Launch{gather_passes_threads(), (int)grid, 1};
         if (blocks_per_cu) *blocks_per_cu = r.blocks_per_cu;
         return;
+    }
+    if (!walk && s > (uint64_t)kMaxPasses) {
+        // Tiled transposition of A[m][c] = in[s*m + c]: column c = g*r is
+        // the pass k = (-r * inv) mod s' of a segment (see GatherArgs).
+        const uint64_t sp = s / gcd, np = n / gcd;
+        const uint64_t rows = (n - 1) / s + 1;
+        if (sp >= 2 && gcd < 32 && rows >= 128 && sp < ((uint64_t)1 << 32) &&
+            (unsigned __int128)sp * np <= (unsigned __int128)UINT64_MAX) {
+            *g = GatherArgs{};
+            g->in = reinterpret_cast<const uint32_t *>(in);
+            g->out = reinterpret_cast<uint32_t *>(out);
+            g->n = n;
+            g->stride = s;
+            g->seg = np;
+            g->reps = gcd;
+            g->sp = sp;
+            g->inv = modinv_host(np % sp, sp);
+            const bool narrow = s < 128;
+            g->tile_mode = narrow ? 1 : 2;
+            g->tile_rows = narrow ? (uint32_t)(kGatherTileWords / s) & ~3u : 128u;
+            g->tiles_m = (rows + g->tile_rows - 1) / g->tile_rows;
+            g->tiles = g->tiles_m * (narrow ? 1 : (s + 127) / 128);
+            g->vectors = (np + 3) / 4;
+            // one block per tile, the grid capped at the table's blocks per
+            // CU for this size (beyond it blocks stride over the tiles)
+            const Row r = get_row(kOpGatherF32, n);
+            const uint64_t cap = (uint64_t)r.blocks_per_cu * (uint64_t)(cus > 0 ? cus : 1);
+            const uint64_t grid = g->tiles < cap ? g->tiles : cap;
+            *l = Launch{gather_tiles_threads(), (int)grid, 1};
+            if (blocks_per_cu) *blocks_per_cu = r.blocks_per_cu;
+            return;
+        }
     }
     uint64_t reps = 1, seg = n;
     if (!walk && gcd >= 2 && gcd <= 8 && (n / gcd) % 4 == 0) {
@@ -647,7 +695,8 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride, 
     Launch l{};
     gather_plan(in, out, n, stride, cus, &g, &l);
     log_launch("gather_f32", n, g.head, g.vectors, g.tail, l,
-               g.passes ? "passes" : g.reps > 1 ? "replicated segments" : "index walk");
+               g.passes ? "passes" : g.tile_mode ? "tiles" : g.reps > 1 ? "replicated segments"
+                                                              : "index walk");
     const hipError_t e = launch_gather(g, l, s);
     return e == hipSuccess ? EW_OK : fail_hip(e);
 }
@@ -1469,6 +1518,7 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     gather_plan(static_cast<const float *>(in), static_cast<float *>(const_cast<void *>(out)), n,
                 stride, cu_count, &g, &l, &bpc);
     plan->path = g.passes ? EW_PATH_GATHER_PASSES
+                 : g.tile_mode ? EW_PATH_GATHER_TILES
                  : (g.stride == 2 && g.reps == 2) ? EW_PATH_GATHER_SPANS
                  : EW_PATH_GATHER_WALK;
     plan->n = n;
@@ -1485,7 +1535,10 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n, size_
     plan->grid = l.grid;
     plan->segment = g.seg;
     plan->reps = (int)g.reps;
-    plan->passes = g.passes ? g.passes / g.skip : 1;     // runs per segment
+    // runs per segment (the tiled path's s' is clamped to INT_MAX)
+    plan->passes = g.passes     ? g.passes / g.skip
+                   : g.tile_mode ? (int)std::min<uint64_t>(g.sp, (uint64_t)INT_MAX)
+                                 : 1;
     return EW_OK;
 }
 

@@ -1,7 +1,8 @@
 // ew_gather.hip -- the strided gather out[i] = in[(s * i) mod n] for CDNA4
 // (gfx950): a per-output index walk, a pass decomposition for strides up to
-// 32 (input staged through LDS, g = gcd(s, n) replicated segments) and a
-// stride-2 kernel reading contiguous spans.
+// 32 (input staged through LDS, g = gcd(s, n) replicated segments), a tiled
+// transposition for larger strides and a stride-2 kernel reading contiguous
+// spans.
 
 #include "ew_device.h"
 #include "ew_gather_args.h"
@@ -310,6 +311,144 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
         }
     }
 }
+
+// Strides beyond the passes (s > 32; here g = gcd(s, n), s' = s/g, n' = n/g
+// as above): view the input as rows of s elements, A[m][c] = in[s*m + c]
+// (the last row stops at n).  Pass k of a segment reads in[s*m + g*r_k] for
+// m = 0, 1, ... while that index is below n, i.e. it is column g*r_k of A,
+// written to the segment's outputs from ceil(k*n'/s') on; every column
+// c = g*r (r < s') is one pass, k = (-r * (n' mod s')^-1) mod s'.  The
+// gather is therefore a transposition of A with the columns placed run by
+// run, and a tile of A through LDS reads every input line once, where the
+// per-output walk fetches a whole 128-byte line for each 4-byte element once
+// s >= 32.  Tiles as in the view transpose: 1024 threads, 16-byte loads
+// along A's rows, LDS rows of 132 words, each lane then reading four
+// consecutive rows of one column and storing them as one 16-byte vector of
+// that column's run (and again `reps` times one segment further on).
+// Narrow (s < 128): a tile is tile_rows whole rows, one contiguous chunk of
+// at most kGatherTileWords input elements, kept in LDS with pitch s; wide:
+// 128 rows by 128 columns.  Consecutive blocks take consecutive row bands
+// of one column band, so each block continues the runs the previous one
+// wrote.  A column's destination needs two 64-bit divisions: the first
+// cols threads compute them once per tile into LDS.
+constexpr int kTileT = 128;                           // wide tile: rows = columns
+constexpr int kTilePitch = kTileT + 4;                // words per LDS row (wide)
+constexpr int kTileLdsWords = kTileT * kTilePitch;    // 16,896 >= kGatherTileWords
+constexpr int kTileThreads = 1024;
+constexpr int kTileSteps = 4;                         // 16-byte loads / stores per thread
+constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
+static_assert(kTileLdsWords >= (int)kGatherTileWords, "a narrow tile fits the LDS tile");
+static_assert(kTileSteps * kTileThreads * 4 == (int)kGatherTileWords &&
+                  kTileSteps * 32 == kTileT,
+              "four steps cover a narrow tile's words and a wide tile's rows");
+
+template <bool Narrow>
+__global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArgs g)
+{
+    __shared__ uint32_t tile[kTileLdsWords];
+    __shared__ uint64_t run_start[kTileT];
+    const uint32_t tid = threadIdx.x;
+    const uint64_t s = g.stride, n = g.n, seg = g.seg;
+    const uint32_t rows = Narrow ? g.tile_rows : (uint32_t)kTileT;   // a multiple of 4
+    const uint32_t cols = Narrow ? (uint32_t)s : (uint32_t)kTileT;
+    const uint32_t pitch = Narrow ? (uint32_t)s : (uint32_t)kTilePitch;
+    const uint32_t groups = rows / 4;         // four-row groups per column
+    for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
+        const uint64_t m0 = (t % g.tiles_m) * rows;
+        const uint64_t c0 = Narrow ? 0 : (t / g.tiles_m) * kTileT;
+        if (tid < cols) {
+            const uint64_t c = c0 + tid;
+            uint64_t d = kNoRun;
+            if (c < s && c % g.reps == 0) {
+                const uint64_t r = c / g.reps;
+                const uint64_t k = (g.sp - r) % g.sp * g.inv % g.sp;   // < sp^2 < 2^64
+                d = (k * seg + g.sp - 1) / g.sp;                       // < sp * seg < 2^64
+            }
+            run_start[tid] = d;
+        }
+        if constexpr (Narrow) {
+            // rows m0 .. m0 + rows - 1 are the contiguous input from s * m0
+            const uint64_t base = s * m0;
+            const uint32_t quads = rows * cols / 4;   // <= kGatherTileWords / 4
+            const bool full = base + 4 * (uint64_t)quads <= n;
+            u32x4 v[kTileSteps];
+#pragma unroll
+            for (int p = 0; p < kTileSteps; ++p) {
+                const uint32_t q = tid + p * kTileThreads;
+                if (q < quads) {
+                    if (full) {
+                        v[p] = load16<false, 4>(
+                            reinterpret_cast<const char *>(g.in + base + 4 * q));
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            v[p][k] = base + 4 * q + k < n ? g.in[base + 4 * q + k] : 0u;
+                    }
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < kTileSteps; ++p) {
+                const uint32_t q = tid + p * kTileThreads;
+                if (q < quads) *reinterpret_cast<u32x4 *>(&tile[4 * q]) = v[p];
+            }
+        } else {
+            // 32 lanes cover 128 columns of one row, 32 rows per step
+            const uint32_t sub = tid / 32, q4 = (tid % 32) * 4;
+            const bool full = c0 + kTileT <= s && s * (m0 + kTileT - 1) + c0 + kTileT <= n;
+            u32x4 v[kTileSteps];
+#pragma unroll
+            for (int p = 0; p < kTileSteps; ++p) {
+                const uint32_t m = p * 32 + sub;
+                const uint64_t e = s * (m0 + m) + c0 + q4;
+                if (full) {
+                    v[p] = load16<false, 4>(reinterpret_cast<const char *>(g.in + e));
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        v[p][k] = c0 + q4 + k < s && e + k < n ? g.in[e + k] : 0u;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < kTileSteps; ++p)
+                *reinterpret_cast<u32x4 *>(&tile[(p * 32 + sub) * kTilePitch + q4]) = v[p];
+        }
+        __syncthreads();
+        // item q: column c, rows 4j .. 4j + 3 of the tile
+        const uint32_t items = cols * groups;        // <= kTileSteps * kTileThreads
+#pragma unroll
+        for (int p = 0; p < kTileSteps; ++p) {
+            const uint32_t q = tid + p * kTileThreads;
+            if (q >= items) break;
+            const uint32_t c = q / groups, j = q % groups;
+            const uint64_t d = run_start[c];
+            if (d == kNoRun) continue;
+            u32x4 w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = tile[(4 * j + k) * pitch + c];
+            const uint64_t m = m0 + 4 * j;            // the group's first row
+            const uint64_t e = s * m + c0 + c;        // its input element
+            const uint64_t o = d + m;                 // its output, within a segment
+            // row m + k exists iff e + k*s < n, and then o + k < seg
+            const bool all = e + 3 * s < n && o + 3 < seg;
+            for (uint64_t k = 0; k < g.reps; ++k) {
+                uint32_t *dst = g.out + k * seg + o;
+                if (all) {
+                    u32x4_a4 *dv = reinterpret_cast<u32x4_a4 *>(dst);
+                    if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w, dv);
+                    else *dv = w;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (e + r * s < n && o + r < seg) dst[r] = w[r];
+                }
+            }
+        }
+        // the tile and run starts are rewritten only if this block has
+        // another round (a block-uniform condition)
+        if (t + gridDim.x < g.tiles) __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Dispatch
 // ---------------------------------------------------------------------------
@@ -351,6 +490,7 @@ const void *gather2_fn()
 }  // namespace
 
 int gather_passes_threads() { return kPassThreads; }
+int gather_tiles_threads() { return kTileThreads; }
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
 {
@@ -371,6 +511,11 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
             if (cap > staging) extra = (size_t)(cap - staging);
         }
         return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, extra, s);
+    }
+    if (args.tile_mode != 0) {
+        fn = args.tile_mode == 1 ? reinterpret_cast<const void *>(&ew_gather_tiles_kernel<true>)
+                                 : reinterpret_cast<const void *>(&ew_gather_tiles_kernel<false>);
+        return hipLaunchKernel(fn, dim3(l.grid), dim3(kTileThreads), kargs, 0, s);
     }
     if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {
         // co-alignment of the input's body start: in + 8 * head

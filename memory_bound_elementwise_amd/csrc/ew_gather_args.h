@@ -45,6 +45,19 @@ struct GatherArgs {
     int passes;
     int skip;
     uint64_t dest[kMaxPasses];
+    // Tiled transposition (larger strides, tile_mode != 0): the input viewed
+    // as rows of `stride` elements, A[m][c] = in[stride * m + c]; column
+    // c = g * r (g = gcd(stride, n) = reps) is one pass of a segment, its
+    // rows m written to out[k * seg + dest(c) + m] for k < reps, where pass
+    // k' = (-r * inv) mod sp starts at dest(c) = ceil(k' * seg / sp),
+    // sp = stride / g and inv = (seg mod sp)^-1 mod sp.  tile_mode 1: one
+    // tile is tile_rows whole rows (stride < 128); 2: 128 x 128 tiles,
+    // tiles_m row bands by ceil(stride / 128) column bands.
+    int tile_mode;
+    uint32_t tile_rows;
+    uint64_t sp;
+    uint64_t inv;
+    uint64_t tiles_m;
 };
 
 hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
@@ -53,5 +66,10 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &launch,
 // Threads per block of the pass-decomposed gather (one group of four slots
 // per thread, one tile per block and round).
 int gather_passes_threads();
+
+// Threads per block of the tiled transposition, and the words of LDS one
+// narrow tile may fill (tile_rows * stride <= this).
+int gather_tiles_threads();
+constexpr uint32_t kGatherTileWords = 16384;
 
 }  // namespace ew

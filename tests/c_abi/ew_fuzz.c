@@ -172,7 +172,7 @@ static void plan_calls(void)
     }
     status_ok(st, "plan");
     if (st != EW_OK) return;
-    if (p.path < EW_PATH_STREAM || p.path > EW_PATH_VIEW_GENERIC) fail("plan path", p.path, which);
+    if (p.path < EW_PATH_STREAM || p.path > EW_PATH_GATHER_TILES) fail("plan path", p.path, which);
     if (which == 0 && p.n > 0) {
         if (p.vec_elems <= 0 || p.head + p.vectors * (size_t)p.vec_elems + p.tail != p.n)
             fail("plan split", (long long)p.n, (long long)p.head);

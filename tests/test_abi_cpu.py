@@ -52,7 +52,7 @@ def test_binding_names_match_the_c_abi():
 
 
 def test_abi_version_and_status_strings():
-    assert ew.ew_abi_version() == 13
+    assert ew.ew_abi_version() == 14
     for code in (EW_OK, EW_ERR_INVALID_ARG, EW_ERR_MISALIGNED, EW_ERR_OVERLAP,
                  EW_ERR_NO_DEVICE, EW_ERR_HIP, EW_ERR_TOO_LARGE):
         s = ew.ew_status_string(code)

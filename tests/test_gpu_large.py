@@ -230,7 +230,40 @@ def test_relu_inplace_past_2_pow_32_elements_misaligned():
     torch.cuda.empty_cache()
 
 
-def test_gather_passes_past_2_pow_32_elements():
+def test_gather_tiles_past_2_pow_32_elements():
+    """The tiled transposition with 64-bit rows, run starts and segments on
+    n = 2^32 + 2^20 = 2^20 * 4097: stride 33 (coprime, narrow tiles of whole
+    rows), 100 (gcd 4: four segments of 25 runs, narrow), 1000 (gcd 8: eight
+    segments of 125 runs, 128 x 128 tiles) and 65537 (coprime, wide),
+    sampled against the oracle's index, replicated segments equal on every
+    element."""
+    n = (1 << 32) + (1 << 20)
+    _need(2 * 4 * n)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    src = torch.empty(n, dtype=torch.int32, device=DEV)
+    out = torch.empty(n, dtype=torch.int32, device=DEV)
+    _fill_bits(src, 2654435761, 32)
+    for stride, reps, runs in ((33, 1, 33), (100, 4, 25), (1000, 8, 125), (65537, 1, 65537)):
+        print(f"[large] gather tiles stride {stride}, n={n}", flush=True)
+        plan = ew.ew_make_gather_plan(out.data_ptr(), src.data_ptr(), n, stride, cus)
+        assert ew.PATHS[plan.path] == "gather_tiles"
+        assert (plan.reps, plan.passes, plan.segment) == (reps, runs, n // reps)
+        ew.ew_gather_f32(src.data_ptr(), out.data_ptr(), stride, n=n)
+        torch.cuda.synchronize()
+        seg = n // reps
+        for k in range(1, reps):
+            assert _chunked_equal(out[:seg], out[k * seg:(k + 1) * seg]), (stride, k)
+        idx = _samples(n)
+        for k in (1, runs // 2, runs - 1):              # around run starts
+            b = -(-k * seg // runs)
+            idx = np.unique(np.concatenate([idx, np.arange(b - 6, b + 6)]))
+        j = np.array([oracle.gather_index(n, stride, int(i)) for i in idx], np.int64)
+        assert np.array_equal(_take(out, idx), _take(src, j)), stride
+    del src, out
+    torch.cuda.empty_cache()
+
+
+def test_gather_passes_stride3_past_2_pow_32_elements():
     """Stride 3 with gcd(3, n) == 1 and n > 2^32: the pass kernel's slot and
     destination arithmetic in 64 bits (host planning in 128)."""
     n = (1 << 32) + 1

@@ -311,6 +311,70 @@ def test_gather_pass_decomposition_small_strides():
     assert not failures, failures[:10]
 
 
+def _tile_cases():
+    """(n, stride) pairs on the tiled transposition: narrow tiles (33..127),
+    wide ones (128 x 128, partial column bands), g = gcd 1..31, exactly 128
+    rows, ragged last rows and bands."""
+    cus = 256
+    pairs = []
+    for n in (4225, 20011, 100003, 1 << 20, (1 << 20) + 5, 3 << 18, 720720 + 1):
+        for s in (33, 34, 37, 40, 48, 63, 65, 97, 100, 126, 127):
+            pairs.append((n, s))
+    for n in ((1 << 20), (1 << 20) + 1, 1000003, 3 * 5 * 7 * 4096 + 1, 4 << 20):
+        for s in (129, 130, 200, 255, 259, 1000, 1281, 4097, 8191):
+            pairs.append((n, s))
+    pairs += [(16511, 129), (33 * 127 + 1, 33), (128 * 1000 + 3, 1000), (31 * 4099, 62),
+              (1 << 20, 80), ((1 << 20) + 48, 176)]
+    out = []
+    for n, s in pairs:
+        p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
+        if ew.PATHS[p.path] == "gather_tiles":
+            out.append((n, s))
+    return out
+
+
+def test_gather_tiled_transposition_large_strides():
+    """Strides above 32 (with g = gcd(s, n) < 32 and at least 128 rows of s
+    elements) take the tiled transposition: narrow and wide tiles, every g
+    from 1 to 31 that the sizes produce, with aligned and misaligned input
+    and output."""
+    print("[parity] gather tiles", flush=True)
+    pairs = _tile_cases()
+    assert len(pairs) > 80
+    assert {math.gcd(n, s) for n, s in pairs} >= {1, 2, 4, 8, 16, 31}
+    assert any(s < 128 for _, s in pairs) and any(s >= 128 for _, s in pairs)
+    cases = []
+    for k, (n, s) in enumerate(pairs):
+        oo, oi = ((0, 0), (1, 0), (0, 3), (3, 2))[k % 4]
+        cases.append((n, oo, [oi], s))
+    failures = _run_cases("gather_f32", cases, seed=345)
+    assert not failures, failures[:10]
+
+
+def test_gather_tiled_transposition_launch_variants():
+    """The tiled transposition with its grid capped below the tile count (the
+    launch table's blocks per CU), so that blocks stride over several tiles
+    and reuse their LDS tile and run starts."""
+    print("[parity] gather tiles variants", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    try:
+        for bpc in (1, 3):
+            _force_launch("gather_f32", 128, bpc, 1)
+            cases = []
+            for n, s in ((cus * bpc * 3 * 16384 + 11, 33), (cus * bpc * 3 * 16384 + 7, 200),
+                         (cus * bpc * 3 * 16384 + 4, 34)):
+                p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
+                assert ew.PATHS[p.path] == "gather_tiles" and p.tiles > 2 * p.grid, \
+                    (n, s, p.tiles, p.grid)
+                cases += [(n, 1, [2], s), (n, 0, [0], s)]
+            failures = _run_cases("gather_f32", cases, seed=350)
+            assert not failures, (bpc, failures[:5])
+    finally:
+        ew.ew_reset_launch_config()
+        if os.path.exists(ew.LAUNCH_TABLE):
+            ew.ew_load_launch_table(ew.LAUNCH_TABLE)
+
+
 def test_gather_pass_decomposition_launch_variants():
     """The pass-decomposed gather under forced grid caps (its block shape is
     fixed), at sizes where the grid-stride loop runs three rounds and the

@@ -144,15 +144,21 @@ def test_plan_rejects_what_the_operation_rejects():
     ((1 << 20) + 1, 9, 1, (1 << 20) + 1, 9),   # stride 9, gcd 1: nine runs
     ((1 << 20) + 1, 16, 1, (1 << 20) + 1, 16),
     ((1 << 20) + 1, 32, 1, (1 << 20) + 1, 32), # the largest pass stride
-    ((1 << 20) + 1, 37, 1, (1 << 20) + 1, 1),  # stride 37 > 32: per output
-    ((1 << 20), 40, 8, 1 << 17, 1),  # stride 40 > 32, gcd 8: walk over one segment
+    ((1 << 20) + 1, 37, 1, (1 << 20) + 1, 37),  # stride 37 > 32: tiles, 37 runs
+    ((1 << 20), 40, 8, 1 << 17, 5),  # stride 40 > 32, gcd 8: tiles, 8 segments of 5 runs
+    ((1 << 20), 64, 1, 1 << 20, 1),  # gcd 64 >= 32: the walk over all n
     (16, 16, 1, 16, 1),              # stride == n: s = 0, gcd(0, n) = n > 8: walk
     (8, 8, 1, 8, 1),                 # s = 0, gcd 8 but n/8 = 1 is not a multiple of 4
 ])
 def test_gather_plan_segments(n, stride, reps, segment, passes):
     p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, stride, CUS)
     assert (p.reps, p.segment, p.passes) == (reps, segment, passes)
-    if ew.PATHS[p.path] != "gather_passes":
+    if ew.PATHS[p.path] == "gather_tiles":
+        # one block of 1024 threads per tile; vectors: output groups of four
+        assert p.head == 0 and p.tail == 0 and p.vectors == -(-segment // 4)
+        assert (p.block, p.unroll) == (1024, 1)
+        assert p.grid == min(p.tiles, p.blocks_per_cu * CUS)
+    elif ew.PATHS[p.path] != "gather_passes":
         assert p.head + p.vectors * 4 + p.tail == segment
         assert p.head == 0 and p.tail == segment % 4
     else:
@@ -253,9 +259,10 @@ def test_every_plan_names_its_kernel_path():
     assert g(out, base, (1 << 20) + 1, 16, 256).path == P["gather_passes"]
     assert g(out, base, 1 << 20, 9, 256).path == P["gather_passes"]
     assert g(out, base, 1 << 20, 31, 256).path == P["gather_passes"]
-    assert g(out, base, 1 << 20, 33, 256).path == P["gather_walk"]
+    assert g(out, base, 1 << 20, 33, 256).path == P["gather_tiles"]
     assert g(out, base, 1 << 20, 18, 256).path == P["gather_passes"]   # gcd 2: two segments
-    assert g(out, base, 1 << 20, 40, 256).path == P["gather_walk"]     # > 32: walk, 8 segments
+    assert g(out, base, 1 << 20, 40, 256).path == P["gather_tiles"]    # > 32: tiles, 8 segments
+    assert g(out, base, 1 << 20, 64, 256).path == P["gather_walk"]     # gcd 64: the walk
     c = ew.ew_make_copy2d_plan
     p = c(base, 0, 2, out, 1, 1 << 20, 256)
     assert p.path == P["gather_spans"] and p.head + 4 * p.vectors + p.tail == 1 << 20
