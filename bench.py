@@ -196,8 +196,8 @@ def kernel_instance(w, launch: dict, split: dict, plan=None, ew=None, prep=None)
             return f"ew_gather_passes_kernel<{w.view[1]}, {w.view[1]}>"
         return f"ew_gather_passes_kernel<{plan.passes * plan.reps}, {plan.reps}>"
     if path == "gather_tiles":
-        # narrow tiles (whole rows) below a stride of 128
-        return f"ew_gather_tiles_kernel<{_b(w.stride % w.n < 128)}>"
+        # narrow tiles (whole rows) below a stride of 136
+        return f"ew_gather_tiles_kernel<{_b(w.stride % w.n < 136)}>"
     if path == "gather_spans":
         # the input's body start co-aligned: in + 8 * head (two inputs per output)
         src = prep.view_src if w.op == "copy2d_f32" else prep.ptrs[1].data_ptr()
@@ -848,7 +848,8 @@ def run_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):
 
 # The stride curve: the gather and the per-output walk at n = 2^26 (the fifth
 # configuration's size and input) for every stride 1..32 and a few beyond.
-STRIDE_SWEEP = list(range(1, 33)) + [33, 64, 1000, (1 << 26) - 1]
+STRIDE_SWEEP = list(range(1, 33)) + [33, 48, 63, 64, 100, 127, 129, 255, 257, 1000, 4097, 65537,
+                                      (1 << 19) + 1, (1 << 26) - 1]
 
 
 def run_stride_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):

@@ -594,7 +594,7 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
             g->reps = gcd;
             g->sp = sp;
             g->inv = modinv_host(np % sp, sp);
-            const bool narrow = s < 128;
+            const bool narrow = s < kGatherNarrowStrides;
             g->tile_mode = narrow ? 1 : 2;
             g->tile_rows = narrow ? (uint32_t)(kGatherTileWords / s) & ~3u : 128u;
             g->tiles_m = (rows + g->tile_rows - 1) / g->tile_rows;

@@ -325,9 +325,11 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 // along A's rows, LDS rows of 132 words, each lane then reading four
 // consecutive rows of one column and storing them as one 16-byte vector of
 // that column's run (and again `reps` times one segment further on).
-// Narrow (s < 128): a tile is tile_rows whole rows, one contiguous chunk of
+// Narrow (s < 136): a tile is tile_rows whole rows, one contiguous chunk of
 // at most kGatherTileWords input elements, kept in LDS with pitch s; wide:
-// 128 rows by 128 columns.  Consecutive blocks take consecutive row bands
+// 128 rows by 128 columns (whole rows ran 9 % faster at s = 129, whose
+// second band would hold one column, equal at 137 and 10-20 % slower from
+// 171 on).  Consecutive blocks take consecutive row bands
 // of one column band, so each block continues the runs the previous one
 // wrote.  A column's destination needs two 64-bit divisions: the first
 // cols threads compute them once per tile into LDS.
@@ -338,6 +340,9 @@ constexpr int kTileThreads = 1024;
 constexpr int kTileSteps = 4;                         // 16-byte loads / stores per thread
 constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
 static_assert(kTileLdsWords >= (int)kGatherTileWords, "a narrow tile fits the LDS tile");
+static_assert(kGatherNarrowStrides >= (uint64_t)kTileT && kGatherNarrowStrides <= kTileThreads &&
+                  kGatherTileWords / (kGatherNarrowStrides - 1) >= 4,
+              "run starts: one per column of a tile, one thread each; narrow tiles hold >= 4 rows");
 static_assert(kTileSteps * kTileThreads * 4 == (int)kGatherTileWords &&
                   kTileSteps * 32 == kTileT,
               "four steps cover a narrow tile's words and a wide tile's rows");
@@ -346,7 +351,7 @@ template <bool Narrow>
 __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArgs g)
 {
     __shared__ uint32_t tile[kTileLdsWords];
-    __shared__ uint64_t run_start[kTileT];
+    __shared__ uint64_t run_start[kGatherNarrowStrides];
     const uint32_t tid = threadIdx.x;
     const uint64_t s = g.stride, n = g.n, seg = g.seg;
     const uint32_t rows = Narrow ? g.tile_rows : (uint32_t)kTileT;   // a multiple of 4
@@ -356,36 +361,46 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         const uint64_t m0 = (t % g.tiles_m) * rows;
         const uint64_t c0 = Narrow ? 0 : (t / g.tiles_m) * kTileT;
-        if (tid < cols) {
-            const uint64_t c = c0 + tid;
-            uint64_t d = kNoRun;
-            if (c < s && c % g.reps == 0) {
-                const uint64_t r = c / g.reps;
-                const uint64_t k = (g.sp - r) % g.sp * g.inv % g.sp;   // < sp^2 < 2^64
-                d = (k * seg + g.sp - 1) / g.sp;                       // < sp * seg < 2^64
+        // the run start of each column of the tile (two 64-bit divisions),
+        // computed while the tile's loads are in flight
+        auto run_starts = [&]() {
+            if (tid < cols) {
+                const uint64_t c = c0 + tid;
+                uint64_t d = kNoRun;
+                if (c < s && c % g.reps == 0) {
+                    const uint64_t r = c / g.reps;
+                    const uint64_t k = (g.sp - r) % g.sp * g.inv % g.sp;   // < sp^2 < 2^64
+                    d = (k * seg + g.sp - 1) / g.sp;                       // < sp * seg < 2^64
+                }
+                run_start[tid] = d;
             }
-            run_start[tid] = d;
-        }
+        };
+        // The full-tile test is the same in every lane, so the fast path's
+        // loads are unconditional (a lane past the tile's last quad reloads
+        // an in-range one and drops it) and all of them are in flight at once.
+        // every row of the tile's columns exists (the same in every lane)
+        const bool full = Narrow ? s * m0 + (uint64_t)rows * cols <= n
+                                 : c0 + kTileT <= s && s * (m0 + kTileT - 1) + c0 + kTileT <= n;
         if constexpr (Narrow) {
             // rows m0 .. m0 + rows - 1 are the contiguous input from s * m0
             const uint64_t base = s * m0;
             const uint32_t quads = rows * cols / 4;   // <= kGatherTileWords / 4
-            const bool full = base + 4 * (uint64_t)quads <= n;
             u32x4 v[kTileSteps];
+            if (full) {
 #pragma unroll
-            for (int p = 0; p < kTileSteps; ++p) {
-                const uint32_t q = tid + p * kTileThreads;
-                if (q < quads) {
-                    if (full) {
-                        v[p] = load16<false, 4>(
-                            reinterpret_cast<const char *>(g.in + base + 4 * q));
-                    } else {
+                for (int p = 0; p < kTileSteps; ++p) {
+                    const uint32_t q = min(tid + p * kTileThreads, quads - 1);
+                    v[p] = load16<false, 4>(reinterpret_cast<const char *>(g.in + base + 4 * q));
+                }
+            } else {
 #pragma unroll
-                        for (int k = 0; k < 4; ++k)
-                            v[p][k] = base + 4 * q + k < n ? g.in[base + 4 * q + k] : 0u;
-                    }
+                for (int p = 0; p < kTileSteps; ++p) {
+                    const uint64_t e = base + 4 * (uint64_t)(tid + p * kTileThreads);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) v[p][k] = e + k < n ? g.in[e + k] : 0u;
                 }
             }
+            run_starts();
 #pragma unroll
             for (int p = 0; p < kTileSteps; ++p) {
                 const uint32_t q = tid + p * kTileThreads;
@@ -394,20 +409,23 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
         } else {
             // 32 lanes cover 128 columns of one row, 32 rows per step
             const uint32_t sub = tid / 32, q4 = (tid % 32) * 4;
-            const bool full = c0 + kTileT <= s && s * (m0 + kTileT - 1) + c0 + kTileT <= n;
             u32x4 v[kTileSteps];
+            if (full) {
 #pragma unroll
-            for (int p = 0; p < kTileSteps; ++p) {
-                const uint32_t m = p * 32 + sub;
-                const uint64_t e = s * (m0 + m) + c0 + q4;
-                if (full) {
+                for (int p = 0; p < kTileSteps; ++p) {
+                    const uint64_t e = s * (m0 + p * 32 + sub) + c0 + q4;
                     v[p] = load16<false, 4>(reinterpret_cast<const char *>(g.in + e));
-                } else {
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < kTileSteps; ++p) {
+                    const uint64_t e = s * (m0 + p * 32 + sub) + c0 + q4;
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         v[p][k] = c0 + q4 + k < s && e + k < n ? g.in[e + k] : 0u;
                 }
             }
+            run_starts();
 #pragma unroll
             for (int p = 0; p < kTileSteps; ++p)
                 *reinterpret_cast<u32x4 *>(&tile[(p * 32 + sub) * kTilePitch + q4]) = v[p];
@@ -415,7 +433,34 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
         __syncthreads();
         // item q: column c, rows 4j .. 4j + 3 of the tile
         const uint32_t items = cols * groups;        // <= kTileSteps * kTileThreads
+        if (full) {
+            // Every row of every column exists: each item whose column is a
+            // run stores whole vectors.  The LDS reads of all steps first,
+            // then the stores, with no per-element checks (a lane past the
+            // last item reads a valid one and stores nothing).
+            u32x4 w[kTileSteps];
+            uint64_t o[kTileSteps];
 #pragma unroll
+            for (int p = 0; p < kTileSteps; ++p) {
+                const uint32_t q = min(tid + p * kTileThreads, items - 1);
+                const uint32_t c = q / groups, j = q % groups;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[p][k] = tile[(4 * j + k) * pitch + c];
+                const uint64_t d = run_start[c];
+                o[p] = d == kNoRun || tid + p * kTileThreads >= items ? kNoRun : d + m0 + 4 * j;
+            }
+#pragma unroll
+            for (int p = 0; p < kTileSteps; ++p) {
+                if (o[p] != kNoRun) {
+                    for (uint64_t k = 0; k < g.reps; ++k) {
+                        u32x4_a4 *dv = reinterpret_cast<u32x4_a4 *>(g.out + k * seg + o[p]);
+                        if constexpr (EW_STORE_NT) __builtin_nontemporal_store(w[p], dv);
+                        else *dv = w[p];
+                    }
+                }
+            }
+        } else
+#pragma unroll 1
         for (int p = 0; p < kTileSteps; ++p) {
             const uint32_t q = tid + p * kTileThreads;
             if (q >= items) break;

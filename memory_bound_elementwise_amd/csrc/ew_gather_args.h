@@ -71,5 +71,8 @@ int gather_passes_threads();
 // narrow tile may fill (tile_rows * stride <= this).
 int gather_tiles_threads();
 constexpr uint32_t kGatherTileWords = 16384;
+// Strides below this take tiles of whole rows: up to 135, so that a stride
+// just above 128 does not leave a 128-column band with a few columns.
+constexpr uint64_t kGatherNarrowStrides = 136;
 
 }  // namespace ew

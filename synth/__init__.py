@@ -118,6 +118,10 @@ WORKLOADS = {
         "gather_f32_2e26_s6", "gather_f32", 1 << 26, 107, "uniform", stride=6,
         description="fp32 strided gather out[i]=in[(6*i) mod n], n=2^26 (gcd 2: two equal "
                     "halves of three runs each, read with stride 6)"),
+    "gather_f32_2e26_s1000": _w(
+        "gather_f32_2e26_s1000", "gather_f32", 1 << 26, 107, "uniform", stride=1000,
+        description="fp32 strided gather out[i]=in[(1000*i) mod n], n=2^26 (gcd 8: eight equal "
+                    "segments of 125 runs, read with stride 1000)"),
     "fused_add_relu_f32_2e28": _w(
         "fused_add_relu_f32_2e28", "add_relu_f32", 1 << 28, 108, "normal",
         description="fp32 C=max(A+B,0) in one pass, n=2^28, A,B normal(0,1)"),

@@ -3,7 +3,9 @@ on the CPU before any launch.
 
 `_model` follows ew_gather_tiles_kernel step by step -- the tile grid, the
 per-column run starts, every thread's loads, LDS writes, LDS reads and
-stores, with the kernel's full-tile and per-element conditions -- using the
+stores, with the kernel's full-tile and per-element conditions (a full tile
+stores every item as whole vectors unchecked, which the model asserts is
+safe) -- using the
 plan the library reports (path, segment, reps, runs, tiles) and the field
 formulas that include/ew.h states for this path.  It asserts that every
 global load and store and every LDS access stays inside its buffer, that
@@ -31,7 +33,7 @@ def _fields(n, s):
     g = math.gcd(s, n)
     sp, seg = s // g, n // g
     rows = (n - 1) // s + 1
-    narrow = s < 128
+    narrow = s < 136
     tile_rows = (TILE_WORDS // s) & ~3 if narrow else 128
     tiles_m = -(-rows // tile_rows)
     tiles = tiles_m * (1 if narrow else -(-s // 128))
@@ -54,7 +56,7 @@ def _model(n, s, x):
     for t in range(f["tiles"]):
         m0 = (t % f["tiles_m"]) * rows
         c0 = 0 if narrow else (t // f["tiles_m"]) * 128
-        run_start = np.full(128, NO_RUN, dtype=object)
+        run_start = np.full(136, NO_RUN, dtype=object)
         for c_t in range(cols):
             c = c0 + c_t
             if c < s and c % g == 0:
@@ -110,6 +112,8 @@ def _model(n, s, x):
             e = s * m + c0 + c
             o = d + m
             every = e + 3 * s < n and o + 3 < seg
+            # a full tile stores whole vectors with no per-element checks
+            assert every or not full, (n, s, t, q)
             for rep in range(g):
                 for k in range(4):
                     if every or (e + k * s < n and o + k < seg):
@@ -127,6 +131,7 @@ def _model(n, s, x):
     (70000, 44), (99999, 63), (40000, 62),
     (33000, 129), (70001, 200), (262144, 1000), (300000, 257), (200001, 1280),
     (16511, 129),               # 128 rows, the last one short by one
+    (100001, 135), (100001, 136),   # the last whole-row stride, the first wide one
     (1 << 18, 2047),            # 128 rows, wide, gcd 1
 ])
 def test_tile_model_matches_the_definition(n, s):

@@ -312,16 +312,16 @@ def test_gather_pass_decomposition_small_strides():
 
 
 def _tile_cases():
-    """(n, stride) pairs on the tiled transposition: narrow tiles (33..127),
-    wide ones (128 x 128, partial column bands), g = gcd 1..31, exactly 128
-    rows, ragged last rows and bands."""
+    """(n, stride) pairs on the tiled transposition: whole-row tiles
+    (33..135), 128 x 128 ones (partial column bands), g = gcd 1..31, exactly
+    128 rows, ragged last rows and bands."""
     cus = 256
     pairs = []
     for n in (4225, 20011, 100003, 1 << 20, (1 << 20) + 5, 3 << 18, 720720 + 1):
         for s in (33, 34, 37, 40, 48, 63, 65, 97, 100, 126, 127):
             pairs.append((n, s))
     for n in ((1 << 20), (1 << 20) + 1, 1000003, 3 * 5 * 7 * 4096 + 1, 4 << 20):
-        for s in (129, 130, 200, 255, 259, 1000, 1281, 4097, 8191):
+        for s in (129, 130, 135, 136, 200, 255, 259, 1000, 1281, 4097, 8191):
             pairs.append((n, s))
     pairs += [(16511, 129), (33 * 127 + 1, 33), (128 * 1000 + 3, 1000), (31 * 4099, 62),
               (1 << 20, 80), ((1 << 20) + 48, 176)]
@@ -342,7 +342,7 @@ def test_gather_tiled_transposition_large_strides():
     pairs = _tile_cases()
     assert len(pairs) > 80
     assert {math.gcd(n, s) for n, s in pairs} >= {1, 2, 4, 8, 16, 31}
-    assert any(s < 128 for _, s in pairs) and any(s >= 128 for _, s in pairs)
+    assert any(s < 136 for _, s in pairs) and any(s >= 136 for _, s in pairs)
     cases = []
     for k, (n, s) in enumerate(pairs):
         oo, oi = ((0, 0), (1, 0), (0, 3), (3, 2))[k % 4]
