@@ -152,7 +152,7 @@ ew_status_t ew_gather_f32(const float *in, float *out, size_t n, size_t stride,
  * section 3.2 computes it: every output element loads its own input element
  * (4-byte loads, index stepped per lane), whatever the stride, with none of
  * ew_gather_f32's reuse (no replicated segments, no pass decomposition, no
- * contiguous-span path).  For stride 2 on even n it reads the input twice
+ * tiled transposition, no contiguous-span path).  For stride 2 on even n it reads the input twice
  * (outputs i and i + n/2 read the same element).  It is the baseline against
  * which the cost of strided reads is measured ([PerfNotes] 3.3).  Arguments,
  * errors and launch rows ("gather_walk_f32") as for ew_gather_f32; stride 1
@@ -426,7 +426,7 @@ ew_status_t ew_set_launch_config(const char *op, int block, int blocks_per_cu, i
  * current device, for pointers 16-byte aligned (as device allocations are):
  * threads per block, grid (0 when n == 0: no launch) and unroll.  For the
  * gather this is the index walk's grid (ew_gather_walk_f32, or
- * ew_gather_f32 at a stride mod n above 32); ew_make_gather_plan gives
+ * ew_gather_f32 at a stride that takes the walk); ew_make_gather_plan gives
  * the grid for a given stride.  Needs a device: EW_ERR_NO_DEVICE without
  * one. */
 ew_status_t ew_get_launch_config(const char *op, size_t n, int *block, int *grid, int *unroll);
