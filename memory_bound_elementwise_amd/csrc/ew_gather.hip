@@ -322,45 +322,66 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 // run, and a tile of A through LDS reads every input line once, where the
 // per-output walk fetches a whole 128-byte line for each 4-byte element once
 // s >= 32.  Tiles as in the view transpose: 1024 threads, 16-byte loads
-// along A's rows, LDS rows of 132 words, each lane then reading four
+// along A's rows, LDS rows padded by 4 words, each lane then reading four
 // consecutive rows of one column and storing them as one 16-byte vector of
 // that column's run (and again `reps` times one segment further on).
-// Narrow (s < 136): a tile is tile_rows whole rows, one contiguous chunk of
-// at most kGatherTileWords input elements, kept in LDS with pitch s; wide:
-// 128 rows by 128 columns (whole rows ran 9 % faster at s = 129, whose
-// second band would hold one column, equal at 137 and 10-20 % slower from
-// 171 on).  Consecutive blocks take consecutive row bands
-// of one column band, so each block continues the runs the previous one
-// wrote.  A column's destination needs two 64-bit divisions: the first
-// cols threads compute them once per tile into LDS.
-constexpr int kTileT = 128;                           // wide tile: rows = columns
-constexpr int kTilePitch = kTileT + 4;                // words per LDS row (wide)
-constexpr int kTileLdsWords = kTileT * kTilePitch;    // 16,896 >= kGatherTileWords
+// Three tile shapes (the template's Mode), all of 16,384 elements:
+//   1  s < 136: tile_rows whole rows, one contiguous chunk of the input,
+//      kept in LDS with pitch s (whole rows ran 9 % faster than two column
+//      bands at s = 129, whose second band would hold one column, equal at
+//      137 and 10-20 % slower from 171 on);
+//   2  128 rows by 128 columns, when A has fewer than 1024 rows;
+//   3  256 rows by 64 columns otherwise: each run gets 1 KiB per tile
+//      instead of 512 bytes, 8-25 % faster from s = 137 to 4097 and equal at
+//      65537 (1024 rows); at 128 rows half of each tile would be empty (24 %
+//      slower at s = 2^19 + 1).
+// Consecutive blocks take consecutive row bands of one column band, so each
+// block continues the runs the previous one wrote.  A column's destination
+// needs two 64-bit divisions: the first cols threads compute them once per
+// tile into LDS.
+template <int Mode> struct TileShape {                // modes 2 and 3
+    static constexpr int kRows = Mode == 2 ? 128 : 256;
+    static constexpr int kCols = Mode == 2 ? 128 : 64;
+    static constexpr int kPitch = kCols + 4;          // words per LDS row
+    static constexpr int kLanesPerRow = kCols / 4;
+};
 constexpr int kTileThreads = 1024;
 constexpr int kTileSteps = 4;                         // 16-byte loads / stores per thread
+constexpr int kTileLdsWords = 256 * (64 + 4);         // the largest shape: 17,408 words
 constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
-static_assert(kTileLdsWords >= (int)kGatherTileWords, "a narrow tile fits the LDS tile");
-static_assert(kGatherNarrowStrides >= (uint64_t)kTileT && kGatherNarrowStrides <= kTileThreads &&
+static_assert(kTileLdsWords >= (int)kGatherTileWords &&
+                  kTileLdsWords >= TileShape<2>::kRows * TileShape<2>::kPitch &&
+                  kTileLdsWords >= TileShape<3>::kRows * TileShape<3>::kPitch,
+              "every tile shape fits the LDS tile");
+static_assert(kGatherNarrowStrides >= 128 && kGatherNarrowStrides <= kTileThreads &&
                   kGatherTileWords / (kGatherNarrowStrides - 1) >= 4,
               "run starts: one per column of a tile, one thread each; narrow tiles hold >= 4 rows");
 static_assert(kTileSteps * kTileThreads * 4 == (int)kGatherTileWords &&
-                  kTileSteps * 32 == kTileT,
+                  kTileSteps * kTileThreads / TileShape<2>::kLanesPerRow == TileShape<2>::kRows &&
+                  kTileSteps * kTileThreads / TileShape<3>::kLanesPerRow == TileShape<3>::kRows,
               "four steps cover a narrow tile's words and a wide tile's rows");
+static_assert(kGatherWideRows[0] == TileShape<2>::kRows &&
+                  kGatherWideCols[0] == TileShape<2>::kCols &&
+                  kGatherWideRows[1] == TileShape<3>::kRows &&
+                  kGatherWideCols[1] == TileShape<3>::kCols,
+              "the host plans the tiles the kernel moves");
 
-template <bool Narrow>
+template <int Mode>
 __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArgs g)
 {
+    constexpr bool Narrow = Mode == 1;
+    using W = TileShape<Narrow ? 2 : Mode>;
     __shared__ uint32_t tile[kTileLdsWords];
     __shared__ uint64_t run_start[kGatherNarrowStrides];
     const uint32_t tid = threadIdx.x;
     const uint64_t s = g.stride, n = g.n, seg = g.seg;
-    const uint32_t rows = Narrow ? g.tile_rows : (uint32_t)kTileT;   // a multiple of 4
-    const uint32_t cols = Narrow ? (uint32_t)s : (uint32_t)kTileT;
-    const uint32_t pitch = Narrow ? (uint32_t)s : (uint32_t)kTilePitch;
+    const uint32_t rows = Narrow ? g.tile_rows : (uint32_t)W::kRows;   // a multiple of 4
+    const uint32_t cols = Narrow ? (uint32_t)s : (uint32_t)W::kCols;
+    const uint32_t pitch = Narrow ? (uint32_t)s : (uint32_t)W::kPitch;
     const uint32_t groups = rows / 4;         // four-row groups per column
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         const uint64_t m0 = (t % g.tiles_m) * rows;
-        const uint64_t c0 = Narrow ? 0 : (t / g.tiles_m) * kTileT;
+        const uint64_t c0 = Narrow ? 0 : (t / g.tiles_m) * W::kCols;
         // the run start of each column of the tile (two 64-bit divisions),
         // computed while the tile's loads are in flight
         auto run_starts = [&]() {
@@ -375,12 +396,13 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
                 run_start[tid] = d;
             }
         };
-        // The full-tile test is the same in every lane, so the fast path's
-        // loads are unconditional (a lane past the tile's last quad reloads
-        // an in-range one and drops it) and all of them are in flight at once.
-        // every row of the tile's columns exists (the same in every lane)
+        // Every row of the tile's columns exists (the same in every lane):
+        // the fast path's loads are then unconditional (a lane past the
+        // tile's last quad reloads an in-range one and drops it), all of
+        // them in flight at once.
         const bool full = Narrow ? s * m0 + (uint64_t)rows * cols <= n
-                                 : c0 + kTileT <= s && s * (m0 + kTileT - 1) + c0 + kTileT <= n;
+                                 : c0 + W::kCols <= s &&
+                                       s * (m0 + W::kRows - 1) + c0 + W::kCols <= n;
         if constexpr (Narrow) {
             // rows m0 .. m0 + rows - 1 are the contiguous input from s * m0
             const uint64_t base = s * m0;
@@ -407,19 +429,21 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
                 if (q < quads) *reinterpret_cast<u32x4 *>(&tile[4 * q]) = v[p];
             }
         } else {
-            // 32 lanes cover 128 columns of one row, 32 rows per step
-            const uint32_t sub = tid / 32, q4 = (tid % 32) * 4;
+            // kLanesPerRow lanes cover a row's kCols columns, kRowsPerStep
+            // rows per step
+            constexpr uint32_t kRowsPerStep = kTileThreads / W::kLanesPerRow;
+            const uint32_t sub = tid / W::kLanesPerRow, q4 = (tid % W::kLanesPerRow) * 4;
             u32x4 v[kTileSteps];
             if (full) {
 #pragma unroll
                 for (int p = 0; p < kTileSteps; ++p) {
-                    const uint64_t e = s * (m0 + p * 32 + sub) + c0 + q4;
+                    const uint64_t e = s * (m0 + p * kRowsPerStep + sub) + c0 + q4;
                     v[p] = load16<false, 4>(reinterpret_cast<const char *>(g.in + e));
                 }
             } else {
 #pragma unroll
                 for (int p = 0; p < kTileSteps; ++p) {
-                    const uint64_t e = s * (m0 + p * 32 + sub) + c0 + q4;
+                    const uint64_t e = s * (m0 + p * kRowsPerStep + sub) + c0 + q4;
 #pragma unroll
                     for (int k = 0; k < 4; ++k)
                         v[p][k] = c0 + q4 + k < s && e + k < n ? g.in[e + k] : 0u;
@@ -428,7 +452,8 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
             run_starts();
 #pragma unroll
             for (int p = 0; p < kTileSteps; ++p)
-                *reinterpret_cast<u32x4 *>(&tile[(p * 32 + sub) * kTilePitch + q4]) = v[p];
+                *reinterpret_cast<u32x4 *>(&tile[(p * kRowsPerStep + sub) * W::kPitch + q4]) =
+                    v[p];
         }
         __syncthreads();
         // item q: column c, rows 4j .. 4j + 3 of the tile
@@ -558,8 +583,12 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
         return hipLaunchKernel(fn, dim3(l.grid), dim3(kPassThreads), kargs, extra, s);
     }
     if (args.tile_mode != 0) {
-        fn = args.tile_mode == 1 ? reinterpret_cast<const void *>(&ew_gather_tiles_kernel<true>)
-                                 : reinterpret_cast<const void *>(&ew_gather_tiles_kernel<false>);
+        switch (args.tile_mode) {
+        case 1: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<1>); break;
+        case 2: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<2>); break;
+        case 3: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<3>); break;
+        default: return hipErrorInvalidValue;
+        }
         return hipLaunchKernel(fn, dim3(l.grid), dim3(kTileThreads), kargs, 0, s);
     }
     if (args.stride == 2 && (args.reps == 2 || (args.reps == 1 && args.n == 2 * args.seg))) {

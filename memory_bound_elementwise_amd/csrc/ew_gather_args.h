@@ -51,8 +51,9 @@ struct GatherArgs {
     // rows m written to out[k * seg + dest(c) + m] for k < reps, where pass
     // k' = (-r * inv) mod sp starts at dest(c) = ceil(k' * seg / sp),
     // sp = stride / g and inv = (seg mod sp)^-1 mod sp.  tile_mode 1: one
-    // tile is tile_rows whole rows (stride < 128); 2: 128 x 128 tiles,
-    // tiles_m row bands by ceil(stride / 128) column bands.
+    // tile is tile_rows whole rows (stride < kGatherNarrowStrides); 2 and 3:
+    // tiles of kGatherWideRows[mode - 2] rows by kGatherWideCols[mode - 2]
+    // columns, tiles_m row bands by ceil(stride / columns) column bands.
     int tile_mode;
     uint32_t tile_rows;
     uint64_t sp;
@@ -74,5 +75,10 @@ constexpr uint32_t kGatherTileWords = 16384;
 // Strides below this take tiles of whole rows: up to 135, so that a stride
 // just above 128 does not leave a 128-column band with a few columns.
 constexpr uint64_t kGatherNarrowStrides = 136;
+// Wider strides: tiles of 128 x 128 (tile_mode 2) while A has fewer than
+// kGatherTallRows rows, else 256 rows x 64 columns (tile_mode 3).
+constexpr uint32_t kGatherWideRows[2] = {128, 256};
+constexpr uint32_t kGatherWideCols[2] = {128, 64};
+constexpr uint64_t kGatherTallRows = 1024;
 
 }  // namespace ew

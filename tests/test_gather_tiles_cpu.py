@@ -23,7 +23,7 @@ BASE = 0x7F0000000000
 CUS = 256
 THREADS = 1024
 STEPS = 4
-LDS_WORDS = 128 * 132
+LDS_WORDS = 256 * 68
 TILE_WORDS = 16384
 NO_RUN = -1
 
@@ -34,28 +34,32 @@ def _fields(n, s):
     sp, seg = s // g, n // g
     rows = (n - 1) // s + 1
     narrow = s < 136
-    tile_rows = (TILE_WORDS // s) & ~3 if narrow else 128
+    mode = 1 if narrow else 2 if rows < 1024 else 3
+    tile_rows = (TILE_WORDS // s) & ~3 if narrow else {2: 128, 3: 256}[mode]
+    cols = s if narrow else {2: 128, 3: 64}[mode]
     tiles_m = -(-rows // tile_rows)
-    tiles = tiles_m * (1 if narrow else -(-s // 128))
-    return dict(g=g, sp=sp, seg=seg, inv=pow(seg % sp, -1, sp), narrow=narrow,
-                tile_rows=tile_rows, tiles_m=tiles_m, tiles=tiles)
+    tiles = tiles_m * -(-s // cols)
+    return dict(g=g, sp=sp, seg=seg, inv=pow(seg % sp, -1, sp), narrow=narrow, mode=mode,
+                tile_rows=tile_rows, tile_cols=cols, tiles_m=tiles_m, tiles=tiles)
 
 
 def _model(n, s, x):
     """Run the kernel's index arithmetic over every block; return the output."""
     f = _fields(n, s)
     g, sp, seg, inv, narrow = f["g"], f["sp"], f["seg"], f["inv"], f["narrow"]
-    rows = f["tile_rows"]
-    cols = s if narrow else 128
-    pitch = s if narrow else 132
+    rows, cols = f["tile_rows"], f["tile_cols"]
+    pitch = s if narrow else cols + 4
+    lanes_per_row = cols // 4
+    rows_per_step = THREADS // lanes_per_row
     groups = rows // 4
-    assert rows % 4 == 0 and rows * cols <= (TILE_WORDS if narrow else 128 * 128)
+    assert rows % 4 == 0 and rows * cols <= TILE_WORDS
+    assert narrow or rows_per_step * STEPS == rows
     out = np.zeros(n, dtype=x.dtype)
     writes = np.zeros(n, dtype=np.int64)
     tid = np.arange(THREADS)
     for t in range(f["tiles"]):
         m0 = (t % f["tiles_m"]) * rows
-        c0 = 0 if narrow else (t // f["tiles_m"]) * 128
+        c0 = 0 if narrow else (t // f["tiles_m"]) * cols
         run_start = np.full(136, NO_RUN, dtype=object)
         for c_t in range(cols):
             c = c0 + c_t
@@ -82,10 +86,10 @@ def _model(n, s, x):
                 assert dst.max(initial=-1) < LDS_WORDS
                 lds[dst] = v
         else:
-            sub, q4 = tid // 32, (tid % 32) * 4
-            full = c0 + 128 <= s and s * (m0 + 127) + c0 + 128 <= n
+            sub, q4 = tid // lanes_per_row, (tid % lanes_per_row) * 4
+            full = c0 + cols <= s and s * (m0 + rows - 1) + c0 + cols <= n
             for p in range(STEPS):
-                m = p * 32 + sub
+                m = p * rows_per_step + sub
                 e = s * (m0 + m) + c0 + q4
                 idx = e[:, None] + np.arange(4)
                 if full:
@@ -94,7 +98,7 @@ def _model(n, s, x):
                 else:
                     ok = ((c0 + q4)[:, None] + np.arange(4) < s) & (idx < n)
                     v = np.where(ok, x[np.minimum(idx, n - 1)], 0)
-                dst = (m * 132 + q4)[:, None] + np.arange(4)
+                dst = (m * pitch + q4)[:, None] + np.arange(4)
                 assert dst.max() < LDS_WORDS
                 lds[dst] = v
         items = cols * groups
@@ -132,6 +136,7 @@ def _model(n, s, x):
     (33000, 129), (70001, 200), (262144, 1000), (300000, 257), (200001, 1280),
     (16511, 129),               # 128 rows, the last one short by one
     (100001, 135), (100001, 136),   # the last whole-row stride, the first wide one
+    (1023 * 300 - 5, 300), (1024 * 300, 301), (1024 * 300 + 7, 300),   # 1023 / 1024 rows
     (1 << 18, 2047),            # 128 rows, wide, gcd 1
 ])
 def test_tile_model_matches_the_definition(n, s):

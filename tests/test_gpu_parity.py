@@ -342,7 +342,10 @@ def test_gather_tiled_transposition_large_strides():
     pairs = _tile_cases()
     assert len(pairs) > 80
     assert {math.gcd(n, s) for n, s in pairs} >= {1, 2, 4, 8, 16, 31}
-    assert any(s < 136 for _, s in pairs) and any(s >= 136 for _, s in pairs)
+    # all three tile shapes: whole rows (s < 136), 128 x 128 (fewer than
+    # 1024 rows of s elements) and 256 x 64
+    modes = {1 if s < 136 else 2 if -(-n // s) < 1024 else 3 for n, s in pairs}
+    assert modes == {1, 2, 3}
     cases = []
     for k, (n, s) in enumerate(pairs):
         oo, oi = ((0, 0), (1, 0), (0, 3), (3, 2))[k % 4]
@@ -354,7 +357,8 @@ def test_gather_tiled_transposition_large_strides():
 def test_gather_tiled_transposition_launch_variants():
     """The tiled transposition with its grid capped below the tile count (the
     launch table's blocks per CU), so that blocks stride over several tiles
-    and reuse their LDS tile and run starts."""
+    and reuse their LDS tile and run starts: whole-row tiles (s = 33, 34),
+    256 x 64 (s = 200) and 128 x 128 (s = 16385, fewer than 1024 rows)."""
     print("[parity] gather tiles variants", flush=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     try:
@@ -362,7 +366,7 @@ def test_gather_tiled_transposition_launch_variants():
             _force_launch("gather_f32", 128, bpc, 1)
             cases = []
             for n, s in ((cus * bpc * 3 * 16384 + 11, 33), (cus * bpc * 3 * 16384 + 7, 200),
-                         (cus * bpc * 3 * 16384 + 4, 34)):
+                         (cus * bpc * 3 * 16384 + 4, 34), (cus * bpc * 3 * 16384 + 1, 16385)):
                 p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
                 assert ew.PATHS[p.path] == "gather_tiles" and p.tiles > 2 * p.grid, \
                     (n, s, p.tiles, p.grid)
