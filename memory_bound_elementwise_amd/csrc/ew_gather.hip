@@ -335,8 +335,17 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 //      instead of 512 bytes, 8-25 % faster from s = 137 to 4097 and equal at
 //      65537 (1024 rows); at 128 rows half of each tile would be empty (24 %
 //      slower at s = 2^19 + 1).
-// Consecutive blocks take consecutive row bands of one column band, so each
-// block continues the runs the previous one wrote.  A column's destination
+// Tiles go in groups of kTileBandGroup (16) row bands: within a group
+// consecutive blocks take consecutive row bands of one column band, so each
+// continues the runs the previous one wrote, and the group then moves to the
+// next column band.  The row pieces of neighbouring bands share the lines at
+// their edges (a band starts mid-line unless the stride is a multiple of
+// 32); with the groups those lines are fetched while the other band's reads
+// are recent, where walking every row band of one column band before the
+// next fetched them twice (stride 1000, 256 x 64 tiles: 1.38 x the input
+// read).  16 row bands per group ran 2-16 % faster than that order from
+// s = 137 to 1281 and 2 % slower at 4097; groups of 4, 32 and 64 lost to 16
+// almost everywhere.  A column's destination
 // needs two 64-bit divisions: the first cols threads compute them once per
 // tile into LDS.
 template <int Mode> struct TileShape {                // modes 2 and 3
@@ -349,6 +358,7 @@ constexpr int kTileThreads = 1024;
 constexpr int kTileSteps = 4;                         // 16-byte loads / stores per thread
 constexpr int kTileLdsWords = 256 * (64 + 4);         // the largest shape: 17,408 words
 constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
+constexpr uint64_t kTileBandGroup = 16;               // row bands per group of tiles
 static_assert(kTileLdsWords >= (int)kGatherTileWords &&
                   kTileLdsWords >= TileShape<2>::kRows * TileShape<2>::kPitch &&
                   kTileLdsWords >= TileShape<3>::kRows * TileShape<3>::kPitch,
@@ -380,8 +390,15 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
     const uint32_t pitch = Narrow ? (uint32_t)s : (uint32_t)W::kPitch;
     const uint32_t groups = rows / 4;         // four-row groups per column
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
-        const uint64_t m0 = (t % g.tiles_m) * rows;
-        const uint64_t c0 = Narrow ? 0 : (t / g.tiles_m) * W::kCols;
+        // tile t: groups of kTileBandGroup row bands, each group walking its
+        // column bands in turn, row band fastest within a group
+        const uint64_t bands = g.tiles / g.tiles_m;
+        const uint64_t grp = t / (kTileBandGroup * bands), in_grp = t % (kTileBandGroup * bands);
+        const uint64_t grp_rows = g.tiles_m - grp * kTileBandGroup < kTileBandGroup
+                                      ? g.tiles_m - grp * kTileBandGroup
+                                      : kTileBandGroup;
+        const uint64_t m0 = (grp * kTileBandGroup + in_grp % grp_rows) * rows;
+        const uint64_t c0 = Narrow ? 0 : (in_grp / grp_rows) * W::kCols;
         // the run start of each column of the tile (two 64-bit divisions),
         // computed while the tile's loads are in flight
         auto run_starts = [&]() {

@@ -43,6 +43,21 @@ def _fields(n, s):
                 tile_rows=tile_rows, tile_cols=cols, tiles_m=tiles_m, tiles=tiles)
 
 
+def _tile_of(t, tiles_m, bands, group=16):
+    """(row band, column band) of tile t: groups of `group` row bands, each
+    group walking its column bands in turn, row band fastest."""
+    grp, rest = divmod(t, group * bands)
+    rows_in_group = min(group, tiles_m - grp * group)
+    return grp * group + rest % rows_in_group, rest // rows_in_group
+
+
+def test_tile_order_covers_every_tile_once():
+    for tiles_m in range(1, 70):
+        for bands in range(1, 9):
+            got = {_tile_of(t, tiles_m, bands) for t in range(tiles_m * bands)}
+            assert got == {(m, c) for m in range(tiles_m) for c in range(bands)}, (tiles_m, bands)
+
+
 def _model(n, s, x):
     """Run the kernel's index arithmetic over every block; return the output."""
     f = _fields(n, s)
@@ -58,8 +73,9 @@ def _model(n, s, x):
     writes = np.zeros(n, dtype=np.int64)
     tid = np.arange(THREADS)
     for t in range(f["tiles"]):
-        m0 = (t % f["tiles_m"]) * rows
-        c0 = 0 if narrow else (t // f["tiles_m"]) * cols
+        mt, ct = _tile_of(t, f["tiles_m"], f["tiles"] // f["tiles_m"])
+        m0 = mt * rows
+        c0 = 0 if narrow else ct * cols
         run_start = np.full(136, NO_RUN, dtype=object)
         for c_t in range(cols):
             c = c0 + c_t
