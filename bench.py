@@ -196,10 +196,10 @@ def kernel_instance(w, launch: dict, split: dict, plan=None, ew=None, prep=None)
             return f"ew_gather_passes_kernel<{w.view[1]}, {w.view[1]}>"
         return f"ew_gather_passes_kernel<{plan.passes * plan.reps}, {plan.reps}>"
     if path == "gather_tiles":
-        # whole rows below a stride of 136; else 128 x 128 tiles below 1024
+        # whole rows below a stride of 68; else 128 x 128 tiles below 1024
         # rows of A, 256 x 64 ones from there on
         s = w.stride % w.n
-        mode = 1 if s < 136 else 2 if -(-w.n // s) < 1024 else 3
+        mode = 1 if s < 68 else 2 if -(-w.n // s) < 1024 else 3
         return f"ew_gather_tiles_kernel<{mode}>"
     if path == "gather_spans":
         # the input's body start co-aligned: in + 8 * head (two inputs per output)

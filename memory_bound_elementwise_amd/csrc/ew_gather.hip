@@ -326,15 +326,17 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 // consecutive rows of one column and storing them as one 16-byte vector of
 // that column's run (and again `reps` times one segment further on).
 // Three tile shapes (the template's Mode), all of 16,384 elements:
-//   1  s < 136: tile_rows whole rows, one contiguous chunk of the input,
-//      kept in LDS with pitch s (whole rows ran 9 % faster than two column
-//      bands at s = 129, whose second band would hold one column, equal at
-//      137 and 10-20 % slower from 171 on);
+//   1  s < 68: tile_rows = floor(16384 / s) whole rows (rounded down to a
+//      multiple of 4), one contiguous chunk of the input kept in LDS with
+//      pitch s;
 //   2  128 rows by 128 columns, when A has fewer than 1024 rows;
 //   3  256 rows by 64 columns otherwise: each run gets 1 KiB per tile
-//      instead of 512 bytes, 8-25 % faster from s = 137 to 4097 and equal at
-//      65537 (1024 rows); at 128 rows half of each tile would be empty (24 %
-//      slower at s = 2^19 + 1).
+//      instead of 512 bytes, 8-25 % faster than 128 x 128 from s = 137 to
+//      4097 and equal at 65537 (1024 rows); at 128 rows half of each tile
+//      would be empty (24 % slower at s = 2^19 + 1).  From s = 72 to 135 it
+//      also beat whole rows (which give each run 120-228 outputs per tile)
+//      by 6-30 %, 113 aside (3 % slower); at 65 and 66, where its second
+//      band would hold one or two columns, whole rows were 9-11 % faster.
 // Tiles go in groups of kTileBandGroup (16) row bands: within a group
 // consecutive blocks take consecutive row bands of one column band, so each
 // continues the runs the previous one wrote, and the group then moves to the
@@ -359,12 +361,14 @@ constexpr int kTileSteps = 4;                         // 16-byte loads / stores 
 constexpr int kTileLdsWords = 256 * (64 + 4);         // the largest shape: 17,408 words
 constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
 constexpr uint64_t kTileBandGroup = 16;               // row bands per group of tiles
+constexpr int kTileRunStarts = 128;                   // the most columns a tile holds
 static_assert(kTileLdsWords >= (int)kGatherTileWords &&
                   kTileLdsWords >= TileShape<2>::kRows * TileShape<2>::kPitch &&
                   kTileLdsWords >= TileShape<3>::kRows * TileShape<3>::kPitch,
               "every tile shape fits the LDS tile");
-static_assert(kGatherNarrowStrides >= 128 && kGatherNarrowStrides <= kTileThreads &&
-                  kGatherTileWords / (kGatherNarrowStrides - 1) >= 4,
+static_assert(kGatherNarrowStrides <= (uint64_t)kTileRunStarts &&
+                  TileShape<2>::kCols <= kTileRunStarts && TileShape<3>::kCols <= kTileRunStarts &&
+                  kTileRunStarts <= kTileThreads && kGatherTileWords / (kGatherNarrowStrides - 1) >= 4,
               "run starts: one per column of a tile, one thread each; narrow tiles hold >= 4 rows");
 static_assert(kTileSteps * kTileThreads * 4 == (int)kGatherTileWords &&
                   kTileSteps * kTileThreads / TileShape<2>::kLanesPerRow == TileShape<2>::kRows &&
@@ -382,7 +386,7 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
     constexpr bool Narrow = Mode == 1;
     using W = TileShape<Narrow ? 2 : Mode>;
     __shared__ uint32_t tile[kTileLdsWords];
-    __shared__ uint64_t run_start[kGatherNarrowStrides];
+    __shared__ uint64_t run_start[kTileRunStarts];
     const uint32_t tid = threadIdx.x;
     const uint64_t s = g.stride, n = g.n, seg = g.seg;
     const uint32_t rows = Narrow ? g.tile_rows : (uint32_t)W::kRows;   // a multiple of 4

@@ -72,9 +72,9 @@ int gather_passes_threads();
 // narrow tile may fill (tile_rows * stride <= this).
 int gather_tiles_threads();
 constexpr uint32_t kGatherTileWords = 16384;
-// Strides below this take tiles of whole rows: up to 135, so that a stride
-// just above 128 does not leave a 128-column band with a few columns.
-constexpr uint64_t kGatherNarrowStrides = 136;
+// Strides below this take tiles of whole rows (each run then gets at least
+// 244 outputs per tile).
+constexpr uint64_t kGatherNarrowStrides = 68;
 // Wider strides: tiles of 128 x 128 (tile_mode 2) while A has fewer than
 // kGatherTallRows rows, else 256 rows x 64 columns (tile_mode 3).
 constexpr uint32_t kGatherWideRows[2] = {128, 256};

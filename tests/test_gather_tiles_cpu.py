@@ -33,7 +33,7 @@ def _fields(n, s):
     g = math.gcd(s, n)
     sp, seg = s // g, n // g
     rows = (n - 1) // s + 1
-    narrow = s < 136
+    narrow = s < 68
     mode = 1 if narrow else 2 if rows < 1024 else 3
     tile_rows = (TILE_WORDS // s) & ~3 if narrow else {2: 128, 3: 256}[mode]
     cols = s if narrow else {2: 128, 3: 64}[mode]
@@ -76,7 +76,7 @@ def _model(n, s, x):
         mt, ct = _tile_of(t, f["tiles_m"], f["tiles"] // f["tiles_m"])
         m0 = mt * rows
         c0 = 0 if narrow else ct * cols
-        run_start = np.full(136, NO_RUN, dtype=object)
+        run_start = np.full(128, NO_RUN, dtype=object)
         for c_t in range(cols):
             c = c0 + c_t
             if c < s and c % g == 0:
@@ -151,7 +151,8 @@ def _model(n, s, x):
     (70000, 44), (99999, 63), (40000, 62),
     (33000, 129), (70001, 200), (262144, 1000), (300000, 257), (200001, 1280),
     (16511, 129),               # 128 rows, the last one short by one
-    (100001, 135), (100001, 136),   # the last whole-row stride, the first wide one
+    (100001, 67), (100001, 68),     # the last whole-row stride, the first wide one
+    (100001, 135), (100001, 136),
     (1023 * 300 - 5, 300), (1024 * 300, 301), (1024 * 300 + 7, 300),   # 1023 / 1024 rows
     (1 << 18, 2047),            # 128 rows, wide, gcd 1
 ])

@@ -65,7 +65,7 @@ def _pass_lds(stride, step):
 
 def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
     """Only the transpose (one 128 x 132 fp32 tile), the gather's tiled
-    transposition (its largest tile, 256 x 68 words, plus 136 run starts of
+    transposition (its largest tile, 256 x 68 words, plus 128 run starts of
     8 bytes) and the
     pass-decomposed gather stage data in LDS.  A pass block that writes several runs (256
     threads, 16 * stride bytes per lane) reserves just over 1/(k + 1) of the
@@ -76,7 +76,7 @@ def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
     assert len(ks) > 100
     for name, (_, meta) in ks.items():
         d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
-        lds = "67584" if "transpose" in name else "70720" if "gather_tiles" in name else (
+        lds = "67584" if "transpose" in name else "70656" if "gather_tiles" in name else (
             str(_pass_lds(*map(int, re.search(r"passes_kernelILi(\d+)ELi(\d+)E", name).groups())))
             if "gather_passes" in name else "0")
         assert d["group_segment_fixed_size"] == lds, name
