@@ -851,8 +851,8 @@ def run_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):
 
 # The stride curve: the gather and the per-output walk at n = 2^26 (the fifth
 # configuration's size and input) for every stride 1..32 and a few beyond.
-STRIDE_SWEEP = list(range(1, 33)) + [33, 48, 63, 64, 100, 127, 129, 255, 257, 1000, 4097, 65537,
-                                      (1 << 19) + 1, (1 << 26) - 1]
+STRIDE_SWEEP = list(range(1, 33)) + [33, 48, 63, 64, 100, 127, 128, 129, 255, 257, 1000, 1024,
+                                      4097, 65537, (1 << 19) + 1, (1 << 26) - 1]
 
 
 def run_stride_sweep(torch, np, ew, synth, stream, cus, flush_buf, out_path=None):

@@ -539,8 +539,9 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * blocks_per_cu per compute unit, vectors = ceil(segment / 4),
  * head = tail = 0.
  * Otherwise (s == 0, or a large stride outside those bounds) the per-output
- * index walk (EW_PATH_GATHER_WALK), on one segment when 2 <= g <= 8 and n/g
- * is a multiple of 4 (else segment = n and reps = 1); passes = 1.
+ * index walk (EW_PATH_GATHER_WALK), on one segment when n/g is a multiple of
+ * 4 and 2 <= g <= 8 or n/g >= 2^14 (else segment = n and reps = 1);
+ * passes = 1.
  * Same validation as ew_gather_f32. */
 ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
                                 size_t stride, int cu_count, ew_plan_t *plan);

@@ -529,9 +529,9 @@ uint64_t modinv_host(uint64_t a, uint64_t m)
 // once instead of g times.  Strides 2..32: the pass decomposition (see
 // GatherArgs).  Larger strides with at least 128 rows of `stride` elements,
 // g < 32, s' = s/g below 2^32 and s' * n/g below 2^64: the tiled
-// transposition.  Otherwise the per-output walk, over one segment when
-// 2 <= g <= 8 and n/g is a multiple of 4 (every copy then has the same
-// 16-byte alignment), else over all n.
+// transposition.  Otherwise the per-output walk, over one segment when n/g
+// is a multiple of 4 (every copy then has the same 16-byte alignment) and
+// 2 <= g <= 8 or n/g >= kGatherLongSegment, else over all n.
 //
 // walk: the per-output index walk whatever the stride (no pass decomposition
 // and no replicated segments: every output element loads its own input
@@ -612,8 +612,12 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
             return;
         }
     }
+    // one segment stored g times when every copy has the same 16-byte
+    // alignment, for g up to 8 or, beyond, segments long enough to spread
+    // over the GPU (each lane then stores its vector g times)
     uint64_t reps = 1, seg = n;
-    if (!walk && gcd >= 2 && gcd <= 8 && (n / gcd) % 4 == 0) {
+    if (!walk && gcd >= 2 && (n / gcd) % 4 == 0 &&
+        (gcd <= 8 || n / gcd >= kGatherLongSegment)) {
         reps = gcd;
         seg = n / gcd;
     }

@@ -80,5 +80,12 @@ constexpr uint64_t kGatherNarrowStrides = 68;
 constexpr uint32_t kGatherWideRows[2] = {128, 256};
 constexpr uint32_t kGatherWideCols[2] = {128, 64};
 constexpr uint64_t kGatherTallRows = 1024;
+// The walk replicates segments of at least this many elements for any
+// g = gcd(stride, n) (below it only for g <= 8): each of a segment's
+// vectors is then stored g times by one lane, so shorter segments leave too
+// few lanes (n = 2^26: s = 64 422 -> 5971 GB/s, 1024 2146 -> 12495 with
+// 2^14; segments of 2^10 elements ran 1.7-6.5 x slower than the unreplicated
+// walk, whose repeated reads of a short segment hit in the caches).
+constexpr uint64_t kGatherLongSegment = (uint64_t)1 << 14;
 
 }  // namespace ew

@@ -354,6 +354,23 @@ def test_gather_tiled_transposition_large_strides():
     assert not failures, failures[:10]
 
 
+def test_gather_walk_long_replicated_segments():
+    """Strides sharing a factor of 32 or more with n take the per-output walk
+    over one segment stored g times once the segment holds at least 2^14
+    elements (below that, the walk over all n)."""
+    print("[parity] gather replicated walk", flush=True)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cases = []
+    for n, s, reps in ((1 << 20, 64, 64), (1 << 21, 128, 128), (3 << 20, 96, 96),
+                       (5 << 20, 320, 320), (1 << 20, 16 * 1025, 16),
+                       (1 << 20, 128, 1), (1 << 20, 1 << 16, 1)):
+        p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
+        assert ew.PATHS[p.path] == "gather_walk" and p.reps == reps, (n, s, p.reps)
+        cases += [(n, 0, [0], s), (n, 1, [3], s)]
+    failures = _run_cases("gather_f32", cases, seed=355)
+    assert not failures, failures[:10]
+
+
 def test_gather_tiled_transposition_launch_variants():
     """The tiled transposition with its grid capped below the tile count (the
     launch table's blocks per CU), so that blocks stride over several tiles

@@ -146,7 +146,9 @@ def test_plan_rejects_what_the_operation_rejects():
     ((1 << 20) + 1, 32, 1, (1 << 20) + 1, 32), # the largest pass stride
     ((1 << 20) + 1, 37, 1, (1 << 20) + 1, 37),  # stride 37 > 32: tiles, 37 runs
     ((1 << 20), 40, 8, 1 << 17, 5),  # stride 40 > 32, gcd 8: tiles, 8 segments of 5 runs
-    ((1 << 20), 64, 1, 1 << 20, 1),  # gcd 64 >= 32: the walk over all n
+    ((1 << 20), 128, 1, 1 << 20, 1),  # gcd 128 >= 32, segment 2^13: the walk over all n
+    ((1 << 20), 64, 64, 1 << 14, 1),  # gcd 64, segment 2^14: the walk over one segment
+    ((1 << 26), 1024, 1024, 1 << 16, 1),
     (16, 16, 1, 16, 1),              # stride == n: s = 0, gcd(0, n) = n > 8: walk
     (8, 8, 1, 8, 1),                 # s = 0, gcd 8 but n/8 = 1 is not a multiple of 4
 ])
