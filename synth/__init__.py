@@ -122,6 +122,14 @@ WORKLOADS = {
         "gather_f32_2e26_s1000", "gather_f32", 1 << 26, 107, "uniform", stride=1000,
         description="fp32 strided gather out[i]=in[(1000*i) mod n], n=2^26 (gcd 8: eight equal "
                     "segments of 125 runs, read with stride 1000)"),
+    "gather_f32_2e26_s33": _w(
+        "gather_f32_2e26_s33", "gather_f32", 1 << 26, 107, "uniform", stride=33,
+        description="fp32 strided gather out[i]=in[(33*i) mod n], n=2^26 (gcd 1: 33 runs, read "
+                    "with stride 33)"),
+    "gather_walk_f32_2e26_s33": _w(
+        "gather_walk_f32_2e26_s33", "gather_walk_f32", 1 << 26, 107, "uniform", stride=33,
+        description="the same stride-33 gather, one 4-byte load per output (the per-output "
+                    "index walk)"),
     "fused_add_relu_f32_2e28": _w(
         "fused_add_relu_f32_2e28", "add_relu_f32", 1 << 28, 108, "normal",
         description="fp32 C=max(A+B,0) in one pass, n=2^28, A,B normal(0,1)"),
