@@ -548,7 +548,7 @@ ew_status_t ew_make_gather_plan(const void *out, const void *in, size_t n,
 
 /* The plan of ew_copy2d_f32 with these arguments: its path (x[::2] ->
  * EW_PATH_GATHER_SPANS, x[::s] with s = 3..32 -> EW_PATH_GATHER_PASSES with
- * passes = s, stride_c == 1 -> EW_PATH_VIEW_ROWS, stride_r == 1 ->
+ * passes = 1 (one run), stride_c == 1 -> EW_PATH_VIEW_ROWS, stride_r == 1 ->
  * EW_PATH_VIEW_TRANSPOSE, else EW_PATH_VIEW_GENERIC) and the launch it makes
  * (block, grid, unroll as launched; a kernel with a fixed block shape reports
  * that shape; tiles counts 128 x 128 tiles for the transpose).  No device is
