@@ -126,6 +126,16 @@ def test_kernel_instance_names_match_the_profiler_s_demangled_names():
     tr = ew.ew_make_copy2d_plan(base, 1, 16384, out, 16384, 16384, 256)
     assert (bench.kernel_instance(W["transpose_f32_16384x16384"], {"unroll": 1}, split, tr, ew,
                                   Prep(base)) == "ew_transpose_kernel")
+    # the tiled transposition: whole rows below stride 68, else 128 x 128 tiles below
+    # 1024 rows of the stride and 256 x 64 from there on
+    import dataclasses
+    for name, stride, mode in (("gather_f32_2e26_s33", 33, 1), ("gather_f32_2e26_s1000", 1000, 3),
+                               ("gather_f32_2e26_s33", 65537 * 3, 2)):
+        w = dataclasses.replace(W[name], stride=stride)
+        tiles = ew.ew_make_gather_plan(out, base, w.n, stride, 256)
+        assert ew.PATHS[tiles.path] == "gather_tiles"
+        assert (bench.kernel_instance(w, {"unroll": 1}, split, tiles, ew, Prep(base))
+                == f"ew_gather_tiles_kernel<{mode}>")
     assert (bench.kernel_instance(W["fused_bias_relu_f32_65536x4096"], {"unroll": 1},
                                   {"in_coaligned": [1, 1], "head": 0})
             == "ew_bias_relu_kernel<1, true, true>")
