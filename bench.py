@@ -199,7 +199,7 @@ def kernel_instance(w, launch: dict, split: dict, plan=None, ew=None, prep=None)
         # whole rows below a stride of 68; else 128 x 128 tiles below 1024
         # rows of A, 256 x 64 ones from there on
         s = w.stride % w.n
-        mode = 1 if s < 68 else 2 if -(-w.n // s) < 1024 else 3
+        mode = (4 if s % 4 == 0 else 1) if s < 68 else 2 if -(-w.n // s) < 1024 else 3
         return f"ew_gather_tiles_kernel<{mode}>"
     if path == "gather_spans":
         # the input's body start co-aligned: in + 8 * head (two inputs per output)

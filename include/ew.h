@@ -534,7 +534,8 @@ ew_status_t ew_make_plan(const char *op, const void *out, const void *in0,
  * is the k-th with k = (-r * (n/g)^-1) mod s'), written from output
  * ceil(k * segment / s') on.  block = 1024, unroll = 1, one block per tile
  * (tiles: for s < 68 bands of floor(16384 / s) rounded down to a multiple
- * of 4 whole rows, else 128 x 128 tiles while A has fewer than 1024 rows and
+ * of 4 whole rows, kept one word apart in LDS when s is a multiple of 4,
+ * else 128 x 128 tiles while A has fewer than 1024 rows and
  * 256 rows x 64 columns from there on), the grid capped at the table's
  * blocks_per_cu per compute unit, vectors = ceil(segment / 4),
  * head = tail = 0.

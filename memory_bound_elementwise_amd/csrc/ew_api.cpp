@@ -595,10 +595,10 @@ void gather_plan(const float *in, float *out, size_t n, size_t stride, int cus, 
             g->sp = sp;
             g->inv = modinv_host(np % sp, sp);
             const bool narrow = s < kGatherNarrowStrides;
-            g->tile_mode = narrow ? 1 : rows < kGatherTallRows ? 2 : 3;
-            const uint32_t cols = narrow ? (uint32_t)s : kGatherWideCols[g->tile_mode - 2];
-            g->tile_rows = narrow ? (uint32_t)(kGatherTileWords / s) & ~3u
-                                  : kGatherWideRows[g->tile_mode - 2];
+            const int wide = rows < kGatherTallRows ? 2 : 3;
+            g->tile_mode = narrow ? (s % 4 == 0 ? 4 : 1) : wide;
+            const uint32_t cols = narrow ? (uint32_t)s : kGatherWideCols[wide - 2];
+            g->tile_rows = narrow ? (uint32_t)(kGatherTileWords / s) & ~3u : kGatherWideRows[wide - 2];
             g->tiles_m = (rows + g->tile_rows - 1) / g->tile_rows;
             g->tiles = g->tiles_m * ((s + cols - 1) / cols);
             g->vectors = (np + 3) / 4;

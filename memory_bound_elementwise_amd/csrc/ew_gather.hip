@@ -329,6 +329,11 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 //   1  s < 68: tile_rows = floor(16384 / s) whole rows (rounded down to a
 //      multiple of 4), one contiguous chunk of the input kept in LDS with
 //      pitch s;
+//   4  the same when s is a multiple of 4, with the rows one word apart in
+//      LDS (pitch s + 1, four 4-byte writes per loaded vector): with pitch s
+//      the four-row reads down a column put 16 to 64 lanes on one bank, and
+//      such strides ran at 3.2-4.1 TB/s against 4.3-4.7 padded (s = 64:
+//      +45 %, 40 and 48: +40 %, 36 and 44: +12-15 %, 52 and 60: +6 %);
 //   2  128 rows by 128 columns, when A has fewer than 1024 rows;
 //   3  256 rows by 64 columns otherwise: each run gets 1 KiB per tile
 //      instead of 512 bytes, 8-25 % faster than 128 x 128 from s = 137 to
@@ -350,7 +355,7 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 // almost everywhere.  A column's destination
 // needs two 64-bit divisions: the first cols threads compute them once per
 // tile into LDS.
-template <int Mode> struct TileShape {                // modes 2 and 3
+template <int Mode> struct TileShape {                // modes 2 and 3 (1 and 4: rows vary)
     static constexpr int kRows = Mode == 2 ? 128 : 256;
     static constexpr int kCols = Mode == 2 ? 128 : 64;
     static constexpr int kPitch = kCols + 4;          // words per LDS row
@@ -362,7 +367,7 @@ constexpr int kTileLdsWords = 256 * (64 + 4);         // the largest shape: 17,4
 constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
 constexpr uint64_t kTileBandGroup = 16;               // row bands per group of tiles
 constexpr int kTileRunStarts = 128;                   // the most columns a tile holds
-static_assert(kTileLdsWords >= (int)kGatherTileWords &&
+static_assert(kTileLdsWords >= (int)(kGatherTileWords + kGatherTileWords / 33) &&
                   kTileLdsWords >= TileShape<2>::kRows * TileShape<2>::kPitch &&
                   kTileLdsWords >= TileShape<3>::kRows * TileShape<3>::kPitch,
               "every tile shape fits the LDS tile");
@@ -383,7 +388,8 @@ static_assert(kGatherWideRows[0] == TileShape<2>::kRows &&
 template <int Mode>
 __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArgs g)
 {
-    constexpr bool Narrow = Mode == 1;
+    constexpr bool Narrow = Mode == 1 || Mode == 4;
+    constexpr bool pad = Mode == 4;           // whole rows one word apart in LDS
     using W = TileShape<Narrow ? 2 : Mode>;
     __shared__ uint32_t tile[kTileLdsWords];
     __shared__ uint64_t run_start[kTileRunStarts];
@@ -391,7 +397,7 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
     const uint64_t s = g.stride, n = g.n, seg = g.seg;
     const uint32_t rows = Narrow ? g.tile_rows : (uint32_t)W::kRows;   // a multiple of 4
     const uint32_t cols = Narrow ? (uint32_t)s : (uint32_t)W::kCols;
-    const uint32_t pitch = Narrow ? (uint32_t)s : (uint32_t)W::kPitch;
+    const uint32_t pitch = Narrow ? (uint32_t)s + (pad ? 1u : 0u) : (uint32_t)W::kPitch;
     const uint32_t groups = rows / 4;         // four-row groups per column
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         // tile t: groups of kTileBandGroup row bands, each group walking its
@@ -444,10 +450,27 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
                 }
             }
             run_starts();
+            if constexpr (!pad) {
 #pragma unroll
-            for (int p = 0; p < kTileSteps; ++p) {
-                const uint32_t q = tid + p * kTileThreads;
-                if (q < quads) *reinterpret_cast<u32x4 *>(&tile[4 * q]) = v[p];
+                for (int p = 0; p < kTileSteps; ++p) {
+                    const uint32_t q = tid + p * kTileThreads;
+                    if (q < quads) *reinterpret_cast<u32x4 *>(&tile[4 * q]) = v[p];
+                }
+            } else {
+#pragma unroll
+                for (int p = 0; p < kTileSteps; ++p) {
+                    const uint32_t q = tid + p * kTileThreads;
+                    if (q < quads) {
+                        // words 4q .. 4q + 3 of the chunk: row 4q / s, one
+                        // row further once the column reaches s
+                        const uint32_t row = 4 * q / cols, col = 4 * q - row * cols;
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) {
+                            const uint32_t wrap = col + k >= cols ? 1u : 0u;
+                            tile[(row + wrap) * pitch + col + k - wrap * cols] = v[p][k];
+                        }
+                    }
+                }
             }
         } else {
             // kLanesPerRow lanes cover a row's kCols columns, kRowsPerStep
@@ -608,6 +631,7 @@ hipError_t launch_gather(const GatherArgs &args, const Launch &l, hipStream_t s)
         case 1: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<1>); break;
         case 2: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<2>); break;
         case 3: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<3>); break;
+        case 4: fn = reinterpret_cast<const void *>(&ew_gather_tiles_kernel<4>); break;
         default: return hipErrorInvalidValue;
         }
         return hipLaunchKernel(fn, dim3(l.grid), dim3(kTileThreads), kargs, 0, s);

@@ -51,7 +51,8 @@ struct GatherArgs {
     // rows m written to out[k * seg + dest(c) + m] for k < reps, where pass
     // k' = (-r * inv) mod sp starts at dest(c) = ceil(k' * seg / sp),
     // sp = stride / g and inv = (seg mod sp)^-1 mod sp.  tile_mode 1: one
-    // tile is tile_rows whole rows (stride < kGatherNarrowStrides); 2 and 3:
+    // tile is tile_rows whole rows (stride < kGatherNarrowStrides); 4: the
+    // same, the rows one word apart in LDS (stride a multiple of 4); 2 and 3:
     // tiles of kGatherWideRows[mode - 2] rows by kGatherWideCols[mode - 2]
     // columns, tiles_m row bands by ceil(stride / columns) column bands.
     int tile_mode;

@@ -130,7 +130,7 @@ def test_kernel_instance_names_match_the_profiler_s_demangled_names():
     # 1024 rows of the stride and 256 x 64 from there on
     import dataclasses
     for name, stride, mode in (("gather_f32_2e26_s33", 33, 1), ("gather_f32_2e26_s1000", 1000, 3),
-                               ("gather_f32_2e26_s33", 65537 * 3, 2)):
+                               ("gather_f32_2e26_s33", 65537 * 3, 2), ("gather_f32_2e26_s33", 36, 4)):
         w = dataclasses.replace(W[name], stride=stride)
         tiles = ew.ew_make_gather_plan(out, base, w.n, stride, 256)
         assert ew.PATHS[tiles.path] == "gather_tiles"

@@ -34,7 +34,7 @@ def _fields(n, s):
     sp, seg = s // g, n // g
     rows = (n - 1) // s + 1
     narrow = s < 68
-    mode = 1 if narrow else 2 if rows < 1024 else 3
+    mode = (4 if s % 4 == 0 else 1) if narrow else 2 if rows < 1024 else 3
     tile_rows = (TILE_WORDS // s) & ~3 if narrow else {2: 128, 3: 256}[mode]
     cols = s if narrow else {2: 128, 3: 64}[mode]
     tiles_m = -(-rows // tile_rows)
@@ -63,7 +63,8 @@ def _model(n, s, x):
     f = _fields(n, s)
     g, sp, seg, inv, narrow = f["g"], f["sp"], f["seg"], f["inv"], f["narrow"]
     rows, cols = f["tile_rows"], f["tile_cols"]
-    pitch = s if narrow else cols + 4
+    pad = narrow and s % 4 == 0          # whole rows one word apart in LDS
+    pitch = (s + pad) if narrow else cols + 4
     lanes_per_row = cols // 4
     rows_per_step = THREADS // lanes_per_row
     groups = rows // 4
@@ -98,7 +99,8 @@ def _model(n, s, x):
                     v = x[idx]
                 else:
                     v = np.where(idx < n, x[np.minimum(idx, n - 1)], 0)
-                dst = 4 * q[:, None] + np.arange(4)
+                w = 4 * q[:, None] + np.arange(4)          # words of the chunk
+                dst = (w // s) * pitch + w % s
                 assert dst.max(initial=-1) < LDS_WORDS
                 lds[dst] = v
         else:
@@ -149,6 +151,7 @@ def _model(n, s, x):
     (4225, 33),                 # 128 rows of 33 and one element: a single narrow tile
     (20000, 33), (20011, 37), (50000, 34), (60000, 104), (65536, 80), (100003, 127),
     (70000, 44), (99999, 63), (40000, 62),
+    (100001, 36), (99999, 40), (100001, 48), (100003, 64),   # whole rows one word apart in LDS
     (33000, 129), (70001, 200), (262144, 1000), (300000, 257), (200001, 1280),
     (16511, 129),               # 128 rows, the last one short by one
     (100001, 67), (100001, 68),     # the last whole-row stride, the first wide one

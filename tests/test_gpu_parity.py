@@ -318,7 +318,7 @@ def _tile_cases():
     cus = 256
     pairs = []
     for n in (4225, 20011, 100003, 1 << 20, (1 << 20) + 5, 3 << 18, 720720 + 1):
-        for s in (33, 34, 37, 40, 48, 63, 65, 67, 68, 97, 100, 126, 127):
+        for s in (33, 34, 36, 37, 40, 44, 48, 52, 63, 64, 65, 67, 68, 97, 100, 126, 127):
             pairs.append((n, s))
     for n in ((1 << 20), (1 << 20) + 1, 1000003, 3 * 5 * 7 * 4096 + 1, 4 << 20):
         for s in (129, 130, 135, 136, 200, 255, 259, 1000, 1281, 4097, 8191):
@@ -342,10 +342,12 @@ def test_gather_tiled_transposition_large_strides():
     pairs = _tile_cases()
     assert len(pairs) > 80
     assert {math.gcd(n, s) for n, s in pairs} >= {1, 2, 4, 8, 16, 31}
-    # all three tile shapes: whole rows (s < 68), 128 x 128 (fewer than
-    # 1024 rows of s elements) and 256 x 64
-    modes = {1 if s < 68 else 2 if -(-n // s) < 1024 else 3 for n, s in pairs}
-    assert modes == {1, 2, 3}
+    # all four tile shapes: whole rows (s < 68; one word apart in LDS when
+    # s is a multiple of 4), 128 x 128 (fewer than 1024 rows of s elements)
+    # and 256 x 64
+    modes = {(4 if s % 4 == 0 else 1) if s < 68 else 2 if -(-n // s) < 1024 else 3
+             for n, s in pairs}
+    assert modes == {1, 2, 3, 4}
     cases = []
     for k, (n, s) in enumerate(pairs):
         oo, oi = ((0, 0), (1, 0), (0, 3), (3, 2))[k % 4]
