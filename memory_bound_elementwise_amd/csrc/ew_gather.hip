@@ -125,13 +125,22 @@ constexpr int kLdsBytesPerCu = 160 * 1024;
 
 constexpr int kPassBlocksPerCu(int s) { return s == 2 ? 4 : s <= 5 ? 2 : 1; }
 
-// Bytes of LDS each pass block reserves: its staging (16 * S bytes per lane)
+// 16-byte LDS slots between the starts of two consecutive 1 KiB loads of a
+// wave's span: 64, or 65 for an even span.  A lane reads back its 16 * S
+// bytes at slots S * lane + v; with S even that puts many lanes of a read on
+// the same banks (all of them for S = 16 and 32), and one slot of padding
+// after each load spreads them (odd spans are spread already).  At
+// n = 2^26 + 1 the even spans ran 3-17 % below their odd neighbours before.
+constexpr int kPassChunk(int s) { return s % 2 == 0 ? 65 : 64; }
+
+// Bytes of LDS each pass block reserves: its staging (the waves' slices)
 // or, with several runs if larger, just over 1/(blocks + 1) of the CU's LDS so
 // that no more than kPassBlocksPerCu(S) blocks are resident on one CU.
+constexpr int kPassStagingBytes(int s) { return kPassThreads / 64 * kPassChunk(s) * s * 16; }
 constexpr int kPassLdsBytes(int s, int runs)
 {
-    return (runs == 1 || kPassThreads * 16 * s > kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024)
-               ? kPassThreads * 16 * s
+    return (runs == 1 || kPassStagingBytes(s) > kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024)
+               ? kPassStagingBytes(s)
                : kLdsBytesPerCu / kPassBlocksPerCu(s) - 1024;
 }
 static_assert(kPassLdsBytes(2, 2) * 5 > kLdsBytesPerCu &&
@@ -154,8 +163,8 @@ __device__ __forceinline__ void wave_lds_order()
 
 // The wave's S KiB input span, read with S 16-byte-per-lane loads that the
 // memory unit writes straight into LDS (buffer_load_dwordx4 ... lds): load v
-// puts lane i's 16 bytes, span bytes 1024 * v + 16 * i, at LDS dst + 64 * v
-// + i.  No VGPR holds the data on its way, and the only per-lane operand is
+// puts lane i's 16 bytes, span bytes 1024 * v + 16 * i, at LDS slot
+// dst + kPassChunk(S) * v + i.  No VGPR holds the data on its way, and the only per-lane operand is
 // the offset 16 * i, so all S loads leave back to back at any S.  `span`
 // and `dst` are the same in every lane of the wave.
 template <int S>
@@ -166,7 +175,8 @@ __device__ __forceinline__ void load_span_to_lds(const char *span, u32x4 *dst, u
 #pragma unroll
     for (int v = 0; v < S; ++v)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void *)(dst + 64 * v), 16, (int)(16 * lane),
+            r, (__attribute__((address_space(3))) void *)(dst + kPassChunk(S) * v), 16,
+            (int)(16 * lane),
             1024 * v, 0, EW_LOAD_NT ? 2 : 0);
 }
 
@@ -184,7 +194,7 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
     __shared__ u32x4 lds[kPassLdsBytes(S, kRuns) / 16];
     const uint32_t tid = threadIdx.x, lane = tid & 63u;
     const uint32_t wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // the same in every lane
-    u32x4 *buf = lds + wv * 64 * S;         // this wave's staging slice
+    u32x4 *buf = lds + wv * kPassChunk(S) * S;   // this wave's staging slice
     const uint64_t seg = g.seg;             // replica distance (elements)
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         const uint64_t grp0 = t * kPassThreads + wv * 64;     // first group of this wave
@@ -200,7 +210,10 @@ __global__ void __launch_bounds__(kPassThreads) ew_gather_passes_kernel(GatherAr
             wave_lds_order();
             u32x4 e[S];
 #pragma unroll
-            for (int v = 0; v < S; ++v) e[v] = buf[S * lane + v];
+            for (int v = 0; v < S; ++v) {
+                const uint32_t x = S * lane + v;        // slot of the unpadded span
+                e[v] = buf[kPassChunk(S) == 64 ? x : x + x / 64];
+            }
             wave_lds_order();       // read back before the next tile's writes
 #pragma unroll
             for (int r = 0; r < kRuns; ++r) {

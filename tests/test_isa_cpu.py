@@ -55,10 +55,13 @@ def _kernels(text):
 
 
 def _pass_lds(stride, step):
+    # staging: 4 waves x stride loads of 1 KiB, each followed by 16 bytes of
+    # padding when the stride is even
+    staging = 4 * (65 if stride % 2 == 0 else 64) * stride * 16
     if step == stride:          # one run: the staging only
-        return 256 * 16 * stride
+        return staging
     blocks_per_cu = 4 if stride == 2 else 2 if stride <= 5 else 1
-    lds = max(256 * 16 * stride, 160 * 1024 // blocks_per_cu - 1024)
+    lds = max(staging, 160 * 1024 // blocks_per_cu - 1024)
     assert lds * (blocks_per_cu + 1) > 160 * 1024 >= lds * blocks_per_cu
     return lds
 
