@@ -365,8 +365,19 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 // next fetched them twice (stride 1000, 256 x 64 tiles: 1.38 x the input
 // read).  16 row bands per group ran 2-16 % faster than that order from
 // s = 137 to 1281 and 2 % slower at 4097; groups of 4, 32 and 64 lost to 16
-// almost everywhere.  A column's destination
-// needs two 64-bit divisions: the first cols threads compute them once per
+// almost everywhere.  The dispatcher deals block b to XCD b % 8, each XCD
+// with an L2 of its own.  With 16 row bands per group, tile t + 16 (the next
+// column band, sharing the lines at the band edge) then runs on the XCD of
+// tile t, two of that XCD's tiles later.  Whole-row tiles have one column
+// band (their neighbours are the adjacent chunks t - 1 and t + 1), and with
+// r < 16 row bands the next column band is tile t + r, on another XCD
+// unless r = 8; there each XCD takes 16 consecutive tiles instead
+// (xcd_run_tile): at n = 2^26, +1.7 to +8.5 % from s = 33 to 67 and +12 to
+// +18 % for s = 65537 to 2^19 + 1 (1 to 4 row bands).  With 16 or more row
+// bands the order above stays: 16 tiles per XCD there lost 2-10 %, and a
+// whole group per XCD (column-band neighbours 16 of its tiles apart) ran
+// from +4 % (s = 1000) to -28 % (s = 2049).  A column's destination needs
+// two 64-bit divisions: the first cols threads compute them once per
 // tile into LDS.
 template <int Mode> struct TileShape {                // modes 2 and 3 (1 and 4: rows vary)
     static constexpr int kRows = Mode == 2 ? 128 : 256;
@@ -380,6 +391,18 @@ constexpr int kTileLdsWords = 256 * (64 + 4);         // the largest shape: 17,4
 constexpr uint64_t kNoRun = ~(uint64_t)0;             // a column no pass reads
 constexpr uint64_t kTileBandGroup = 16;               // row bands per group of tiles
 constexpr int kTileRunStarts = 128;                   // the most columns a tile holds
+
+// Tile t of `tiles`, dealt so that each XCD takes kXcdRun consecutive tiles:
+// within each window of 8 * kXcdRun tiles, block b (on XCD b % 8) takes tile
+// (b % 8) * kXcdRun + b / 8 of the window; the last, partial window keeps its
+// order.  A bijection on [0, tiles), whatever the grid.
+constexpr uint64_t kXcdRun = 16;
+__device__ __forceinline__ uint64_t xcd_run_tile(uint64_t t, uint64_t tiles)
+{
+    constexpr uint64_t W = 8 * kXcdRun;
+    const uint64_t win = t / W * W;
+    return win + W <= tiles ? win + (t - win) % 8 * kXcdRun + (t - win) / 8 : t;
+}
 static_assert(kTileLdsWords >= (int)(kGatherTileWords + kGatherTileWords / 33) &&
                   kTileLdsWords >= TileShape<2>::kRows * TileShape<2>::kPitch &&
                   kTileLdsWords >= TileShape<3>::kRows * TileShape<3>::kPitch,
@@ -413,10 +436,13 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
     const uint32_t pitch = Narrow ? (uint32_t)s + (pad ? 1u : 0u) : (uint32_t)W::kPitch;
     const uint32_t groups = rows / 4;         // four-row groups per column
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
-        // tile t: groups of kTileBandGroup row bands, each group walking its
-        // column bands in turn, row band fastest within a group
+        // tile u: groups of kTileBandGroup row bands, each group walking its
+        // column bands in turn, row band fastest within a group; with one
+        // column band or fewer than kTileBandGroup row bands, 16 consecutive
+        // tiles per XCD
         const uint64_t bands = g.tiles / g.tiles_m;
-        const uint64_t grp = t / (kTileBandGroup * bands), in_grp = t % (kTileBandGroup * bands);
+        const uint64_t u = Narrow || g.tiles_m < kTileBandGroup ? xcd_run_tile(t, g.tiles) : t;
+        const uint64_t grp = u / (kTileBandGroup * bands), in_grp = u % (kTileBandGroup * bands);
         const uint64_t grp_rows = g.tiles_m - grp * kTileBandGroup < kTileBandGroup
                                       ? g.tiles_m - grp * kTileBandGroup
                                       : kTileBandGroup;

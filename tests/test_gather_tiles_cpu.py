@@ -51,6 +51,23 @@ def _tile_of(t, tiles_m, bands, group=16):
     return grp * group + rest % rows_in_group, rest // rows_in_group
 
 
+def _xcd_run_tile(t, tiles, run=16):
+    """Tile t dealt so that each of the 8 XCDs takes `run` consecutive tiles
+    per window of 8 * run (the last, partial window as is)."""
+    w = 8 * run
+    win = t // w * w
+    return win + (t - win) % 8 * run + (t - win) // 8 if win + w <= tiles else t
+
+
+def test_xcd_runs_are_a_bijection():
+    for tiles in list(range(1, 400)) + [1023, 1024, 1025, 4130, 65536]:
+        got = sorted(_xcd_run_tile(t, tiles) for t in range(tiles))
+        assert got == list(range(tiles)), tiles
+    # block b of a full window lands on XCD b % 8 and its tiles there are consecutive
+    for x in range(8):
+        assert [_xcd_run_tile(b, 256) for b in range(x, 128, 8)] == list(range(16 * x, 16 * x + 16))
+
+
 def test_tile_order_covers_every_tile_once():
     for tiles_m in range(1, 70):
         for bands in range(1, 9):
@@ -74,7 +91,8 @@ def _model(n, s, x):
     writes = np.zeros(n, dtype=np.int64)
     tid = np.arange(THREADS)
     for t in range(f["tiles"]):
-        mt, ct = _tile_of(t, f["tiles_m"], f["tiles"] // f["tiles_m"])
+        u = _xcd_run_tile(t, f["tiles"]) if narrow or f["tiles_m"] < 16 else t
+        mt, ct = _tile_of(u, f["tiles_m"], f["tiles"] // f["tiles_m"])
         m0 = mt * rows
         c0 = 0 if narrow else ct * cols
         run_start = np.full(128, NO_RUN, dtype=object)
@@ -158,6 +176,8 @@ def _model(n, s, x):
     (100001, 135), (100001, 136),
     (1023 * 300 - 5, 300), (1024 * 300, 301), (1024 * 300 + 7, 300),   # 1023 / 1024 rows
     (1 << 18, 2047),            # 128 rows, wide, gcd 1
+    (2200000, 35),              # 135 whole-row tiles: one full window of XCD runs
+    (128 * 16385 - 3, 16385),   # one row band of 129 wide tiles: XCD runs
 ])
 def test_tile_model_matches_the_definition(n, s):
     p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, s, CUS)

@@ -325,6 +325,9 @@ def _tile_cases():
             pairs.append((n, s))
     pairs += [(16511, 129), (33 * 127 + 1, 33), (128 * 1000 + 3, 1000), (31 * 4099, 62),
               (1 << 20, 80), ((1 << 20) + 48, 176)]
+    # more than one window of 128 tiles dealt to the XCDs in runs of 16
+    # (whole rows, and a single row band of wide tiles)
+    pairs += [(2200000, 35), (4 << 20, 33), (4 << 20, 60), (128 * 16385 - 3, 16385)]
     out = []
     for n, s in pairs:
         p = ew.ew_make_gather_plan(1 << 40, 1 << 42, n, s, cus)
