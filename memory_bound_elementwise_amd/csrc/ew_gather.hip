@@ -359,26 +359,31 @@ __global__ void __launch_bounds__(1024) ew_gather2_kernel(GatherArgs g)
 // consecutive blocks take consecutive row bands of one column band, so each
 // continues the runs the previous one wrote, and the group then moves to the
 // next column band.  The row pieces of neighbouring bands share the lines at
-// their edges (a band starts mid-line unless the stride is a multiple of
-// 32); with the groups those lines are fetched while the other band's reads
-// are recent, where walking every row band of one column band before the
-// next fetched them twice (stride 1000, 256 x 64 tiles: 1.38 x the input
-// read).  16 row bands per group ran 2-16 % faster than that order from
-// s = 137 to 1281 and 2 % slower at 4097; groups of 4, 32 and 64 lost to 16
-// almost everywhere.  The dispatcher deals block b to XCD b % 8, each XCD
-// with an L2 of its own.  With 16 row bands per group, tile t + 16 (the next
-// column band, sharing the lines at the band edge) then runs on the XCD of
-// tile t, two of that XCD's tiles later.  Whole-row tiles have one column
-// band (their neighbours are the adjacent chunks t - 1 and t + 1), and with
-// r < 16 row bands the next column band is tile t + r, on another XCD
-// unless r = 8; there each XCD takes 16 consecutive tiles instead
-// (xcd_run_tile): at n = 2^26, +1.7 to +8.5 % from s = 33 to 67 and +12 to
-// +18 % for s = 65537 to 2^19 + 1 (1 to 4 row bands).  With 16 or more row
-// bands the order above stays: 16 tiles per XCD there lost 2-10 %, and a
-// whole group per XCD (column-band neighbours 16 of its tiles apart) ran
-// from +4 % (s = 1000) to -28 % (s = 2049).  A column's destination needs
-// two 64-bit divisions: the first cols threads compute them once per
-// tile into LDS.
+// their edges (a band starts mid-line unless the stride is a multiple of 32);
+// with the groups those lines are fetched while the other band's reads are
+// recent, where walking every row band of one column band before the next
+// fetched them twice (stride 1000, 256 x 64 tiles: 1.38 x the input read).
+// 16 row bands per group ran 2-16 % faster than that order from s = 137 to
+// 1281 and 2 % slower at 4097; groups of 4, 32 and 64 lost to 16 almost
+// everywhere.  The dispatcher deals block b to XCD b % 8, each XCD with an L2
+// of its own.  Within a full group (16 row bands) block i of the group, on
+// XCD i % 8, takes row band 2 (i % 8) + (i / 8) % 2 of column band i / 16:
+// each XCD works through two adjacent row bands of each column band in turn,
+// so that a tile's column-band neighbour (sharing the lines at the band edge)
+// runs on the same XCD two tiles later, and one row-band neighbour in two
+// (continuing the same runs) shares the L2 as well.  At n = 2^26 that gained
+// 1 to 5 % from s = 72 to 4097 (113: -0.3 %) over dealing the group in order
+// (one row band per XCD and column band); against that order, four adjacent
+// row bands in groups of 32 ran from +9 % (4097) to -6 % (2049), 16
+// consecutive tiles per XCD lost 2-10 %, and a whole group per XCD
+// (column-band neighbours 16 of its tiles apart) ran from +4 % (1000) to
+// -28 % (2049).  Whole-row tiles have one column band (their neighbours are
+// the chunks t - 1 and t + 1), and with r < 16 row bands the next column
+// band, tile t + r, lands on another XCD unless r = 8; there each XCD takes
+// 16 consecutive tiles instead (xcd_run_tile): +1.7 to +8.5 % from s = 33 to
+// 67 and +12 to +18 % for s = 65537 to 2^19 + 1 (1 to 4 row bands).  A
+// column's destination needs two 64-bit divisions: the first cols threads
+// compute them once per tile into LDS.
 template <int Mode> struct TileShape {                // modes 2 and 3 (1 and 4: rows vary)
     static constexpr int kRows = Mode == 2 ? 128 : 256;
     static constexpr int kCols = Mode == 2 ? 128 : 64;
@@ -437,17 +442,24 @@ __global__ void __launch_bounds__(kTileThreads) ew_gather_tiles_kernel(GatherArg
     const uint32_t groups = rows / 4;         // four-row groups per column
     for (uint64_t t = blockIdx.x; t < g.tiles; t += gridDim.x) {
         // tile u: groups of kTileBandGroup row bands, each group walking its
-        // column bands in turn, row band fastest within a group; with one
-        // column band or fewer than kTileBandGroup row bands, 16 consecutive
-        // tiles per XCD
+        // column bands in turn; with one column band or fewer than
+        // kTileBandGroup row bands, 16 consecutive tiles per XCD
         const uint64_t bands = g.tiles / g.tiles_m;
         const uint64_t u = Narrow || g.tiles_m < kTileBandGroup ? xcd_run_tile(t, g.tiles) : t;
         const uint64_t grp = u / (kTileBandGroup * bands), in_grp = u % (kTileBandGroup * bands);
         const uint64_t grp_rows = g.tiles_m - grp * kTileBandGroup < kTileBandGroup
                                       ? g.tiles_m - grp * kTileBandGroup
                                       : kTileBandGroup;
-        const uint64_t m0 = (grp * kTileBandGroup + in_grp % grp_rows) * rows;
-        const uint64_t c0 = Narrow ? 0 : (in_grp / grp_rows) * W::kCols;
+        uint64_t rb = in_grp % grp_rows, cb = in_grp / grp_rows;
+        if (!Narrow && g.tiles_m >= kTileBandGroup && grp_rows == kTileBandGroup) {
+            // a full group: block i of it (on XCD i % 8) takes row band
+            // 2 (i % 8) + (i / 8) % 2 of column band i / 16
+            constexpr uint64_t q = kTileBandGroup / 8;       // row bands per XCD
+            cb = in_grp / 8 / q;
+            rb = q * (in_grp % 8) + in_grp / 8 % q;
+        }
+        const uint64_t m0 = (grp * kTileBandGroup + rb) * rows;
+        const uint64_t c0 = Narrow ? 0 : cb * W::kCols;
         // the run start of each column of the tile (two 64-bit divisions),
         // computed while the tile's loads are in flight
         auto run_starts = [&]() {

@@ -43,11 +43,16 @@ def _fields(n, s):
                 tile_rows=tile_rows, tile_cols=cols, tiles_m=tiles_m, tiles=tiles)
 
 
-def _tile_of(t, tiles_m, bands, group=16):
+def _tile_of(t, tiles_m, bands, group=16, pairs=False):
     """(row band, column band) of tile t: groups of `group` row bands, each
-    group walking its column bands in turn, row band fastest."""
+    group walking its column bands in turn, row band fastest; with `pairs`,
+    block i of a full group (on XCD i % 8) takes row band
+    2 (i % 8) + (i // 8) % 2 of column band i // 16."""
     grp, rest = divmod(t, group * bands)
     rows_in_group = min(group, tiles_m - grp * group)
+    if pairs and rows_in_group == group:
+        q = group // 8
+        return grp * group + q * (rest % 8) + rest // 8 % q, rest // 8 // q
     return grp * group + rest % rows_in_group, rest // rows_in_group
 
 
@@ -71,8 +76,16 @@ def test_xcd_runs_are_a_bijection():
 def test_tile_order_covers_every_tile_once():
     for tiles_m in range(1, 70):
         for bands in range(1, 9):
-            got = {_tile_of(t, tiles_m, bands) for t in range(tiles_m * bands)}
-            assert got == {(m, c) for m in range(tiles_m) for c in range(bands)}, (tiles_m, bands)
+            for pairs in (False, True):
+                got = {_tile_of(t, tiles_m, bands, pairs=pairs) for t in range(tiles_m * bands)}
+                assert got == {(m, c) for m in range(tiles_m) for c in range(bands)}, \
+                    (tiles_m, bands, pairs)
+    # paired: each XCD (t % 8) holds row bands 2x, 2x + 1 of every column band,
+    # the column-band neighbour of a tile two of that XCD's tiles later
+    for t in range(16 * 3):
+        m, c = _tile_of(t, 16, 3, pairs=True)
+        assert m // 2 == t % 8 and c == t // 16
+        assert c == 2 or _tile_of(t + 16, 16, 3, pairs=True) == (m, c + 1)
 
 
 def _model(n, s, x):
@@ -92,7 +105,8 @@ def _model(n, s, x):
     tid = np.arange(THREADS)
     for t in range(f["tiles"]):
         u = _xcd_run_tile(t, f["tiles"]) if narrow or f["tiles_m"] < 16 else t
-        mt, ct = _tile_of(u, f["tiles_m"], f["tiles"] // f["tiles_m"])
+        mt, ct = _tile_of(u, f["tiles_m"], f["tiles"] // f["tiles_m"],
+                          pairs=not narrow and f["tiles_m"] >= 16)
         m0 = mt * rows
         c0 = 0 if narrow else ct * cols
         run_start = np.full(128, NO_RUN, dtype=object)
@@ -178,6 +192,7 @@ def _model(n, s, x):
     (1 << 18, 2047),            # 128 rows, wide, gcd 1
     (2200000, 35),              # 135 whole-row tiles: one full window of XCD runs
     (128 * 16385 - 3, 16385),   # one row band of 129 wide tiles: XCD runs
+    (300001, 69),               # 17 row bands of wide tiles: a full group in XCD pairs
 ])
 def test_tile_model_matches_the_definition(n, s):
     p = ew.ew_make_gather_plan(BASE + (8 << 30), BASE, n, s, CUS)
