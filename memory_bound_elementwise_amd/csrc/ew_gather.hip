@@ -402,6 +402,8 @@ constexpr int kTileRunStarts = 128;                   // the most columns a tile
 // (b % 8) * kXcdRun + b / 8 of the window; the last, partial window keeps its
 // order.  A bijection on [0, tiles), whatever the grid.
 constexpr uint64_t kXcdRun = 16;
+static_assert(kTileBandGroup % 8 == 0,
+              "a full group deals each of the 8 XCDs the same number of adjacent row bands");
 __device__ __forceinline__ uint64_t xcd_run_tile(uint64_t t, uint64_t tiles)
 {
     constexpr uint64_t W = 8 * kXcdRun;
