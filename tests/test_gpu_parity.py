@@ -380,7 +380,10 @@ def test_gather_tiled_transposition_launch_variants():
     """The tiled transposition with its grid capped below the tile count (the
     launch table's blocks per CU), so that blocks stride over several tiles
     and reuse their LDS tile and run starts: whole-row tiles (s = 33, 34),
-    256 x 64 (s = 200) and 128 x 128 (s = 16385, fewer than 1024 rows)."""
+    256 x 64 (s = 200) and 128 x 128 (s = 16385, fewer than 1024 rows).
+    Between them they take each tile order: XCD runs of 16 tiles over many
+    windows (whole rows; s = 16385 with 6 and 9 row bands) and two adjacent
+    row bands per XCD in full groups (s = 200, 246 and 738 row bands)."""
     print("[parity] gather tiles variants", flush=True)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     try:
