@@ -88,6 +88,24 @@ def test_every_kernel_has_no_lds_no_scratch_and_preserves_denormals(asm):
         assert d["float_denorm_mode_16_64"] == "3", name
 
 
+def test_wide_tile_instances_fit_two_blocks_per_cu(asm):
+    """The gather's 128 x 128 and 256 x 64 tile instances run two 1024-thread
+    blocks per CU: 32 waves, 8 per SIMD, so each wave may hold at most 64 of
+    a SIMD's 512 VGPRs per lane, and two blocks' LDS must fit in the CU's
+    160 KiB.  (The whole-row instances hold more registers and run one block
+    per CU.)"""
+    seen = 0
+    for name, (_, meta) in _kernels(asm).items():
+        m = re.search(r"gather_tiles_kernelILi(\d)E", name)
+        if not m or m.group(1) not in ("2", "3"):
+            continue
+        d = dict(re.findall(r"\.amdhsa_(\w+) (\S+)", meta))
+        assert int(d["next_free_vgpr"]) <= 64, (name, d["next_free_vgpr"])
+        assert 2 * int(d["group_segment_fixed_size"]) <= 160 * 1024, name
+        seen += 1
+    assert seen == 2
+
+
 def test_no_forbidden_instructions(asm):
     for pat in (r"\bv_pk_(add|mul|fma)_f32\b", r"\bv_fma_mix(lo|hi)_f16\b",
                 r"\bv_mad_mix(lo|hi)_f16\b", r"\bv_cvt_pkrtz"):
